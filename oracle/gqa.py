@@ -1,0 +1,161 @@
+"""Oracle for com.microsoft.GroupQueryAttention (float caches only).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+"""
+
+import numpy as np
+
+from .common import attend, default_scale, rms_norm, rotary, round_to, softcap
+
+
+def gqa(query, key, value, *, seqlens_k, total_sequence_length,
+        present_key, present_value,
+        past_key=None, past_value=None,
+        cos_cache=None, sin_cache=None, attention_bias=None, head_sink=None,
+        q_norm_weight=None, k_norm_weight=None,
+        num_heads, kv_num_heads, causal=1, do_rotary=0, local_window_size=-1,
+        qk_norm_epsilon=1e-6, scale=0.0, smooth_softmax=-1, softcap_value=0.0,
+        query_rows=None):
+    """Grouped-query attention with a BNSH key/value cache.
+
+    Follows the GroupQueryAttention page: Description, Inputs, Outputs and
+    Attributes tables.  Arguments carry the page's input names; ``present_key``
+    and ``present_value`` are the present buffers' contents before the call
+    (for a shared past/present buffer pass the past arrays themselves; the
+    oracle works on copies).  ``softcap_value`` is the ``softcap`` attribute.
+
+    Steps, in the page's terms:
+
+    1. head_size H = query hidden / num_heads; kv_num_heads divides num_heads,
+       group g = num_heads / kv_num_heads, and query head h reads kv head
+       h // g (Inputs table shapes; the head map is the usual grouped-query
+       one).
+    2. Each sample's total length is ``seqlens_k[b] + 1`` (Inputs table,
+       ``seqlens_k``).  With a past cache the new rows are right-aligned:
+       past_b = total_b - S, and query s sits at absolute position
+       p = past_b + s (Implementation variants, the right-aligned causal bound
+       of the chunked-prefill and shared-append routes).  Without a past
+       cache past_b = 0.
+    3. If both norm weights are given, each query and key head is RMS
+       normalised (Inputs table, ``q_norm_weight``/``k_norm_weight``).
+    4. If ``do_rotary``, queries and the new keys are rotated at p with the
+       NeoX half-split (the page implements no interleaved rotary).
+    5. Present cache: rows [0, past_b) come from the past cache, rows
+       [past_b, past_b + S) are the new (normed, rotated) keys and the values,
+       rounded to T; other rows keep the buffer's prior contents (Outputs
+       table; Implementation variants on retaining unchanged cache rows).
+    6. Attention reads keys/values from the T-rounded present cache.  With
+       ``causal`` key j is visible iff j < total_b and j <= p, and, when
+       ``local_window_size`` W >= 0, j >= p - W (W keys to the left of the
+       query plus the query's own position).  With ``causal`` = 0 (allowed
+       only without a past cache and with W = -1) every one of the S new keys
+       is visible and ``seqlens_k`` is metadata only.
+    7. score = scale * q . k; then softcap; then + attention_bias[b|0, h|0, s, j].
+    8. Softmax over visible keys; ``head_sink[h]`` (or 0 when
+       ``smooth_softmax`` = 1 and no sink is given) adds exp(sink) to the
+       denominator only.  Output is the weighted sum of values, BSH layout.
+
+    ``query_rows`` (optional iterable of s indices) restricts the attention
+    output to those query rows (the cache is always updated in full); the
+    output then has shape (B, len(query_rows), num_heads * H).
+
+    Returns ``(output float64, present_key T, present_value T)``.
+    """
+    q_in = np.asarray(query)
+    k_in = np.asarray(key)
+    v_in = np.asarray(value)
+    dtype = q_in.dtype
+    B, S, qh = q_in.shape
+    N, kvN = int(num_heads), int(kv_num_heads)
+    if N <= 0 or kvN <= 0 or N % kvN:
+        raise ValueError("kv_num_heads must divide num_heads")
+    if qh % N:
+        raise ValueError("query hidden size must be a multiple of num_heads")
+    H = qh // N
+    g = N // kvN
+    if k_in.shape != (B, S, kvN * H) or v_in.shape != (B, S, kvN * H):
+        raise ValueError("key/value must be (B, S, kv_num_heads * head_size)")
+    if (q_norm_weight is None) != (k_norm_weight is None):
+        raise ValueError("q_norm_weight and k_norm_weight must be given together")
+    if not causal and local_window_size != -1:
+        raise ValueError("causal = 0 requires local_window_size = -1")
+    if not causal and past_key is not None:
+        raise ValueError("bidirectional attention takes no past cache")
+
+    pk_out = np.array(present_key, copy=True)
+    pv_out = np.array(present_value, copy=True)
+    cap = pk_out.shape[2]
+    total_b = np.asarray(seqlens_k, dtype=np.int64) + 1
+    if past_key is not None:
+        past_b = total_b - S
+    else:
+        past_b = np.zeros(B, dtype=np.int64)
+    if np.any(past_b < 0) or np.any(past_b + S > cap):
+        raise ValueError("seqlens_k inconsistent with sequence length or cache capacity")
+
+    sc = default_scale(scale, H)
+    q = q_in.astype(np.float64).reshape(B, S, N, H)
+    k = k_in.astype(np.float64).reshape(B, S, kvN, H)
+    v = v_in.astype(np.float64).reshape(B, S, kvN, H)
+
+    if q_norm_weight is not None:
+        q = rms_norm(q, q_norm_weight, qk_norm_epsilon)
+        k = rms_norm(k, k_norm_weight, qk_norm_epsilon)
+
+    pos = past_b[:, None] + np.arange(S)[None, :]          # (B, S) absolute positions
+    if do_rotary:
+        if cos_cache is None or sin_cache is None:
+            raise ValueError("do_rotary needs cos_cache and sin_cache")
+        cos = np.asarray(cos_cache, dtype=np.float64)
+        sin = np.asarray(sin_cache, dtype=np.float64)
+        if cos.shape[1] * 2 != H:
+            raise ValueError("cos_cache width must be head_size / 2")
+        if np.max(pos) >= cos.shape[0]:
+            raise ValueError("rotary position beyond the cos/sin cache")
+        c = cos[pos][:, :, None, :]                          # (B, S, 1, H/2)
+        s_ = sin[pos][:, :, None, :]
+        q = rotary(q, c, s_)
+        k = rotary(k, c, s_)
+
+    # present cache (materialised in T)
+    for b in range(B):
+        pb = int(past_b[b])
+        if past_key is not None and pb > 0:
+            pk_out[b, :, :pb, :] = np.asarray(past_key)[b, :, :pb, :]
+            pv_out[b, :, :pb, :] = np.asarray(past_value)[b, :, :pb, :]
+        pk_out[b, :, pb:pb + S, :] = round_to(k[b].transpose(1, 0, 2), dtype)
+        pv_out[b, :, pb:pb + S, :] = round_to(v[b].transpose(1, 0, 2), dtype)
+
+    rows = np.arange(S) if query_rows is None else np.asarray(list(query_rows), dtype=np.int64)
+    out = np.zeros((B, len(rows), N, H), dtype=np.float64)
+    if head_sink is not None:
+        sinks = np.asarray(head_sink, dtype=np.float64).reshape(N)
+    elif smooth_softmax == 1:
+        sinks = np.zeros(N)
+    else:
+        sinks = None
+    bias = None if attention_bias is None else np.asarray(attention_bias, dtype=np.float64)
+    W = int(local_window_size)
+
+    for b in range(B):
+        n_keys = S if not causal else int(total_b[b])
+        p = pos[b, rows]                                      # (R,)
+        j = np.arange(n_keys)
+        if causal:
+            vis = j[None, :] <= p[:, None]
+            if W >= 0:
+                vis &= j[None, :] >= (p[:, None] - W)
+        else:
+            vis = np.ones((len(rows), n_keys), dtype=bool)
+        for h in range(N):
+            kh = h // g
+            keys = pk_out[b, kh, :n_keys, :].astype(np.float64)
+            vals = pv_out[b, kh, :n_keys, :].astype(np.float64)
+            x = sc * (q[b, rows, h, :] @ keys.T)
+            x = softcap(x, softcap_value)
+            if bias is not None:
+                bb = bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]
+                x = x + bb[rows][:, :n_keys]
+            o, _ = attend(x, vis, vals, None if sinks is None else sinks[h])
+            out[b, :, h, :] = o
+    return out.reshape(B, len(rows), N * H), pk_out, pv_out

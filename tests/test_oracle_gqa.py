@@ -1,0 +1,360 @@
+"""Pins of the GroupQueryAttention oracle against things other than itself:
+pure-Python brute force, torch's float64 SDPA on the CPU, closed forms and
+invariants.  CPU only."""
+
+import itertools
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.brute import brute_gqa
+from kv_cache_transformer_amd import workloads as wl
+
+
+def _run(case, **kw):
+    i = dict(case["inputs"])
+    a = dict(case["attrs"])
+    a["softcap_value"] = a.pop("softcap")
+    a.update(kw)
+    return oracle.gqa(i.pop("query"), i.pop("key"), i.pop("value"),
+                      total_sequence_length=case["total_sequence_length"], **i, **a)
+
+
+def _brute(case):
+    i = dict(case["inputs"])
+    a = dict(case["attrs"])
+    a["softcap_value"] = a.pop("softcap")
+    return brute_gqa(i.pop("query"), i.pop("key"), i.pop("value"), **i, **a)
+
+
+# ---------------------------------------------------------------------------
+# brute force over the feature matrix (tiny shapes)
+# ---------------------------------------------------------------------------
+
+FEATURES = list(itertools.product(
+    [None, "shared", "concat"],      # past mode
+    [-1, 0, 1, 2],                   # local window
+    [0.0, 1.5],                      # softcap
+    [None, "full", "h1", "b1"],      # bias
+    ["none", "sink", "smooth"],      # denominator term
+    [False, True],                   # q/k norm
+    [False, True],                   # rotary
+))
+
+
+@pytest.mark.parametrize("past,window,cap,bias,den,norm,rot",
+                         FEATURES[::3] + FEATURES[1::7])
+def test_gqa_matches_brute_force(past, window, cap, bias, den, norm, rot):
+    seed = zlib.crc32(repr((past, window, cap, bias, den, norm, rot)).encode())
+    rng = np.random.default_rng(seed)
+    S = 3 if past else 5
+    case = wl.gqa_case(rng, B=2, S=S, N=4, kvN=2, H=8, dtype=np.float32, past=past,
+                       cap=8 if past else None, rotary=rot, norm=norm, bias=bias,
+                       sink=(den == "sink"), smooth_softmax=1 if den == "smooth" else -1,
+                       softcap=cap, window=window)
+    o, pk, pv = _run(case)
+    ob, pkb, pvb = _brute(case)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
+    # cache rows: identical T values (the brute force rounds through numpy scalars)
+    mask = ~np.isnan(pk.astype(np.float64))
+    np.testing.assert_array_equal(pk[mask], pkb[mask])
+    np.testing.assert_array_equal(np.isnan(pk.astype(np.float64)), np.isnan(pkb.astype(np.float64)))
+    np.testing.assert_array_equal(pv[mask], pvb[mask])
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_gqa_prompt_padding_and_bidirectional_brute(dtype):
+    rng = np.random.default_rng(7)
+    case = wl.gqa_case(rng, B=2, S=5, N=2, kvN=1, H=4, dtype=dtype, total_lens=[3, 5])
+    o, _, _ = _run(case)
+    ob, _, _ = _brute(case)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
+    case = wl.gqa_case(rng, B=2, S=4, N=2, kvN=2, H=4, dtype=dtype, causal=0,
+                       total_lens=[2, 4])
+    o, _, _ = _run(case)
+    ob, _, _ = _brute(case)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# torch SDPA (float64, CPU) as an independent library routine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,window,past", [(1, -1, None), (1, 3, None), (0, -1, None),
+                                                (1, -1, "shared"), (1, 5, "shared")])
+def test_gqa_matches_torch_sdpa(causal, window, past):
+    rng = np.random.default_rng(11)
+    B, S, N, kvN, H = 2, 9, 6, 2, 16
+    case = wl.gqa_case(rng, B=B, S=S, N=N, kvN=kvN, H=H, dtype=np.float32, past=past,
+                       cap=24 if past else None, causal=causal, window=window, scale=0.3)
+    o, pk, pv = _run(case)
+    i = case["inputs"]
+    g = N // kvN
+    seqlens = i["seqlens_k"].astype(np.int64)
+    for b in range(B):
+        total = int(seqlens[b]) + 1
+        past_b = total - S if past else 0
+        n_keys = total if causal else S
+        q = torch.tensor(i["query"][b].astype(np.float64)).view(S, N, H).transpose(0, 1)
+        k = torch.tensor(pk[b, :, :n_keys].astype(np.float64)).repeat_interleave(g, 0)
+        v = torch.tensor(pv[b, :, :n_keys].astype(np.float64)).repeat_interleave(g, 0)
+        p = past_b + torch.arange(S)[:, None]
+        j = torch.arange(n_keys)[None, :]
+        m = torch.ones(S, n_keys, dtype=torch.bool)
+        if causal:
+            m &= j <= p
+            if window >= 0:
+                m &= j >= p - window
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=0.3)
+        np.testing.assert_allclose(o[b].reshape(S, N, H).transpose(1, 0, 2), ref.numpy(),
+                                   rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# invariants and closed forms
+# ---------------------------------------------------------------------------
+
+def test_rows_sum_to_one_and_constant_v():
+    rng = np.random.default_rng(3)
+    case = wl.gqa_case(rng, B=1, S=7, N=4, kvN=1, H=8, dtype=np.float32, window=2, softcap=2.0,
+                       bias="full")
+    case["inputs"]["value"][...] = 1.0
+    o, _, _ = _run(case)
+    np.testing.assert_allclose(o, 1.0, rtol=1e-13)
+    case["inputs"]["value"][...] = -2.5
+    o, _, _ = _run(case)
+    np.testing.assert_allclose(o, -2.5, rtol=1e-13)
+
+
+def test_causal_query_zero_returns_v0():
+    rng = np.random.default_rng(4)
+    case = wl.gqa_case(rng, B=2, S=6, N=4, kvN=2, H=8, dtype=np.float16, rotary=True,
+                       norm=True, softcap=3.0, scale=-0.7)
+    o, _, pv = _run(case)
+    v = case["inputs"]["value"].astype(np.float64).reshape(2, 6, 2, 8)
+    for h in range(4):
+        np.testing.assert_array_equal(o[:, 0, h * 8:(h + 1) * 8], v[:, 0, h // 2, :])
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    rng = np.random.default_rng(5)
+    B, S, N, kvN, H = 2, 6, 6, 3, 8
+    case = wl.gqa_case(rng, B=B, S=S, N=N, kvN=kvN, H=H, dtype=np.float32, window=3)
+    o, _, _ = _run(case)
+    i = case["inputs"]
+    g = N // kvN
+    k = i["key"].reshape(B, S, kvN, H).repeat(g, axis=2).reshape(B, S, N * H)
+    v = i["value"].reshape(B, S, kvN, H).repeat(g, axis=2).reshape(B, S, N * H)
+    mha = dict(case)
+    mha["inputs"] = dict(i, key=k, value=v,
+                         present_key=np.zeros((B, N, S, H), np.float32),
+                         present_value=np.zeros((B, N, S, H), np.float32))
+    mha["attrs"] = dict(case["attrs"], kv_num_heads=N)
+    o2, _, _ = _run(mha)
+    np.testing.assert_allclose(o, o2, rtol=1e-13, atol=1e-14)
+
+
+def test_head_sink_closed_forms():
+    rng = np.random.default_rng(6)
+    B, S, N, kvN, H = 1, 5, 2, 1, 4
+    case = wl.gqa_case(rng, B=B, S=S, N=N, kvN=kvN, H=H, dtype=np.float32, sink=True)
+    sink = case["inputs"]["head_sink"].astype(np.float64)
+    # V == 1: out = sum e^x / (sum e^x + e^sink)
+    case["inputs"]["value"][...] = 1.0
+    o, pk, _ = _run(case)
+    q = case["inputs"]["query"].astype(np.float64).reshape(S, N, H)
+    k = pk[0, 0].astype(np.float64)
+    sc = 1 / math.sqrt(H)
+    for h in range(N):
+        for s in range(S):
+            e = np.exp(sc * (k[:s + 1] @ q[s, h]))
+            expect = e.sum() / (e.sum() + math.exp(sink[h]))
+            np.testing.assert_allclose(o[0, s, h * H:(h + 1) * H], expect, rtol=1e-13)
+    # causal query 0: out = V0 * logistic(x00 - sink)
+    case2 = wl.gqa_case(np.random.default_rng(9), B=1, S=3, N=2, kvN=1, H=4,
+                        dtype=np.float32, sink=True)
+    o, pk, _ = _run(case2)
+    q = case2["inputs"]["query"].astype(np.float64).reshape(3, 2, 4)
+    v0 = case2["inputs"]["value"].astype(np.float64).reshape(3, 4)[0]
+    s2 = case2["inputs"]["head_sink"].astype(np.float64)
+    for h in range(2):
+        x00 = 0.5 * (q[0, h] @ pk[0, 0, 0].astype(np.float64))
+        np.testing.assert_allclose(o[0, 0, h * 4:(h + 1) * 4],
+                                   v0 / (1 + math.exp(s2[h] - x00)), rtol=1e-13)
+    # sink -> -inf reduces to the plain softmax
+    case2["inputs"]["head_sink"][...] = -1e4
+    o_s, _, _ = _run(case2)
+    i = dict(case2["inputs"])
+    i.pop("head_sink")
+    o_p, _, _ = _run(dict(case2, inputs=i))
+    np.testing.assert_allclose(o_s, o_p, rtol=1e-13)
+
+
+def test_smooth_softmax_is_zero_sink():
+    rng = np.random.default_rng(12)
+    case = wl.gqa_case(rng, B=1, S=4, N=2, kvN=1, H=4, dtype=np.float32, smooth_softmax=1)
+    o1, _, _ = _run(case)
+    i = dict(case["inputs"], head_sink=np.zeros(2, np.float32))
+    o2, _, _ = _run(dict(case, inputs=i, attrs=dict(case["attrs"], smooth_softmax=-1)))
+    np.testing.assert_array_equal(o1, o2)
+
+
+def test_softcap_limits():
+    rng = np.random.default_rng(13)
+    case = wl.gqa_case(rng, B=1, S=6, N=2, kvN=1, H=8, dtype=np.float32, scale=3.0)
+    o_none, _, _ = _run(case)
+    o_big, _, _ = _run(dict(case, attrs=dict(case["attrs"], softcap=1e7)))
+    np.testing.assert_allclose(o_big, o_none, rtol=1e-9, atol=1e-12)
+    x = np.linspace(-12, 12, 1001)
+    y = oracle.softcap(x, 2.0)
+    assert np.all(np.abs(y) < 2.0) and np.all(np.diff(y) > 0)
+    np.testing.assert_allclose(oracle.softcap(x, 0.0), x)
+
+
+def test_window_special_cases():
+    rng = np.random.default_rng(14)
+    case = wl.gqa_case(rng, B=2, S=7, N=2, kvN=1, H=4, dtype=np.float32, window=7)
+    o_w, _, _ = _run(case)
+    o_c, _, _ = _run(dict(case, attrs=dict(case["attrs"], local_window_size=-1)))
+    np.testing.assert_array_equal(o_w, o_c)
+    o_0, _, _ = _run(dict(case, attrs=dict(case["attrs"], local_window_size=0)))
+    v = case["inputs"]["value"].astype(np.float64).reshape(2, 7, 1, 4)
+    for h in range(2):
+        np.testing.assert_array_equal(o_0[:, :, h * 4:(h + 1) * 4], v[:, :, 0, :])
+    # W = 1: each row sees itself and the one before (closed form with V == position)
+    case1 = wl.gqa_case(np.random.default_rng(15), B=1, S=5, N=1, kvN=1, H=2,
+                        dtype=np.float32, window=1)
+    case1["inputs"]["value"][0, :, :] = np.arange(5, dtype=np.float32)[:, None]
+    o1, pk, _ = _run(case1)
+    q = case1["inputs"]["query"].astype(np.float64)[0]
+    k = pk[0, 0].astype(np.float64)
+    for s in range(1, 5):
+        x = np.array([q[s] @ k[s - 1], q[s] @ k[s]]) / math.sqrt(2)
+        p = np.exp(x - x.max())
+        p /= p.sum()
+        np.testing.assert_allclose(o1[0, s, 0], p[0] * (s - 1) + p[1] * s, rtol=1e-13)
+
+
+def test_bias_invariants():
+    rng = np.random.default_rng(16)
+    case = wl.gqa_case(rng, B=2, S=5, N=2, kvN=1, H=4, dtype=np.float32, bias="full")
+    i = dict(case["inputs"])
+    i.pop("attention_bias")
+    o_none, _, _ = _run(dict(case, inputs=i))
+    zero = dict(case["inputs"], attention_bias=np.zeros_like(case["inputs"]["attention_bias"]))
+    o_zero, _, _ = _run(dict(case, inputs=zero))
+    np.testing.assert_array_equal(o_zero, o_none)
+    rowc = np.broadcast_to(rng.standard_normal((2, 2, 5, 1)), (2, 2, 5, 5)).astype(np.float32)
+    o_row, _, _ = _run(dict(case, inputs=dict(case["inputs"], attention_bias=rowc.copy())))
+    np.testing.assert_allclose(o_row, o_none, rtol=1e-12, atol=1e-13)
+    # a large negative bias on one key removes it
+    big = np.zeros((1, 1, 5, 5), np.float32)
+    big[..., 0] = -1e30
+    o_drop, _, _ = _run(dict(case, inputs=dict(case["inputs"], attention_bias=big)))
+    v = case["inputs"]["value"].astype(np.float64).reshape(2, 5, 4)
+    np.testing.assert_allclose(o_drop[:, 1, :4], v[:, 1], rtol=1e-13)
+
+
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((3, 5, 16))
+    w = 1 + 0.1 * rng.standard_normal(16)
+    ref = torch.nn.functional.rms_norm(torch.tensor(x), (16,), torch.tensor(w), eps=1e-6)
+    np.testing.assert_allclose(oracle.rms_norm(x, w, 1e-6), ref.numpy(), rtol=1e-14)
+    y = oracle.rms_norm(x, np.ones(16), 1e-6)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), (1 + 1e-6 / ms) ** -0.5, rtol=1e-13)
+
+
+def test_rotary_closed_forms():
+    rng = np.random.default_rng(18)
+    H, S = 16, 12
+    c, s = wl.rope_cache(S, H, np.float64)
+    x = rng.standard_normal((S, H))
+    y = oracle.rotary(x, c, s)
+    np.testing.assert_array_equal(y[0], x[0])                                   # position 0
+    half = H // 2
+    np.testing.assert_allclose(y[:, :half] ** 2 + y[:, half:] ** 2,
+                               x[:, :half] ** 2 + x[:, half:] ** 2, rtol=1e-13)  # pair norms
+    # complex form: (a + i b) * exp(i p theta_i)
+    z = (x[:, :half] + 1j * x[:, half:]) * (c + 1j * s)
+    np.testing.assert_allclose(y[:, :half], z.real, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(y[:, half:], z.imag, rtol=1e-13, atol=1e-14)
+    # relative positions: q(p).k(p') depends on p - p' only
+    q1, k1 = rng.standard_normal(H), rng.standard_normal(H)
+    dots = {}
+    for p in range(S):
+        for pp in range(S):
+            qp = oracle.rotary(q1, c[p], s[p])
+            kp = oracle.rotary(k1, c[pp], s[pp])
+            dots.setdefault(p - pp, []).append(qp @ kp)
+    for v in dots.values():
+        np.testing.assert_allclose(v, v[0], rtol=1e-10, atol=1e-12)
+    # interleaved equals NeoX under the pair permutation
+    perm = np.empty(H, dtype=int)
+    perm[0::2] = np.arange(half)
+    perm[1::2] = np.arange(half, H)
+    yi = oracle.rotary(x[:, perm], c, s, interleaved=True)
+    np.testing.assert_allclose(yi, y[:, perm], rtol=1e-14)
+    # partial rotary leaves the tail alone
+    yp = oracle.rotary(x, c[:, :4], s[:, :4])
+    np.testing.assert_array_equal(yp[:, 8:], x[:, 8:])
+
+
+def test_cache_rows_copy_exact_and_untouched_rows_kept():
+    rng = np.random.default_rng(19)
+    case = wl.gqa_case(rng, B=2, S=2, N=4, kvN=2, H=8, dtype=np.float16, past="shared",
+                       cap=10, past_lens=[3, 8])
+    _, pk, pv = _run(case)
+    i = case["inputs"]
+    k = i["key"].reshape(2, 2, 2, 8)
+    for b, pb in enumerate([3, 8]):
+        np.testing.assert_array_equal(pk[b, :, pb:pb + 2], k[b].transpose(1, 0, 2))
+        np.testing.assert_array_equal(pk[b, :, :pb], i["past_key"][b, :, :pb])
+        np.testing.assert_array_equal(pk[b, :, pb + 2:], i["past_key"][b, :, pb + 2:])
+    # concatenated buffer: rows past the new ones keep the buffer's prior contents
+    case = wl.gqa_case(rng, B=2, S=2, N=4, kvN=2, H=8, dtype=np.float16, past="concat",
+                       cap=10, past_lens=[3, 8])
+    _, pk, _ = _run(case)
+    assert np.all(np.isnan(pk[0, :, 5:].astype(np.float64)))
+    np.testing.assert_array_equal(pk[0, :, :3], case["inputs"]["past_key"][0, :, :3])
+
+
+def test_transformed_cache_rows_are_rounded_float64():
+    rng = np.random.default_rng(20)
+    case = wl.gqa_case(rng, B=1, S=3, N=2, kvN=1, H=8, dtype=np.float16, rotary=True, norm=True)
+    _, pk, _ = _run(case)
+    i = case["inputs"]
+    k = i["key"].astype(np.float64).reshape(3, 8)
+    k = oracle.rms_norm(k, i["k_norm_weight"], 1e-6)
+    k = oracle.rotary(k, i["cos_cache"][:3], i["sin_cache"][:3])
+    np.testing.assert_array_equal(pk[0, 0, :3], k.astype(np.float16))
+
+
+def test_query_rows_subset_matches_full():
+    rng = np.random.default_rng(21)
+    case = wl.gqa_case(rng, B=2, S=9, N=4, kvN=2, H=8, dtype=np.float16, window=3, sink=True,
+                       rotary=True)
+    o, _, _ = _run(case)
+    rows = [0, 4, 8]
+    o2, _, _ = _run(case, query_rows=rows)
+    np.testing.assert_array_equal(o[:, rows], o2)
+
+
+def test_validation_errors():
+    rng = np.random.default_rng(22)
+    case = wl.gqa_case(rng, B=1, S=3, N=3, kvN=2, H=4, dtype=np.float32)
+    with pytest.raises(ValueError):
+        _run(case)
+    case = wl.gqa_case(rng, B=1, S=3, N=2, kvN=1, H=4, dtype=np.float32, norm=True)
+    i = dict(case["inputs"])
+    i.pop("k_norm_weight")
+    with pytest.raises(ValueError):
+        _run(dict(case, inputs=i))
+    case = wl.gqa_case(rng, B=1, S=3, N=2, kvN=1, H=4, dtype=np.float32, causal=0)
+    with pytest.raises(ValueError):
+        _run(case, local_window_size=2)

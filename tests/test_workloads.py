@@ -1,0 +1,53 @@
+"""The seeded generators produce the stated shapes, distributions and integer
+structures.  CPU only; the big workloads are built once each."""
+
+import numpy as np
+import pytest
+
+from kv_cache_transformer_amd import workloads as wl
+
+
+def test_csr_layouts_of_sparse_prompt():
+    rp, cols = wl.local_vertical_layouts(4, 128, local=8, stride=8)
+    np.testing.assert_array_equal(rp[:, -1], [1851, 1866, 1881, 1896])
+    assert cols.shape == (4, 1896)
+    for l in range(4):
+        assert rp[l, 0] == 0 and np.all(np.diff(rp[l]) >= 0)
+        for r in range(128):
+            row = cols[l, rp[l, r]:rp[l, r + 1]]
+            assert np.all(np.diff(row) > 0) and row.max() == r and row.min() >= 0
+            assert set(range(max(0, r - 7), r + 1)) <= set(row.tolist())
+            assert all(c % 8 == 7 - l for c in row if c < r - 7)
+
+
+def test_packed_schedule_inputs():
+    tok, cum = wl.packed_schedule_inputs([3, 1, 2], 4)
+    np.testing.assert_array_equal(cum, [0, 3, 4, 6])
+    np.testing.assert_array_equal(tok.reshape(-1), [0, 1, 2, 4, 8, 9, 3, 5, 6, 7, 10, 11])
+
+
+def test_rope_cache_values():
+    c, s = wl.rope_cache(8, 4, np.float64)
+    np.testing.assert_allclose(c[3, 1], np.cos(3 * 10000 ** -0.5))
+    np.testing.assert_allclose(s[5, 0], np.sin(5.0))
+
+
+def test_small_workloads_shapes():
+    c1 = wl.gqa_prompt_small()
+    assert c1["inputs"]["query"].shape == (1, 128, 512) and c1["inputs"]["query"].dtype == np.float32
+    c5 = wl.packed_varlen()
+    L = c5["lengths"]
+    assert L.min() >= 32 and L.max() <= 512 and len(L) == 64
+    assert c5["inputs"]["input"].shape == (int(L.sum()), 768)
+    assert c5["inputs"]["weights"].shape == (768, 2304)
+    assert abs(float(c5["inputs"]["weights"].astype(np.float64).std()) - 0.02) < 1e-3
+
+
+@pytest.mark.parametrize("name", ["gqa_decode"])
+def test_decode_workload(name):
+    c = wl.WORKLOADS[name]()
+    i = c["inputs"]
+    assert i["past_key"].shape == (16, 8, 4096, 128) and i["past_key"].dtype == np.float16
+    assert i["present_key"] is i["past_key"]
+    assert i["seqlens_k"].min() >= 1024 and i["seqlens_k"].max() <= 4095
+    assert c["total_sequence_length"] == int(i["seqlens_k"].max()) + 1
