@@ -1,0 +1,373 @@
+"""Benchmark of the MI355X attention library on its named workloads.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu]
+
+Prints ONE JSON line.  The headline ("value") is the GroupQueryAttention
+decode workload: B=16, N=32, kvN=8, H=128, fp16, shared BNSH cache of
+capacity 4096 with past lengths uniform in [1024, 4095], rotary on; one step
+is one gqa_attention call, and the value is live key/value bytes read per
+second (K and V rows 0..past_b of every sample and kv head).  The decode call
+rotates over several independently generated caches so that every call
+streams from HBM rather than from the 256 MB last-level cache.
+
+The other workloads (long prefill, small fp32 prompt, block-sparse prompt,
+packed varlen) are timed in the same run and reported under "workloads",
+each with its own roofline object.  Kernel durations come from HIP events
+that the library records around the kernel of interest
+(kvattn_profile_events); call durations from torch events on the same
+stream.  The CPU oracle is timed on a bounded sample of the decode workload
+("cpu_baseline").
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16 MFMA
+MFMA_F32_PEAK_TFS = 157.3      # MI355X fp32 matrix
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", nargs="*", default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--rotations", type=int, default=4)
+    return ap.parse_args()
+
+
+class Timer:
+    """Call time (torch events) and dominant-kernel time (library hook events)."""
+
+    def __init__(self, torch, lib, kind):
+        self.torch, self.lib, self.kind = torch, lib, kind
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ke = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record()
+        for i in range(steps):
+            self.lib.kvattn_profile_events(ks[i].cuda_event, ke[i].cuda_event, self.kind)
+            fn(warmup + i)
+        self.lib.kvattn_profile_events(None, None, 0)
+        c1.record()
+        torch.cuda.synchronize()
+        call_ms = c0.elapsed_time(c1) / steps
+        kern = [ks[i].elapsed_time(ke[i]) for i in range(steps)]
+        return call_ms, float(np.mean(kern)), float(np.median(kern))
+
+
+def decode_workload(torch, kv, wl, args, timer):
+    case = wl.gqa_decode()
+    i = case["inputs"]
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in i.items() if k not in ("present_key", "present_value")}
+    sets = [(t["past_key"], t["past_value"])]
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+    for _ in range(args.rotations - 1):
+        sets.append((torch.randn(t["past_key"].shape, generator=g, device=dev).half(),
+                     torch.randn(t["past_value"].shape, generator=g, device=dev).half()))
+    a = case["attrs"]
+    out = torch.empty_like(t["query"])
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def step(n):
+        pk, pv = sets[n % len(sets)]
+        kv.gqa_attention(t["query"], t["key"], t["value"], pk, pv, t["seqlens_k"],
+                         case["total_sequence_length"], t["cos_cache"], t["sin_cache"],
+                         num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"],
+                         do_rotary=1, output=out, present_key=pk, present_value=pv, workspace=ws)
+
+    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    lens = i["seqlens_k"].astype(np.int64) + 1
+    kvN, H = 8, 128
+    kv_bytes = int(lens.sum()) * kvN * H * 2 * 2
+    return dict(case=case, call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med,
+                kv_bytes=kv_bytes)
+
+
+def causal_window_pairs(S, W):
+    p = np.arange(S, dtype=np.int64)
+    return int(np.minimum(p + 1, W + 1 if W >= 0 else S).sum())
+
+
+def prefill_workload(torch, kv, wl, args, timer):
+    case = wl.gqa_long_prefill()
+    i = case["inputs"]
+    a = case["attrs"]
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
+    out = torch.empty_like(t["query"])
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+
+    def step(n):
+        kv.gqa_attention(t["query"], t["key"], t["value"], None, None, t["seqlens_k"],
+                         case["total_sequence_length"], t["cos_cache"], t["sin_cache"], None,
+                         t["head_sink"], t["q_norm_weight"], t["k_norm_weight"],
+                         num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"],
+                         do_rotary=1, local_window_size=a["local_window_size"],
+                         softcap=a["softcap"], output=out, present_key=t["present_key"],
+                         present_value=t["present_value"], workspace=ws)
+
+    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    B, S, N, H = 4, 4096, 32, 128
+    flops = 4 * H * causal_window_pairs(S, a["local_window_size"]) * B * N
+    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, flops=flops)
+
+
+def prompt_small_workload(torch, kv, wl, args, timer):
+    case = wl.gqa_prompt_small()
+    i = case["inputs"]
+    a = case["attrs"]
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
+    out = torch.empty_like(t["query"])
+
+    def step(n):
+        kv.gqa_attention(t["query"], t["key"], t["value"], None, None, t["seqlens_k"], 128,
+                         num_heads=8, kv_num_heads=2, scale=0.125, output=out,
+                         present_key=t["present_key"], present_value=t["present_value"])
+
+    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    flops = 4 * 64 * causal_window_pairs(128, -1) * 8
+    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, flops=flops)
+
+
+def sparse_pairs(rp, cols, N, B, S, bs):
+    L = rp.shape[0]
+    per_layout = []
+    for l in range(L):
+        tot = 0
+        for r in range(rp.shape[1] - 1):
+            for c in cols[l, rp[l, r]:rp[l, r + 1]]:
+                if c < r:
+                    tot += bs * bs
+                elif c == r:
+                    tot += bs * (bs + 1) // 2
+        per_layout.append(tot)
+    return B * sum(per_layout[h % L] for h in range(N))
+
+
+def sparse_workload(torch, kv, wl, args, timer):
+    case = wl.sparse_prompt()
+    i = case["inputs"]
+    a = case["attrs"]
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
+    out = torch.empty_like(t["query"])
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+
+    def step(n):
+        kv.sparse_attention(t["query"], t["key"], t["value"], t["past_key"], t["past_value"],
+                            t["block_row_indices"], t["block_col_indices"], 8192,
+                            t["key_total_sequence_lengths"], t["cos_cache"], t["sin_cache"],
+                            num_heads=32, kv_num_heads=8, sparse_block_size=64, do_rotary=1,
+                            output=out, workspace=ws)
+
+    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    pairs = sparse_pairs(i["block_row_indices"], i["block_col_indices"], 32, 2, 8192, 64)
+    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, flops=4 * 128 * pairs)
+
+
+def packed_workload(torch, kv, wl, args, timer):
+    case = wl.packed_varlen()
+    i = case["inputs"]
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
+    T = i["input"].shape[0]
+    out = torch.empty((T, 768), dtype=torch.float16, device=dev)
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+
+    def step(n):
+        kv.packed_attention(t["input"], t["weights"], t["bias"], t["token_offset"],
+                            t["cumulative_sequence_length"], num_heads=12, output=out,
+                            workspace=ws)
+
+    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    L = case["lengths"].astype(np.int64)
+    gemm = 2 * T * 768 * 2304
+    attn = 4 * 64 * 12 * int((L * L).sum())
+    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, gemm_flops=gemm,
+                attn_flops=attn, tokens=T)
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """Time the oracle on the decode workload, a growing prefix of the batch,
+    until about budget_s seconds of CPU work; report live KV GB/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    i = case["inputs"]
+    lens = i["seqlens_k"].astype(np.int64) + 1
+    done_bytes = 0
+    elapsed = 0.0
+    nb = 0
+    B = lens.shape[0]
+    while nb < B and elapsed < budget_s:
+        b = nb
+        sl = slice(b, b + 1)
+        t0 = time.perf_counter()
+        oracle.gqa(i["query"][sl], i["key"][sl], i["value"][sl],
+                   seqlens_k=i["seqlens_k"][sl], total_sequence_length=case["total_sequence_length"],
+                   past_key=i["past_key"][sl], past_value=i["past_value"][sl],
+                   present_key=i["past_key"][sl], present_value=i["past_value"][sl],
+                   cos_cache=i["cos_cache"], sin_cache=i["sin_cache"],
+                   num_heads=32, kv_num_heads=8, do_rotary=1)
+        elapsed += time.perf_counter() - t0
+        done_bytes += int(lens[b]) * 8 * 128 * 2 * 2
+        nb += 1
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle on the first {nb} of 16 samples of the decode "
+                      f"workload ({done_bytes / 1e6:.1f} MB of live K/V, {elapsed:.1f} s)"}
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data.get(kernel_key)
+        if not ent:
+            return None
+        import hashlib
+        h = hashlib.sha256()
+        for f in ent["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != ent["source_sha256"]:
+            return None
+        return ent["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
+              "no multi-GPU path: every workload here is one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv_cache_transformer_amd as kv
+    from kv_cache_transformer_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib = kv.library()
+    lib.kvattn_profile_events.restype = None
+    import ctypes
+    lib.kvattn_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+    only = set(args.only) if args.only else None
+
+    def want(name):
+        return only is None or name in only
+
+    res = {}
+    if want("gqa_decode"):
+        res["gqa_decode"] = decode_workload(torch, kv, wl, args, Timer(torch, lib, 1))
+        print(f"# gqa_decode done: {res['gqa_decode']['call_ms']*1e3:.1f} us/call", file=sys.stderr, flush=True)
+    if want("gqa_long_prefill"):
+        res["gqa_long_prefill"] = prefill_workload(torch, kv, wl, args, Timer(torch, lib, 2))
+        print("# gqa_long_prefill done", file=sys.stderr, flush=True)
+    if want("gqa_prompt_small"):
+        res["gqa_prompt_small"] = prompt_small_workload(torch, kv, wl, args, Timer(torch, lib, 2))
+        print("# gqa_prompt_small done", file=sys.stderr, flush=True)
+    if want("sparse_prompt"):
+        res["sparse_prompt"] = sparse_workload(torch, kv, wl, args, Timer(torch, lib, 2))
+        print("# sparse_prompt done", file=sys.stderr, flush=True)
+    if want("packed_varlen"):
+        res["packed_varlen"] = packed_workload(torch, kv, wl, args, Timer(torch, lib, 4))
+        print("# packed_varlen done", file=sys.stderr, flush=True)
+
+    workloads = {}
+    if "gqa_long_prefill" in res:
+        r = res["gqa_long_prefill"]
+        tf_k = r["flops"] / (r["kern_ms"] * 1e-3) / 1e12
+        workloads["gqa_long_prefill"] = {
+            "config": "B4 S4096 N32 kvN8 H128 fp16 causal window 1024 softcap 50 sink qk-norm rotary",
+            "call_ms": round(r["call_ms"], 4), "call_TFLOPs": round(r["flops"] / (r["call_ms"] * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "kernel": "flash", "achieved": round(tf_k, 2),
+                         "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tf_k / MFMA_F16_PEAK_TFS, 4), "kernel_ms": round(r["kern_ms"], 4),
+                         "algorithmic_flops": r["flops"], "traffic": traffic_for("flash_gqa_long_prefill")}}
+    if "gqa_prompt_small" in res:
+        r = res["gqa_prompt_small"]
+        tf_k = r["flops"] / (r["kern_ms"] * 1e-3) / 1e12
+        workloads["gqa_prompt_small"] = {
+            "config": "B1 S128 N8 kvN2 H64 fp32 causal", "call_us": round(r["call_ms"] * 1e3, 2),
+            "roofline": {"bound": "mfma", "kernel": "flash", "achieved": round(tf_k, 4),
+                         "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tf_k / MFMA_F32_PEAK_TFS, 5), "kernel_us": round(r["kern_ms"] * 1e3, 2),
+                         "algorithmic_flops": r["flops"], "traffic": None}}
+    if "sparse_prompt" in res:
+        r = res["sparse_prompt"]
+        tf_k = r["flops"] / (r["kern_ms"] * 1e-3) / 1e12
+        workloads["sparse_prompt"] = {
+            "config": "B2 S8192 N32 kvN8 H128 fp16 block 64, 4 CSR layouts, NeoX rotary",
+            "call_ms": round(r["call_ms"], 4), "call_TFLOPs": round(r["flops"] / (r["call_ms"] * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "kernel": "flash", "achieved": round(tf_k, 2),
+                         "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tf_k / MFMA_F16_PEAK_TFS, 4), "kernel_ms": round(r["kern_ms"], 4),
+                         "algorithmic_flops": r["flops"], "traffic": traffic_for("flash_sparse_prompt")}}
+    if "packed_varlen" in res:
+        r = res["packed_varlen"]
+        tot = r["gemm_flops"] + r["attn_flops"]
+        tf_g = r["gemm_flops"] / (r["kern_ms"] * 1e-3) / 1e12
+        workloads["packed_varlen"] = {
+            "config": f"64 seqs of 32..512 tokens (T={r['tokens']}), D768, QKV 768x2304, 12x64 fp16",
+            "call_ms": round(r["call_ms"], 4), "call_TFLOPs": round(tot / (r["call_ms"] * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "kernel": "qkv_gemm", "achieved": round(tf_g, 2),
+                         "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tf_g / MFMA_F16_PEAK_TFS, 4), "kernel_ms": round(r["kern_ms"], 4),
+                         "algorithmic_flops": r["gemm_flops"], "traffic": None}}
+
+    line = {"metric": "GQA prefill TFLOP/s and decode KV GB/s on 1 MI355X, % of roofline",
+            "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "gqa_decode: GroupQueryAttention decode, B16 N32 kvN8 H128 fp16, "
+                                   "shared BNSH cache 4096, past lengths U[1024,4095], rotary theta 1e4",
+                       "batch": 16, "cache_capacity": 4096}}
+    if "gqa_decode" in res:
+        r = res["gqa_decode"]
+        gbs_call = r["kv_bytes"] / (r["call_ms"] * 1e-3) / 1e9
+        gbs_k = r["kv_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
+        line["value"] = round(gbs_call, 2)
+        line["ms_per_step"] = round(r["call_ms"], 5)
+        line["config"]["live_kv_bytes"] = r["kv_bytes"]
+        line["config"]["cache_rotations"] = args.rotations
+        tr = traffic_for("decode_gqa_decode")
+        line["roofline"] = {"bound": "hbm", "kernel": "decode", "achieved": round(gbs_k, 2),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
+                            "kernel_us": round(r["kern_ms"] * 1e3, 3),
+                            "algorithmic_bytes": r["kv_bytes"], "traffic": tr}
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_baseline(r["case"])
+    line["workloads"] = workloads
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,348 @@
+"""ctypes binding of libkvattn.so: tensor descriptors, attribute structs and
+the four operator calls.  Argument marshalling only."""
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libkvattn.so")
+
+# dtype codes (kvattn_dtype)
+DT_NONE, DT_F32, DT_F16, DT_I32 = 0, 1, 2, 3
+
+# slot counts (include/kvattn.h)
+GQA_NUM_INPUTS, GQA_NUM_OUTPUTS = 14, 3
+DMMHA_NUM_INPUTS, DMMHA_NUM_OUTPUTS = 8, 4
+SPARSE_NUM_INPUTS, SPARSE_NUM_OUTPUTS = 10, 3
+PACKED_NUM_INPUTS, PACKED_NUM_OUTPUTS = 6, 1
+
+
+class KvattnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"kvattn status {status}: {message}")
+        self.status = status
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("dims", ctypes.c_int64 * 4)]
+
+
+class GqaAttrs(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("kv_num_heads", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("do_rotary", ctypes.c_int32),
+                ("local_window_size", ctypes.c_int32), ("qk_norm_epsilon", ctypes.c_float),
+                ("scale", ctypes.c_float), ("sliding_window_cache", ctypes.c_int32),
+                ("smooth_softmax", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("k_quant_type", ctypes.c_int32), ("v_quant_type", ctypes.c_int32),
+                ("kv_cache_bit_width", ctypes.c_int32)]
+
+
+class DmmhaAttrs(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("mask_filter_value", ctypes.c_float),
+                ("output_qk", ctypes.c_int32), ("past_present_share_buffer", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class SparseAttrs(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("kv_num_heads", ctypes.c_int32),
+                ("sparse_block_size", ctypes.c_int32), ("do_rotary", ctypes.c_int32),
+                ("rotary_interleaved", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class PackedAttrs(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("qkv_hidden_sizes", ctypes.c_int32 * 3),
+                ("scale", ctypes.c_float)]
+
+
+_lib = None
+_lock = threading.Lock()
+_PT = ctypes.POINTER(Tensor)
+_SZ = ctypes.POINTER(ctypes.c_size_t)
+
+
+def library():
+    """Load libkvattn.so once; raise RuntimeError if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it with "
+                "`python -m kv_cache_transformer_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        lib.kvattn_status_string.restype = ctypes.c_char_p
+        lib.kvattn_status_string.argtypes = [i32]
+        lib.kvattn_last_error.restype = ctypes.c_char_p
+        lib.kvattn_last_error.argtypes = []
+        lib.kvattn_version.restype = i32
+        lib.gqa_attention.restype = i32
+        lib.gqa_attention.argtypes = [ctypes.POINTER(GqaAttrs), _PT, i32, i32, _PT, i32, vp, sz, vp]
+        lib.gqa_attention_workspace_size.restype = i32
+        lib.gqa_attention_workspace_size.argtypes = [ctypes.POINTER(GqaAttrs), _PT, i32, i32, _PT, i32, _SZ]
+        lib.decode_mha.restype = i32
+        lib.decode_mha.argtypes = [ctypes.POINTER(DmmhaAttrs), _PT, i32, _PT, i32, vp, sz, vp]
+        lib.decode_mha_workspace_size.restype = i32
+        lib.decode_mha_workspace_size.argtypes = [ctypes.POINTER(DmmhaAttrs), _PT, i32, _PT, i32, _SZ]
+        lib.sparse_attention.restype = i32
+        lib.sparse_attention.argtypes = [ctypes.POINTER(SparseAttrs), _PT, i32, i32, _PT, i32, vp, sz, vp]
+        lib.sparse_attention_workspace_size.restype = i32
+        lib.sparse_attention_workspace_size.argtypes = [ctypes.POINTER(SparseAttrs), _PT, i32, i32, _PT, i32, _SZ]
+        lib.packed_attention.restype = i32
+        lib.packed_attention.argtypes = [ctypes.POINTER(PackedAttrs), _PT, i32, _PT, i32, vp, sz, vp]
+        lib.packed_attention_workspace_size.restype = i32
+        lib.packed_attention_workspace_size.argtypes = [ctypes.POINTER(PackedAttrs), _PT, i32, _PT, i32, _SZ]
+        lib.kvattn_packed_schedule.restype = i32
+        lib.kvattn_packed_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        lib.kvattn_profile_events.restype = None
+        lib.kvattn_profile_events.argtypes = [vp, vp, i32]
+        for name in ("gqa_attrs_default", "dmmha_attrs_default", "sparse_attrs_default",
+                     "packed_attrs_default"):
+            getattr(lib, name).restype = None
+        _lib = lib
+        return lib
+
+
+def _check(status):
+    if status != 0:
+        lib = library()
+        raise KvattnError(status, lib.kvattn_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _desc(t):
+    """kvattn_tensor for a torch tensor (or an empty slot for None)."""
+    d = Tensor()
+    if t is None:
+        return d
+    torch = _torch()
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    if t.dim() > 4:
+        raise ValueError("at most 4 dims")
+    d.data = t.data_ptr()
+    d.dtype = {torch.float32: DT_F32, torch.float16: DT_F16, torch.int32: DT_I32}.get(t.dtype, -1)
+    d.rank = t.dim()
+    for i, s in enumerate(t.shape):
+        d.dims[i] = int(s)
+    return d
+
+
+def _array(descs):
+    arr = (Tensor * len(descs))()
+    for i, d in enumerate(descs):
+        arr[i] = d
+    return arr
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace of {nbytes} bytes needed")
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# operators
+# ---------------------------------------------------------------------------
+def gqa_attention(query, key, value, past_key=None, past_value=None, seqlens_k=None,
+                  total_sequence_length=None, cos_cache=None, sin_cache=None,
+                  attention_bias=None, head_sink=None, q_norm_weight=None, k_norm_weight=None,
+                  *, num_heads, kv_num_heads, causal=1, do_rotary=0, local_window_size=-1,
+                  qk_norm_epsilon=1e-6, scale=0.0, smooth_softmax=-1, softcap=0.0,
+                  output=None, present_key=None, present_value=None, workspace=None,
+                  stream=None):
+    """GroupQueryAttention (include/kvattn.h, gqa_attention).
+
+    ``total_sequence_length`` is a host int.  Pass ``present_key=past_key``
+    (and likewise for values) to append in place to a shared buffer; when the
+    presents are None they are allocated (zero-filled) with a sequence axis of
+    past_seq + S (or S without a past).  Returns (output, present_key,
+    present_value).
+    """
+    torch = _torch()
+    lib = library()
+    B, S, _ = query.shape
+    H = query.shape[2] // num_heads
+    if total_sequence_length is None:
+        raise ValueError("total_sequence_length (host int) is required")
+    if output is None:
+        output = torch.empty_like(query)
+    if present_key is None:
+        seq = (past_key.shape[2] if past_key is not None else 0) + S
+        present_key = torch.zeros((B, kv_num_heads, seq, H), dtype=query.dtype, device=query.device)
+    if present_value is None:
+        present_value = torch.zeros_like(present_key)
+    a = GqaAttrs()
+    lib.gqa_attrs_default(ctypes.byref(a))
+    a.num_heads, a.kv_num_heads = num_heads, kv_num_heads
+    a.causal, a.do_rotary, a.local_window_size = causal, do_rotary, local_window_size
+    a.qk_norm_epsilon, a.scale = qk_norm_epsilon, scale
+    a.smooth_softmax, a.softcap = smooth_softmax, softcap
+    ins = _array([_desc(query), _desc(key), _desc(value), _desc(past_key), _desc(past_value),
+                  _desc(seqlens_k), _desc(cos_cache), _desc(sin_cache), _desc(attention_bias),
+                  _desc(head_sink), Tensor(), Tensor(), _desc(q_norm_weight),
+                  _desc(k_norm_weight)])
+    outs = _array([_desc(output), _desc(present_key), _desc(present_value)])
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.gqa_attention_workspace_size(ctypes.byref(a), ins, GQA_NUM_INPUTS,
+                                            int(total_sequence_length), outs, GQA_NUM_OUTPUTS,
+                                            ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, query.device, workspace)
+    _check(lib.gqa_attention(ctypes.byref(a), ins, GQA_NUM_INPUTS, int(total_sequence_length),
+                             outs, GQA_NUM_OUTPUTS, _ptr(ws), wsb, _stream(stream, query.device)))
+    return output, present_key, present_value
+
+
+def decode_mha(query, key, value, mask_index=None, attention_bias=None, past_key=None,
+               past_value=None, past_sequence_length=None, *, num_heads,
+               mask_filter_value=-10000.0, output_qk=0, past_present_share_buffer=None,
+               scale=0.0, output=None, qk=None, workspace=None, stream=None):
+    """DecoderMaskedMultiHeadAttention (include/kvattn.h, decode_mha).
+
+    Self attention (past_key given) appends in place to past_key/past_value.
+    Returns (output, qk) where qk is None unless output_qk = 1.
+    """
+    torch = _torch()
+    lib = library()
+    B = query.shape[0]
+    if past_present_share_buffer is None:
+        past_present_share_buffer = 1 if past_key is not None else 0
+    if output is None:
+        output = torch.empty_like(query)
+    if output_qk and qk is None:
+        qk = torch.empty((B, num_heads, 1, key.shape[2]), dtype=query.dtype, device=query.device)
+    a = DmmhaAttrs()
+    lib.dmmha_attrs_default(ctypes.byref(a))
+    a.num_heads = num_heads
+    a.mask_filter_value = mask_filter_value
+    a.output_qk = output_qk
+    a.past_present_share_buffer = past_present_share_buffer
+    a.scale = scale
+    ins = _array([_desc(query), _desc(key), _desc(value), _desc(mask_index), _desc(attention_bias),
+                  _desc(past_key), _desc(past_value), _desc(past_sequence_length)])
+    outs = _array([_desc(output), _desc(past_key), _desc(past_value), _desc(qk)])
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.decode_mha_workspace_size(ctypes.byref(a), ins, DMMHA_NUM_INPUTS, outs,
+                                         DMMHA_NUM_OUTPUTS, ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, query.device, workspace)
+    _check(lib.decode_mha(ctypes.byref(a), ins, DMMHA_NUM_INPUTS, outs, DMMHA_NUM_OUTPUTS,
+                          _ptr(ws), wsb, _stream(stream, query.device)))
+    return output, qk
+
+
+def sparse_attention(query, key, value, past_key, past_value, block_row_indices,
+                     block_col_indices, total_sequence_length, key_total_sequence_lengths,
+                     cos_cache=None, sin_cache=None, *, num_heads, kv_num_heads,
+                     sparse_block_size, do_rotary=0, rotary_interleaved=0, scale=0.0,
+                     output=None, workspace=None, stream=None):
+    """SparseAttention (include/kvattn.h, sparse_attention).
+
+    The caches are updated in place.  ``total_sequence_length`` is a host int.
+    Returns the output.
+    """
+    torch = _torch()
+    lib = library()
+    B, S, W = query.shape
+    H = W // num_heads if key is not None else W // (num_heads + 2 * kv_num_heads)
+    if output is None:
+        output = torch.empty((B, S, num_heads * H), dtype=query.dtype, device=query.device)
+    a = SparseAttrs()
+    lib.sparse_attrs_default(ctypes.byref(a))
+    a.num_heads, a.kv_num_heads = num_heads, kv_num_heads
+    a.sparse_block_size, a.do_rotary = sparse_block_size, do_rotary
+    a.rotary_interleaved, a.scale = rotary_interleaved, scale
+    ins = _array([_desc(query), _desc(key), _desc(value), _desc(past_key), _desc(past_value),
+                  _desc(block_row_indices), _desc(block_col_indices),
+                  _desc(key_total_sequence_lengths), _desc(cos_cache), _desc(sin_cache)])
+    outs = _array([_desc(output), _desc(past_key), _desc(past_value)])
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.sparse_attention_workspace_size(ctypes.byref(a), ins, SPARSE_NUM_INPUTS,
+                                               int(total_sequence_length), outs,
+                                               SPARSE_NUM_OUTPUTS, ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, query.device, workspace)
+    _check(lib.sparse_attention(ctypes.byref(a), ins, SPARSE_NUM_INPUTS, int(total_sequence_length),
+                                outs, SPARSE_NUM_OUTPUTS, _ptr(ws), wsb,
+                                _stream(stream, query.device)))
+    return output
+
+
+def packed_attention(input, weights, bias, token_offset, cumulative_sequence_length,
+                     attention_bias=None, *, num_heads, qkv_hidden_sizes=None, scale=0.0,
+                     output=None, workspace=None, stream=None):
+    """PackedAttention (include/kvattn.h, packed_attention).  Returns the output."""
+    torch = _torch()
+    lib = library()
+    T = input.shape[0]
+    C = weights.shape[1]
+    vh = C // 3 if not qkv_hidden_sizes else int(qkv_hidden_sizes[2])
+    if output is None:
+        output = torch.empty((T, vh), dtype=input.dtype, device=input.device)
+    a = PackedAttrs()
+    lib.packed_attrs_default(ctypes.byref(a))
+    a.num_heads = num_heads
+    if qkv_hidden_sizes:
+        for i in range(3):
+            a.qkv_hidden_sizes[i] = int(qkv_hidden_sizes[i])
+    a.scale = scale
+    ins = _array([_desc(input), _desc(weights), _desc(bias), _desc(token_offset),
+                  _desc(cumulative_sequence_length), _desc(attention_bias)])
+    outs = _array([_desc(output)])
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.packed_attention_workspace_size(ctypes.byref(a), ins, PACKED_NUM_INPUTS, outs,
+                                               PACKED_NUM_OUTPUTS, ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, input.device, workspace)
+    _check(lib.packed_attention(ctypes.byref(a), ins, PACKED_NUM_INPUTS, outs, PACKED_NUM_OUTPUTS,
+                                _ptr(ws), wsb, _stream(stream, input.device)))
+    return output
+
+
+def packed_schedule(cumulative_sequence_length, token_count, padded_sequence_length,
+                    tile_rows=128, per_token=True, stream=None):
+    """Run the packed schedule on its own (include/kvattn.h, kvattn_packed_schedule).
+
+    Returns (bounds (B, 2), work (1 + 2*max_items), token_sequence, token_position).
+    """
+    torch = _torch()
+    lib = library()
+    cum = cumulative_sequence_length
+    B = cum.shape[0] - 1
+    dev = cum.device
+    items = B * ((padded_sequence_length + tile_rows - 1) // tile_rows)
+    bounds = torch.zeros((B, 2), dtype=torch.int32, device=dev)
+    work = torch.zeros(1 + 2 * items, dtype=torch.int32, device=dev)
+    seq = pos = None
+    if per_token:
+        seq = torch.full((max(token_count, 1),), -1, dtype=torch.int32, device=dev)
+        pos = torch.full((max(token_count, 1),), -1, dtype=torch.int32, device=dev)
+    _check(lib.kvattn_packed_schedule(cum.data_ptr(), B, token_count, padded_sequence_length,
+                                      tile_rows, bounds.data_ptr(), work.data_ptr(), _ptr(seq),
+                                      _ptr(pos), _stream(stream, dev)))
+    return bounds, work, seq, pos

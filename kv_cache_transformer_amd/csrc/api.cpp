@@ -1,0 +1,984 @@
+// C ABI of the attention library: argument validation, launch planning and
+// kernel launches.  Every check happens before the first launch, so a call
+// that fails writes nothing.  The entry points never allocate, free or
+// synchronise; all work goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/kvattn.h"
+#include "kvattn_internal.hpp"
+
+using namespace kvattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// measurement hook (kvattn_profile_events)
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+thread_local int g_prof_kind = 0;
+
+// Launch `f` bracketed by the profiling events when `kind` is the one asked for.
+template <typename F>
+hipError_t profiled(int kind, hipStream_t st, F&& f) {
+  const bool on = g_prof_kind == kind && g_prof_start != nullptr && g_prof_stop != nullptr;
+  if (on) {
+    hipError_t e = hipEventRecord(g_prof_start, st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = f();
+  if (on && e == hipSuccess) e = hipEventRecord(g_prof_stop, st);
+  return e;
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return KVATTN_OK;
+}
+
+bool has(const kvattn_tensor& t) { return t.data != nullptr; }
+
+int64_t numel(const kvattn_tensor& t) {
+  int64_t n = 1;
+  for (int i = 0; i < t.rank; ++i) n *= t.dims[i];
+  return n;
+}
+
+std::string shape_str(const kvattn_tensor& t) {
+  std::string s = "(";
+  for (int i = 0; i < t.rank; ++i) {
+    if (i) s += ", ";
+    s += std::to_string((long long)t.dims[i]);
+  }
+  return s + ")";
+}
+
+// Check dtype, rank and dims (-1 = any) of a tensor.
+int check(const kvattn_tensor& t, const char* name, int dtype, int rank,
+          std::initializer_list<int64_t> dims) {
+  if (t.dtype != dtype)
+    return fail(KVATTN_ERR_INVALID_ARG, "%s: dtype %d, expected %d", name, t.dtype, dtype);
+  if (t.rank != rank)
+    return fail(KVATTN_ERR_INVALID_ARG, "%s: rank %d, expected %d", name, t.rank, rank);
+  int i = 0;
+  for (int64_t d : dims) {
+    if (d >= 0 && t.dims[i] != d)
+      return fail(KVATTN_ERR_INVALID_ARG, "%s: shape %s, dim %d expected %lld", name,
+                  shape_str(t).c_str(), i, (long long)d);
+    if (t.dims[i] < 0)
+      return fail(KVATTN_ERR_INVALID_ARG, "%s: negative dim", name);
+    ++i;
+  }
+  return KVATTN_OK;
+}
+
+#define CHECK(x)                       \
+  do {                                 \
+    int _rc = (x);                     \
+    if (_rc != KVATTN_OK) return _rc;  \
+  } while (0)
+
+DType to_dtype(int dt) { return dt == KVATTN_DT_F16 ? DType::F16 : DType::F32; }
+size_t elem_size(int dt) { return dt == KVATTN_DT_F16 ? 2 : 4; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_head_size(int H, const char* op) {
+  if (H <= 0 || H % 8 != 0 || H > 256)
+    return fail(KVATTN_ERR_UNSUPPORTED, "%s: head size %d (must be a multiple of 8, at most 256)", op, H);
+  return KVATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return KVATTN_OK;
+}
+
+float resolve_scale(float scale, int H) {
+  return scale == 0.f ? 1.f / std::sqrt((float)H) : scale;
+}
+
+// ===========================================================================
+// GroupQueryAttention
+// ===========================================================================
+struct GqaPlan {
+  int B, S, N, kvN, H, HP, cap, past_seq;
+  int dt;
+  bool has_past, shared, decode, q_transform;
+  int total;
+  // decode
+  int chunk, max_chunks, head_groups;
+  size_t ws_q, ws_part, ws_total;
+};
+
+int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int total,
+                 const kvattn_tensor* out, int n_out, GqaPlan& P) {
+  if (!a || !in || !out) return fail(KVATTN_ERR_INVALID_ARG, "gqa_attention: null argument");
+  if (n_in != GQA_NUM_INPUTS || n_out != GQA_NUM_OUTPUTS)
+    return fail(KVATTN_ERR_INVALID_ARG, "gqa_attention: expected %d inputs and %d outputs",
+                GQA_NUM_INPUTS, GQA_NUM_OUTPUTS);
+  const kvattn_tensor& q = in[GQA_IN_QUERY];
+  if (!has(q)) return fail(KVATTN_ERR_INVALID_ARG, "query is required");
+  if (q.dtype != KVATTN_DT_F16 && q.dtype != KVATTN_DT_F32)
+    return fail(KVATTN_ERR_UNSUPPORTED, "query dtype %d: only float16 and float32", q.dtype);
+  const int dt = q.dtype;
+  CHECK(check(q, "query", dt, 3, {-1, -1, -1}));
+  P.dt = dt;
+  P.B = (int)q.dims[0];
+  P.S = (int)q.dims[1];
+  P.N = a->num_heads;
+  P.kvN = a->kv_num_heads;
+  if (P.N <= 0 || P.kvN <= 0 || P.N % P.kvN)
+    return fail(KVATTN_ERR_INVALID_ARG, "num_heads %d / kv_num_heads %d: kv_num_heads must divide num_heads", P.N, P.kvN);
+  if (q.dims[2] % P.N) return fail(KVATTN_ERR_INVALID_ARG, "query hidden %lld not divisible by num_heads", (long long)q.dims[2]);
+  P.H = (int)(q.dims[2] / P.N);
+  CHECK(check_head_size(P.H, "gqa_attention"));
+  P.HP = padded_head(P.H);
+  if (a->k_quant_type != 0 || a->v_quant_type != 0 || a->kv_cache_bit_width != 0 ||
+      has(in[GQA_IN_K_SCALE]) || has(in[GQA_IN_V_SCALE]))
+    return fail(KVATTN_ERR_UNSUPPORTED, "quantised key/value caches are not implemented");
+  if (a->sliding_window_cache != 0)
+    return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache is not implemented");
+  if (a->causal != 0 && a->causal != 1) return fail(KVATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (a->local_window_size < -1) return fail(KVATTN_ERR_INVALID_ARG, "local_window_size must be >= -1");
+  if (!a->causal && a->local_window_size != -1)
+    return fail(KVATTN_ERR_INVALID_ARG, "causal = 0 requires local_window_size = -1");
+  if (!(a->softcap >= 0.f)) return fail(KVATTN_ERR_INVALID_ARG, "softcap must be >= 0");
+  if (!std::isfinite(a->scale)) return fail(KVATTN_ERR_INVALID_ARG, "scale must be finite");
+
+  const kvattn_tensor& k = in[GQA_IN_KEY];
+  const kvattn_tensor& v = in[GQA_IN_VALUE];
+  if (!has(k) || !has(v)) return fail(KVATTN_ERR_UNSUPPORTED, "packed QKV (no key/value) is not implemented");
+  CHECK(check(k, "key", dt, 3, {P.B, -1, (int64_t)P.kvN * P.H}));
+  CHECK(check(v, "value", dt, 3, {P.B, k.dims[1], (int64_t)P.kvN * P.H}));
+  if (k.dims[1] != P.S) return fail(KVATTN_ERR_UNSUPPORTED, "kv_sequence_length %lld != sequence_length %d", (long long)k.dims[1], P.S);
+
+  const kvattn_tensor& pk = in[GQA_IN_PAST_KEY];
+  const kvattn_tensor& pv = in[GQA_IN_PAST_VALUE];
+  if (has(pk) != has(pv)) return fail(KVATTN_ERR_INVALID_ARG, "past_key and past_value go together");
+  P.has_past = has(pk);
+  if (P.has_past) {
+    if (!a->causal) return fail(KVATTN_ERR_UNSUPPORTED, "bidirectional attention takes no past cache");
+    CHECK(check(pk, "past_key", dt, 4, {P.B, P.kvN, -1, P.H}));
+    CHECK(check(pv, "past_value", dt, 4, {P.B, P.kvN, pk.dims[2], P.H}));
+    P.past_seq = (int)pk.dims[2];
+  } else {
+    P.past_seq = 0;
+  }
+  const kvattn_tensor& sl = in[GQA_IN_SEQLENS_K];
+  if (!has(sl)) return fail(KVATTN_ERR_INVALID_ARG, "seqlens_k is required");
+  CHECK(check(sl, "seqlens_k", KVATTN_DT_I32, 1, {P.B}));
+  if (total < 1) return fail(KVATTN_ERR_INVALID_ARG, "total_sequence_length must be >= 1");
+  P.total = total;
+
+  const kvattn_tensor& o = out[GQA_OUT_OUTPUT];
+  const kvattn_tensor& ck = out[GQA_OUT_PRESENT_KEY];
+  const kvattn_tensor& cv = out[GQA_OUT_PRESENT_VALUE];
+  if (!has(o) || !has(ck) || !has(cv)) return fail(KVATTN_ERR_INVALID_ARG, "output, present_key and present_value are required");
+  CHECK(check(o, "output", dt, 3, {P.B, P.S, (int64_t)P.N * P.H}));
+  CHECK(check(ck, "present_key", dt, 4, {P.B, P.kvN, -1, P.H}));
+  CHECK(check(cv, "present_value", dt, 4, {P.B, P.kvN, ck.dims[2], P.H}));
+  P.cap = (int)ck.dims[2];
+  P.shared = P.has_past && ck.data == pk.data;
+  if (P.has_past && ((cv.data == pv.data) != P.shared))
+    return fail(KVATTN_ERR_INVALID_ARG, "present_key and present_value must both share the past buffers or neither");
+  if (P.shared && ck.dims[2] != pk.dims[2])
+    return fail(KVATTN_ERR_INVALID_ARG, "a shared present buffer must have the past buffer's dims");
+  if (P.has_past && P.cap < total)
+    return fail(KVATTN_ERR_INVALID_ARG, "present sequence axis %d cannot hold total_sequence_length %d", P.cap, total);
+  if (!P.has_past && P.cap < P.S)
+    return fail(KVATTN_ERR_INVALID_ARG, "present sequence axis %d < sequence_length %d", P.cap, P.S);
+
+  const kvattn_tensor& cs = in[GQA_IN_COS_CACHE];
+  const kvattn_tensor& sn = in[GQA_IN_SIN_CACHE];
+  if (a->do_rotary) {
+    if (!has(cs) || !has(sn)) return fail(KVATTN_ERR_INVALID_ARG, "do_rotary needs cos_cache and sin_cache");
+    CHECK(check(cs, "cos_cache", dt, 2, {-1, P.H / 2}));
+    CHECK(check(sn, "sin_cache", dt, 2, {cs.dims[0], P.H / 2}));
+    const int need = P.has_past ? total : P.S;
+    if (cs.dims[0] < need)
+      return fail(KVATTN_ERR_INVALID_ARG, "cos_cache has %lld rows, positions up to %d are used", (long long)cs.dims[0], need - 1);
+  }
+  const kvattn_tensor& bias = in[GQA_IN_ATTENTION_BIAS];
+  if (has(bias)) {
+    CHECK(check(bias, "attention_bias", dt, 4, {-1, -1, P.S, a->causal ? total : P.S}));
+    if (bias.dims[0] != 1 && bias.dims[0] != P.B) return fail(KVATTN_ERR_INVALID_ARG, "attention_bias dim 0 must be 1 or batch");
+    if (bias.dims[1] != 1 && bias.dims[1] != P.N) return fail(KVATTN_ERR_INVALID_ARG, "attention_bias dim 1 must be 1 or num_heads");
+  }
+  if (has(in[GQA_IN_HEAD_SINK])) CHECK(check(in[GQA_IN_HEAD_SINK], "head_sink", dt, 1, {P.N}));
+  const bool qn = has(in[GQA_IN_Q_NORM_WEIGHT]), kn = has(in[GQA_IN_K_NORM_WEIGHT]);
+  if (qn != kn) return fail(KVATTN_ERR_INVALID_ARG, "q_norm_weight and k_norm_weight must be given together");
+  if (qn) {
+    CHECK(check(in[GQA_IN_Q_NORM_WEIGHT], "q_norm_weight", dt, 1, {P.H}));
+    CHECK(check(in[GQA_IN_K_NORM_WEIGHT], "k_norm_weight", dt, 1, {P.H}));
+  }
+
+  P.decode = P.has_past && P.S == 1;
+  P.q_transform = qn || a->do_rotary;
+  size_t esz = elem_size(dt);
+  P.ws_q = 0;
+  P.ws_part = 0;
+  if (P.decode) {
+    P.head_groups = (P.N / P.kvN + 15) / 16;
+    const long units = (long)P.B * P.kvN * P.head_groups;
+    int chunk = 256;
+    while (chunk > 128 && units * ((total + chunk - 1) / chunk) < 1024) chunk /= 2;
+    while (chunk < 8192 && units * ((total + chunk - 1) / chunk) > 4096) chunk *= 2;
+    P.chunk = chunk;
+    P.max_chunks = (total + chunk - 1) / chunk;
+    if (P.max_chunks > 1)
+      P.ws_part = align256((size_t)P.B * P.N * P.max_chunks * (P.HP + 2) * sizeof(float));
+  } else if (P.q_transform) {
+    P.ws_q = align256((size_t)P.B * P.S * P.N * P.H * esz);
+  }
+  P.ws_total = P.ws_q + P.ws_part;
+  return KVATTN_OK;
+}
+
+int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* out,
+            const GqaPlan& P, void* ws, hipStream_t st) {
+  const DType dt = to_dtype(P.dt);
+  const kvattn_tensor& ck = out[GQA_OUT_PRESENT_KEY];
+  const kvattn_tensor& cv = out[GQA_OUT_PRESENT_VALUE];
+  const float scale = resolve_scale(a->scale, P.H);
+  char* wsb = static_cast<char*>(ws);
+
+  if (P.has_past && !P.shared) {
+    CopyPastParams c{};
+    c.pk = in[GQA_IN_PAST_KEY].data;
+    c.pv = in[GQA_IN_PAST_VALUE].data;
+    c.ck = ck.data;
+    c.cv = cv.data;
+    c.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
+    c.B = P.B; c.kvN = P.kvN; c.H = P.H; c.S = P.S; c.past_seq = P.past_seq; c.cap = P.cap;
+    CHECK(hip_status(launch_copy_past(dt, c, st), "copy_past launch"));
+  }
+
+  const kvattn_tensor& bias = in[GQA_IN_ATTENTION_BIAS];
+  if (P.decode) {
+    DecodeParams d{};
+    d.q = in[GQA_IN_QUERY].data;
+    d.k_new = in[GQA_IN_KEY].data;
+    d.v_new = in[GQA_IN_VALUE].data;
+    d.kc = ck.data;
+    d.vc = cv.data;
+    d.q_norm = in[GQA_IN_Q_NORM_WEIGHT].data;
+    d.k_norm = in[GQA_IN_K_NORM_WEIGHT].data;
+    d.eps = a->qk_norm_epsilon;
+    if (a->do_rotary) {
+      d.cos = in[GQA_IN_COS_CACHE].data;
+      d.sin = in[GQA_IN_SIN_CACHE].data;
+      d.rot_rows = (int)in[GQA_IN_COS_CACHE].dims[0];
+    }
+    if (has(bias)) {
+      d.bias = bias.data;
+      d.bias_cols = (int)bias.dims[3];
+      d.bias_sb = bias.dims[0] > 1 ? bias.dims[1] * bias.dims[3] : 0;
+      d.bias_sh = bias.dims[1] > 1 ? bias.dims[3] : 0;
+    }
+    d.sink = in[GQA_IN_HEAD_SINK].data;
+    d.smooth = a->smooth_softmax == 1;
+    d.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
+    d.len_mode = 0;
+    d.window = a->local_window_size;
+    d.out = out[GQA_OUT_OUTPUT].data;
+    d.part = reinterpret_cast<float*>(wsb + P.ws_q);
+    d.B = P.B; d.N = P.N; d.kvN = P.kvN; d.H = P.H; d.cap = P.cap;
+    d.scale = scale;
+    d.softcap = a->softcap;
+    d.chunk = P.chunk; d.max_chunks = P.max_chunks; d.head_groups = P.head_groups;
+    CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st, [&] { return launch_decode(dt, P.HP, d, st); }),
+                     "decode launch"));
+    return ok();
+  }
+
+  // prefill: prep (k/v into the cache, transformed queries), then flash
+  PrepParams pp{};
+  pp.q = in[GQA_IN_QUERY].data;
+  pp.k = in[GQA_IN_KEY].data;
+  pp.v = in[GQA_IN_VALUE].data;
+  pp.q_stride = (int64_t)P.N * P.H;
+  pp.k_stride = pp.v_stride = (int64_t)P.kvN * P.H;
+  pp.q_out = P.q_transform ? ws : nullptr;
+  pp.kc = ck.data;
+  pp.vc = cv.data;
+  pp.q_norm = in[GQA_IN_Q_NORM_WEIGHT].data;
+  pp.k_norm = in[GQA_IN_K_NORM_WEIGHT].data;
+  pp.eps = a->qk_norm_epsilon;
+  if (a->do_rotary) {
+    pp.cos = in[GQA_IN_COS_CACHE].data;
+    pp.sin = in[GQA_IN_SIN_CACHE].data;
+    pp.rot_half = P.H / 2;
+    pp.rot_rows = (int)in[GQA_IN_COS_CACHE].dims[0];
+  }
+  pp.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
+  pp.pos_mode = P.has_past ? 1 : 0;
+  pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
+  pp.write_q = P.q_transform;
+  pp.write_kv = 1;
+  CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
+                   "prep launch"));
+
+  FlashParams f{};
+  f.q = P.q_transform ? ws : in[GQA_IN_QUERY].data;
+  f.q_s = (int64_t)P.N * P.H;
+  f.q_b = f.q_s * P.S;
+  f.q_h = P.H;
+  f.kc = ck.data;
+  f.vc = cv.data;
+  f.k_j = P.H;
+  f.k_h = (int64_t)P.cap * P.H;
+  f.k_b = f.k_h * P.kvN;
+  f.out = out[GQA_OUT_OUTPUT].data;
+  f.o_s = (int64_t)P.N * P.H;
+  f.o_b = f.o_s * P.S;
+  f.o_h = P.H;
+  if (has(bias)) {
+    f.bias = bias.data;
+    const int64_t cols = bias.dims[3];
+    f.bias_ss = cols;
+    f.bias_sh = bias.dims[1] > 1 ? P.S * cols : 0;
+    f.bias_sb = bias.dims[0] > 1 ? bias.dims[1] * P.S * cols : 0;
+    f.bias_cols = (int)cols;
+  }
+  f.sink = in[GQA_IN_HEAD_SINK].data;
+  f.smooth = a->smooth_softmax == 1;
+  f.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
+  f.has_past = P.has_past;
+  f.causal = a->causal;
+  f.window = a->local_window_size;
+  f.kv_rows = P.cap;
+  f.B = P.B; f.S = P.S; f.N = P.N; f.kvN = P.kvN; f.H = P.H;
+  f.scale = scale;
+  f.softcap = a->softcap;
+  const int g = P.N / P.kvN;
+  const int hw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  f.heads_per_wg = hw;
+  f.rows_per_wg = 128 / hw;
+  f.mode = kDense;
+  const int gx = (P.S + f.rows_per_wg - 1) / f.rows_per_wg;
+  CHECK(hip_status(profiled(KVATTN_PROFILE_FLASH, st,
+                            [&] { return launch_flash(dt, P.HP, f, gx, P.kvN * (g / hw), P.B, st); }),
+                   "flash launch"));
+  return ok();
+}
+
+// ===========================================================================
+// DecoderMaskedMultiHeadAttention
+// ===========================================================================
+struct DmmhaPlan {
+  int B, N, H, HP, dt, cap, kv_len;
+  bool self;
+  int chunk, max_chunks;
+  size_t ws_total;
+};
+
+int dmmha_validate(const dmmha_attrs* a, const kvattn_tensor* in, int n_in,
+                   const kvattn_tensor* out, int n_out, DmmhaPlan& P) {
+  if (!a || !in || !out) return fail(KVATTN_ERR_INVALID_ARG, "decode_mha: null argument");
+  if (n_in != DMMHA_NUM_INPUTS || n_out != DMMHA_NUM_OUTPUTS)
+    return fail(KVATTN_ERR_INVALID_ARG, "decode_mha: expected %d inputs and %d outputs", DMMHA_NUM_INPUTS, DMMHA_NUM_OUTPUTS);
+  const kvattn_tensor& q = in[DMMHA_IN_QUERY];
+  if (!has(q)) return fail(KVATTN_ERR_INVALID_ARG, "query is required");
+  if (q.dtype != KVATTN_DT_F16 && q.dtype != KVATTN_DT_F32)
+    return fail(KVATTN_ERR_UNSUPPORTED, "query dtype %d: only float16 and float32", q.dtype);
+  const int dt = q.dtype;
+  P.dt = dt;
+  CHECK(check(q, "query", dt, 3, {-1, 1, -1}));
+  P.B = (int)q.dims[0];
+  P.N = a->num_heads;
+  if (P.N <= 0 || q.dims[2] % P.N) return fail(KVATTN_ERR_INVALID_ARG, "num_heads %d must divide the query hidden size", P.N);
+  P.H = (int)(q.dims[2] / P.N);
+  CHECK(check_head_size(P.H, "decode_mha"));
+  P.HP = padded_head(P.H);
+  if (!std::isfinite(a->scale) || !std::isfinite(a->mask_filter_value))
+    return fail(KVATTN_ERR_INVALID_ARG, "scale and mask_filter_value must be finite");
+  const kvattn_tensor& k = in[DMMHA_IN_KEY];
+  const kvattn_tensor& v = in[DMMHA_IN_VALUE];
+  if (!has(k) || !has(v)) return fail(KVATTN_ERR_INVALID_ARG, "key and value are required");
+  const kvattn_tensor& pk = in[DMMHA_IN_PAST_KEY];
+  const kvattn_tensor& pv = in[DMMHA_IN_PAST_VALUE];
+  if (has(pk) != has(pv)) return fail(KVATTN_ERR_INVALID_ARG, "past_key and past_value go together");
+  P.self = has(pk);
+  const kvattn_tensor& o = out[DMMHA_OUT_OUTPUT];
+  if (!has(o)) return fail(KVATTN_ERR_INVALID_ARG, "output is required");
+  CHECK(check(o, "output", dt, 3, {P.B, 1, (int64_t)P.N * P.H}));
+  const kvattn_tensor& qk = out[DMMHA_OUT_QK];
+  if (P.self) {
+    if (a->past_present_share_buffer != 1)
+      return fail(KVATTN_ERR_INVALID_ARG, "self attention requires past_present_share_buffer = 1");
+    CHECK(check(k, "key", dt, 3, {P.B, 1, (int64_t)P.N * P.H}));
+    CHECK(check(v, "value", dt, 3, {P.B, 1, (int64_t)P.N * P.H}));
+    CHECK(check(pk, "past_key", dt, 4, {P.B, P.N, -1, P.H}));
+    CHECK(check(pv, "past_value", dt, 4, {P.B, P.N, pk.dims[2], P.H}));
+    P.cap = (int)pk.dims[2];
+    if (P.cap < 1) return fail(KVATTN_ERR_INVALID_ARG, "past_key capacity must be >= 1");
+    const kvattn_tensor& psl = in[DMMHA_IN_PAST_SEQUENCE_LENGTH];
+    if (!has(psl)) return fail(KVATTN_ERR_INVALID_ARG, "self attention needs past_sequence_length");
+    if (psl.dtype != KVATTN_DT_I32 || numel(psl) != 1)
+      return fail(KVATTN_ERR_INVALID_ARG, "past_sequence_length must hold one int32");
+    const kvattn_tensor& ck = out[DMMHA_OUT_PRESENT_KEY];
+    const kvattn_tensor& cv = out[DMMHA_OUT_PRESENT_VALUE];
+    if ((has(ck) && ck.data != pk.data) || (has(cv) && cv.data != pv.data))
+      return fail(KVATTN_ERR_INVALID_ARG, "present_key/present_value must be the past buffers (shared) or absent");
+    if (a->output_qk || has(qk))
+      return fail(KVATTN_ERR_INVALID_ARG, "qk is produced for cross attention only");
+    P.kv_len = P.cap;
+  } else {
+    if (a->past_present_share_buffer != 0)
+      return fail(KVATTN_ERR_INVALID_ARG, "cross attention has no cache: past_present_share_buffer must be 0");
+    CHECK(check(k, "key", dt, 4, {P.B, P.N, -1, P.H}));
+    CHECK(check(v, "value", dt, 4, {P.B, P.N, k.dims[2], P.H}));
+    P.kv_len = (int)k.dims[2];
+    P.cap = P.kv_len;
+    if (P.kv_len < 1) return fail(KVATTN_ERR_INVALID_ARG, "key must hold at least one position");
+    if (has(in[DMMHA_IN_ATTENTION_BIAS]))
+      return fail(KVATTN_ERR_INVALID_ARG, "attention_bias is for self attention only");
+    if (has(out[DMMHA_OUT_PRESENT_KEY]) || has(out[DMMHA_OUT_PRESENT_VALUE]))
+      return fail(KVATTN_ERR_INVALID_ARG, "cross attention has no present cache");
+    if ((a->output_qk != 0) != has(qk))
+      return fail(KVATTN_ERR_INVALID_ARG, "output_qk must agree with the presence of the qk output");
+    if (has(qk)) CHECK(check(qk, "qk", dt, 4, {P.B, P.N, 1, P.kv_len}));
+  }
+  const kvattn_tensor& m = in[DMMHA_IN_MASK_INDEX];
+  if (has(m)) {
+    CHECK(check(m, "mask_index", KVATTN_DT_I32, 2, {P.B, -1}));
+    if (!P.self && m.dims[1] != P.kv_len) return fail(KVATTN_ERR_INVALID_ARG, "mask_index must be (batch, kv_sequence_length)");
+  }
+  const kvattn_tensor& bias = in[DMMHA_IN_ATTENTION_BIAS];
+  if (has(bias)) {
+    CHECK(check(bias, "attention_bias", dt, 4, {-1, -1, 1, -1}));
+    if (bias.dims[0] != 1 && bias.dims[0] != P.B) return fail(KVATTN_ERR_INVALID_ARG, "attention_bias dim 0 must be 1 or batch");
+    if (bias.dims[1] != 1 && bias.dims[1] != P.N) return fail(KVATTN_ERR_INVALID_ARG, "attention_bias dim 1 must be 1 or num_heads");
+  }
+  const long units = (long)P.B * P.N;
+  int chunk = 256;
+  while (chunk > 128 && units * ((P.kv_len + chunk - 1) / chunk) < 1024) chunk /= 2;
+  while (chunk < 8192 && units * ((P.kv_len + chunk - 1) / chunk) > 4096) chunk *= 2;
+  P.chunk = chunk;
+  P.max_chunks = (P.kv_len + chunk - 1) / chunk;
+  P.ws_total = P.max_chunks > 1 ? align256((size_t)P.B * P.N * P.max_chunks * (P.HP + 2) * sizeof(float)) : 0;
+  return KVATTN_OK;
+}
+
+int dmmha_run(const dmmha_attrs* a, const kvattn_tensor* in, const kvattn_tensor* out,
+              const DmmhaPlan& P, void* ws, hipStream_t st) {
+  DecodeParams d{};
+  d.q = in[DMMHA_IN_QUERY].data;
+  if (P.self) {
+    d.k_new = in[DMMHA_IN_KEY].data;
+    d.v_new = in[DMMHA_IN_VALUE].data;
+    d.kc = in[DMMHA_IN_PAST_KEY].data;
+    d.vc = in[DMMHA_IN_PAST_VALUE].data;
+    d.lens = static_cast<const int32_t*>(in[DMMHA_IN_PAST_SEQUENCE_LENGTH].data);
+    d.len_mode = 1;
+  } else {
+    d.kc = in[DMMHA_IN_KEY].data;
+    d.vc = in[DMMHA_IN_VALUE].data;
+    d.len_mode = 2;
+    d.host_n = P.kv_len;
+    d.qk = out[DMMHA_OUT_QK].data;
+  }
+  const kvattn_tensor& bias = in[DMMHA_IN_ATTENTION_BIAS];
+  if (has(bias)) {
+    d.bias = bias.data;
+    d.bias_cols = (int)bias.dims[3];
+    d.bias_sb = bias.dims[0] > 1 ? bias.dims[1] * bias.dims[3] : 0;
+    d.bias_sh = bias.dims[1] > 1 ? bias.dims[3] : 0;
+  }
+  const kvattn_tensor& m = in[DMMHA_IN_MASK_INDEX];
+  if (has(m)) {
+    d.mask = static_cast<const int32_t*>(m.data);
+    d.mask_cols = (int)m.dims[1];
+  }
+  d.mask_filter = a->mask_filter_value;
+  d.window = -1;
+  d.out = out[DMMHA_OUT_OUTPUT].data;
+  d.part = static_cast<float*>(ws);
+  d.B = P.B; d.N = P.N; d.kvN = P.N; d.H = P.H; d.cap = P.cap;
+  d.scale = resolve_scale(a->scale, P.H);
+  d.chunk = P.chunk; d.max_chunks = P.max_chunks; d.head_groups = 1;
+  CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st,
+                            [&] { return launch_decode(to_dtype(P.dt), P.HP, d, st); }),
+                   "decode launch"));
+  return ok();
+}
+
+// ===========================================================================
+// SparseAttention
+// ===========================================================================
+struct SparsePlan {
+  int B, S, N, kvN, H, HP, dt, cap, L, max_blocks, max_nnz, rot_half, bs;
+  bool packed_qkv, rotary;
+  size_t ws_q, ws_total;
+};
+
+int sparse_validate(const sparse_attrs* a, const kvattn_tensor* in, int n_in, int total,
+                    const kvattn_tensor* out, int n_out, SparsePlan& P) {
+  if (!a || !in || !out) return fail(KVATTN_ERR_INVALID_ARG, "sparse_attention: null argument");
+  if (n_in != SPARSE_NUM_INPUTS || n_out != SPARSE_NUM_OUTPUTS)
+    return fail(KVATTN_ERR_INVALID_ARG, "sparse_attention: expected %d inputs and %d outputs", SPARSE_NUM_INPUTS, SPARSE_NUM_OUTPUTS);
+  const kvattn_tensor& q = in[SPARSE_IN_QUERY];
+  if (!has(q)) return fail(KVATTN_ERR_INVALID_ARG, "query is required");
+  if (q.dtype != KVATTN_DT_F16 && q.dtype != KVATTN_DT_F32)
+    return fail(KVATTN_ERR_UNSUPPORTED, "query dtype %d: only float16 and float32", q.dtype);
+  const int dt = q.dtype;
+  P.dt = dt;
+  CHECK(check(q, "query", dt, 3, {-1, -1, -1}));
+  P.B = (int)q.dims[0];
+  P.S = (int)q.dims[1];
+  P.N = a->num_heads;
+  P.kvN = a->kv_num_heads;
+  if (P.N <= 0 || P.kvN <= 0 || P.N % P.kvN)
+    return fail(KVATTN_ERR_INVALID_ARG, "kv_num_heads must divide num_heads");
+  const kvattn_tensor& k = in[SPARSE_IN_KEY];
+  const kvattn_tensor& v = in[SPARSE_IN_VALUE];
+  if (has(k) != has(v)) return fail(KVATTN_ERR_INVALID_ARG, "key and value go together");
+  P.packed_qkv = !has(k);
+  const int64_t width = q.dims[2];
+  const int64_t heads = P.packed_qkv ? (P.N + 2 * P.kvN) : P.N;
+  if (width % heads) return fail(KVATTN_ERR_INVALID_ARG, "query width %lld not divisible by %lld heads", (long long)width, (long long)heads);
+  P.H = (int)(width / heads);
+  if (P.H <= 0 || P.H % 8) return fail(KVATTN_ERR_INVALID_ARG, "head size %d must be a non-zero multiple of 8", P.H);
+  CHECK(check_head_size(P.H, "sparse_attention"));
+  P.HP = padded_head(P.H);
+  if (!P.packed_qkv) {
+    CHECK(check(k, "key", dt, 3, {P.B, P.S, (int64_t)P.kvN * P.H}));
+    CHECK(check(v, "value", dt, 3, {P.B, P.S, (int64_t)P.kvN * P.H}));
+  }
+  const kvattn_tensor& pk = in[SPARSE_IN_PAST_KEY];
+  const kvattn_tensor& pv = in[SPARSE_IN_PAST_VALUE];
+  if (!has(pk) || !has(pv)) return fail(KVATTN_ERR_INVALID_ARG, "past_key and past_value are required");
+  CHECK(check(pk, "past_key", dt, 4, {P.B, P.kvN, -1, P.H}));
+  CHECK(check(pv, "past_value", dt, 4, {P.B, P.kvN, pk.dims[2], P.H}));
+  P.cap = (int)pk.dims[2];
+  const int bs = a->sparse_block_size;
+  if (bs != 16 && bs != 32 && bs != 64 && bs != 128)
+    return fail(KVATTN_ERR_INVALID_ARG, "sparse_block_size %d must be 16, 32, 64 or 128", bs);
+  P.bs = bs;
+  const kvattn_tensor& rp = in[SPARSE_IN_BLOCK_ROW_INDICES];
+  const kvattn_tensor& cols = in[SPARSE_IN_BLOCK_COL_INDICES];
+  if (!has(rp) || !has(cols)) return fail(KVATTN_ERR_INVALID_ARG, "block_row_indices and block_col_indices are required");
+  CHECK(check(rp, "block_row_indices", KVATTN_DT_I32, 2, {-1, -1}));
+  CHECK(check(cols, "block_col_indices", KVATTN_DT_I32, 2, {rp.dims[0], -1}));
+  P.L = (int)rp.dims[0];
+  P.max_blocks = (int)rp.dims[1] - 1;
+  P.max_nnz = (int)cols.dims[1];
+  if (P.L < 1 || P.max_blocks < 1) return fail(KVATTN_ERR_INVALID_ARG, "block_row_indices must be (num_layout >= 1, max_blocks + 1 >= 2)");
+  const kvattn_tensor& kt = in[SPARSE_IN_KEY_TOTAL_SEQUENCE_LENGTHS];
+  if (!has(kt)) return fail(KVATTN_ERR_INVALID_ARG, "key_total_sequence_lengths is required");
+  CHECK(check(kt, "key_total_sequence_lengths", KVATTN_DT_I32, 1, {P.B}));
+  if (total < 1) return fail(KVATTN_ERR_INVALID_ARG, "total_sequence_length must be >= 1");
+  if (total > P.cap) return fail(KVATTN_ERR_INVALID_ARG, "total_sequence_length %d exceeds the cache capacity %d", total, P.cap);
+  if ((int64_t)total > (int64_t)P.max_blocks * bs)
+    return fail(KVATTN_ERR_INVALID_ARG, "total_sequence_length %d exceeds max_blocks * sparse_block_size", total);
+  if (total != P.S) return fail(KVATTN_ERR_UNSUPPORTED, "sparse token generation (total_sequence_length != sequence_length) is not implemented");
+  P.rotary = a->do_rotary == 1;
+  if (P.rotary) {
+    const kvattn_tensor& cs = in[SPARSE_IN_COS_CACHE];
+    const kvattn_tensor& sn = in[SPARSE_IN_SIN_CACHE];
+    if (!has(cs) || !has(sn)) return fail(KVATTN_ERR_INVALID_ARG, "do_rotary needs cos_cache and sin_cache");
+    CHECK(check(cs, "cos_cache", dt, 2, {-1, -1}));
+    CHECK(check(sn, "sin_cache", dt, 2, {cs.dims[0], cs.dims[1]}));
+    P.rot_half = (int)cs.dims[1];
+    if (P.rot_half < 8 || P.rot_half % 8 || 2 * P.rot_half > P.H)
+      return fail(KVATTN_ERR_INVALID_ARG, "rotary width %d must be a multiple of 8 and at most head_size/2", P.rot_half);
+    if (cs.dims[0] < total) return fail(KVATTN_ERR_INVALID_ARG, "cos_cache rows %lld < total_sequence_length %d", (long long)cs.dims[0], total);
+  }
+  const kvattn_tensor& o = out[SPARSE_OUT_OUTPUT];
+  if (!has(o)) return fail(KVATTN_ERR_INVALID_ARG, "output is required");
+  CHECK(check(o, "output", dt, 3, {P.B, P.S, (int64_t)P.N * P.H}));
+  if ((has(out[SPARSE_OUT_PRESENT_KEY]) && out[SPARSE_OUT_PRESENT_KEY].data != pk.data) ||
+      (has(out[SPARSE_OUT_PRESENT_VALUE]) && out[SPARSE_OUT_PRESENT_VALUE].data != pv.data))
+    return fail(KVATTN_ERR_INVALID_ARG, "the present caches are the past buffers updated in place");
+  P.ws_q = P.rotary ? align256((size_t)P.B * P.S * P.N * P.H * elem_size(dt)) : 0;
+  P.ws_total = P.ws_q;
+  return KVATTN_OK;
+}
+
+int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tensor* out,
+               const SparsePlan& P, void* ws, hipStream_t st) {
+  const DType dt = to_dtype(P.dt);
+  const int64_t width = in[SPARSE_IN_QUERY].dims[2];
+  PrepParams pp{};
+  pp.q = in[SPARSE_IN_QUERY].data;
+  pp.q_stride = width;
+  if (P.packed_qkv) {
+    pp.k = pp.v = in[SPARSE_IN_QUERY].data;
+    pp.k_stride = pp.v_stride = width;
+    pp.k_off = (int64_t)P.N * P.H;
+    pp.v_off = (int64_t)(P.N + P.kvN) * P.H;
+  } else {
+    pp.k = in[SPARSE_IN_KEY].data;
+    pp.v = in[SPARSE_IN_VALUE].data;
+    pp.k_stride = pp.v_stride = (int64_t)P.kvN * P.H;
+  }
+  pp.q_out = P.rotary ? ws : nullptr;
+  pp.kc = in[SPARSE_IN_PAST_KEY].data;
+  pp.vc = in[SPARSE_IN_PAST_VALUE].data;
+  if (P.rotary) {
+    pp.cos = in[SPARSE_IN_COS_CACHE].data;
+    pp.sin = in[SPARSE_IN_SIN_CACHE].data;
+    pp.rot_half = P.rot_half;
+    pp.rot_rows = (int)in[SPARSE_IN_COS_CACHE].dims[0];
+    pp.interleaved = a->rotary_interleaved == 1;
+  }
+  pp.lens = static_cast<const int32_t*>(in[SPARSE_IN_KEY_TOTAL_SEQUENCE_LENGTHS].data);
+  pp.pos_mode = 0;
+  pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
+  pp.write_q = P.rotary;
+  pp.write_kv = 1;
+  CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
+                   "prep launch"));
+
+  FlashParams f{};
+  if (P.rotary) {
+    f.q = ws;
+    f.q_s = (int64_t)P.N * P.H;
+  } else {
+    f.q = in[SPARSE_IN_QUERY].data;
+    f.q_s = width;
+  }
+  f.q_b = f.q_s * P.S;
+  f.q_h = P.H;
+  f.kc = in[SPARSE_IN_PAST_KEY].data;
+  f.vc = in[SPARSE_IN_PAST_VALUE].data;
+  f.k_j = P.H;
+  f.k_h = (int64_t)P.cap * P.H;
+  f.k_b = f.k_h * P.kvN;
+  f.out = out[SPARSE_OUT_OUTPUT].data;
+  f.o_s = (int64_t)P.N * P.H;
+  f.o_b = f.o_s * P.S;
+  f.o_h = P.H;
+  f.causal = 1;
+  f.window = -1;
+  f.rp = static_cast<const int32_t*>(in[SPARSE_IN_BLOCK_ROW_INDICES].data);
+  f.cols = static_cast<const int32_t*>(in[SPARSE_IN_BLOCK_COL_INDICES].data);
+  f.rp_stride = P.max_blocks + 1;
+  f.cols_stride = P.max_nnz;
+  f.num_layout = P.L;
+  f.block = P.bs;
+  f.max_blocks = P.max_blocks;
+  f.key_total = static_cast<const int32_t*>(in[SPARSE_IN_KEY_TOTAL_SEQUENCE_LENGTHS].data);
+  f.kv_rows = P.cap;
+  f.B = P.B; f.S = P.S; f.N = P.N; f.kvN = P.kvN; f.H = P.H;
+  f.scale = resolve_scale(a->scale, P.H);
+  f.heads_per_wg = 1;
+  f.rows_per_wg = P.bs >= 128 ? 128 : P.bs;
+  f.mode = kCsr;
+  const int gx = (P.S + f.rows_per_wg - 1) / f.rows_per_wg;
+  CHECK(hip_status(profiled(KVATTN_PROFILE_FLASH, st,
+                            [&] { return launch_flash(dt, P.HP, f, gx, P.N, P.B, st); }),
+                   "flash launch"));
+  return ok();
+}
+
+// ===========================================================================
+// PackedAttention
+// ===========================================================================
+constexpr int kPackedTile = 128;
+
+struct PackedPlan {
+  int T, D, C, B, S, N, H, HP, dt, qh, kh, vh;
+  size_t ws_y, ws_bounds, ws_work, ws_total;
+};
+
+int packed_validate(const packed_attrs* a, const kvattn_tensor* in, int n_in,
+                    const kvattn_tensor* out, int n_out, PackedPlan& P) {
+  if (!a || !in || !out) return fail(KVATTN_ERR_INVALID_ARG, "packed_attention: null argument");
+  if (n_in != PACKED_NUM_INPUTS || n_out != PACKED_NUM_OUTPUTS)
+    return fail(KVATTN_ERR_INVALID_ARG, "packed_attention: expected %d inputs and %d outputs", PACKED_NUM_INPUTS, PACKED_NUM_OUTPUTS);
+  const kvattn_tensor& x = in[PACKED_IN_INPUT];
+  if (!has(x)) return fail(KVATTN_ERR_INVALID_ARG, "input is required");
+  if (x.dtype != KVATTN_DT_F16 && x.dtype != KVATTN_DT_F32)
+    return fail(KVATTN_ERR_UNSUPPORTED, "input dtype %d: only float16 and float32", x.dtype);
+  const int dt = x.dtype;
+  P.dt = dt;
+  CHECK(check(x, "input", dt, 2, {-1, -1}));
+  P.T = (int)x.dims[0];
+  P.D = (int)x.dims[1];
+  const kvattn_tensor& w = in[PACKED_IN_WEIGHTS];
+  const kvattn_tensor& bias = in[PACKED_IN_BIAS];
+  if (!has(w) || !has(bias)) return fail(KVATTN_ERR_INVALID_ARG, "weights and bias are required");
+  CHECK(check(w, "weights", dt, 2, {P.D, -1}));
+  P.C = (int)w.dims[1];
+  CHECK(check(bias, "bias", dt, 1, {P.C}));
+  P.N = a->num_heads;
+  if (P.N <= 0) return fail(KVATTN_ERR_INVALID_ARG, "num_heads must be positive");
+  const int* hs = a->qkv_hidden_sizes;
+  if (hs[0] == 0 && hs[1] == 0 && hs[2] == 0) {
+    if (P.C % 3) return fail(KVATTN_ERR_INVALID_ARG, "bias length %d does not split in three", P.C);
+    P.qh = P.kh = P.vh = P.C / 3;
+  } else {
+    P.qh = hs[0]; P.kh = hs[1]; P.vh = hs[2];
+    if (P.qh <= 0 || P.kh <= 0 || P.vh <= 0 || P.qh + P.kh + P.vh != P.C)
+      return fail(KVATTN_ERR_INVALID_ARG, "qkv_hidden_sizes must be positive and sum to the weight columns");
+  }
+  if (P.qh != P.kh) return fail(KVATTN_ERR_INVALID_ARG, "q_hidden must equal k_hidden");
+  if (P.qh % P.N || P.vh % P.N) return fail(KVATTN_ERR_INVALID_ARG, "hidden sizes must be divisible by num_heads");
+  if (P.vh != P.qh) return fail(KVATTN_ERR_UNSUPPORTED, "a value head size different from the query head size is not implemented on the GPU");
+  P.H = P.qh / P.N;
+  CHECK(check_head_size(P.H, "packed_attention"));
+  P.HP = padded_head(P.H);
+  if (P.D % 8 || P.C % 8) return fail(KVATTN_ERR_UNSUPPORTED, "input hidden %d and weight columns %d must be multiples of 8", P.D, P.C);
+  const kvattn_tensor& to = in[PACKED_IN_TOKEN_OFFSET];
+  const kvattn_tensor& cum = in[PACKED_IN_CUMULATIVE_SEQUENCE_LENGTH];
+  if (!has(to) || !has(cum)) return fail(KVATTN_ERR_INVALID_ARG, "token_offset and cumulative_sequence_length are required");
+  CHECK(check(to, "token_offset", KVATTN_DT_I32, 2, {-1, -1}));
+  P.B = (int)to.dims[0];
+  P.S = (int)to.dims[1];
+  CHECK(check(cum, "cumulative_sequence_length", KVATTN_DT_I32, 1, {(int64_t)P.B + 1}));
+  if ((int64_t)P.T > (int64_t)P.B * P.S) return fail(KVATTN_ERR_INVALID_ARG, "token_count %d exceeds batch * sequence_length", P.T);
+  if (P.B < 1 || P.B > 4096) return fail(KVATTN_ERR_UNSUPPORTED, "batch %d outside 1..4096", P.B);
+  const kvattn_tensor& ab = in[PACKED_IN_ATTENTION_BIAS];
+  if (has(ab)) {
+    CHECK(check(ab, "attention_bias", dt, 4, {-1, -1, P.S, P.S}));
+    if (ab.dims[0] != 1 && ab.dims[0] != P.B) return fail(KVATTN_ERR_INVALID_ARG, "attention_bias dim 0 must be 1 or batch");
+    if (ab.dims[1] != 1 && ab.dims[1] != P.N) return fail(KVATTN_ERR_INVALID_ARG, "attention_bias dim 1 must be 1 or num_heads");
+  }
+  const kvattn_tensor& o = out[PACKED_OUT_OUTPUT];
+  if (!has(o)) return fail(KVATTN_ERR_INVALID_ARG, "output is required");
+  CHECK(check(o, "output", dt, 2, {P.T, P.vh}));
+  P.ws_y = align256((size_t)P.T * P.C * elem_size(dt));
+  P.ws_bounds = align256((size_t)2 * P.B * sizeof(int32_t));
+  const size_t items = (size_t)P.B * ((P.S + kPackedTile - 1) / kPackedTile);
+  P.ws_work = align256((1 + 2 * items) * sizeof(int32_t));
+  P.ws_total = P.ws_y + P.ws_bounds + P.ws_work;
+  return KVATTN_OK;
+}
+
+int packed_run(const packed_attrs* a, const kvattn_tensor* in, const kvattn_tensor* out,
+               const PackedPlan& P, void* ws, hipStream_t st) {
+  const DType dt = to_dtype(P.dt);
+  char* wsb = static_cast<char*>(ws);
+  void* y = wsb;
+  int32_t* bounds = reinterpret_cast<int32_t*>(wsb + P.ws_y);
+  int32_t* work = reinterpret_cast<int32_t*>(wsb + P.ws_y + P.ws_bounds);
+
+  PackedSchedParams sp{};
+  sp.cum = static_cast<const int32_t*>(in[PACKED_IN_CUMULATIVE_SEQUENCE_LENGTH].data);
+  sp.bounds = bounds;
+  sp.work = work;
+  sp.B = P.B; sp.T = P.T; sp.pad_seq = P.S; sp.tile = kPackedTile;
+  CHECK(hip_status(launch_packed_sched(sp, st), "schedule launch"));
+
+  GemmParams g{};
+  g.x = in[PACKED_IN_INPUT].data;
+  g.w = in[PACKED_IN_WEIGHTS].data;
+  g.bias = in[PACKED_IN_BIAS].data;
+  g.y = y;
+  g.M = P.T; g.K = P.D; g.Ncol = P.C;
+  CHECK(hip_status(profiled(KVATTN_PROFILE_GEMM, st, [&] { return launch_qkv_gemm(dt, g, st); }),
+                   "qkv gemm launch"));
+
+  FlashParams f{};
+  const size_t esz = elem_size(P.dt);
+  f.q = y;
+  f.q_s = P.C;
+  f.q_h = P.H;
+  f.kc = static_cast<char*>(y) + (size_t)P.qh * esz;
+  f.vc = static_cast<char*>(y) + (size_t)(P.qh + P.kh) * esz;
+  f.k_j = P.C;
+  f.k_h = P.H;
+  f.out = out[PACKED_OUT_OUTPUT].data;
+  f.o_s = P.vh;
+  f.o_h = P.H;
+  const kvattn_tensor& ab = in[PACKED_IN_ATTENTION_BIAS];
+  if (has(ab)) {
+    f.bias = ab.data;
+    f.bias_ss = P.S;
+    f.bias_cols = P.S;
+    f.bias_sh = ab.dims[1] > 1 ? (int64_t)P.S * P.S : 0;
+    f.bias_sb = ab.dims[0] > 1 ? (int64_t)ab.dims[1] * P.S * P.S : 0;
+    f.token_offset = static_cast<const int32_t*>(in[PACKED_IN_TOKEN_OFFSET].data);
+    f.pad_seq = P.S;
+  }
+  f.lens = bounds;
+  f.work = work;
+  f.kv_rows = P.T;
+  f.B = P.B; f.S = P.S; f.N = P.N; f.kvN = P.N; f.H = P.H;
+  f.scale = resolve_scale(a->scale, P.H);
+  f.heads_per_wg = 1;
+  f.rows_per_wg = kPackedTile;
+  f.mode = kVarlen;
+  const int gx = P.B * ((P.S + kPackedTile - 1) / kPackedTile);
+  CHECK(hip_status(profiled(KVATTN_PROFILE_FLASH, st,
+                            [&] { return launch_flash(dt, P.HP, f, gx, P.N, 1, st); }),
+                   "flash launch"));
+  return ok();
+}
+
+int check_ws(size_t need, void* ws, size_t bytes) {
+  if (need > 0 && (ws == nullptr || bytes < need))
+    return fail(KVATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? bytes : (size_t)0);
+  return KVATTN_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// exported symbols
+// ===========================================================================
+extern "C" {
+
+const char* kvattn_status_string(int32_t s) {
+  switch (s) {
+    case KVATTN_OK: return "ok";
+    case KVATTN_ERR_INVALID_ARG: return "invalid argument";
+    case KVATTN_ERR_UNSUPPORTED: return "unsupported";
+    case KVATTN_ERR_WORKSPACE: return "workspace too small";
+    case KVATTN_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvattn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kvattn_version(void) { return 100; }
+
+void kvattn_profile_events(void* start, void* stop, int32_t kind) {
+  g_prof_start = static_cast<hipEvent_t>(start);
+  g_prof_stop = static_cast<hipEvent_t>(stop);
+  g_prof_kind = (start && stop) ? kind : 0;
+}
+
+void gqa_attrs_default(gqa_attrs* a) {
+  if (!a) return;
+  std::memset(a, 0, sizeof(*a));
+  a->causal = 1;
+  a->local_window_size = -1;
+  a->qk_norm_epsilon = 1e-6f;
+  a->smooth_softmax = -1;
+}
+
+void dmmha_attrs_default(dmmha_attrs* a) {
+  if (!a) return;
+  std::memset(a, 0, sizeof(*a));
+  a->mask_filter_value = -10000.f;
+}
+
+void sparse_attrs_default(sparse_attrs* a) {
+  if (!a) return;
+  std::memset(a, 0, sizeof(*a));
+}
+
+void packed_attrs_default(packed_attrs* a) {
+  if (!a) return;
+  std::memset(a, 0, sizeof(*a));
+}
+
+int32_t gqa_attention_workspace_size(const gqa_attrs* a, const kvattn_tensor* in, int32_t n_in,
+                                     int32_t total, const kvattn_tensor* out, int32_t n_out,
+                                     size_t* bytes) {
+  if (!bytes) return fail(KVATTN_ERR_INVALID_ARG, "workspace_bytes is null");
+  GqaPlan P{};
+  CHECK(gqa_validate(a, in, n_in, total, out, n_out, P));
+  *bytes = P.ws_total;
+  return ok();
+}
+
+int32_t gqa_attention(const gqa_attrs* a, const kvattn_tensor* in, int32_t n_in, int32_t total,
+                      const kvattn_tensor* out, int32_t n_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  GqaPlan P{};
+  CHECK(gqa_validate(a, in, n_in, total, out, n_out, P));
+  CHECK(check_ws(P.ws_total, ws, ws_bytes));
+  if (P.B == 0 || P.S == 0) return ok();
+  return gqa_run(a, in, out, P, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t decode_mha_workspace_size(const dmmha_attrs* a, const kvattn_tensor* in, int32_t n_in,
+                                  const kvattn_tensor* out, int32_t n_out, size_t* bytes) {
+  if (!bytes) return fail(KVATTN_ERR_INVALID_ARG, "workspace_bytes is null");
+  DmmhaPlan P{};
+  CHECK(dmmha_validate(a, in, n_in, out, n_out, P));
+  *bytes = P.ws_total;
+  return ok();
+}
+
+int32_t decode_mha(const dmmha_attrs* a, const kvattn_tensor* in, int32_t n_in,
+                   const kvattn_tensor* out, int32_t n_out, void* ws, size_t ws_bytes,
+                   void* stream) {
+  DmmhaPlan P{};
+  CHECK(dmmha_validate(a, in, n_in, out, n_out, P));
+  CHECK(check_ws(P.ws_total, ws, ws_bytes));
+  if (P.B == 0) return ok();
+  return dmmha_run(a, in, out, P, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t sparse_attention_workspace_size(const sparse_attrs* a, const kvattn_tensor* in,
+                                        int32_t n_in, int32_t total, const kvattn_tensor* out,
+                                        int32_t n_out, size_t* bytes) {
+  if (!bytes) return fail(KVATTN_ERR_INVALID_ARG, "workspace_bytes is null");
+  SparsePlan P{};
+  CHECK(sparse_validate(a, in, n_in, total, out, n_out, P));
+  *bytes = P.ws_total;
+  return ok();
+}
+
+int32_t sparse_attention(const sparse_attrs* a, const kvattn_tensor* in, int32_t n_in,
+                         int32_t total, const kvattn_tensor* out, int32_t n_out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  SparsePlan P{};
+  CHECK(sparse_validate(a, in, n_in, total, out, n_out, P));
+  CHECK(check_ws(P.ws_total, ws, ws_bytes));
+  if (P.B == 0 || P.S == 0) return ok();
+  return sparse_run(a, in, out, P, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t packed_attention_workspace_size(const packed_attrs* a, const kvattn_tensor* in,
+                                        int32_t n_in, const kvattn_tensor* out, int32_t n_out,
+                                        size_t* bytes) {
+  if (!bytes) return fail(KVATTN_ERR_INVALID_ARG, "workspace_bytes is null");
+  PackedPlan P{};
+  CHECK(packed_validate(a, in, n_in, out, n_out, P));
+  *bytes = P.ws_total;
+  return ok();
+}
+
+int32_t packed_attention(const packed_attrs* a, const kvattn_tensor* in, int32_t n_in,
+                         const kvattn_tensor* out, int32_t n_out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  PackedPlan P{};
+  CHECK(packed_validate(a, in, n_in, out, n_out, P));
+  CHECK(check_ws(P.ws_total, ws, ws_bytes));
+  if (P.T == 0) return ok();
+  return packed_run(a, in, out, P, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t kvattn_packed_schedule(const int32_t* cum, int32_t batch, int32_t token_count,
+                               int32_t padded_sequence_length, int32_t tile_rows,
+                               int32_t* bounds, int32_t* work, int32_t* token_sequence,
+                               int32_t* token_position, void* stream) {
+  if (!cum || !bounds || !work || batch < 1 || batch > 4096 || token_count < 0 ||
+      padded_sequence_length < 1 || tile_rows < 1)
+    return fail(KVATTN_ERR_INVALID_ARG, "kvattn_packed_schedule: invalid argument");
+  if ((token_sequence == nullptr) != (token_position == nullptr))
+    return fail(KVATTN_ERR_INVALID_ARG, "token_sequence and token_position go together");
+  PackedSchedParams sp{};
+  sp.cum = cum;
+  sp.bounds = bounds;
+  sp.work = work;
+  sp.tok_seq = token_sequence;
+  sp.tok_pos = token_position;
+  sp.B = batch; sp.T = token_count; sp.pad_seq = padded_sequence_length; sp.tile = tile_rows;
+  CHECK(hip_status(launch_packed_sched(sp, static_cast<hipStream_t>(stream)), "schedule launch"));
+  return ok();
+}
+
+}  // extern "C"

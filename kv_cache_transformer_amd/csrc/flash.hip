@@ -1,0 +1,483 @@
+// K2: tiled online-softmax attention on MFMA (prefill / prompt paths).
+//
+// One workgroup owns a block of query rows for one or more query heads that
+// share a kv head; every wave owns 32 query rows of one head.  Key/value
+// tiles of BN rows are staged in LDS (double-buffered, filled from registers
+// loaded one tile ahead) and shared by all waves of the workgroup.
+//
+//   S^T[keys][32 queries] = K_tile . Q^T        (f16: 32x32x16, f32: 32x32x2)
+//   O^T[H][32 queries]   += V_tile^T . P^T
+//
+// With the scores transposed, each lane holds one query's scores, so the
+// running max/sum (online softmax) needs one cross-lane step (lane ^ 32) per
+// tile, and P^T leaves the score MFMA already in the operand layout of the
+// PV MFMA (the contraction order over keys is permuted to match).  For f16
+// the V^T operand is read from the row-major LDS tile with ds_read_b64_tr_b16.
+//
+// Modes (one kernel template):
+//   dense  - GroupQueryAttention: causal bound right-aligned to the live
+//            length (seqlens_k), optional local window, softcap, additive bias,
+//            head sink / smooth softmax, or bidirectional without a past
+//            (GroupQueryAttention page: Inputs and Attributes tables;
+//            Implementation variants on causal tile skipping).
+//   csr    - SparseAttention: the key tiles of a query block come from its CSR
+//            row (layout = head mod num_layout), causal inside the diagonal
+//            block (SparseAttention page: Description and Inputs table).
+//   varlen - PackedAttention: each token attends the keys of its own
+//            sequence [cum[b], cum[b+1]); work items come from a device work
+//            list (PackedAttention page: Description and Inputs table).
+#include "device_common.hpp"
+#include "kvattn_internal.hpp"
+
+namespace kvattn {
+namespace {
+
+typedef __fp16 lds_half4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+__device__ __forceinline__ half4v lds_read_tr16(const f16* p) {
+  auto r = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (__attribute__((address_space(3))) lds_half4*)(p));
+  half4v o;
+  o[0] = (f16)r[0];
+  o[1] = (f16)r[1];
+  o[2] = (f16)r[2];
+  o[3] = (f16)r[3];
+  return o;
+}
+
+template <typename T, int HP> struct FlashMma;
+
+// ------------------------------- f16 ----------------------------------------
+template <int HP> struct FlashMma<f16, HP> {
+  static constexpr int KS = HP + 8;    // K tile row stride (elements)
+  static constexpr int VS = HP + 16;   // V tile row stride (elements)
+  static constexpr int NS = HP / 16;   // 16-dim k-steps of the score MFMA
+  static constexpr int ND = HP / 32;   // 32-dim output blocks
+  static constexpr int CH = 8;         // elements per 16-byte chunk
+  half8v qf[NS];
+  float16v o[ND];
+
+  __device__ void init() {
+#pragma unroll
+    for (int i = 0; i < ND; ++i) o[i] = float16v{};
+  }
+  // lane l: Q[q = l%32][16s + 8(l/32) + i]
+  __device__ void load_q(const f16* qrow, int H, int lane) {
+    const int hi = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      int d = 16 * s + 8 * hi;
+      qf[s] = (d < H) ? load_half8(qrow + d) : half8v{};
+    }
+  }
+  __device__ float16v qk_block(const f16* Kt, int kb, int lane) const {
+    float16v acc = {};
+    const f16* kr = Kt + (kb + (lane & 31)) * KS + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      half8v a = *reinterpret_cast<const half8v*>(kr + 16 * s);
+      acc = mfma32x32x16(a, qf[s], acc);
+    }
+    return acc;
+  }
+  // p: this lane's 16 probabilities of the 32-key block at kb
+  __device__ void pv_block(const f16* Vt, int kb, const float (&p)[16], int lane) {
+    const int G = lane >> 4, t = lane & 15;
+    const int c = t & 3, ir = t >> 2;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      half8v pb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[i] = (f16)p[8 * hf + i];
+      const int row = kb + 16 * hf + 4 * (G >> 1) + ir;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const f16* a1 = Vt + row * VS + 32 * db + 16 * (G & 1) + 4 * c;
+        half4v lo = lds_read_tr16(a1);
+        half4v hi = lds_read_tr16(a1 + 8 * VS);
+        half8v a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[db] = mfma32x32x16(a, pb, o[db]);
+      }
+    }
+  }
+};
+
+// ------------------------------- f32 ----------------------------------------
+template <int HP> struct FlashMma<float, HP> {
+  static constexpr int KS = HP + 4;
+  static constexpr int VS = HP + 4;
+  static constexpr int NS = HP / 2;    // 2-dim k-steps of the score MFMA
+  static constexpr int ND = HP / 32;
+  static constexpr int CH = 4;
+  float qf[NS];
+  float16v o[ND];
+
+  __device__ void init() {
+#pragma unroll
+    for (int i = 0; i < ND; ++i) o[i] = float16v{};
+  }
+  // lane l: Q[q = l%32][2s + l/32]
+  __device__ void load_q(const float* qrow, int H, int lane) {
+    const int hi = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      int d = 2 * s + hi;
+      qf[s] = (d < H) ? qrow[d] : 0.f;
+    }
+  }
+  __device__ float16v qk_block(const float* Kt, int kb, int lane) const {
+    float16v acc = {};
+    const float* kr = Kt + (kb + (lane & 31)) * KS + (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc = mfma32x32x2f32(kr[2 * s], qf[s], acc);
+    return acc;
+  }
+  __device__ void pv_block(const float* Vt, int kb, const float (&p)[16], int lane) {
+    const int hi = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int key = kb + 8 * (t >> 2) + 4 * hi + (t & 3);
+      const float* vr = Vt + key * VS + col;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) o[db] = mfma32x32x2f32(vr[32 * db], p[t], o[db]);
+    }
+  }
+};
+
+// Tile schedule of one workgroup: tile t covers keys [start, start + BN) of
+// which [start, lim) may be visible.
+struct TileRange {
+  int start, lim;
+};
+
+template <typename T, int HP, int BN, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void flash_kernel(FlashParams p) {
+  using Mma = FlashMma<T, HP>;
+  constexpr int KS = Mma::KS, VS = Mma::VS, CH = Mma::CH;
+  constexpr int TILE = BN * (KS + VS);
+  constexpr int CPR = HP / CH;  // 16-byte chunks per row
+  constexpr int nthreads = 64 * NW;
+  // chunks (K and V) each thread moves per tile; prefetching a whole tile into
+  // registers only when that stays small
+  constexpr int CPT = (2 * BN * CPR + nthreads - 1) / nthreads;
+  constexpr bool kPrefetch = CPT <= 16;
+  __shared__ __attribute__((aligned(16))) T lds[2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = p.H;
+  const int g = p.N / p.kvN;
+  const int HW = p.heads_per_wg;
+
+  // ---- workgroup -> (sample, kv head, heads, rows) --------------------------
+  int b, kvh, h, r0, nrows;  // nrows: valid query rows of this workgroup's row block
+  int64_t row_base = 0;      // varlen: first packed token of the sequence
+  if (MODE == kVarlen) {
+    const int count = p.work[0];
+    if ((int)blockIdx.x >= count) return;
+    b = p.work[1 + 2 * blockIdx.x];
+    const int tile = p.work[2 + 2 * blockIdx.x];
+    h = blockIdx.y;
+    kvh = h / g;
+    r0 = tile * p.rows_per_wg;
+    row_base = p.lens[2 * b];
+    nrows = p.lens[2 * b + 1] - p.lens[2 * b];
+  } else {
+    b = blockIdx.z;
+    const int groups = g / HW;
+    kvh = blockIdx.y / groups;
+    h = kvh * g + (blockIdx.y % groups) * HW + (wave % HW);
+    r0 = blockIdx.x * p.rows_per_wg;
+    nrows = p.S;
+  }
+  const int wrow0 = r0 + 32 * (MODE == kDense ? wave / HW : wave);  // this wave's first row
+  const int wg_rows_end = min(r0 + p.rows_per_wg, nrows);
+  const bool wave_rows = wrow0 < wg_rows_end;
+
+  // ---- key range ------------------------------------------------------------
+  int n_keys, past = 0;
+  if (MODE == kDense) {
+    n_keys = p.causal ? p.lens[b] + 1 : p.S;
+    if (p.has_past) past = n_keys - p.S;
+  } else if (MODE == kCsr) {
+    n_keys = p.key_total[b];
+    if (p.has_past) past = n_keys - p.S;
+  } else {
+    n_keys = nrows;
+  }
+  const int pmin = past + r0, pmax = past + wg_rows_end - 1;
+  int k_lo = 0, k_hi = n_keys;
+  if (MODE == kDense && p.causal) {
+    k_hi = min(n_keys, pmax + 1);
+    if (p.window >= 0) k_lo = max(0, pmin - p.window);
+  }
+  int n_tiles, csr_lo = 0, layout = 0, tiles_per_block = 1;
+  if (MODE == kCsr) {
+    layout = h % p.num_layout;
+    const int rb = pmin / p.block;
+    csr_lo = max(p.rp[layout * p.rp_stride + rb], 0);
+    const int csr_hi = min(p.rp[layout * p.rp_stride + rb + 1], (int)p.cols_stride);
+    tiles_per_block = p.block > BN ? p.block / BN : 1;
+    n_tiles = max(0, csr_hi - csr_lo) * tiles_per_block;
+  } else {
+    n_tiles = (k_hi > k_lo) ? (k_hi - k_lo + BN - 1) / BN : 0;
+  }
+  auto tile_range = [&](int t) -> TileRange {
+    TileRange r;
+    if (MODE == kCsr) {
+      int e = csr_lo + t / tiles_per_block;
+      int c = min(max(p.cols[layout * p.cols_stride + e], 0), p.max_blocks - 1);
+      r.start = c * p.block + (t % tiles_per_block) * BN;
+      int blk_end = (c + 1) * p.block;
+      r.lim = min(min(r.start + BN, blk_end), min(n_keys, pmax + 1));
+    } else {
+      r.start = k_lo + t * BN;
+      r.lim = min(r.start + BN, k_hi);
+    }
+    return r;
+  };
+
+  // ---- global addresses -------------------------------------------------------
+  const T* qg = static_cast<const T*>(p.q);
+  const T* kg = static_cast<const T*>(p.kc);
+  const T* vg = static_cast<const T*>(p.vc);
+  int64_t kv_base;
+  if (MODE == kVarlen) kv_base = row_base * p.k_j + (int64_t)kvh * p.k_h;
+  else kv_base = (int64_t)b * p.k_b + (int64_t)kvh * p.k_h;
+
+  // ---- queries of this wave (registers) ---------------------------------------
+  Mma mma;
+  mma.init();
+  const int qrow = wrow0 + (lane & 31);
+  const bool row_ok = wave_rows && qrow < wg_rows_end;
+  {
+    const int rr = min(qrow, nrows - 1);
+    const T* qp = (MODE == kVarlen)
+                      ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
+                      : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
+    mma.load_q(qp, H, lane);
+  }
+  const int pos = past + qrow;  // absolute position of this lane's query
+
+  // ---- tile loader: 16-byte chunks (K rows then V rows) -> LDS ----------------
+  auto chunk_src = [&](const TileRange& r, int idx, bool& zero) -> const T* {
+    const bool isv = idx >= BN * CPR;
+    const int ci = isv ? idx - BN * CPR : idx;
+    const int row = ci / CPR, d = (ci % CPR) * CH;
+    const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1);
+    const int grow = min(r.start + row, last);
+    zero = d >= H;
+    return (isv ? vg : kg) + kv_base + (int64_t)grow * p.k_j + d;
+  };
+  auto chunk_dst = [&](int buf, int idx) -> T* {
+    T* base = lds + buf * TILE;
+    const bool isv = idx >= BN * CPR;
+    const int ci = isv ? idx - BN * CPR : idx;
+    const int row = ci / CPR, d = (ci % CPR) * CH;
+    return isv ? base + BN * KS + row * VS + d : base + row * KS + d;
+  };
+  uint4v stage[kPrefetch ? CPT : 1];
+  auto load_tile = [&](int t) {
+    const TileRange r = tile_range(t);
+#pragma unroll
+    for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
+      const int idx = tid + u * nthreads;
+      if (idx < 2 * BN * CPR) {
+        bool zero;
+        const T* src = chunk_src(r, idx, zero);
+        stage[u] = zero ? uint4v{0u, 0u, 0u, 0u} : *reinterpret_cast<const uint4v*>(src);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
+      const int idx = tid + u * nthreads;
+      if (idx < 2 * BN * CPR) *reinterpret_cast<uint4v*>(chunk_dst(buf, idx)) = stage[u];
+    }
+  };
+  // direct copy without holding a whole tile in registers (large tiles per thread)
+  auto copy_tile = [&](int t, int buf) {
+    const TileRange r = tile_range(t);
+    for (int idx = tid; idx < 2 * BN * CPR; idx += nthreads) {
+      bool zero;
+      const T* src = chunk_src(r, idx, zero);
+      uint4v v = zero ? uint4v{0u, 0u, 0u, 0u} : *reinterpret_cast<const uint4v*>(src);
+      *reinterpret_cast<uint4v*>(chunk_dst(buf, idx)) = v;
+    }
+  };
+
+  const float scale = p.scale;
+  const float cap = p.softcap, inv_cap = cap > 0.f ? 1.f / cap : 0.f;
+  const T* bias = static_cast<const T*>(p.bias);
+  int64_t bias_row = 0;
+  int pad_q = 0;
+  if (bias != nullptr) {
+    if (MODE == kVarlen) {
+      pad_q = p.token_offset[row_base + min(qrow, nrows - 1)] - b * p.pad_seq;
+      pad_q = min(max(pad_q, 0), p.pad_seq - 1);
+      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)pad_q * p.bias_ss;
+    } else {
+      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)min(qrow, nrows - 1) * p.bias_ss;
+    }
+  }
+
+  float m = kNegInf, lsum = 0.f;
+  if (kPrefetch && n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (kPrefetch) {
+      if (t + 1 < n_tiles) load_tile(t + 1);
+    } else {
+      // buffer buf was last read two tiles ago; every wave has passed the
+      // barrier that followed that tile
+      copy_tile(t, buf);
+      __syncthreads();
+    }
+    const TileRange r = tile_range(t);
+    if (wave_rows) {
+      const T* Kt = lds + buf * TILE;
+      const T* Vt = Kt + BN * KS;
+      float x[BN / 32][16];
+      float tmax = kNegInf;
+      float16v sacc[BN / 32];
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk) sacc[blk] = mma.qk_block(Kt, 32 * blk, lane);
+      mfma_result_fence();
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk) {
+        const float16v s = sacc[blk];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          bool ok = row_ok && key < r.lim;
+          if (MODE == kDense) {
+            if (p.causal) {
+              ok = ok && key <= pos;
+              if (p.window >= 0) ok = ok && key >= pos - p.window;
+            }
+          } else if (MODE == kCsr) {
+            ok = ok && key <= pos;
+          }
+          float v = s[i] * scale;
+          if (cap > 0.f) v = softcap_apply(v, cap, inv_cap);
+          if (bias != nullptr && ok) {
+            if (MODE == kVarlen) {
+              int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
+              pad_k = min(max(pad_k, 0), p.pad_seq - 1);
+              v += to_f32(bias[bias_row + pad_k]);
+            } else if (key < p.bias_cols) {
+              v += to_f32(bias[bias_row + key]);
+            }
+          }
+          v = ok ? v * kLog2e : kNegInf;
+          x[blk][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      }
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      const float mnew = fmaxf(m, tmax);
+      const float muse = (mnew == kNegInf) ? 0.f : mnew;
+      const float alpha = fast_exp2(m - muse);
+      m = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float e = fast_exp2(x[blk][i] - muse);
+          x[blk][i] = e;
+          psum += e;
+        }
+      lsum = lsum * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
+    }
+    if (kPrefetch) {
+      if (t + 1 < n_tiles) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- normalise and store -----------------------------------------------------
+  mfma_result_fence();
+  if (!wave_rows) return;
+  lsum += shfl_xor(lsum, 32);
+  bool has_sink = false;
+  float sg = 0.f;
+  if (p.sink != nullptr) {
+    has_sink = true;
+    sg = kLog2e * to_f32(static_cast<const T*>(p.sink)[h]);
+  } else if (p.smooth == 1) {
+    has_sink = true;
+  }
+  float inv;
+  if (lsum == 0.f) {
+    inv = 0.f;
+  } else if (has_sink) {
+    const float M2 = fmaxf(m, sg);
+    const float den = lsum * fast_exp2(m - M2) + fast_exp2(sg - M2);
+    inv = fast_exp2(m - M2) / den;
+  } else {
+    inv = 1.f / lsum;
+  }
+  if (!row_ok) return;
+  T* og = static_cast<T*>(p.out);
+  T* orow = (MODE == kVarlen) ? og + (row_base + qrow) * p.o_s + (int64_t)h * p.o_h
+                              : og + (int64_t)b * p.o_b + (int64_t)qrow * p.o_s + (int64_t)h * p.o_h;
+#pragma unroll
+  for (int db = 0; db < Mma::ND; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 32 * db + 8 * gq + 4 * (lane >> 5);
+      if (d < H) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) orow[d + i] = from_f32<T>(mma.o[db][4 * gq + i] * inv);
+      }
+    }
+}
+
+template <typename T, int HP, int BN, int MODE>
+hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
+  if (nw == 4) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 4>), grid, dim3(256), 0, s, p);
+  else if (nw == 2) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 2>), grid, dim3(128), 0, s, p);
+  else hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 1>), grid, dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int HP, int BN>
+hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
+  switch (p.mode) {
+    case kDense:
+      return launch_mode<T, HP, BN, kDense>(p, grid, 4, s);
+    case kCsr: {
+      int nw = (p.rows_per_wg + 31) / 32;
+      return launch_mode<T, HP, BN, kCsr>(p, grid, nw >= 4 ? 4 : (nw == 2 ? 2 : 1), s);
+    }
+    default:
+      return launch_mode<T, HP, BN, kVarlen>(p, grid, 4, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_flash(DType dt, int hp, const FlashParams& p, int gx, int gy, int gz,
+                        hipStream_t s) {
+  dim3 grid(gx, gy, gz);
+  if (gx == 0 || gy == 0 || gz == 0) return hipSuccess;
+  if (dt == DType::F16) {
+    if (hp == 64) return launch_flash_t<f16, 64, 64>(p, grid, s);
+    if (hp == 128) return launch_flash_t<f16, 128, 64>(p, grid, s);
+    return launch_flash_t<f16, 256, 64>(p, grid, s);
+  }
+  if (hp == 64) return launch_flash_t<float, 64, 32>(p, grid, s);
+  if (hp == 128) return launch_flash_t<float, 128, 32>(p, grid, s);
+  return launch_flash_t<float, 256, 32>(p, grid, s);
+}
+
+}  // namespace kvattn

@@ -1,0 +1,157 @@
+// Internal interface between the C ABI (api.cpp) and the HIP kernels.
+// Parameter blocks are plain structs passed by value to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvattn {
+
+enum class DType : int { F32 = 1, F16 = 2 };
+
+// ---------------------------------------------------------------------------
+// K1 prep: per new token, optional per-head RMSNorm and rotary on the query
+// heads (written to a query workspace) and on the key heads (written with the
+// values into the cache rows at the token's absolute position).
+// ---------------------------------------------------------------------------
+struct PrepParams {
+  const void* q;            // (B, S, q_stride) storage T; heads at q_off + h*H
+  const void* k;            // (B, S, k_stride)
+  const void* v;            // (B, S, v_stride)
+  int64_t q_stride, k_stride, v_stride;   // elements per token row
+  int64_t q_off, k_off, v_off;            // element offset of head 0 in a row
+  void* q_out;              // (B, S, N*H) transformed queries, or null
+  void* kc;                 // key cache (B, kvN, cap, H)
+  void* vc;                 // value cache
+  const void* q_norm;       // (H) or null
+  const void* k_norm;       // (H) or null
+  float eps;
+  const void* cos;          // (rot_rows, rot_half) or null
+  const void* sin;
+  int rot_half;             // rotary pairs per head (r/2)
+  int rot_rows;             // rows of the cos/sin tables
+  int interleaved;          // 1: pairs (2i, 2i+1); 0: pairs (i, i + r/2)
+  const int32_t* lens;      // per-batch lengths (device)
+  int pos_mode;             // 0: none (past 0); 1: past = lens[b] + 1 - S; 2: past = lens[b] - S
+  int B, S, N, kvN, H, cap;
+  int write_q;              // 1: write transformed queries
+  int write_kv;             // 1: append k, v into the caches
+};
+
+// Copy the live past rows [0, past_b) into a separate present buffer.
+struct CopyPastParams {
+  const void* pk; const void* pv;   // (B, kvN, past_seq, H)
+  void* ck; void* cv;               // (B, kvN, cap, H)
+  const int32_t* lens;              // seqlens_k
+  int B, kvN, H, S, past_seq, cap;
+};
+
+// ---------------------------------------------------------------------------
+// K3 decode: one query token per sample against a BNSH cache, split over the
+// key axis with a log-sum-exp combine.
+// ---------------------------------------------------------------------------
+struct DecodeParams {
+  const void* q;            // (B, N*H)
+  const void* k_new;        // (B, kvN*H) token key row, or null (no append)
+  const void* v_new;
+  void* kc;                 // (B, kvN, cap, H)
+  void* vc;
+  const void* q_norm;       // (H) or null
+  const void* k_norm;
+  float eps;
+  const void* cos;          // (rows, H/2) NeoX rotary tables or null
+  const void* sin;
+  int rot_rows;             // rows of the rotary tables
+  const void* bias;         // additive score bias or null: bias[b*bias_sb + h*bias_sh + j]
+  int64_t bias_sb, bias_sh;
+  int bias_cols;            // columns of the bias (keys beyond get no bias)
+  const int32_t* mask;      // (B, mask_cols) int32 or null; 0 adds mask_filter
+  int mask_cols;
+  float mask_filter;
+  const void* sink;         // (N) or null
+  int smooth;               // 1: zero sink when no sink tensor
+  const int32_t* lens;      // device lengths
+  int len_mode;             // 0: n_b = lens[b] + 1; 1: n_b = lens[0] + 1; 2: n_b = host_n
+  int host_n;
+  int window;               // >= 0: keys j >= (n_b - 1) - window
+  void* out;                // (B, N*H)
+  void* qk;                 // (B, N, 1, host_n) scores after mask, or null
+  float* part;              // (B, N, max_chunks, HP + 2) partial results
+  int B, N, kvN, H, cap;
+  float scale, softcap;
+  int chunk, max_chunks, head_groups;
+};
+
+// ---------------------------------------------------------------------------
+// K2 flash attention (dense causal/window, CSR block-sparse, packed varlen).
+// ---------------------------------------------------------------------------
+enum FlashMode : int { kDense = 0, kCsr = 1, kVarlen = 2 };
+
+struct FlashParams {
+  const void* q;            // queries, element (b, s, h, d) at q_b*b + q_s*s + q_h*h + d
+  int64_t q_b, q_s, q_h;
+  const void* kc;           // keys, element (b, kvh, j, d) at k_b*b + k_h*kvh + k_j*j + d
+  const void* vc;
+  int64_t k_b, k_h, k_j;
+  void* out;                // element (b, s, h, d) at o_b*b + o_s*s + o_h*h + d
+  int64_t o_b, o_s, o_h;
+  const void* bias;         // dense: bias[b*sb + h*sh + s*ss + j]; varlen: padded coords
+  int64_t bias_sb, bias_sh, bias_ss;
+  int bias_cols;            // key columns of the bias (keys beyond get no bias)
+  const void* sink;         // (N) or null
+  int smooth;
+  const int32_t* lens;      // dense: seqlens_k (n_b = lens[b] + 1); varlen: per-sequence [start, end)
+  int has_past;             // dense: 1 => past_b = n_b - S
+  int causal;
+  int window;
+  // CSR
+  const int32_t* rp; const int32_t* cols; int64_t rp_stride, cols_stride;
+  int num_layout, block;    // block = sparse block size
+  int max_blocks;           // column entries are clamped into [0, max_blocks)
+  const int32_t* key_total; // sparse: per-batch key totals
+  // varlen
+  const int32_t* token_offset; int pad_seq;
+  const int32_t* work;      // varlen work list: work[0] = count, then (b, tile) pairs
+  int kv_rows;              // rows addressable in the K/V buffers (per sample / total)
+  int B, S, N, kvN, H;
+  float scale, softcap;
+  int rows_per_wg;          // query rows per workgroup
+  int heads_per_wg;         // query heads per workgroup (GQA grouping)
+  int mode;
+};
+
+// ---------------------------------------------------------------------------
+// K5 packed: schedule + QKV projection GEMM.
+// ---------------------------------------------------------------------------
+struct PackedSchedParams {
+  const int32_t* cum;       // (B + 1) as given
+  int32_t* bounds;          // (B, 2) sanitised [start, end) per sequence
+  int32_t* work;            // work[0] = count, then (b, tile) pairs, longest sequences first
+  int32_t* tok_seq;         // optional (T): owning sequence per packed token
+  int32_t* tok_pos;         // optional (T): position inside the sequence
+  int B, T, pad_seq, tile;  // tile = query rows per attention workgroup
+};
+
+struct GemmParams {
+  const void* x;            // (M, K) row-major
+  const void* w;            // (K, Ncol) row-major
+  const void* bias;         // (Ncol)
+  void* y;                  // (M, Ncol) row-major
+  int M, K, Ncol;
+};
+
+// Launchers (defined in the .hip sources).  Each returns hipSuccess or the
+// launch error.
+hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s);
+hipError_t launch_copy_past(DType dt, const CopyPastParams& p, hipStream_t s);
+hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s);
+hipError_t launch_flash(DType dt, int hp, const FlashParams& p, int grid_x, int grid_y,
+                        int grid_z, hipStream_t s);
+hipError_t launch_packed_sched(const PackedSchedParams& p, hipStream_t s);
+hipError_t launch_qkv_gemm(DType dt, const GemmParams& p, hipStream_t s);
+
+// Head-size padding used by the kernels (multiple of 64, <= 256).
+inline int padded_head(int H) { return H <= 64 ? 64 : (H <= 128 ? 128 : 256); }
+
+}  // namespace kvattn

@@ -1,0 +1,271 @@
+"""The C-ABI library loads, exports every symbol include/kvattn.h declares,
+fills the pages' attribute defaults and rejects malformed calls on the host
+before any launch.  CPU only: no call here reaches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_transformer_amd import _binding as kb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvattn.h")
+
+FAKE = 0x10000  # a non-null pointer value; validation never dereferences it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kb.library_path):
+        pytest.fail("libkvattn.so is not built (python -m kv_cache_transformer_amd.build)")
+    return kb.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"gqa_attention", "decode_mha", "sparse_attention", "packed_attention"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kvattn_version() >= 100
+    assert lib.kvattn_status_string(0) == b"ok"
+    assert lib.kvattn_status_string(-2) == b"unsupported"
+
+
+def test_attribute_defaults(lib):
+    a = kb.GqaAttrs()
+    a.causal = 7
+    lib.gqa_attrs_default(ctypes.byref(a))
+    assert (a.causal, a.do_rotary, a.local_window_size, a.smooth_softmax) == (1, 0, -1, -1)
+    assert abs(a.qk_norm_epsilon - 1e-6) < 1e-12 and a.scale == 0 and a.softcap == 0
+    d = kb.DmmhaAttrs()
+    lib.dmmha_attrs_default(ctypes.byref(d))
+    assert d.mask_filter_value == -10000.0 and d.scale == 0 and d.output_qk == 0
+    s = kb.SparseAttrs()
+    lib.sparse_attrs_default(ctypes.byref(s))
+    assert s.do_rotary == 0 and s.rotary_interleaved == 0
+    p = kb.PackedAttrs()
+    lib.packed_attrs_default(ctypes.byref(p))
+    assert list(p.qkv_hidden_sizes) == [0, 0, 0]
+
+
+def T(dtype, *dims, ptr=FAKE):
+    t = kb.Tensor()
+    t.data = ptr
+    t.dtype = dtype
+    t.rank = len(dims)
+    for i, d in enumerate(dims):
+        t.dims[i] = d
+    return t
+
+
+F16, F32, I32 = kb.DT_F16, kb.DT_F32, kb.DT_I32
+
+
+def gqa_args(B=2, S=16, N=8, kvN=2, H=64, past=None, cap=64, dt=F16, slots=None):
+    ins = [kb.Tensor() for _ in range(kb.GQA_NUM_INPUTS)]
+    ins[0] = T(dt, B, S, N * H)
+    ins[1] = T(dt, B, S, kvN * H)
+    ins[2] = T(dt, B, S, kvN * H)
+    if past:
+        ins[3] = T(dt, B, kvN, cap, H, ptr=0x20000)
+        ins[4] = T(dt, B, kvN, cap, H, ptr=0x30000)
+    ins[5] = T(I32, B)
+    for k, v in (slots or {}).items():
+        ins[k] = v
+    outs = [T(dt, B, S, N * H), T(dt, B, kvN, cap, H, ptr=0x20000 if past == "shared" else 0x40000),
+            T(dt, B, kvN, cap, H, ptr=0x30000 if past == "shared" else 0x50000)]
+    return ins, outs
+
+
+def gqa_call(lib, ins, outs, total=16, attrs=None, N=8, kvN=2, **akw):
+    a = kb.GqaAttrs()
+    lib.gqa_attrs_default(ctypes.byref(a))
+    a.num_heads, a.kv_num_heads = N, kvN
+    for k, v in akw.items():
+        setattr(a, k, v)
+    size = ctypes.c_size_t(0)
+    rc = lib.gqa_attention_workspace_size(ctypes.byref(a), kb._array(ins), len(ins), total,
+                                          kb._array(outs), len(outs), ctypes.byref(size))
+    return rc, size.value, lib.kvattn_last_error().decode()
+
+
+def test_gqa_valid_shapes_give_workspace(lib):
+    ins, outs = gqa_args()
+    rc, size, _ = gqa_call(lib, ins, outs)
+    assert rc == 0 and size == 0
+    ins, outs = gqa_args(past="shared", S=1, cap=4096)
+    rc, size, _ = gqa_call(lib, ins, outs, total=4000)
+    assert rc == 0 and size > 0        # split-key partials
+    c = T(F16, 64, 32)
+    ins, outs = gqa_args(slots={6: c, 7: T(F16, 64, 32)})
+    rc, size, _ = gqa_call(lib, ins, outs, do_rotary=1)
+    assert rc == 0 and size == 2 * 16 * 8 * 64 * 2  # transformed queries
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda ins, outs, a: ins.__setitem__(0, kb.Tensor()), -1),             # no query
+    (lambda ins, outs, a: ins.__setitem__(0, T(I32, 2, 16, 512)), -2),      # int query
+    (lambda ins, outs, a: a.update(kvN=3), -1),                             # kvN does not divide
+    (lambda ins, outs, a: (ins.__setitem__(1, T(F16, 2, 8, 128)),
+                           ins.__setitem__(2, T(F16, 2, 8, 128))), -2),     # kv_S != S
+    (lambda ins, outs, a: ins.__setitem__(12, T(F16, 64)), -1),             # unpaired norm
+    (lambda ins, outs, a: a.update(k_quant_type=1), -2),                    # quantised cache
+    (lambda ins, outs, a: a.update(sliding_window_cache=1), -2),
+    (lambda ins, outs, a: a.update(causal=0, local_window_size=4), -1),
+    (lambda ins, outs, a: a.update(do_rotary=1), -1),                       # no cos/sin
+    (lambda ins, outs, a: ins.__setitem__(10, T(F32, 1)), -2),              # k_scale
+    (lambda ins, outs, a: ins.__setitem__(8, T(F16, 3, 8, 16, 16)), -1),    # bias batch 3
+    (lambda ins, outs, a: ins.__setitem__(9, T(F16, 7)), -1),               # head_sink shape
+    (lambda ins, outs, a: outs.__setitem__(0, T(F16, 2, 16, 256)), -1),     # output shape
+    (lambda ins, outs, a: a.update(softcap=-1.0), -1),
+    (lambda ins, outs, a: a.update(total=0), -1),
+])
+def test_gqa_rejections(lib, mutate, code):
+    ins, outs = gqa_args()
+    a = {}
+    mutate(ins, outs, a)
+    kvN = a.pop("kvN", 2)
+    total = a.pop("total", 16)
+    rc, _, msg = gqa_call(lib, ins, outs, total=total, kvN=kvN, **a)
+    assert rc == code and msg
+
+
+def test_gqa_head_size_and_sharing_rules(lib):
+    ins, outs = gqa_args(H=12)
+    assert gqa_call(lib, ins, outs)[0] == -2           # head size not a multiple of 8
+    ins, outs = gqa_args(H=264)
+    assert gqa_call(lib, ins, outs)[0] == -2           # above 256
+    ins, outs = gqa_args(past="shared", S=1, cap=64)
+    outs[2] = T(F16, 2, 2, 64, 64, ptr=0x60000)        # value not shared, key shared
+    assert gqa_call(lib, ins, outs, total=20)[0] == -1
+    ins, outs = gqa_args(past="shared", S=1, cap=64)
+    assert gqa_call(lib, ins, outs, total=65)[0] == -1  # total beyond capacity
+
+
+def test_workspace_too_small_is_rejected_before_launch(lib):
+    ins, outs = gqa_args(past="shared", S=1, cap=4096)
+    a = kb.GqaAttrs()
+    lib.gqa_attrs_default(ctypes.byref(a))
+    a.num_heads, a.kv_num_heads = 8, 2
+    rc = lib.gqa_attention(ctypes.byref(a), kb._array(ins), len(ins), 4000, kb._array(outs),
+                           len(outs), None, 0, None)
+    assert rc == -3
+
+
+def test_slot_counts_checked(lib):
+    ins, outs = gqa_args()
+    a = kb.GqaAttrs()
+    lib.gqa_attrs_default(ctypes.byref(a))
+    a.num_heads, a.kv_num_heads = 8, 2
+    size = ctypes.c_size_t(0)
+    rc = lib.gqa_attention_workspace_size(ctypes.byref(a), kb._array(ins), len(ins) - 1, 16,
+                                          kb._array(outs), len(outs), ctypes.byref(size))
+    assert rc == -1
+
+
+def dmmha_call(lib, ins, outs, **akw):
+    a = kb.DmmhaAttrs()
+    lib.dmmha_attrs_default(ctypes.byref(a))
+    a.num_heads = 4
+    for k, v in akw.items():
+        setattr(a, k, v)
+    size = ctypes.c_size_t(0)
+    return lib.decode_mha_workspace_size(ctypes.byref(a), kb._array(ins), len(ins),
+                                         kb._array(outs), len(outs), ctypes.byref(size))
+
+
+def test_dmmha_rules(lib):
+    B, N, H = 2, 4, 32
+    base = [T(F16, B, 1, N * H), T(F16, B, 1, N * H), T(F16, B, 1, N * H), kb.Tensor(),
+            kb.Tensor(), T(F16, B, N, 64, H, ptr=0x20000), T(F16, B, N, 64, H, ptr=0x30000),
+            T(I32, 1)]
+    outs = [T(F16, B, 1, N * H), kb.Tensor(), kb.Tensor(), kb.Tensor()]
+    assert dmmha_call(lib, base, outs, past_present_share_buffer=1) == 0
+    assert dmmha_call(lib, base, outs, past_present_share_buffer=0) == -1
+    o2 = list(outs)
+    o2[1] = T(F16, B, N, 64, H, ptr=0x99000)         # present not the past buffer
+    assert dmmha_call(lib, base, o2, past_present_share_buffer=1) == -1
+    o3 = list(outs)
+    o3[3] = T(F16, B, N, 1, 64)                       # qk with self attention
+    assert dmmha_call(lib, base, o3, past_present_share_buffer=1, output_qk=1) == -1
+    cross = [T(F16, B, 1, N * H), T(F16, B, N, 10, H), T(F16, B, N, 10, H)] + [kb.Tensor()] * 5
+    assert dmmha_call(lib, cross, outs) == 0
+    assert dmmha_call(lib, cross, outs, output_qk=1) == -1      # qk output missing
+    o4 = list(outs)
+    o4[3] = T(F16, B, N, 1, 10)
+    assert dmmha_call(lib, cross, o4, output_qk=1) == 0
+    c2 = list(cross)
+    c2[4] = T(F16, 1, 1, 1, 10)                       # bias with cross attention
+    assert dmmha_call(lib, c2, outs) == -1
+
+
+def sparse_call(lib, ins, outs, total, **akw):
+    a = kb.SparseAttrs()
+    lib.sparse_attrs_default(ctypes.byref(a))
+    a.num_heads, a.kv_num_heads, a.sparse_block_size = 4, 2, 16
+    for k, v in akw.items():
+        setattr(a, k, v)
+    size = ctypes.c_size_t(0)
+    return lib.sparse_attention_workspace_size(ctypes.byref(a), kb._array(ins), len(ins), total,
+                                               kb._array(outs), len(outs), ctypes.byref(size))
+
+
+def test_sparse_rules(lib):
+    B, S, H = 1, 64, 16
+    ins = [T(F16, B, S, 4 * H), T(F16, B, S, 2 * H), T(F16, B, S, 2 * H),
+           T(F16, B, 2, 64, H, ptr=0x20000), T(F16, B, 2, 64, H, ptr=0x30000),
+           T(I32, 2, 5), T(I32, 2, 10), T(I32, B), kb.Tensor(), kb.Tensor()]
+    outs = [T(F16, B, S, 4 * H), kb.Tensor(), kb.Tensor()]
+    assert sparse_call(lib, ins, outs, 64) == 0
+    assert sparse_call(lib, ins, outs, 64, sparse_block_size=24) == -1
+    assert sparse_call(lib, ins, outs, 65) == -1                    # beyond capacity
+    assert sparse_call(lib, ins, outs, 48) == -2                    # token generation
+    assert sparse_call(lib, ins, outs, 64, do_rotary=1) == -1       # no cos/sin
+    i2 = list(ins)
+    i2[8], i2[9] = T(F16, 64, 4), T(F16, 64, 4)                     # width 4 not multiple of 8
+    assert sparse_call(lib, i2, outs, 64, do_rotary=1) == -1
+    i2[8], i2[9] = T(F16, 64, 8), T(F16, 64, 8)
+    assert sparse_call(lib, i2, outs, 64, do_rotary=1) == 0
+    packed = [T(F16, B, S, 8 * H), kb.Tensor(), kb.Tensor()] + ins[3:]
+    assert sparse_call(lib, packed, outs, 64) == 0
+
+
+def packed_call(lib, ins, outs, N=2, sizes=(0, 0, 0)):
+    a = kb.PackedAttrs()
+    lib.packed_attrs_default(ctypes.byref(a))
+    a.num_heads = N
+    for i in range(3):
+        a.qkv_hidden_sizes[i] = sizes[i]
+    size = ctypes.c_size_t(0)
+    rc = lib.packed_attention_workspace_size(ctypes.byref(a), kb._array(ins), len(ins),
+                                             kb._array(outs), len(outs), ctypes.byref(size))
+    return rc, size.value
+
+
+def test_packed_rules(lib):
+    Tn, D, C, B, S = 10, 32, 96, 2, 8
+    ins = [T(F16, Tn, D), T(F16, D, C), T(F16, C), T(I32, B, S), T(I32, B + 1), kb.Tensor()]
+    outs = [T(F16, Tn, C // 3)]
+    rc, size = packed_call(lib, ins, outs)
+    assert rc == 0 and size > Tn * C * 2
+    assert packed_call(lib, ins, outs, sizes=(32, 32, 32))[0] == 0
+    assert packed_call(lib, ins, outs, sizes=(32, 16, 48))[0] == -1    # q != k
+    assert packed_call(lib, ins, [T(F16, Tn, 48)], sizes=(24, 24, 48))[0] == -2  # Hv != Hq
+    assert packed_call(lib, ins, outs, N=3)[0] == -1
+    i2 = list(ins)
+    i2[0] = T(F16, 17, D)                                               # more tokens than B*S
+    assert packed_call(lib, i2, [T(F16, 17, 32)])[0] == -1
+    small = [T(F16, 2, 4), T(F16, 4, 12), T(F16, 12), T(I32, 1, 2), T(I32, 2), kb.Tensor()]
+    assert packed_call(lib, small, [T(F16, 2, 4)])[0] == -2             # head size 2
