@@ -44,31 +44,74 @@ def parse():
     return ap.parse_args()
 
 
-class Timer:
-    """Call time (torch events) and dominant-kernel time (library hook events)."""
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime (the library records them on
+    the stream it launches on; torch events cannot be read after a foreign
+    record)."""
 
-    def __init__(self, torch, lib, kind):
-        self.torch, self.lib, self.kind = torch, lib, kind
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+class Timer:
+    """Dominant-kernel time from HIP events that the library records around
+    that kernel on eager calls, and step time from a HIP graph holding exactly
+    `steps` calls (replayed once untimed, then once between two events), so
+    that host launch overhead is not part of the step."""
+
+    def __init__(self, torch, lib, kind, hip):
+        self.torch, self.lib, self.kind, self.hip = torch, lib, kind, hip
 
     def run(self, fn, steps, warmup):
         torch = self.torch
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
-        ks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ke = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        c0.record()
+        ks = [self.hip.create() for _ in range(steps)]
+        ke = [self.hip.create() for _ in range(steps)]
         for i in range(steps):
-            self.lib.kvattn_profile_events(ks[i].cuda_event, ke[i].cuda_event, self.kind)
+            self.lib.kvattn_profile_events(ks[i], ke[i], self.kind)
             fn(warmup + i)
         self.lib.kvattn_profile_events(None, None, 0)
+        torch.cuda.synchronize()
+        kern = [self.hip.elapsed_ms(ks[i], ke[i]) for i in range(steps)]
+        for e in ks + ke:
+            self.hip.destroy(e)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        graph.replay()
         c1.record()
         torch.cuda.synchronize()
         call_ms = c0.elapsed_time(c1) / steps
-        kern = [ks[i].elapsed_time(ke[i]) for i in range(steps)]
+        del graph
         return call_ms, float(np.mean(kern)), float(np.median(kern))
 
 
@@ -208,8 +251,9 @@ def packed_workload(torch, kv, wl, args, timer):
 
 
 def cpu_baseline(case, budget_s=12.0):
-    """Time the oracle on the decode workload, a growing prefix of the batch,
-    until about budget_s seconds of CPU work; report live KV GB/s."""
+    """Time the oracle on the decode workload (all 16 samples per pass),
+    repeating passes until about budget_s seconds of CPU work; report live KV
+    GB/s of the oracle."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -218,27 +262,28 @@ def cpu_baseline(case, budget_s=12.0):
         threads = os.cpu_count() or 1
     i = case["inputs"]
     lens = i["seqlens_k"].astype(np.int64) + 1
-    done_bytes = 0
-    elapsed = 0.0
-    nb = 0
     B = lens.shape[0]
-    while nb < B and elapsed < budget_s:
-        b = nb
-        sl = slice(b, b + 1)
-        t0 = time.perf_counter()
-        oracle.gqa(i["query"][sl], i["key"][sl], i["value"][sl],
-                   seqlens_k=i["seqlens_k"][sl], total_sequence_length=case["total_sequence_length"],
-                   past_key=i["past_key"][sl], past_value=i["past_value"][sl],
-                   present_key=i["past_key"][sl], present_value=i["past_value"][sl],
-                   cos_cache=i["cos_cache"], sin_cache=i["sin_cache"],
-                   num_heads=32, kv_num_heads=8, do_rotary=1)
-        elapsed += time.perf_counter() - t0
-        done_bytes += int(lens[b]) * 8 * 128 * 2 * 2
-        nb += 1
-    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"float64 numpy oracle on the first {nb} of 16 samples of the decode "
-                      f"workload ({done_bytes / 1e6:.1f} MB of live K/V, {elapsed:.1f} s)"}
+    per_pass = int(lens.sum()) * 8 * 128 * 2 * 2
+    elapsed = 0.0
+    passes = 0
+    while elapsed < budget_s and passes < 100:
+        for b in range(B):
+            sl = slice(b, b + 1)
+            t0 = time.perf_counter()
+            oracle.gqa(i["query"][sl], i["key"][sl], i["value"][sl],
+                       seqlens_k=i["seqlens_k"][sl],
+                       total_sequence_length=case["total_sequence_length"],
+                       past_key=i["past_key"][sl], past_value=i["past_value"][sl],
+                       present_key=i["past_key"][sl], present_value=i["past_value"][sl],
+                       cos_cache=i["cos_cache"], sin_cache=i["sin_cache"],
+                       num_heads=32, kv_num_heads=8, do_rotary=1)
+            elapsed += time.perf_counter() - t0
+        passes += 1
+    return {"value": round(per_pass * passes / elapsed / 1e9, 4), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle over the whole decode workload (16 samples, "
+                      f"{per_pass / 1e6:.1f} MB of live K/V per pass), {passes} passes in "
+                      f"{elapsed:.1f} s"}
 
 
 def traffic_for(kernel_key):
@@ -276,9 +321,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     lib = kv.library()
-    lib.kvattn_profile_events.restype = None
-    import ctypes
-    lib.kvattn_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+    hip = HipEvents()
     only = set(args.only) if args.only else None
 
     def want(name):
@@ -286,19 +329,19 @@ def main():
 
     res = {}
     if want("gqa_decode"):
-        res["gqa_decode"] = decode_workload(torch, kv, wl, args, Timer(torch, lib, 1))
+        res["gqa_decode"] = decode_workload(torch, kv, wl, args, Timer(torch, lib, 1, hip))
         print(f"# gqa_decode done: {res['gqa_decode']['call_ms']*1e3:.1f} us/call", file=sys.stderr, flush=True)
     if want("gqa_long_prefill"):
-        res["gqa_long_prefill"] = prefill_workload(torch, kv, wl, args, Timer(torch, lib, 2))
+        res["gqa_long_prefill"] = prefill_workload(torch, kv, wl, args, Timer(torch, lib, 2, hip))
         print("# gqa_long_prefill done", file=sys.stderr, flush=True)
     if want("gqa_prompt_small"):
-        res["gqa_prompt_small"] = prompt_small_workload(torch, kv, wl, args, Timer(torch, lib, 2))
+        res["gqa_prompt_small"] = prompt_small_workload(torch, kv, wl, args, Timer(torch, lib, 2, hip))
         print("# gqa_prompt_small done", file=sys.stderr, flush=True)
     if want("sparse_prompt"):
-        res["sparse_prompt"] = sparse_workload(torch, kv, wl, args, Timer(torch, lib, 2))
+        res["sparse_prompt"] = sparse_workload(torch, kv, wl, args, Timer(torch, lib, 2, hip))
         print("# sparse_prompt done", file=sys.stderr, flush=True)
     if want("packed_varlen"):
-        res["packed_varlen"] = packed_workload(torch, kv, wl, args, Timer(torch, lib, 4))
+        res["packed_varlen"] = packed_workload(torch, kv, wl, args, Timer(torch, lib, 4, hip))
         print("# packed_varlen done", file=sys.stderr, flush=True)
 
     workloads = {}

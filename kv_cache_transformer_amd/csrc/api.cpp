@@ -7,10 +7,11 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
-#include "../../include/kvattn.h"
+#include "kvattn.h"
 #include "kvattn_internal.hpp"
 
 using namespace kvattn;
@@ -18,6 +19,9 @@ using namespace kvattn;
 namespace {
 
 thread_local std::string g_last_error;
+
+// the decode combine kernel merges at most this many key chunks per head
+constexpr int kMaxDecodeChunks = 256;
 
 // measurement hook (kvattn_profile_events)
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
@@ -107,6 +111,16 @@ int check_head_size(int H, const char* op) {
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(KVATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return KVATTN_OK;
+}
+
+// KVATTN_DECODE_CHUNK=<keys> overrides the decode chunk size (tuning aid;
+// multiples of 128 between 128 and 65536 are accepted).
+int debug_chunk_override(int chunk) {
+  const char* e = std::getenv("KVATTN_DECODE_CHUNK");
+  if (!e) return chunk;
+  int v = std::atoi(e);
+  if (v >= 128 && v <= 65536 && v % 128 == 0) return v;
+  return chunk;
 }
 
 float resolve_scale(float scale, int H) {
@@ -239,6 +253,8 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     int chunk = 256;
     while (chunk > 128 && units * ((total + chunk - 1) / chunk) < 1024) chunk /= 2;
     while (chunk < 8192 && units * ((total + chunk - 1) / chunk) > 4096) chunk *= 2;
+    chunk = debug_chunk_override(chunk);
+    while ((total + chunk - 1) / chunk > kMaxDecodeChunks) chunk *= 2;
     P.chunk = chunk;
     P.max_chunks = (total + chunk - 1) / chunk;
     if (P.max_chunks > 1)
@@ -470,6 +486,7 @@ int dmmha_validate(const dmmha_attrs* a, const kvattn_tensor* in, int n_in,
   int chunk = 256;
   while (chunk > 128 && units * ((P.kv_len + chunk - 1) / chunk) < 1024) chunk /= 2;
   while (chunk < 8192 && units * ((P.kv_len + chunk - 1) / chunk) > 4096) chunk *= 2;
+  while ((P.kv_len + chunk - 1) / chunk > kMaxDecodeChunks) chunk *= 2;
   P.chunk = chunk;
   P.max_chunks = (P.kv_len + chunk - 1) / chunk;
   P.ws_total = P.max_chunks > 1 ? align256((size_t)P.B * P.N * P.max_chunks * (P.HP + 2) * sizeof(float)) : 0;

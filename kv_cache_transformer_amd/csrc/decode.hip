@@ -21,6 +21,8 @@
 //   O^T[H][16 heads]      += V^T[H][16] . P^T    (f16: 16x16x16, f32: 16x16x4)
 // For f16, V^T fragments come from an identity MFMA on the row-major V
 // fragment (exact: products with 1 and sums with 0), so V needs no LDS.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kvattn_internal.hpp"
 
@@ -29,58 +31,70 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kNT = 2;  // 16-key sub-tiles per wave iteration
+constexpr int kNT = 1;  // 16-key sub-tiles per wave iteration (per prefetch buffer)
+// Register buffers per wave: with 3, two sub-tiles are in flight while one is
+// computed; wide heads (and f32 beyond 64 dims) keep one buffer to stay
+// within two waves per SIMD without spilling.
+template <typename T, int HP> struct Ring { static constexpr int value = 1; };
+template <> struct Ring<f16, 64> { static constexpr int value = 3; };
+template <> struct Ring<f16, 128> { static constexpr int value = 3; };
+template <> struct Ring<float, 64> { static constexpr int value = 3; };
+constexpr int kMaxCombineChunks = 256;  // combine kernel: chunks per (sample, head)
 
 template <typename T, int HP> struct DecTile;
 
 // ------------------------------- f16 ----------------------------------------
+// Fragments of R key/value sub-tiles are kept in registers, so that the next
+// R - 1 sub-tiles' loads are in flight while one is computed.
 template <int HP> struct DecTile<f16, HP> {
   static constexpr int NS = HP / 32;
   half8v qf[NS];
   float4v o[2 * NS];
-  half8v kf[kNT][NS];
-  half8v vf[kNT][NS];
+  static constexpr int R = Ring<f16, HP>::value;
+  half8v kf[R][kNT][NS];
+  half8v vf[R][kNT][NS];
 
   __device__ void init() {
 #pragma unroll
     for (int e = 0; e < 2 * NS; ++e) o[e] = float4v{0.f, 0.f, 0.f, 0.f};
   }
   // lane l: Q[hh = l%16][32s + 8(l/16) + i]
-  __device__ void load_q(const float* qs, int lane) {
+  __device__ void load_q(const float* qs, int sq, int lane) {
     const int hh = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[s][i] = (f16)qs[hh * HP + 32 * s + 8 * g4 + i];
+      for (int i = 0; i < 8; ++i) qf[s][i] = (f16)qs[hh * sq + 32 * s + 8 * g4 + i];
   }
-  // K and V rows j0 + 64u + l%16 (clamped to the last valid row), dims 32s + 8(l/16)..+7
+  // K and V rows j0 + 64u + l%16 (clamped to the last valid row), dims 32s + 8(l/16)..+7;
+  // dims at or beyond H read as zero (the clamp keeps the address inside the row).
+  template <int BUF>
   __device__ void load_kv(const f16* kb, const f16* vb, int j0, int last, int H, int lane) {
     const int g4 = lane >> 4;
 #pragma unroll
     for (int u = 0; u < kNT; ++u) {
-      int row = min(j0 + 64 * u + (lane & 15), last);
+      const int row = min(j0 + 64 * u + (lane & 15), last);
       const f16* kr = kb + (int64_t)row * H;
       const f16* vr = vb + (int64_t)row * H;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        int d = 32 * s + 8 * g4;
-        if (d < H) {
-          kf[u][s] = load_half8(kr + d);
-          vf[u][s] = load_half8(vr + d);
-        } else {
-          kf[u][s] = half8v{};
-          vf[u][s] = half8v{};
-        }
+        const int d = 32 * s + 8 * g4;
+        const int dc = d < H ? d : 0;
+        half8v k = load_half8(kr + dc), v = load_half8(vr + dc);
+        if (d >= H) { k = half8v{}; v = half8v{}; }
+        kf[BUF][u][s] = k;
+        vf[BUF][u][s] = v;
       }
     }
   }
   // sc[u][i] = S^T[key j0 + 64u + 4(l/16) + i][head l%16]
+  template <int BUF>
   __device__ void scores(float4v (&sc)[kNT]) {
 #pragma unroll
     for (int u = 0; u < kNT; ++u) {
       float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) acc = mfma16x16x32(kf[u][s], qf[s], acc);
+      for (int s = 0; s < NS; ++s) acc = mfma16x16x32(kf[BUF][u][s], qf[s], acc);
       sc[u] = acc;
     }
   }
@@ -88,6 +102,7 @@ template <int HP> struct DecTile<f16, HP> {
 #pragma unroll
     for (int e = 0; e < 2 * NS; ++e) o[e] *= a;
   }
+  template <int BUF>
   __device__ void pv(const float4v (&p)[kNT], half4v ident) {
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -97,27 +112,29 @@ template <int HP> struct DecTile<f16, HP> {
       for (int i = 0; i < 4; ++i) pb[i] = (f16)p[u][i];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        half4v lo = {vf[u][s][0], vf[u][s][1], vf[u][s][2], vf[u][s][3]};
-        half4v hi = {vf[u][s][4], vf[u][s][5], vf[u][s][6], vf[u][s][7]};
-        float4v tlo = mfma16x16x16(lo, ident, zero);
-        float4v thi = mfma16x16x16(hi, ident, zero);
-        half4v alo, ahi;
+        const half8v v = vf[BUF][u][s];
+        const float4v tl = mfma16x16x16(half4v{v[0], v[1], v[2], v[3]}, ident, zero);
+        const float4v th = mfma16x16x16(half4v{v[4], v[5], v[6], v[7]}, ident, zero);
+        half4v al, ah;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { alo[i] = (f16)tlo[i]; ahi[i] = (f16)thi[i]; }
-        o[2 * s] = mfma16x16x16(alo, pb, o[2 * s]);
-        o[2 * s + 1] = mfma16x16x16(ahi, pb, o[2 * s + 1]);
+        for (int i = 0; i < 4; ++i) {
+          al[i] = (f16)tl[i];
+          ah[i] = (f16)th[i];
+        }
+        o[2 * s] = mfma16x16x16(al, pb, o[2 * s]);
+        o[2 * s + 1] = mfma16x16x16(ah, pb, o[2 * s + 1]);
       }
     }
   }
   // lane l holds O^T[32s + 8(l/16) + 4*half + i][head l%16]
-  __device__ void store_o(float* so, int lane, int H) {
+  __device__ void store_o(float* so, int sq, int lane) {
     const int hh = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) so[hh * HP + 32 * s + 8 * g4 + 4 * hf + i] = o[2 * s + hf][i];
+        for (int i = 0; i < 4; ++i) so[hh * sq + 32 * s + 8 * g4 + 4 * hf + i] = o[2 * s + hf][i];
   }
 };
 
@@ -126,44 +143,49 @@ template <int HP> struct DecTile<float, HP> {
   static constexpr int NU = HP / 16;
   float qf[NU][4];
   float4v o[NU];
-  float4v kf[kNT][NU];
-  float vf[kNT][4][NU];
+  static constexpr int R = Ring<float, HP>::value;
+  float4v kf[R][kNT][NU];
+  float vf[R][kNT][4][NU];
 
   __device__ void init() {
 #pragma unroll
     for (int t = 0; t < NU; ++t) o[t] = float4v{0.f, 0.f, 0.f, 0.f};
   }
   // lane l: Q[hh = l%16][16t + 4(l/16) + e]
-  __device__ void load_q(const float* qs, int lane) {
+  __device__ void load_q(const float* qs, int sq, int lane) {
     const int hh = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int t = 0; t < NU; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf[t][e] = qs[hh * HP + 16 * t + 4 * g4 + e];
+      for (int e = 0; e < 4; ++e) qf[t][e] = qs[hh * sq + 16 * t + 4 * g4 + e];
   }
+  template <int BUF>
   __device__ void load_kv(const float* kb, const float* vb, int j0, int last, int H, int lane) {
     const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
     for (int u = 0; u < kNT; ++u) {
-      int krow = min(j0 + 64 * u + l16, last);
+      const int krow = min(j0 + 64 * u + l16, last);
       const float* kr = kb + (int64_t)krow * H;
 #pragma unroll
       for (int t = 0; t < NU; ++t) {
-        int d = 16 * t + 4 * g4;
-        kf[u][t] = (d < H) ? *reinterpret_cast<const float4v*>(kr + d) : float4v{0.f, 0.f, 0.f, 0.f};
+        const int d = 16 * t + 4 * g4;
+        float4v k = *reinterpret_cast<const float4v*>(kr + (d < H ? d : 0));
+        kf[BUF][u][t] = (d < H) ? k : float4v{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        int vrow = min(j0 + 64 * u + 4 * g4 + k, last);
+        const int vrow = min(j0 + 64 * u + 4 * g4 + k, last);
         const float* vr = vb + (int64_t)vrow * H;
 #pragma unroll
         for (int t = 0; t < NU; ++t) {
-          int d = 16 * t + l16;
-          vf[u][k][t] = (d < H) ? vr[d] : 0.f;
+          const int d = 16 * t + l16;
+          const float v = vr[d < H ? d : 0];
+          vf[BUF][u][k][t] = (d < H) ? v : 0.f;
         }
       }
     }
   }
+  template <int BUF>
   __device__ void scores(float4v (&sc)[kNT]) {
 #pragma unroll
     for (int u = 0; u < kNT; ++u) {
@@ -171,7 +193,7 @@ template <int HP> struct DecTile<float, HP> {
 #pragma unroll
       for (int t = 0; t < NU; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma16x16x4f32(kf[u][t][e], qf[t][e], acc);
+        for (int e = 0; e < 4; ++e) acc = mfma16x16x4f32(kf[BUF][u][t][e], qf[t][e], acc);
       sc[u] = acc;
     }
   }
@@ -179,21 +201,22 @@ template <int HP> struct DecTile<float, HP> {
 #pragma unroll
     for (int t = 0; t < NU; ++t) o[t] *= a;
   }
+  template <int BUF>
   __device__ void pv(const float4v (&p)[kNT], half4v) {
 #pragma unroll
     for (int u = 0; u < kNT; ++u)
 #pragma unroll
       for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int t = 0; t < NU; ++t) o[t] = mfma16x16x4f32(vf[u][k][t], p[u][k], o[t]);
+        for (int t = 0; t < NU; ++t) o[t] = mfma16x16x4f32(vf[BUF][u][k][t], p[u][k], o[t]);
   }
   // lane l holds O^T[16t + 4(l/16) + i][head l%16]
-  __device__ void store_o(float* so, int lane, int H) {
+  __device__ void store_o(float* so, int sq, int lane) {
     const int hh = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int t = 0; t < NU; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) so[hh * HP + 16 * t + 4 * g4 + i] = o[t][i];
+      for (int i = 0; i < 4; ++i) so[hh * sq + 16 * t + 4 * g4 + i] = o[t][i];
   }
 };
 
@@ -228,9 +251,13 @@ __device__ __forceinline__ float read_sink(const DecodeParams& p, int h, bool& h
   return 0.f;
 }
 
-template <typename T, int HP>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
-  __shared__ float smem[kWaves * 16 * HP];
+// FEAT bits: kSoftcap (scores are soft-capped), kExtras (additive bias and/or
+// mask, and/or the qk output).  The plain variant has no per-score checks.
+constexpr int kSoftcap = 1, kExtras = 2;
+
+template <typename T, int HP, int FEAT>
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
+  __shared__ float smem[kWaves * 16 * (HP + 4)];
   __shared__ float s_m[kWaves][16], s_l[kWaves][16], s_r[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -255,49 +282,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   T* kb = static_cast<T*>(p.kc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
   T* vb = static_cast<T*>(p.vc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
   const int half = H / 2;
+  const T* cs = static_cast<const T*>(p.cos);
+  const T* sn = static_cast<const T*>(p.sin);
 
-  // ---- query heads into LDS (float), then per-head RMSNorm and rotary ------
-  float* qs = smem;
-  for (int idx = tid; idx < 16 * HP; idx += kThreads) {
-    int hh = idx / HP, d = idx % HP;
-    qs[idx] = (hh < nh && d < H) ? to_f32(qg[(h0 + hh) * H + d]) : 0.f;
-  }
-  __syncthreads();
-  if (p.q_norm != nullptr) {
-    // 16 lanes per head
-    int hh = tid >> 4, part = tid & 15;
-    float ss = 0.f;
-    for (int d = part; d < H; d += 16) ss += qs[hh * HP + d] * qs[hh * HP + d];
-    ss = wave_sum_xor(ss, 1, 8);
-    if (part == 0) s_r[hh] = rsqrtf(ss / (float)H + p.eps);
-    __syncthreads();
-  }
-  if (p.q_norm != nullptr || p.cos != nullptr) {
-    const T* qw = static_cast<const T*>(p.q_norm);
-    const T* cs = static_cast<const T*>(p.cos);
-    const T* sn = static_cast<const T*>(p.sin);
-    const int pos = min(max(n - 1, 0), max(p.rot_rows - 1, 0));
-    for (int idx = tid; idx < nh * half; idx += kThreads) {
-      int hh = idx / half, i = idx % half;
-      float a = qs[hh * HP + i], e = qs[hh * HP + i + half];
-      if (qw != nullptr) {
-        a *= s_r[hh] * to_f32(qw[i]);
-        e *= s_r[hh] * to_f32(qw[i + half]);
-      }
-      if (cs != nullptr) {
-        float co = to_f32(cs[(int64_t)pos * half + i]), si = to_f32(sn[(int64_t)pos * half + i]);
-        float a2 = a * co - e * si;
-        float e2 = e * co + a * si;
-        a = a2;
-        e = e2;
-      }
-      qs[hh * HP + i] = a;
-      qs[hh * HP + i + half] = e;
-    }
-    __syncthreads();
-  }
-
-  // ---- append the new token's key/value (the chunk that holds its row) -----
+  // ---- append the new token's key/value (the workgroup whose chunk holds its
+  // row does it before it reads any key row, so that its loads see the row) --
   if (newrow >= 0 && newrow >= c0 && newrow < c1) {
     const T* kn = static_cast<const T*>(p.k_new) + ((int64_t)b * p.kvN + kvh) * H;
     const T* vn = static_cast<const T*>(p.v_new) + ((int64_t)b * p.kvN + kvh) * H;
@@ -310,8 +299,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         rinv = rsqrtf(ss / (float)H + p.eps);
       }
       const T* kw = static_cast<const T*>(p.k_norm);
-      const T* cs = static_cast<const T*>(p.cos);
-      const T* sn = static_cast<const T*>(p.sin);
       for (int i = lane; i < half; i += 64) {
         float a = to_f32(kn[i]), e = to_f32(kn[i + half]);
         if (kw != nullptr) {
@@ -320,10 +307,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
         if (cs != nullptr) {
           const int rrow = min(newrow, p.rot_rows - 1);
-          float co = to_f32(cs[(int64_t)rrow * half + i]);
-          float si = to_f32(sn[(int64_t)rrow * half + i]);
-          float a2 = a * co - e * si;
-          float e2 = e * co + a * si;
+          const float co = to_f32(cs[(int64_t)rrow * half + i]);
+          const float si = to_f32(sn[(int64_t)rrow * half + i]);
+          const float a2 = a * co - e * si;
+          const float e2 = e * co + a * si;
           a = a2;
           e = e2;
         }
@@ -336,9 +323,70 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     __syncthreads();
   }
 
+  // ---- start streaming: the first R - 1 sub-tiles' loads go out now, so the
+  // query set-up below overlaps with them --------------------------------------
   DecTile<T, HP> tile;
   tile.init();
-  tile.load_q(qs, lane);
+  constexpr int R = DecTile<T, HP>::R;
+  const int step = 16 * kWaves * kNT;
+  const int first = c0 + 16 * wave;
+  const int nsub = first < c1 ? (c1 - first + step - 1) / step : 0;
+  auto jof = [&](int k) { return first + k * step; };
+  if constexpr (R == 3) {
+    if (nsub > 0) tile.template load_kv<0>(kb, vb, jof(0), c1 - 1, H, lane);
+    if (nsub > 1) tile.template load_kv<1>(kb, vb, jof(1), c1 - 1, H, lane);
+  }
+
+  // ---- query heads into LDS (float), per-head RMSNorm and rotary ------------
+  // The rotary table entries of this thread's pairs are loaded together with
+  // the query so that the set-up waits for memory once.
+  constexpr int SQ = HP + 4;                    // padded LDS row (floats)
+  constexpr int PH = HP / 2;                    // rotary pairs per padded head
+  constexpr int PPT = 16 * PH / kThreads;       // pairs per thread
+  float* qs = smem;
+  for (int idx = tid; idx < 16 * HP; idx += kThreads) {
+    const int hh = idx / HP, d = idx % HP;
+    qs[hh * SQ + d] = (hh < nh && d < H) ? to_f32(qg[(h0 + hh) * H + d]) : 0.f;
+  }
+  const int pos = min(max(n - 1, 0), max(p.rot_rows - 1, 0));
+  float co_r[PPT], si_r[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int i = (tid + kThreads * k) % PH;
+    co_r[k] = (cs != nullptr && i < half) ? to_f32(cs[(int64_t)pos * half + i]) : 1.f;
+    si_r[k] = (cs != nullptr && i < half) ? to_f32(sn[(int64_t)pos * half + i]) : 0.f;
+  }
+  __syncthreads();
+  if (p.q_norm != nullptr) {
+    // 16 lanes per head
+    const int hh = tid >> 4, part = tid & 15;
+    float ss = 0.f;
+    for (int d = part; d < H; d += 16) ss += qs[hh * SQ + d] * qs[hh * SQ + d];
+    ss = wave_sum_xor(ss, 1, 8);
+    if (part == 0) s_r[hh] = rsqrtf(ss / (float)H + p.eps);
+    __syncthreads();
+  }
+  if (p.q_norm != nullptr || cs != nullptr) {
+    const T* qw = static_cast<const T*>(p.q_norm);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int idx = tid + kThreads * k;
+      const int hh = idx / PH, i = idx % PH;
+      if (hh < nh && i < half) {
+        float a = qs[hh * SQ + i], e = qs[hh * SQ + i + half];
+        if (qw != nullptr) {
+          a *= s_r[hh] * to_f32(qw[i]);
+          e *= s_r[hh] * to_f32(qw[i + half]);
+        }
+        const float a2 = a * co_r[k] - e * si_r[k];
+        const float e2 = e * co_r[k] + a * si_r[k];
+        qs[hh * SQ + i] = a2;
+        qs[hh * SQ + i + half] = e2;
+      }
+    }
+    __syncthreads();
+  }
+  tile.load_q(qs, SQ, lane);
   __syncthreads();  // qs is reused below
 
   // identity for the f16 V transpose: lane l holds B[k = 4(l/16)+i][n = l%16]
@@ -355,10 +403,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   T* qk = static_cast<T*>(p.qk);
 
   float m = kNegInf, l = 0.f;
-  for (int j0 = c0 + 16 * wave; j0 < c1; j0 += 16 * kWaves * kNT) {
-    tile.load_kv(kb, vb, j0, c1 - 1, H, lane);
+  // Score transform, online softmax and PV for the sub-tiles held in BUF.
+  auto process = [&](auto buf_tag, int j0) {
+    constexpr int BUF = decltype(buf_tag)::value;
     float4v sc[kNT];
-    tile.scores(sc);
+    tile.template scores<BUF>(sc);
     mfma_result_fence();
     float tmax = kNegInf;
     float4v x[kNT];
@@ -366,15 +415,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     for (int u = 0; u < kNT; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int key = j0 + 64 * u + 4 * (lane >> 4) + i;
-        bool ok = head_ok && key < c1;
+        const int key = j0 + 64 * u + 4 * (lane >> 4) + i;
+        const bool ok = head_ok && key < c1;
         float v = sc[u][i] * scale;
-        if (cap > 0.f) v = softcap_apply(v, cap, inv_cap);
-        if (ok && bias != nullptr && key < p.bias_cols)
-          v += to_f32(bias[b * p.bias_sb + h * p.bias_sh + key]);
-        if (ok && p.mask != nullptr && key < p.mask_cols)
-          v += (p.mask[(int64_t)b * p.mask_cols + key] == 0) ? p.mask_filter : 0.f;
-        if (ok && qk != nullptr) qk[((int64_t)b * p.N + h) * p.host_n + key] = from_f32<T>(v);
+        if (FEAT & kSoftcap) v = softcap_apply(v, cap, inv_cap);
+        if (FEAT & kExtras) {
+          if (ok && bias != nullptr && key < p.bias_cols)
+            v += to_f32(bias[b * p.bias_sb + h * p.bias_sh + key]);
+          if (ok && p.mask != nullptr && key < p.mask_cols)
+            v += (p.mask[(int64_t)b * p.mask_cols + key] == 0) ? p.mask_filter : 0.f;
+          if (ok && qk != nullptr) qk[((int64_t)b * p.N + h) * p.host_n + key] = from_f32<T>(v);
+        }
         v = ok ? v * kLog2e : kNegInf;
         x[u][i] = v;
         tmax = fmaxf(tmax, v);
@@ -391,21 +442,46 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     for (int u = 0; u < kNT; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float e = fast_exp2(x[u][i] - muse);
+        const float e = fast_exp2(x[u][i] - muse);
         pr[u][i] = e;
         psum += e;
       }
     l = l * alpha + psum;
     tile.scale_o(alpha);
-    tile.pv(pr, ident);
+    tile.template pv<BUF>(pr, ident);
+  };
+
+  // Each wave walks its sub-tiles (every kWaves-th one of the chunk) through a
+  // ring of R register buffers, loads running R - 1 sub-tiles ahead (the
+  // first R - 1 were issued before the query set-up).
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if constexpr (R == 3) {
+    for (int k = 0; k < nsub; k += 3) {
+      if (k + 2 < nsub) tile.template load_kv<2>(kb, vb, jof(k + 2), c1 - 1, H, lane);
+      process(I0{}, jof(k));
+      if (k + 1 >= nsub) break;
+      if (k + 3 < nsub) tile.template load_kv<0>(kb, vb, jof(k + 3), c1 - 1, H, lane);
+      process(I1{}, jof(k + 1));
+      if (k + 2 >= nsub) break;
+      if (k + 4 < nsub) tile.template load_kv<1>(kb, vb, jof(k + 4), c1 - 1, H, lane);
+      process(I2{}, jof(k + 2));
+    }
+  } else {
+    static_assert(R == 1, "ring depth 1 or 3");
+    for (int k = 0; k < nsub; ++k) {
+      tile.template load_kv<0>(kb, vb, jof(k), c1 - 1, H, lane);
+      process(I0{}, jof(k));
+    }
   }
   mfma_result_fence();
   l += shfl_xor(l, 16);
   l += shfl_xor(l, 32);
 
   // ---- merge the waves of this workgroup ------------------------------------
-  float* so = smem + wave * 16 * HP;
-  tile.store_o(so, lane, H);
+  float* so = smem + wave * 16 * SQ;
+  tile.store_o(so, SQ, lane);
   if (lane < 16) {
     s_m[wave][lane] = m;
     s_l[wave][lane] = l;
@@ -424,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     for (int w = 0; w < kWaves; ++w) {
       float f = fast_exp2(s_m[w][hj] - Mu);
       L += s_l[w][hj] * f;
-      O += smem[w * 16 * HP + hj * HP + d] * f;
+      O += smem[w * 16 * SQ + hj * SQ + d] * f;
     }
     const int hq = h0 + hj;
     if (nchunks == 1) {
@@ -451,10 +527,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Merge the chunk partials of one (sample, query head).
+// Merge the chunk partials of one (sample, query head): the chunk maxima and
+// sums are read by all threads at once into LDS, then every thread sums its
+// dims over the chunks with independent loads.
 template <typename T, int HP>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y;
+  __shared__ float w_s[kMaxCombineChunks];
+  __shared__ float red[2][4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int n, newrow;
   decode_len(p, b, n, newrow);
   const int kstart = decode_kstart(p, n);
@@ -462,38 +542,66 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   if (nchunks <= 1) return;
   const int rec = HP + 2;
   const float* base = p.part + ((int64_t)b * p.N + h) * p.max_chunks * rec;
-  float M = kNegInf;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, base[c * rec]);
+  // chunk maxima -> weights exp2(M_c - M), and the weighted sum of the L_c
+  float mc = kNegInf, lc = 0.f;
+  if (tid < nchunks) {
+    mc = base[tid * rec];
+    lc = base[tid * rec + 1];
+  }
+  const int wave = tid >> 6, nw = blockDim.x >> 6;
+  float M = wave_max_xor(mc, 1, 32);
+  if ((tid & 63) == 0) red[0][wave] = M;
+  __syncthreads();
+  M = red[0][0];
+  for (int w = 1; w < nw; ++w) M = fmaxf(M, red[0][w]);
   const float Mu = (M == kNegInf) ? 0.f : M;
+  const float wgt = (tid < nchunks) ? fast_exp2(mc - Mu) : 0.f;
+  if (tid < nchunks) w_s[tid] = wgt;
+  float L = wave_sum_xor(lc * wgt, 1, 32);
+  if ((tid & 63) == 0) red[1][wave] = L;
+  __syncthreads();
+  L = red[1][0];
+  for (int w = 1; w < nw; ++w) L += red[1][w];
   bool has;
   const float sg = read_sink<T>(p, h, has);
-  for (int d = threadIdx.x; d < p.H; d += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      float f = fast_exp2(base[c * rec] - Mu);
-      L += base[c * rec + 1] * f;
-      O += base[c * rec + 2 + d] * f;
-    }
-    float out;
-    if (has) {
-      float M2 = fmaxf(M, sg);
-      float den = L * fast_exp2(M - M2) + fast_exp2(sg - M2);
-      out = (L == 0.f) ? 0.f : O * fast_exp2(M - M2) / den;
-    } else {
-      out = (L > 0.f) ? O / L : 0.f;
-    }
-    static_cast<T*>(p.out)[((int64_t)b * p.N + h) * p.H + d] = from_f32<T>(out);
+  float inv;
+  if (L == 0.f) {
+    inv = 0.f;
+  } else if (has) {
+    const float M2 = fmaxf(M, sg);
+    const float den = L * fast_exp2(M - M2) + fast_exp2(sg - M2);
+    inv = fast_exp2(M - M2) / den;
+  } else {
+    inv = 1.f / L;
+  }
+  for (int d = tid; d < p.H; d += blockDim.x) {
+    float O = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < nchunks; ++c) O += base[c * rec + 2 + d] * w_s[c];
+    static_cast<T*>(p.out)[((int64_t)b * p.N + h) * p.H + d] = from_f32<T>(O * inv);
   }
 }
 
-template <typename T, int HP>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+template <typename T, int HP, int FEAT>
+hipError_t launch_decode_f(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.max_chunks, p.kvN * p.head_groups, p.B);
-  hipLaunchKernelGGL((decode_kernel<T, HP>), grid, dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<T, HP, FEAT>), grid, dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_chunks <= 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, HP>), dim3(p.N, p.B), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+template <typename T, int HP>
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+  const bool extras = p.bias != nullptr || p.mask != nullptr || p.qk != nullptr;
+  const bool cap = p.softcap > 0.f;
+  if (extras) {
+    if (cap) return launch_decode_f<T, HP, kSoftcap | kExtras>(p, s);
+    return launch_decode_f<T, HP, kExtras>(p, s);
+  }
+  if (cap) return launch_decode_f<T, HP, kSoftcap>(p, s);
+  return launch_decode_f<T, HP, 0>(p, s);
 }
 
 }  // namespace
