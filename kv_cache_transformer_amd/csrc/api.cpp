@@ -4,6 +4,7 @@
 // synchronise; all work goes to the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -20,8 +21,10 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// the decode combine kernel merges at most this many key chunks per head
-constexpr int kMaxDecodeChunks = 256;
+// decode: waves per compute unit in the grid (two groups of four waves)
+constexpr int64_t kDecodeWavesPerCu = 8;
+// decode: a wave streams at least this many keys when a unit is split
+constexpr int64_t kDecodeMinKeysPerWave = 64;
 
 // measurement hook (kvattn_profile_events)
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
@@ -113,14 +116,35 @@ int hip_status(hipError_t e, const char* what) {
   return KVATTN_OK;
 }
 
-// KVATTN_DECODE_CHUNK=<keys> overrides the decode chunk size (tuning aid;
-// multiples of 128 between 128 and 65536 are accepted).
-int debug_chunk_override(int chunk) {
-  const char* e = std::getenv("KVATTN_DECODE_CHUNK");
-  if (!e) return chunk;
-  int v = std::atoi(e);
-  if (v >= 128 && v <= 65536 && v % 128 == 0) return v;
-  return chunk;
+// Compute units of the current device (cached per device; 256 when the
+// query fails, e.g. without a GPU).
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev >= 0 && dev < 64) cache[dev] = cus;
+  return cus;
+}
+
+// Waves of the decode grid: enough to fill the device, no more than the
+// units could use (each split unit's wave streams >= 64 keys), at least one
+// per unit, a multiple of four.  KVATTN_DECODE_WAVES_PER_CU=<1..32> overrides
+// the fill target (tuning aid).
+int64_t decode_waves(int64_t units, int64_t max_keys) {
+  int64_t per_cu = kDecodeWavesPerCu;
+  if (const char* e = std::getenv("KVATTN_DECODE_WAVES_PER_CU")) {
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= 32) per_cu = v;
+  }
+  const int64_t fill = per_cu * device_cu_count();
+  const int64_t useful = units + (units * std::max<int64_t>(max_keys, 0) + kDecodeMinKeysPerWave - 1) /
+                                     kDecodeMinKeysPerWave;
+  const int64_t w = std::max(units, std::min(fill, useful));
+  return (w + 3) / 4 * 4;
 }
 
 float resolve_scale(float scale, int H) {
@@ -136,7 +160,8 @@ struct GqaPlan {
   bool has_past, shared, decode, q_transform;
   int total;
   // decode
-  int chunk, max_chunks, head_groups;
+  int head_groups, hpw;
+  int64_t waves;
   size_t ws_q, ws_part, ws_total;
 };
 
@@ -248,17 +273,14 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   P.ws_q = 0;
   P.ws_part = 0;
   if (P.decode) {
-    P.head_groups = (P.N / P.kvN + 15) / 16;
-    const long units = (long)P.B * P.kvN * P.head_groups;
-    int chunk = 256;
-    while (chunk > 128 && units * ((total + chunk - 1) / chunk) < 1024) chunk /= 2;
-    while (chunk < 8192 && units * ((total + chunk - 1) / chunk) > 4096) chunk *= 2;
-    chunk = debug_chunk_override(chunk);
-    while ((total + chunk - 1) / chunk > kMaxDecodeChunks) chunk *= 2;
-    P.chunk = chunk;
-    P.max_chunks = (total + chunk - 1) / chunk;
-    if (P.max_chunks > 1)
-      P.ws_part = align256((size_t)P.B * P.N * P.max_chunks * (P.HP + 2) * sizeof(float));
+    const int g = P.N / P.kvN;
+    P.head_groups = (g + 15) / 16;
+    P.hpw = std::min(16, g);
+    const int64_t units = (int64_t)P.B * P.kvN * P.head_groups;
+    P.waves = decode_waves(units, std::min<int64_t>(total, P.cap));
+    if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode: too many (sample, head) units");
+    if (P.waves > units)
+      P.ws_part = align256((size_t)P.waves * P.hpw * (P.HP + 4) * sizeof(float));
   } else if (P.q_transform) {
     P.ws_q = align256((size_t)P.B * P.S * P.N * P.H * esz);
   }
@@ -317,9 +339,10 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     d.B = P.B; d.N = P.N; d.kvN = P.kvN; d.H = P.H; d.cap = P.cap;
     d.scale = scale;
     d.softcap = a->softcap;
-    d.chunk = P.chunk; d.max_chunks = P.max_chunks; d.head_groups = P.head_groups;
+    d.head_groups = P.head_groups; d.hpw = P.hpw; d.waves = (int)P.waves;
     CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st, [&] { return launch_decode(dt, P.HP, d, st); }),
                      "decode launch"));
+    CHECK(hip_status(launch_decode_combine(dt, P.HP, d, st), "decode combine launch"));
     return ok();
   }
 
@@ -400,7 +423,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
 struct DmmhaPlan {
   int B, N, H, HP, dt, cap, kv_len;
   bool self;
-  int chunk, max_chunks;
+  int64_t waves;
   size_t ws_total;
 };
 
@@ -482,14 +505,10 @@ int dmmha_validate(const dmmha_attrs* a, const kvattn_tensor* in, int n_in,
     if (bias.dims[0] != 1 && bias.dims[0] != P.B) return fail(KVATTN_ERR_INVALID_ARG, "attention_bias dim 0 must be 1 or batch");
     if (bias.dims[1] != 1 && bias.dims[1] != P.N) return fail(KVATTN_ERR_INVALID_ARG, "attention_bias dim 1 must be 1 or num_heads");
   }
-  const long units = (long)P.B * P.N;
-  int chunk = 256;
-  while (chunk > 128 && units * ((P.kv_len + chunk - 1) / chunk) < 1024) chunk /= 2;
-  while (chunk < 8192 && units * ((P.kv_len + chunk - 1) / chunk) > 4096) chunk *= 2;
-  while ((P.kv_len + chunk - 1) / chunk > kMaxDecodeChunks) chunk *= 2;
-  P.chunk = chunk;
-  P.max_chunks = (P.kv_len + chunk - 1) / chunk;
-  P.ws_total = P.max_chunks > 1 ? align256((size_t)P.B * P.N * P.max_chunks * (P.HP + 2) * sizeof(float)) : 0;
+  const int64_t units = (int64_t)P.B * P.N;
+  P.waves = decode_waves(units, P.kv_len);
+  if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode_mha: too many (sample, head) units");
+  P.ws_total = P.waves > units ? align256((size_t)P.waves * (P.HP + 4) * sizeof(float)) : 0;
   return KVATTN_OK;
 }
 
@@ -529,10 +548,11 @@ int dmmha_run(const dmmha_attrs* a, const kvattn_tensor* in, const kvattn_tensor
   d.part = static_cast<float*>(ws);
   d.B = P.B; d.N = P.N; d.kvN = P.N; d.H = P.H; d.cap = P.cap;
   d.scale = resolve_scale(a->scale, P.H);
-  d.chunk = P.chunk; d.max_chunks = P.max_chunks; d.head_groups = 1;
+  d.head_groups = 1; d.hpw = 1; d.waves = (int)P.waves;
   CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st,
                             [&] { return launch_decode(to_dtype(P.dt), P.HP, d, st); }),
                    "decode launch"));
+  CHECK(hip_status(launch_decode_combine(to_dtype(P.dt), P.HP, d, st), "decode combine launch"));
   return ok();
 }
 

@@ -77,10 +77,12 @@ struct DecodeParams {
   int window;               // >= 0: keys j >= (n_b - 1) - window
   void* out;                // (B, N*H)
   void* qk;                 // (B, N, 1, host_n) scores after mask, or null
-  float* part;              // (B, N, max_chunks, HP + 2) partial results
+  float* part;              // (waves, hpw, HP + 4) per-wave partials: m, l, -, -, o[HP]
   int B, N, kvN, H, cap;
   float scale, softcap;
-  int chunk, max_chunks, head_groups;
+  int head_groups;          // query-head groups of <= 16 per kv head
+  int hpw;                  // partial records per wave: min(16, N / kvN)
+  int waves;                // waves in the grid (a multiple of 4, >= B * kvN * head_groups)
 };
 
 // ---------------------------------------------------------------------------
@@ -146,6 +148,7 @@ struct GemmParams {
 hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s);
 hipError_t launch_copy_past(DType dt, const CopyPastParams& p, hipStream_t s);
 hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_combine(DType dt, int hp, const DecodeParams& p, hipStream_t s);
 hipError_t launch_flash(DType dt, int hp, const FlashParams& p, int grid_x, int grid_y,
                         int grid_z, hipStream_t s);
 hipError_t launch_packed_sched(const PackedSchedParams& p, hipStream_t s);
