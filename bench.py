@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--only", nargs="*", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--rotations", type=int, default=4)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first copy this many MiB device to device (a plain copy of known size, "
+                         "to scale the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -327,6 +330,16 @@ def main():
     def want(name):
         return only is None or name in only
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy probe: {args.copy_probe_mib} MiB read and written", file=sys.stderr, flush=True)
+        del src, dst
+
     res = {}
     if want("gqa_decode"):
         res["gqa_decode"] = decode_workload(torch, kv, wl, args, Timer(torch, lib, 1, hip))
@@ -401,7 +414,7 @@ def main():
         line["ms_per_step"] = round(r["call_ms"], 5)
         line["config"]["live_kv_bytes"] = r["kv_bytes"]
         line["config"]["cache_rotations"] = args.rotations
-        tr = traffic_for("decode_gqa_decode")
+        tr = traffic_for("decode")
         line["roofline"] = {"bound": "hbm", "kernel": "decode", "achieved": round(gbs_k, 2),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
                             "kernel_us": round(r["kern_ms"] * 1e3, 3),

@@ -21,7 +21,8 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// decode: waves per compute unit in the grid (two groups of four waves)
+// decode: waves per compute unit in the grid (two groups of four waves: two
+// waves per SIMD)
 constexpr int64_t kDecodeWavesPerCu = 8;
 // decode: a wave streams at least this many keys when a unit is split
 constexpr int64_t kDecodeMinKeysPerWave = 64;
@@ -131,9 +132,9 @@ int device_cu_count() {
 }
 
 // Waves of the decode grid: enough to fill the device, no more than the
-// units could use (each split unit's wave streams >= 64 keys), at least one
-// per unit, a multiple of four.  KVATTN_DECODE_WAVES_PER_CU=<1..32> overrides
-// the fill target (tuning aid).
+// units could use (a pair of waves streams >= 128 keys of a split unit), at
+// least one pair per unit, a multiple of eight (workgroups of four pairs).  KVATTN_DECODE_WAVES_PER_CU=<1..32> overrides the fill
+// target (tuning aid).
 int64_t decode_waves(int64_t units, int64_t max_keys) {
   int64_t per_cu = kDecodeWavesPerCu;
   if (const char* e = std::getenv("KVATTN_DECODE_WAVES_PER_CU")) {
@@ -141,10 +142,10 @@ int64_t decode_waves(int64_t units, int64_t max_keys) {
     if (v >= 1 && v <= 32) per_cu = v;
   }
   const int64_t fill = per_cu * device_cu_count();
-  const int64_t useful = units + (units * std::max<int64_t>(max_keys, 0) + kDecodeMinKeysPerWave - 1) /
-                                     kDecodeMinKeysPerWave;
-  const int64_t w = std::max(units, std::min(fill, useful));
-  return (w + 3) / 4 * 4;
+  const int64_t pair_keys = 2 * kDecodeMinKeysPerWave;
+  const int64_t useful = 2 * (units + (units * std::max<int64_t>(max_keys, 0) + pair_keys - 1) / pair_keys);
+  const int64_t w = std::max(2 * units, std::min(fill, useful));
+  return (w + 7) / 8 * 8;
 }
 
 float resolve_scale(float scale, int H) {
@@ -279,8 +280,7 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     const int64_t units = (int64_t)P.B * P.kvN * P.head_groups;
     P.waves = decode_waves(units, std::min<int64_t>(total, P.cap));
     if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode: too many (sample, head) units");
-    if (P.waves > units)
-      P.ws_part = align256((size_t)P.waves * P.hpw * (P.HP + 4) * sizeof(float));
+    P.ws_part = align256((size_t)(P.waves / 2) * P.hpw * (P.HP + 4) * sizeof(float));
   } else if (P.q_transform) {
     P.ws_q = align256((size_t)P.B * P.S * P.N * P.H * esz);
   }
@@ -508,7 +508,7 @@ int dmmha_validate(const dmmha_attrs* a, const kvattn_tensor* in, int n_in,
   const int64_t units = (int64_t)P.B * P.N;
   P.waves = decode_waves(units, P.kv_len);
   if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode_mha: too many (sample, head) units");
-  P.ws_total = P.waves > units ? align256((size_t)P.waves * (P.HP + 4) * sizeof(float)) : 0;
+  P.ws_total = align256((size_t)(P.waves / 2) * (P.HP + 4) * sizeof(float));
   return KVATTN_OK;
 }
 

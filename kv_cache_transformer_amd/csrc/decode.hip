@@ -4,25 +4,34 @@
 // Work split (GroupQueryAttention page, Implementation variants: decode is
 // partitioned along the key axis and the partial online-softmax results are
 // merged).  A unit is (sample b, kv head, group of <= 16 query heads sharing
-// that kv head).  Every wave of the grid is an independent worker: the live
-// keys of all units are dealt out so that each wave streams about the same
-// number of key rows, each unit receiving a whole number of waves (at least
-// one) and each of its waves one contiguous run of its keys.  The lengths are
-// device data, so every wave derives the deal from them itself.  A wave reads
-// its rows of the cache once for all query heads of its unit, with up to
-// three 16-row sub-tiles in flight in a register ring, and writes one partial
-// (max, sum, unnormalised output) per head; a unit served by a single wave
-// writes the output directly.  decode_combine_kernel merges the partials with
-// a log-sum-exp combine and adds the head-sink term.
+// that kv head).  The live keys of all units are dealt out to pairs of waves
+// so that every pair streams about the same number of key rows, each unit
+// receiving a whole number of pairs (at least one) and each pair a contiguous
+// run of its keys.  The lengths are device data, so every wave derives the
+// deal from them itself.
+//
+// A workgroup is eight waves on one CU; waves j and j + 4 share a SIMD and
+// form pair j.  Of two waves on a SIMD the older one wins the memory-issue
+// arbitration and the younger one gets what is left (measured: about 60 % of
+// the rate, and the issue priority does not change it), so the two waves of
+// a pair do not split their run statically: the run is cut into chunks that
+// they claim from an LDS counter.  Each chunk's partial (max, sum,
+// unnormalised output per head) goes to its own LDS record and the pair
+// merges them in chunk order, so the result does not depend on which wave
+// took which chunk.  A pair writes one partial per head, or the output when
+// its unit is small enough for one pair; decode_combine_kernel merges the
+// pairs of the other units with a log-sum-exp combine and adds the head-sink
+// term.  A wave reads its rows of the cache once for all query heads of its
+// unit, with up to three 16-row sub-tiles in flight in a register ring.
 //
 // The query (optionally RMS-normed per head, then NeoX-rotated at the new
-// token's position) is built in registers in the MFMA operand layout; its
-// loads are issued before the first key/value loads so that waiting for it
-// does not wait for them.  The new token's key (normed and rotated the same
-// way) and value are appended by the wave whose run holds the new row, before
-// that wave loads the row (GroupQueryAttention page, Inputs table:
-// past_key/present_key, q/k_norm_weight, cos/sin_cache).  Lanes of one wave
-// see each other's global stores in program order, so no barrier is needed.
+// token's position) is built in registers in the MFMA operand layout before
+// the wave issues its first key/value load.  The new token's key (normed and
+// rotated the same way) and value are appended by the wave whose run holds
+// the new row, before that wave loads the row (GroupQueryAttention page,
+// Inputs table: past_key/present_key, q/k_norm_weight, cos/sin_cache).  Lanes
+// of one wave see each other's global stores in program order, so no barrier
+// is needed.
 //
 // MFMA mapping per 16-key sub-tile (wave64):
 //   S^T[16 keys][16 heads] = K[16][H] . Q^T      (f16: 16x16x32, f32: 16x16x4)
@@ -38,18 +47,28 @@
 namespace kvattn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWavesPerGroup = kThreads / 64;
+constexpr int kPairsPerGroup = kWavesPerGroup / 2;
+// LDS for the chunk partials of a workgroup's pairs (floats), and the most
+// chunks a pair's run is cut into
+constexpr int kPartFloats = 30720;
+constexpr int kMaxChunks = 16;
 constexpr int64_t kMinKeysPerWave = 64;
+// s_waitcnt immediate for vmcnt(0) with the other counters unconstrained
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// A unit with at most this many keys and a single pair writes the output
+// directly (no combine).
+constexpr int kDirectKeys = 64;
 
 // Register ring depth (16-row sub-tiles held per wave): R - 1 are in flight
-// while one is computed.  Sized to stay within 256 registers per lane (two
-// waves per SIMD) without spilling.
+// while one is computed, sized to stay within 256 registers without spilling.
 template <typename T, int HP> struct Ring { static constexpr int value = 1; };
 template <> struct Ring<f16, 64> { static constexpr int value = 4; };
 template <> struct Ring<f16, 128> { static constexpr int value = 4; };
 template <> struct Ring<float, 64> { static constexpr int value = 3; };
-template <> struct Ring<float, 128> { static constexpr int value = 2; };
 
 // Four consecutive elements of a head row ("quad"): the unit of the query
 // set-up, the append and the output stores.
@@ -73,15 +92,22 @@ template <> struct Quad<float> {
   __device__ static void store_raw(float* p, type v) { *reinterpret_cast<float4v*>(p) = v; }
 };
 
-template <typename T, int HP> struct DecTile;
+// Compiler barrier on a register value: what uses v after this point cannot
+// be moved above it (used to keep conversions of loaded values inside the
+// branch that needs them, so other paths never wait for those loads).
+template <typename V>
+__device__ __forceinline__ void pin(V& v) {
+  asm volatile("" : "+v"(v));
+}
+
+template <typename T, int HP, int R> struct DecTile;
 
 // ------------------------------- f16 ----------------------------------------
 // Lane l works on head hh = l % 16 and quarter g4 = l / 16.  Quad qi of the
 // lane covers dims quad_dim(qi, g4) .. + 3 of the query, and of the output.
-template <int HP> struct DecTile<f16, HP> {
+template <int HP, int R> struct DecTile<f16, HP, R> {
   static constexpr int NS = HP / 32;  // 32-dim k-steps of the score MFMA
   static constexpr int NQ = HP / 16;  // quads per lane
-  static constexpr int R = Ring<f16, HP>::value;
   half8v qf[NS];
   float4v o[NQ];
   half8v kf[R][NS];
@@ -101,7 +127,10 @@ template <int HP> struct DecTile<f16, HP> {
                      (f16)x[2 * s + 1][2], (f16)x[2 * s + 1][3]};
   }
   // K and V rows j0 + l%16 (clamped to the last row of the run), dims
-  // 32s + 8 g4 .. + 7; dims at or beyond H read as zero.
+  // 32s + 8 g4 .. + 7.  Slots at or beyond H re-read dims 0..7 of the row:
+  // the query is zero there, so they add nothing to the scores, and those
+  // output dims are never stored.  (Masking the loaded values would make
+  // every load wait for its data at once.)
   template <int BUF>
   __device__ void load_kv(const f16* kb, const f16* vb, int j0, int last, int H, int lane) {
     const int g4 = lane >> 4;
@@ -112,13 +141,8 @@ template <int HP> struct DecTile<f16, HP> {
     for (int s = 0; s < NS; ++s) {
       const int d = 32 * s + 8 * g4;
       const int dc = d < H ? d : 0;
-      half8v k = load_half8(kr + dc), v = load_half8(vr + dc);
-      if (d >= H) {
-        k = half8v{};
-        v = half8v{};
-      }
-      kf[BUF][s] = k;
-      vf[BUF][s] = v;
+      kf[BUF][s] = load_half8(kr + dc);
+      vf[BUF][s] = load_half8(vr + dc);
     }
   }
   // S^T[key j0 + 4 g4 + i][head hh] for i < 4
@@ -151,9 +175,8 @@ template <int HP> struct DecTile<f16, HP> {
 };
 
 // ------------------------------- f32 ----------------------------------------
-template <int HP> struct DecTile<float, HP> {
+template <int HP, int R> struct DecTile<float, HP, R> {
   static constexpr int NQ = HP / 16;
-  static constexpr int R = Ring<float, HP>::value;
   float qf[NQ][4];
   float4v o[NQ];
   float4v kf[R][NQ];
@@ -176,11 +199,11 @@ template <int HP> struct DecTile<float, HP> {
     const int g4 = lane >> 4, l16 = lane & 15;
     const int krow = min(j0 + l16, last);
     const float* kr = kb + (int64_t)krow * H;
+    // slots at or beyond H re-read the row's first dims (see the f16 tile)
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
       const int d = 16 * t + 4 * g4;
-      float4v k = *reinterpret_cast<const float4v*>(kr + (d < H ? d : 0));
-      kf[BUF][t] = (d < H) ? k : float4v{0.f, 0.f, 0.f, 0.f};
+      kf[BUF][t] = *reinterpret_cast<const float4v*>(kr + (d < H ? d : 0));
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -189,8 +212,7 @@ template <int HP> struct DecTile<float, HP> {
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
         const int d = 16 * t + l16;
-        const float v = vr[d < H ? d : 0];
-        vf[BUF][k][t] = (d < H) ? v : 0.f;
+        vf[BUF][k][t] = vr[d < H ? d : 0];
       }
     }
   }
@@ -238,22 +260,23 @@ __device__ __forceinline__ int sample_count(const DecodeParams& p, int b) {
   return max(n - kstart, 0);
 }
 
-// Keys per wave: every unit gets ceil(c / quota) waves (at least one), with
-// quota = max(64, ceil(K / (W - U))) for K live keys over U units and W waves,
-// so the units never need more than W waves.  Called by all lanes of a wave.
-__device__ int64_t deal_quota(const DecodeParams& p, int ups, int lane) {
-  int64_t k = 0;
-  for (int b = lane; b < p.B; b += 64) k += sample_count(p, b);
+// Keys per pair of waves: every unit gets ceil(c / quota) pairs (at least
+// one), with quota = max(128, ceil(K / (P - U))) for K live keys over U units
+// and P = W / 2 pairs, so the units never need more than P pairs.  Called by
+// all lanes of a wave; c0 is the count of sample `lane` (0 beyond the batch).
+__device__ int64_t deal_quota(const DecodeParams& p, int ups, int lane, int c0) {
+  int64_t k = c0;
+  for (int b = lane + 64; b < p.B; b += 64) k += sample_count(p, b);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) k += __shfl_xor(k, m, 64);
   k *= ups;
   const int64_t units = (int64_t)p.B * ups;
-  const int64_t spare = (int64_t)p.waves - units;
+  const int64_t spare = (int64_t)(p.waves / 2) - units;
   if (spare <= 0) return INT64_MAX;
-  return max(kMinKeysPerWave, (k + spare - 1) / spare);
+  return max(2 * kMinKeysPerWave, (k + spare - 1) / spare);
 }
 
-__device__ __forceinline__ int waves_for(int c, int64_t quota) {
+__device__ __forceinline__ int pairs_for(int c, int64_t quota) {
   if (c <= 0 || quota >= c) return 1;
   return (int)(((int64_t)c + quota - 1) / quota);
 }
@@ -268,16 +291,17 @@ __device__ __forceinline__ int wave_scan(int v, int lane) {
   return v;
 }
 
-// Sample served by global wave gw and the first wave of that sample's units;
-// false when gw is beyond the waves in use.
-__device__ bool find_sample(const DecodeParams& p, int ups, int64_t quota, int gw, int lane,
+// Sample served by pair pr and the first pair of that sample's units; false
+// when pr is beyond the pairs in use.
+__device__ bool find_sample(const DecodeParams& p, int ups, int64_t quota, int pr, int lane, int c0,
                             int& b_out, int& first_out) {
   int base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int b = b0 + lane;
-    const int v = (b < p.B) ? waves_for(sample_count(p, b), quota) * ups : 0;
+    const int c = b0 == 0 ? c0 : (b < p.B ? sample_count(p, b) : 0);
+    const int v = (b < p.B) ? pairs_for(c, quota) * ups : 0;
     const int incl = wave_scan(v, lane);
-    const bool hit = b < p.B && gw >= base + incl - v && gw < base + incl;
+    const bool hit = b < p.B && pr >= base + incl - v && pr < base + incl;
     const unsigned long long mask = __ballot(hit);
     if (mask != 0ull) {
       const int src = __ffsll((long long)mask) - 1;
@@ -290,17 +314,19 @@ __device__ bool find_sample(const DecodeParams& p, int ups, int64_t quota, int g
   return false;
 }
 
-// First wave of sample b (all lanes of a wave call it).
-__device__ int sample_first_wave(const DecodeParams& p, int ups, int64_t quota, int b, int lane) {
+// First pair of sample b (all lanes of a wave call it).
+__device__ int sample_first_pair(const DecodeParams& p, int ups, int64_t quota, int b, int lane) {
   int acc = 0;
   for (int b0 = 0; b0 < b; b0 += 64) {
     const int s = b0 + lane;
-    acc += (s < b) ? waves_for(sample_count(p, s), quota) * ups : 0;
+    acc += (s < b) ? pairs_for(sample_count(p, s), quota) * ups : 0;
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m, 64);
   return acc;
 }
+
+__device__ __forceinline__ bool unit_direct(int c, int nb) { return nb == 1 && c <= kDirectKeys; }
 
 template <typename T>
 __device__ __forceinline__ float read_sink(const DecodeParams& p, int h, bool& has) {
@@ -322,8 +348,13 @@ __device__ __forceinline__ float final_scale(float m, float l, bool has_sink, fl
   return fast_exp2(m - m2) / den;
 }
 
-// Calls f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>) in order
-// while f returns true.
+// Calls f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>) in order.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+
+// As static_for, while f returns true.
 template <typename F, int... Is>
 __device__ __forceinline__ void static_for_while(F&& f, std::integer_sequence<int, Is...>) {
   bool go = true;
@@ -335,37 +366,70 @@ __device__ __forceinline__ void static_for_while(F&& f, std::integer_sequence<in
 constexpr int kSoftcap = 1, kExtras = 2;
 
 template <typename T, int HP, int FEAT>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
-  using Tile = DecTile<T, HP>;
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
+  // the bias/mask/qk variant keeps one buffer less (more live state per score)
+  constexpr int R = (FEAT & kExtras) ? (Ring<T, HP>::value > 1 ? Ring<T, HP>::value - 1 : 1)
+                                     : Ring<T, HP>::value;
+  using Tile = DecTile<T, HP, R>;
   using Q4 = Quad<T>;
   using QT = typename Q4::type;
-  constexpr int NQ = HP / 16, NH = NQ / 2, R = Tile::R;
+  constexpr int NQ = HP / 16, NH = NQ / 2;
+  constexpr int RS = HP + 4;  // partial record: m, l, -, -, o[HP]
+  __shared__ int s_claim[kPairsPerGroup];
+  __shared__ __attribute__((aligned(16))) float s_part[kPartFloats];
 
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int jp = wave % kPairsPerGroup;      // pair of this wave (waves jp, jp + 4 share a SIMD)
+  const int younger = wave / kPairsPerGroup;
+  const int pr = blockIdx.x * kPairsPerGroup + jp;
+  if (tid < kPairsPerGroup) s_claim[tid] = 0;
+  __syncthreads();
+
   const int H = p.H;
   const int g = p.N / p.kvN;
   const int hg = p.head_groups;
   const int ups = p.kvN * hg;
 
-  // ---- which unit and which run of its keys ---------------------------------
-  const int64_t quota = deal_quota(p, ups, lane);
-  int b, first;
-  if (!find_sample(p, ups, quota, gw, lane, b, first)) return;  // idle wave
-  int n, newrow, kstart;
-  sample_keys(p, b, n, newrow, kstart);
-  const int c = max(n - kstart, 0);
-  const int wb = waves_for(c, quota);
-  const int local = gw - first;
-  const int ui = local / wb, part = local % wb;
+  // ---- which unit and which run of its keys (the same for both waves) -------
+  // lane i reads the length of sample i once; the deal and this pair's sample
+  // take it from there
+  int n_l = 0, newrow_l = -1, kstart_l = 0;
+  if (lane < p.B) sample_keys(p, lane, n_l, newrow_l, kstart_l);
+  const int64_t quota = deal_quota(p, ups, lane, max(n_l - kstart_l, 0));
+  int b = 0, first = 0;
+  const bool live = find_sample(p, ups, quota, pr, lane, max(n_l - kstart_l, 0), b, first);
+  int n = 0, newrow = -1, kstart = 0;
+  if (b < 64) {
+    n = __shfl(n_l, b, 64);
+    newrow = __shfl(newrow_l, b, 64);
+    kstart = __shfl(kstart_l, b, 64);
+  } else {
+    sample_keys(p, b, n, newrow, kstart);
+  }
+  const int c = live ? max(n - kstart, 0) : 0;
+  const int nb = pairs_for(c, quota);
+  const int local = pr - first;
+  const int ui = live ? local / nb : 0;
+  const int kp = live ? local % nb : 0;  // pair within the unit
+  const bool direct = unit_direct(c, nb);
   const int kvh = ui / hg, hgrp = ui % hg;
   const int h0 = kvh * g + hgrp * 16;
   const int nh = min(16, g - hgrp * 16);
-  const int j_begin = kstart + (int)((int64_t)c * part / wb);
-  const int j_end = kstart + (int)((int64_t)c * (part + 1) / wb);
-  const int nsub = (j_end - j_begin + 15) / 16;
-  const int last = j_end - 1;
-  const bool append = newrow >= j_begin && newrow < j_end;
+  const int lo = kstart + (int)((int64_t)c * kp / nb);
+  const int len = kstart + (int)((int64_t)c * (kp + 1) / nb) - lo;
+  // chunks of the run: chunk ch holds keys [chunk_lo(ch), chunk_lo(ch + 1))
+  // each pair owns a fixed slice of the LDS records: chunk ch, head hj at
+  // pair_part + (ch * nh + hj) * RS (pairs of one group may differ in nh)
+  float* pair_part = s_part + jp * (kPartFloats / kPairsPerGroup);
+  const int nch_cap = max(1, min(kMaxChunks, kPartFloats / kPairsPerGroup / (nh * RS)));
+  // chunks of csz keys (a multiple of 16, at least 32); the last may be short
+  const int csz = len > 0 ? max(32, (len + nch_cap * 16 - 1) / (nch_cap * 16) * 16) : 32;
+  const int nch = (len + csz - 1) / csz;
+  // the new token's row is the unit's last key: the last chunk of its last
+  // pair, kept for the older wave, which appends the row before reading it
+  const bool append = live && newrow >= lo && newrow < lo + len;
+  const bool appender = append && !younger;
+  const int claimable = nch - (append ? 1 : 0);
 
   T* kb = static_cast<T*>(p.kc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
   T* vb = static_cast<T*>(p.vc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
@@ -380,10 +444,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
   // ---- the query: RMSNorm and rotary in registers ------------------------------
   // x[qi][e] = query element quad_dim(qi, g4) + e of head h0 + hh.  With H
   // equal to the padded size both members of a rotary pair (d, d + H/2) are
-  // quads qi and qi + NQ/2 of the same lane and the set-up is split: its
-  // loads go out before the first key/value loads, its arithmetic runs while
-  // those are in flight.  Other head sizes load the partner quads and finish
-  // the set-up before streaming starts.
+  // quads qi and qi + NQ/2 of the same lane, and the loads of the query, the
+  // rotary rows and the appended row all go out together; other head sizes
+  // load the partner quads.
   const int hh = lane & 15, g4 = lane >> 4;
   const T* qrow = static_cast<const T*>(p.q) + ((int64_t)b * p.N + h0 + min(hh, nh - 1)) * H;
   const T* qw = static_cast<const T*>(p.q_norm);
@@ -474,6 +537,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
     }
   }
   auto do_append = [&]() {
+    pin(ak);
+    pin(av);
+    pin(aw);
+    pin(ac);
+    pin(as);
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = to_f32(ak[e]);
@@ -499,29 +567,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
       Q4::store(kb + (int64_t)newrow * H + ad, y);
       Q4::store_raw(vb + (int64_t)newrow * H + ad, av);
     }
-    // the row is read back by other lanes of this wave: order the stores
-    // before those loads (no instruction is needed within one wave)
+    // The row is read back by other lanes of this wave: order the stores
+    // before those loads (no instruction is needed within one wave).  The
+    // stores are also retired here: loads and stores share one counter, and
+    // a store left pending past the join would make every later wait of the
+    // other waves a full drain.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   };
 
-  // ---- start streaming --------------------------------------------------------
-  auto jof = [&](int k) { return j_begin + 16 * k; };
-  const bool append_early = append && (newrow - j_begin) / 16 < R - 1;
-  if (append_early) do_append();
+  // ---- finish the query (and the append) before streaming --------------------
+  // The query and rotary rows are isolated lines: issued behind the key/value
+  // stream of the whole grid they would wait for most of it, so every wave
+  // completes them while the memory system is still idle.
+  if (appender) do_append();
   Tile tile;
   tile.init();
-  static_for_while(
-      [&](auto rt) -> bool {
-        constexpr int r = decltype(rt)::value;
-        if (r >= nsub) return false;
-        tile.template load_kv<r>(kb, vb, jof(r), last, H, lane);
-        return true;
-      },
-      std::make_integer_sequence<int, R - 1>{});
-  if (append && !append_early) do_append();
-
   if (same_lane_pairs) {
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi)
@@ -556,7 +619,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
 
   float m = kNegInf, l = 0.f;
   // Score transform, online softmax and PV for the sub-tile held in BUF.
-  auto process = [&](auto buf_tag, int j0) {
+  auto process = [&](auto buf_tag, int j0, int j_end) {
     constexpr int BUF = decltype(buf_tag)::value;
     const float4v sc = tile.template scores<BUF>();
     mfma_result_fence();
@@ -598,48 +661,112 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
     tile.template pv<BUF>(pr, ident);
   };
 
-  // The ring: sub-tile k lives in buffer k % R; the load of sub-tile k + R - 1
-  // is issued before sub-tile k is computed.
-  for (int k = 0; k < nsub; k += R) {
-    static_for_while(
-        [&](auto rt) -> bool {
+  // ---- streaming: chunks claimed by the two waves of the pair ----------------
+  // Chunk sub-tiles go through a ring of R register buffers; the load of the
+  // sub-tile R - 1 places ahead is issued before a sub-tile is computed, and
+  // the next chunk is claimed when the loads reach the end of the current one.
+  // Loads are issued on every step (past the end they re-read a valid row), so
+  // every path between a load and its use issues the same loads.
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_claim[jp], 1);
+    v = __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
+    return v < claimable ? v : nch;
+  };
+  // next load: chunk lc, its keys [ca, ce), sub-tile ls of ns
+  int lc = nch, ls = 0, ca = 0, ce = 0, ns = 0;
+  auto enter = [&](int ch) {
+    lc = ch;
+    ls = 0;
+    ca = lo + ch * csz;
+    ce = min(ca + csz, lo + len);
+    ns = (ce - ca + 15) / 16;
+  };
+  if (live) enter(appender ? nch - 1 : claim());
+  int b_j0[R], b_end[R], b_ch[R];
+  bool b_last[R];
+  auto next_load = [&](auto rt) {
+    constexpr int r = decltype(rt)::value;
+    if (lc < nch) {
+      b_j0[r] = ca + 16 * ls;
+      b_end[r] = ce;
+      b_ch[r] = lc;
+      b_last[r] = ls == ns - 1;
+      if (++ls == ns) enter(claim());
+    } else {
+      b_j0[r] = kstart;
+      b_end[r] = kstart + 1;
+      b_ch[r] = -1;
+      b_last[r] = false;
+    }
+    tile.template load_kv<r>(kb, vb, b_j0[r], b_end[r] - 1, H, lane);
+  };
+  // the chunk's (m, l, o) into its LDS record; the state restarts
+  auto flush = [&](int ch) {
+    mfma_result_fence();
+    const float lt = l + shfl_xor(l, 16) + shfl_xor(l, 32) + shfl_xor(shfl_xor(l, 16), 32);
+    if (head_ok) {
+      float* row = pair_part + (ch * nh + hh) * RS;
+      if (g4 == 0) *reinterpret_cast<float2v*>(row) = float2v{m, lt};
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) {
+        const int d = Tile::quad_dim(qi, g4);
+        if (d < H) *reinterpret_cast<float4v*>(row + 4 + d) = tile.o[qi];
+      }
+    }
+    m = kNegInf;
+    l = 0.f;
+    tile.init();
+  };
+  static_for(next_load, std::make_integer_sequence<int, R - 1>{});
+  bool go = live;
+  while (go) {
+    static_for(
+        [&](auto rt) {
           constexpr int r = decltype(rt)::value;
-          const int kk = k + r;
-          if (kk >= nsub) return false;
-          if (kk + R - 1 < nsub)
-            tile.template load_kv<(r + R - 1) % R>(kb, vb, jof(kk + R - 1), last, H, lane);
-          process(std::integral_constant<int, r>{}, jof(kk));
-          return true;
+          next_load(std::integral_constant<int, (r + R - 1) % R>{});
+          if (go && b_ch[r] >= 0) {
+            process(std::integral_constant<int, r>{}, b_j0[r], b_end[r]);
+            if (b_last[r]) flush(b_ch[r]);
+          } else {
+            go = false;
+          }
         },
         std::make_integer_sequence<int, R>{});
   }
   mfma_result_fence();
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
-  if (!head_ok) return;
+  __syncthreads();
 
-  // ---- output (single wave per unit) or partial ---------------------------------
-  if (wb == 1) {
-    bool has;
-    const float sg = read_sink<T>(p, h, has);
-    const float inv = final_scale(m, l, has, sg);
-    T* orow = static_cast<T*>(p.out) + ((int64_t)b * p.N + h) * H;
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-      const int d = Tile::quad_dim(qi, g4);
-      if (d < H) {
-        const float v[4] = {tile.o[qi][0] * inv, tile.o[qi][1] * inv, tile.o[qi][2] * inv,
-                            tile.o[qi][3] * inv};
-        Q4::store(orow + d, v);
-      }
+  // ---- merge the pair's chunks in chunk order: output or the pair's partial --
+  if (!live) return;
+  const int t = younger * 64 + lane;
+  constexpr int NQD = HP / 4;
+  for (int e = t; e < nh * NQD; e += 2 * 64) {
+    const int hj = e / NQD, d = 4 * (e % NQD);
+    if (d >= H) continue;
+    const float* base = pair_part + hj * RS;
+    float M = kNegInf;
+    for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, base[ch * nh * RS]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float L = 0.f;
+    float4v O = {0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < nch; ++ch) {
+      const float* row = base + ch * nh * RS;
+      const float f = fast_exp2(row[0] - Mu);
+      L += row[1] * f;
+      O += *reinterpret_cast<const float4v*>(row + 4 + d) * f;
     }
-  } else {
-    float* rec = p.part + ((int64_t)gw * p.hpw + hh) * (HP + 4);
-    if (g4 == 0) *reinterpret_cast<float2v*>(rec) = float2v{m, l};
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-      const int d = Tile::quad_dim(qi, g4);
-      if (d < H) *reinterpret_cast<float4v*>(rec + 4 + d) = tile.o[qi];
+    const int hq = h0 + hj;
+    if (direct) {
+      bool has;
+      const float sg = read_sink<T>(p, hq, has);
+      const float inv = final_scale(M, L, has, sg);
+      const float v[4] = {O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
+      Q4::store(static_cast<T*>(p.out) + ((int64_t)b * p.N + hq) * H + d, v);
+    } else {
+      float* rec = p.part + ((int64_t)pr * p.hpw + hj) * RS;
+      if (d == 0) *reinterpret_cast<float2v*>(rec) = float2v{M, L};
+      *reinterpret_cast<float4v*>(rec + 4 + d) = O;
     }
   }
 }
@@ -656,13 +783,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = p.N / p.kvN, hg = p.head_groups, ups = p.kvN * hg;
-  const int64_t quota = deal_quota(p, ups, lane);
-  const int wb = waves_for(sample_count(p, b), quota);
-  if (wb <= 1) return;  // written directly
-  const int first = sample_first_wave(p, ups, quota, b, lane);
+  const int64_t quota = deal_quota(p, ups, lane, lane < p.B ? sample_count(p, lane) : 0);
+  const int c = sample_count(p, b);
+  const int nb = pairs_for(c, quota);
+  if (unit_direct(c, nb)) return;  // written directly
+  const int first = sample_first_pair(p, ups, quota, b, lane);
   const int kvh = h / g, hgrp = (h % g) / 16, hh = (h % g) % 16;
-  const int w0 = first + (kvh * hg + hgrp) * wb;
-  auto rec = [&](int i) { return p.part + ((int64_t)(w0 + i) * p.hpw + hh) * (HP + 4); };
+  const int pair0 = first + (kvh * hg + hgrp) * nb;
+  const int wb = nb;  // one partial per pair of the unit
+  auto rec = [&](int i) { return p.part + ((int64_t)(pair0 + i) * p.hpw + hh) * (HP + 4); };
 
   // pass 1: M = max m_i, L = sum l_i 2^(m_i - M)
   float M = kNegInf, L = 0.f;
@@ -756,10 +885,9 @@ hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s)
   return launch_decode_t<float, 256>(p, s);
 }
 
-// Needed only when some unit may be served by more than one wave, i.e. when
-// the grid has more waves than units.
+// Merges the units that more than one wave served (the others return at once).
 hipError_t launch_decode_combine(DType dt, int hp, const DecodeParams& p, hipStream_t s) {
-  if (p.B == 0 || (int64_t)p.waves <= (int64_t)p.B * p.kvN * p.head_groups) return hipSuccess;
+  if (p.B == 0) return hipSuccess;
   if (dt == DType::F16) {
     if (hp == 64) return launch_combine_t<f16, 64>(p, s);
     if (hp == 128) return launch_combine_t<f16, 128>(p, s);
