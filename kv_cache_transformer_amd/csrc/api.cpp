@@ -281,8 +281,6 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     P.waves = decode_waves(units, std::min<int64_t>(total, P.cap));
     if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode: too many (sample, head) units");
     P.ws_part = align256((size_t)(P.waves / 2) * P.hpw * (P.HP + 4) * sizeof(float));
-  } else if (P.q_transform) {
-    P.ws_q = align256((size_t)P.B * P.S * P.N * P.H * esz);
   }
   P.ws_total = P.ws_q + P.ws_part;
   return KVATTN_OK;
@@ -353,7 +351,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   pp.v = in[GQA_IN_VALUE].data;
   pp.q_stride = (int64_t)P.N * P.H;
   pp.k_stride = pp.v_stride = (int64_t)P.kvN * P.H;
-  pp.q_out = P.q_transform ? ws : nullptr;
+  pp.q_out = nullptr;  // the flash kernel prepares the queries as it loads them
   pp.kc = ck.data;
   pp.vc = cv.data;
   pp.q_norm = in[GQA_IN_Q_NORM_WEIGHT].data;
@@ -368,13 +366,20 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   pp.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
   pp.pos_mode = P.has_past ? 1 : 0;
   pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
-  pp.write_q = P.q_transform;
+  pp.write_q = 0;
   pp.write_kv = 1;
   CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
                    "prep launch"));
 
   FlashParams f{};
-  f.q = P.q_transform ? ws : in[GQA_IN_QUERY].data;
+  f.q = in[GQA_IN_QUERY].data;
+  f.q_norm = pp.q_norm;
+  f.eps = a->qk_norm_epsilon;
+  f.cos = pp.cos;
+  f.sin = pp.sin;
+  f.rot_half = pp.rot_half;
+  f.rot_rows = pp.rot_rows;
+  f.interleaved = 0;
   f.q_s = (int64_t)P.N * P.H;
   f.q_b = f.q_s * P.S;
   f.q_h = P.H;
@@ -643,7 +648,7 @@ int sparse_validate(const sparse_attrs* a, const kvattn_tensor* in, int n_in, in
   if ((has(out[SPARSE_OUT_PRESENT_KEY]) && out[SPARSE_OUT_PRESENT_KEY].data != pk.data) ||
       (has(out[SPARSE_OUT_PRESENT_VALUE]) && out[SPARSE_OUT_PRESENT_VALUE].data != pv.data))
     return fail(KVATTN_ERR_INVALID_ARG, "the present caches are the past buffers updated in place");
-  P.ws_q = P.rotary ? align256((size_t)P.B * P.S * P.N * P.H * elem_size(dt)) : 0;
+  P.ws_q = 0;  // the flash kernel rotates the queries as it loads them
   P.ws_total = P.ws_q;
   return KVATTN_OK;
 }
@@ -665,7 +670,7 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
     pp.v = in[SPARSE_IN_VALUE].data;
     pp.k_stride = pp.v_stride = (int64_t)P.kvN * P.H;
   }
-  pp.q_out = P.rotary ? ws : nullptr;
+  pp.q_out = nullptr;
   pp.kc = in[SPARSE_IN_PAST_KEY].data;
   pp.vc = in[SPARSE_IN_PAST_VALUE].data;
   if (P.rotary) {
@@ -678,19 +683,19 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
   pp.lens = static_cast<const int32_t*>(in[SPARSE_IN_KEY_TOTAL_SEQUENCE_LENGTHS].data);
   pp.pos_mode = 0;
   pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
-  pp.write_q = P.rotary;
+  pp.write_q = 0;
   pp.write_kv = 1;
   CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
                    "prep launch"));
 
   FlashParams f{};
-  if (P.rotary) {
-    f.q = ws;
-    f.q_s = (int64_t)P.N * P.H;
-  } else {
-    f.q = in[SPARSE_IN_QUERY].data;
-    f.q_s = width;
-  }
+  f.q = in[SPARSE_IN_QUERY].data;
+  f.q_s = width;
+  f.cos = pp.cos;
+  f.sin = pp.sin;
+  f.rot_half = pp.rot_half;
+  f.rot_rows = pp.rot_rows;
+  f.interleaved = pp.interleaved;
   f.q_b = f.q_s * P.S;
   f.q_h = P.H;
   f.kc = in[SPARSE_IN_PAST_KEY].data;

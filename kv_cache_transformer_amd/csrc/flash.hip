@@ -49,11 +49,15 @@ template <typename T, int HP> struct FlashMma;
 
 // ------------------------------- f16 ----------------------------------------
 template <int HP> struct FlashMma<f16, HP> {
-  static constexpr int KS = HP + 8;    // K tile row stride (elements)
-  static constexpr int VS = HP + 16;   // V tile row stride (elements)
+  static constexpr int KS = HP + 8;    // K tile row stride (elements): rows 4 banks apart
+  // V tile row stride (elements): a multiple of 128 plus 32, so that the two
+  // 16-lane groups of a transposing read hit disjoint bank halves
+  static constexpr int VS = HP <= 128 ? 160 : 288;
   static constexpr int NS = HP / 16;   // 16-dim k-steps of the score MFMA
   static constexpr int ND = HP / 32;   // 32-dim output blocks
   static constexpr int CH = 8;         // elements per 16-byte chunk
+  static constexpr int NE = HP / 2;    // query elements per lane
+  static constexpr bool kPairInLane = true;  // interleaved rotary pairs share a lane
   half8v qf[NS];
   float16v o[ND];
 
@@ -61,13 +65,25 @@ template <int HP> struct FlashMma<f16, HP> {
 #pragma unroll
     for (int i = 0; i < ND; ++i) o[i] = float16v{};
   }
-  // lane l: Q[q = l%32][16s + 8(l/32) + i]
-  __device__ void load_q(const f16* qrow, int H, int lane) {
-    const int hi = lane >> 5;
+  // lane l holds Q[q = l%32][edim(e, l/32)], e < NE
+  __device__ static int edim(int e, int h) { return 16 * (e >> 3) + 8 * h + (e & 7); }
+  __device__ static void load_raw(const f16* qrow, int H, int lane, float (&x)[NE]) {
+    const int h = lane >> 5;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      int d = 16 * s + 8 * hi;
-      qf[s] = (d < H) ? load_half8(qrow + d) : half8v{};
+      const int d = 16 * s + 8 * h;
+      const half8v v = (d < H) ? load_half8(qrow + d) : half8v{};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[8 * s + i] = (float)v[i];
+    }
+  }
+  __device__ void set_q(const float (&x)[NE]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      half8v v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (f16)x[8 * s + i];
+      qf[s] = v;
     }
   }
   __device__ float16v qk_block(const f16* Kt, int kb, int lane) const {
@@ -109,6 +125,8 @@ template <int HP> struct FlashMma<float, HP> {
   static constexpr int NS = HP / 2;    // 2-dim k-steps of the score MFMA
   static constexpr int ND = HP / 32;
   static constexpr int CH = 4;
+  static constexpr int NE = HP / 2;
+  static constexpr bool kPairInLane = false;  // interleaved pairs: lanes l and l ^ 32
   float qf[NS];
   float16v o[ND];
 
@@ -116,14 +134,19 @@ template <int HP> struct FlashMma<float, HP> {
 #pragma unroll
     for (int i = 0; i < ND; ++i) o[i] = float16v{};
   }
-  // lane l: Q[q = l%32][2s + l/32]
-  __device__ void load_q(const float* qrow, int H, int lane) {
-    const int hi = lane >> 5;
+  // lane l holds Q[q = l%32][edim(e, l/32)] = Q[q][2e + l/32]
+  __device__ static int edim(int e, int h) { return 2 * e + h; }
+  __device__ static void load_raw(const float* qrow, int H, int lane, float (&x)[NE]) {
+    const int h = lane >> 5;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      int d = 2 * s + hi;
-      qf[s] = (d < H) ? qrow[d] : 0.f;
+      const int d = 2 * s + h;
+      x[s] = (d < H) ? qrow[d] : 0.f;
     }
+  }
+  __device__ void set_q(const float (&x)[NE]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = x[s];
   }
   __device__ float16v qk_block(const float* Kt, int kb, int lane) const {
     float16v acc = {};
@@ -150,8 +173,94 @@ struct TileRange {
   int start, lim;
 };
 
-template <typename T, int HP, int BN, int MODE, int NW>
-__global__ __launch_bounds__(64 * NW) void flash_kernel(FlashParams p) {
+// The query row of this lane as the score MFMA operand: per-head RMSNorm
+// (GroupQueryAttention page, Inputs table: q_norm_weight, before rotary),
+// rotary at position pos (GroupQueryAttention page, Inputs table: cos/sin_cache;
+// SparseAttention page, Attributes table: rotary_interleaved; the first
+// 2 * rot_half dims rotate), then the factor qscale that turns the scores
+// into the exponent the softmax needs.  Lanes l and l ^ 32 share a row.
+template <typename Mma, typename T>
+__device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& p, float qscale,
+                           int lane) {
+  constexpr int NE = Mma::NE;
+  const int H = p.H, h = lane >> 5;
+  float x[NE];
+  Mma::load_raw(qrow, H, lane, x);
+  const T* qn = static_cast<const T*>(p.q_norm);
+  float rn = 1.f;
+  if (qn != nullptr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) ss += x[e] * x[e];
+    ss += shfl_xor(ss, 32);
+    rn = rsqrtf(ss / (float)H + p.eps);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int d = Mma::edim(e, h);
+      if (d < H) x[e] *= rn * to_f32(qn[d]);
+    }
+  }
+  const T* cs = static_cast<const T*>(p.cos);
+  if (cs != nullptr) {
+    const T* sn = static_cast<const T*>(p.sin);
+    const int rh = p.rot_half;
+    const int prow = min(max(pos, 0), p.rot_rows - 1);
+    const T* cr = cs + (int64_t)prow * rh;
+    const T* sr = sn + (int64_t)prow * rh;
+    if (!p.interleaved && 2 * rh == H && H == Mma::NE * 2) {
+      // both members of every pair (d, d + H/2) are elements e, e + NE/2 of this lane
+#pragma unroll
+      for (int e = 0; e < NE / 2; ++e) {
+        const int i = Mma::edim(e, h);
+        const float c = to_f32(cr[i]), s = to_f32(sr[i]);
+        const float a = x[e], z = x[e + NE / 2];
+        x[e] = a * c - z * s;
+        x[e + NE / 2] = z * c + a * s;
+      }
+    } else if (p.interleaved) {
+      // pairs (2i, 2i + 1): the partner is element e ^ 1 (f16) or lane l ^ 32 (f32)
+      float y[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int d = Mma::edim(e, h);
+        float z;
+        if (Mma::kPairInLane) z = x[e ^ 1];
+        else z = shfl_xor(x[e], 32);
+        y[e] = x[e];
+        if (d < 2 * rh) {
+          const float c = to_f32(cr[d >> 1]), s = to_f32(sr[d >> 1]);
+          y[e] = (d & 1) ? x[e] * c + z * s : x[e] * c - z * s;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < NE; ++e) x[e] = y[e];
+    } else {
+      // general NeoX width: the partner comes from memory (normed the same way)
+      float y[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int d = Mma::edim(e, h);
+        y[e] = x[e];
+        if (d < 2 * rh && d < H) {
+          const int pd = d < rh ? d + rh : d - rh;
+          const int i = d < rh ? d : d - rh;
+          float z = to_f32(qrow[pd]);
+          if (qn != nullptr) z *= rn * to_f32(qn[pd]);
+          const float c = to_f32(cr[i]), s = to_f32(sr[i]);
+          y[e] = d < rh ? x[e] * c - z * s : x[e] * c + z * s;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < NE; ++e) x[e] = y[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) x[e] *= qscale;
+  mma.set_q(x);
+}
+
+template <typename T, int HP, int BN, int MODE, int NW, bool SOFTCAP>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash_kernel(FlashParams p) {
   using Mma = FlashMma<T, HP>;
   constexpr int KS = Mma::KS, VS = Mma::VS, CH = Mma::CH;
   constexpr int TILE = BN * (KS + VS);
@@ -249,12 +358,19 @@ __global__ __launch_bounds__(64 * NW) void flash_kernel(FlashParams p) {
   mma.init();
   const int qrow = wrow0 + (lane & 31);
   const bool row_ok = wave_rows && qrow < wg_rows_end;
+  // The scores come out of the MFMA already as the softmax exponent
+  // (log2 domain): the query carries scale * log2(e), or, with a softcap c,
+  // 2 * log2(e) * scale / c, the argument of the exp2 inside tanh.
+  const float cap = p.softcap;
+  const bool use_cap = SOFTCAP && cap > 0.f;
+  const float qscale = use_cap ? 2.f * kLog2e * p.scale / cap : kLog2e * p.scale;
+  const float capA = cap * kLog2e, capB = 2.f * cap * kLog2e;
   {
     const int rr = min(qrow, nrows - 1);
     const T* qp = (MODE == kVarlen)
                       ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
                       : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
-    mma.load_q(qp, H, lane);
+    prep_query(mma, qp, past + rr, p, qscale, lane);
   }
   const int pos = past + qrow;  // absolute position of this lane's query
 
@@ -306,8 +422,6 @@ __global__ __launch_bounds__(64 * NW) void flash_kernel(FlashParams p) {
     }
   };
 
-  const float scale = p.scale;
-  const float cap = p.softcap, inv_cap = cap > 0.f ? 1.f / cap : 0.f;
   const T* bias = static_cast<const T*>(p.bias);
   int64_t bias_row = 0;
   int pad_q = 0;
@@ -341,43 +455,59 @@ __global__ __launch_bounds__(64 * NW) void flash_kernel(FlashParams p) {
     if (wave_rows) {
       const T* Kt = lds + buf * TILE;
       const T* Vt = Kt + BN * KS;
+      // a tile visible to every row of the workgroup needs no mask
+      bool full = r.lim == r.start + BN;
+      if (MODE == kDense && p.causal)
+        full = full && r.start + BN - 1 <= pmin && (p.window < 0 || r.start >= pmax - p.window);
+      else if (MODE == kCsr)
+        full = full && r.start + BN - 1 <= pmin;
       float x[BN / 32][16];
-      float tmax = kNegInf;
       float16v sacc[BN / 32];
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) sacc[blk] = mma.qk_block(Kt, 32 * blk, lane);
       mfma_result_fence();
+      // softcap: c * log2(e) * tanh(y) = A - B / (2^u + 1) with u = 2 * log2(e) * y
 #pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk) {
-        const float16v s = sacc[blk];
+      for (int blk = 0; blk < BN / 32; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          bool ok = row_ok && key < r.lim;
-          if (MODE == kDense) {
-            if (p.causal) {
-              ok = ok && key <= pos;
-              if (p.window >= 0) ok = ok && key >= pos - p.window;
-            }
-          } else if (MODE == kCsr) {
-            ok = ok && key <= pos;
-          }
-          float v = s[i] * scale;
-          if (cap > 0.f) v = softcap_apply(v, cap, inv_cap);
-          if (bias != nullptr && ok) {
-            if (MODE == kVarlen) {
-              int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
-              pad_k = min(max(pad_k, 0), p.pad_seq - 1);
-              v += to_f32(bias[bias_row + pad_k]);
-            } else if (key < p.bias_cols) {
-              v += to_f32(bias[bias_row + key]);
-            }
-          }
-          v = ok ? v * kLog2e : kNegInf;
+          float v = sacc[blk][i];
+          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
           x[blk][i] = v;
-          tmax = fmaxf(tmax, v);
         }
+      if (bias != nullptr || !full) {
+#pragma unroll
+        for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            bool ok = row_ok && key < r.lim;
+            if (MODE == kDense) {
+              if (p.causal) {
+                ok = ok && key <= pos;
+                if (p.window >= 0) ok = ok && key >= pos - p.window;
+              }
+            } else if (MODE == kCsr) {
+              ok = ok && key <= pos;
+            }
+            float v = x[blk][i];
+            if (bias != nullptr && ok) {
+              if (MODE == kVarlen) {
+                int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
+                pad_k = min(max(pad_k, 0), p.pad_seq - 1);
+                v += kLog2e * to_f32(bias[bias_row + pad_k]);
+              } else if (key < p.bias_cols) {
+                v += kLog2e * to_f32(bias[bias_row + key]);
+              }
+            }
+            x[blk][i] = ok ? v : kNegInf;
+          }
       }
+      float tmax = kNegInf;
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[blk][i]);
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
       const float mnew = fmaxf(m, tmax);
       const float muse = (mnew == kNegInf) ? 0.f : mnew;
@@ -393,8 +523,10 @@ __global__ __launch_bounds__(64 * NW) void flash_kernel(FlashParams p) {
           psum += e;
         }
       lsum = lsum * alpha + psum;
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
+        for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
+      }
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
     }
@@ -442,11 +574,11 @@ __global__ __launch_bounds__(64 * NW) void flash_kernel(FlashParams p) {
     }
 }
 
-template <typename T, int HP, int BN, int MODE>
+template <typename T, int HP, int BN, int MODE, bool SOFTCAP = false>
 hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
-  if (nw == 4) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 4>), grid, dim3(256), 0, s, p);
-  else if (nw == 2) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 2>), grid, dim3(128), 0, s, p);
-  else hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 1>), grid, dim3(64), 0, s, p);
+  if (nw == 4) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 4, SOFTCAP>), grid, dim3(256), 0, s, p);
+  else if (nw == 2) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 2, SOFTCAP>), grid, dim3(128), 0, s, p);
+  else hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 1, SOFTCAP>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -454,7 +586,8 @@ template <typename T, int HP, int BN>
 hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
   switch (p.mode) {
     case kDense:
-      return launch_mode<T, HP, BN, kDense>(p, grid, 4, s);
+      if (p.softcap > 0.f) return launch_mode<T, HP, BN, kDense, true>(p, grid, 4, s);
+      return launch_mode<T, HP, BN, kDense, false>(p, grid, 4, s);
     case kCsr: {
       int nw = (p.rows_per_wg + 31) / 32;
       return launch_mode<T, HP, BN, kCsr>(p, grid, nw >= 4 ? 4 : (nw == 2 ? 2 : 1), s);

@@ -121,6 +121,15 @@ struct FlashParams {
   int rows_per_wg;          // query rows per workgroup
   int heads_per_wg;         // query heads per workgroup (GQA grouping)
   int mode;
+  // query preparation at load (dense and CSR modes): per-head RMSNorm with
+  // q_norm (or null), rotary of the first 2 * rot_half dims with the cos/sin
+  // tables (or null) at position past + row, NeoX pairs (i, i + rot_half) or
+  // interleaved pairs (2i, 2i + 1)
+  const void* q_norm;
+  float eps;
+  const void* cos;
+  const void* sin;
+  int rot_half, rot_rows, interleaved;
 };
 
 // ---------------------------------------------------------------------------

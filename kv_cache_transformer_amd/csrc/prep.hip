@@ -16,6 +16,8 @@
 // One workgroup (4 waves) per token; each wave transforms one head at a
 // time with its lanes spread over the head's dims.  The transformed head is
 // staged in LDS so that a lane can read its rotary partner.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kvattn_internal.hpp"
 
@@ -23,6 +25,18 @@ namespace kvattn {
 namespace {
 
 constexpr int kPrepThreads = 256;
+
+// 16 bytes of T as float (8 halves or 4 floats), and back
+__device__ __forceinline__ void load8_or_4(const f16* p, float (&x)[8]) { load8_f32<f16>(p, x); }
+__device__ __forceinline__ void load8_or_4(const float* p, float (&x)[4]) {
+  const float4v v = *reinterpret_cast<const float4v*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = v[i];
+}
+__device__ __forceinline__ void store8_or_4(f16* p, const float (&x)[8]) { store8_from_f32<f16>(p, x); }
+__device__ __forceinline__ void store8_or_4(float* p, const float (&x)[4]) {
+  *reinterpret_cast<float4v*>(p) = float4v{x[0], x[1], x[2], x[3]};
+}
 
 template <typename T>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
@@ -132,6 +146,96 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
   }
 }
 
+// Keys and values only, vectorised: every lane moves one 16-byte chunk of a
+// row and a group of H / CH lanes holds a whole head row, so the norm is a
+// sum over the group and the rotary partner (chunk +- rot_half / CH for
+// half-split pairs, the neighbouring element for interleaved pairs) comes
+// from a lane of the same group.  Used when rot_half is a multiple of CH (or
+// no rotary, or interleaved pairs); rows are (token, kv head) in order.
+template <typename T>
+__global__ __launch_bounds__(kPrepThreads) void prep_kv_kernel(PrepParams p) {
+  constexpr int CH = 16 / sizeof(T);
+  const int H = p.H;
+  const int lpr = H / CH;                    // lanes per head row (<= 64)
+  const int rows_per_wave = 64 / lpr;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane / lpr, j = lane % lpr;
+  const int64_t nrows = (int64_t)p.B * p.S * p.kvN;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  const int64_t wstride = (int64_t)gridDim.x * blockDim.x / 64;
+  const T* cs = static_cast<const T*>(p.cos);
+  const T* sn = static_cast<const T*>(p.sin);
+  const T* kw = static_cast<const T*>(p.k_norm);
+  const int rh = p.rot_half;
+  for (int64_t w = wave0; w * rows_per_wave < nrows; w += wstride) {
+    const int64_t row = w * rows_per_wave + grp;
+    const bool live = grp < rows_per_wave && row < nrows;
+    const int64_t rr = live ? row : 0;
+    const int64_t tok = rr / p.kvN;
+    const int kvh = (int)(rr % p.kvN);
+    const int b = (int)(tok / p.S), s = (int)(tok % p.S);
+    int past = 0;
+    if (p.pos_mode == 1) past = p.lens[b] + 1 - p.S;
+    else if (p.pos_mode == 2) past = p.lens[b] - p.S;
+    const int pos = past + s;
+    const bool row_ok = live && pos >= 0 && pos < p.cap;
+    const int d0 = CH * j;
+    const T* ksrc = static_cast<const T*>(p.k) + tok * p.k_stride + p.k_off + (int64_t)kvh * H + d0;
+    const T* vsrc = static_cast<const T*>(p.v) + tok * p.v_stride + p.v_off + (int64_t)kvh * H + d0;
+    const uint4v kraw = *reinterpret_cast<const uint4v*>(ksrc);
+    const uint4v vraw = *reinterpret_cast<const uint4v*>(vsrc);
+    const int64_t dst = (((int64_t)b * p.kvN + kvh) * p.cap + pos) * H + d0;
+    if (row_ok) *reinterpret_cast<uint4v*>(static_cast<T*>(p.vc) + dst) = vraw;
+    float x[CH];
+    load8_or_4(reinterpret_cast<const T*>(&kraw), x);
+    if (kw != nullptr) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < CH; ++e) ss += x[e] * x[e];
+      for (int m = 1; m < lpr; m <<= 1) ss += shfl_xor(ss, m);
+      const float r = rsqrtf(ss / (float)H + p.eps);
+      float wv[CH];
+      load8_or_4(kw + d0, wv);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) x[e] *= r * wv[e];
+    }
+    if (cs != nullptr) {
+      const int prow = min(max(pos, 0), p.rot_rows - 1);
+      float y[CH];
+      if (p.interleaved) {
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+          const int d = d0 + e;
+          y[e] = x[e];
+          if (d < 2 * rh) {
+            const float c = to_f32(cs[(int64_t)prow * rh + (d >> 1)]);
+            const float si = to_f32(sn[(int64_t)prow * rh + (d >> 1)]);
+            y[e] = (d & 1) ? x[e] * c + x[e ^ 1] * si : x[e] * c - x[e ^ 1] * si;
+          }
+        }
+      } else {
+        const int pj = (d0 < rh) ? j + rh / CH : j - rh / CH;  // partner lane in the group
+        const int src = grp * lpr + ((d0 < 2 * rh) ? pj : j);
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+          const float z = __shfl(x[e], src, 64);
+          const int d = d0 + e;
+          y[e] = x[e];
+          if (d < 2 * rh) {
+            const int i = d < rh ? d : d - rh;
+            const float c = to_f32(cs[(int64_t)prow * rh + i]);
+            const float si = to_f32(sn[(int64_t)prow * rh + i]);
+            y[e] = d < rh ? x[e] * c - z * si : x[e] * c + z * si;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < CH; ++e) x[e] = y[e];
+    }
+    if (row_ok) store8_or_4(static_cast<T*>(p.kc) + dst, x);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void copy_past_kernel(CopyPastParams p) {
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -155,6 +259,21 @@ __global__ __launch_bounds__(256) void copy_past_kernel(CopyPastParams p) {
 
 hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
   if (p.B * p.S == 0) return hipSuccess;
+  const int ch = dt == DType::F16 ? 8 : 4;
+  const int lpr = p.H / ch;  // lanes per row: a power of two (the norm sums by xor)
+  const bool vec_ok = !p.write_q && p.write_kv && p.H % ch == 0 && lpr <= 64 && (lpr & (lpr - 1)) == 0 &&
+                      (p.cos == nullptr || p.interleaved || p.rot_half % ch == 0);
+  if (vec_ok) {
+    const int64_t rows = (int64_t)p.B * p.S * p.kvN;
+    const int rows_per_wave = 64 / (p.H / ch);
+    const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
+    const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 8192);
+    if (dt == DType::F16)
+      hipLaunchKernelGGL(prep_kv_kernel<f16>, dim3((int)blocks), dim3(kPrepThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(prep_kv_kernel<float>, dim3((int)blocks), dim3(kPrepThreads), 0, s, p);
+    return hipGetLastError();
+  }
   dim3 grid(p.B * p.S);
   if (dt == DType::F16)
     hipLaunchKernelGGL(prep_kernel<f16>, grid, dim3(kPrepThreads), 0, s, p);
