@@ -167,6 +167,9 @@ template <int HP> struct FlashMma<float, HP> {
   }
 };
 
+// Slack of the running maximum (log2 domain): see the online softmax below.
+constexpr float kMaxSlack = 8.f;
+
 // Tile schedule of one workgroup: tile t covers keys [start, start + BN) of
 // which [start, lim) may be visible.
 struct TileRange {
@@ -272,7 +275,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash
   constexpr bool kPrefetch = CPT <= 16;
   __shared__ __attribute__((aligned(16))) T lds[2 * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (so that everything derived from it stays in scalar registers)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H;
   const int g = p.N / p.kvN;
   const int HW = p.heads_per_wg;
@@ -391,24 +396,40 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash
     const int row = ci / CPR, d = (ci % CPR) * CH;
     return isv ? base + BN * KS + row * VS + d : base + row * KS + d;
   };
+  // Prefetch path: thread tid moves chunks tid + u * nthreads, u < CPT; the
+  // first KU are K chunks, the rest V chunks, all at column d0 of rows
+  // row0 + RSTEP * (u % KU), so per tile only the first row moves.
+  constexpr int KU = (BN * CPR) / nthreads;   // K chunks per thread
+  constexpr int RSTEP = nthreads / CPR;
+  static_assert(!kPrefetch || (BN * CPR) % nthreads == 0, "whole K/V chunk rows per thread");
+  const int row0 = tid / CPR, d0 = (tid % CPR) * CH;
+  const bool zero_col = d0 >= H;  // columns beyond the head stay zero in LDS
+  const bool pad_cols = H < HP;   // uniform: only then can zero_col be true
+  const int kj = (int)p.k_j;      // row stride (elements); a slab of rows fits 32 bits
   uint4v stage[kPrefetch ? CPT : 1];
   auto load_tile = [&](int t) {
     const TileRange r = tile_range(t);
+    // uniform base at the tile's first row; per-thread 32-bit offsets
+    const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
+    const T* kt = kg + kv_base + (int64_t)r.start * p.k_j;
+    const T* vt = vg + kv_base + (int64_t)r.start * p.k_j;
 #pragma unroll
     for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
-      const int idx = tid + u * nthreads;
-      if (idx < 2 * BN * CPR) {
-        bool zero;
-        const T* src = chunk_src(r, idx, zero);
-        stage[u] = zero ? uint4v{0u, 0u, 0u, 0u} : *reinterpret_cast<const uint4v*>(src);
-      }
+      const int off = min(row0 + RSTEP * (u % KU), last) * kj + d0;
+      const T* src = (u < KU ? kt : vt) + off;
+      if (pad_cols)
+        stage[u] = zero_col ? uint4v{0u, 0u, 0u, 0u} : *reinterpret_cast<const uint4v*>(src);
+      else
+        stage[u] = *reinterpret_cast<const uint4v*>(src);
     }
   };
   auto store_tile = [&](int buf) {
+    T* base = lds + buf * TILE;
 #pragma unroll
     for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
-      const int idx = tid + u * nthreads;
-      if (idx < 2 * BN * CPR) *reinterpret_cast<uint4v*>(chunk_dst(buf, idx)) = stage[u];
+      const int row = row0 + RSTEP * (u % KU);
+      T* dst = u < KU ? base + row * KS + d0 : base + BN * KS + row * VS + d0;
+      *reinterpret_cast<uint4v*>(dst) = stage[u];
     }
   };
   // direct copy without holding a whole tile in registers (large tiles per thread)
@@ -509,10 +530,19 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash
 #pragma unroll
         for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[blk][i]);
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m, tmax);
-      const float muse = (mnew == kNegInf) ? 0.f : mnew;
-      const float alpha = fast_exp2(m - muse);
-      m = mnew;
+      // The running max m moves only when a score exceeds it by more than
+      // kMaxSlack (log2 units): probabilities then stay <= 2^kMaxSlack, exact
+      // enough in fp16 and far from overflow, and O is rescaled rarely.
+      const bool grow = tmax > m + kMaxSlack;
+      if (__any(grow)) {
+        const float mnew = grow ? tmax : m;
+        const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
+      }
+      const float muse = (m == kNegInf) ? 0.f : m;
       float psum = 0.f;
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk)
@@ -522,11 +552,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash
           x[blk][i] = e;
           psum += e;
         }
-      lsum = lsum * alpha + psum;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
-      }
+      lsum += psum;
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
     }
