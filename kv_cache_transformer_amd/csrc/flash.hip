@@ -262,8 +262,17 @@ __device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& 
   mma.set_q(x);
 }
 
+// Waves per SIMD the launch bounds ask for (the second launch-bounds value):
+// two where LDS lets that many workgroups share a CU.  4-wave groups
+// double-buffer their K/V tiles (two groups per CU); smaller groups keep one
+// buffer so that four of them fit.
+template <int NW, int HP> struct FlashOcc {
+  static constexpr int nbuf = NW >= 4 ? 2 : 1;
+  static constexpr int waves_per_simd = (HP <= 128 && NW >= 2) ? 2 : 1;
+};
+
 template <typename T, int HP, int BN, int MODE, int NW, bool SOFTCAP>
-__global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash_kernel(FlashParams p) {
+__global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void flash_kernel(FlashParams p) {
   using Mma = FlashMma<T, HP>;
   constexpr int KS = Mma::KS, VS = Mma::VS, CH = Mma::CH;
   constexpr int TILE = BN * (KS + VS);
@@ -273,7 +282,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash
   // registers only when that stays small
   constexpr int CPT = (2 * BN * CPR + nthreads - 1) / nthreads;
   constexpr bool kPrefetch = CPT <= 16;
-  __shared__ __attribute__((aligned(16))) T lds[2 * TILE];
+  constexpr int NBUF = FlashOcc<NW, HP>::nbuf;
+  __shared__ __attribute__((aligned(16))) T lds[NBUF * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (so that everything derived from it stays in scalar registers)
@@ -463,12 +473,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash
     __syncthreads();
   }
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+    const int buf = NBUF == 2 ? (t & 1) : 0;
     if (kPrefetch) {
       if (t + 1 < n_tiles) load_tile(t + 1);
     } else {
-      // buffer buf was last read two tiles ago; every wave has passed the
-      // barrier that followed that tile
+      // with two buffers, buf was last read two tiles ago and every wave has
+      // passed the barrier that followed that tile; with one, wait for the
+      // readers of the previous tile
+      if (NBUF == 1 && t > 0) __syncthreads();
       copy_tile(t, buf);
       __syncthreads();
     }
@@ -557,7 +569,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && HP <= 128) ? 2 : 1) void flash
       for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
     }
     if (kPrefetch) {
-      if (t + 1 < n_tiles) store_tile(buf ^ 1);
+      if (t + 1 < n_tiles) {
+        if (NBUF == 1) __syncthreads();  // every wave is done with the one buffer
+        store_tile(NBUF == 2 ? buf ^ 1 : 0);
+      }
       __syncthreads();
     }
   }
