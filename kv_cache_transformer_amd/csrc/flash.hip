@@ -26,6 +26,8 @@
 //   varlen - PackedAttention: each token attends the keys of its own
 //            sequence [cum[b], cum[b+1]); work items come from a device work
 //            list (PackedAttention page: Description and Inputs table).
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kvattn_internal.hpp"
 
@@ -33,6 +35,9 @@ namespace kvattn {
 namespace {
 
 typedef __fp16 lds_half4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+// instruction classes of sched_group_barrier masks
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 __device__ __forceinline__ half4v lds_read_tr16(const f16* p) {
   auto r = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
@@ -89,12 +94,76 @@ template <int HP> struct FlashMma<f16, HP> {
   __device__ float16v qk_block(const f16* Kt, int kb, int lane) const {
     float16v acc = {};
     const f16* kr = Kt + (kb + (lane & 31)) * KS + 8 * (lane >> 5);
+    // operand reads run one k-step ahead of the MFMA that uses them
+    half8v a = *reinterpret_cast<const half8v*>(kr);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      half8v a = *reinterpret_cast<const half8v*>(kr + 16 * s);
+      half8v nxt = a;
+      if (s + 1 < NS) nxt = *reinterpret_cast<const half8v*>(kr + 16 * (s + 1));
       acc = mfma32x32x16(a, qf[s], acc);
+      a = nxt;
     }
     return acc;
+  }
+  // both 32-key blocks of a 64-key tile, interleaved, reads one step ahead
+  __device__ void qk_tile64(const f16* Kt, int lane, float16v (&acc)[2]) const {
+    acc[0] = float16v{};
+    acc[1] = float16v{};
+    const f16* k0 = Kt + (lane & 31) * KS + 8 * (lane >> 5);
+    const f16* k1 = k0 + 32 * KS;
+    half8v a0 = *reinterpret_cast<const half8v*>(k0);
+    half8v a1 = *reinterpret_cast<const half8v*>(k1);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      half8v n0 = a0, n1 = a1;
+      if (s + 1 < NS) {
+        n0 = *reinterpret_cast<const half8v*>(k0 + 16 * (s + 1));
+        n1 = *reinterpret_cast<const half8v*>(k1 + 16 * (s + 1));
+      }
+      acc[0] = mfma32x32x16(a0, qf[s], acc[0]);
+      acc[1] = mfma32x32x16(a1, qf[s], acc[1]);
+      a0 = n0;
+      a1 = n1;
+    }
+    // issue order: four operand reads, then one MFMA and one read at a time,
+    // so that each read is several MFMAs ahead of its use
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+  }
+  // both 32-key blocks of a 64-key tile (p[blk]: this lane's probabilities),
+  // operand reads pinned ahead of the MFMAs that use them
+  __device__ void pv_tile64(const f16* Vt, const float (&p)[2][16], int lane) {
+    const int G = lane >> 4, t = lane & 15;
+    const int c = t & 3, ir = t >> 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // q = 2 * block + half: 16 keys each
+      half8v pb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[i] = (f16)p[q >> 1][8 * (q & 1) + i];
+      const int row = 16 * q + 4 * (G >> 1) + ir;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const f16* a1 = Vt + row * VS + 32 * db + 16 * (G & 1) + 4 * c;
+        half4v lo = lds_read_tr16(a1);
+        half4v hi = lds_read_tr16(a1 + 8 * VS);
+        half8v a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[db] = mfma32x32x16(a, pb, o[db]);
+      }
+    }
+    // six reads (three MFMAs' operands) ahead, then one MFMA and its
+    // successor's two reads at a time
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * ND - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 0);
   }
   // p: this lane's 16 probabilities of the 32-key block at kb
   __device__ void pv_block(const f16* Vt, int kb, const float (&p)[16], int lane) {
@@ -496,8 +565,12 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
         full = full && r.start + BN - 1 <= pmin;
       float x[BN / 32][16];
       float16v sacc[BN / 32];
+      if constexpr (std::is_same<T, f16>::value && BN == 64) {
+        mma.qk_tile64(Kt, lane, sacc);
+      } else {
 #pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk) sacc[blk] = mma.qk_block(Kt, 32 * blk, lane);
+        for (int blk = 0; blk < BN / 32; ++blk) sacc[blk] = mma.qk_block(Kt, 32 * blk, lane);
+      }
       mfma_result_fence();
       // softcap: c * log2(e) * tanh(y) = A - B / (2^u + 1) with u = 2 * log2(e) * y
 #pragma unroll
@@ -565,8 +638,12 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
           psum += e;
         }
       lsum += psum;
+      if constexpr (std::is_same<T, f16>::value && BN == 64) {
+        mma.pv_tile64(Vt, x, lane);
+      } else {
 #pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
+        for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
+      }
     }
     if (kPrefetch) {
       if (t + 1 < n_tiles) {
