@@ -817,26 +817,33 @@ int packed_run(const packed_attrs* a, const kvattn_tensor* in, const kvattn_tens
   sp.bounds = bounds;
   sp.work = work;
   sp.B = P.B; sp.T = P.T; sp.pad_seq = P.S; sp.tile = kPackedTile;
-  CHECK(hip_status(launch_packed_sched(sp, st), "schedule launch"));
 
   GemmParams g{};
+  if (P.B <= kGemmSchedMaxB) {
+    g.with_sched = 1;  // the GEMM launch builds the schedule in one extra workgroup
+    g.sched = sp;
+  } else {
+    CHECK(hip_status(launch_packed_sched(sp, st), "schedule launch"));
+  }
   g.x = in[PACKED_IN_INPUT].data;
   g.w = in[PACKED_IN_WEIGHTS].data;
   g.bias = in[PACKED_IN_BIAS].data;
   g.y = y;
   g.M = P.T; g.K = P.D; g.Ncol = P.C;
+  g.head_dim = P.H;  // Q, K, V head-major: every head's rows contiguous for the attention tiles
   CHECK(hip_status(profiled(KVATTN_PROFILE_GEMM, st, [&] { return launch_qkv_gemm(dt, g, st); }),
                    "qkv gemm launch"));
 
   FlashParams f{};
   const size_t esz = elem_size(P.dt);
+  const int64_t head_el = (int64_t)P.T * P.H;  // elements of one head's rows
   f.q = y;
-  f.q_s = P.C;
-  f.q_h = P.H;
-  f.kc = static_cast<char*>(y) + (size_t)P.qh * esz;
-  f.vc = static_cast<char*>(y) + (size_t)(P.qh + P.kh) * esz;
-  f.k_j = P.C;
-  f.k_h = P.H;
+  f.q_s = P.H;
+  f.q_h = head_el;
+  f.kc = static_cast<char*>(y) + (size_t)P.N * head_el * esz;
+  f.vc = static_cast<char*>(y) + (size_t)2 * P.N * head_el * esz;
+  f.k_j = P.H;
+  f.k_h = head_el;
   f.out = out[PACKED_OUT_OUTPUT].data;
   f.o_s = P.vh;
   f.o_h = P.H;

@@ -55,9 +55,9 @@ template <typename T, int HP> struct FlashMma;
 // ------------------------------- f16 ----------------------------------------
 template <int HP> struct FlashMma<f16, HP> {
   static constexpr int KS = HP + 8;    // K tile row stride (elements): rows 4 banks apart
-  // V tile row stride (elements): a multiple of 128 plus 32, so that the two
+  // V tile row stride (elements): 32 or 96 modulo 128, so that the two
   // 16-lane groups of a transposing read hit disjoint bank halves
-  static constexpr int VS = HP <= 128 ? 160 : 288;
+  static constexpr int VS = HP <= 64 ? 96 : (HP <= 128 ? 160 : 288);
   static constexpr int NS = HP / 16;   // 16-dim k-steps of the score MFMA
   static constexpr int ND = HP / 32;   // 32-dim output blocks
   static constexpr int CH = 8;         // elements per 16-byte chunk
@@ -486,7 +486,12 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   const bool pad_cols = H < HP;   // uniform: only then can zero_col be true
   const int kj = (int)p.k_j;      // row stride (elements); a slab of rows fits 32 bits
   uint4v stage[kPrefetch ? CPT : 1];
-  auto load_tile = [&](int t) {
+  // Prefetch depth: with short per-tile compute (64-dim heads) the next
+  // tile's loads would not return in time, so those kernels load two tiles
+  // ahead into a second register stage.
+  constexpr int kStages = (kPrefetch && HP <= 64) ? 2 : 1;
+  uint4v stage2[kStages == 2 ? CPT : 1];
+  auto load_tile_to = [&](int t, uint4v* dst) {
     const TileRange r = tile_range(t);
     // uniform base at the tile's first row; per-thread 32-bit offsets
     const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
@@ -497,20 +502,22 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
       const int off = min(row0 + RSTEP * (u % KU), last) * kj + d0;
       const T* src = (u < KU ? kt : vt) + off;
       if (pad_cols)
-        stage[u] = zero_col ? uint4v{0u, 0u, 0u, 0u} : *reinterpret_cast<const uint4v*>(src);
+        dst[u] = zero_col ? uint4v{0u, 0u, 0u, 0u} : *reinterpret_cast<const uint4v*>(src);
       else
-        stage[u] = *reinterpret_cast<const uint4v*>(src);
+        dst[u] = *reinterpret_cast<const uint4v*>(src);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto load_tile = [&](int t) { load_tile_to(t, stage); };
+  auto store_tile_from = [&](int buf, const uint4v* srcs) {
     T* base = lds + buf * TILE;
 #pragma unroll
     for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
       const int row = row0 + RSTEP * (u % KU);
       T* dst = u < KU ? base + row * KS + d0 : base + BN * KS + row * VS + d0;
-      *reinterpret_cast<uint4v*>(dst) = stage[u];
+      *reinterpret_cast<uint4v*>(dst) = srcs[u];
     }
   };
+  auto store_tile = [&](int buf) { store_tile_from(buf, stage); };
   // direct copy without holding a whole tile in registers (large tiles per thread)
   auto copy_tile = [&](int t, int buf) {
     const TileRange r = tile_range(t);
@@ -539,12 +546,17 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   if (kPrefetch && n_tiles > 0) {
     load_tile(0);
     store_tile(0);
+    if (kStages == 2) load_tile(min(1, n_tiles - 1));  // stage: tile 1
     __syncthreads();
   }
-  for (int t = 0; t < n_tiles; ++t) {
+  // One tile: compute tile t from LDS; `cur` holds tile t + 1 (two-stage
+  // prefetch) and `nxt` receives tile t + 2.  Loads past the last tile re-read
+  // it, so every path issues the same loads.
+  auto tile_step = [&](int t, uint4v* cur, uint4v* nxt) {
     const int buf = NBUF == 2 ? (t & 1) : 0;
     if (kPrefetch) {
-      if (t + 1 < n_tiles) load_tile(t + 1);
+      if (kStages == 2) load_tile_to(min(t + 2, n_tiles - 1), nxt);
+      else if (t + 1 < n_tiles) load_tile_to(t + 1, cur);
     } else {
       // with two buffers, buf was last read two tiles ago and every wave has
       // passed the barrier that followed that tile; with one, wait for the
@@ -648,9 +660,129 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     if (kPrefetch) {
       if (t + 1 < n_tiles) {
         if (NBUF == 1) __syncthreads();  // every wave is done with the one buffer
-        store_tile(NBUF == 2 ? buf ^ 1 : 0);
+        store_tile_from(NBUF == 2 ? buf ^ 1 : 0, cur);
       }
       __syncthreads();
+    }
+  };
+  if constexpr (kStages == 2) {
+    for (int t = 0; t < n_tiles; t += 2) {
+      tile_step(t, stage, stage2);
+      if (t + 1 < n_tiles) tile_step(t + 1, stage2, stage);
+    }
+  } else {
+    for (int t = 0; t < n_tiles; ++t) {
+    const int buf = NBUF == 2 ? (t & 1) : 0;
+    if (kPrefetch) {
+      if (kStages == 2) load_tile_to(min(t + 2, n_tiles - 1), stage);
+      else if (t + 1 < n_tiles) load_tile_to(t + 1, stage);
+    } else {
+      // with two buffers, buf was last read two tiles ago and every wave has
+      // passed the barrier that followed that tile; with one, wait for the
+      // readers of the previous tile
+      if (NBUF == 1 && t > 0) __syncthreads();
+      copy_tile(t, buf);
+      __syncthreads();
+    }
+    const TileRange r = tile_range(t);
+    if (wave_rows) {
+      const T* Kt = lds + buf * TILE;
+      const T* Vt = Kt + BN * KS;
+      // a tile visible to every row of the workgroup needs no mask
+      bool full = r.lim == r.start + BN;
+      if (MODE == kDense && p.causal)
+        full = full && r.start + BN - 1 <= pmin && (p.window < 0 || r.start >= pmax - p.window);
+      else if (MODE == kCsr)
+        full = full && r.start + BN - 1 <= pmin;
+      float x[BN / 32][16];
+      float16v sacc[BN / 32];
+      if constexpr (std::is_same<T, f16>::value && BN == 64) {
+        mma.qk_tile64(Kt, lane, sacc);
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < BN / 32; ++blk) sacc[blk] = mma.qk_block(Kt, 32 * blk, lane);
+      }
+      mfma_result_fence();
+      // softcap: c * log2(e) * tanh(y) = A - B / (2^u + 1) with u = 2 * log2(e) * y
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v = sacc[blk][i];
+          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
+          x[blk][i] = v;
+        }
+      if (bias != nullptr || !full) {
+#pragma unroll
+        for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            bool ok = row_ok && key < r.lim;
+            if (MODE == kDense) {
+              if (p.causal) {
+                ok = ok && key <= pos;
+                if (p.window >= 0) ok = ok && key >= pos - p.window;
+              }
+            } else if (MODE == kCsr) {
+              ok = ok && key <= pos;
+            }
+            float v = x[blk][i];
+            if (bias != nullptr && ok) {
+              if (MODE == kVarlen) {
+                int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
+                pad_k = min(max(pad_k, 0), p.pad_seq - 1);
+                v += kLog2e * to_f32(bias[bias_row + pad_k]);
+              } else if (key < p.bias_cols) {
+                v += kLog2e * to_f32(bias[bias_row + key]);
+              }
+            }
+            x[blk][i] = ok ? v : kNegInf;
+          }
+      }
+      float tmax = kNegInf;
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[blk][i]);
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      // The running max m moves only when a score exceeds it by more than
+      // kMaxSlack (log2 units): probabilities then stay <= 2^kMaxSlack, exact
+      // enough in fp16 and far from overflow, and O is rescaled rarely.
+      const bool grow = tmax > m + kMaxSlack;
+      if (__any(grow)) {
+        const float mnew = grow ? tmax : m;
+        const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
+      }
+      const float muse = (m == kNegInf) ? 0.f : m;
+      float psum = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float e = fast_exp2(x[blk][i] - muse);
+          x[blk][i] = e;
+          psum += e;
+        }
+      lsum += psum;
+      if constexpr (std::is_same<T, f16>::value && BN == 64) {
+        mma.pv_tile64(Vt, x, lane);
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
+      }
+    }
+    if (kPrefetch) {
+      if (t + 1 < n_tiles) {
+        if (NBUF == 1) __syncthreads();  // every wave is done with the one buffer
+        store_tile_from(NBUF == 2 ? buf ^ 1 : 0, stage);
+      }
+      __syncthreads();
+    }
     }
   }
 

@@ -150,7 +150,12 @@ struct GemmParams {
   const void* bias;         // (Ncol)
   void* y;                  // (M, Ncol) row-major
   int M, K, Ncol;
+  int head_dim;             // > 0: write Y head-major, (Ncol / head_dim, M, head_dim)
+  int with_sched;           // 1: workgroup 0 also builds `sched` (B <= kGemmSchedMaxB)
+  PackedSchedParams sched;
 };
+// most sequences the GEMM's extra workgroup can schedule in its LDS
+constexpr int kGemmSchedMaxB = 3000;
 
 // Launchers (defined in the .hip sources).  Each returns hipSuccess or the
 // launch error.

@@ -22,8 +22,8 @@ namespace {
 // ---------------------------------------------------------------------------
 // schedule
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void packed_sched_kernel(PackedSchedParams p) {
-  extern __shared__ int32_t sh[];
+// One workgroup builds the schedule; sh holds 3 * B + 1 ints.
+__device__ void build_schedule(const PackedSchedParams& p, int32_t* sh) {
   int32_t* len = sh;               // B
   int32_t* order = sh + p.B;       // B: sequence at each rank
   int32_t* off = sh + 2 * p.B;     // B + 1: first item of each rank
@@ -73,10 +73,18 @@ __global__ __launch_bounds__(256) void packed_sched_kernel(PackedSchedParams p) 
   }
 }
 
+__global__ __launch_bounds__(256) void packed_sched_kernel(PackedSchedParams p) {
+  extern __shared__ int32_t sh[];
+  build_schedule(p, sh);
+}
+
 // ---------------------------------------------------------------------------
 // QKV projection GEMM
 // ---------------------------------------------------------------------------
-constexpr int BM = 128, BNC = 128, BK = 32;
+constexpr int BM = 128, BNC = 128;
+// k depth of a tile (64 measured slower for f16: three waves per SIMD become two)
+template <typename T> struct GemmBK { static constexpr int value = 32; };
+template <> struct GemmBK<float> { static constexpr int value = 32; };
 
 typedef __fp16 lds_half4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 __device__ __forceinline__ half4v lds_tr16(const f16* ptr) {
@@ -88,6 +96,7 @@ __device__ __forceinline__ half4v lds_tr16(const f16* ptr) {
 template <typename T> struct GemmTile;
 
 template <> struct GemmTile<f16> {
+  static constexpr int BK = GemmBK<f16>::value;
   static constexpr int AS = BK + 8;     // A tile row stride (elements), rows = M
   static constexpr int BS = BNC + 16;   // B tile row stride (elements), rows = K
   static constexpr int CH = 8;
@@ -118,6 +127,7 @@ template <> struct GemmTile<f16> {
 };
 
 template <> struct GemmTile<float> {
+  static constexpr int BK = GemmBK<float>::value;
   static constexpr int AS = BK + 4;
   static constexpr int BS = BNC + 4;
   static constexpr int CH = 4;
@@ -142,17 +152,26 @@ template <> struct GemmTile<float> {
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
   using G = GemmTile<T>;
-  constexpr int AS = G::AS, BS = G::BS, CH = G::CH;
+  constexpr int AS = G::AS, BS = G::BS, CH = G::CH, BK = G::BK;
   constexpr int A_EL = BM * AS, B_EL = BK * BS;
   constexpr int A_CH = BM * BK / CH, B_CH = BK * BNC / CH;   // 16-byte chunks per tile
   constexpr int CPT = (A_CH + B_CH) / 256;
   __shared__ __attribute__((aligned(16))) T lds[2 * (A_EL + B_EL)];
+  static_assert(sizeof(lds) / sizeof(int32_t) >= 3 * kGemmSchedMaxB + 1, "schedule fits the tile LDS");
 
+  // workgroup 0 builds the attention schedule when asked (no separate launch)
+  if (p.with_sched) {
+    if (blockIdx.x == 0) {
+      build_schedule(p.sched, reinterpret_cast<int32_t*>(lds));
+      return;
+    }
+  }
+  const int tile = blockIdx.x - (p.with_sched ? 1 : 0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = (p.Ncol + BNC - 1) / BNC;
-  const int m0 = (blockIdx.x / tiles_n) * BM;
-  const int n0 = (blockIdx.x % tiles_n) * BNC;
+  const int m0 = (tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BNC;
   const T* X = static_cast<const T*>(p.x);
   const T* W = static_cast<const T*>(p.w);
 
@@ -220,12 +239,21 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
     const int n = n0 + 64 * wn + 32 * j + (lane & 31);
     if (n >= p.Ncol) continue;
     const float bv = to_f32(bias[n]);
+    // row-major Y[m][n], or head-major Y[n / hd][m][n % hd] for head size hd
+    int64_t col, mstride;
+    if (p.head_dim > 0) {
+      col = (int64_t)(n / p.head_dim) * p.M * p.head_dim + n % p.head_dim;
+      mstride = p.head_dim;
+    } else {
+      col = n;
+      mstride = p.Ncol;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (m < p.M) Y[(int64_t)m * p.Ncol + n] = from_f32<T>(acc[i][j][e] + bv);
+        if (m < p.M) Y[col + (int64_t)m * mstride] = from_f32<T>(acc[i][j][e] + bv);
       }
   }
 }
@@ -239,8 +267,8 @@ hipError_t launch_packed_sched(const PackedSchedParams& p, hipStream_t s) {
 }
 
 hipError_t launch_qkv_gemm(DType dt, const GemmParams& p, hipStream_t s) {
-  if (p.M == 0) return hipSuccess;
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.Ncol + BNC - 1) / BNC);
+  if (p.M == 0 && !p.with_sched) return hipSuccess;
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.Ncol + BNC - 1) / BNC) + (p.with_sched ? 1 : 0);
   if (dt == DType::F16)
     hipLaunchKernelGGL(qkv_gemm_kernel<f16>, dim3(tiles), dim3(256), 0, s, p);
   else
