@@ -44,6 +44,11 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first copy this many MiB device to device (a plain copy of known size, "
                          "to scale the HBM byte counters of a profiler run)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="CPU only: summarise two rocprofv3 --pmc output folders (FETCH_SIZE, then "
+                         "WRITE_SIZE, each from a run with --copy-probe-mib) into profiles/traffic.json")
+    ap.add_argument("--traffic-cmd", nargs=2, default=None,
+                    help="the two profiler commands, recorded in the traffic summary")
     return ap.parse_args()
 
 
@@ -289,6 +294,83 @@ def cpu_baseline(case, budget_s=12.0):
                       f"{elapsed:.1f} s"}
 
 
+# Kernels whose HBM traffic is summarised, keyed as bench lines look them up:
+# (key, pattern on the mangled kernel name, sources whose hash pins the figure)
+_KERNEL_SOURCES = ["kv_cache_transformer_amd/csrc/device_common.hpp",
+                   "kv_cache_transformer_amd/csrc/kvattn_internal.hpp",
+                   "kv_cache_transformer_amd/csrc/api.cpp"]
+TRAFFIC_KERNELS = [
+    ("decode", r"decode_kernelIDF16_Li128E", "kv_cache_transformer_amd/csrc/decode.hip", "gqa_decode"),
+    ("flash_gqa_long_prefill", r"flash_kernelIDF16_Li128ELi\d+ELi0E", "kv_cache_transformer_amd/csrc/flash.hip",
+     "gqa_long_prefill"),
+    ("flash_sparse_prompt", r"flash_kernelIDF16_Li128ELi\d+ELi1E", "kv_cache_transformer_amd/csrc/flash.hip",
+     "sparse_prompt"),
+    ("qkv_gemm_packed_varlen", r"qkv_gemm_kernelIDF16_", "kv_cache_transformer_amd/csrc/packed.hip",
+     "packed_varlen"),
+]
+
+
+def _sources_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def summarise_traffic(fetch_dir, write_dir, cmds, probe_mib):
+    """Per-launch HBM bytes of the library's kernels from two rocprofv3
+    counter runs.  Each counter is scaled by what it reads for the largest
+    device-to-device copy of the same run (a copy of known size), and the
+    figure is stored with a hash of the kernel's sources."""
+    import csv
+    import glob
+    import re
+
+    def load(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        if not rows:
+            raise SystemExit(f"no {counter} rows under {d}")
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit(f"no copy-probe dispatch under {d} (run with --copy-probe-mib)")
+        probe = max(copies, key=lambda r: float(r["Counter_Value"]))
+        return rows, float(probe["Counter_Value"])
+
+    probe_kib = probe_mib * 1024
+    fetch, f_probe = load(fetch_dir, "FETCH_SIZE")
+    write, w_probe = load(write_dir, "WRITE_SIZE")
+    f_scale, w_scale = probe_kib / f_probe, probe_kib / w_probe
+    out = {}
+    lines = ["# HBM traffic per launch of the library's kernels, all bench workloads",
+             "# commands (on the GPU host, from the repository root), one counter per run:"]
+    lines += [f"#   {c}" for c in (cmds or ["(not recorded)"])]
+    lines += [f"# calibration: the {probe_mib} MiB device-to-device copy of each run reads FETCH_SIZE "
+              f"{f_probe:.0f} KiB (scale {f_scale:.4f}) and WRITE_SIZE {w_probe:.0f} KiB (scale {w_scale:.4f})",
+              f"{'kernel':<26} {'launches':>8} {'FETCH KiB':>12} {'WRITE KiB':>12} {'read MB':>10} {'written MB':>10}"]
+    for key, pat, src, workload in TRAFFIC_KERNELS:
+        fr = [float(r["Counter_Value"]) for r in fetch if re.search(pat, r["Kernel_Name"])]
+        wr = [float(r["Counter_Value"]) for r in write if re.search(pat, r["Kernel_Name"])]
+        if not fr or not wr:
+            continue
+        fk, wk = sum(fr) / len(fr), sum(wr) / len(wr)
+        rb, wb = fk * 1024 * f_scale, wk * 1024 * w_scale
+        sources = [src] + _KERNEL_SOURCES
+        out[key] = {"bytes_per_launch": int(round(rb + wb)), "fetch_bytes": int(round(rb)),
+                    "write_bytes": int(round(wb)), "fetch_scale": f_scale, "write_scale": w_scale,
+                    "launches": len(fr), "sources": sources, "source_sha256": _sources_sha(sources),
+                    "workload": workload, "profile": "profiles/traffic_all_workloads.txt"}
+        lines.append(f"{key:<26} {len(fr):>8} {fk:>12.1f} {wk:>12.1f} {rb / 1e6:>10.2f} {wb / 1e6:>10.2f}")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    with open(os.path.join(ROOT, "profiles", "traffic_all_workloads.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_for(kernel_key):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
     when the kernel source changed since the counters were taken."""
@@ -300,11 +382,7 @@ def traffic_for(kernel_key):
         ent = data.get(kernel_key)
         if not ent:
             return None
-        import hashlib
-        h = hashlib.sha256()
-        for f in ent["sources"]:
-            h.update(open(os.path.join(ROOT, f), "rb").read())
-        if h.hexdigest() != ent["source_sha256"]:
+        if _sources_sha(ent["sources"]) != ent["source_sha256"]:
             return None
         return ent["bytes_per_launch"]
     except Exception:
@@ -313,6 +391,10 @@ def traffic_for(kernel_key):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        summarise_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_cmd,
+                          args.copy_probe_mib or 512)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
               "no multi-GPU path: every workload here is one GPU's share.", file=sys.stderr)
@@ -397,7 +479,7 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "qkv_gemm", "achieved": round(tf_g, 2),
                          "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tf_g / MFMA_F16_PEAK_TFS, 4), "kernel_ms": round(r["kern_ms"], 4),
-                         "algorithmic_flops": r["gemm_flops"], "traffic": None}}
+                         "algorithmic_flops": r["gemm_flops"], "traffic": traffic_for("qkv_gemm_packed_varlen")}}
 
     line = {"metric": "GQA prefill TFLOP/s and decode KV GB/s on 1 MI355X, % of roofline",
             "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
