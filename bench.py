@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="CPU only: summarise two rocprofv3 --pmc output folders (FETCH_SIZE, then "
                          "WRITE_SIZE, each from a run with --copy-probe-mib) into profiles/traffic.json")
+    ap.add_argument("--counters-from", nargs=2, metavar=("DIR", "COMMAND"), default=None,
+                    help="CPU only: summarise one rocprofv3 --pmc run of SQ/GRBM counters (made by "
+                         "COMMAND) into profiles/sq_counters_all_workloads.txt")
     ap.add_argument("--traffic-cmd", nargs=2, default=None,
                     help="the two profiler commands, recorded in the traffic summary")
     return ap.parse_args()
@@ -371,6 +374,57 @@ def summarise_traffic(fetch_dir, write_dir, cmds, probe_mib):
     print("\n".join(lines))
 
 
+def summarise_counters(d, cmd):
+    """Per-kernel averages of one rocprofv3 counter run, with the MFMA and VALU
+    busy fractions.  GRBM_GUI_ACTIVE sums the eight XCDs' busy clocks, so the
+    SIMD-cycles of a launch are GRBM_GUI_ACTIVE / 8 * 1024 SIMDs;
+    SQ_ACTIVE_INST_VALU counts quad-cycles."""
+    import csv
+    import glob
+    import re
+    pat = re.compile(r"(flash_kernel|decode_kernel|decode_combine_kernel|qkv_gemm_kernel|prep_kv_kernel|"
+                     r"prep_kernel|packed_sched_kernel)(?:I(DF16_|f)(?:Li(\d+)ELi(\d+)ELi(\d+))?)?")
+    agg, dur = {}, {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            m = pat.search(r["Kernel_Name"])
+            if not m:
+                continue
+            t = {"DF16_": "f16", "f": "f32", None: ""}[m.group(2)]
+            hd, md = m.group(3), m.group(5)
+            dm = re.search(r"<float(?:, (\d+), (\d+), (\d+))?", r["Kernel_Name"])
+            if not t and dm:  # names of float instances come demangled
+                t, hd, md = "f32", dm.group(1), dm.group(3)
+            mode = {"0": "dense", "1": "csr", "2": "varlen"}.get(md, "")
+            key = m.group(1) + (f"<{t},{hd},{mode}>" if hd else (f"<{t}>" if t else ""))
+            agg.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                dur.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["# SQ / GRBM counters per launch, all bench workloads (one counter run, averages over launches)",
+             "# command (on the GPU host, from the repository root):", f"#   {cmd}",
+             "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD-cycles; valu_busy = 4 * SQ_ACTIVE_INST_VALU / SIMD-cycles;",
+             "# SIMD-cycles = GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8 * 1024 SIMDs; clock = GRBM_GUI_ACTIVE / 8 / duration",
+             "# (GRBM_GUI_ACTIVE also counts a few microseconds of dispatch around the kernel, so the clock",
+             "# column reads high on short kernels; the long kernels show the clock under load)",
+             f"{'kernel':<28} {'launches':>8} {'dur_us':>8} {'clock_GHz':>9} {'mfma_busy':>9} {'valu_busy':>9} "
+             f"{'lds_bank_conf':>13} {'lds_active':>11} {'mfma_insts':>11} {'valu_insts':>11}"]
+    for key in sorted(agg):
+        g = {c: sum(v) / len(v) for c, v in agg[key].items()}
+        gui = g.get("GRBM_GUI_ACTIVE", 0.0)
+        ns = sum(dur.get(key, [0])) / max(1, len(dur.get(key, [])))
+        simd_cyc = gui / 8 * 1024
+        if simd_cyc <= 0 or ns <= 0:
+            continue
+        lines.append(f"{key:<28} {len(agg[key].get('GRBM_GUI_ACTIVE', [])):>8} {ns / 1e3:>8.1f} "
+                     f"{gui / 8 / ns:>9.2f} {g.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / simd_cyc:>9.3f} "
+                     f"{4 * g.get('SQ_ACTIVE_INST_VALU', 0) / simd_cyc:>9.3f} "
+                     f"{g.get('SQ_LDS_BANK_CONFLICT', 0):>13.4g} {g.get('SQ_ACTIVE_INST_LDS', 0):>11.4g} "
+                     f"{g.get('SQ_INSTS_MFMA', 0):>11.4g} {g.get('SQ_INSTS_VALU', 0):>11.4g}")
+    with open(os.path.join(ROOT, "profiles", "sq_counters_all_workloads.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_for(kernel_key):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
     when the kernel source changed since the counters were taken."""
@@ -391,6 +445,9 @@ def traffic_for(kernel_key):
 
 def main():
     args = parse()
+    if args.counters_from:
+        summarise_counters(args.counters_from[0], args.counters_from[1])
+        return
     if args.traffic_from:
         summarise_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_cmd,
                           args.copy_probe_mib or 512)
