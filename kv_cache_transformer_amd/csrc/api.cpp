@@ -413,7 +413,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   const int g = P.N / P.kvN;
   const int hw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
   f.heads_per_wg = hw;
-  f.rows_per_wg = 128 / hw;
+  f.rows_per_wg = 128 / hw;  // four waves of 32 rows
   f.mode = kDense;
   const int gx = (P.S + f.rows_per_wg - 1) / f.rows_per_wg;
   CHECK(hip_status(profiled(KVATTN_PROFILE_FLASH, st,

@@ -37,7 +37,9 @@ namespace {
 typedef __fp16 lds_half4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
 // instruction classes of sched_group_barrier masks
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+// s_waitcnt operand: vmcnt(0), other counters unconstrained
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ half4v lds_read_tr16(const f16* p) {
   auto r = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
@@ -106,6 +108,8 @@ template <int HP> struct FlashMma<f16, HP> {
     return acc;
   }
   // both 32-key blocks of a 64-key tile, interleaved, reads one step ahead
+  // (PIN: fix the issue order of reads and MFMAs here; otherwise the caller does)
+  template <bool PIN = true>
   __device__ void qk_tile64(const f16* Kt, int lane, float16v (&acc)[2]) const {
     acc[0] = float16v{};
     acc[1] = float16v{};
@@ -127,24 +131,24 @@ template <int HP> struct FlashMma<f16, HP> {
     }
     // issue order: four operand reads, then one MFMA and one read at a time,
     // so that each read is several MFMAs ahead of its use
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+    if (PIN) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * NS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      for (int i = 0; i < 2 * NS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   }
-  // both 32-key blocks of a 64-key tile (p[blk]: this lane's probabilities),
-  // operand reads pinned ahead of the MFMAs that use them
-  __device__ void pv_tile64(const f16* Vt, const float (&p)[2][16], int lane) {
+  // both 32-key blocks of a 64-key tile (pb[2 * blk + half]: this lane's
+  // probabilities of 16 keys each, in f16), operand reads pinned ahead of the
+  // MFMAs that use them
+  __device__ void pv_tile64(const f16* Vt, const half8v (&pb)[4], int lane) {
     const int G = lane >> 4, t = lane & 15;
     const int c = t & 3, ir = t >> 2;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {  // q = 2 * block + half: 16 keys each
-      half8v pb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = (f16)p[q >> 1][8 * (q & 1) + i];
       const int row = 16 * q + 4 * (G >> 1) + ir;
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
@@ -152,7 +156,7 @@ template <int HP> struct FlashMma<f16, HP> {
         half4v lo = lds_read_tr16(a1);
         half4v hi = lds_read_tr16(a1 + 8 * VS);
         half8v a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = mfma32x32x16(a, pb, o[db]);
+        o[db] = mfma32x32x16(a, pb[q], o[db]);
       }
     }
     // six reads (three MFMAs' operands) ahead, then one MFMA and its
@@ -331,6 +335,115 @@ __device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& 
   mma.set_q(x);
 }
 
+// What one workgroup and wave of a flash launch cover: sample, heads, query
+// rows, the key range and its tile schedule, and the K/V slab base.
+template <int MODE, int BN> struct FlashWork {
+  int b, kvh, h, r0, nrows;  // nrows: valid query rows of this workgroup's row block
+  int wrow0, wg_rows_end;    // this wave's first row; end of the workgroup's rows
+  bool wave_rows;            // the wave owns at least one valid row
+  int n_keys, past, pmin, pmax, k_lo, k_hi;
+  int n_tiles, csr_lo, layout, tiles_per_block;
+  int64_t row_base;          // varlen: first packed token of the sequence
+  int64_t kv_base;           // K/V slab of (sample, kv head), in elements
+
+  // false when the workgroup has no work item (varlen grids are padded)
+  __device__ bool init(const FlashParams& p, int wave) {
+    const int g = p.N / p.kvN;
+    const int HW = p.heads_per_wg;
+    row_base = 0;
+    if (MODE == kVarlen) {
+      const int count = p.work[0];
+      if ((int)blockIdx.x >= count) return false;
+      b = p.work[1 + 2 * blockIdx.x];
+      const int tile = p.work[2 + 2 * blockIdx.x];
+      h = blockIdx.y;
+      kvh = h / g;
+      r0 = tile * p.rows_per_wg;
+      row_base = p.lens[2 * b];
+      nrows = p.lens[2 * b + 1] - p.lens[2 * b];
+    } else {
+      // Workgroups are dealt to the eight XCDs round-robin by linear id; the
+      // remap gives each XCD a contiguous range of (row block, head group,
+      // sample) items, so the workgroups sharing a K/V slab share one L2.
+      const int gx = gridDim.x, gy = gridDim.y;
+      const int n = gx * gy * (int)gridDim.z;
+      int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+      if (n % 8 == 0) id = (id % 8) * (n / 8) + id / 8;
+      const int bx = id % gx, by = (id / gx) % gy;
+      b = id / (gx * gy);
+      const int groups = g / HW;
+      kvh = by / groups;
+      h = kvh * g + (by % groups) * HW + (wave % HW);
+      r0 = bx * p.rows_per_wg;
+      nrows = p.S;
+    }
+    wrow0 = r0 + 32 * (MODE == kDense ? wave / HW : wave);
+    wg_rows_end = min(r0 + p.rows_per_wg, nrows);
+    wave_rows = wrow0 < wg_rows_end;
+
+    past = 0;
+    if (MODE == kDense) {
+      n_keys = p.causal ? p.lens[b] + 1 : p.S;
+      if (p.has_past) past = n_keys - p.S;
+    } else if (MODE == kCsr) {
+      n_keys = p.key_total[b];
+      if (p.has_past) past = n_keys - p.S;
+    } else {
+      n_keys = nrows;
+    }
+    pmin = past + r0;
+    pmax = past + wg_rows_end - 1;
+    k_lo = 0;
+    k_hi = n_keys;
+    if (MODE == kDense && p.causal) {
+      k_hi = min(n_keys, pmax + 1);
+      if (p.window >= 0) k_lo = max(0, pmin - p.window);
+    }
+    csr_lo = 0;
+    layout = 0;
+    tiles_per_block = 1;
+    if (MODE == kCsr) {
+      layout = h % p.num_layout;
+      const int rb = pmin / p.block;
+      csr_lo = max(p.rp[layout * p.rp_stride + rb], 0);
+      const int csr_hi = min(p.rp[layout * p.rp_stride + rb + 1], (int)p.cols_stride);
+      tiles_per_block = p.block > BN ? p.block / BN : 1;
+      n_tiles = max(0, csr_hi - csr_lo) * tiles_per_block;
+    } else {
+      n_tiles = (k_hi > k_lo) ? (k_hi - k_lo + BN - 1) / BN : 0;
+    }
+    if (MODE == kVarlen) kv_base = row_base * p.k_j + (int64_t)kvh * p.k_h;
+    else kv_base = (int64_t)b * p.k_b + (int64_t)kvh * p.k_h;
+    return true;
+  }
+
+  // keys [start, start + BN) of tile t, of which [start, lim) may be visible
+  __device__ TileRange tile(const FlashParams& p, int t) const {
+    TileRange r;
+    if (MODE == kCsr) {
+      const int e = csr_lo + t / tiles_per_block;
+      const int c = min(max(p.cols[layout * p.cols_stride + e], 0), p.max_blocks - 1);
+      r.start = c * p.block + (t % tiles_per_block) * BN;
+      const int blk_end = (c + 1) * p.block;
+      r.lim = min(min(r.start + BN, blk_end), min(n_keys, pmax + 1));
+    } else {
+      r.start = k_lo + t * BN;
+      r.lim = min(r.start + BN, k_hi);
+    }
+    return r;
+  }
+
+  // a tile visible to every row of the workgroup needs no mask
+  __device__ bool full(const FlashParams& p, const TileRange& r) const {
+    bool f = r.lim == r.start + BN;
+    if (MODE == kDense && p.causal)
+      f = f && r.start + BN - 1 <= pmin && (p.window < 0 || r.start >= pmax - p.window);
+    else if (MODE == kCsr)
+      f = f && r.start + BN - 1 <= pmin;
+    return f;
+  }
+};
+
 // Waves per SIMD the launch bounds ask for (the second launch-bounds value):
 // two where LDS lets that many workgroups share a CU.  4-wave groups
 // double-buffer their K/V tiles (two groups per CU); smaller groups keep one
@@ -358,84 +471,17 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   // wave-uniform (so that everything derived from it stays in scalar registers)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H;
-  const int g = p.N / p.kvN;
-  const int HW = p.heads_per_wg;
-
-  // ---- workgroup -> (sample, kv head, heads, rows) --------------------------
-  int b, kvh, h, r0, nrows;  // nrows: valid query rows of this workgroup's row block
-  int64_t row_base = 0;      // varlen: first packed token of the sequence
-  if (MODE == kVarlen) {
-    const int count = p.work[0];
-    if ((int)blockIdx.x >= count) return;
-    b = p.work[1 + 2 * blockIdx.x];
-    const int tile = p.work[2 + 2 * blockIdx.x];
-    h = blockIdx.y;
-    kvh = h / g;
-    r0 = tile * p.rows_per_wg;
-    row_base = p.lens[2 * b];
-    nrows = p.lens[2 * b + 1] - p.lens[2 * b];
-  } else {
-    b = blockIdx.z;
-    const int groups = g / HW;
-    kvh = blockIdx.y / groups;
-    h = kvh * g + (blockIdx.y % groups) * HW + (wave % HW);
-    r0 = blockIdx.x * p.rows_per_wg;
-    nrows = p.S;
-  }
-  const int wrow0 = r0 + 32 * (MODE == kDense ? wave / HW : wave);  // this wave's first row
-  const int wg_rows_end = min(r0 + p.rows_per_wg, nrows);
-  const bool wave_rows = wrow0 < wg_rows_end;
-
-  // ---- key range ------------------------------------------------------------
-  int n_keys, past = 0;
-  if (MODE == kDense) {
-    n_keys = p.causal ? p.lens[b] + 1 : p.S;
-    if (p.has_past) past = n_keys - p.S;
-  } else if (MODE == kCsr) {
-    n_keys = p.key_total[b];
-    if (p.has_past) past = n_keys - p.S;
-  } else {
-    n_keys = nrows;
-  }
-  const int pmin = past + r0, pmax = past + wg_rows_end - 1;
-  int k_lo = 0, k_hi = n_keys;
-  if (MODE == kDense && p.causal) {
-    k_hi = min(n_keys, pmax + 1);
-    if (p.window >= 0) k_lo = max(0, pmin - p.window);
-  }
-  int n_tiles, csr_lo = 0, layout = 0, tiles_per_block = 1;
-  if (MODE == kCsr) {
-    layout = h % p.num_layout;
-    const int rb = pmin / p.block;
-    csr_lo = max(p.rp[layout * p.rp_stride + rb], 0);
-    const int csr_hi = min(p.rp[layout * p.rp_stride + rb + 1], (int)p.cols_stride);
-    tiles_per_block = p.block > BN ? p.block / BN : 1;
-    n_tiles = max(0, csr_hi - csr_lo) * tiles_per_block;
-  } else {
-    n_tiles = (k_hi > k_lo) ? (k_hi - k_lo + BN - 1) / BN : 0;
-  }
-  auto tile_range = [&](int t) -> TileRange {
-    TileRange r;
-    if (MODE == kCsr) {
-      int e = csr_lo + t / tiles_per_block;
-      int c = min(max(p.cols[layout * p.cols_stride + e], 0), p.max_blocks - 1);
-      r.start = c * p.block + (t % tiles_per_block) * BN;
-      int blk_end = (c + 1) * p.block;
-      r.lim = min(min(r.start + BN, blk_end), min(n_keys, pmax + 1));
-    } else {
-      r.start = k_lo + t * BN;
-      r.lim = min(r.start + BN, k_hi);
-    }
-    return r;
-  };
-
-  // ---- global addresses -------------------------------------------------------
+  // ---- workgroup -> (sample, kv head, heads, rows, key tiles) ---------------
+  FlashWork<MODE, BN> w;
+  if (!w.init(p, wave)) return;
+  const int b = w.b, h = w.h, nrows = w.nrows, past = w.past, pmin = w.pmin;
+  const int wrow0 = w.wrow0, wg_rows_end = w.wg_rows_end, n_tiles = w.n_tiles;
+  const bool wave_rows = w.wave_rows;
+  const int64_t row_base = w.row_base, kv_base = w.kv_base;
+  auto tile_range = [&](int t) -> TileRange { return w.tile(p, t); };
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.kc);
   const T* vg = static_cast<const T*>(p.vc);
-  int64_t kv_base;
-  if (MODE == kVarlen) kv_base = row_base * p.k_j + (int64_t)kvh * p.k_h;
-  else kv_base = (int64_t)b * p.k_b + (int64_t)kvh * p.k_h;
 
   // ---- queries of this wave (registers) ---------------------------------------
   Mma mma;
@@ -446,7 +492,8 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   // (log2 domain): the query carries scale * log2(e), or, with a softcap c,
   // 2 * log2(e) * scale / c, the argument of the exp2 inside tanh.
   const float cap = p.softcap;
-  const bool use_cap = SOFTCAP && cap > 0.f;
+  // the softcap instance is launched only with a positive cap
+  constexpr bool use_cap = SOFTCAP;
   const float qscale = use_cap ? 2.f * kLog2e * p.scale / cap : kLog2e * p.scale;
   const float capA = cap * kLog2e, capB = 2.f * cap * kLog2e;
   {
@@ -484,6 +531,15 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   const int row0 = tid / CPR, d0 = (tid % CPR) * CH;
   const bool zero_col = d0 >= H;  // columns beyond the head stay zero in LDS
   const bool pad_cols = H < HP;   // uniform: only then can zero_col be true
+  // Every lane loads (a column past the head reads column 0 instead), so all
+  // paths issue the same loads; those lanes skip the store, and the columns
+  // past the head stay as zeroed here.
+  const int dload = zero_col ? 0 : d0;
+  if (kPrefetch && pad_cols) {
+    for (int i = tid; i < NBUF * TILE * (int)sizeof(T) / 16; i += nthreads)
+      reinterpret_cast<uint4v*>(lds)[i] = uint4v{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
   const int kj = (int)p.k_j;      // row stride (elements); a slab of rows fits 32 bits
   uint4v stage[kPrefetch ? CPT : 1];
   // Prefetch depth: with short per-tile compute (64-dim heads) the next
@@ -499,12 +555,9 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     const T* vt = vg + kv_base + (int64_t)r.start * p.k_j;
 #pragma unroll
     for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
-      const int off = min(row0 + RSTEP * (u % KU), last) * kj + d0;
+      const int off = min(row0 + RSTEP * (u % KU), last) * kj + dload;
       const T* src = (u < KU ? kt : vt) + off;
-      if (pad_cols)
-        dst[u] = zero_col ? uint4v{0u, 0u, 0u, 0u} : *reinterpret_cast<const uint4v*>(src);
-      else
-        dst[u] = *reinterpret_cast<const uint4v*>(src);
+      dst[u] = *reinterpret_cast<const uint4v*>(src);
     }
   };
   auto load_tile = [&](int t) { load_tile_to(t, stage); };
@@ -514,7 +567,7 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
       const int row = row0 + RSTEP * (u % KU);
       T* dst = u < KU ? base + row * KS + d0 : base + BN * KS + row * VS + d0;
-      *reinterpret_cast<uint4v*>(dst) = srcs[u];
+      if (!(pad_cols && zero_col)) *reinterpret_cast<uint4v*>(dst) = srcs[u];
     }
   };
   auto store_tile = [&](int buf) { store_tile_from(buf, stage); };
@@ -549,121 +602,137 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     if (kStages == 2) load_tile(min(1, n_tiles - 1));  // stage: tile 1
     __syncthreads();
   }
+  // Scores, online softmax and PV of one tile whose K and V rows sit in LDS.
+  auto compute = [&](const TileRange& r, const T* Kt, const T* Vt) {
+    const bool plain = w.full(p, r) && bias == nullptr;  // uniform: no per-score mask or bias
+    float16v sacc[BN / 32];
+    if constexpr (std::is_same<T, f16>::value && BN == 64) {
+      mma.qk_tile64(Kt, lane, sacc);
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk) sacc[blk] = mma.qk_block(Kt, 32 * blk, lane);
+    }
+    mfma_result_fence();
+    // softcap: c * log2(e) * tanh(y) = A - B / (2^u + 1) with u = 2 * log2(e) * y.
+    // A plain tile keeps its raw scores: the cap is monotone, so the capped
+    // maximum is the cap of the raw one, and the cap is applied in the exponent.
+    if (!plain) {
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          bool ok = row_ok && key < r.lim;
+          if (MODE == kDense) {
+            if (p.causal) {
+              ok = ok && key <= pos;
+              if (p.window >= 0) ok = ok && key >= pos - p.window;
+            }
+          } else if (MODE == kCsr) {
+            ok = ok && key <= pos;
+          }
+          float v = sacc[blk][i];
+          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
+          if (bias != nullptr && ok) {
+            if (MODE == kVarlen) {
+              int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
+              pad_k = min(max(pad_k, 0), p.pad_seq - 1);
+              v += kLog2e * to_f32(bias[bias_row + pad_k]);
+            } else if (key < p.bias_cols) {
+              v += kLog2e * to_f32(bias[bias_row + key]);
+            }
+          }
+          sacc[blk][i] = ok ? v : kNegInf;
+        }
+    }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[blk][i]);
+    if (use_cap && plain) tmax = capA - capB * fast_rcp(fast_exp2(tmax) + 1.f);
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    // The running max m moves only when a score exceeds it by more than
+    // kMaxSlack (log2 units): probabilities then stay <= 2^kMaxSlack, exact
+    // enough in fp16 and far from overflow, and O is rescaled rarely.
+    const bool grow = tmax > m + kMaxSlack;
+    if (__any(grow)) {
+      // a side effect keeps this a branch: executed unconditionally, the
+      // rescale of O would cost a multiply per accumulator on every tile
+      asm volatile("" ::: "memory");
+      const float mnew = grow ? tmax : m;
+      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
+    }
+    const float muse = (m == kNegInf) ? 0.f : m;
+    // probabilities: on a plain softcap tile the cap and the max subtraction
+    // share one FMA; otherwise the scores already hold the exponent
+    const float c0 = capA - muse;
+    if constexpr (std::is_same<T, f16>::value && BN == 64) {
+      // P in f16 (the PV operand); the row sum adds the same rounded values
+      half8v pb[4];
+      if (use_cap && plain) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            pb[q][i] = (f16)fast_exp2(c0 - capB * fast_rcp(fast_exp2(sacc[q >> 1][8 * (q & 1) + i]) + 1.f));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pb[q][i] = (f16)fast_exp2(sacc[q >> 1][8 * (q & 1) + i] - muse);
+      }
+      const half2v one2 = {(f16)1.f, (f16)1.f};
+      float ps[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ps[q] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ps[q] = __builtin_amdgcn_fdot2(half2v{pb[q][2 * j], pb[q][2 * j + 1]}, one2, ps[q], false);
+      }
+      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      mma.pv_tile64(Vt, pb, lane);
+    } else {
+      float pr[BN / 32][16];
+      if (use_cap && plain) {
+#pragma unroll
+        for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            pr[blk][i] = fast_exp2(c0 - capB * fast_rcp(fast_exp2(sacc[blk][i]) + 1.f));
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pr[blk][i] = fast_exp2(sacc[blk][i] - muse);
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) psum += pr[blk][i];
+      lsum += psum;
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, pr[blk], lane);
+    }
+  };
   // One tile: compute tile t from LDS; `cur` holds tile t + 1 (two-stage
   // prefetch) and `nxt` receives tile t + 2.  Loads past the last tile re-read
   // it, so every path issues the same loads.
   auto tile_step = [&](int t, uint4v* cur, uint4v* nxt) {
     const int buf = NBUF == 2 ? (t & 1) : 0;
-    if (kPrefetch) {
-      if (kStages == 2) load_tile_to(min(t + 2, n_tiles - 1), nxt);
-      else if (t + 1 < n_tiles) load_tile_to(t + 1, cur);
-    } else {
-      // with two buffers, buf was last read two tiles ago and every wave has
-      // passed the barrier that followed that tile; with one, wait for the
-      // readers of the previous tile
-      if (NBUF == 1 && t > 0) __syncthreads();
-      copy_tile(t, buf);
-      __syncthreads();
+    load_tile_to(min(t + 2, n_tiles - 1), nxt);
+    compute(tile_range(t), lds + buf * TILE, lds + buf * TILE + BN * KS);
+    if (t + 1 < n_tiles) {
+      if (NBUF == 1) __syncthreads();  // every wave is done with the one buffer
+      store_tile_from(NBUF == 2 ? buf ^ 1 : 0, cur);
     }
-    const TileRange r = tile_range(t);
-    if (wave_rows) {
-      const T* Kt = lds + buf * TILE;
-      const T* Vt = Kt + BN * KS;
-      // a tile visible to every row of the workgroup needs no mask
-      bool full = r.lim == r.start + BN;
-      if (MODE == kDense && p.causal)
-        full = full && r.start + BN - 1 <= pmin && (p.window < 0 || r.start >= pmax - p.window);
-      else if (MODE == kCsr)
-        full = full && r.start + BN - 1 <= pmin;
-      float x[BN / 32][16];
-      float16v sacc[BN / 32];
-      if constexpr (std::is_same<T, f16>::value && BN == 64) {
-        mma.qk_tile64(Kt, lane, sacc);
-      } else {
-#pragma unroll
-        for (int blk = 0; blk < BN / 32; ++blk) sacc[blk] = mma.qk_block(Kt, 32 * blk, lane);
-      }
-      mfma_result_fence();
-      // softcap: c * log2(e) * tanh(y) = A - B / (2^u + 1) with u = 2 * log2(e) * y
-#pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = sacc[blk][i];
-          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
-          x[blk][i] = v;
-        }
-      if (bias != nullptr || !full) {
-#pragma unroll
-        for (int blk = 0; blk < BN / 32; ++blk)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            bool ok = row_ok && key < r.lim;
-            if (MODE == kDense) {
-              if (p.causal) {
-                ok = ok && key <= pos;
-                if (p.window >= 0) ok = ok && key >= pos - p.window;
-              }
-            } else if (MODE == kCsr) {
-              ok = ok && key <= pos;
-            }
-            float v = x[blk][i];
-            if (bias != nullptr && ok) {
-              if (MODE == kVarlen) {
-                int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
-                pad_k = min(max(pad_k, 0), p.pad_seq - 1);
-                v += kLog2e * to_f32(bias[bias_row + pad_k]);
-              } else if (key < p.bias_cols) {
-                v += kLog2e * to_f32(bias[bias_row + key]);
-              }
-            }
-            x[blk][i] = ok ? v : kNegInf;
-          }
-      }
-      float tmax = kNegInf;
-#pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[blk][i]);
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      // The running max m moves only when a score exceeds it by more than
-      // kMaxSlack (log2 units): probabilities then stay <= 2^kMaxSlack, exact
-      // enough in fp16 and far from overflow, and O is rescaled rarely.
-      const bool grow = tmax > m + kMaxSlack;
-      if (__any(grow)) {
-        const float mnew = grow ? tmax : m;
-        const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
-      }
-      const float muse = (m == kNegInf) ? 0.f : m;
-      float psum = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float e = fast_exp2(x[blk][i] - muse);
-          x[blk][i] = e;
-          psum += e;
-        }
-      lsum += psum;
-      if constexpr (std::is_same<T, f16>::value && BN == 64) {
-        mma.pv_tile64(Vt, x, lane);
-      } else {
-#pragma unroll
-        for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
-      }
-    }
-    if (kPrefetch) {
-      if (t + 1 < n_tiles) {
-        if (NBUF == 1) __syncthreads();  // every wave is done with the one buffer
-        store_tile_from(NBUF == 2 ? buf ^ 1 : 0, cur);
-      }
-      __syncthreads();
-    }
+    __syncthreads();
   };
   if constexpr (kStages == 2) {
     for (int t = 0; t < n_tiles; t += 2) {
@@ -672,117 +741,25 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     }
   } else {
     for (int t = 0; t < n_tiles; ++t) {
-    const int buf = NBUF == 2 ? (t & 1) : 0;
-    if (kPrefetch) {
-      if (kStages == 2) load_tile_to(min(t + 2, n_tiles - 1), stage);
-      else if (t + 1 < n_tiles) load_tile_to(t + 1, stage);
-    } else {
-      // with two buffers, buf was last read two tiles ago and every wave has
-      // passed the barrier that followed that tile; with one, wait for the
-      // readers of the previous tile
-      if (NBUF == 1 && t > 0) __syncthreads();
-      copy_tile(t, buf);
-      __syncthreads();
-    }
-    const TileRange r = tile_range(t);
-    if (wave_rows) {
-      const T* Kt = lds + buf * TILE;
-      const T* Vt = Kt + BN * KS;
-      // a tile visible to every row of the workgroup needs no mask
-      bool full = r.lim == r.start + BN;
-      if (MODE == kDense && p.causal)
-        full = full && r.start + BN - 1 <= pmin && (p.window < 0 || r.start >= pmax - p.window);
-      else if (MODE == kCsr)
-        full = full && r.start + BN - 1 <= pmin;
-      float x[BN / 32][16];
-      float16v sacc[BN / 32];
-      if constexpr (std::is_same<T, f16>::value && BN == 64) {
-        mma.qk_tile64(Kt, lane, sacc);
+      const int buf = NBUF == 2 ? (t & 1) : 0;
+      if (kPrefetch) {
+        if (t + 1 < n_tiles) load_tile(t + 1);
       } else {
-#pragma unroll
-        for (int blk = 0; blk < BN / 32; ++blk) sacc[blk] = mma.qk_block(Kt, 32 * blk, lane);
+        // with two buffers, buf was last read two tiles ago and every wave has
+        // passed the barrier that followed that tile; with one, wait for the
+        // readers of the previous tile
+        if (NBUF == 1 && t > 0) __syncthreads();
+        copy_tile(t, buf);
+        __syncthreads();
       }
-      mfma_result_fence();
-      // softcap: c * log2(e) * tanh(y) = A - B / (2^u + 1) with u = 2 * log2(e) * y
-#pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = sacc[blk][i];
-          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
-          x[blk][i] = v;
+      compute(tile_range(t), lds + buf * TILE, lds + buf * TILE + BN * KS);
+      if (kPrefetch) {
+        if (t + 1 < n_tiles) {
+          if (NBUF == 1) __syncthreads();  // every wave is done with the one buffer
+          store_tile(NBUF == 2 ? buf ^ 1 : 0);
         }
-      if (bias != nullptr || !full) {
-#pragma unroll
-        for (int blk = 0; blk < BN / 32; ++blk)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            bool ok = row_ok && key < r.lim;
-            if (MODE == kDense) {
-              if (p.causal) {
-                ok = ok && key <= pos;
-                if (p.window >= 0) ok = ok && key >= pos - p.window;
-              }
-            } else if (MODE == kCsr) {
-              ok = ok && key <= pos;
-            }
-            float v = x[blk][i];
-            if (bias != nullptr && ok) {
-              if (MODE == kVarlen) {
-                int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
-                pad_k = min(max(pad_k, 0), p.pad_seq - 1);
-                v += kLog2e * to_f32(bias[bias_row + pad_k]);
-              } else if (key < p.bias_cols) {
-                v += kLog2e * to_f32(bias[bias_row + key]);
-              }
-            }
-            x[blk][i] = ok ? v : kNegInf;
-          }
+        __syncthreads();
       }
-      float tmax = kNegInf;
-#pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[blk][i]);
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      // The running max m moves only when a score exceeds it by more than
-      // kMaxSlack (log2 units): probabilities then stay <= 2^kMaxSlack, exact
-      // enough in fp16 and far from overflow, and O is rescaled rarely.
-      const bool grow = tmax > m + kMaxSlack;
-      if (__any(grow)) {
-        const float mnew = grow ? tmax : m;
-        const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
-      }
-      const float muse = (m == kNegInf) ? 0.f : m;
-      float psum = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float e = fast_exp2(x[blk][i] - muse);
-          x[blk][i] = e;
-          psum += e;
-        }
-      lsum += psum;
-      if constexpr (std::is_same<T, f16>::value && BN == 64) {
-        mma.pv_tile64(Vt, x, lane);
-      } else {
-#pragma unroll
-        for (int blk = 0; blk < BN / 32; ++blk) mma.pv_block(Vt, 32 * blk, x[blk], lane);
-      }
-    }
-    if (kPrefetch) {
-      if (t + 1 < n_tiles) {
-        if (NBUF == 1) __syncthreads();  // every wave is done with the one buffer
-        store_tile_from(NBUF == 2 ? buf ^ 1 : 0, stage);
-      }
-      __syncthreads();
-    }
     }
   }
 
@@ -824,6 +801,429 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined f16 kernel (64-key tiles, heads of 64 or 128).
+//
+// K and V tiles go straight from global memory into LDS (global_load_lds, 16
+// bytes per lane; no register staging), K one tile ahead of V, each in two
+// buffers.  Per tile t a wave issues the loads of K(t + 2) and V(t + 1), then
+// the score MFMAs of tile t + 1 interleaved with the softmax of tile t, then
+// the PV MFMAs of tile t interleaved with the maximum of tile t + 1, so the
+// matrix pipe and the vector ALU work side by side within the wave.
+//
+// LDS rows: K rows are padded by one 16-byte chunk (the score operand reads
+// of 16 consecutive rows then hit distinct banks); V rows are unpadded with
+// their 16-byte chunks XOR-swizzled by row, which keeps the transposing PV
+// operand reads conflict-free.  A global_load_lds instruction fills 64
+// consecutive 16-byte slots, so every slot, padding included, is loaded (a
+// padding slot repeats chunk 0 of its row).
+template <int HP> struct PipeLayout {
+  static constexpr int BN = 64;
+  static constexpr int CPR = HP / 8;              // 16-byte chunks per row
+  static constexpr int KS = HP + 8;               // K row stride (elements)
+  static constexpr int KTILE = BN * KS;           // elements
+  static constexpr int VTILE = BN * HP;
+  static constexpr int NKI = KTILE * 2 / 1024;    // 1 KiB wave loads per K tile (CPR + 1)
+  static constexpr int NVI = VTILE * 2 / 1024;    // per V tile (CPR)
+  // chunk swizzle of V row r: the rows one transposing read touches (four
+  // consecutive rows, and rows 8 apart) differ in it or in their bank half
+  __device__ static constexpr int swv_of_ir(int ir) { return HP >= 128 ? ir : ((ir >> 1) & 1); }
+  __device__ static int swv(int r) { return 4 * swv_of_ir(r & 3); }
+};
+
+// both 32-key blocks of a 64-key tile from a swizzled V tile (pb[2 * blk + half]:
+// this lane's probabilities of 16 keys each); operand reads pinned ahead of the
+// MFMAs, VALU work of the caller may be scheduled between them
+template <int HP>
+__device__ __forceinline__ void pv_tile64_swz(float16v (&o)[HP / 32], const f16* Vt, const half8v (&pb)[4],
+                                              int lane) {
+  using L = PipeLayout<HP>;
+  constexpr int ND = HP / 32;
+  const int G = lane >> 4, t = lane & 15;
+  const int c = t & 3, ir = t >> 2;
+  const int wsw = L::swv_of_ir(ir);
+  const f16* base = Vt + (4 * (G >> 1) + ir) * HP + 16 * (G & 1) + 4 * c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const f16* a1 = base + 16 * q * HP + 32 * (db ^ wsw);
+      half4v lo = lds_read_tr16(a1);
+      half4v hi = lds_read_tr16(a1 + 8 * HP);
+      half8v a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[db] = mfma32x32x16(a, pb[q], o[db]);
+    }
+  }
+}
+
+template <int HP, int MODE, int NW, bool SOFTCAP>
+__global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
+  using T = f16;
+  using Mma = FlashMma<f16, HP>;
+  using L = PipeLayout<HP>;
+  constexpr int BN = 64;
+  constexpr int KS = L::KS;
+  static_assert(KS == Mma::KS, "score operand reads use the padded K rows");
+  constexpr int MK = (L::NKI + NW - 1) / NW;   // K loads per wave per tile
+  constexpr int MV = (L::NVI + NW - 1) / NW;   // V loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) f16 lds[2 * L::KTILE + 2 * L::VTILE];
+  f16* const K0 = lds;
+  f16* const K1 = lds + L::KTILE;
+  f16* const V0 = lds + 2 * L::KTILE;
+  f16* const V1 = V0 + L::VTILE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = p.H;
+  FlashWork<MODE, BN> w;
+  if (!w.init(p, wave)) return;
+  const int b = w.b, h = w.h, nrows = w.nrows, past = w.past;
+  const int n_tiles = w.n_tiles;
+  const int64_t row_base = w.row_base;
+  const f16* kg = static_cast<const f16*>(p.kc) + w.kv_base;
+  const f16* vg = static_cast<const f16*>(p.vc) + w.kv_base;
+  const int kj = (int)p.k_j;
+
+  // ---- per-lane load slots ---------------------------------------------------
+  // Slot j of a K tile is row j / (CPR + 1), chunk j % (CPR + 1) (the last
+  // chunk of a row is padding and repeats chunk 0); slot j of a V tile is row
+  // j / CPR, stored chunk j % CPR, which holds chunk (j % CPR) ^ swv(row).
+  // Chunks past the head read chunk 0 (any valid data: Q is zero there, and
+  // those output columns are not stored).
+  auto k_slot = [&](int u, int& r, int& col) {
+    const int j = 64 * (wave + NW * u) + lane;
+    r = j / (L::CPR + 1);
+    const int pc = j - r * (L::CPR + 1);
+    int cc = pc < L::CPR ? pc : 0;
+    if (8 * cc >= H) cc = 0;
+    col = 8 * cc;
+  };
+  auto v_slot = [&](int u, int& r, int& col) {
+    const int j = 64 * (wave + NW * u) + lane;
+    r = j / L::CPR;
+    int cc = (j % L::CPR) ^ L::swv(r);
+    if (8 * cc >= H) cc = 0;
+    col = 8 * cc;
+  };
+  // offsets (elements) of this lane's slots in a tile whose rows are all valid
+  int koff[MK], voff[MV];
+#pragma unroll
+  for (int u = 0; u < MK; ++u) {
+    int r, col;
+    k_slot(u, r, col);
+    koff[u] = r * kj + col;
+  }
+#pragma unroll
+  for (int u = 0; u < MV; ++u) {
+    int r, col;
+    v_slot(u, r, col);
+    voff[u] = r * kj + col;
+  }
+  // a tile with fewer valid rows repeats its last valid row
+  auto load_k = [&](int t, f16* dst) {
+    const TileRange r = w.tile(p, t);
+    const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
+    const f16* src = kg + (int64_t)r.start * p.k_j;
+    const bool whole = last == BN - 1;
+#pragma unroll
+    for (int u = 0; u < MK; ++u) {
+      if (wave + NW * u < L::NKI) {
+        int off = koff[u];
+        if (!whole) {
+          int rr, col;
+          k_slot(u, rr, col);
+          off = min(rr, last) * kj + col;
+        }
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src + off),
+            (__attribute__((address_space(3))) void*)(dst + 512 * (wave + NW * u)), 16, 0, 0);
+      }
+    }
+  };
+  auto load_v = [&](int t, f16* dst) {
+    const TileRange r = w.tile(p, t);
+    const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
+    const f16* src = vg + (int64_t)r.start * p.k_j;
+    const bool whole = last == BN - 1;
+#pragma unroll
+    for (int u = 0; u < MV; ++u) {
+      if (wave + NW * u < L::NVI) {
+        int off = voff[u];
+        if (!whole) {
+          int rr, col;
+          v_slot(u, rr, col);
+          off = min(rr, last) * kj + col;
+        }
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src + off),
+            (__attribute__((address_space(3))) void*)(dst + 512 * (wave + NW * u)), 16, 0, 0);
+      }
+    }
+  };
+
+
+  // ---- queries of this wave ------------------------------------------------
+  Mma mma;
+  mma.init();
+  const int qrow = w.wrow0 + (lane & 31);
+  const bool row_ok = w.wave_rows && qrow < w.wg_rows_end;
+  const float cap = p.softcap;
+  constexpr bool use_cap = SOFTCAP;  // launched only with a positive cap
+  const float qscale = use_cap ? 2.f * kLog2e * p.scale / cap : kLog2e * p.scale;
+  const float capA = cap * kLog2e, capB = 2.f * cap * kLog2e;
+  {
+    const int rr = min(qrow, nrows - 1);
+    const f16* qg = static_cast<const f16*>(p.q);
+    const f16* qp = (MODE == kVarlen)
+                        ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
+                        : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
+    prep_query(mma, qp, past + rr, p, qscale, lane);
+  }
+  const int pos = past + qrow;
+  const f16* bias = static_cast<const f16*>(p.bias);
+  int64_t bias_row = 0;
+  if (bias != nullptr) {
+    if (MODE == kVarlen) {
+      int pad_q = p.token_offset[row_base + min(qrow, nrows - 1)] - b * p.pad_seq;
+      pad_q = min(max(pad_q, 0), p.pad_seq - 1);
+      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)pad_q * p.bias_ss;
+    } else {
+      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)min(qrow, nrows - 1) * p.bias_ss;
+    }
+  }
+
+  // ---- score helpers -------------------------------------------------------
+  // Scores of a tile that is not plain: softcap, bias and masks in the exponent.
+  auto mask_scores = [&](const TileRange& r, float16v (&sc)[2]) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        bool ok = row_ok && key < r.lim;
+        if (MODE == kDense) {
+          if (p.causal) {
+            ok = ok && key <= pos;
+            if (p.window >= 0) ok = ok && key >= pos - p.window;
+          }
+        } else if (MODE == kCsr) {
+          ok = ok && key <= pos;
+        }
+        float v = sc[blk][i];
+        if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
+        if (bias != nullptr && ok) {
+          if (MODE == kVarlen) {
+            int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
+            pad_k = min(max(pad_k, 0), p.pad_seq - 1);
+            v += kLog2e * to_f32(bias[bias_row + pad_k]);
+          } else if (key < p.bias_cols) {
+            v += kLog2e * to_f32(bias[bias_row + key]);
+          }
+        }
+        sc[blk][i] = ok ? v : kNegInf;
+      }
+  };
+  auto raw_max = [&](const float16v (&sc)[2]) -> float {
+    float t = kNegInf;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t = fmaxf(t, sc[blk][i]);
+    return t;
+  };
+  float m = kNegInf, lsum = 0.f;
+  // running-max update from this lane's tile maximum (exponent domain)
+  auto update_max = [&](float tmax) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over lanes l and l ^ 32
+    // The running max moves only when a score exceeds it by more than
+    // kMaxSlack: probabilities stay <= 2^kMaxSlack and O is rescaled rarely.
+    const bool grow = tmax > m + kMaxSlack;
+    if (__any(grow)) {
+      asm volatile("" ::: "memory");
+      mfma_result_fence();  // O may still be accumulating
+      const float mnew = grow ? tmax : m;
+      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
+    }
+  };
+  // tile maximum in the exponent domain (plain tiles: cap of the raw maximum)
+  auto tile_max = [&](const TileRange& r, bool plain, float16v (&sc)[2]) -> float {
+    float t;
+    if (plain) {
+      t = raw_max(sc);
+      if (use_cap) t = capA - capB * fast_rcp(fast_exp2(t) + 1.f);
+    } else {
+      mask_scores(r, sc);
+      t = raw_max(sc);
+    }
+    return t;
+  };
+  auto plain_of = [&](const TileRange& r) { return w.full(p, r) && bias == nullptr; };
+
+  // probabilities of tile scores sc (f16, PV operand layout) and their sum,
+  // with the score MFMAs of the next tile (Kn -> scn) interleaved
+  auto probs_qk = [&](bool plain, float16v (&sc)[2], half8v (&pb)[4], const f16* Kn, float16v (&scn)[2]) {
+    const float muse = (m == kNegInf) ? 0.f : m;
+    const float c0 = capA - muse;
+    constexpr int NMF = 2 * Mma::NS;  // score MFMAs (and operand reads) of a tile
+    if (use_cap && plain) {
+      mma.template qk_tile64<false>(Kn, lane, scn);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pb[q][i] = (f16)fast_exp2(c0 - capB * fast_rcp(fast_exp2(sc[q >> 1][8 * (q & 1) + i]) + 1.f));
+      // four operand reads ahead, then one MFMA, one read and a share of the
+      // softmax's VALU work at a time (176 VALU instructions in all)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+#pragma unroll
+      for (int i = 0; i < NMF - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 176 / NMF, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
+    } else {
+      mma.template qk_tile64<false>(Kn, lane, scn);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[q][i] = (f16)fast_exp2(sc[q >> 1][8 * (q & 1) + i] - muse);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+#pragma unroll
+      for (int i = 0; i < NMF - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 80 / NMF, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
+    }
+  };
+  // PV of a tile with the row sum and the raw maximum of the next tile's scores
+  auto pv_sum_max = [&](const f16* Vt, const half8v (&pb)[4], const float16v (&scn)[2]) -> float {
+    // the score MFMAs were issued on either side of a branch: their results
+    // are read below
+    mfma_result_fence();
+    pv_tile64_swz<HP>(mma.o, Vt, pb, lane);
+    const half2v one2 = {(f16)1.f, (f16)1.f};
+    float ps[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ps[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ps[q] = __builtin_amdgcn_fdot2(half2v{pb[q][2 * j], pb[q][2 * j + 1]}, one2, ps[q], false);
+    }
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    const float t = raw_max(scn);
+    // six reads ahead, then one MFMA, two reads and two VALU instructions at a time
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 2);
+#pragma unroll
+    for (int i = 0; i < 4 * Mma::ND - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 2);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 2);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 2);
+    return t;
+  };
+
+  // ---- prologue: tiles 0 (K, V) and 1 (K); scores and maximum of tile 0 ----
+  float16v sA[2], sB[2];
+  half8v pb[4];
+  TileRange rn = {0, 0};
+  bool plain_n = true;
+  if (n_tiles > 0) {
+    load_k(0, K0);
+    load_v(0, V0);
+    if (n_tiles > 1) load_k(1, K1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    mma.qk_tile64(K0, lane, sA);
+    mfma_result_fence();
+    rn = w.tile(p, 0);
+    plain_n = plain_of(rn);
+    update_max(tile_max(rn, plain_n, sA));
+  }
+  // ---- steady state: step t computes P(t), PV(t), and S(t + 1) ------------
+  // sc: scores of tile t (transformed when not plain), scn receives S(t + 1);
+  // Kc/Vc: buffers of K(t) / V(t); Kn/Vn: of K(t + 1) / V(t + 1)
+  auto step = [&](int t, float16v (&sc)[2], float16v (&scn)[2], f16* Kc, f16* Kn, f16* Vc, f16* Vn) {
+    const bool plain_t = plain_n;
+    // K(t) and V(t - 1) are no longer read by any wave (barrier of step t - 1)
+    if (t + 2 < n_tiles) load_k(t + 2, Kc);
+    if (t + 1 < n_tiles) load_v(t + 1, Vn);
+    probs_qk(plain_t, sc, pb, Kn, scn);
+    float tmax = pv_sum_max(Vc, pb, scn);
+    const bool more = t + 1 < n_tiles;
+    if (more) {
+      rn = w.tile(p, t + 1);
+      plain_n = plain_of(rn);
+      if (!plain_n) {
+        mfma_result_fence();
+        tmax = tile_max(rn, false, scn);
+      } else if (use_cap) {
+        tmax = capA - capB * fast_rcp(fast_exp2(tmax) + 1.f);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (more) update_max(tmax);
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, sA, sB, K0, K1, V0, V1);
+    if (t + 1 < n_tiles) step(t + 1, sB, sA, K1, K0, V1, V0);
+  }
+
+  // ---- normalise and store -------------------------------------------------
+  mfma_result_fence();
+  if (!w.wave_rows) return;
+  lsum += shfl_xor(lsum, 32);
+  bool has_sink = false;
+  float sg = 0.f;
+  if (p.sink != nullptr) {
+    has_sink = true;
+    sg = kLog2e * to_f32(static_cast<const f16*>(p.sink)[h]);
+  } else if (p.smooth == 1) {
+    has_sink = true;
+  }
+  float inv;
+  if (lsum == 0.f) {
+    inv = 0.f;
+  } else if (has_sink) {
+    const float M2 = fmaxf(m, sg);
+    const float den = lsum * fast_exp2(m - M2) + fast_exp2(sg - M2);
+    inv = fast_exp2(m - M2) / den;
+  } else {
+    inv = 1.f / lsum;
+  }
+  if (!row_ok) return;
+  f16* og = static_cast<f16*>(p.out);
+  f16* orow = (MODE == kVarlen) ? og + (row_base + qrow) * p.o_s + (int64_t)h * p.o_h
+                                : og + (int64_t)b * p.o_b + (int64_t)qrow * p.o_s + (int64_t)h * p.o_h;
+#pragma unroll
+  for (int db = 0; db < Mma::ND; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 32 * db + 8 * gq + 4 * (lane >> 5);
+      if (d < H) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) orow[d + i] = (f16)(mma.o[db][4 * gq + i] * inv);
+      }
+    }
+}
+
+template <int HP, int MODE, bool SOFTCAP = false>
+hipError_t launch_pipe(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
+  if (nw != 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((flash_pipe_kernel<HP, MODE, 4, SOFTCAP>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <typename T, int HP, int BN, int MODE, bool SOFTCAP = false>
 hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
   if (nw == 4) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 4, SOFTCAP>), grid, dim3(256), 0, s, p);
@@ -834,6 +1234,13 @@ hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
 
 template <typename T, int HP, int BN>
 hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
+  if constexpr (std::is_same<T, f16>::value && BN == 64 && HP <= 128) {
+    if (p.mode == kDense) {
+      const int nw = p.rows_per_wg / 32 * p.heads_per_wg;
+      if (p.softcap > 0.f) return launch_pipe<HP, kDense, true>(p, grid, nw, s);
+      return launch_pipe<HP, kDense, false>(p, grid, nw, s);
+    }
+  }
   switch (p.mode) {
     case kDense:
       if (p.softcap > 0.f) return launch_mode<T, HP, BN, kDense, true>(p, grid, 4, s);

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
   constexpr int A_CH = BM * BK / CH, B_CH = BK * BNC / CH;   // 16-byte chunks per tile
   constexpr int CPT = (A_CH + B_CH) / 256;
   __shared__ __attribute__((aligned(16))) T lds[2 * (A_EL + B_EL)];
-  static_assert(sizeof(lds) / sizeof(int32_t) >= 3 * kGemmSchedMaxB + 1, "schedule fits the tile LDS");
+  static_assert(sizeof(lds) / (sizeof(int32_t)) >= 3 * kGemmSchedMaxB + 1, "schedule fits the tile LDS");
 
   // workgroup 0 builds the attention schedule when asked (no separate launch)
   if (p.with_sched) {
