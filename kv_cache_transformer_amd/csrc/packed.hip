@@ -98,7 +98,9 @@ template <typename T> struct GemmTile;
 template <> struct GemmTile<f16> {
   static constexpr int BK = GemmBK<f16>::value;
   static constexpr int AS = BK + 8;     // A tile row stride (elements), rows = M
-  static constexpr int BS = BNC + 16;   // B tile row stride (elements), rows = K
+  // B tile row stride (elements), rows = K: 64 modulo 256 bytes, so the four
+  // rows of one transposing read (64 bytes each) tile the banks exactly
+  static constexpr int BS = BNC + 32;
   static constexpr int CH = 8;
   // acc[i][j]: 32x32 output block (i: m, j: n) of this wave's 64x64
   __device__ static void step(const f16* As, const f16* Bs, int wm, int wn, int lane,
