@@ -1234,23 +1234,28 @@ hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
 
 template <typename T, int HP, int BN>
 hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
-  if constexpr (std::is_same<T, f16>::value && BN == 64 && HP <= 128) {
-    if (p.mode == kDense) {
-      const int nw = p.rows_per_wg / 32 * p.heads_per_wg;
-      if (p.softcap > 0.f) return launch_pipe<HP, kDense, true>(p, grid, nw, s);
-      return launch_pipe<HP, kDense, false>(p, grid, nw, s);
-    }
-  }
+  // dense f16 prompts with heads up to 128 run on the pipelined kernel
+  constexpr bool kPipeDense = std::is_same<T, f16>::value && BN == 64 && HP <= 128;
   switch (p.mode) {
-    case kDense:
-      if (p.softcap > 0.f) return launch_mode<T, HP, BN, kDense, true>(p, grid, 4, s);
-      return launch_mode<T, HP, BN, kDense, false>(p, grid, 4, s);
+    case kDense: {
+      const int nw = p.rows_per_wg / 32 * p.heads_per_wg;
+      if constexpr (kPipeDense) {
+        if (p.softcap > 0.f) return launch_pipe<HP, kDense, true>(p, grid, nw, s);
+        return launch_pipe<HP, kDense, false>(p, grid, nw, s);
+      } else {
+        if (nw != 4) return hipErrorInvalidValue;
+        if (p.softcap > 0.f) hipLaunchKernelGGL((flash_kernel<T, HP, BN, kDense, 4, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((flash_kernel<T, HP, BN, kDense, 4, false>), grid, dim3(256), 0, s, p);
+        return hipGetLastError();
+      }
+    }
     case kCsr: {
-      int nw = (p.rows_per_wg + 31) / 32;
+      const int nw = (p.rows_per_wg + 31) / 32;
       return launch_mode<T, HP, BN, kCsr>(p, grid, nw >= 4 ? 4 : (nw == 2 ? 2 : 1), s);
     }
     default:
-      return launch_mode<T, HP, BN, kVarlen>(p, grid, 4, s);
+      hipLaunchKernelGGL((flash_kernel<T, HP, BN, kVarlen, 4, false>), grid, dim3(256), 0, s, p);
+      return hipGetLastError();
   }
 }
 
