@@ -15,7 +15,7 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
         q_norm_weight=None, k_norm_weight=None,
         num_heads, kv_num_heads, causal=1, do_rotary=0, local_window_size=-1,
         qk_norm_epsilon=1e-6, scale=0.0, smooth_softmax=-1, softcap_value=0.0,
-        query_rows=None):
+        sliding_window_cache=0, query_rows=None):
     """Grouped-query attention with a BNSH key/value cache.
 
     Follows the GroupQueryAttention page: Description, Inputs, Outputs and
@@ -55,6 +55,24 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
        ``smooth_softmax`` = 1 and no sink is given) adds exp(sink) to the
        denominator only.  Output is the weighted sum of values, BSH layout.
 
+    With ``sliding_window_cache`` = 1 (Attributes table: the caches are
+    fixed-size window buffers that evict old tokens from the front; needs
+    ``local_window_size`` > 0 and enough capacity; Implementation variants: the
+    window-shift pass compacts surviving rows and appends the chunk, and
+    attention keeps both the window floor and the causal bound) steps 2 and 5
+    read, for cache capacity C:
+
+    2'. The buffer holds the most recent tokens, oldest first: before the call
+        rows [0, F_b) with F_b = min(total_b - S, C).  Query s still sits at
+        absolute position total_b - S + s.
+    5'. D_b = max(0, F_b + S - C) oldest rows are dropped: rows [D_b, F_b)
+        move to [0, F_b - D_b), the new rows follow, and the buffer then holds
+        fill_b = F_b - D_b + S rows; row i holds absolute position
+        a_b + i with a_b = total_b - fill_b.  Keys are visible by absolute
+        position (step 6).  "Enough capacity" is read as C >= W + S, so every
+        key in any new query's window is still in the buffer; the attention
+        bias is not supported with this attribute.
+
     ``query_rows`` (optional iterable of s indices) restricts the attention
     output to those query rows (the cache is always updated in full); the
     output then has shape (B, len(query_rows), num_heads * H).
@@ -86,11 +104,25 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
     pv_out = np.array(present_value, copy=True)
     cap = pk_out.shape[2]
     total_b = np.asarray(seqlens_k, dtype=np.int64) + 1
+    win = bool(sliding_window_cache)
     if past_key is not None:
         past_b = total_b - S
     else:
         past_b = np.zeros(B, dtype=np.int64)
-    if np.any(past_b < 0) or np.any(past_b + S > cap):
+    if win:
+        if not causal or local_window_size <= 0 or past_key is None:
+            raise ValueError("sliding_window_cache needs causal, local_window_size > 0 and a past cache")
+        if cap < local_window_size + S:
+            raise ValueError("sliding_window_cache needs capacity >= local_window_size + S")
+        if attention_bias is not None:
+            raise ValueError("sliding_window_cache takes no attention_bias")
+        if np.any(past_b < 0):
+            raise ValueError("seqlens_k inconsistent with sequence length")
+        fill_prev = np.minimum(past_b, cap)                   # F_b
+        drop = np.maximum(0, fill_prev + S - cap)             # D_b
+        fill = fill_prev - drop + S
+        first_pos = total_b - fill                            # a_b
+    elif np.any(past_b < 0) or np.any(past_b + S > cap):
         raise ValueError("seqlens_k inconsistent with sequence length or cache capacity")
 
     sc = default_scale(scale, H)
@@ -119,10 +151,18 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
 
     # present cache (materialised in T)
     for b in range(B):
-        pb = int(past_b[b])
-        if past_key is not None and pb > 0:
-            pk_out[b, :, :pb, :] = np.asarray(past_key)[b, :, :pb, :]
-            pv_out[b, :, :pb, :] = np.asarray(past_value)[b, :, :pb, :]
+        if win:
+            f0, d = int(fill_prev[b]), int(drop[b])
+            keep_k = np.asarray(past_key)[b, :, d:f0, :].copy()
+            keep_v = np.asarray(past_value)[b, :, d:f0, :].copy()
+            pk_out[b, :, :f0 - d, :] = keep_k
+            pv_out[b, :, :f0 - d, :] = keep_v
+            pb = f0 - d
+        else:
+            pb = int(past_b[b])
+            if past_key is not None and pb > 0:
+                pk_out[b, :, :pb, :] = np.asarray(past_key)[b, :, :pb, :]
+                pv_out[b, :, :pb, :] = np.asarray(past_value)[b, :, :pb, :]
         pk_out[b, :, pb:pb + S, :] = round_to(k[b].transpose(1, 0, 2), dtype)
         pv_out[b, :, pb:pb + S, :] = round_to(v[b].transpose(1, 0, 2), dtype)
 
@@ -140,7 +180,10 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
     for b in range(B):
         n_keys = S if not causal else int(total_b[b])
         p = pos[b, rows]                                      # (R,)
-        j = np.arange(n_keys)
+        j = np.arange(n_keys)                                 # absolute key positions
+        if win:
+            n_keys = int(fill[b])
+            j = int(first_pos[b]) + np.arange(n_keys)
         if causal:
             vis = j[None, :] <= p[:, None]
             if W >= 0:
