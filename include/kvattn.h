@@ -148,7 +148,7 @@ typedef struct gqa_attrs {
   int32_t local_window_size;     /* default -1 (off) */
   float qk_norm_epsilon;         /* default 1e-6 */
   float scale;                   /* default 0 = 1/sqrt(H) */
-  int32_t sliding_window_cache;  /* default 0; 1 is UNSUPPORTED */
+  int32_t sliding_window_cache;  /* default 0; 1 = window buffers evicting from the front (below) */
   int32_t smooth_softmax;        /* default -1; 1 adds exp(0) to the denominator */
   float softcap;                 /* default 0 = off */
   int32_t k_quant_type;          /* 0 = NONE (default); other values UNSUPPORTED */
@@ -182,8 +182,19 @@ void gqa_attrs_default(gqa_attrs* attrs);
  * total_sequence_length (host) must be >= every total_b and is the last dim
  * of attention_bias.  rotary needs cos/sin rows for every position used.
  *
+ * sliding_window_cache = 1 (GroupQueryAttention page, Attributes table): the
+ * shared past/present buffers of capacity C hold a sample's most recent
+ * tokens, oldest first.  Before the call they hold F_b = min(total_b - S, C)
+ * rows; D_b = max(0, F_b + S - C) rows are evicted from the front (rows
+ * [D_b, F_b) move to [0, F_b - D_b)) and the S new rows follow, so row i then
+ * holds absolute position total_b - fill_b + i, fill_b = F_b - D_b + S.
+ * Rotary and the causal/window bounds use absolute positions.  Needs causal,
+ * local_window_size > 0, C >= local_window_size + S and shared buffers; no
+ * attention_bias.
+ *
  * UNSUPPORTED: quantised caches (k/v_quant_type, kv_cache_bit_width, k/v
- * scales), sliding_window_cache = 1, kv sequence length != S.
+ * scales), kv sequence length != S, sliding_window_cache with separate
+ * past/present buffers or with attention_bias.
  */
 int32_t gqa_attention(const gqa_attrs* attrs,
                       const kvattn_tensor* inputs, int32_t n_inputs,

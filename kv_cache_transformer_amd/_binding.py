@@ -177,8 +177,8 @@ def gqa_attention(query, key, value, past_key=None, past_value=None, seqlens_k=N
                   attention_bias=None, head_sink=None, q_norm_weight=None, k_norm_weight=None,
                   *, num_heads, kv_num_heads, causal=1, do_rotary=0, local_window_size=-1,
                   qk_norm_epsilon=1e-6, scale=0.0, smooth_softmax=-1, softcap=0.0,
-                  output=None, present_key=None, present_value=None, workspace=None,
-                  stream=None):
+                  sliding_window_cache=0, output=None, present_key=None, present_value=None,
+                  workspace=None, stream=None):
     """GroupQueryAttention (include/kvattn.h, gqa_attention).
 
     ``total_sequence_length`` is a host int.  Pass ``present_key=past_key``
@@ -206,6 +206,7 @@ def gqa_attention(query, key, value, past_key=None, past_value=None, seqlens_k=N
     a.causal, a.do_rotary, a.local_window_size = causal, do_rotary, local_window_size
     a.qk_norm_epsilon, a.scale = qk_norm_epsilon, scale
     a.smooth_softmax, a.softcap = smooth_softmax, softcap
+    a.sliding_window_cache = sliding_window_cache
     ins = _array([_desc(query), _desc(key), _desc(value), _desc(past_key), _desc(past_value),
                   _desc(seqlens_k), _desc(cos_cache), _desc(sin_cache), _desc(attention_bias),
                   _desc(head_sink), Tensor(), Tensor(), _desc(q_norm_weight),

@@ -159,6 +159,7 @@ struct GqaPlan {
   int B, S, N, kvN, H, HP, cap, past_seq;
   int dt;
   bool has_past, shared, decode, q_transform;
+  bool window_cache;  // sliding-window cache: fixed-size buffers evicting from the front
   int total;
   // decode
   int head_groups, hpw;
@@ -192,8 +193,11 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   if (a->k_quant_type != 0 || a->v_quant_type != 0 || a->kv_cache_bit_width != 0 ||
       has(in[GQA_IN_K_SCALE]) || has(in[GQA_IN_V_SCALE]))
     return fail(KVATTN_ERR_UNSUPPORTED, "quantised key/value caches are not implemented");
-  if (a->sliding_window_cache != 0)
-    return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache is not implemented");
+  if (a->sliding_window_cache != 0 && a->sliding_window_cache != 1)
+    return fail(KVATTN_ERR_INVALID_ARG, "sliding_window_cache must be 0 or 1");
+  P.window_cache = a->sliding_window_cache == 1;
+  if (P.window_cache && (a->causal != 1 || a->local_window_size <= 0))
+    return fail(KVATTN_ERR_INVALID_ARG, "sliding_window_cache needs causal = 1 and local_window_size > 0");
   if (a->causal != 0 && a->causal != 1) return fail(KVATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (a->local_window_size < -1) return fail(KVATTN_ERR_INVALID_ARG, "local_window_size must be >= -1");
   if (!a->causal && a->local_window_size != -1)
@@ -239,8 +243,17 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     return fail(KVATTN_ERR_INVALID_ARG, "present_key and present_value must both share the past buffers or neither");
   if (P.shared && ck.dims[2] != pk.dims[2])
     return fail(KVATTN_ERR_INVALID_ARG, "a shared present buffer must have the past buffer's dims");
-  if (P.has_past && P.cap < total)
+  if (P.window_cache) {
+    if (!P.shared)
+      return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache needs shared past/present buffers");
+    if (P.cap < a->local_window_size + P.S)
+      return fail(KVATTN_ERR_INVALID_ARG, "sliding_window_cache: capacity %d < local_window_size + sequence_length (%d)",
+                  P.cap, a->local_window_size + P.S);
+    if (has(in[GQA_IN_ATTENTION_BIAS]))
+      return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache with attention_bias is not implemented");
+  } else if (P.has_past && P.cap < total) {
     return fail(KVATTN_ERR_INVALID_ARG, "present sequence axis %d cannot hold total_sequence_length %d", P.cap, total);
+  }
   if (!P.has_past && P.cap < P.S)
     return fail(KVATTN_ERR_INVALID_ARG, "present sequence axis %d < sequence_length %d", P.cap, P.S);
 
@@ -305,6 +318,15 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     CHECK(hip_status(launch_copy_past(dt, c, st), "copy_past launch"));
   }
 
+  if (P.window_cache) {
+    WindowShiftParams w{};
+    w.kc = ck.data;
+    w.vc = cv.data;
+    w.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
+    w.B = P.B; w.kvN = P.kvN; w.H = P.H; w.S = P.S; w.cap = P.cap;
+    CHECK(hip_status(launch_window_shift(dt, w, st), "window shift launch"));
+  }
+
   const kvattn_tensor& bias = in[GQA_IN_ATTENTION_BIAS];
   if (P.decode) {
     DecodeParams d{};
@@ -332,6 +354,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     d.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
     d.len_mode = 0;
     d.window = a->local_window_size;
+    d.win_cap = P.window_cache ? P.cap : 0;
     d.out = out[GQA_OUT_OUTPUT].data;
     d.part = reinterpret_cast<float*>(wsb + P.ws_q);
     d.B = P.B; d.N = P.N; d.kvN = P.kvN; d.H = P.H; d.cap = P.cap;
@@ -368,6 +391,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
   pp.write_q = 0;
   pp.write_kv = 1;
+  pp.win_cap = P.window_cache ? P.cap : 0;
   CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
                    "prep launch"));
 
@@ -404,6 +428,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   f.smooth = a->smooth_softmax == 1;
   f.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
   f.has_past = P.has_past;
+  f.win_cap = P.window_cache ? P.cap : 0;
   f.causal = a->causal;
   f.window = a->local_window_size;
   f.kv_rows = P.cap;
@@ -685,6 +710,7 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
   pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
   pp.write_q = 0;
   pp.write_kv = 1;
+  pp.win_cap = 0;
   CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
                    "prep launch"));
 

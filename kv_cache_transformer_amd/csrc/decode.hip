@@ -243,11 +243,16 @@ template <int HP, int R> struct DecTile<float, HP, R> {
 // ---------------------------------------------------------------------------
 // Key count n of sample b, the row of its appended token (-1: none) and the
 // first visible key (local window).
+// Keys of sample b: n buffer rows, the row of the new token (or -1), the
+// first key of the window, and the new token's absolute position.
 __device__ __forceinline__ void sample_keys(const DecodeParams& p, int b, int& n, int& newrow,
-                                            int& kstart) {
+                                            int& kstart, int& last_pos) {
   if (p.len_mode == 0) n = p.lens[b] + 1;
   else if (p.len_mode == 1) n = p.lens[0] + 1;
   else n = p.host_n;
+  last_pos = n - 1;
+  // sliding-window cache: the buffer's rows after the eviction
+  if (p.win_cap > 0) n = window_geom(n, 1, p.win_cap).fill;
   newrow = (p.k_new != nullptr) ? n - 1 : -1;
   if (n > p.cap) { n = p.cap; newrow = -1; }  // precondition violated: stay in bounds
   if (n < 0) { n = 0; newrow = -1; }
@@ -255,8 +260,8 @@ __device__ __forceinline__ void sample_keys(const DecodeParams& p, int b, int& n
 }
 
 __device__ __forceinline__ int sample_count(const DecodeParams& p, int b) {
-  int n, newrow, kstart;
-  sample_keys(p, b, n, newrow, kstart);
+  int n, newrow, kstart, last_pos;
+  sample_keys(p, b, n, newrow, kstart, last_pos);
   return max(n - kstart, 0);
 }
 
@@ -393,18 +398,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   // ---- which unit and which run of its keys (the same for both waves) -------
   // lane i reads the length of sample i once; the deal and this pair's sample
   // take it from there
-  int n_l = 0, newrow_l = -1, kstart_l = 0;
-  if (lane < p.B) sample_keys(p, lane, n_l, newrow_l, kstart_l);
+  int n_l = 0, newrow_l = -1, kstart_l = 0, last_l = 0;
+  if (lane < p.B) sample_keys(p, lane, n_l, newrow_l, kstart_l, last_l);
   const int64_t quota = deal_quota(p, ups, lane, max(n_l - kstart_l, 0));
   int b = 0, first = 0;
   const bool live = find_sample(p, ups, quota, pr, lane, max(n_l - kstart_l, 0), b, first);
-  int n = 0, newrow = -1, kstart = 0;
+  int n = 0, newrow = -1, kstart = 0, last_pos = 0;
   if (b < 64) {
     n = __shfl(n_l, b, 64);
     newrow = __shfl(newrow_l, b, 64);
     kstart = __shfl(kstart_l, b, 64);
+    last_pos = __shfl(last_l, b, 64);
   } else {
-    sample_keys(p, b, n, newrow, kstart);
+    sample_keys(p, b, n, newrow, kstart, last_pos);
   }
   const int c = live ? max(n - kstart, 0) : 0;
   const int nb = pairs_for(c, quota);
@@ -437,7 +443,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   const T* cs = static_cast<const T*>(p.cos);
   const T* sn = static_cast<const T*>(p.sin);
   const bool rot = cs != nullptr;
-  const int pos = min(max(n - 1, 0), max(p.rot_rows - 1, 0));  // rotary row of the new token
+  // rotary row of the new token: its absolute position (the last buffer row
+  // unless a sliding-window cache has evicted rows)
+  const int pos = min(max(last_pos, 0), max(p.rot_rows - 1, 0));
   const T* cs_row = rot ? cs + (int64_t)pos * half : nullptr;
   const T* sn_row = rot ? sn + (int64_t)pos * half : nullptr;
 

@@ -342,6 +342,7 @@ template <int MODE, int BN> struct FlashWork {
   int wrow0, wg_rows_end;    // this wave's first row; end of the workgroup's rows
   bool wave_rows;            // the wave owns at least one valid row
   int n_keys, past, pmin, pmax, k_lo, k_hi;
+  int rot_past;              // absolute position of query row 0 (rotary)
   int n_tiles, csr_lo, layout, tiles_per_block;
   int64_t row_base;          // varlen: first packed token of the sequence
   int64_t kv_base;           // K/V slab of (sample, kv head), in elements
@@ -385,12 +386,20 @@ template <int MODE, int BN> struct FlashWork {
     if (MODE == kDense) {
       n_keys = p.causal ? p.lens[b] + 1 : p.S;
       if (p.has_past) past = n_keys - p.S;
+      rot_past = past;
+      if (p.win_cap > 0) {
+        // sliding-window cache: keys are the buffer's rows after the eviction,
+        // masks work in row coordinates, rotary in absolute positions
+        n_keys = window_geom(p.lens[b] + 1, p.S, p.win_cap).fill;
+        past = n_keys - p.S;
+      }
     } else if (MODE == kCsr) {
       n_keys = p.key_total[b];
       if (p.has_past) past = n_keys - p.S;
     } else {
       n_keys = nrows;
     }
+    if (MODE != kDense) rot_past = past;
     pmin = past + r0;
     pmax = past + wg_rows_end - 1;
     k_lo = 0;
@@ -501,7 +510,7 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     const T* qp = (MODE == kVarlen)
                       ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
                       : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
-    prep_query(mma, qp, past + rr, p, qscale, lane);
+    prep_query(mma, qp, w.rot_past + rr, p, qscale, lane);
   }
   const int pos = past + qrow;  // absolute position of this lane's query
 
@@ -977,7 +986,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
     const f16* qp = (MODE == kVarlen)
                         ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
                         : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
-    prep_query(mma, qp, past + rr, p, qscale, lane);
+    prep_query(mma, qp, w.rot_past + rr, p, qscale, lane);
   }
   const int pos = past + qrow;
   const f16* bias = static_cast<const f16*>(p.bias);

@@ -37,6 +37,33 @@ struct PrepParams {
   int B, S, N, kvN, H, cap;
   int write_q;              // 1: write transformed queries
   int write_kv;             // 1: append k, v into the caches
+  int win_cap;              // > 0: sliding-window cache of this capacity (rows from window_geom)
+};
+
+// Sliding-window cache of capacity cap (GroupQueryAttention page, Attributes
+// table: sliding_window_cache): the buffer holds the most recent tokens,
+// oldest first.  For a sample with `total` tokens seen (the S new ones
+// included): `held` rows before the call, `drop` rows evicted from the front,
+// `fill` rows after the append, and the absolute position of row 0.
+struct WindowGeom {
+  int held, drop, fill, first;
+};
+__host__ __device__ inline WindowGeom window_geom(int total, int S, int cap) {
+  WindowGeom g;
+  const int before = total - S < 0 ? 0 : total - S;
+  g.held = before < cap ? before : cap;
+  g.drop = g.held + S - cap > 0 ? g.held + S - cap : 0;
+  g.fill = g.held - g.drop + S;
+  g.first = total - g.fill;
+  return g;
+}
+
+// Move the rows of each (sample, kv head) slab that survive the eviction to
+// the front of the buffer (rows [drop, held) to [0, held - drop)).
+struct WindowShiftParams {
+  void* kc; void* vc;               // (B, kvN, cap, H), shifted in place
+  const int32_t* lens;              // seqlens_k (total = lens[b] + 1)
+  int B, kvN, H, S, cap;
 };
 
 // Copy the live past rows [0, past_b) into a separate present buffer.
@@ -75,6 +102,7 @@ struct DecodeParams {
   int len_mode;             // 0: n_b = lens[b] + 1; 1: n_b = lens[0] + 1; 2: n_b = host_n
   int host_n;
   int window;               // >= 0: keys j >= (n_b - 1) - window
+  int win_cap;              // > 0: sliding-window cache of this capacity (len_mode 0 only)
   void* out;                // (B, N*H)
   void* qk;                 // (B, N, 1, host_n) scores after mask, or null
   float* part;              // (waves, hpw, HP + 4) per-wave partials: m, l, -, -, o[HP]
@@ -105,6 +133,7 @@ struct FlashParams {
   int smooth;
   const int32_t* lens;      // dense: seqlens_k (n_b = lens[b] + 1); varlen: per-sequence [start, end)
   int has_past;             // dense: 1 => past_b = n_b - S
+  int win_cap;              // dense: > 0 => sliding-window cache of this capacity
   int causal;
   int window;
   // CSR
@@ -161,6 +190,7 @@ constexpr int kGemmSchedMaxB = 3000;
 // launch error.
 hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s);
 hipError_t launch_copy_past(DType dt, const CopyPastParams& p, hipStream_t s);
+hipError_t launch_window_shift(DType dt, const WindowShiftParams& p, hipStream_t s);
 hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_combine(DType dt, int hp, const DecodeParams& p, hipStream_t s);
 hipError_t launch_flash(DType dt, int hp, const FlashParams& p, int grid_x, int grid_y,

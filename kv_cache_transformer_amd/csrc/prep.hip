@@ -49,7 +49,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
   int past = 0;
   if (p.pos_mode == 1) past = p.lens[b] + 1 - p.S;
   else if (p.pos_mode == 2) past = p.lens[b] - p.S;
-  const int pos = past + s;
+  const int pos = past + s;  // rotary position
+  // cache row: the position, or after the eviction of a sliding-window cache
+  const int crow = p.win_cap > 0 ? window_geom(p.lens[b] + 1, p.S, p.win_cap).fill - p.S + s : pos;
 
   const int nq = p.write_q ? p.N : 0;
   const int nk = p.write_kv ? p.kvN : 0;
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
   const T* cs = static_cast<const T*>(p.cos);
   const T* sn = static_cast<const T*>(p.sin);
   const int rpos = (cs != nullptr) ? min(max(pos, 0), p.rot_rows - 1) : 0;
-  const bool row_ok = pos >= 0 && pos < p.cap;
+  const bool row_ok = crow >= 0 && crow < p.cap;
 
   for (int base = 0; base < total; base += 4) {
     const int item = base + wave;
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
 
       if (kind == 2) {
         if (row_ok) {
-          T* dst = static_cast<T*>(p.vc) + (((int64_t)b * p.kvN + h) * p.cap + pos) * H;
+          T* dst = static_cast<T*>(p.vc) + (((int64_t)b * p.kvN + h) * p.cap + crow) * H;
           for (int d = lane; d < H; d += 64) dst[d] = src[d];
         }
       } else {
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
             if (d < H) dst[d] = from_f32<T>(y[u]);
           }
         } else if (row_ok) {
-          T* dst = static_cast<T*>(p.kc) + (((int64_t)b * p.kvN + h) * p.cap + pos) * H;
+          T* dst = static_cast<T*>(p.kc) + (((int64_t)b * p.kvN + h) * p.cap + crow) * H;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             int d = lane + 64 * u;
@@ -177,14 +179,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kv_kernel(PrepParams p) {
     int past = 0;
     if (p.pos_mode == 1) past = p.lens[b] + 1 - p.S;
     else if (p.pos_mode == 2) past = p.lens[b] - p.S;
-    const int pos = past + s;
-    const bool row_ok = live && pos >= 0 && pos < p.cap;
+    const int pos = past + s;  // rotary position
+    const int crow = p.win_cap > 0 ? window_geom(p.lens[b] + 1, p.S, p.win_cap).fill - p.S + s : pos;
+    const bool row_ok = live && crow >= 0 && crow < p.cap;
     const int d0 = CH * j;
     const T* ksrc = static_cast<const T*>(p.k) + tok * p.k_stride + p.k_off + (int64_t)kvh * H + d0;
     const T* vsrc = static_cast<const T*>(p.v) + tok * p.v_stride + p.v_off + (int64_t)kvh * H + d0;
     const uint4v kraw = *reinterpret_cast<const uint4v*>(ksrc);
     const uint4v vraw = *reinterpret_cast<const uint4v*>(vsrc);
-    const int64_t dst = (((int64_t)b * p.kvN + kvh) * p.cap + pos) * H + d0;
+    const int64_t dst = (((int64_t)b * p.kvN + kvh) * p.cap + crow) * H + d0;
     if (row_ok) *reinterpret_cast<uint4v*>(static_cast<T*>(p.vc) + dst) = vraw;
     float x[CH];
     load8_or_4(reinterpret_cast<const T*>(&kraw), x);
@@ -255,6 +258,46 @@ __global__ __launch_bounds__(256) void copy_past_kernel(CopyPastParams p) {
   }
 }
 
+// Sliding-window eviction: rows [drop, held) of every (sample, kv head) slab
+// move to [0, held - drop), in steps of kShiftRows rows.  A step loads all its
+// rows before any is stored (barrier), so a step's stores may overwrite its
+// own sources; the next step's sources lie above the rows stored so far
+// (drop >= 1), so steps need no further ordering.
+constexpr int kShiftThreads = 256, kShiftChunks = 4;  // 16-byte chunks per thread per step
+template <typename T>
+__global__ __launch_bounds__(kShiftThreads) void window_shift_kernel(WindowShiftParams p) {
+  const int slab = blockIdx.x;           // (b, kvh)
+  const int b = slab / p.kvN;
+  const WindowGeom g = window_geom(p.lens[b] + 1, p.S, p.cap);
+  const int keep = g.held - g.drop;
+  if (g.drop <= 0 || keep <= 0) return;  // nothing moves (block-uniform)
+  const int cpr = p.H * (int)sizeof(T) / 16;                   // chunks per row
+  const int rows_step = kShiftThreads * kShiftChunks / cpr;     // whole rows per step
+  for (int which = 0; which < 2; ++which) {
+    char* base = static_cast<char*>(which == 0 ? p.kc : p.vc) +
+                 (int64_t)slab * p.cap * p.H * sizeof(T);
+    for (int r0 = 0; r0 < keep; r0 += rows_step) {
+      uint4v v[kShiftChunks];
+#pragma unroll
+      for (int u = 0; u < kShiftChunks; ++u) {
+        const int idx = threadIdx.x + kShiftThreads * u;
+        const int r = r0 + idx / cpr, c = idx % cpr;
+        if (r < keep && r < r0 + rows_step)
+          v[u] = *reinterpret_cast<const uint4v*>(base + ((int64_t)(r + g.drop) * cpr + c) * 16);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kShiftChunks; ++u) {
+        const int idx = threadIdx.x + kShiftThreads * u;
+        const int r = r0 + idx / cpr, c = idx % cpr;
+        if (r < keep && r < r0 + rows_step)
+          *reinterpret_cast<uint4v*>(base + ((int64_t)r * cpr + c) * 16) = v[u];
+      }
+      __syncthreads();
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
@@ -279,6 +322,16 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
     hipLaunchKernelGGL(prep_kernel<f16>, grid, dim3(kPrepThreads), 0, s, p);
   else
     hipLaunchKernelGGL(prep_kernel<float>, grid, dim3(kPrepThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_shift(DType dt, const WindowShiftParams& p, hipStream_t s) {
+  const int slabs = p.B * p.kvN;
+  if (slabs == 0) return hipSuccess;
+  if (dt == DType::F16)
+    hipLaunchKernelGGL(window_shift_kernel<f16>, dim3(slabs), dim3(kShiftThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(window_shift_kernel<float>, dim3(slabs), dim3(kShiftThreads), 0, s, p);
   return hipGetLastError();
 }
 

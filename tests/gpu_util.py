@@ -138,7 +138,8 @@ def gqa_gpu(case, workspace=None):
         t.get("k_norm_weight"), num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"],
         causal=a["causal"], do_rotary=a["do_rotary"], local_window_size=a["local_window_size"],
         qk_norm_epsilon=a["qk_norm_epsilon"], scale=a["scale"],
-        smooth_softmax=a["smooth_softmax"], softcap=a["softcap"], present_key=pk,
+        smooth_softmax=a["smooth_softmax"], softcap=a["softcap"],
+        sliding_window_cache=a.get("sliding_window_cache", 0), present_key=pk,
         present_value=pv, workspace=workspace)
     torch.cuda.synchronize()
     return host(out), host(pk), host(pv)
@@ -154,8 +155,12 @@ def gqa_transformed_rows(case):
     if not (a["do_rotary"] or i.get("q_norm_weight") is not None):
         return m
     total = i["seqlens_k"].astype(np.int64) + 1
+    cap = pk.shape[2]
     for b in range(B):
         past = int(total[b]) - S if i.get("past_key") is not None else 0
+        if a.get("sliding_window_cache"):
+            held = min(past, cap)
+            past = held - max(0, held + S - cap)      # rows kept before the new ones
         m[b, :, past:past + S] = True
     return m
 

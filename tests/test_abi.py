@@ -122,7 +122,8 @@ def test_gqa_valid_shapes_give_workspace(lib):
                            ins.__setitem__(2, T(F16, 2, 8, 128))), -2),     # kv_S != S
     (lambda ins, outs, a: ins.__setitem__(12, T(F16, 64)), -1),             # unpaired norm
     (lambda ins, outs, a: a.update(k_quant_type=1), -2),                    # quantised cache
-    (lambda ins, outs, a: a.update(sliding_window_cache=1), -2),
+    (lambda ins, outs, a: a.update(sliding_window_cache=1), -1),            # needs a window
+    (lambda ins, outs, a: a.update(sliding_window_cache=1, local_window_size=4), -2),  # no shared past
     (lambda ins, outs, a: a.update(causal=0, local_window_size=4), -1),
     (lambda ins, outs, a: a.update(do_rotary=1), -1),                       # no cos/sin
     (lambda ins, outs, a: ins.__setitem__(10, T(F32, 1)), -2),              # k_scale
@@ -269,3 +270,21 @@ def test_packed_rules(lib):
     assert packed_call(lib, i2, [T(F16, 17, 32)])[0] == -1
     small = [T(F16, 2, 4), T(F16, 4, 12), T(F16, 12), T(I32, 1, 2), T(I32, 2), kb.Tensor()]
     assert packed_call(lib, small, [T(F16, 2, 4)])[0] == -2             # head size 2
+
+
+def test_gqa_window_cache_validation(lib):
+    # shared buffers of capacity 64: totals may exceed the capacity
+    ins, outs = gqa_args(past="shared", S=16, cap=64)
+    rc, _, msg = gqa_call(lib, ins, outs, total=500, sliding_window_cache=1, local_window_size=48)
+    assert rc == 0, msg
+    rc, _, msg = gqa_call(lib, ins, outs, total=500, sliding_window_cache=1, local_window_size=49)
+    assert rc == -1 and "capacity" in msg          # 64 < 49 + 16
+    ins, outs = gqa_args(past="concat", S=16, cap=64)
+    rc, _, _ = gqa_call(lib, ins, outs, total=60, sliding_window_cache=1, local_window_size=8)
+    assert rc == -2                                 # separate buffers
+    ins, outs = gqa_args(past="shared", S=16, cap=64, slots={8: T(F16, 2, 8, 16, 500)})
+    rc, _, _ = gqa_call(lib, ins, outs, total=500, sliding_window_cache=1, local_window_size=8)
+    assert rc == -2                                 # attention_bias
+    ins, outs = gqa_args(past="shared", S=16, cap=64)
+    rc, _, _ = gqa_call(lib, ins, outs, total=500, sliding_window_cache=2, local_window_size=8)
+    assert rc == -1

@@ -118,3 +118,27 @@ def test_workload_gqa_long_prefill_sampled_rows():
     print("gqa_long_prefill rows", rows, flush=True)
     err, n1 = _compare(case, rows)
     print(f"max |d| {err:.3g}; normed+rotated key elements off by 1 ulp: {n1}")
+
+
+# Sliding-window cache (GroupQueryAttention page, Attributes table): shared
+# buffers of capacity cap hold the most recent tokens; past_lens are the
+# tokens seen before the call (above cap, rows are evicted from the front).
+WINDOW = [
+    dict(dtype=F16, B=3, S=1, N=8, kvN=2, H=128, cap=300, window=200,
+         past_lens=[150, 299, 700], rotary=True, norm=True),
+    dict(dtype=F16, B=2, S=40, N=8, kvN=2, H=64, cap=120, window=64,
+         past_lens=[30, 500], softcap=10.0, sink=True),
+    dict(dtype=F16, B=2, S=64, N=8, kvN=2, H=128, cap=200, window=100,
+         past_lens=[150, 1000], rotary=True),
+    dict(dtype=F32, B=2, S=1, N=4, kvN=2, H=64, cap=64, window=32, past_lens=[10, 100]),
+    dict(dtype=F32, B=1, S=17, N=4, kvN=1, H=64, cap=50, window=33, past_lens=[90],
+         rotary=True, norm=True),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(WINDOW)))
+def test_window_cache_parity(idx):
+    case = _case(WINDOW[idx], 3000 + idx)
+    case["attrs"]["sliding_window_cache"] = 1
+    err, _ = _compare(case)
+    assert err >= 0
