@@ -156,6 +156,37 @@ def decode_workload(torch, kv, wl, args, timer):
                 kv_bytes=kv_bytes)
 
 
+def window_decode_workload(torch, kv, wl, args, timer):
+    """Decode steps on a full sliding-window cache: each call evicts one row
+    (the shift moves the other 1023 rows of every slab) and attends the 1024
+    rows held.  Repeated calls shift the same amount, so every call costs the
+    same."""
+    case = wl.gqa_window_decode()
+    i = case["inputs"]
+    a = case["attrs"]
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in i.items() if k not in ("present_key", "present_value")}
+    out = torch.empty_like(t["query"])
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def step(n):
+        kv.gqa_attention(t["query"], t["key"], t["value"], t["past_key"], t["past_value"],
+                         t["seqlens_k"], case["total_sequence_length"], t["cos_cache"],
+                         t["sin_cache"], num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"],
+                         do_rotary=1, local_window_size=a["local_window_size"],
+                         sliding_window_cache=1, output=out, present_key=t["past_key"],
+                         present_value=t["past_value"], workspace=ws)
+
+    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    B, kvN, H = 16, 8, 128
+    cap = i["past_key"].shape[2]
+    row = H * 2                                      # bytes of one fp16 row
+    shift_bytes = B * kvN * 2 * (cap - 1) * row * 2  # K and V: read and written once
+    read_bytes = B * kvN * 2 * cap * row             # rows attended (K and V)
+    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, shift_bytes=shift_bytes,
+                read_bytes=read_bytes)
+
+
 def causal_window_pairs(S, W):
     p = np.arange(S, dtype=np.int64)
     return int(np.minimum(p + 1, W + 1 if W >= 0 else S).sum())
@@ -310,6 +341,8 @@ TRAFFIC_KERNELS = [
      "sparse_prompt"),
     ("qkv_gemm_packed_varlen", r"qkv_gemm_kernelIDF16_", "kv_cache_transformer_amd/csrc/packed.hip",
      "packed_varlen"),
+    ("window_shift_gqa_window_decode", r"window_shift_kernelIDF16_", "kv_cache_transformer_amd/csrc/prep.hip",
+     "gqa_window_decode"),
 ]
 
 
@@ -383,7 +416,7 @@ def summarise_counters(d, cmd):
     import glob
     import re
     pat = re.compile(r"(flash_pipe_kernel|flash_kernel|decode_kernel|decode_combine_kernel|qkv_gemm_kernel|prep_kv_kernel|"
-                     r"prep_kernel|packed_sched_kernel)(?:I(DF16_|f)(?:Li(\d+)ELi(\d+)ELi(\d+))?)?")
+                     r"window_shift_kernel|prep_kernel|packed_sched_kernel)(?:I(DF16_|f)(?:Li(\d+)ELi(\d+)ELi(\d+))?)?")
     agg, dur = {}, {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
@@ -495,6 +528,9 @@ def main():
     if want("sparse_prompt"):
         res["sparse_prompt"] = sparse_workload(torch, kv, wl, args, Timer(torch, lib, 2, hip))
         print("# sparse_prompt done", file=sys.stderr, flush=True)
+    if want("gqa_window_decode"):
+        res["gqa_window_decode"] = window_decode_workload(torch, kv, wl, args, Timer(torch, lib, 5, hip))
+        print("# gqa_window_decode done", file=sys.stderr, flush=True)
     if want("packed_varlen"):
         res["packed_varlen"] = packed_workload(torch, kv, wl, args, Timer(torch, lib, 4, hip))
         print("# packed_varlen done", file=sys.stderr, flush=True)
@@ -540,6 +576,21 @@ def main():
                          "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tf_g / MFMA_F16_PEAK_TFS, 4), "kernel_ms": round(r["kern_ms"], 4),
                          "algorithmic_flops": r["gemm_flops"], "traffic": traffic_for("qkv_gemm_packed_varlen")}}
+
+    if "gqa_window_decode" in res:
+        r = res["gqa_window_decode"]
+        tot = r["shift_bytes"] + r["read_bytes"]
+        gbs_k = r["shift_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
+        workloads["gqa_window_decode"] = {
+            "config": "B16 N32 kvN8 H128 fp16, sliding-window cache 1024 (window 1023), "
+                      "past tokens U[1024,4095], rotary",
+            "call_ms": round(r["call_ms"], 4),
+            "call_GBs": round(tot / (r["call_ms"] * 1e-3) / 1e9, 2),
+            "algorithmic_bytes": tot,
+            "roofline": {"bound": "hbm", "kernel": "window_shift", "achieved": round(gbs_k, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
+                         "kernel_ms": round(r["kern_ms"], 4), "algorithmic_bytes": r["shift_bytes"],
+                         "traffic": traffic_for("window_shift_gqa_window_decode")}}
 
     line = {"metric": "GQA prefill TFLOP/s and decode KV GB/s on 1 MI355X, % of roofline",
             "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

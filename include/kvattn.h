@@ -97,6 +97,7 @@ int32_t kvattn_version(void);
  *   KVATTN_PROFILE_FLASH    tiled attention kernel (prefill, sparse, packed)
  *   KVATTN_PROFILE_PREP     norm/rotary/append kernel
  *   KVATTN_PROFILE_GEMM     packed QKV projection GEMM
+ *   KVATTN_PROFILE_SHIFT    sliding-window cache eviction (row shift)
  * Passing NULL events turns the hook off.  The library never creates or
  * destroys the events.
  */
@@ -104,7 +105,8 @@ enum {
   KVATTN_PROFILE_DECODE = 1,
   KVATTN_PROFILE_FLASH = 2,
   KVATTN_PROFILE_PREP = 3,
-  KVATTN_PROFILE_GEMM = 4
+  KVATTN_PROFILE_GEMM = 4,
+  KVATTN_PROFILE_SHIFT = 5
 };
 void kvattn_profile_events(void* start, void* stop, int32_t kind);
 

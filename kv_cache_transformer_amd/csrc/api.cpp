@@ -324,7 +324,8 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     w.vc = cv.data;
     w.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
     w.B = P.B; w.kvN = P.kvN; w.H = P.H; w.S = P.S; w.cap = P.cap;
-    CHECK(hip_status(launch_window_shift(dt, w, st), "window shift launch"));
+    CHECK(hip_status(profiled(KVATTN_PROFILE_SHIFT, st, [&] { return launch_window_shift(dt, w, st); }),
+                     "window shift launch"));
   }
 
   const kvattn_tensor& bias = in[GQA_IN_ATTENTION_BIAS];

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void copy_past_kernel(CopyPastParams p) {
 // rows before any is stored (barrier), so a step's stores may overwrite its
 // own sources; the next step's sources lie above the rows stored so far
 // (drop >= 1), so steps need no further ordering.
-constexpr int kShiftThreads = 256, kShiftChunks = 4;  // 16-byte chunks per thread per step
+constexpr int kShiftThreads = 1024, kShiftChunks = 8;  // 16-byte chunks per thread per step
 template <typename T>
 __global__ __launch_bounds__(kShiftThreads) void window_shift_kernel(WindowShiftParams p) {
   const int slab = blockIdx.x;           // (b, kvh)

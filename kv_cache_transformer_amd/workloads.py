@@ -164,6 +164,30 @@ def gqa_decode(seed=2, batch=16, cap=4096):
                 total_sequence_length=int(past.max()) + 1, shared=True)
 
 
+def gqa_window_decode(seed=6, batch=16, cap=1024, window=1023, max_total=4096):
+    """GroupQueryAttention decode on a sliding-window cache: B=16 N=32 kvN=8
+    H=128 fp16, shared window buffers of capacity 1024, window 1023, tokens
+    seen before the step uniform in [1024, 4095] (every step evicts one row),
+    rotary at absolute positions."""
+    rng = np.random.default_rng(seed)
+    B, S, N, kvN, H = batch, 1, 32, 8, 128
+    past = rng.integers(cap, max_total, B)
+    q = normal(rng, (B, S, N * H), F16)
+    k = normal(rng, (B, S, kvN * H), F16)
+    v = normal(rng, (B, S, kvN * H), F16)
+    pk = normal(rng, (B, kvN, cap, H), F16)
+    pv = normal(rng, (B, kvN, cap, H), F16)
+    c, s_ = rope_cache(max_total, H, F16)
+    inputs = dict(query=q, key=k, value=v, past_key=pk, past_value=pv,
+                  present_key=pk, present_value=pv,
+                  seqlens_k=past.astype(np.int32), cos_cache=c, sin_cache=s_)
+    attrs = dict(num_heads=N, kv_num_heads=kvN, causal=1, do_rotary=1,
+                 local_window_size=window, qk_norm_epsilon=1e-6, scale=0.0,
+                 smooth_softmax=-1, softcap=0.0, sliding_window_cache=1)
+    return dict(op="gqa", name="gqa_window_decode", inputs=inputs, attrs=attrs,
+                total_sequence_length=int(past.max()) + 1, shared=True)
+
+
 def gqa_long_prefill(seed=3, batch=4, seq=4096):
     """GroupQueryAttention prompt: B=4 S=4096 N=32 kvN=8 H=128 fp16, window 1024,
     softcap 50, head sink, Q/K RMSNorm, rotary."""
@@ -379,6 +403,7 @@ def packed_varlen(seed=5, n_seq=64, padded_seq=512):
 WORKLOADS = {
     "gqa_prompt_small": gqa_prompt_small,
     "gqa_decode": gqa_decode,
+    "gqa_window_decode": gqa_window_decode,
     "gqa_long_prefill": gqa_long_prefill,
     "sparse_prompt": sparse_prompt,
     "packed_varlen": packed_varlen,

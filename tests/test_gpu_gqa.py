@@ -142,3 +142,10 @@ def test_window_cache_parity(idx):
     case["attrs"]["sliding_window_cache"] = 1
     err, _ = _compare(case)
     assert err >= 0
+
+
+def test_workload_window_decode():
+    """The sliding-window decode workload at full size, every output checked."""
+    case = wl.gqa_window_decode()
+    err, _ = _compare(case)
+    assert err >= 0

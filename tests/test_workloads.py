@@ -51,3 +51,13 @@ def test_decode_workload(name):
     assert i["present_key"] is i["past_key"]
     assert i["seqlens_k"].min() >= 1024 and i["seqlens_k"].max() <= 4095
     assert c["total_sequence_length"] == int(i["seqlens_k"].max()) + 1
+
+
+def test_window_decode_workload():
+    c = wl.WORKLOADS["gqa_window_decode"]()
+    i, a = c["inputs"], c["attrs"]
+    assert i["past_key"].shape == (16, 8, 1024, 128) and i["present_key"] is i["past_key"]
+    assert a["sliding_window_cache"] == 1 and a["local_window_size"] == 1023
+    # every sample has seen at least a full buffer: each step evicts one row
+    assert i["seqlens_k"].min() >= 1024 and i["seqlens_k"].max() <= 4095
+    assert i["cos_cache"].shape[0] >= c["total_sequence_length"]
