@@ -241,8 +241,6 @@ template <int HP, int R> struct DecTile<float, HP, R> {
 // ---------------------------------------------------------------------------
 // lengths and the deal of waves
 // ---------------------------------------------------------------------------
-// Key count n of sample b, the row of its appended token (-1: none) and the
-// first visible key (local window).
 // Keys of sample b: n buffer rows, the row of the new token (or -1), the
 // first key of the window, and the new token's absolute position.
 __device__ __forceinline__ void sample_keys(const DecodeParams& p, int b, int& n, int& newrow,

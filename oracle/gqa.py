@@ -6,6 +6,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 import numpy as np
 
 from .common import attend, default_scale, rms_norm, rotary, round_to, softcap
+from . import quant
 
 
 def gqa(query, key, value, *, seqlens_k, total_sequence_length,
@@ -15,7 +16,8 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
         q_norm_weight=None, k_norm_weight=None,
         num_heads, kv_num_heads, causal=1, do_rotary=0, local_window_size=-1,
         qk_norm_epsilon=1e-6, scale=0.0, smooth_softmax=-1, softcap_value=0.0,
-        sliding_window_cache=0, query_rows=None):
+        sliding_window_cache=0, k_scale=None, v_scale=None, k_quant_type=0, v_quant_type=0,
+        kv_cache_bit_width=0, query_rows=None, info=None):
     """Grouped-query attention with a BNSH key/value cache.
 
     Follows the GroupQueryAttention page: Description, Inputs, Outputs and
@@ -73,6 +75,15 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
         key in any new query's window is still in the buffer; the attention
         bias is not supported with this attribute.
 
+    With ``kv_cache_bit_width`` b = 8 or 4 (``k_quant_type``/``v_quant_type``
+    PER_TENSOR = 1 or PER_CHANNEL = 2, scales ``k_scale``/``v_scale``) the
+    caches hold codes (``oracle.quant``): attention reads code * scale, and
+    the new rows are stored as codes of the transformed keys and the values
+    (T = float32; the quotient by the scale is taken in float32).  If ``info``
+    is a dict it receives ``k_quotient`` and ``v_quotient``, the float32
+    quotients of the new rows (B, kvN, S, H), from which a caller can tell how
+    close each code is to a rounding boundary.
+
     ``query_rows`` (optional iterable of s indices) restricts the attention
     output to those query rows (the cache is always updated in full); the
     output then has shape (B, len(query_rows), num_heads * H).
@@ -103,6 +114,22 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
     pk_out = np.array(present_key, copy=True)
     pv_out = np.array(present_value, copy=True)
     cap = pk_out.shape[2]
+    bits = int(kv_cache_bit_width)
+    if bits not in (0, 4, 8):
+        raise ValueError("kv_cache_bit_width must be 0, 4 or 8")
+    if bits:
+        want = (np.int8, H) if bits == 8 else (np.uint8, H // 2)
+        for arr in (pk_out, pv_out) + ((np.asarray(past_key), np.asarray(past_value))
+                                       if past_key is not None else ()):
+            if arr.dtype != want[0] or arr.shape[3] != want[1]:
+                raise ValueError("quantised caches hold int8 (8 bits) or packed uint8 (4 bits, H/2 bytes per row)")
+        ks = quant.channel_scales(k_scale, int(k_quant_type), kvN, H)
+        vs = quant.channel_scales(v_scale, int(v_quant_type), kvN, H)
+        if info is not None:
+            info["k_quotient"] = np.zeros((B, kvN, S, H))
+            info["v_quotient"] = np.zeros((B, kvN, S, H))
+    elif int(k_quant_type) or int(v_quant_type):
+        raise ValueError("quantisation types need kv_cache_bit_width 8 or 4")
     total_b = np.asarray(seqlens_k, dtype=np.int64) + 1
     win = bool(sliding_window_cache)
     if past_key is not None:
@@ -163,8 +190,17 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
             if past_key is not None and pb > 0:
                 pk_out[b, :, :pb, :] = np.asarray(past_key)[b, :, :pb, :]
                 pv_out[b, :, :pb, :] = np.asarray(past_value)[b, :, :pb, :]
-        pk_out[b, :, pb:pb + S, :] = round_to(k[b].transpose(1, 0, 2), dtype)
-        pv_out[b, :, pb:pb + S, :] = round_to(v[b].transpose(1, 0, 2), dtype)
+        if bits:
+            kc = quant.quantize(k[b].transpose(1, 0, 2), ks[:, None, :], bits)
+            vc = quant.quantize(v[b].transpose(1, 0, 2), vs[:, None, :], bits)
+            if info is not None:
+                info["k_quotient"][b] = quant.quotient(k[b].transpose(1, 0, 2), ks[:, None, :])
+                info["v_quotient"][b] = quant.quotient(v[b].transpose(1, 0, 2), vs[:, None, :])
+            pk_out[b, :, pb:pb + S, :] = quant.store_codes(kc, bits)
+            pv_out[b, :, pb:pb + S, :] = quant.store_codes(vc, bits)
+        else:
+            pk_out[b, :, pb:pb + S, :] = round_to(k[b].transpose(1, 0, 2), dtype)
+            pv_out[b, :, pb:pb + S, :] = round_to(v[b].transpose(1, 0, 2), dtype)
 
     rows = np.arange(S) if query_rows is None else np.asarray(list(query_rows), dtype=np.int64)
     out = np.zeros((B, len(rows), N, H), dtype=np.float64)
@@ -192,8 +228,12 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
             vis = np.ones((len(rows), n_keys), dtype=bool)
         for h in range(N):
             kh = h // g
-            keys = pk_out[b, kh, :n_keys, :].astype(np.float64)
-            vals = pv_out[b, kh, :n_keys, :].astype(np.float64)
+            if bits:
+                keys = quant.dequantize(quant.load_codes(pk_out[b, kh, :n_keys, :], bits), ks[kh])
+                vals = quant.dequantize(quant.load_codes(pv_out[b, kh, :n_keys, :], bits), vs[kh])
+            else:
+                keys = pk_out[b, kh, :n_keys, :].astype(np.float64)
+                vals = pv_out[b, kh, :n_keys, :].astype(np.float64)
             x = sc * (q[b, rows, h, :] @ keys.T)
             x = softcap(x, softcap_value)
             if bias is not None:
