@@ -42,7 +42,9 @@
  *
  * Storage types.  T is float32 or float16 for every operator (bfloat16 and
  * float8 are not implemented, as on the pages).  Kernels accumulate in
- * float32.  Head sizes must be multiples of 8 and at most 256.
+ * float32.  Head sizes must be multiples of 8 and at most 256.  The
+ * GroupQueryAttention caches may instead hold int8 codes or packed uint8
+ * nibbles (quantised caches, below).
  */
 #ifndef KVATTN_H_
 #define KVATTN_H_
@@ -70,7 +72,9 @@ typedef enum kvattn_dtype {
   KVATTN_DT_NONE = 0,
   KVATTN_DT_F32 = 1,
   KVATTN_DT_F16 = 2,
-  KVATTN_DT_I32 = 3
+  KVATTN_DT_I32 = 3,
+  KVATTN_DT_I8 = 4,    /* int8 cache codes */
+  KVATTN_DT_U8 = 5     /* uint8: two packed 4-bit cache codes */
 } kvattn_dtype;
 
 typedef struct kvattn_tensor {
@@ -121,15 +125,15 @@ typedef enum gqa_input {
   GQA_IN_QUERY = 0,          /* T (B, S, N*H)                                   required */
   GQA_IN_KEY,                /* T (B, S, kvN*H)                                 required */
   GQA_IN_VALUE,              /* T (B, S, kvN*H)                                 required */
-  GQA_IN_PAST_KEY,           /* T (B, kvN, past_seq or capacity, H)             optional */
-  GQA_IN_PAST_VALUE,         /* T like past_key                                 optional */
+  GQA_IN_PAST_KEY,           /* T_CACHE (B, kvN, past_seq or capacity, Hc)      optional */
+  GQA_IN_PAST_VALUE,         /* T_CACHE like past_key                           optional */
   GQA_IN_SEQLENS_K,          /* int32 (B): total length - 1 per sample (device) required */
   GQA_IN_COS_CACHE,          /* T (max_seq, H/2)                                optional */
   GQA_IN_SIN_CACHE,          /* T (max_seq, H/2)                                optional */
   GQA_IN_ATTENTION_BIAS,     /* T (B|1, N|1, S, total_sequence_length)          optional */
   GQA_IN_HEAD_SINK,          /* T (N)                                           optional */
-  GQA_IN_K_SCALE,            /* float32; quantised caches only: UNSUPPORTED if given */
-  GQA_IN_V_SCALE,            /* float32; quantised caches only: UNSUPPORTED if given */
+  GQA_IN_K_SCALE,            /* float32 (1) PER_TENSOR or (kvN*H) PER_CHANNEL   quantised caches */
+  GQA_IN_V_SCALE,            /* float32, like k_scale with v_quant_type         quantised caches */
   GQA_IN_Q_NORM_WEIGHT,      /* T (H), paired with k_norm_weight                optional */
   GQA_IN_K_NORM_WEIGHT,      /* T (H), paired with q_norm_weight                optional */
   GQA_NUM_INPUTS
@@ -137,8 +141,8 @@ typedef enum gqa_input {
 
 typedef enum gqa_output {
   GQA_OUT_OUTPUT = 0,        /* T (B, S, N*H)                                   required */
-  GQA_OUT_PRESENT_KEY,       /* T (B, kvN, present_seq, H)                      required */
-  GQA_OUT_PRESENT_VALUE,     /* T like present_key                              required */
+  GQA_OUT_PRESENT_KEY,       /* T_CACHE (B, kvN, present_seq, Hc)               required */
+  GQA_OUT_PRESENT_VALUE,     /* T_CACHE like present_key                        required */
   GQA_NUM_OUTPUTS
 } gqa_output;
 
@@ -153,10 +157,16 @@ typedef struct gqa_attrs {
   int32_t sliding_window_cache;  /* default 0; 1 = window buffers evicting from the front (below) */
   int32_t smooth_softmax;        /* default -1; 1 adds exp(0) to the denominator */
   float softcap;                 /* default 0 = off */
-  int32_t k_quant_type;          /* 0 = NONE (default); other values UNSUPPORTED */
-  int32_t v_quant_type;          /* 0 = NONE (default); other values UNSUPPORTED */
-  int32_t kv_cache_bit_width;    /* 0 (default); quantised caches UNSUPPORTED */
+  int32_t k_quant_type;          /* gqa_quant_type, default NONE */
+  int32_t v_quant_type;          /* gqa_quant_type, default NONE */
+  int32_t kv_cache_bit_width;    /* 0 (default, float caches), 8 or 4 */
 } gqa_attrs;
+
+typedef enum gqa_quant_type {
+  GQA_QUANT_NONE = 0,
+  GQA_QUANT_PER_TENSOR = 1,      /* one float32 scale */
+  GQA_QUANT_PER_CHANNEL = 2      /* kv_num_heads * head_size scales, head-major */
+} gqa_quant_type;
 
 /* Fill the page defaults; num_heads and kv_num_heads are set to 0 (required). */
 void gqa_attrs_default(gqa_attrs* attrs);
@@ -169,7 +179,7 @@ void gqa_attrs_default(gqa_attrs* attrs);
  *   q, k  <- per-head RMSNorm (both norm weights given), then NeoX rotary at
  *            position past_b + s (do_rotary);
  *   present rows [0, past_b) = past rows, rows [past_b, past_b + S) = new k, v
- *            (rounded to T), other rows untouched;
+ *            (rounded to T, or quantised), other rows untouched;
  *   keys j < total_b visible with j <= past_b + s (causal) and
  *            j >= past_b + s - local_window_size (window >= 0); bidirectional
  *            (causal 0) sees all S new keys;
@@ -194,9 +204,24 @@ void gqa_attrs_default(gqa_attrs* attrs);
  * local_window_size > 0, C >= local_window_size + S and shared buffers; no
  * attention_bias.
  *
- * UNSUPPORTED: quantised caches (k/v_quant_type, kv_cache_bit_width, k/v
- * scales), kv sequence length != S, sliding_window_cache with separate
- * past/present buffers or with attention_bias.
+ * Quantised caches (GroupQueryAttention page, Attributes table: k_quant_type,
+ * v_quant_type, kv_cache_bit_width; Inputs table: k_scale, v_scale and the
+ * int4 packing).  With kv_cache_bit_width 8 or 4 both quant types must be
+ * PER_TENSOR or PER_CHANNEL, both scales are given, and query, key, value,
+ * output and the other T inputs are float32.  T_CACHE is int8 (KVATTN_DT_I8,
+ * Hc = H) for 8 bits, uint8 (KVATTN_DT_U8, Hc = H/2) for 4 bits, where byte i
+ * of a row holds dim 2i in its low nibble and dim 2i+1 in its high nibble,
+ * each as code + 8.  A cache element stands for code * scale (the scale of
+ * its kv head and dim); a new key (after norm and rotary) or value x is
+ * stored as code = clamp(rint(x / scale), -2^(b-1), 2^(b-1) - 1), the
+ * quotient in float32 and rounded half to even.  Scales must be positive and
+ * finite (other values give unspecified codes).  int8 serves the prompt (no
+ * past) and decode (a past, S = 1, shared or separate buffers); int4 is
+ * prompt-only.
+ *
+ * UNSUPPORTED: kv sequence length != S; sliding_window_cache with separate
+ * past/present buffers, with attention_bias or with a quantised cache; int4
+ * with a past; int8 with a past and S > 1.
  */
 int32_t gqa_attention(const gqa_attrs* attrs,
                       const kvattn_tensor* inputs, int32_t n_inputs,

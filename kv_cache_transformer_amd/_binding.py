@@ -9,7 +9,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkvattn.so")
 
 # dtype codes (kvattn_dtype)
-DT_NONE, DT_F32, DT_F16, DT_I32 = 0, 1, 2, 3
+DT_NONE, DT_F32, DT_F16, DT_I32, DT_I8, DT_U8 = 0, 1, 2, 3, 4, 5
+# gqa_quant_type
+QUANT_NONE, QUANT_PER_TENSOR, QUANT_PER_CHANNEL = 0, 1, 2
 
 # slot counts (include/kvattn.h)
 GQA_NUM_INPUTS, GQA_NUM_OUTPUTS = 14, 3
@@ -133,7 +135,8 @@ def _desc(t):
     if t.dim() > 4:
         raise ValueError("at most 4 dims")
     d.data = t.data_ptr()
-    d.dtype = {torch.float32: DT_F32, torch.float16: DT_F16, torch.int32: DT_I32}.get(t.dtype, -1)
+    d.dtype = {torch.float32: DT_F32, torch.float16: DT_F16, torch.int32: DT_I32,
+               torch.int8: DT_I8, torch.uint8: DT_U8}.get(t.dtype, -1)
     d.rank = t.dim()
     for i, s in enumerate(t.shape):
         d.dims[i] = int(s)
@@ -175,17 +178,20 @@ def _ptr(t):
 def gqa_attention(query, key, value, past_key=None, past_value=None, seqlens_k=None,
                   total_sequence_length=None, cos_cache=None, sin_cache=None,
                   attention_bias=None, head_sink=None, q_norm_weight=None, k_norm_weight=None,
+                  k_scale=None, v_scale=None,
                   *, num_heads, kv_num_heads, causal=1, do_rotary=0, local_window_size=-1,
                   qk_norm_epsilon=1e-6, scale=0.0, smooth_softmax=-1, softcap=0.0,
-                  sliding_window_cache=0, output=None, present_key=None, present_value=None,
+                  sliding_window_cache=0, k_quant_type=0, v_quant_type=0, kv_cache_bit_width=0,
+                  output=None, present_key=None, present_value=None,
                   workspace=None, stream=None):
     """GroupQueryAttention (include/kvattn.h, gqa_attention).
 
     ``total_sequence_length`` is a host int.  Pass ``present_key=past_key``
     (and likewise for values) to append in place to a shared buffer; when the
     presents are None they are allocated (zero-filled) with a sequence axis of
-    past_seq + S (or S without a past).  Returns (output, present_key,
-    present_value).
+    past_seq + S (or S without a past).  With ``kv_cache_bit_width`` 8 or 4
+    the caches are int8 / packed uint8 tensors and ``k_scale``/``v_scale``
+    float32 tensors.  Returns (output, present_key, present_value).
     """
     torch = _torch()
     lib = library()
@@ -197,7 +203,9 @@ def gqa_attention(query, key, value, past_key=None, past_value=None, seqlens_k=N
         output = torch.empty_like(query)
     if present_key is None:
         seq = (past_key.shape[2] if past_key is not None else 0) + S
-        present_key = torch.zeros((B, kv_num_heads, seq, H), dtype=query.dtype, device=query.device)
+        cdt = {8: torch.int8, 4: torch.uint8}.get(kv_cache_bit_width, query.dtype)
+        hc = H // 2 if kv_cache_bit_width == 4 else H
+        present_key = torch.zeros((B, kv_num_heads, seq, hc), dtype=cdt, device=query.device)
     if present_value is None:
         present_value = torch.zeros_like(present_key)
     a = GqaAttrs()
@@ -207,9 +215,11 @@ def gqa_attention(query, key, value, past_key=None, past_value=None, seqlens_k=N
     a.qk_norm_epsilon, a.scale = qk_norm_epsilon, scale
     a.smooth_softmax, a.softcap = smooth_softmax, softcap
     a.sliding_window_cache = sliding_window_cache
+    a.k_quant_type, a.v_quant_type = k_quant_type, v_quant_type
+    a.kv_cache_bit_width = kv_cache_bit_width
     ins = _array([_desc(query), _desc(key), _desc(value), _desc(past_key), _desc(past_value),
                   _desc(seqlens_k), _desc(cos_cache), _desc(sin_cache), _desc(attention_bias),
-                  _desc(head_sink), Tensor(), Tensor(), _desc(q_norm_weight),
+                  _desc(head_sink), _desc(k_scale), _desc(v_scale), _desc(q_norm_weight),
                   _desc(k_norm_weight)])
     outs = _array([_desc(output), _desc(present_key), _desc(present_value)])
     nbytes = ctypes.c_size_t(0)

@@ -160,12 +160,41 @@ struct GqaPlan {
   int dt;
   bool has_past, shared, decode, q_transform;
   bool window_cache;  // sliding-window cache: fixed-size buffers evicting from the front
+  int bits;           // quantised caches: 8 (int8) or 4 (packed nibbles); 0 = float caches
+  bool k_pc, v_pc;    // per-channel scales
   int total;
   // decode
   int head_groups, hpw;
   int64_t waves;
-  size_t ws_q, ws_part, ws_total;
+  size_t ws_q, ws_part, ws_deq, ws_total;
 };
+
+// Quantised-cache attributes and scales (GroupQueryAttention page,
+// Attributes table: k_quant_type, v_quant_type, kv_cache_bit_width; Inputs
+// table: k_scale, v_scale, and the requirement of float32 query/key/value
+// and output; int4 caches are prompt-only).
+int gqa_validate_quant(const gqa_attrs* a, const kvattn_tensor* in, int dt, GqaPlan& P) {
+  const kvattn_tensor& ksc = in[GQA_IN_K_SCALE];
+  const kvattn_tensor& vsc = in[GQA_IN_V_SCALE];
+  P.bits = 0;
+  P.k_pc = P.v_pc = false;
+  if (a->kv_cache_bit_width == 0 && a->k_quant_type == 0 && a->v_quant_type == 0 && !has(ksc) && !has(vsc))
+    return KVATTN_OK;
+  if (a->kv_cache_bit_width != 8 && a->kv_cache_bit_width != 4)
+    return fail(KVATTN_ERR_INVALID_ARG, "kv_cache_bit_width %d: quantised caches take 8 or 4", a->kv_cache_bit_width);
+  for (int t : {a->k_quant_type, a->v_quant_type})
+    if (t != GQA_QUANT_PER_TENSOR && t != GQA_QUANT_PER_CHANNEL)
+      return fail(KVATTN_ERR_INVALID_ARG, "quantised caches need k_quant_type and v_quant_type PER_TENSOR (1) or PER_CHANNEL (2)");
+  if (dt != KVATTN_DT_F32)
+    return fail(KVATTN_ERR_INVALID_ARG, "quantised caches need float32 query, key, value and output");
+  if (!has(ksc) || !has(vsc)) return fail(KVATTN_ERR_INVALID_ARG, "quantised caches need k_scale and v_scale");
+  P.k_pc = a->k_quant_type == GQA_QUANT_PER_CHANNEL;
+  P.v_pc = a->v_quant_type == GQA_QUANT_PER_CHANNEL;
+  CHECK(check(ksc, "k_scale", KVATTN_DT_F32, 1, {P.k_pc ? (int64_t)P.kvN * P.H : 1}));
+  CHECK(check(vsc, "v_scale", KVATTN_DT_F32, 1, {P.v_pc ? (int64_t)P.kvN * P.H : 1}));
+  P.bits = a->kv_cache_bit_width;
+  return KVATTN_OK;
+}
 
 int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int total,
                  const kvattn_tensor* out, int n_out, GqaPlan& P) {
@@ -190,9 +219,11 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   P.H = (int)(q.dims[2] / P.N);
   CHECK(check_head_size(P.H, "gqa_attention"));
   P.HP = padded_head(P.H);
-  if (a->k_quant_type != 0 || a->v_quant_type != 0 || a->kv_cache_bit_width != 0 ||
-      has(in[GQA_IN_K_SCALE]) || has(in[GQA_IN_V_SCALE]))
-    return fail(KVATTN_ERR_UNSUPPORTED, "quantised key/value caches are not implemented");
+  CHECK(gqa_validate_quant(a, in, dt, P));
+  // cache element type and row width (elements): int8 rows of H, or H / 2
+  // bytes of packed nibbles
+  const int cdt = P.bits == 8 ? KVATTN_DT_I8 : (P.bits == 4 ? KVATTN_DT_U8 : dt);
+  const int64_t Hc = P.bits == 4 ? P.H / 2 : P.H;
   if (a->sliding_window_cache != 0 && a->sliding_window_cache != 1)
     return fail(KVATTN_ERR_INVALID_ARG, "sliding_window_cache must be 0 or 1");
   P.window_cache = a->sliding_window_cache == 1;
@@ -218,8 +249,8 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   P.has_past = has(pk);
   if (P.has_past) {
     if (!a->causal) return fail(KVATTN_ERR_UNSUPPORTED, "bidirectional attention takes no past cache");
-    CHECK(check(pk, "past_key", dt, 4, {P.B, P.kvN, -1, P.H}));
-    CHECK(check(pv, "past_value", dt, 4, {P.B, P.kvN, pk.dims[2], P.H}));
+    CHECK(check(pk, "past_key", cdt, 4, {P.B, P.kvN, -1, Hc}));
+    CHECK(check(pv, "past_value", cdt, 4, {P.B, P.kvN, pk.dims[2], Hc}));
     P.past_seq = (int)pk.dims[2];
   } else {
     P.past_seq = 0;
@@ -235,14 +266,20 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   const kvattn_tensor& cv = out[GQA_OUT_PRESENT_VALUE];
   if (!has(o) || !has(ck) || !has(cv)) return fail(KVATTN_ERR_INVALID_ARG, "output, present_key and present_value are required");
   CHECK(check(o, "output", dt, 3, {P.B, P.S, (int64_t)P.N * P.H}));
-  CHECK(check(ck, "present_key", dt, 4, {P.B, P.kvN, -1, P.H}));
-  CHECK(check(cv, "present_value", dt, 4, {P.B, P.kvN, ck.dims[2], P.H}));
+  CHECK(check(ck, "present_key", cdt, 4, {P.B, P.kvN, -1, Hc}));
+  CHECK(check(cv, "present_value", cdt, 4, {P.B, P.kvN, ck.dims[2], Hc}));
   P.cap = (int)ck.dims[2];
   P.shared = P.has_past && ck.data == pk.data;
   if (P.has_past && ((cv.data == pv.data) != P.shared))
     return fail(KVATTN_ERR_INVALID_ARG, "present_key and present_value must both share the past buffers or neither");
   if (P.shared && ck.dims[2] != pk.dims[2])
     return fail(KVATTN_ERR_INVALID_ARG, "a shared present buffer must have the past buffer's dims");
+  if (P.bits == 4 && P.has_past)
+    return fail(KVATTN_ERR_UNSUPPORTED, "int4 caches are prompt-only (no past_key)");
+  if (P.bits == 8 && P.has_past && P.S != 1)
+    return fail(KVATTN_ERR_UNSUPPORTED, "int8 caches with a past take one new token (decode)");
+  if (P.bits != 0 && P.window_cache)
+    return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache with a quantised cache is not implemented");
   if (P.window_cache) {
     if (!P.shared)
       return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache needs shared past/present buffers");
@@ -286,6 +323,7 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   size_t esz = elem_size(dt);
   P.ws_q = 0;
   P.ws_part = 0;
+  P.ws_deq = 0;
   if (P.decode) {
     const int g = P.N / P.kvN;
     P.head_groups = (g + 15) / 16;
@@ -295,7 +333,9 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode: too many (sample, head) units");
     P.ws_part = align256((size_t)(P.waves / 2) * P.hpw * (P.HP + 4) * sizeof(float));
   }
-  P.ws_total = P.ws_q + P.ws_part;
+  if (P.bits != 0 && !P.decode)  // prompt: the dequantised keys and values, float32 (B, kvN, S, H) each
+    P.ws_deq = 2 * align256((size_t)P.B * P.kvN * P.S * P.H * sizeof(float));
+  P.ws_total = P.ws_q + P.ws_part + P.ws_deq;
   return KVATTN_OK;
 }
 
@@ -315,7 +355,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     c.cv = cv.data;
     c.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
     c.B = P.B; c.kvN = P.kvN; c.H = P.H; c.S = P.S; c.past_seq = P.past_seq; c.cap = P.cap;
-    CHECK(hip_status(launch_copy_past(dt, c, st), "copy_past launch"));
+    CHECK(hip_status(launch_copy_past(P.bits == 8 ? DType::Q8 : dt, c, st), "copy_past launch"));
   }
 
   if (P.window_cache) {
@@ -362,7 +402,12 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     d.scale = scale;
     d.softcap = a->softcap;
     d.head_groups = P.head_groups; d.hpw = P.hpw; d.waves = (int)P.waves;
-    CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st, [&] { return launch_decode(dt, P.HP, d, st); }),
+    d.k_scale = static_cast<const float*>(in[GQA_IN_K_SCALE].data);
+    d.v_scale = static_cast<const float*>(in[GQA_IN_V_SCALE].data);
+    d.k_scale_pc = P.k_pc;
+    d.v_scale_pc = P.v_pc;
+    const DType ddt = P.bits == 8 ? DType::Q8 : dt;
+    CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st, [&] { return launch_decode(ddt, P.HP, d, st); }),
                      "decode launch"));
     CHECK(hip_status(launch_decode_combine(dt, P.HP, d, st), "decode combine launch"));
     return ok();
@@ -393,6 +438,25 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   pp.write_q = 0;
   pp.write_kv = 1;
   pp.win_cap = P.window_cache ? P.cap : 0;
+  // quantised prompt: codes into the present caches, dequantised rows into
+  // the workspace, which the attention reads
+  float* deq_k = nullptr;
+  float* deq_v = nullptr;
+  if (P.bits != 0) {
+    deq_k = reinterpret_cast<float*>(wsb + P.ws_q + P.ws_part);
+    deq_v = reinterpret_cast<float*>(wsb + P.ws_q + P.ws_part + P.ws_deq / 2);
+    pp.bits = P.bits;
+    pp.kq = ck.data;
+    pp.vq = cv.data;
+    pp.qcap = P.cap;
+    pp.kc = deq_k;
+    pp.vc = deq_v;
+    pp.cap = P.S;
+    pp.k_scale = static_cast<const float*>(in[GQA_IN_K_SCALE].data);
+    pp.v_scale = static_cast<const float*>(in[GQA_IN_V_SCALE].data);
+    pp.k_scale_pc = P.k_pc;
+    pp.v_scale_pc = P.v_pc;
+  }
   CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
                    "prep launch"));
 
@@ -408,10 +472,10 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   f.q_s = (int64_t)P.N * P.H;
   f.q_b = f.q_s * P.S;
   f.q_h = P.H;
-  f.kc = ck.data;
-  f.vc = cv.data;
+  f.kc = P.bits != 0 ? deq_k : ck.data;
+  f.vc = P.bits != 0 ? deq_v : cv.data;
   f.k_j = P.H;
-  f.k_h = (int64_t)P.cap * P.H;
+  f.k_h = (int64_t)(P.bits != 0 ? P.S : P.cap) * P.H;
   f.k_b = f.k_h * P.kvN;
   f.out = out[GQA_OUT_OUTPUT].data;
   f.o_s = (int64_t)P.N * P.H;
@@ -432,7 +496,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   f.win_cap = P.window_cache ? P.cap : 0;
   f.causal = a->causal;
   f.window = a->local_window_size;
-  f.kv_rows = P.cap;
+  f.kv_rows = P.bits != 0 ? P.S : P.cap;
   f.B = P.B; f.S = P.S; f.N = P.N; f.kvN = P.kvN; f.H = P.H;
   f.scale = scale;
   f.softcap = a->softcap;

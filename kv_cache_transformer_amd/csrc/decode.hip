@@ -38,6 +38,16 @@
 //   O^T[H][16 heads]      += V^T[H][16] . P^T    (f16: 16x16x16, f32: 16x16x4)
 // For f16 the V^T fragments come from an identity MFMA on the row-major V
 // fragment (exact: products with 1 and sums with 0), so V needs no LDS.
+//
+// int8 caches (GroupQueryAttention page, Attributes table: k/v_quant_type,
+// kv_cache_bit_width 8; Inputs table: k_scale, v_scale; float32 activations)
+// run the f16 tile on the codes, which f16 holds exactly: the key scales are
+// folded into the query, a power of two per head brings its largest element
+// into [2^13, 2^14), and the query and the probabilities (times 2^12) are
+// each split into two f16 terms hi + lo, so that the products stay within
+// float32 rounding of the float32 computation.  The value scales and 2^-12
+// are applied once per pair, to its merged output.  The appended row is
+// quantised in place: code = clamp(rint(x / scale)) with the float32 quotient.
 #include <type_traits>
 #include <utility>
 
@@ -63,12 +73,23 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // directly (no combine).
 constexpr int kDirectKeys = 64;
 
+// Cache type tag: float32 activations (query, new rows, output) over an int8
+// key/value cache.
+struct QuantI8 {};
+template <typename T> struct ActOf { using type = T; };
+template <> struct ActOf<QuantI8> { using type = float; };
+template <typename T> struct CacheOf { using type = T; };
+template <> struct CacheOf<QuantI8> { using type = int8_t; };
+
 // Register ring depth (16-row sub-tiles held per wave): R - 1 are in flight
 // while one is computed, sized to stay within 256 registers without spilling.
 template <typename T, int HP> struct Ring { static constexpr int value = 1; };
 template <> struct Ring<f16, 64> { static constexpr int value = 4; };
 template <> struct Ring<f16, 128> { static constexpr int value = 4; };
 template <> struct Ring<float, 64> { static constexpr int value = 3; };
+template <> struct Ring<QuantI8, 64> { static constexpr int value = 4; };
+template <> struct Ring<QuantI8, 128> { static constexpr int value = 4; };
+template <> struct Ring<QuantI8, 256> { static constexpr int value = 1; };
 
 // Four consecutive elements of a head row ("quad"): the unit of the query
 // set-up, the append and the output stores.
@@ -238,6 +259,119 @@ template <int HP, int R> struct DecTile<float, HP, R> {
   }
 };
 
+// ------------------------------ int8 ----------------------------------------
+// Eight int8 codes as f16.  Each byte u = code + 128 (sign bit flipped)
+// becomes the low mantissa byte of 1024.0 (0x6400 | u = 1024 + u, exact),
+// and 1152 is subtracted (exact).
+__device__ __forceinline__ half8v codes_to_half8(uint2v w) {
+  half8v out;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t a = w[k] ^ 0x80808080u;
+    const uint32_t lo = (a & 0xFFu) | ((a << 8) & 0xFF0000u) | 0x64006400u;
+    const uint32_t hi = ((a >> 16) & 0xFFu) | ((a >> 8) & 0xFF0000u) | 0x64006400u;
+    const half2v l2 = __builtin_bit_cast(half2v, lo) - half2v{(f16)1152.f, (f16)1152.f};
+    const half2v h2 = __builtin_bit_cast(half2v, hi) - half2v{(f16)1152.f, (f16)1152.f};
+    out[4 * k] = l2[0];
+    out[4 * k + 1] = l2[1];
+    out[4 * k + 2] = h2[0];
+    out[4 * k + 3] = h2[1];
+  }
+  return out;
+}
+
+// Code of x for scale s at 8 bits: the float32 quotient rounded half to even,
+// clamped to [-128, 127].
+__device__ __forceinline__ uint32_t quant8(float x, float s) {
+  const float c = fminf(fmaxf(rintf(x / s), -128.f), 127.f);
+  return (uint32_t)(int)c & 0xFFu;
+}
+
+// Lane layout as the f16 tile; the codes stay packed in the ring (8 per lane
+// and k-step) and are widened when used.
+template <int HP, int R> struct DecTile<QuantI8, HP, R> {
+  static constexpr int NS = HP / 32;
+  static constexpr int NQ = HP / 16;
+  static constexpr float kPScale = 4096.f;  // probabilities are split at 2^12 scale
+  half8v qh[NS], ql[NS];
+  float4v o[NQ];
+  uint2v kr[R][NS];
+  uint2v vr[R][NS];
+
+  __device__ static int quad_dim(int qi, int g4) { return 32 * (qi >> 1) + 8 * g4 + 4 * (qi & 1); }
+  __device__ void init() {
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) o[e] = float4v{0.f, 0.f, 0.f, 0.f};
+  }
+  // x: the query with the key scales folded in, scaled by a power of two;
+  // hi = f16(x), lo = f16(x - hi)
+  __device__ void set_q(const float (&x)[NQ][4]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = x[2 * s + (i >> 2)][i & 3];
+        const f16 h = (f16)v;
+        qh[s][i] = h;
+        ql[s][i] = (f16)(v - (float)h);
+      }
+  }
+  // rows as the f16 tile, 8 codes per k-step (slots at or beyond H re-read
+  // the row's first codes, against a zero query)
+  template <int BUF>
+  __device__ void load_kv(const int8_t* kb, const int8_t* vb, int j0, int last, int H, int lane) {
+    const int g4 = lane >> 4;
+    const int row = min(j0 + (lane & 15), last);
+    const int8_t* krow = kb + (int64_t)row * H;
+    const int8_t* vrow = vb + (int64_t)row * H;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int d = 32 * s + 8 * g4;
+      const int dc = d < H ? d : 0;
+      kr[BUF][s] = *reinterpret_cast<const uint2v*>(krow + dc);
+      vr[BUF][s] = *reinterpret_cast<const uint2v*>(vrow + dc);
+    }
+  }
+  template <int BUF>
+  __device__ float4v scores() const {
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const half8v k = codes_to_half8(kr[BUF][s]);
+      acc = mfma16x16x32(k, qh[s], acc);
+      acc = mfma16x16x32(k, ql[s], acc);
+    }
+    return acc;
+  }
+  __device__ void scale_o(float a) {
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) o[e] *= a;
+  }
+  template <int BUF>
+  __device__ void pv(const float4v& p, half4v ident) {
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    half4v ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = p[i] * kPScale;
+      ph[i] = (f16)v;
+      pl[i] = (f16)(v - (float)ph[i]);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const half8v v = codes_to_half8(vr[BUF][s]);
+      const float4v tl = mfma16x16x16(half4v{v[0], v[1], v[2], v[3]}, ident, zero);
+      const float4v th = mfma16x16x16(half4v{v[4], v[5], v[6], v[7]}, ident, zero);
+      const half4v al = {(f16)tl[0], (f16)tl[1], (f16)tl[2], (f16)tl[3]};
+      const half4v ah = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
+      o[2 * s] = mfma16x16x16(al, ph, o[2 * s]);
+      o[2 * s] = mfma16x16x16(al, pl, o[2 * s]);
+      o[2 * s + 1] = mfma16x16x16(ah, ph, o[2 * s + 1]);
+      o[2 * s + 1] = mfma16x16x16(ah, pl, o[2 * s + 1]);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // lengths and the deal of waves
 // ---------------------------------------------------------------------------
@@ -374,7 +508,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   constexpr int R = (FEAT & kExtras) ? (Ring<T, HP>::value > 1 ? Ring<T, HP>::value - 1 : 1)
                                      : Ring<T, HP>::value;
   using Tile = DecTile<T, HP, R>;
-  using Q4 = Quad<T>;
+  using AT = typename ActOf<T>::type;    // query, new rows, rotary, bias, sink, output
+  using CT = typename CacheOf<T>::type;  // cache elements
+  constexpr bool kQuant = std::is_same<T, QuantI8>::value;
+  using Q4 = Quad<AT>;
   using QT = typename Q4::type;
   constexpr int NQ = HP / 16, NH = NQ / 2;
   constexpr int RS = HP + 4;  // partial record: m, l, -, -, o[HP]
@@ -435,17 +572,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   const bool appender = append && !younger;
   const int claimable = nch - (append ? 1 : 0);
 
-  T* kb = static_cast<T*>(p.kc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
-  T* vb = static_cast<T*>(p.vc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
+  CT* kb = static_cast<CT*>(p.kc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
+  CT* vb = static_cast<CT*>(p.vc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
   const int half = H / 2;
-  const T* cs = static_cast<const T*>(p.cos);
-  const T* sn = static_cast<const T*>(p.sin);
+  const AT* cs = static_cast<const AT*>(p.cos);
+  const AT* sn = static_cast<const AT*>(p.sin);
   const bool rot = cs != nullptr;
   // rotary row of the new token: its absolute position (the last buffer row
   // unless a sliding-window cache has evicted rows)
   const int pos = min(max(last_pos, 0), max(p.rot_rows - 1, 0));
-  const T* cs_row = rot ? cs + (int64_t)pos * half : nullptr;
-  const T* sn_row = rot ? sn + (int64_t)pos * half : nullptr;
+  const AT* cs_row = rot ? cs + (int64_t)pos * half : nullptr;
+  const AT* sn_row = rot ? sn + (int64_t)pos * half : nullptr;
 
   // ---- the query: RMSNorm and rotary in registers ------------------------------
   // x[qi][e] = query element quad_dim(qi, g4) + e of head h0 + hh.  With H
@@ -454,11 +591,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   // rotary rows and the appended row all go out together; other head sizes
   // load the partner quads.
   const int hh = lane & 15, g4 = lane >> 4;
-  const T* qrow = static_cast<const T*>(p.q) + ((int64_t)b * p.N + h0 + min(hh, nh - 1)) * H;
-  const T* qw = static_cast<const T*>(p.q_norm);
+  const AT* qrow = static_cast<const AT*>(p.q) + ((int64_t)b * p.N + h0 + min(hh, nh - 1)) * H;
+  const AT* qw = static_cast<const AT*>(p.q_norm);
   const bool same_lane_pairs = (H == HP);
   float x[NQ][4];
-  auto load_quads = [&](QT (&dst)[NQ], const T* src, bool on) {
+  auto load_quads = [&](QT (&dst)[NQ], const AT* src, bool on) {
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
       const int d = Tile::quad_dim(qi, g4);
@@ -482,6 +619,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     return r;
   };
   QT qr[NQ], wr[NQ], cr[NH], sr[NH];
+  // int8 caches: the key scales of the query's dims
+  QT ksr[NQ];
+  if constexpr (kQuant) {
+    if (p.k_scale_pc) {
+      load_quads(ksr, p.k_scale + (int64_t)kvh * H, true);
+    } else {
+      const float s0 = p.k_scale[0];
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) ksr[qi] = QT{s0, s0, s0, s0};
+    }
+  }
   if (same_lane_pairs) {
     load_quads(qr, qrow, true);
     load_quads(wr, qw, qw != nullptr);
@@ -531,11 +679,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   const int ad = 4 * lane;
   const bool alane = ad < H;
   QT ak = Q4::zero(), av = Q4::zero(), aw = Q4::zero(), ac = Q4::zero(), as = Q4::zero();
+  QT aks = Q4::zero(), avs = Q4::zero();  // int8 caches: scales of the row's dims
   if (append && alane) {
     const int64_t nrow = ((int64_t)b * p.kvN + kvh) * H;
-    ak = Q4::load(static_cast<const T*>(p.k_new) + nrow + ad);
-    av = Q4::load(static_cast<const T*>(p.v_new) + nrow + ad);
-    if (p.k_norm != nullptr) aw = Q4::load(static_cast<const T*>(p.k_norm) + ad);
+    ak = Q4::load(static_cast<const AT*>(p.k_new) + nrow + ad);
+    av = Q4::load(static_cast<const AT*>(p.v_new) + nrow + ad);
+    if constexpr (kQuant) {
+      if (p.k_scale_pc) aks = Q4::load(p.k_scale + (int64_t)kvh * H + ad);
+      else aks = QT{p.k_scale[0], p.k_scale[0], p.k_scale[0], p.k_scale[0]};
+      if (p.v_scale_pc) avs = Q4::load(p.v_scale + (int64_t)kvh * H + ad);
+      else avs = QT{p.v_scale[0], p.v_scale[0], p.v_scale[0], p.v_scale[0]};
+    }
+    if (p.k_norm != nullptr) aw = Q4::load(static_cast<const AT*>(p.k_norm) + ad);
     if (rot) {
       const int i = ad < half ? ad : ad - half;
       ac = Q4::load(cs_row + i);
@@ -548,6 +703,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     pin(aw);
     pin(ac);
     pin(as);
+    if constexpr (kQuant) {
+      pin(aks);
+      pin(avs);
+    }
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = to_f32(ak[e]);
@@ -570,8 +729,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
       }
     }
     if (alane) {
-      Q4::store(kb + (int64_t)newrow * H + ad, y);
-      Q4::store_raw(vb + (int64_t)newrow * H + ad, av);
+      if constexpr (kQuant) {
+        uint32_t kw = 0, vw = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kw |= quant8(y[e], aks[e]) << (8 * e);
+          vw |= quant8(av[e], avs[e]) << (8 * e);
+        }
+        *reinterpret_cast<uint32_t*>(kb + (int64_t)newrow * H + ad) = kw;
+        *reinterpret_cast<uint32_t*>(vb + (int64_t)newrow * H + ad) = vw;
+      } else {
+        Q4::store(kb + (int64_t)newrow * H + ad, y);
+        Q4::store_raw(vb + (int64_t)newrow * H + ad, av);
+      }
     }
     // The row is read back by other lanes of this wave: order the stores
     // before those loads (no instruction is needed within one wave).  The
@@ -609,6 +779,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         }
     }
   }
+  // int8 caches: fold the key scales into the query and bring the head's
+  // largest |element| into [2^13, 2^14) (scores are scaled back in smul)
+  float smul = p.scale;
+  if constexpr (kQuant) {
+    float mx = 0.f;
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[qi][e] *= ksr[qi][e];
+        mx = fmaxf(mx, fabsf(x[qi][e]));
+      }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    int ex = 0;
+    frexpf(mx, &ex);
+    const int sh = min(max(14 - ex, -60), 60);
+    const float up = ldexpf(1.f, sh);
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[qi][e] *= up;
+    smul = p.scale * ldexpf(1.f, -sh);
+  }
   tile.set_q(x);
 
   // identity for the f16 V transpose: lane l holds B[k = 4(l/16)+i][n = l%16]
@@ -618,10 +812,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
   const bool head_ok = hh < nh;
   const int h = h0 + hh;
-  const float scale = p.scale;
   const float cap = p.softcap, inv_cap = p.softcap > 0.f ? 1.f / p.softcap : 0.f;
-  const T* bias = static_cast<const T*>(p.bias);
-  T* qk = static_cast<T*>(p.qk);
+  const AT* bias = static_cast<const AT*>(p.bias);
+  AT* qk = static_cast<AT*>(p.qk);
 
   float m = kNegInf, l = 0.f;
   // Score transform, online softmax and PV for the sub-tile held in BUF.
@@ -635,14 +828,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     for (int i = 0; i < 4; ++i) {
       const int key = j0 + 4 * g4 + i;
       const bool ok = head_ok && key < j_end;
-      float v = sc[i] * scale;
+      float v = sc[i] * smul;
       if (FEAT & kSoftcap) v = softcap_apply(v, cap, inv_cap);
       if (FEAT & kExtras) {
         if (ok && bias != nullptr && key < p.bias_cols)
           v += to_f32(bias[b * p.bias_sb + h * p.bias_sh + key]);
         if (ok && p.mask != nullptr && key < p.mask_cols)
           v += (p.mask[(int64_t)b * p.mask_cols + key] == 0) ? p.mask_filter : 0.f;
-        if (ok && qk != nullptr) qk[((int64_t)b * p.N + h) * p.host_n + key] = from_f32<T>(v);
+        if (ok && qk != nullptr) qk[((int64_t)b * p.N + h) * p.host_n + key] = from_f32<AT>(v);
       }
       v = ok ? v * kLog2e : kNegInf;
       x[i] = v;
@@ -763,12 +956,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
       O += *reinterpret_cast<const float4v*>(row + 4 + d) * f;
     }
     const int hq = h0 + hj;
+    if constexpr (kQuant) {
+      // value scales, and the 2^12 of the probabilities
+      const float u = 1.f / Tile::kPScale;
+      if (p.v_scale_pc) O *= *reinterpret_cast<const float4v*>(p.v_scale + (int64_t)kvh * H + d) * u;
+      else O *= p.v_scale[0] * u;
+    }
     if (direct) {
       bool has;
-      const float sg = read_sink<T>(p, hq, has);
+      const float sg = read_sink<AT>(p, hq, has);
       const float inv = final_scale(M, L, has, sg);
       const float v[4] = {O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
-      Q4::store(static_cast<T*>(p.out) + ((int64_t)b * p.N + hq) * H + d, v);
+      Q4::store(static_cast<AT*>(p.out) + ((int64_t)b * p.N + hq) * H + d, v);
     } else {
       float* rec = p.part + ((int64_t)pr * p.hpw + hj) * RS;
       if (d == 0) *reinterpret_cast<float2v*>(rec) = float2v{M, L};
@@ -886,12 +1085,18 @@ hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s)
     if (hp == 128) return launch_decode_t<f16, 128>(p, s);
     return launch_decode_t<f16, 256>(p, s);
   }
+  if (dt == DType::Q8) {
+    if (hp == 64) return launch_decode_t<QuantI8, 64>(p, s);
+    if (hp == 128) return launch_decode_t<QuantI8, 128>(p, s);
+    return launch_decode_t<QuantI8, 256>(p, s);
+  }
   if (hp == 64) return launch_decode_t<float, 64>(p, s);
   if (hp == 128) return launch_decode_t<float, 128>(p, s);
   return launch_decode_t<float, 256>(p, s);
 }
 
 // Merges the units that more than one wave served (the others return at once).
+// The partials are float32 for every cache type; Q8 merges as F32.
 hipError_t launch_decode_combine(DType dt, int hp, const DecodeParams& p, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
   if (dt == DType::F16) {

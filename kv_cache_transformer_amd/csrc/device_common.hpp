@@ -82,10 +82,28 @@ __device__ __forceinline__ void mfma_result_fence() {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// c * tanh(x / c) for c > 0, from tanh(y) = 1 - 2 / (exp(2y) + 1).
+// tanh(y) given u = 2 * log2(e) * y, within a few float32 ulps of the result:
+// for |y| < 1/4 the odd Taylor polynomial through y^9 (the next term is below
+// 1e-8 of the result), elsewhere 1 - 2 / (2^u + 1), whose cancellation there
+// costs at most a factor of about three.  (1 - 2 / (2^u + 1) alone loses
+// absolute, not relative, precision as y -> 0: after scaling by a large cap
+// that is a visible error in a small score.)
+__device__ __forceinline__ float tanh_from_u(float u) {
+  if (fabsf(u) < 0.72134752f) {        // 0.25 * 2 * log2(e)
+    const float y = u * 0.34657359f;   // ln(2) / 2
+    const float y2 = y * y;
+    float t = 62.f / 2835.f;
+    t = fmaf(t, y2, -17.f / 315.f);
+    t = fmaf(t, y2, 2.f / 15.f);
+    t = fmaf(t, y2, -1.f / 3.f);
+    return fmaf(t * y2, y, y);
+  }
+  return 1.f - 2.f * fast_rcp(fast_exp2(u) + 1.f);
+}
+
+// c * tanh(x / c) for c > 0.
 __device__ __forceinline__ float softcap_apply(float x, float cap, float inv_cap) {
-  float e = fast_exp2(2.0f * kLog2e * x * inv_cap);
-  return cap * (1.0f - 2.0f * fast_rcp(e + 1.0f));
+  return cap * tanh_from_u(2.0f * kLog2e * x * inv_cap);
 }
 
 // ---------------------------------------------------------------------------

@@ -503,6 +503,9 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   const float cap = p.softcap;
   // the softcap instance is launched only with a positive cap
   constexpr bool use_cap = SOFTCAP;
+  // float32 storage evaluates tanh to float32 accuracy near zero (the float16
+  // path keeps the shorter formula: its probabilities are rounded to f16)
+  constexpr bool kExactCap = std::is_same<T, float>::value;
   const float qscale = use_cap ? 2.f * kLog2e * p.scale / cap : kLog2e * p.scale;
   const float capA = cap * kLog2e, capB = 2.f * cap * kLog2e;
   {
@@ -641,7 +644,7 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
             ok = ok && key <= pos;
           }
           float v = sacc[blk][i];
-          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
+          if (use_cap) v = kExactCap ? capA * tanh_from_u(v) : capA - capB * fast_rcp(fast_exp2(v) + 1.f);
           if (bias != nullptr && ok) {
             if (MODE == kVarlen) {
               int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
@@ -659,7 +662,8 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     for (int blk = 0; blk < BN / 32; ++blk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[blk][i]);
-    if (use_cap && plain) tmax = capA - capB * fast_rcp(fast_exp2(tmax) + 1.f);
+    if (use_cap && plain)
+      tmax = kExactCap ? capA * tanh_from_u(tmax) : capA - capB * fast_rcp(fast_exp2(tmax) + 1.f);
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
     // The running max m moves only when a score exceeds it by more than
     // kMaxSlack (log2 units): probabilities then stay <= 2^kMaxSlack, exact
@@ -713,7 +717,8 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
         for (int blk = 0; blk < BN / 32; ++blk)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            pr[blk][i] = fast_exp2(c0 - capB * fast_rcp(fast_exp2(sacc[blk][i]) + 1.f));
+            pr[blk][i] = kExactCap ? fast_exp2(capA * tanh_from_u(sacc[blk][i]) - muse)
+                                   : fast_exp2(c0 - capB * fast_rcp(fast_exp2(sacc[blk][i]) + 1.f));
       } else {
 #pragma unroll
         for (int blk = 0; blk < BN / 32; ++blk)

@@ -8,7 +8,9 @@
 
 namespace kvattn {
 
-enum class DType : int { F32 = 1, F16 = 2 };
+// Q8: float32 activations over an int8 key/value cache (decode, and the
+// byte copies of such a cache)
+enum class DType : int { F32 = 1, F16 = 2, Q8 = 3 };
 
 // ---------------------------------------------------------------------------
 // K1 prep: per new token, optional per-head RMSNorm and rotary on the query
@@ -38,6 +40,14 @@ struct PrepParams {
   int write_q;              // 1: write transformed queries
   int write_kv;             // 1: append k, v into the caches
   int win_cap;              // > 0: sliding-window cache of this capacity (rows from window_geom)
+  // quantised caches (T = float32, write_kv only): the new keys and values
+  // are stored as codes in kq/vq (rows of H int8, or H/2 bytes of two
+  // +8-biased nibbles, capacity qcap) and as code * scale in kc/vc
+  int bits;                 // 0: float caches; 8 or 4
+  void* kq; void* vq;
+  int qcap;
+  const float* k_scale; const float* v_scale;
+  int k_scale_pc, v_scale_pc;  // 1: kvN*H per-channel scales; 0: one scale
 };
 
 // Sliding-window cache of capacity cap (GroupQueryAttention page, Attributes
@@ -111,6 +121,10 @@ struct DecodeParams {
   int head_groups;          // query-head groups of <= 16 per kv head
   int hpw;                  // partial records per wave: min(16, N / kvN)
   int waves;                // waves in the grid (a multiple of 4, >= B * kvN * head_groups)
+  // int8 caches (DType::Q8): cache value = code * scale; the key scales are
+  // folded into the query, the value scales applied to each pair's output
+  const float* k_scale; const float* v_scale;
+  int k_scale_pc, v_scale_pc;  // 1: kvN*H per-channel scales; 0: one scale
 };
 
 // ---------------------------------------------------------------------------

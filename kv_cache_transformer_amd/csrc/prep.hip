@@ -13,10 +13,18 @@
 // keeps every unchanged row (GroupQueryAttention page, Implementation
 // variants on retaining existing cache rows).
 //
+// Quantised caches (GroupQueryAttention page, Attributes table: k/v_quant_type,
+// kv_cache_bit_width; Inputs table: k_scale, v_scale and the int4 packing;
+// float32 rows only): the transformed key and the value become codes
+// clamp(rint(x / scale)) (float32 quotient) in the code cache, int8 or two
+// +8-biased nibbles per byte with the even dim low, and code * scale in the
+// float cache that the attention kernel reads.
+//
 // One workgroup (4 waves) per token; each wave transforms one head at a
 // time with its lanes spread over the head's dims.  The transformed head is
 // staged in LDS so that a lane can read its rotary partner.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kvattn_internal.hpp"
@@ -36,6 +44,37 @@ __device__ __forceinline__ void load8_or_4(const float* p, float (&x)[4]) {
 __device__ __forceinline__ void store8_or_4(f16* p, const float (&x)[8]) { store8_from_f32<f16>(p, x); }
 __device__ __forceinline__ void store8_or_4(float* p, const float (&x)[4]) {
   *reinterpret_cast<float4v*>(p) = float4v{x[0], x[1], x[2], x[3]};
+}
+
+// Quantised store of row element d = lane + 64u (u < 4) of head h, value y[u]:
+// the code into the code cache row, code * scale into the float cache row.
+// Called by all 64 lanes of a wave (the int4 pairs meet by a lane shuffle).
+__device__ void quant_store(const PrepParams& p, bool key, int b, int h, int crow, int lane,
+                            const float (&y)[4]) {
+  const int H = p.H;
+  const float* sc = key ? p.k_scale : p.v_scale;
+  const bool pc = (key ? p.k_scale_pc : p.v_scale_pc) != 0;
+  const int64_t slab = (int64_t)b * p.kvN + h;
+  float* deq = static_cast<float*>(key ? p.kc : p.vc) + (slab * p.cap + crow) * H;
+  const float top = p.bits == 8 ? 127.f : 7.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = lane + 64 * u;
+    int c = 0;
+    if (d < H) {
+      const float s = pc ? sc[(int64_t)h * H + d] : sc[0];
+      c = (int)fminf(fmaxf(rintf(y[u] / s), -top - 1.f), top);
+      deq[d] = (float)c * s;
+    }
+    if (p.bits == 8) {
+      int8_t* codes = static_cast<int8_t*>(key ? p.kq : p.vq) + (slab * p.qcap + crow) * H;
+      if (d < H) codes[d] = (int8_t)c;
+    } else {
+      const int cp = __shfl_xor(c, 1, 64);  // the odd partner of an even dim
+      uint8_t* codes = static_cast<uint8_t*>(key ? p.kq : p.vq) + (slab * p.qcap + crow) * (H / 2);
+      if (d < H && (d & 1) == 0) codes[d >> 1] = (uint8_t)((c + 8) | ((cp + 8) << 4));
+    }
+  }
 }
 
 template <typename T>
@@ -75,8 +114,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
 
       if (kind == 2) {
         if (row_ok) {
-          T* dst = static_cast<T*>(p.vc) + (((int64_t)b * p.kvN + h) * p.cap + crow) * H;
-          for (int d = lane; d < H; d += 64) dst[d] = src[d];
+          bool done = false;
+          if constexpr (std::is_same<T, float>::value) {
+            if (p.bits != 0) {
+              float y[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) y[u] = (lane + 64 * u < H) ? src[lane + 64 * u] : 0.f;
+              quant_store(p, false, b, h, crow, lane, y);
+              done = true;
+            }
+          }
+          if (!done) {
+            T* dst = static_cast<T*>(p.vc) + (((int64_t)b * p.kvN + h) * p.cap + crow) * H;
+            for (int d = lane; d < H; d += 64) dst[d] = src[d];
+          }
         }
       } else {
         const T* nw = static_cast<const T*>(kind == 0 ? p.q_norm : p.k_norm);
@@ -135,11 +186,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
             if (d < H) dst[d] = from_f32<T>(y[u]);
           }
         } else if (row_ok) {
-          T* dst = static_cast<T*>(p.kc) + (((int64_t)b * p.kvN + h) * p.cap + crow) * H;
+          bool done = false;
+          if constexpr (std::is_same<T, float>::value) {
+            if (p.bits != 0) {
+              quant_store(p, true, b, h, crow, lane, y);
+              done = true;
+            }
+          }
+          if (!done) {
+            T* dst = static_cast<T*>(p.kc) + (((int64_t)b * p.kvN + h) * p.cap + crow) * H;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            int d = lane + 64 * u;
-            if (d < H) dst[d] = from_f32<T>(y[u]);
+            for (int u = 0; u < 4; ++u) {
+              int d = lane + 64 * u;
+              if (d < H) dst[d] = from_f32<T>(y[u]);
+            }
           }
         }
       }
@@ -304,7 +364,7 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
   if (p.B * p.S == 0) return hipSuccess;
   const int ch = dt == DType::F16 ? 8 : 4;
   const int lpr = p.H / ch;  // lanes per row: a power of two (the norm sums by xor)
-  const bool vec_ok = !p.write_q && p.write_kv && p.H % ch == 0 && lpr <= 64 && (lpr & (lpr - 1)) == 0 &&
+  const bool vec_ok = p.bits == 0 && !p.write_q && p.write_kv && p.H % ch == 0 && lpr <= 64 && (lpr & (lpr - 1)) == 0 &&
                       (p.cos == nullptr || p.interleaved || p.rot_half % ch == 0);
   if (vec_ok) {
     const int64_t rows = (int64_t)p.B * p.S * p.kvN;
@@ -342,6 +402,8 @@ hipError_t launch_copy_past(DType dt, const CopyPastParams& p, hipStream_t s) {
   dim3 grid(gx, p.kvN, p.B);
   if (dt == DType::F16)
     hipLaunchKernelGGL(copy_past_kernel<f16>, grid, dim3(256), 0, s, p);
+  else if (dt == DType::Q8)
+    hipLaunchKernelGGL(copy_past_kernel<int8_t>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(copy_past_kernel<float>, grid, dim3(256), 0, s, p);
   return hipGetLastError();

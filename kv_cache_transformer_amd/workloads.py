@@ -14,6 +14,9 @@ Named workloads (sizes and distributions):
 * ``gqa_decode``        GroupQueryAttention decode of one new token: B=16, N=32,
   kvN=8, H=128, fp16, shared BNSH cache of capacity 4096, past lengths uniform
   in [1024, 4095], rotary (theta 10000), Q/K/V/cache ~ N(0,1).
+* ``gqa_decode_int8``   the decode above over an int8 cache: float32 Q/K/V,
+  uniform random int8 codes, per-channel key and value scales 3/127 times
+  uniform [0.5, 1.5).
 * ``gqa_long_prefill``  GroupQueryAttention prompt: B=4, S=4096, N=32, kvN=8,
   H=128, fp16, causal, local window 1024, softcap 50, head_sink ~ N(0,1),
   Q/K RMSNorm weights ~ 1+N(0,0.1), rotary theta 10000.
@@ -59,7 +62,7 @@ def rope_cache(max_seq, rot_dim, dtype, theta=10000.0):
 def gqa_case(rng, *, B, S, N, kvN, H, dtype=F16, past=None, past_lens=None,
              cap=None, rotary=False, rope_rows=None, norm=False, bias=None,
              sink=False, smooth_softmax=-1, softcap=0.0, window=-1, causal=1,
-             scale=0.0, total_lens=None):
+             scale=0.0, total_lens=None, quant=None):
     """A GroupQueryAttention call with random data.
 
     past: None (prompt), "shared" (present buffer is the past buffer, capacity
@@ -67,6 +70,9 @@ def gqa_case(rng, *, B, S, N, kvN, H, dtype=F16, past=None, past_lens=None,
     past_lens: per-batch past length (int array); drawn when None.
     total_lens: prompt only: per-batch total length (<= S); default S.
     bias: None or one of "full", "b1" (batch dim 1), "h1" (head dim 1), "11".
+    quant: None or dict(bits=8|4, k="tensor"|"channel", v=...): quantised
+    caches (float32 dtype) holding uniform random codes, with scales drawn by
+    ``quant_scales``; a separate present buffer starts as bytes 0x5A.
     Returns dict(inputs=..., attrs=..., shared=bool).
     """
     q = normal(rng, (B, S, N * H), dtype)
@@ -74,6 +80,12 @@ def gqa_case(rng, *, B, S, N, kvN, H, dtype=F16, past=None, past_lens=None,
     v = normal(rng, (B, S, kvN * H), dtype)
     inputs = dict(query=q, key=k, value=v)
     shared = False
+    if quant is not None:
+        return _gqa_quant_case(rng, inputs, B=B, S=S, N=N, kvN=kvN, H=H, past=past,
+                               past_lens=past_lens, cap=cap, rotary=rotary, norm=norm,
+                               bias=bias, sink=sink, smooth_softmax=smooth_softmax,
+                               softcap=softcap, window=window, causal=causal, scale=scale,
+                               total_lens=total_lens, quant=quant)
     if past is None:
         tl = np.full(B, S, dtype=np.int64) if total_lens is None else np.asarray(total_lens)
         seqlens_k = (tl - 1).astype(np.int32)
@@ -121,6 +133,84 @@ def gqa_case(rng, *, B, S, N, kvN, H, dtype=F16, past=None, past_lens=None,
     attrs = dict(num_heads=N, kv_num_heads=kvN, causal=causal, do_rotary=int(rotary),
                  local_window_size=window, qk_norm_epsilon=1e-6, scale=scale,
                  smooth_softmax=smooth_softmax, softcap=softcap)
+    return dict(op="gqa", inputs=inputs, attrs=attrs, total_sequence_length=total,
+                shared=shared)
+
+
+def quant_scales(rng, kind, kvN, H, bits):
+    """float32 cache scales: one value ("tensor") or kvN*H values ("channel").
+    The base step is 3/127 (8 bits) or 3/7 (4 bits), so that N(0,1) data
+    spans about three standard deviations of the code range; per-channel
+    scales are the base times uniform [0.5, 1.5)."""
+    base = 3.0 / ((1 << (bits - 1)) - 1)
+    if kind == "tensor":
+        return np.array([base], np.float32)
+    return (base * rng.uniform(0.5, 1.5, kvN * H)).astype(np.float32)
+
+
+def random_codes(rng, shape, bits):
+    """Uniform random cache elements: int8 codes, or packed uint8 bytes."""
+    if bits == 8:
+        return rng.integers(-128, 128, shape).astype(np.int8)
+    return rng.integers(0, 256, shape).astype(np.uint8)
+
+
+def _gqa_quant_case(rng, inputs, *, B, S, N, kvN, H, past, past_lens, cap, rotary, norm, bias,
+                    sink, smooth_softmax, softcap, window, causal, scale, total_lens, quant):
+    bits = int(quant["bits"])
+    hc = H if bits == 8 else H // 2
+    cdt = np.int8 if bits == 8 else np.uint8
+    shared = False
+    if past is None:
+        tl = np.full(B, S, dtype=np.int64) if total_lens is None else np.asarray(total_lens)
+        seqlens_k = (tl - 1).astype(np.int32)
+        present_seq = S if cap is None else cap
+        inputs.update(present_key=np.zeros((B, kvN, present_seq, hc), cdt),
+                      present_value=np.zeros((B, kvN, present_seq, hc), cdt))
+        max_pos = S
+    else:
+        if cap is None:
+            cap = S + 16
+        if past_lens is None:
+            past_lens = rng.integers(0, cap - S + 1, B)
+        past_lens = np.asarray(past_lens, dtype=np.int64)
+        seqlens_k = (past_lens + S - 1).astype(np.int32)
+        if past == "shared":
+            pk = random_codes(rng, (B, kvN, cap, hc), bits)
+            pv = random_codes(rng, (B, kvN, cap, hc), bits)
+            inputs.update(past_key=pk, past_value=pv, present_key=pk, present_value=pv)
+            shared = True
+        else:
+            past_seq = cap - S
+            pk = random_codes(rng, (B, kvN, past_seq, hc), bits)
+            pv = random_codes(rng, (B, kvN, past_seq, hc), bits)
+            fill = np.full((B, kvN, past_seq + S, hc), 0x5A, np.uint8).view(cdt)
+            inputs.update(past_key=pk, past_value=pv, present_key=fill, present_value=fill.copy())
+        max_pos = int(np.max(past_lens)) + S
+    inputs["seqlens_k"] = seqlens_k
+    total = int(np.max(seqlens_k)) + 1
+    if causal == 0:
+        total = S
+    dtype = F32
+    if rotary:
+        c, s_ = rope_cache(max(max_pos, total), H, dtype)
+        inputs.update(cos_cache=c, sin_cache=s_)
+    if bias is not None:
+        bshape = {"full": (B, N), "b1": (1, N), "h1": (B, 1), "11": (1, 1)}[bias]
+        inputs["attention_bias"] = normal(rng, bshape + (S, total), dtype)
+    if sink:
+        inputs["head_sink"] = normal(rng, (N,), dtype)
+    if norm:
+        inputs["q_norm_weight"] = normal(rng, (H,), dtype, std=0.1, mean=1.0)
+        inputs["k_norm_weight"] = normal(rng, (H,), dtype, std=0.1, mean=1.0)
+    kind = {"tensor": 1, "channel": 2}
+    inputs["k_scale"] = quant_scales(rng, quant["k"], kvN, H, bits)
+    inputs["v_scale"] = quant_scales(rng, quant["v"], kvN, H, bits)
+    attrs = dict(num_heads=N, kv_num_heads=kvN, causal=causal, do_rotary=int(rotary),
+                 local_window_size=window, qk_norm_epsilon=1e-6, scale=scale,
+                 smooth_softmax=smooth_softmax, softcap=softcap,
+                 k_quant_type=kind[quant["k"]], v_quant_type=kind[quant["v"]],
+                 kv_cache_bit_width=bits)
     return dict(op="gqa", inputs=inputs, attrs=attrs, total_sequence_length=total,
                 shared=shared)
 
@@ -186,6 +276,18 @@ def gqa_window_decode(seed=6, batch=16, cap=1024, window=1023, max_total=4096):
                  smooth_softmax=-1, softcap=0.0, sliding_window_cache=1)
     return dict(op="gqa", name="gqa_window_decode", inputs=inputs, attrs=attrs,
                 total_sequence_length=int(past.max()) + 1, shared=True)
+
+
+def gqa_decode_int8(seed=8, batch=16, cap=4096):
+    """GroupQueryAttention decode over an int8 cache: B=16 N=32 kvN=8 H=128,
+    float32 Q/K/V, shared int8 BNSH cache of capacity 4096 with uniform random
+    codes, per-channel key and value scales (3/127 times uniform [0.5, 1.5)),
+    past lengths uniform in [1024, 4095], rotary theta 10000."""
+    rng = np.random.default_rng(seed)
+    past = rng.integers(1024, cap, batch)
+    return gqa_case(rng, B=batch, S=1, N=32, kvN=8, H=128, dtype=F32, past="shared",
+                    past_lens=past, cap=cap, rotary=True,
+                    quant=dict(bits=8, k="channel", v="channel")) | dict(name="gqa_decode_int8")
 
 
 def gqa_long_prefill(seed=3, batch=4, seq=4096):
@@ -404,6 +506,7 @@ WORKLOADS = {
     "gqa_prompt_small": gqa_prompt_small,
     "gqa_decode": gqa_decode,
     "gqa_window_decode": gqa_window_decode,
+    "gqa_decode_int8": gqa_decode_int8,
     "gqa_long_prefill": gqa_long_prefill,
     "sparse_prompt": sparse_prompt,
     "packed_varlen": packed_varlen,

@@ -113,13 +113,13 @@ def check_cache(got, ref, transformed_rows=None, what="cache"):
 # ---------------------------------------------------------------------------
 # GroupQueryAttention
 # ---------------------------------------------------------------------------
-def gqa_oracle(case, query_rows=None):
+def gqa_oracle(case, query_rows=None, info=None):
     i = dict(case["inputs"])
     a = dict(case["attrs"])
     a["softcap_value"] = a.pop("softcap")
     return oracle.gqa(i.pop("query"), i.pop("key"), i.pop("value"),
                       total_sequence_length=case["total_sequence_length"],
-                      query_rows=query_rows, **i, **a)
+                      query_rows=query_rows, info=info, **i, **a)
 
 
 def gqa_gpu(case, workspace=None):
@@ -135,14 +135,85 @@ def gqa_gpu(case, workspace=None):
         t["query"], t["key"], t["value"], t.get("past_key"), t.get("past_value"),
         t["seqlens_k"], case["total_sequence_length"], t.get("cos_cache"), t.get("sin_cache"),
         t.get("attention_bias"), t.get("head_sink"), t.get("q_norm_weight"),
-        t.get("k_norm_weight"), num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"],
+        t.get("k_norm_weight"), t.get("k_scale"), t.get("v_scale"),
+        num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"],
         causal=a["causal"], do_rotary=a["do_rotary"], local_window_size=a["local_window_size"],
         qk_norm_epsilon=a["qk_norm_epsilon"], scale=a["scale"],
         smooth_softmax=a["smooth_softmax"], softcap=a["softcap"],
-        sliding_window_cache=a.get("sliding_window_cache", 0), present_key=pk,
+        sliding_window_cache=a.get("sliding_window_cache", 0),
+        k_quant_type=a.get("k_quant_type", 0), v_quant_type=a.get("v_quant_type", 0),
+        kv_cache_bit_width=a.get("kv_cache_bit_width", 0), present_key=pk,
         present_value=pv, workspace=workspace)
     torch.cuda.synchronize()
     return host(out), host(pk), host(pv)
+
+
+def gqa_new_rows(case):
+    """Cache row of each new token: int array (B, S)."""
+    i = case["inputs"]
+    B, S = i["query"].shape[:2]
+    total = i["seqlens_k"].astype(np.int64) + 1
+    past = total - S if i.get("past_key") is not None else np.zeros(B, np.int64)
+    return past[:, None] + np.arange(S)[None, :]
+
+
+# Rounding slack of transformed keys in quantised caches (code units): the
+# GPU computes a normed/rotated key in float32, the oracle in float64 rounded
+# once to float32, so their quotients by the scale may differ by float32
+# rounding of the operands (about 1e-5 here); a code may differ only where the
+# oracle's quotient lies this close to a rounding boundary.
+QUANT_SLACK = 1e-3
+
+
+def check_quant_gqa(case, got, ref, info, query_rows=None):
+    """Compare a quantised-cache call: codes of values and of untransformed
+    keys bit-exact; codes of normed/rotated keys bit-exact except within
+    QUANT_SLACK of a rounding boundary, where they may differ by one; every
+    other cache row untouched or copied exactly; the output within the float32
+    tolerance for every (sample, kv head) whose codes all match the oracle's
+    (the others depend on the tie's side and are only counted).  Returns the
+    number of codes taken on the other side of a near tie."""
+    from oracle import quant
+    out, pk, pv = got
+    rout, rpk, rpv = ref
+    a = case["attrs"]
+    bits = a["kv_cache_bit_width"]
+    transformed = bool(a["do_rotary"] or case["inputs"].get("q_norm_weight") is not None)
+    assert pk.dtype == rpk.dtype and pk.shape == rpk.shape
+    assert np.array_equal(pv, rpv), f"present_value: {int(np.sum(pv != rpv))} bytes differ"
+    rows = gqa_new_rows(case)                       # (B, S)
+    B, S = rows.shape
+    # key rows other than the new ones: exact
+    new = np.zeros(pk.shape[:3], bool)
+    for b in range(B):
+        for s_ in range(S):
+            if 0 <= rows[b, s_] < pk.shape[2]:
+                new[b, :, rows[b, s_]] = True
+    assert np.array_equal(pk[~new], rpk[~new]), "present_key: rows other than the new ones differ"
+    gc = quant.load_codes(pk, bits)
+    rc = quant.load_codes(rpk, bits)
+    diff = gc != rc                                 # (B, kvN, cap, H)
+    n_off = 0
+    bad_units = np.zeros(pk.shape[:2], bool)
+    if diff.any():
+        assert transformed, f"present_key: {int(diff.sum())} codes of untransformed keys differ"
+        margin = quant.rounding_margin(info["k_quotient"])   # (B, kvN, S, H)
+        for b, kh, r, d in np.argwhere(diff):
+            s_ = int(np.nonzero(rows[b] == r)[0][0])
+            assert margin[b, kh, s_, d] < QUANT_SLACK and abs(int(gc[b, kh, r, d]) - int(rc[b, kh, r, d])) == 1, (
+                f"present_key code at {(b, kh, r, d)}: gpu {gc[b, kh, r, d]} oracle {rc[b, kh, r, d]} "
+                f"(quotient {info['k_quotient'][b, kh, s_, d]!r})")
+            bad_units[b, kh] = True
+            n_off += 1
+    N, kvN = a["num_heads"], a["kv_num_heads"]
+    H = out.shape[-1] // N
+    o = out if query_rows is None else out[:, query_rows]
+    o = o.reshape(o.shape[0], o.shape[1], N, H)
+    r = rout.reshape(rout.shape[0], rout.shape[1], N, H)
+    keep = np.repeat(~bad_units, N // kvN, axis=1)  # (B, N)
+    assert keep.mean() >= 0.9, "too many units off a near tie"
+    check_output(o.transpose(0, 2, 1, 3)[keep], r.transpose(0, 2, 1, 3)[keep], np.float32)
+    return n_off
 
 
 def gqa_transformed_rows(case):

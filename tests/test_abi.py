@@ -121,12 +121,12 @@ def test_gqa_valid_shapes_give_workspace(lib):
     (lambda ins, outs, a: (ins.__setitem__(1, T(F16, 2, 8, 128)),
                            ins.__setitem__(2, T(F16, 2, 8, 128))), -2),     # kv_S != S
     (lambda ins, outs, a: ins.__setitem__(12, T(F16, 64)), -1),             # unpaired norm
-    (lambda ins, outs, a: a.update(k_quant_type=1), -2),                    # quantised cache
+    (lambda ins, outs, a: a.update(k_quant_type=1), -1),                    # quant type, no bit width
     (lambda ins, outs, a: a.update(sliding_window_cache=1), -1),            # needs a window
     (lambda ins, outs, a: a.update(sliding_window_cache=1, local_window_size=4), -2),  # no shared past
     (lambda ins, outs, a: a.update(causal=0, local_window_size=4), -1),
     (lambda ins, outs, a: a.update(do_rotary=1), -1),                       # no cos/sin
-    (lambda ins, outs, a: ins.__setitem__(10, T(F32, 1)), -2),              # k_scale
+    (lambda ins, outs, a: ins.__setitem__(10, T(F32, 1)), -1),              # k_scale, no bit width
     (lambda ins, outs, a: ins.__setitem__(8, T(F16, 3, 8, 16, 16)), -1),    # bias batch 3
     (lambda ins, outs, a: ins.__setitem__(9, T(F16, 7)), -1),               # head_sink shape
     (lambda ins, outs, a: outs.__setitem__(0, T(F16, 2, 16, 256)), -1),     # output shape
@@ -141,6 +141,63 @@ def test_gqa_rejections(lib, mutate, code):
     total = a.pop("total", 16)
     rc, _, msg = gqa_call(lib, ins, outs, total=total, kvN=kvN, **a)
     assert rc == code and msg
+
+
+I8, U8 = kb.DT_I8, kb.DT_U8
+
+
+def quant_args(bits=8, past=None, S=16, B=2, N=8, kvN=2, H=64, cap=64, kpc=False, vpc=True):
+    """float32 activations with int8 / packed uint8 caches and float32 scales."""
+    cdt, hc = (I8, H) if bits == 8 else (U8, H // 2)
+    ins = [kb.Tensor() for _ in range(kb.GQA_NUM_INPUTS)]
+    ins[0] = T(F32, B, S, N * H)
+    ins[1] = T(F32, B, S, kvN * H)
+    ins[2] = T(F32, B, S, kvN * H)
+    if past:
+        ins[3] = T(cdt, B, kvN, cap, hc, ptr=0x20000)
+        ins[4] = T(cdt, B, kvN, cap, hc, ptr=0x30000)
+    ins[5] = T(I32, B)
+    ins[10] = T(F32, kvN * H if kpc else 1)
+    ins[11] = T(F32, kvN * H if vpc else 1)
+    outs = [T(F32, B, S, N * H), T(cdt, B, kvN, cap, hc, ptr=0x20000 if past == "shared" else 0x40000),
+            T(cdt, B, kvN, cap, hc, ptr=0x30000 if past == "shared" else 0x50000)]
+    attrs = dict(kv_cache_bit_width=bits, k_quant_type=2 if kpc else 1, v_quant_type=2 if vpc else 1)
+    return ins, outs, attrs
+
+
+def test_gqa_quant_validation(lib):
+    align = lambda x: (x + 255) // 256 * 256
+    for bits in (8, 4):                                          # prompts: dequantised K/V workspace
+        ins, outs, at = quant_args(bits=bits)
+        rc, size, msg = gqa_call(lib, ins, outs, **at)
+        assert rc == 0, msg
+        assert size == 2 * align(2 * 2 * 16 * 64 * 4)
+    ins, outs, at = quant_args(past="shared", S=1, cap=4096, kpc=True)
+    rc, size, msg = gqa_call(lib, ins, outs, total=4000, **at)   # int8 decode, shared buffer
+    assert rc == 0 and size > 0, msg
+    ins, outs, at = quant_args(past="separate", S=1, cap=64)
+    assert gqa_call(lib, ins, outs, total=40, **at)[0] == 0      # separate past/present buffers
+
+    def code(mutate, **kw):
+        ins, outs, at = quant_args(**kw)
+        total = 40 if kw.get("past") else 16
+        mutate(ins, outs, at)
+        return gqa_call(lib, ins, outs, total=total, **at)[0]
+
+    assert code(lambda i, o, a: i.__setitem__(0, T(F16, 2, 16, 512))) == -1     # float16 query
+    assert code(lambda i, o, a: a.update(kv_cache_bit_width=2)) == -1
+    assert code(lambda i, o, a: a.update(v_quant_type=3)) == -1
+    assert code(lambda i, o, a: a.update(k_quant_type=0)) == -1                 # bits without a type
+    assert code(lambda i, o, a: i.__setitem__(11, kb.Tensor())) == -1           # no v_scale
+    assert code(lambda i, o, a: i.__setitem__(11, T(F32, 3))) == -1             # per-channel size
+    assert code(lambda i, o, a: i.__setitem__(10, T(F16, 1))) == -1             # scale dtype
+    assert code(lambda i, o, a: o.__setitem__(1, T(F32, 2, 2, 64, 64))) == -1   # float cache
+    assert code(lambda i, o, a: o.__setitem__(1, T(U8, 2, 2, 64, 64, ptr=0x40000)), bits=4) == -1  # H/2 bytes
+    assert code(lambda i, o, a: o.__setitem__(1, T(I8, 2, 2, 64, 64, ptr=0x40000)), bits=4) == -1  # uint8
+    assert code(lambda i, o, a: None, bits=4, past="shared", S=1) == -2         # int4 is prompt-only
+    assert code(lambda i, o, a: None, past="shared", S=4) == -2                 # int8 past: decode only
+    assert code(lambda i, o, a: a.update(sliding_window_cache=1, local_window_size=8),
+                past="shared", S=1) == -2
 
 
 def test_gqa_head_size_and_sharing_rules(lib):

@@ -9,7 +9,8 @@ import pytest
 
 from kv_cache_transformer_amd import workloads as wl
 
-from gpu_util import (check_cache, check_output, gqa_gpu, gqa_oracle, gqa_transformed_rows)
+from gpu_util import (check_cache, check_output, check_quant_gqa, gqa_gpu, gqa_oracle,
+                      gqa_transformed_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +150,51 @@ def test_workload_window_decode():
     case = wl.gqa_window_decode()
     err, _ = _compare(case)
     assert err >= 0
+
+
+# Quantised caches (GroupQueryAttention page, Attributes table: k_quant_type,
+# v_quant_type, kv_cache_bit_width; Inputs table: k_scale, v_scale): float32
+# activations, int8 for prompts and decode, packed int4 for prompts.
+Q8T = dict(bits=8, k="tensor", v="tensor")
+Q8C = dict(bits=8, k="channel", v="channel")
+QUANT = [
+    dict(B=2, S=150, N=8, kvN=2, H=64, quant=Q8T),
+    dict(B=2, S=130, N=8, kvN=2, H=128, window=37, softcap=30.0, sink=True, bias="full",
+         quant=dict(bits=8, k="channel", v="tensor")),
+    dict(B=2, S=100, N=8, kvN=2, H=128, causal=0, total_lens=[60, 100],
+         quant=dict(bits=4, k="channel", v="channel")),
+    dict(B=1, S=24, N=4, kvN=1, H=64, rotary=True, norm=True,
+         quant=dict(bits=4, k="tensor", v="channel")),
+    dict(B=1, S=20, N=4, kvN=1, H=128, rotary=True, quant=Q8C),
+    dict(B=2, S=9, N=2, kvN=1, H=8, quant=dict(bits=4, k="tensor", v="tensor")),
+    dict(B=3, S=1, N=32, kvN=8, H=128, cap=600, past_lens=[1, 300, 599], rotary=True, quant=Q8C),
+    dict(B=2, S=1, N=8, kvN=2, H=64, past="concat", cap=200, past_lens=[0, 150],
+         quant=dict(bits=8, k="tensor", v="channel")),
+    dict(B=2, S=1, N=4, kvN=4, H=256, cap=1100, past_lens=[1099, 513], softcap=20.0, sink=True,
+         window=100, quant=dict(bits=8, k="channel", v="tensor")),
+    dict(B=1, S=1, N=8, kvN=2, H=72, cap=300, past_lens=[299], norm=True, rotary=True, quant=Q8C),
+    dict(B=4, S=1, N=16, kvN=4, H=128, cap=2100, past_lens=[2099, 1024, 128, 127], bias="h1",
+         smooth_softmax=1, quant=Q8T),
+    dict(B=2, S=1, N=2, kvN=1, H=8, cap=8, past_lens=[7, 3], quant=Q8C),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(QUANT)))
+def test_quant_cache_parity(idx):
+    print(f"quant case {idx}: {QUANT[idx]}", flush=True)
+    case = _case(dict(QUANT[idx], dtype=F32), 400 + idx)
+    got = gqa_gpu(case)
+    info = {}
+    ref = gqa_oracle(case, info=info)
+    n = check_quant_gqa(case, got, ref, info)
+    print(f"key codes on the other side of a near tie: {n}")
+
+
+def test_workload_gqa_decode_int8():
+    case = wl.gqa_decode_int8()
+    print("gqa_decode_int8", flush=True)
+    got = gqa_gpu(case)
+    info = {}
+    ref = gqa_oracle(case, info=info)
+    n = check_quant_gqa(case, got, ref, info)
+    print(f"key codes on the other side of a near tie: {n}")

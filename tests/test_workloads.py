@@ -61,3 +61,28 @@ def test_window_decode_workload():
     # every sample has seen at least a full buffer: each step evicts one row
     assert i["seqlens_k"].min() >= 1024 and i["seqlens_k"].max() <= 4095
     assert i["cos_cache"].shape[0] >= c["total_sequence_length"]
+
+
+def test_int8_decode_workload():
+    c = wl.WORKLOADS["gqa_decode_int8"]()
+    i, a = c["inputs"], c["attrs"]
+    assert c["name"] == "gqa_decode_int8" and c["shared"]
+    assert i["query"].dtype == np.float32 and i["query"].shape == (16, 1, 32 * 128)
+    assert i["past_key"].dtype == np.int8 and i["past_key"].shape == (16, 8, 4096, 128)
+    assert i["present_key"] is i["past_key"] and i["present_value"] is i["past_value"]
+    assert i["k_scale"].shape == (8 * 128,) and i["v_scale"].dtype == np.float32
+    assert np.all((i["k_scale"] >= 0.5 * 3 / 127) & (i["k_scale"] < 1.5 * 3 / 127 + 1e-7))
+    assert a["kv_cache_bit_width"] == 8 and a["k_quant_type"] == 2 and a["v_quant_type"] == 2
+    assert 1024 <= i["seqlens_k"].min() and i["seqlens_k"].max() <= 4095
+    # codes cover the whole int8 range
+    assert i["past_key"].min() == -128 and i["past_key"].max() == 127
+
+
+def test_quant_case_int4_layout():
+    rng = np.random.default_rng(0)
+    c = wl.gqa_case(rng, B=2, S=10, N=4, kvN=2, H=64, dtype=np.float32,
+                    quant=dict(bits=4, k="tensor", v="channel"))
+    i = c["inputs"]
+    assert i["present_key"].dtype == np.uint8 and i["present_key"].shape == (2, 2, 10, 32)
+    assert i["k_scale"].shape == (1,) and np.isclose(i["k_scale"][0], 3 / 7)
+    assert i["v_scale"].shape == (128,)
