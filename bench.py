@@ -156,6 +156,39 @@ def decode_workload(torch, kv, wl, args, timer):
                 kv_bytes=kv_bytes)
 
 
+def decode_int8_workload(torch, kv, wl, args, timer):
+    """The decode over an int8 cache (float32 Q/K/V, per-channel scales):
+    rotations of random int8 caches as for the float16 decode."""
+    case = wl.gqa_decode_int8()
+    i = case["inputs"]
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in i.items() if k not in ("present_key", "present_value")}
+    sets = [(t["past_key"], t["past_value"])]
+    g = torch.Generator(device=dev)
+    g.manual_seed(54321)
+    for _ in range(args.rotations - 1):
+        sets.append(tuple(torch.randint(-128, 128, t["past_key"].shape, generator=g, device=dev,
+                                        dtype=torch.int8) for _ in range(2)))
+    a = case["attrs"]
+    out = torch.empty_like(t["query"])
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def step(n):
+        pk, pv = sets[n % len(sets)]
+        kv.gqa_attention(t["query"], t["key"], t["value"], pk, pv, t["seqlens_k"],
+                         case["total_sequence_length"], t["cos_cache"], t["sin_cache"],
+                         k_scale=t["k_scale"], v_scale=t["v_scale"],
+                         num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"], do_rotary=1,
+                         k_quant_type=2, v_quant_type=2, kv_cache_bit_width=8,
+                         output=out, present_key=pk, present_value=pv, workspace=ws)
+
+    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    lens = i["seqlens_k"].astype(np.int64) + 1
+    kvN, H = 8, 128
+    kv_bytes = int(lens.sum()) * kvN * H * 2     # K and V codes, one byte each
+    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, kv_bytes=kv_bytes)
+
+
 def window_decode_workload(torch, kv, wl, args, timer):
     """Decode steps on a full sliding-window cache: each call evicts one row
     (the shift moves the other 1023 rows of every slab) and attends the 1024
@@ -343,6 +376,8 @@ TRAFFIC_KERNELS = [
      "packed_varlen"),
     ("window_shift_gqa_window_decode", r"window_shift_kernelIDF16_", "kv_cache_transformer_amd/csrc/prep.hip",
      "gqa_window_decode"),
+    ("decode_gqa_decode_int8", r"decode_kernelINS0_7QuantI8ELi128E", "kv_cache_transformer_amd/csrc/decode.hip",
+     "gqa_decode_int8"),
 ]
 
 
@@ -431,6 +466,9 @@ def summarise_counters(d, cmd):
             dm = re.search(r"<float(?:, (\d+), (\d+), (\d+))?", r["Kernel_Name"])
             if not t and dm:  # names of float instances come demangled
                 t, hd, md = "f32", dm.group(1), dm.group(3)
+            qm = re.search(r"QuantI8(?:E|, )(?:Li)?(\d+)", r["Kernel_Name"])
+            if qm:  # int8-cache decode
+                t, hd, md = "q8", qm.group(1), None
             mode = {"0": "dense", "1": "csr", "2": "varlen"}.get(md, "")
             key = m.group(1) + (f"<{t},{hd},{mode}>" if hd else (f"<{t}>" if t else ""))
             agg.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
@@ -531,6 +569,10 @@ def main():
     if want("gqa_window_decode"):
         res["gqa_window_decode"] = window_decode_workload(torch, kv, wl, args, Timer(torch, lib, 5, hip))
         print("# gqa_window_decode done", file=sys.stderr, flush=True)
+    if want("gqa_decode_int8"):
+        res["gqa_decode_int8"] = decode_int8_workload(torch, kv, wl, args, Timer(torch, lib, 1, hip))
+        print(f"# gqa_decode_int8 done: {res['gqa_decode_int8']['call_ms']*1e3:.1f} us/call",
+              file=sys.stderr, flush=True)
     if want("packed_varlen"):
         res["packed_varlen"] = packed_workload(torch, kv, wl, args, Timer(torch, lib, 4, hip))
         print("# packed_varlen done", file=sys.stderr, flush=True)
@@ -591,6 +633,19 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
                          "kernel_ms": round(r["kern_ms"], 4), "algorithmic_bytes": r["shift_bytes"],
                          "traffic": traffic_for("window_shift_gqa_window_decode")}}
+
+    if "gqa_decode_int8" in res:
+        r = res["gqa_decode_int8"]
+        gbs_k = r["kv_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
+        workloads["gqa_decode_int8"] = {
+            "config": "B16 N32 kvN8 H128 fp32 Q/K/V, shared int8 cache 4096, per-channel scales, "
+                      "past lengths U[1024,4095], rotary",
+            "call_us": round(r["call_ms"] * 1e3, 2),
+            "call_GBs": round(r["kv_bytes"] / (r["call_ms"] * 1e-3) / 1e9, 2),
+            "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs_k, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
+                         "kernel_us": round(r["kern_ms"] * 1e3, 3), "algorithmic_bytes": r["kv_bytes"],
+                         "traffic": traffic_for("decode_gqa_decode_int8")}}
 
     line = {"metric": "GQA prefill TFLOP/s and decode KV GB/s on 1 MI355X, % of roofline",
             "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

@@ -69,6 +69,10 @@ constexpr int64_t kMinKeysPerWave = 64;
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Slack of the running maximum (log2 units): probabilities stay <= 2^3, which
+// the int8 tile's 2^12-scaled f16 split holds (2^15 < 65504).
+constexpr float kDecodeSlack = 3.f;
+
 // A unit with at most this many keys and a single pair writes the output
 // directly (no combine).
 constexpr int kDirectKeys = 64;
@@ -268,8 +272,10 @@ __device__ __forceinline__ half8v codes_to_half8(uint2v w) {
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const uint32_t a = w[k] ^ 0x80808080u;
-    const uint32_t lo = (a & 0xFFu) | ((a << 8) & 0xFF0000u) | 0x64006400u;
-    const uint32_t hi = ((a >> 16) & 0xFFu) | ((a >> 8) & 0xFF0000u) | 0x64006400u;
+    // v_perm_b32: selector bytes 0-3 take bytes of the second operand, 4-7 of
+    // the first: (a.b0, 0x64, a.b1, 0x64) and (a.b2, 0x64, a.b3, 0x64)
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u);
     const half2v l2 = __builtin_bit_cast(half2v, lo) - half2v{(f16)1152.f, (f16)1152.f};
     const half2v h2 = __builtin_bit_cast(half2v, hi) - half2v{(f16)1152.f, (f16)1152.f};
     out[4 * k] = l2[0];
@@ -287,18 +293,48 @@ __device__ __forceinline__ uint32_t quant8(float x, float s) {
   return (uint32_t)(int)c & 0xFFu;
 }
 
-// Lane layout as the f16 tile; the codes stay packed in the ring (8 per lane
-// and k-step) and are widened when used.
+// Lane layout as the f16 tile (lane l: key row l % 16, quarter g4 = l / 16),
+// the codes packed in the ring and widened when used.  For HP >= 128 a lane
+// loads 16 codes at a time, dims 64 i + 16 g4 .. + 15 (two k-steps: load i
+// serves k-steps 2i and 2i + 1), which keeps the rotary partners d, d + HP/2
+// in quads qi, qi + NQ/2 of one lane.  A load that would cross the row's end
+// (H not a multiple of 16) starts 8 codes early instead; that lane then
+// labels its k-steps the other way round (the early half stands for dims past
+// the head, where the query is zero and no output is stored).  HP = 64 keeps
+// 8-code loads (dims 32 s + 8 g4 .. + 7).
 template <int HP, int R> struct DecTile<QuantI8, HP, R> {
-  static constexpr int NS = HP / 32;
-  static constexpr int NQ = HP / 16;
+  static constexpr int NS = HP / 32;  // 32-dim k-steps of the score MFMA
+  static constexpr int NQ = HP / 16;  // quads per lane
+  static constexpr bool kWide = HP >= 128;
+  static constexpr int NL = kWide ? HP / 64 : NS;  // loads per matrix and sub-tile
+  using Raw = typename std::conditional<kWide, uint4v, uint2v>::type;
   static constexpr float kPScale = 4096.f;  // probabilities are split at 2^12 scale
   half8v qh[NS], ql[NS];
   float4v o[NQ];
-  uint2v kr[R][NS];
-  uint2v vr[R][NS];
+  Raw kr[R][NL];
+  Raw vr[R][NL];
+  uint32_t swap = 0;  // bit i: load i starts 8 codes early (its k-steps are exchanged)
 
-  __device__ static int quad_dim(int qi, int g4) { return 32 * (qi >> 1) + 8 * g4 + 4 * (qi & 1); }
+  __device__ int quad_dim(int qi, int g4) const {
+    if constexpr (kWide) {
+      const int i = qi >> 2;
+      const int j = ((qi >> 1) & 1) ^ (int)((swap >> i) & 1u);
+      return 64 * i + 16 * g4 + 8 * j + 4 * (qi & 1);
+    } else {
+      return 32 * (qi >> 1) + 8 * g4 + 4 * (qi & 1);
+    }
+  }
+  __device__ void set_layout(int H, int lane) {
+    swap = 0;
+    if constexpr (kWide) {
+      const int g4 = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int d = 64 * i + 16 * g4;
+        if (d < H && d + 16 > H) swap |= 1u << i;
+      }
+    }
+  }
   __device__ void init() {
 #pragma unroll
     for (int e = 0; e < NQ; ++e) o[e] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -316,8 +352,8 @@ template <int HP, int R> struct DecTile<QuantI8, HP, R> {
         ql[s][i] = (f16)(v - (float)h);
       }
   }
-  // rows as the f16 tile, 8 codes per k-step (slots at or beyond H re-read
-  // the row's first codes, against a zero query)
+  // Rows j0 + l % 16 (clamped to the last row of the run); every load stays
+  // inside its row (slots past the head re-read the row's first codes).
   template <int BUF>
   __device__ void load_kv(const int8_t* kb, const int8_t* vb, int j0, int last, int H, int lane) {
     const int g4 = lane >> 4;
@@ -325,11 +361,26 @@ template <int HP, int R> struct DecTile<QuantI8, HP, R> {
     const int8_t* krow = kb + (int64_t)row * H;
     const int8_t* vrow = vb + (int64_t)row * H;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int d = 32 * s + 8 * g4;
-      const int dc = d < H ? d : 0;
-      kr[BUF][s] = *reinterpret_cast<const uint2v*>(krow + dc);
-      vr[BUF][s] = *reinterpret_cast<const uint2v*>(vrow + dc);
+    for (int i = 0; i < NL; ++i) {
+      int off;
+      if constexpr (kWide) {
+        const int d = 64 * i + 16 * g4;
+        off = d + 16 <= H ? d : (d < H ? d - 8 : 0);
+      } else {
+        const int d = 32 * i + 8 * g4;
+        off = d < H ? d : 0;
+      }
+      kr[BUF][i] = *reinterpret_cast<const Raw*>(krow + off);
+      vr[BUF][i] = *reinterpret_cast<const Raw*>(vrow + off);
+    }
+  }
+  // the 8 codes of k-step s
+  __device__ static uint2v step_codes(const Raw (&r)[NL], int s) {
+    if constexpr (kWide) {
+      const uint4v w = r[s >> 1];
+      return (s & 1) ? uint2v{w[2], w[3]} : uint2v{w[0], w[1]};
+    } else {
+      return r[s];
     }
   }
   template <int BUF>
@@ -337,7 +388,7 @@ template <int HP, int R> struct DecTile<QuantI8, HP, R> {
     float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const half8v k = codes_to_half8(kr[BUF][s]);
+      const half8v k = codes_to_half8(step_codes(kr[BUF], s));
       acc = mfma16x16x32(k, qh[s], acc);
       acc = mfma16x16x32(k, ql[s], acc);
     }
@@ -359,7 +410,7 @@ template <int HP, int R> struct DecTile<QuantI8, HP, R> {
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const half8v v = codes_to_half8(vr[BUF][s]);
+      const half8v v = codes_to_half8(step_codes(vr[BUF], s));
       const float4v tl = mfma16x16x16(half4v{v[0], v[1], v[2], v[3]}, ident, zero);
       const float4v th = mfma16x16x16(half4v{v[4], v[5], v[6], v[7]}, ident, zero);
       const half4v al = {(f16)tl[0], (f16)tl[1], (f16)tl[2], (f16)tl[3]};
@@ -411,6 +462,13 @@ __device__ int64_t deal_quota(const DecodeParams& p, int ups, int lane, int c0) 
   const int64_t spare = (int64_t)(p.waves / 2) - units;
   if (spare <= 0) return INT64_MAX;
   return max(2 * kMinKeysPerWave, (k + spare - 1) / spare);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ int pairs_for(int c, int64_t quota) {
@@ -518,7 +576,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   __shared__ int s_claim[kPairsPerGroup];
   __shared__ __attribute__((aligned(16))) float s_part[kPartFloats];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int jp = wave % kPairsPerGroup;      // pair of this wave (waves jp, jp + 4 share a SIMD)
   const int younger = wave / kPairsPerGroup;
   const int pr = blockIdx.x * kPairsPerGroup + jp;
@@ -535,9 +594,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   // take it from there
   int n_l = 0, newrow_l = -1, kstart_l = 0, last_l = 0;
   if (lane < p.B) sample_keys(p, lane, n_l, newrow_l, kstart_l, last_l);
-  const int64_t quota = deal_quota(p, ups, lane, max(n_l - kstart_l, 0));
+  // (the deal is the same in every lane: the values are made scalar, so that
+  // the chunk bookkeeping of the streaming loop runs on the scalar unit)
+  const int64_t quota = uniform64(deal_quota(p, ups, lane, max(n_l - kstart_l, 0)));
   int b = 0, first = 0;
   const bool live = find_sample(p, ups, quota, pr, lane, max(n_l - kstart_l, 0), b, first);
+  b = __builtin_amdgcn_readfirstlane(b);
+  first = __builtin_amdgcn_readfirstlane(first);
   int n = 0, newrow = -1, kstart = 0, last_pos = 0;
   if (b < 64) {
     n = __shfl(n_l, b, 64);
@@ -547,6 +610,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   } else {
     sample_keys(p, b, n, newrow, kstart, last_pos);
   }
+  n = __builtin_amdgcn_readfirstlane(n);
+  newrow = __builtin_amdgcn_readfirstlane(newrow);
+  kstart = __builtin_amdgcn_readfirstlane(kstart);
+  last_pos = __builtin_amdgcn_readfirstlane(last_pos);
   const int c = live ? max(n - kstart, 0) : 0;
   const int nb = pairs_for(c, quota);
   const int local = pr - first;
@@ -591,6 +658,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   // rotary rows and the appended row all go out together; other head sizes
   // load the partner quads.
   const int hh = lane & 15, g4 = lane >> 4;
+  Tile tile;  // (the int8 tile's dims per quad depend on the head size)
+  if constexpr (kQuant) tile.set_layout(H, lane);
   const AT* qrow = static_cast<const AT*>(p.q) + ((int64_t)b * p.N + h0 + min(hh, nh - 1)) * H;
   const AT* qw = static_cast<const AT*>(p.q_norm);
   const bool same_lane_pairs = (H == HP);
@@ -598,7 +667,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   auto load_quads = [&](QT (&dst)[NQ], const AT* src, bool on) {
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
-      const int d = Tile::quad_dim(qi, g4);
+      const int d = tile.quad_dim(qi, g4);
       dst[qi] = (on && d < H) ? Q4::load(src + d) : Q4::zero();
     }
   };
@@ -636,7 +705,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     if (rot) {
 #pragma unroll
       for (int qi = 0; qi < NH; ++qi) {
-        const int d = Tile::quad_dim(qi, g4);  // < H / 2
+        const int d = tile.quad_dim(qi, g4);  // < H / 2
         cr[qi] = Q4::load(cs_row + d);
         sr[qi] = Q4::load(sn_row + d);
       }
@@ -656,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     if (rot) {
 #pragma unroll
       for (int qi = 0; qi < NQ; ++qi) {
-        const int d = Tile::quad_dim(qi, g4);
+        const int d = tile.quad_dim(qi, g4);
         if (d < H) {
           const int i = d < half ? d : d - half;
           const int dp = d < half ? d + half : d - half;
@@ -759,7 +828,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   // stream of the whole grid they would wait for most of it, so every wave
   // completes them while the memory system is still idle.
   if (appender) do_append();
-  Tile tile;
   tile.init();
   if (same_lane_pairs) {
 #pragma unroll
@@ -817,7 +885,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   AT* qk = static_cast<AT*>(p.qk);
 
   float m = kNegInf, l = 0.f;
+  // plain scores go to the log2 domain in the same multiply
+  const float smul_l2 = smul * kLog2e;
   // Score transform, online softmax and PV for the sub-tile held in BUF.
+  // The running max m moves only when a score exceeds it by more than
+  // kDecodeSlack (log2 units): the probabilities then stay <= 2^kDecodeSlack
+  // and the rescale of the output is skipped on most sub-tiles.
   auto process = [&](auto buf_tag, int j0, int j_end) {
     constexpr int BUF = decltype(buf_tag)::value;
     const float4v sc = tile.template scores<BUF>();
@@ -828,6 +901,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     for (int i = 0; i < 4; ++i) {
       const int key = j0 + 4 * g4 + i;
       const bool ok = head_ok && key < j_end;
+      if constexpr (FEAT == 0) {
+        const float v = sc[i] * smul_l2;
+        x[i] = ok ? v : kNegInf;
+        tmax = fmaxf(tmax, x[i]);
+        continue;
+      }
       float v = sc[i] * smul;
       if (FEAT & kSoftcap) v = softcap_apply(v, cap, inv_cap);
       if (FEAT & kExtras) {
@@ -843,10 +922,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     }
     tmax = fmaxf(tmax, shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = fast_exp2(m - muse);
-    m = mnew;
+    const bool grow = tmax > m + kDecodeSlack;
+    if (__any(grow)) {
+      // a side effect keeps this a branch (executed unconditionally the
+      // rescale would cost a multiply per accumulator on every sub-tile)
+      asm volatile("" ::: "memory");
+      const float alpha = grow ? fast_exp2(m - tmax) : 1.f;
+      m = grow ? tmax : m;
+      l *= alpha;
+      tile.scale_o(alpha);
+    }
+    const float muse = (m == kNegInf) ? 0.f : m;
     float4v pr;
     float psum = 0.f;
 #pragma unroll
@@ -855,8 +941,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
       pr[i] = e;
       psum += e;
     }
-    l = l * alpha + psum;
-    tile.scale_o(alpha);
+    l += psum;
     tile.template pv<BUF>(pr, ident);
   };
 
@@ -909,7 +994,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
       if (g4 == 0) *reinterpret_cast<float2v*>(row) = float2v{m, lt};
 #pragma unroll
       for (int qi = 0; qi < NQ; ++qi) {
-        const int d = Tile::quad_dim(qi, g4);
+        const int d = tile.quad_dim(qi, g4);
         if (d < H) *reinterpret_cast<float4v*>(row + 4 + d) = tile.o[qi];
       }
     }
