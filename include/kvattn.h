@@ -346,8 +346,8 @@ void sparse_attrs_default(sparse_attrs* attrs);
  * total_sequence_length must fit the capacity, max_blocks * block_size and the
  * rotary rows.  rp must be monotone from 0 and its entries <= max_nnz; active
  * column entries must lie in [0, max_blocks).
- *
- * UNSUPPORTED on the GPU: token generation (total_sequence_length != S).
+ * Token generation (total_sequence_length != S) needs
+ * key_total_sequence_lengths[b] >= S for every sample.
  */
 int32_t sparse_attention(const sparse_attrs* attrs,
                          const kvattn_tensor* inputs, int32_t n_inputs,

@@ -656,7 +656,7 @@ int dmmha_run(const dmmha_attrs* a, const kvattn_tensor* in, const kvattn_tensor
 // ===========================================================================
 struct SparsePlan {
   int B, S, N, kvN, H, HP, dt, cap, L, max_blocks, max_nnz, rot_half, bs;
-  bool packed_qkv, rotary;
+  bool packed_qkv, rotary, generation;
   size_t ws_q, ws_total;
 };
 
@@ -719,7 +719,11 @@ int sparse_validate(const sparse_attrs* a, const kvattn_tensor* in, int n_in, in
   if (total > P.cap) return fail(KVATTN_ERR_INVALID_ARG, "total_sequence_length %d exceeds the cache capacity %d", total, P.cap);
   if ((int64_t)total > (int64_t)P.max_blocks * bs)
     return fail(KVATTN_ERR_INVALID_ARG, "total_sequence_length %d exceeds max_blocks * sparse_block_size", total);
-  if (total != P.S) return fail(KVATTN_ERR_UNSUPPORTED, "sparse token generation (total_sequence_length != sequence_length) is not implemented");
+  if (total < P.S)
+    return fail(KVATTN_ERR_INVALID_ARG, "total_sequence_length %d < sequence_length %d", total, P.S);
+  // token generation (SparseAttention page, Description and Inputs table):
+  // the new rows follow a past of key_total_sequence_lengths[b] - S rows
+  P.generation = total != P.S;
   P.rotary = a->do_rotary == 1;
   if (P.rotary) {
     const kvattn_tensor& cs = in[SPARSE_IN_COS_CACHE];
@@ -771,7 +775,7 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
     pp.interleaved = a->rotary_interleaved == 1;
   }
   pp.lens = static_cast<const int32_t*>(in[SPARSE_IN_KEY_TOTAL_SEQUENCE_LENGTHS].data);
-  pp.pos_mode = 0;
+  pp.pos_mode = P.generation ? 2 : 0;  // past_b = key_total[b] - S
   pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
   pp.write_q = 0;
   pp.write_kv = 1;
@@ -808,13 +812,15 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
   f.block = P.bs;
   f.max_blocks = P.max_blocks;
   f.key_total = static_cast<const int32_t*>(in[SPARSE_IN_KEY_TOTAL_SEQUENCE_LENGTHS].data);
+  f.has_past = P.generation;
   f.kv_rows = P.cap;
   f.B = P.B; f.S = P.S; f.N = P.N; f.kvN = P.kvN; f.H = P.H;
   f.scale = resolve_scale(a->scale, P.H);
   f.heads_per_wg = 1;
   f.rows_per_wg = P.bs >= 128 ? 128 : P.bs;
   f.mode = kCsr;
-  const int gx = (P.S + f.rows_per_wg - 1) / f.rows_per_wg;
+  // token generation: row blocks aligned to absolute positions need one more
+  const int gx = (P.S + f.rows_per_wg - 1) / f.rows_per_wg + (P.generation ? 1 : 0);
   CHECK(hip_status(profiled(KVATTN_PROFILE_FLASH, st,
                             [&] { return launch_flash(dt, P.HP, f, gx, P.N, P.B, st); }),
                    "flash launch"));

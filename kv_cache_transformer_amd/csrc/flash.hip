@@ -377,10 +377,17 @@ template <int MODE, int BN> struct FlashWork {
       h = kvh * g + (by % groups) * HW + (wave % HW);
       r0 = bx * p.rows_per_wg;
       nrows = p.S;
+      // CSR token generation: a workgroup's rows are one block of absolute
+      // positions (one CSR row), so the blocks start (past mod block) rows
+      // early and the grid has one workgroup more; rows before 0 do not exist
+      if (MODE == kCsr && p.has_past) {
+        r0 -= max(p.key_total[b] - p.S, 0) % p.rows_per_wg;
+        if (r0 + p.rows_per_wg <= 0 || r0 >= nrows) return false;
+      }
     }
     wrow0 = r0 + 32 * (MODE == kDense ? wave / HW : wave);
     wg_rows_end = min(r0 + p.rows_per_wg, nrows);
-    wave_rows = wrow0 < wg_rows_end;
+    wave_rows = wrow0 < wg_rows_end && wrow0 + 32 > 0;
 
     past = 0;
     if (MODE == kDense) {
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   Mma mma;
   mma.init();
   const int qrow = wrow0 + (lane & 31);
-  const bool row_ok = wave_rows && qrow < wg_rows_end;
+  const bool row_ok = wave_rows && qrow >= 0 && qrow < wg_rows_end;
   // The scores come out of the MFMA already as the softmax exponent
   // (log2 domain): the query carries scale * log2(e), or, with a softcap c,
   // 2 * log2(e) * scale / c, the argument of the exp2 inside tanh.
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   const float qscale = use_cap ? 2.f * kLog2e * p.scale / cap : kLog2e * p.scale;
   const float capA = cap * kLog2e, capB = 2.f * cap * kLog2e;
   {
-    const int rr = min(qrow, nrows - 1);
+    const int rr = min(max(qrow, 0), nrows - 1);
     const T* qp = (MODE == kVarlen)
                       ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
                       : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;

@@ -289,7 +289,10 @@ def test_sparse_rules(lib):
     assert sparse_call(lib, ins, outs, 64) == 0
     assert sparse_call(lib, ins, outs, 64, sparse_block_size=24) == -1
     assert sparse_call(lib, ins, outs, 65) == -1                    # beyond capacity
-    assert sparse_call(lib, ins, outs, 48) == -2                    # token generation
+    assert sparse_call(lib, ins, outs, 48) == -1                    # total below S
+    g = list(ins)
+    g[0], g[1], g[2] = T(F16, B, 1, 4 * H), T(F16, B, 1, 2 * H), T(F16, B, 1, 2 * H)
+    assert sparse_call(lib, g, [T(F16, B, 1, 4 * H), kb.Tensor(), kb.Tensor()], 48) == 0  # generation
     assert sparse_call(lib, ins, outs, 64, do_rotary=1) == -1       # no cos/sin
     i2 = list(ins)
     i2[8], i2[9] = T(F16, 64, 4), T(F16, 64, 4)                     # width 4 not multiple of 8

@@ -85,6 +85,35 @@ SPARSE = [
 ]
 
 
+# token generation (total_sequence_length != S): the new rows follow a past
+# of key_total - S rows in the in-place cache
+SPARSE_GEN = [
+    dict(dtype=F16, B=2, S=1, N=8, kvN=2, H=64, bs=64, cap=512, past_lens=[300, 511], rotary=True),
+    dict(dtype=F16, B=1, S=37, N=4, kvN=2, H=128, bs=16, cap=400, past_lens=[200], rotary=True,
+         interleaved=1),
+    dict(dtype=F32, B=2, S=5, N=4, kvN=4, H=64, bs=32, cap=256, past_lens=[3, 100]),
+    dict(dtype=F16, B=1, S=1, N=8, kvN=2, H=128, bs=128, cap=1000, past_lens=[999],
+         packed_qkv=True, rotary=True, rot_dim=64),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SPARSE_GEN)))
+def test_sparse_generation_parity(idx):
+    spec = dict(SPARSE_GEN[idx])
+    print(f"sparse generation {idx}: {spec}", flush=True)
+    dtype = spec.pop("dtype")
+    case = wl.sparse_case(np.random.default_rng(650 + idx), dtype=dtype, **spec)
+    out, pk, pv = sparse_gpu(case)
+    ref, rpk, rpv = sparse_oracle(case)
+    check_output(out, ref, dtype)
+    tr = np.zeros(pk.shape[:3], bool)
+    if spec.get("rotary"):
+        for b, past in enumerate(spec["past_lens"]):
+            tr[b, :, past:past + spec["S"]] = True
+    check_cache(pk, rpk, tr, "key cache")
+    check_cache(pv, rpv, None, "value cache")
+
+
 @pytest.mark.parametrize("idx", range(len(SPARSE)))
 def test_sparse_parity(idx):
     spec = dict(SPARSE[idx])
