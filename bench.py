@@ -303,6 +303,39 @@ def sparse_workload(torch, kv, wl, args, timer):
     return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, flops=4 * 128 * pairs)
 
 
+def sparse_generation_workload(torch, kv, wl, args, timer):
+    """One generated token per sample over the sparse layouts: the K/V rows
+    of the blocks any query head of a kv head sees are the bytes that must
+    be read."""
+    case = wl.sparse_generation()
+    i = case["inputs"]
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
+    out = torch.empty_like(t["query"])
+    total = case["total_sequence_length"]
+
+    def step(n):
+        kv.sparse_attention(t["query"], t["key"], t["value"], t["past_key"], t["past_value"],
+                            t["block_row_indices"], t["block_col_indices"], total,
+                            t["key_total_sequence_lengths"], t["cos_cache"], t["sin_cache"],
+                            num_heads=32, kv_num_heads=8, sparse_block_size=64, do_rotary=1,
+                            output=out)
+
+    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    rp, cols = i["block_row_indices"], i["block_col_indices"]
+    B, N, kvN, H, bs = 2, 32, 8, 128, 64
+    row = (total - 1) // bs
+    blocks = 0
+    for kh in range(kvN):
+        seen = set()
+        for h in range(kh * (N // kvN), (kh + 1) * (N // kvN)):
+            l = h % rp.shape[0]
+            seen |= set(int(c) for c in cols[l, rp[l, row]:rp[l, row + 1]])
+        blocks += len(seen)
+    kv_bytes = B * blocks * bs * H * 2 * 2
+    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, kv_bytes=kv_bytes)
+
+
 def packed_workload(torch, kv, wl, args, timer):
     case = wl.packed_varlen()
     i = case["inputs"]
@@ -371,7 +404,9 @@ TRAFFIC_KERNELS = [
     ("flash_gqa_long_prefill", r"flash_pipe_kernel(?:ILi128ELi0E|<128, 0,)", "kv_cache_transformer_amd/csrc/flash.hip",
      "gqa_long_prefill"),
     ("flash_sparse_prompt", r"flash_kernelIDF16_Li128ELi\d+ELi1E", "kv_cache_transformer_amd/csrc/flash.hip",
-     "sparse_prompt"),
+     "sparse_prompt", lambda grid: grid >= 1 << 20),
+    ("flash_sparse_generation", r"flash_kernelIDF16_Li128ELi\d+ELi1E", "kv_cache_transformer_amd/csrc/flash.hip",
+     "sparse_generation", lambda grid: grid < 1 << 20),
     ("qkv_gemm_packed_varlen", r"qkv_gemm_kernelIDF16_", "kv_cache_transformer_amd/csrc/packed.hip",
      "packed_varlen"),
     ("window_shift_gqa_window_decode", r"window_shift_kernelIDF16_", "kv_cache_transformer_amd/csrc/prep.hip",
@@ -421,9 +456,13 @@ def summarise_traffic(fetch_dir, write_dir, cmds, probe_mib):
     lines += [f"# calibration: the {probe_mib} MiB device-to-device copy of each run reads FETCH_SIZE "
               f"{f_probe:.0f} KiB (scale {f_scale:.4f}) and WRITE_SIZE {w_probe:.0f} KiB (scale {w_scale:.4f})",
               f"{'kernel':<26} {'launches':>8} {'FETCH KiB':>12} {'WRITE KiB':>12} {'read MB':>10} {'written MB':>10}"]
-    for key, pat, src, workload in TRAFFIC_KERNELS:
-        fr = [float(r["Counter_Value"]) for r in fetch if re.search(pat, r["Kernel_Name"])]
-        wr = [float(r["Counter_Value"]) for r in write if re.search(pat, r["Kernel_Name"])]
+    for key, pat, src, workload, *grid_ok in TRAFFIC_KERNELS:
+        # kernels that two workloads share are told apart by their grid size (threads)
+        ok = grid_ok[0] if grid_ok else (lambda grid: True)
+        fr = [float(r["Counter_Value"]) for r in fetch
+              if re.search(pat, r["Kernel_Name"]) and ok(int(r["Grid_Size"]))]
+        wr = [float(r["Counter_Value"]) for r in write
+              if re.search(pat, r["Kernel_Name"]) and ok(int(r["Grid_Size"]))]
         if not fr or not wr:
             continue
         fk, wk = sum(fr) / len(fr), sum(wr) / len(wr)
@@ -566,6 +605,9 @@ def main():
     if want("sparse_prompt"):
         res["sparse_prompt"] = sparse_workload(torch, kv, wl, args, Timer(torch, lib, 2, hip))
         print("# sparse_prompt done", file=sys.stderr, flush=True)
+    if want("sparse_generation"):
+        res["sparse_generation"] = sparse_generation_workload(torch, kv, wl, args, Timer(torch, lib, 2, hip))
+        print("# sparse_generation done", file=sys.stderr, flush=True)
     if want("gqa_window_decode"):
         res["gqa_window_decode"] = window_decode_workload(torch, kv, wl, args, Timer(torch, lib, 5, hip))
         print("# gqa_window_decode done", file=sys.stderr, flush=True)
@@ -634,6 +676,16 @@ def main():
                          "kernel_ms": round(r["kern_ms"], 4), "algorithmic_bytes": r["shift_bytes"],
                          "traffic": traffic_for("window_shift_gqa_window_decode")}}
 
+    if "sparse_generation" in res:
+        r = res["sparse_generation"]
+        gbs_k = r["kv_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
+        workloads["sparse_generation"] = {
+            "config": "B2 S1 after 8191 past rows, N32 kvN8 H128 fp16 block 64, 4 CSR layouts, NeoX rotary",
+            "call_us": round(r["call_ms"] * 1e3, 2),
+            "roofline": {"bound": "hbm", "kernel": "flash", "achieved": round(gbs_k, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
+                         "kernel_us": round(r["kern_ms"] * 1e3, 3), "algorithmic_bytes": r["kv_bytes"],
+                         "traffic": traffic_for("flash_sparse_generation")}}
     if "gqa_decode_int8" in res:
         r = res["gqa_decode_int8"]
         gbs_k = r["kv_bytes"] / (r["kern_ms"] * 1e-3) / 1e9

@@ -23,6 +23,8 @@ Named workloads (sizes and distributions):
 * ``sparse_prompt``     SparseAttention prompt: B=2, S=8192, N=32, kvN=8, H=128,
   fp16, block 64, four CSR layouts (8 local blocks plus every 8th vertical
   block, lower triangular), NeoX rotary over the full head.
+* ``sparse_generation`` SparseAttention token generation: the sparse prompt's
+  configuration continued by one token after a past of 8191 rows.
 * ``packed_varlen``     PackedAttention: 64 sequences, lengths uniform in
   [32, 512] (padded length 512), hidden 768, weights [768, 2304] ~ N(0,0.02),
   bias ~ N(0,0.02), 12 heads of 64, fp16.
@@ -452,6 +454,30 @@ def sparse_prompt(seed=4, batch=2, seq=8192):
                 total_sequence_length=S)
 
 
+def sparse_generation(seed=5, batch=2, context=8192):
+    """SparseAttention token generation: the sparse prompt's configuration
+    (N=32 kvN=8 H=128 fp16, block 64, the same four layouts, NeoX rotary)
+    continued by one new token per sample after a past of context - 1 rows
+    (cache ~ N(0,1))."""
+    rng = np.random.default_rng(seed)
+    B, S, N, kvN, H, bs = batch, 1, 32, 8, 128, 64
+    q = normal(rng, (B, S, N * H), F16)
+    k = normal(rng, (B, S, kvN * H), F16)
+    v = normal(rng, (B, S, kvN * H), F16)
+    pk = normal(rng, (B, kvN, context, H), F16)
+    pv = normal(rng, (B, kvN, context, H), F16)
+    rp, cols = local_vertical_layouts(4, context // bs, local=8, stride=8)
+    c, s_ = rope_cache(context, H, F16)
+    inputs = dict(query=q, key=k, value=v, past_key=pk, past_value=pv,
+                  block_row_indices=rp, block_col_indices=cols,
+                  key_total_sequence_lengths=np.full(B, context, np.int32),
+                  cos_cache=c, sin_cache=s_)
+    attrs = dict(num_heads=N, kv_num_heads=kvN, sparse_block_size=bs, do_rotary=1,
+                 rotary_interleaved=0, scale=0.0)
+    return dict(op="sparse", name="sparse_generation", inputs=inputs, attrs=attrs,
+                total_sequence_length=context)
+
+
 # --------------------------------------------------------------------------
 # PackedAttention
 # --------------------------------------------------------------------------
@@ -509,5 +535,6 @@ WORKLOADS = {
     "gqa_decode_int8": gqa_decode_int8,
     "gqa_long_prefill": gqa_long_prefill,
     "sparse_prompt": sparse_prompt,
+    "sparse_generation": sparse_generation,
     "packed_varlen": packed_varlen,
 }

@@ -160,6 +160,18 @@ def test_workload_sparse_prompt_sampled_rows():
     print(f"rotated key elements off by 1 ulp: {n1}")
 
 
+def test_workload_sparse_generation():
+    case = wl.sparse_generation()
+    print("sparse_generation", flush=True)
+    out, pk, pv = sparse_gpu(case)
+    ref, rpk, rpv = sparse_oracle(case)
+    check_output(out, ref, F16)
+    tr = np.zeros(pk.shape[:3], bool)
+    tr[:, :, 8191] = True                      # the new (rotated) key row
+    check_cache(pk, rpk, tr, "key cache")
+    check_cache(pv, rpv, None, "value cache")
+
+
 # ---------------------------------------------------------------------------
 # PackedAttention
 # ---------------------------------------------------------------------------

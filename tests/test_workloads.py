@@ -86,3 +86,14 @@ def test_quant_case_int4_layout():
     assert i["present_key"].dtype == np.uint8 and i["present_key"].shape == (2, 2, 10, 32)
     assert i["k_scale"].shape == (1,) and np.isclose(i["k_scale"][0], 3 / 7)
     assert i["v_scale"].shape == (128,)
+
+
+def test_sparse_generation_workload():
+    c = wl.WORKLOADS["sparse_generation"]()
+    i = c["inputs"]
+    assert i["query"].shape == (2, 1, 32 * 128) and i["past_key"].shape == (2, 8, 8192, 128)
+    assert c["total_sequence_length"] == 8192 and np.all(i["key_total_sequence_lengths"] == 8192)
+    rp = i["block_row_indices"]
+    assert rp.shape == (4, 129)
+    # the last row block sees its 8 local blocks plus every 8th block of its layout
+    assert all(rp[l, 128] - rp[l, 127] == 8 + 15 for l in range(4))
