@@ -657,8 +657,13 @@ int dmmha_run(const dmmha_attrs* a, const kvattn_tensor* in, const kvattn_tensor
 struct SparsePlan {
   int B, S, N, kvN, H, HP, dt, cap, L, max_blocks, max_nnz, rot_half, bs;
   bool packed_qkv, rotary, generation;
-  size_t ws_q, ws_total;
+  bool decode;      // one new token: split-key decode over the CSR blocks
+  int64_t waves;
+  size_t ws_q, ws_part, ws_total;
 };
+
+// most CSR blocks per row the decode route takes (its block table sits in LDS)
+constexpr int kSparseDecodeMaxBlocks = 4096;
 
 int sparse_validate(const sparse_attrs* a, const kvattn_tensor* in, int n_in, int total,
                     const kvattn_tensor* out, int n_out, SparsePlan& P) {
@@ -743,7 +748,19 @@ int sparse_validate(const sparse_attrs* a, const kvattn_tensor* in, int n_in, in
       (has(out[SPARSE_OUT_PRESENT_VALUE]) && out[SPARSE_OUT_PRESENT_VALUE].data != pv.data))
     return fail(KVATTN_ERR_INVALID_ARG, "the present caches are the past buffers updated in place");
   P.ws_q = 0;  // the flash kernel rotates the queries as it loads them
-  P.ws_total = P.ws_q;
+  P.ws_part = 0;
+  P.waves = 0;
+  // one generated token: the decode kernel, one unit per query head, over the
+  // blocks of its CSR row; prep writes the rotated query to the workspace
+  P.decode = P.generation && P.S == 1 && P.max_blocks <= kSparseDecodeMaxBlocks;
+  if (P.decode) {
+    const int64_t units = (int64_t)P.B * P.N;
+    P.waves = decode_waves(units, std::min<int64_t>(total, (int64_t)P.max_nnz * bs));
+    if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "sparse decode: too many units");
+    P.ws_q = align256((size_t)P.B * P.N * P.H * elem_size(dt));
+    P.ws_part = align256((size_t)(P.waves / 2) * (P.HP + 4) * sizeof(float));
+  }
+  P.ws_total = P.ws_q + P.ws_part;
   return KVATTN_OK;
 }
 
@@ -777,11 +794,40 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
   pp.lens = static_cast<const int32_t*>(in[SPARSE_IN_KEY_TOTAL_SEQUENCE_LENGTHS].data);
   pp.pos_mode = P.generation ? 2 : 0;  // past_b = key_total[b] - S
   pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
-  pp.write_q = 0;
+  pp.write_q = P.decode ? 1 : 0;
+  pp.q_out = P.decode ? ws : nullptr;
   pp.write_kv = 1;
   pp.win_cap = 0;
   CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
                    "prep launch"));
+
+  if (P.decode) {
+    DecodeParams d{};
+    d.q = ws;
+    d.k_new = d.v_new = nullptr;  // prep wrote the new rows
+    d.kc = in[SPARSE_IN_PAST_KEY].data;
+    d.vc = in[SPARSE_IN_PAST_VALUE].data;
+    d.lens = static_cast<const int32_t*>(in[SPARSE_IN_KEY_TOTAL_SEQUENCE_LENGTHS].data);
+    d.len_mode = 3;
+    d.window = -1;
+    d.out = out[SPARSE_OUT_OUTPUT].data;
+    d.part = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_q);
+    d.B = P.B; d.N = P.N; d.kvN = P.N; d.H = P.H; d.cap = P.cap;
+    d.kv_div = P.N / P.kvN;
+    d.scale = resolve_scale(a->scale, P.H);
+    d.head_groups = 1; d.hpw = 1; d.waves = (int)P.waves;
+    d.csr_rp = static_cast<const int32_t*>(in[SPARSE_IN_BLOCK_ROW_INDICES].data);
+    d.csr_cols = static_cast<const int32_t*>(in[SPARSE_IN_BLOCK_COL_INDICES].data);
+    d.rp_stride = P.max_blocks + 1;
+    d.cols_stride = P.max_nnz;
+    d.num_layout = P.L;
+    d.block = P.bs;
+    d.max_blocks = P.max_blocks;
+    CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st, [&] { return launch_decode(dt, P.HP, d, st); }),
+                     "decode launch"));
+    CHECK(hip_status(launch_decode_combine(dt, P.HP, d, st), "decode combine launch"));
+    return ok();
+  }
 
   FlashParams f{};
   f.q = in[SPARSE_IN_QUERY].data;

@@ -432,6 +432,7 @@ __device__ __forceinline__ void sample_keys(const DecodeParams& p, int b, int& n
                                             int& kstart, int& last_pos) {
   if (p.len_mode == 0) n = p.lens[b] + 1;
   else if (p.len_mode == 1) n = p.lens[0] + 1;
+  else if (p.len_mode == 3) n = p.lens[b];
   else n = p.host_n;
   last_pos = n - 1;
   // sliding-window cache: the buffer's rows after the eviction
@@ -442,9 +443,33 @@ __device__ __forceinline__ void sample_keys(const DecodeParams& p, int b, int& n
   kstart = (p.window >= 0) ? max(0, n - 1 - p.window) : 0;
 }
 
+// CSR block keys: entries [lo, hi) of layout l's column list for the row of
+// the query at position n - 1 (clamped into the arrays, as for prompts).
+__device__ __forceinline__ void csr_row(const DecodeParams& p, int l, int n, int& lo, int& hi) {
+  lo = hi = 0;
+  if (n <= 0) return;
+  const int r = min((n - 1) / p.block, p.max_blocks - 1);
+  lo = max(p.csr_rp[l * p.rp_stride + r], 0);
+  hi = max(min(p.csr_rp[l * p.rp_stride + r + 1], (int)p.cols_stride), lo);
+}
+
+// Keys of the largest unit of a sample with n keys: every unit of the sample
+// is dealt as many pairs (units of shorter rows get shorter runs).
+__device__ int csr_max_keys(const DecodeParams& p, int n) {
+  int m = 0;
+  for (int l = 0; l < min(p.num_layout, p.N); ++l) {
+    int lo, hi;
+    csr_row(p, l, n, lo, hi);
+    m = max(m, hi - lo);
+  }
+  return m * p.block;
+}
+
+template <bool CSR>
 __device__ __forceinline__ int sample_count(const DecodeParams& p, int b) {
   int n, newrow, kstart, last_pos;
   sample_keys(p, b, n, newrow, kstart, last_pos);
+  if constexpr (CSR) return csr_max_keys(p, n);
   return max(n - kstart, 0);
 }
 
@@ -452,9 +477,10 @@ __device__ __forceinline__ int sample_count(const DecodeParams& p, int b) {
 // one), with quota = max(128, ceil(K / (P - U))) for K live keys over U units
 // and P = W / 2 pairs, so the units never need more than P pairs.  Called by
 // all lanes of a wave; c0 is the count of sample `lane` (0 beyond the batch).
+template <bool CSR>
 __device__ int64_t deal_quota(const DecodeParams& p, int ups, int lane, int c0) {
   int64_t k = c0;
-  for (int b = lane + 64; b < p.B; b += 64) k += sample_count(p, b);
+  for (int b = lane + 64; b < p.B; b += 64) k += sample_count<CSR>(p, b);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) k += __shfl_xor(k, m, 64);
   k *= ups;
@@ -488,12 +514,13 @@ __device__ __forceinline__ int wave_scan(int v, int lane) {
 
 // Sample served by pair pr and the first pair of that sample's units; false
 // when pr is beyond the pairs in use.
+template <bool CSR>
 __device__ bool find_sample(const DecodeParams& p, int ups, int64_t quota, int pr, int lane, int c0,
                             int& b_out, int& first_out) {
   int base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int b = b0 + lane;
-    const int c = b0 == 0 ? c0 : (b < p.B ? sample_count(p, b) : 0);
+    const int c = b0 == 0 ? c0 : (b < p.B ? sample_count<CSR>(p, b) : 0);
     const int v = (b < p.B) ? pairs_for(c, quota) * ups : 0;
     const int incl = wave_scan(v, lane);
     const bool hit = b < p.B && pr >= base + incl - v && pr < base + incl;
@@ -510,11 +537,12 @@ __device__ bool find_sample(const DecodeParams& p, int ups, int64_t quota, int p
 }
 
 // First pair of sample b (all lanes of a wave call it).
+template <bool CSR>
 __device__ int sample_first_pair(const DecodeParams& p, int ups, int64_t quota, int b, int lane) {
   int acc = 0;
   for (int b0 = 0; b0 < b; b0 += 64) {
     const int s = b0 + lane;
-    acc += (s < b) ? pairs_for(sample_count(p, s), quota) * ups : 0;
+    acc += (s < b) ? pairs_for(sample_count<CSR>(p, s), quota) * ups : 0;
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m, 64);
@@ -558,7 +586,8 @@ __device__ __forceinline__ void static_for_while(F&& f, std::integer_sequence<in
 
 // FEAT bits: kSoftcap (scores are soft-capped), kExtras (additive bias and/or
 // mask, and/or the qk output).  The plain variant has no per-score checks.
-constexpr int kSoftcap = 1, kExtras = 2;
+// kCsrKeys: keys are CSR blocks (SparseAttention token generation).
+constexpr int kSoftcap = 1, kExtras = 2, kCsrKeys = 4;
 
 template <typename T, int HP, int FEAT>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
@@ -592,13 +621,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   // ---- which unit and which run of its keys (the same for both waves) -------
   // lane i reads the length of sample i once; the deal and this pair's sample
   // take it from there
-  int n_l = 0, newrow_l = -1, kstart_l = 0, last_l = 0;
-  if (lane < p.B) sample_keys(p, lane, n_l, newrow_l, kstart_l, last_l);
+  constexpr bool csr = (FEAT & kCsrKeys) != 0;  // p.csr_rp is set exactly then
+  int n_l = 0, newrow_l = -1, kstart_l = 0, last_l = 0, c_l = 0;
+  if (lane < p.B) {
+    sample_keys(p, lane, n_l, newrow_l, kstart_l, last_l);
+    c_l = csr ? csr_max_keys(p, n_l) : max(n_l - kstart_l, 0);
+  }
   // (the deal is the same in every lane: the values are made scalar, so that
   // the chunk bookkeeping of the streaming loop runs on the scalar unit)
-  const int64_t quota = uniform64(deal_quota(p, ups, lane, max(n_l - kstart_l, 0)));
+  const int64_t quota = uniform64(deal_quota<csr>(p, ups, lane, c_l));
   int b = 0, first = 0;
-  const bool live = find_sample(p, ups, quota, pr, lane, max(n_l - kstart_l, 0), b, first);
+  const bool live = find_sample<csr>(p, ups, quota, pr, lane, c_l, b, first);
   b = __builtin_amdgcn_readfirstlane(b);
   first = __builtin_amdgcn_readfirstlane(first);
   int n = 0, newrow = -1, kstart = 0, last_pos = 0;
@@ -614,7 +647,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   newrow = __builtin_amdgcn_readfirstlane(newrow);
   kstart = __builtin_amdgcn_readfirstlane(kstart);
   last_pos = __builtin_amdgcn_readfirstlane(last_pos);
-  const int c = live ? max(n - kstart, 0) : 0;
+  int c_s = csr ? (b < 64 ? __shfl(c_l, b, 64) : csr_max_keys(p, n)) : max(n - kstart, 0);
+  c_s = __builtin_amdgcn_readfirstlane(c_s);
+  const int c = live ? c_s : 0;
   const int nb = pairs_for(c, quota);
   const int local = pr - first;
   const int ui = live ? local / nb : 0;
@@ -623,13 +658,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   const int kvh = ui / hg, hgrp = ui % hg;
   const int h0 = kvh * g + hgrp * 16;
   const int nh = min(16, g - hgrp * 16);
-  const int lo = kstart + (int)((int64_t)c * kp / nb);
-  const int len = kstart + (int)((int64_t)c * (kp + 1) / nb) - lo;
+  // the run [lo, lo + len) of the unit's keys; CSR units count their keys
+  // block by block in row order ("virtual" keys) and cut runs at multiples of
+  // 16, so that no 16-key sub-tile straddles two blocks
+  int lo, len, csr_lo = 0;
+  if constexpr (csr) {
+    int e_hi;
+    csr_row(p, kvh % p.num_layout, n, csr_lo, e_hi);
+    csr_lo = __builtin_amdgcn_readfirstlane(csr_lo);
+    const int cu = live ? __builtin_amdgcn_readfirstlane((e_hi - csr_lo) * p.block) : 0;
+    lo = (int)((int64_t)cu * kp / nb) & ~15;
+    const int hi = (kp == nb - 1) ? cu : ((int)((int64_t)cu * (kp + 1) / nb) & ~15);
+    len = hi - lo;
+  } else {
+    lo = kstart + (int)((int64_t)c * kp / nb);
+    len = kstart + (int)((int64_t)c * (kp + 1) / nb) - lo;
+  }
   // chunks of the run: chunk ch holds keys [chunk_lo(ch), chunk_lo(ch + 1))
   // each pair owns a fixed slice of the LDS records: chunk ch, head hj at
-  // pair_part + (ch * nh + hj) * RS (pairs of one group may differ in nh)
-  float* pair_part = s_part + jp * (kPartFloats / kPairsPerGroup);
-  const int nch_cap = max(1, min(kMaxChunks, kPartFloats / kPairsPerGroup / (nh * RS)));
+  // pair_part + (ch * nh + hj) * RS (pairs of one group may differ in nh); a
+  // CSR pair keeps the cache blocks of its run at the end of its slice
+  constexpr int kSlice = kPartFloats / kPairsPerGroup;
+  float* pair_part = s_part + jp * kSlice;
+  const int blk0 = csr ? lo / p.block : 0;
+  const int tbl_n = (csr && len > 0) ? (lo + len - 1) / p.block - blk0 + 1 : 0;
+  int* tbl = reinterpret_cast<int*>(pair_part + kSlice) - tbl_n;
+  const int nch_cap = max(1, min(kMaxChunks, (kSlice - tbl_n) / (nh * RS)));
   // chunks of csz keys (a multiple of 16, at least 32); the last may be short
   const int csz = len > 0 ? max(32, (len + nch_cap * 16 - 1) / (nch_cap * 16) * 16) : 32;
   const int nch = (len + csz - 1) / csz;
@@ -639,8 +693,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   const bool appender = append && !younger;
   const int claimable = nch - (append ? 1 : 0);
 
-  CT* kb = static_cast<CT*>(p.kc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
-  CT* vb = static_cast<CT*>(p.vc) + ((int64_t)b * p.kvN + kvh) * p.cap * H;
+  const int kv_div = csr ? max(p.kv_div, 1) : 1;
+  const int64_t slab = (int64_t)b * (p.kvN / kv_div) + kvh / kv_div;
+  CT* kb = static_cast<CT*>(p.kc) + slab * p.cap * H;
+  CT* vb = static_cast<CT*>(p.vc) + slab * p.cap * H;
+  // CSR: the cache block of each block of the run (both waves of the pair
+  // fill the table; every wave of the group passes the barrier)
+  if constexpr (csr) {
+    const int* cols = p.csr_cols + (int64_t)(kvh % p.num_layout) * p.cols_stride + csr_lo + blk0;
+    for (int i = younger * 64 + lane; i < tbl_n; i += 128) tbl[i] = min(max(cols[i], 0), p.max_blocks - 1);
+    __syncthreads();
+  }
   const int half = H / 2;
   const AT* cs = static_cast<const AT*>(p.cos);
   const AT* sn = static_cast<const AT*>(p.sin);
@@ -901,7 +964,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     for (int i = 0; i < 4; ++i) {
       const int key = j0 + 4 * g4 + i;
       const bool ok = head_ok && key < j_end;
-      if constexpr (FEAT == 0) {
+      if constexpr ((FEAT & (kSoftcap | kExtras)) == 0) {
         const float v = sc[i] * smul_l2;
         x[i] = ok ? v : kNegInf;
         tmax = fmaxf(tmax, x[i]);
@@ -967,15 +1030,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     ns = (ce - ca + 15) / 16;
   };
   if (live) enter(appender ? nch - 1 : claim());
-  int b_j0[R], b_end[R], b_ch[R];
+  // b_off: cache row minus key index in the sub-tile (CSR block keys; else 0)
+  int b_j0[R], b_end[R], b_ch[R], b_off[R];
   bool b_last[R];
   auto next_load = [&](auto rt) {
     constexpr int r = decltype(rt)::value;
+    b_off[r] = 0;
     if (lc < nch) {
       b_j0[r] = ca + 16 * ls;
       b_end[r] = ce;
       b_ch[r] = lc;
       b_last[r] = ls == ns - 1;
+      if constexpr (csr) {
+        const int e = b_j0[r] / p.block;
+        b_off[r] = __builtin_amdgcn_readfirstlane((tbl[e - blk0] - e) * p.block);
+      }
       if (++ls == ns) enter(claim());
     } else {
       b_j0[r] = kstart;
@@ -983,7 +1052,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
       b_ch[r] = -1;
       b_last[r] = false;
     }
-    tile.template load_kv<r>(kb, vb, b_j0[r], b_end[r] - 1, H, lane);
+    // rows of the sub-tile (a 16-key sub-tile lies inside one block)
+    const int pj = min(b_j0[r] + b_off[r], p.cap - 1);
+    const int pl = min(min(b_end[r] - 1, b_j0[r] + 15) + b_off[r], p.cap - 1);
+    tile.template load_kv<r>(kb, vb, pj, pl, H, lane);
   };
   // the chunk's (m, l, o) into its LDS record; the state restarts
   auto flush = [&](int ch) {
@@ -1010,7 +1082,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
           constexpr int r = decltype(rt)::value;
           next_load(std::integral_constant<int, (r + R - 1) % R>{});
           if (go && b_ch[r] >= 0) {
-            process(std::integral_constant<int, r>{}, b_j0[r], b_end[r]);
+            // CSR block keys: visible up to the query's own row
+            const int j_end = csr ? min(b_end[r], last_pos - b_off[r] + 1) : b_end[r];
+            process(std::integral_constant<int, r>{}, b_j0[r], j_end);
             if (b_last[r]) flush(b_ch[r]);
           } else {
             go = false;
@@ -1064,7 +1138,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 // Merge the partials of one (sample, query head): a first pass over the
 // partials' (max, sum) pairs, then every thread sums one quad of dims over a
 // stride of the partials, and the strides are added in LDS.
-template <typename T, int HP>
+template <typename T, int HP, bool CSR>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   constexpr int NQD = HP / 4;            // quads of a padded head
   constexpr int NG = 256 / NQD;          // partial strides
@@ -1073,11 +1147,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = p.N / p.kvN, hg = p.head_groups, ups = p.kvN * hg;
-  const int64_t quota = deal_quota(p, ups, lane, lane < p.B ? sample_count(p, lane) : 0);
-  const int c = sample_count(p, b);
+  const int64_t quota = deal_quota<CSR>(p, ups, lane, lane < p.B ? sample_count<CSR>(p, lane) : 0);
+  const int c = sample_count<CSR>(p, b);
   const int nb = pairs_for(c, quota);
   if (unit_direct(c, nb)) return;  // written directly
-  const int first = sample_first_pair(p, ups, quota, b, lane);
+  const int first = sample_first_pair<CSR>(p, ups, quota, b, lane);
   const int kvh = h / g, hgrp = (h % g) / 16, hh = (h % g) % 16;
   const int pair0 = first + (kvh * hg + hgrp) * nb;
   const int wb = nb;  // one partial per pair of the unit
@@ -1145,6 +1219,10 @@ hipError_t launch_decode_f(const DecodeParams& p, hipStream_t s) {
 
 template <typename T, int HP>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+  if constexpr (!std::is_same<T, QuantI8>::value) {
+    // CSR block keys come without bias, mask, qk or softcap
+    if (p.csr_rp != nullptr) return launch_decode_f<T, HP, kCsrKeys>(p, s);
+  }
   const bool extras = p.bias != nullptr || p.mask != nullptr || p.qk != nullptr;
   const bool cap = p.softcap > 0.f;
   if (extras) {
@@ -1157,7 +1235,10 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
 
 template <typename T, int HP>
 hipError_t launch_combine_t(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_combine_kernel<T, HP>), dim3(p.N, p.B), dim3(256), 0, s, p);
+  if (p.csr_rp != nullptr)
+    hipLaunchKernelGGL((decode_combine_kernel<T, HP, true>), dim3(p.N, p.B), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<T, HP, false>), dim3(p.N, p.B), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -109,7 +109,7 @@ struct DecodeParams {
   const void* sink;         // (N) or null
   int smooth;               // 1: zero sink when no sink tensor
   const int32_t* lens;      // device lengths
-  int len_mode;             // 0: n_b = lens[b] + 1; 1: n_b = lens[0] + 1; 2: n_b = host_n
+  int len_mode;             // 0: n_b = lens[b] + 1; 1: n_b = lens[0] + 1; 2: n_b = host_n; 3: n_b = lens[b]
   int host_n;
   int window;               // >= 0: keys j >= (n_b - 1) - window
   int win_cap;              // > 0: sliding-window cache of this capacity (len_mode 0 only)
@@ -125,6 +125,16 @@ struct DecodeParams {
   // folded into the query, the value scales applied to each pair's output
   const float* k_scale; const float* v_scale;
   int k_scale_pc, v_scale_pc;  // 1: kvN*H per-channel scales; 0: one scale
+  // cache slabs: unit kv index k reads slab b * (kvN / kv_div) + k / kv_div
+  // (0 = 1: one slab per unit kv index)
+  int kv_div;
+  // CSR block keys (SparseAttention token generation, len_mode 3): a unit is
+  // one query head h (kvN = N); its keys are the blocks of CSR row
+  // (n_b - 1) / block of layout h mod num_layout, in row order; a key is
+  // visible iff its row is <= n_b - 1.  Null csr_rp: keys [kstart, n_b).
+  const int32_t* csr_rp; const int32_t* csr_cols;
+  int64_t rp_stride, cols_stride;
+  int num_layout, block, max_blocks;
 };
 
 // ---------------------------------------------------------------------------

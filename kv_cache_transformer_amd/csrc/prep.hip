@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
   const int rpos = (cs != nullptr) ? min(max(pos, 0), p.rot_rows - 1) : 0;
   const bool row_ok = crow >= 0 && crow < p.cap;
 
-  for (int base = 0; base < total; base += 4) {
+  for (int base = 4 * (int)blockIdx.y; base < total; base += 4 * (int)gridDim.y) {
     const int item = base + wave;
     if (item < total) {
       int kind, h;  // kind 0 = query, 1 = key, 2 = value
@@ -377,7 +377,11 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
       hipLaunchKernelGGL(prep_kv_kernel<float>, dim3((int)blocks), dim3(kPrepThreads), 0, s, p);
     return hipGetLastError();
   }
-  dim3 grid(p.B * p.S);
+  // few tokens (decode-sized calls): the heads of a token are spread over
+  // several workgroups as well
+  const int items = (p.write_q ? p.N : 0) + (p.write_kv ? 2 * p.kvN : 0);
+  const int gy = (p.B * p.S < 1024) ? std::min((items + 3) / 4, 16) : 1;
+  dim3 grid(p.B * p.S, std::max(gy, 1));
   if (dt == DType::F16)
     hipLaunchKernelGGL(prep_kernel<f16>, grid, dim3(kPrepThreads), 0, s, p);
   else

@@ -94,6 +94,9 @@ SPARSE_GEN = [
     dict(dtype=F32, B=2, S=5, N=4, kvN=4, H=64, bs=32, cap=256, past_lens=[3, 100]),
     dict(dtype=F16, B=1, S=1, N=8, kvN=2, H=128, bs=128, cap=1000, past_lens=[999],
          packed_qkv=True, rotary=True, rot_dim=64),
+    dict(dtype=F32, B=3, S=1, N=4, kvN=1, H=64, bs=16, cap=300, past_lens=[5, 299, 100],
+         rotary=True, rot_dim=32, interleaved=1),
+    dict(dtype=F16, B=1, S=1, N=16, kvN=4, H=256, bs=32, cap=2000, past_lens=[1234]),
 ]
 
 
