@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--counters-from", nargs=2, metavar=("DIR", "COMMAND"), default=None,
                     help="CPU only: summarise one rocprofv3 --pmc run of SQ/GRBM counters (made by "
                          "COMMAND) into profiles/sq_counters_all_workloads.txt")
+    ap.add_argument("--traffic-merge", action="store_true",
+                    help="CPU only, with --traffic-from: keep the entries of profiles/traffic.json this run "
+                         "does not measure")
     ap.add_argument("--traffic-cmd", nargs=2, default=None,
                     help="the two profiler commands, recorded in the traffic summary")
     return ap.parse_args()
@@ -402,7 +405,7 @@ _KERNEL_SOURCES = ["kv_cache_transformer_amd/csrc/device_common.hpp",
                    "kv_cache_transformer_amd/csrc/kvattn_internal.hpp",
                    "kv_cache_transformer_amd/csrc/api.cpp"]
 TRAFFIC_KERNELS = [
-    ("decode", r"decode_kernelIDF16_Li128E", "kv_cache_transformer_amd/csrc/decode.hip", "gqa_decode"),
+    ("decode", r"decode_kernelIDF16_Li128ELi0E", "kv_cache_transformer_amd/csrc/decode.hip", "gqa_decode"),
     ("flash_gqa_long_prefill", r"flash_pipe_kernel(?:ILi128ELi0E|<128, 0,)", "kv_cache_transformer_amd/csrc/flash.hip",
      "gqa_long_prefill"),
     ("flash_sparse_prompt", r"flash_kernelIDF16_Li128ELi\d+ELi1E", "kv_cache_transformer_amd/csrc/flash.hip",
@@ -411,8 +414,8 @@ TRAFFIC_KERNELS = [
      "packed_varlen"),
     ("window_shift_gqa_window_decode", r"window_shift_kernelIDF16_", "kv_cache_transformer_amd/csrc/prep.hip",
      "gqa_window_decode"),
-    ("decode_gqa_decode_int8", r"decode_kernelINS0_7QuantI8ELi128E", "kv_cache_transformer_amd/csrc/decode.hip",
-     "gqa_decode_int8"),
+    ("decode_gqa_decode_int8", r"decode_kernel(?:INS0_7QuantI8ELi128E|<[^<>]*QuantI8, 128,)",
+     "kv_cache_transformer_amd/csrc/decode.hip", "gqa_decode_int8"),
 ]
 
 
@@ -424,11 +427,13 @@ def _sources_sha(files):
     return h.hexdigest()
 
 
-def summarise_traffic(fetch_dir, write_dir, cmds, probe_mib):
+def summarise_traffic(fetch_dir, write_dir, cmds, probe_mib, merge=False):
     """Per-launch HBM bytes of the library's kernels from two rocprofv3
     counter runs.  Each counter is scaled by what it reads for the largest
     device-to-device copy of the same run (a copy of known size), and the
-    figure is stored with a hash of the kernel's sources."""
+    figure is stored with a hash of the kernel's sources.  With ``merge`` the
+    entries of profiles/traffic.json that this run does not measure are kept
+    (workloads launching the same kernel are counted in runs of their own)."""
     import csv
     import glob
     import re
@@ -449,14 +454,20 @@ def summarise_traffic(fetch_dir, write_dir, cmds, probe_mib):
     fetch, f_probe = load(fetch_dir, "FETCH_SIZE")
     write, w_probe = load(write_dir, "WRITE_SIZE")
     f_scale, w_scale = probe_kib / f_probe, probe_kib / w_probe
-    out = {}
-    lines = ["# HBM traffic per launch of the library's kernels, all bench workloads",
-             "# commands (on the GPU host, from the repository root), one counter per run:"]
-    lines += [f"#   {c}" for c in (cmds or ["(not recorded)"])]
-    lines += [f"# calibration: the {probe_mib} MiB device-to-device copy of each run reads FETCH_SIZE "
-              f"{f_probe:.0f} KiB (scale {f_scale:.4f}) and WRITE_SIZE {w_probe:.0f} KiB (scale {w_scale:.4f})",
-              f"{'kernel':<26} {'launches':>8} {'FETCH KiB':>12} {'WRITE KiB':>12} {'read MB':>10} {'written MB':>10}"]
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    out = json.load(open(path)) if (merge and os.path.exists(path)) else {}
+    # a run measures the workloads its command names (bench.py --only ...), or all
+    ran = set()
+    for c in cmds or []:
+        toks = c.split()
+        if "--only" in toks:
+            for t in toks[toks.index("--only") + 1:]:
+                if t.startswith("--"):
+                    break
+                ran.add(t)
     for key, pat, src, workload, *grid_ok in TRAFFIC_KERNELS:
+        if ran and workload not in ran:
+            continue
         # kernels that two workloads share are told apart by their grid size (threads)
         ok = grid_ok[0] if grid_ok else (lambda grid: True)
         fr = [float(r["Counter_Value"]) for r in fetch
@@ -469,15 +480,34 @@ def summarise_traffic(fetch_dir, write_dir, cmds, probe_mib):
         rb, wb = fk * 1024 * f_scale, wk * 1024 * w_scale
         sources = [src] + _KERNEL_SOURCES
         out[key] = {"bytes_per_launch": int(round(rb + wb)), "fetch_bytes": int(round(rb)),
-                    "write_bytes": int(round(wb)), "fetch_scale": f_scale, "write_scale": w_scale,
+                    "write_bytes": int(round(wb)), "fetch_kib": fk, "write_kib": wk,
+                    "fetch_scale": f_scale, "write_scale": w_scale, "probe_mib": probe_mib,
+                    "probe_fetch_kib": f_probe, "probe_write_kib": w_probe,
                     "launches": len(fr), "sources": sources, "source_sha256": _sources_sha(sources),
-                    "workload": workload, "profile": "profiles/traffic_all_workloads.txt"}
-        lines.append(f"{key:<26} {len(fr):>8} {fk:>12.1f} {wk:>12.1f} {rb / 1e6:>10.2f} {wb / 1e6:>10.2f}")
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+                    "workload": workload, "commands": list(cmds or ["(not recorded)"]),
+                    "profile": "profiles/traffic_all_workloads.txt"}
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
+    lines = ["# HBM traffic per launch of the library's kernels (bench workloads)",
+             "# each group: the commands (on the GPU host, from the repository root), one counter per",
+             "# run, and the calibration of that group's counters by its device-to-device copy"]
+    groups = {}
+    for key, e in out.items():
+        groups.setdefault(tuple(e.get("commands", [])), []).append((key, e))
+    for cmd_group, ents in groups.items():
+        e0 = ents[0][1]
+        lines += [f"#   {c}" for c in cmd_group]
+        lines += [f"# calibration: the {e0.get('probe_mib', probe_mib)} MiB copy reads FETCH_SIZE "
+                  f"{e0.get('probe_fetch_kib', 0):.0f} KiB (scale {e0['fetch_scale']:.4f}) and WRITE_SIZE "
+                  f"{e0.get('probe_write_kib', 0):.0f} KiB (scale {e0['write_scale']:.4f})",
+                  f"{'kernel':<32} {'launches':>8} {'FETCH KiB':>12} {'WRITE KiB':>12} {'read MB':>10} {'written MB':>10}"]
+        for key, e in ents:
+            lines.append(f"{key:<32} {e['launches']:>8} {e.get('fetch_kib', 0):>12.1f} {e.get('write_kib', 0):>12.1f} "
+                         f"{e['fetch_bytes'] / 1e6:>10.2f} {e['write_bytes'] / 1e6:>10.2f}")
+        lines.append("")
     with open(os.path.join(ROOT, "profiles", "traffic_all_workloads.txt"), "w") as f:
-        f.write("\n".join(lines) + "\n")
+        f.write("\n".join(lines))
     print("\n".join(lines))
 
 
@@ -490,7 +520,7 @@ def summarise_counters(d, cmd):
     import glob
     import re
     pat = re.compile(r"(flash_pipe_kernel|flash_kernel|decode_kernel|decode_combine_kernel|qkv_gemm_kernel|prep_kv_kernel|"
-                     r"window_shift_kernel|prep_kernel|packed_sched_kernel)(?:I(DF16_|f)(?:Li(\d+)ELi(\d+)ELi(\d+))?)?")
+                     r"window_shift_kernel|prep_kernel|packed_sched_kernel)(?:I(DF16_|f)(?:Li(\d+)ELi(\d+)(?:ELi(\d+))?)?)?")
     agg, dur = {}, {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
@@ -509,6 +539,8 @@ def summarise_counters(d, cmd):
             if qm:  # int8-cache decode
                 t, hd, md = "q8", qm.group(1), None
             mode = {"0": "dense", "1": "csr", "2": "varlen"}.get(md, "")
+            if m.group(1) == "decode_kernel" and m.group(4) is not None and not qm:
+                mode = "feat" + m.group(4)  # decode_kernel<type, head, features>
             key = m.group(1) + (f"<{t},{hd},{mode}>" if hd else (f"<{t}>" if t else ""))
             agg.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
@@ -563,7 +595,7 @@ def main():
         return
     if args.traffic_from:
         summarise_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_cmd,
-                          args.copy_probe_mib or 512)
+                          args.copy_probe_mib or 512, merge=args.traffic_merge)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
