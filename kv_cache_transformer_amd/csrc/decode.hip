@@ -1135,17 +1135,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Merge the partials of one (sample, query head): a first pass over the
-// partials' (max, sum) pairs, then every thread sums one quad of dims over a
-// stride of the partials, and the strides are added in LDS.
+// Merge the partials of one (sample, query head): every thread merges one
+// quad of dims over a stride of the partials in one pass (running maximum),
+// and the strides are merged in LDS.
 template <typename T, int HP, bool CSR>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   constexpr int NQD = HP / 4;            // quads of a padded head
   constexpr int NG = 256 / NQD;          // partial strides
-  __shared__ float red_m[4], red_l[4];
   __shared__ float4v acc_s[NG][NQD];
+  __shared__ float2v ml_s[NG];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
   const int g = p.N / p.kvN, hg = p.head_groups, ups = p.kvN * hg;
   const int64_t quota = deal_quota<CSR>(p, ups, lane, lane < p.B ? sample_count<CSR>(p, lane) : 0);
   const int c = sample_count<CSR>(p, b);
@@ -1157,51 +1157,40 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int wb = nb;  // one partial per pair of the unit
   auto rec = [&](int i) { return p.part + ((int64_t)(pair0 + i) * p.hpw + hh) * (HP + 4); };
 
-  // pass 1: M = max m_i, L = sum l_i 2^(m_i - M)
-  float M = kNegInf, L = 0.f;
-  for (int i = tid; i < wb; i += 256) {
-    const float2v ml = *reinterpret_cast<const float2v*>(rec(i));
-    const float mn = fmaxf(M, ml[0]);
-    const float mu = (mn == kNegInf) ? 0.f : mn;
-    L = L * fast_exp2(M - mu) + ml[1] * fast_exp2(ml[0] - mu);
-    M = mn;
-  }
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const float m2 = shfl_xor(M, s), l2 = shfl_xor(L, s);
-    const float mn = fmaxf(M, m2);
-    const float mu = (mn == kNegInf) ? 0.f : mn;
-    L = L * fast_exp2(M - mu) + l2 * fast_exp2(m2 - mu);
-    M = mn;
-  }
-  if (lane == 0) {
-    red_m[wave] = M;
-    red_l[wave] = L;
-  }
-  __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  L = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) L += red_l[w] * fast_exp2(red_m[w] - Mu);
-
-  // pass 2: sum of o_i 2^(m_i - M) per quad of dims
+  // One pass: thread (dq, gs) merges the partials gs, gs + NG, ... of its quad
+  // of dims online (running max); the NG strides are then merged in LDS.
   const int dq = tid % NQD, gs = tid / NQD;
+  const bool dq_ok = 4 * dq < p.H;
+  float Ms = kNegInf, Ls = 0.f;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  if (4 * dq < p.H) {
-#pragma unroll 4
-    for (int i = gs; i < wb; i += NG) {
-      const float* r = rec(i);
-      const float f = fast_exp2(r[0] - Mu);
-      acc += *reinterpret_cast<const float4v*>(r + 4 + 4 * dq) * f;
-    }
+#pragma unroll 2
+  for (int i = gs; i < wb; i += NG) {
+    const float* r = rec(i);
+    const float2v ml = *reinterpret_cast<const float2v*>(r);
+    const float4v o4 = dq_ok ? *reinterpret_cast<const float4v*>(r + 4 + 4 * dq) : float4v{0.f, 0.f, 0.f, 0.f};
+    const float mn = fmaxf(Ms, ml[0]);
+    const float mu = (mn == kNegInf) ? 0.f : mn;
+    const float fa = fast_exp2(Ms - mu), fb = fast_exp2(ml[0] - mu);
+    Ls = Ls * fa + ml[1] * fb;
+    acc = acc * fa + o4 * fb;
+    Ms = mn;
   }
   acc_s[gs][dq] = acc;
+  if (dq == 0) ml_s[gs] = float2v{Ms, Ls};
   __syncthreads();
-  if (tid < NQD && 4 * tid < p.H) {
-    float4v o = acc_s[0][tid];
+  if (tid < NQD && dq_ok) {
+    float M = kNegInf;
 #pragma unroll
-    for (int s = 1; s < NG; ++s) o += acc_s[s][tid];
+    for (int s = 0; s < NG; ++s) M = fmaxf(M, ml_s[s][0]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float L = 0.f;
+    float4v o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NG; ++s) {
+      const float f = fast_exp2(ml_s[s][0] - Mu);
+      L += ml_s[s][1] * f;
+      o += acc_s[s][tid] * f;
+    }
     bool has;
     const float sg = read_sink<T>(p, h, has);
     const float inv = final_scale(M, L, has, sg);
