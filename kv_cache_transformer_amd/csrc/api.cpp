@@ -920,6 +920,7 @@ int packed_validate(const packed_attrs* a, const kvattn_tensor* in, int n_in,
   P.H = P.qh / P.N;
   CHECK(check_head_size(P.H, "packed_attention"));
   P.HP = padded_head(P.H);
+  if (P.D <= 0) return fail(KVATTN_ERR_INVALID_ARG, "input hidden size must be positive");
   if (P.D % 8 || P.C % 8) return fail(KVATTN_ERR_UNSUPPORTED, "input hidden %d and weight columns %d must be multiples of 8", P.D, P.C);
   const kvattn_tensor& to = in[PACKED_IN_TOKEN_OFFSET];
   const kvattn_tensor& cum = in[PACKED_IN_CUMULATIVE_SEQUENCE_LENGTH];

@@ -10,9 +10,14 @@
 //   * QKV projection: qkv[T, q+k+v] = input[T, D] . weights[D, q+k+v] + bias
 //     (PackedAttention page, Inputs table: weights columns are [Q all heads |
 //     K all heads | V all heads]) as an MFMA GEMM with 128x128 output tiles,
-//     LDS double buffering and the bias added in the epilogue.  The weights
-//     are row-major [D][cols], so the B operand (k-contiguous per lane) is
-//     read from the LDS tile with ds_read_b64_tr_b16.
+//     LDS double buffering fed from register stages a few tiles ahead, and
+//     the bias added in an epilogue that goes through LDS so that the output
+//     is stored in 16-byte chunks.  The weights are row-major [D][cols], so
+//     the B operand (k-contiguous per lane) is read from the LDS tile with
+//     ds_read_b64_tr_b16.
+#include <type_traits>
+#include <utility>
+
 #include "device_common.hpp"
 #include "kvattn_internal.hpp"
 
@@ -82,6 +87,18 @@ __global__ __launch_bounds__(256) void packed_sched_kernel(PackedSchedParams p) 
 // QKV projection GEMM
 // ---------------------------------------------------------------------------
 constexpr int BM = 128, BNC = 128;
+// register stages of the operand prefetch (tiles in flight while one is used)
+constexpr int kGemmStages = 3;
+
+// Calls f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>).
+template <int N, typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for_int(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 // k depth of a tile (64 measured slower for f16: three waves per SIMD become two)
 template <typename T> struct GemmBK { static constexpr int value = 32; };
 template <> struct GemmBK<float> { static constexpr int value = 32; };
@@ -93,6 +110,19 @@ __device__ __forceinline__ half4v lds_tr16(const f16* ptr) {
   return half4v{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
 }
 
+// four consecutive elements stored at once
+template <typename T> struct Quad4;
+template <> struct Quad4<f16> {
+  __device__ static void store(f16* y, const float (&v)[4]) {
+    *reinterpret_cast<half4v*>(y) = half4v{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+  }
+};
+template <> struct Quad4<float> {
+  __device__ static void store(float* y, const float (&v)[4]) {
+    *reinterpret_cast<float4v*>(y) = float4v{v[0], v[1], v[2], v[3]};
+  }
+};
+
 template <typename T> struct GemmTile;
 
 template <> struct GemmTile<f16> {
@@ -102,7 +132,9 @@ template <> struct GemmTile<f16> {
   // rows of one transposing read (64 bytes each) tile the banks exactly
   static constexpr int BS = BNC + 32;
   static constexpr int CH = 8;
-  // acc[i][j]: 32x32 output block (i: m, j: n) of this wave's 64x64
+  // acc[i][j]: 32x32 output block (i: m, j: n) of this wave's 64x64, held
+  // transposed (B^T A^T): lane l has m = l % 32 and four runs of four
+  // consecutive n, so the epilogue stores 4 elements at a time
   __device__ static void step(const f16* As, const f16* Bs, int wm, int wn, int lane,
                               float16v (&acc)[2][2]) {
     const int G = lane >> 4, t = lane & 15, c = t & 3, ir = t >> 2;
@@ -123,7 +155,7 @@ template <> struct GemmTile<f16> {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
     }
   }
 };
@@ -146,7 +178,7 @@ template <> struct GemmTile<float> {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x2f32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x2f32(b[j], a[i], acc[i][j]);
     }
   }
 };
@@ -177,39 +209,47 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
   const T* X = static_cast<const T*>(p.x);
   const T* W = static_cast<const T*>(p.w);
 
-  uint4v stage[CPT];
-  auto load = [&](int k0) {
+  // register stages: tile kt + 1 waits in registers for its LDS buffer while
+  // tiles up to kt + NS are still in flight
+  constexpr int NS = kGemmStages;
+  uint4v stages[NS][CPT];
+  // Every load is issued (addresses clamped into the operands, K >= CH and
+  // Ncol a multiple of CH), so the waits can stay partial; chunks past the
+  // operands' edges are zeroed when they are written to LDS.
+  static_assert(A_CH % 256 == 0 && B_CH % 256 == 0, "whole chunk rows per thread");
+  auto load = [&](auto st, int k0) {
+    uint4v (&stage)[CPT] = stages[decltype(st)::value];
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int idx = tid + 256 * u;
-      if (idx < A_CH) {
+      if (u < A_CH / 256) {
         const int r = idx / (BK / CH), kc = (idx % (BK / CH)) * CH;
-        const int gm = min(m0 + r, p.M - 1), gk = k0 + kc;
-        stage[u] = (gk < p.K) ? *reinterpret_cast<const uint4v*>(X + (int64_t)gm * p.K + gk)
-                              : uint4v{0u, 0u, 0u, 0u};
+        const int gm = min(m0 + r, p.M - 1), gk = min(k0 + kc, p.K - CH);
+        stage[u] = *reinterpret_cast<const uint4v*>(X + (int64_t)gm * p.K + gk);
       } else {
         const int bi = idx - A_CH;
         const int r = bi / (BNC / CH), nc = (bi % (BNC / CH)) * CH;
-        const int gk = k0 + r, gn = n0 + nc;
-        stage[u] = (gk < p.K && gn < p.Ncol)
-                       ? *reinterpret_cast<const uint4v*>(W + (int64_t)gk * p.Ncol + gn)
-                       : uint4v{0u, 0u, 0u, 0u};
+        const int gk = min(k0 + r, p.K - 1), gn = min(n0 + nc, p.Ncol - CH);
+        stage[u] = *reinterpret_cast<const uint4v*>(W + (int64_t)gk * p.Ncol + gn);
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](auto st, int buf, int k0) {
+    const uint4v (&stage)[CPT] = stages[decltype(st)::value];
     T* As = lds + buf * (A_EL + B_EL);
     T* Bs = As + A_EL;
+    const uint4v zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int idx = tid + 256 * u;
-      if (idx < A_CH) {
+      if (u < A_CH / 256) {
         const int r = idx / (BK / CH), kc = (idx % (BK / CH)) * CH;
-        *reinterpret_cast<uint4v*>(As + r * AS + kc) = stage[u];
+        *reinterpret_cast<uint4v*>(As + r * AS + kc) = (k0 + kc < p.K) ? stage[u] : zero;
       } else {
         const int bi = idx - A_CH;
         const int r = bi / (BNC / CH), nc = (bi % (BNC / CH)) * CH;
-        *reinterpret_cast<uint4v*>(Bs + r * BS + nc) = stage[u];
+        *reinterpret_cast<uint4v*>(Bs + r * BS + nc) =
+            (k0 + r < p.K && n0 + nc < p.Ncol) ? stage[u] : zero;
       }
     }
   };
@@ -221,42 +261,68 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
     for (int j = 0; j < 2; ++j) acc[i][j] = float16v{};
 
   const int nk = (p.K + BK - 1) / BK;
-  load(0);
-  store(0);
+  // prologue: tiles 0 .. NS - 1 in flight (past the last tile: the last one
+  // again), tile 0 into LDS buffer 0
+  const int k_last = (nk - 1) * BK;
+  static_for_int<NS>([&](auto st) { load(st, min(decltype(st)::value * BK, k_last)); });
+  store(std::integral_constant<int, 0>{}, 0, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * BK);
-    const T* As = lds + buf * (A_EL + B_EL);
-    G::step(As, As + A_EL, wm, wn, lane, acc);
-    if (kt + 1 < nk) store(buf ^ 1);
-    __syncthreads();
+  // iteration kt: MFMAs on buffer kt & 1; tile kt + 1 (stage (kt + 1) % NS)
+  // into the other buffer; tile kt + NS loads into stage kt % NS, free since
+  // tile kt went to LDS
+  for (int k0 = 0; k0 < nk; k0 += NS) {
+    static_for_int<NS>([&](auto st) {
+      constexpr int s0 = decltype(st)::value;
+      const int kt = k0 + s0;
+      if (kt < nk) {
+        const T* As = lds + (kt & 1) * (A_EL + B_EL);
+        G::step(As, As + A_EL, wm, wn, lane, acc);
+        if (kt + 1 < nk) store(std::integral_constant<int, (s0 + 1) % NS>{}, (kt + 1) & 1, (kt + 1) * BK);
+        load(std::integral_constant<int, s0>{}, min((kt + NS) * BK, k_last));
+        __syncthreads();
+      }
+    });
   }
 
   mfma_result_fence();
-  T* Y = static_cast<T*>(p.y);
+  // Epilogue through LDS: the transposed blocks (element e of acc[i][j] is
+  // m = ... + lane % 32, n = ... + 8 (e / 4) + 4 (lane / 32) + e % 4) go with
+  // the bias into a row-major tile, which is then stored in 16-byte chunks
+  // (Ncol and the head size are multiples of 8, so a chunk stays in one head).
+  // The last loop iteration ended with a barrier, so the stage buffers are free.
+  constexpr int CS = BNC + 8;  // tile row stride (elements)
+  static_assert(BM * CS <= 2 * (A_EL + B_EL), "the output tile fits the stage buffers");
+  T* Cs = lds;
   const T* bias = static_cast<const T*>(p.bias);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + 64 * wn + 32 * j + (lane & 31);
-    if (n >= p.Ncol) continue;
-    const float bv = to_f32(bias[n]);
-    // row-major Y[m][n], or head-major Y[n / hd][m][n % hd] for head size hd
-    int64_t col, mstride;
-    if (p.head_dim > 0) {
-      col = (int64_t)(n / p.head_dim) * p.M * p.head_dim + n % p.head_dim;
-      mstride = p.head_dim;
-    } else {
-      col = n;
-      mstride = p.Ncol;
-    }
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int q = 0; q < 4; ++q) {
+      const int nl = 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
+      float bv[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (m < p.M) Y[col + (int64_t)m * mstride] = from_f32<T>(acc[i][j][e] + bv);
+      for (int r = 0; r < 4; ++r) bv[r] = (n0 + nl + r < p.Ncol) ? to_f32(bias[n0 + nl + r]) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ml = 64 * wm + 32 * i + (lane & 31);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + bv[r];
+        Quad4<T>::store(Cs + ml * CS + nl, v);
       }
+    }
+  __syncthreads();
+  T* Y = static_cast<T*>(p.y);
+  constexpr int CPR = BNC / CH;  // chunks per tile row
+  for (int c = tid; c < BM * CPR; c += 256) {
+    const int r = c / CPR, cc = (c % CPR) * CH;
+    const int m = m0 + r, n = n0 + cc;
+    if (m >= p.M || n >= p.Ncol) continue;
+    // row-major Y[m][n], or head-major Y[n / hd][m][n % hd] for head size hd
+    const int64_t at = (p.head_dim > 0)
+                           ? ((int64_t)(n / p.head_dim) * p.M + m) * p.head_dim + n % p.head_dim
+                           : (int64_t)m * p.Ncol + n;
+    *reinterpret_cast<uint4v*>(Y + at) = *reinterpret_cast<const uint4v*>(Cs + r * CS + cc);
   }
 }
 
