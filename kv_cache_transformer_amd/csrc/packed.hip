@@ -86,9 +86,11 @@ __global__ __launch_bounds__(256) void packed_sched_kernel(PackedSchedParams p) 
 // ---------------------------------------------------------------------------
 // QKV projection GEMM
 // ---------------------------------------------------------------------------
-constexpr int BM = 128, BNC = 128;
+constexpr int BNC = 128;
 // register stages of the operand prefetch (tiles in flight while one is used)
 constexpr int kGemmStages = 3;
+// 32-row blocks per wave of the f16 GEMM (workgroup tile 256 x 128)
+constexpr int kGemmMbF16 = 4;
 
 // Calls f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>).
 template <int N, typename F, int... Is>
@@ -132,18 +134,19 @@ template <> struct GemmTile<f16> {
   // rows of one transposing read (64 bytes each) tile the banks exactly
   static constexpr int BS = BNC + 32;
   static constexpr int CH = 8;
-  // acc[i][j]: 32x32 output block (i: m, j: n) of this wave's 64x64, held
-  // transposed (B^T A^T): lane l has m = l % 32 and four runs of four
+  // acc[i][j]: 32x32 output block (i: m, j: n) of this wave's (32 MB)x64,
+  // held transposed (B^T A^T): lane l has m = l % 32 and four runs of four
   // consecutive n, so the epilogue stores 4 elements at a time
+  template <int MB>
   __device__ static void step(const f16* As, const f16* Bs, int wm, int wn, int lane,
-                              float16v (&acc)[2][2]) {
+                              float16v (&acc)[MB][2]) {
     const int G = lane >> 4, t = lane & 15, c = t & 3, ir = t >> 2;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      half8v a[2], b[2];
+      half8v a[MB], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const half8v*>(As + (64 * wm + 32 * i + (lane & 31)) * AS +
+      for (int i = 0; i < MB; ++i)
+        a[i] = *reinterpret_cast<const half8v*>(As + (32 * MB * wm + 32 * i + (lane & 31)) * AS +
                                                 16 * ks + 8 * (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -153,7 +156,7 @@ template <> struct GemmTile<f16> {
         b[j] = half8v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
     }
@@ -165,32 +168,38 @@ template <> struct GemmTile<float> {
   static constexpr int AS = BK + 4;
   static constexpr int BS = BNC + 4;
   static constexpr int CH = 4;
+  template <int MB>
   __device__ static void step(const float* As, const float* Bs, int wm, int wn, int lane,
-                              float16v (&acc)[2][2]) {
+                              float16v (&acc)[MB][2]) {
     const int hi = lane >> 5, l32 = lane & 31;
 #pragma unroll 4
     for (int ks = 0; ks < BK / 2; ++ks) {
-      float a[2], b[2];
+      float a[MB], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = As[(64 * wm + 32 * i + l32) * AS + 2 * ks + hi];
+      for (int i = 0; i < MB; ++i) a[i] = As[(32 * MB * wm + 32 * i + l32) * AS + 2 * ks + hi];
 #pragma unroll
       for (int j = 0; j < 2; ++j) b[j] = Bs[(2 * ks + hi) * BS + 64 * wn + 32 * j + l32];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x2f32(b[j], a[i], acc[i][j]);
     }
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
+// MB: 32-row blocks of a wave's tile; the workgroup tile is (64 MB) x 128
+// (four waves, 2 x 2).  Taller wave tiles read less LDS per MFMA.
+template <typename T, int MB>
+__global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmParams p) {
   using G = GemmTile<T>;
   constexpr int AS = G::AS, BS = G::BS, CH = G::CH, BK = G::BK;
+  constexpr int BM = 64 * MB;
+  constexpr int CS = BNC + 8;  // output tile row stride (elements), epilogue
   constexpr int A_EL = BM * AS, B_EL = BK * BS;
   constexpr int A_CH = BM * BK / CH, B_CH = BK * BNC / CH;   // 16-byte chunks per tile
   constexpr int CPT = (A_CH + B_CH) / 256;
-  __shared__ __attribute__((aligned(16))) T lds[2 * (A_EL + B_EL)];
+  constexpr int LDS_EL = (2 * (A_EL + B_EL) > BM * CS) ? 2 * (A_EL + B_EL) : BM * CS;
+  __shared__ __attribute__((aligned(16))) T lds[LDS_EL];
   static_assert(sizeof(lds) / (sizeof(int32_t)) >= 3 * kGemmSchedMaxB + 1, "schedule fits the tile LDS");
 
   // workgroup 0 builds the attention schedule when asked (no separate launch)
@@ -254,9 +263,9 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
     }
   };
 
-  float16v acc[2][2];
+  float16v acc[MB][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = float16v{};
 
@@ -276,7 +285,7 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
       const int kt = k0 + s0;
       if (kt < nk) {
         const T* As = lds + (kt & 1) * (A_EL + B_EL);
-        G::step(As, As + A_EL, wm, wn, lane, acc);
+        G::template step<MB>(As, As + A_EL, wm, wn, lane, acc);
         if (kt + 1 < nk) store(std::integral_constant<int, (s0 + 1) % NS>{}, (kt + 1) & 1, (kt + 1) * BK);
         load(std::integral_constant<int, s0>{}, min((kt + NS) * BK, k_last));
         __syncthreads();
@@ -290,8 +299,6 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
   // the bias into a row-major tile, which is then stored in 16-byte chunks
   // (Ncol and the head size are multiples of 8, so a chunk stays in one head).
   // The last loop iteration ended with a barrier, so the stage buffers are free.
-  constexpr int CS = BNC + 8;  // tile row stride (elements)
-  static_assert(BM * CS <= 2 * (A_EL + B_EL), "the output tile fits the stage buffers");
   T* Cs = lds;
   const T* bias = static_cast<const T*>(p.bias);
 #pragma unroll
@@ -303,8 +310,8 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) bv[r] = (n0 + nl + r < p.Ncol) ? to_f32(bias[n0 + nl + r]) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ml = 64 * wm + 32 * i + (lane & 31);
+      for (int i = 0; i < MB; ++i) {
+        const int ml = 32 * MB * wm + 32 * i + (lane & 31);
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + bv[r];
@@ -336,11 +343,12 @@ hipError_t launch_packed_sched(const PackedSchedParams& p, hipStream_t s) {
 
 hipError_t launch_qkv_gemm(DType dt, const GemmParams& p, hipStream_t s) {
   if (p.M == 0 && !p.with_sched) return hipSuccess;
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.Ncol + BNC - 1) / BNC) + (p.with_sched ? 1 : 0);
+  const int bm = dt == DType::F16 ? 64 * kGemmMbF16 : 128;
+  const int tiles = ((p.M + bm - 1) / bm) * ((p.Ncol + BNC - 1) / BNC) + (p.with_sched ? 1 : 0);
   if (dt == DType::F16)
-    hipLaunchKernelGGL(qkv_gemm_kernel<f16>, dim3(tiles), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((qkv_gemm_kernel<f16, kGemmMbF16>), dim3(tiles), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(qkv_gemm_kernel<float>, dim3(tiles), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((qkv_gemm_kernel<float, 2>), dim3(tiles), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
