@@ -279,17 +279,18 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kv_kernel(PrepParams p) {
       } else {
         const int pj = (d0 < rh) ? j + rh / CH : j - rh / CH;  // partner lane in the group
         const int src = grp * lpr + ((d0 < 2 * rh) ? pj : j);
+        // the chunk's dims d0 .. d0 + CH - 1 take the consecutive table entries
+        // i0 .. i0 + CH - 1 (rh is a multiple of CH): one 16-byte load each
+        const bool rot_chunk = d0 < 2 * rh;
+        const int i0 = rot_chunk ? (d0 < rh ? d0 : d0 - rh) : 0;
+        float cv[CH], sv[CH];
+        load8_or_4(cs + (int64_t)prow * rh + i0, cv);
+        load8_or_4(sn + (int64_t)prow * rh + i0, sv);
 #pragma unroll
         for (int e = 0; e < CH; ++e) {
           const float z = __shfl(x[e], src, 64);
-          const int d = d0 + e;
           y[e] = x[e];
-          if (d < 2 * rh) {
-            const int i = d < rh ? d : d - rh;
-            const float c = to_f32(cs[(int64_t)prow * rh + i]);
-            const float si = to_f32(sn[(int64_t)prow * rh + i]);
-            y[e] = d < rh ? x[e] * c - z * si : x[e] * c + z * si;
-          }
+          if (rot_chunk) y[e] = d0 < rh ? x[e] * cv[e] - z * sv[e] : x[e] * cv[e] + z * sv[e];
         }
       }
 #pragma unroll
