@@ -12,7 +12,9 @@
  * ---------------------------------------
  * Tensors.  Every tensor argument is a kvattn_tensor: a DEVICE pointer to a
  * contiguous row-major buffer plus its element type and dims.  An optional
- * input that is absent has data == NULL (its other fields are ignored).  The
+ * input that is absent has data == NULL and rank 0.  A present tensor with
+ * no elements (a zero dim) may have data == NULL; calls over an empty batch
+ * or an empty new sequence launch nothing that touches it.  The
  * input slots of each operator follow the order of that page's Inputs table;
  * the output slots follow its Outputs table.  The caller passes the slot
  * count it filled (n_inputs / n_outputs) and the library checks it.

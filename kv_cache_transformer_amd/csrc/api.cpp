@@ -59,12 +59,16 @@ int ok() {
   return KVATTN_OK;
 }
 
-bool has(const kvattn_tensor& t) { return t.data != nullptr; }
-
 int64_t numel(const kvattn_tensor& t) {
   int64_t n = 1;
-  for (int i = 0; i < t.rank; ++i) n *= t.dims[i];
+  for (int i = 0; i < t.rank && i < 4; ++i) n *= t.dims[i];
   return n;
+}
+
+// A tensor is present when it has data, or dims with no element (an empty
+// tensor may come with a null pointer); absent slots are null with rank 0.
+bool has(const kvattn_tensor& t) {
+  return t.data != nullptr || (t.rank > 0 && t.rank <= 4 && numel(t) == 0);
 }
 
 std::string shape_str(const kvattn_tensor& t) {
@@ -1091,7 +1095,8 @@ int32_t gqa_attention(const gqa_attrs* a, const kvattn_tensor* in, int32_t n_in,
   GqaPlan P{};
   CHECK(gqa_validate(a, in, n_in, total, out, n_out, P));
   CHECK(check_ws(P.ws_total, ws, ws_bytes));
-  if (P.B == 0 || P.S == 0) return ok();
+  // no new token still copies the past rows into a separate present buffer
+  if (P.B == 0 || (P.S == 0 && !(P.has_past && !P.shared))) return ok();
   return gqa_run(a, in, out, P, ws, static_cast<hipStream_t>(stream));
 }
 

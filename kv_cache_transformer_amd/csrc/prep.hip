@@ -401,6 +401,7 @@ hipError_t launch_window_shift(DType dt, const WindowShiftParams& p, hipStream_t
 }
 
 hipError_t launch_copy_past(DType dt, const CopyPastParams& p, hipStream_t s) {
+  if (p.B == 0 || p.kvN == 0) return hipSuccess;
   int64_t per = (int64_t)p.past_seq * p.H;
   int gx = (int)std::min<int64_t>((per + 255) / 256, 1024);
   if (gx < 1) gx = 1;

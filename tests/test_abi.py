@@ -348,3 +348,21 @@ def test_gqa_window_cache_validation(lib):
     ins, outs = gqa_args(past="shared", S=16, cap=64)
     rc, _, _ = gqa_call(lib, ins, outs, total=500, sliding_window_cache=2, local_window_size=8)
     assert rc == -1
+
+
+def test_empty_tensors_are_present(lib):
+    """An empty tensor (a zero dim) may come with a null pointer: an empty
+    batch is a valid call that launches nothing; a null pointer with rank 0
+    stays an absent slot."""
+    ins, outs = gqa_args(B=0)
+    for t in ins[:3] + [ins[5]] + outs:
+        t.data = None
+    rc, size, msg = gqa_call(lib, ins, outs)
+    assert rc == 0 and size == 0, msg
+    ins, outs = gqa_args(past="shared", S=1, cap=64, B=0)
+    for t in ins[:6] + outs:
+        t.data = None
+    assert gqa_call(lib, ins, outs, total=20)[0] == 0
+    ins, outs = gqa_args()
+    ins[0] = kb.Tensor()                      # rank 0, null: absent, and query is required
+    assert gqa_call(lib, ins, outs)[0] == -1

@@ -198,3 +198,48 @@ def test_workload_gqa_decode_int8():
     ref = gqa_oracle(case, info=info)
     n = check_quant_gqa(case, got, ref, info)
     print(f"key codes on the other side of a near tie: {n}")
+
+
+def _empty_case(B, S, past=None, cap=64, N=8, kvN=2, H=64, dtype=F16):
+    """A call over an empty batch (B = 0) or with no new tokens (S = 0)."""
+    rng = np.random.default_rng(900 + B + S)
+    inputs = dict(query=wl.normal(rng, (B, S, N * H), dtype),
+                  key=wl.normal(rng, (B, S, kvN * H), dtype),
+                  value=wl.normal(rng, (B, S, kvN * H), dtype))
+    lens = np.full(B, 20, np.int64)
+    if past is None:
+        inputs.update(present_key=np.zeros((B, kvN, max(S, 1), H), dtype),
+                      present_value=np.zeros((B, kvN, max(S, 1), H), dtype))
+        inputs["seqlens_k"] = np.full(B, S - 1, np.int32)
+    else:
+        pk = wl.normal(rng, (B, kvN, cap, H), dtype)
+        pv = wl.normal(rng, (B, kvN, cap, H), dtype)
+        if past == "shared":
+            inputs.update(past_key=pk, past_value=pv, present_key=pk, present_value=pv)
+        else:
+            inputs.update(past_key=pk, past_value=pv,
+                          present_key=np.full((B, kvN, cap + S, H), np.nan, dtype),
+                          present_value=np.full((B, kvN, cap + S, H), np.nan, dtype))
+        inputs["seqlens_k"] = (lens + S - 1).astype(np.int32)
+    attrs = dict(num_heads=N, kv_num_heads=kvN, causal=1, do_rotary=0, local_window_size=-1,
+                 qk_norm_epsilon=1e-6, scale=0.0, smooth_softmax=-1, softcap=0.0)
+    return dict(op="gqa", inputs=inputs, attrs=attrs, total_sequence_length=21,
+                shared=past == "shared")
+
+
+@pytest.mark.parametrize("B,S,past", [(0, 16, None), (0, 1, "shared"), (2, 0, None),
+                                      (2, 0, "concat"), (2, 0, "shared")])
+def test_empty_batch_or_sequence(B, S, past):
+    """Degenerate calls: nothing to attend; the output is empty and the caches
+    hold what the definition says (past rows copied to a separate present)."""
+    case = _empty_case(B, S, past)
+    out, pk, pv = gqa_gpu(case)
+    ref, rpk, rpv = gqa_oracle(case)
+    assert out.shape == ref.shape == (B, S, 8 * 64)
+    if past == "concat":
+        live = np.zeros(pk.shape[:3], bool)
+        live[:, :, :20] = True                   # rows [0, past_b) are copied
+        assert np.array_equal(pk[live], rpk[live]) and np.array_equal(pv[live], rpv[live])
+    else:
+        check_cache(pk, rpk, None, "present_key")
+        check_cache(pv, rpv, None, "present_value")

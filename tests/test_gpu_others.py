@@ -163,6 +163,13 @@ def test_workload_sparse_prompt_sampled_rows():
     print(f"rotated key elements off by 1 ulp: {n1}")
 
 
+def test_sparse_empty_batch():
+    case = wl.sparse_case(np.random.default_rng(1), B=0, S=64, N=4, kvN=2, H=64, bs=16, dtype=F16)
+    out, pk, pv = sparse_gpu(case)
+    ref, rpk, rpv = sparse_oracle(case)
+    assert out.shape == ref.shape == (0, 64, 4 * 64) and pk.shape == rpk.shape
+
+
 def test_workload_sparse_generation():
     case = wl.sparse_generation()
     print("sparse_generation", flush=True)
