@@ -52,6 +52,9 @@ DECODE = [
     dict(dtype=F16, B=2, N=2, kvN=1, H=8, cap=8, past_lens=[7, 3]),
     dict(dtype=F16, B=4, N=16, kvN=4, H=128, cap=2100, past_lens=[2099, 1024, 128, 127],
          bias="h1", sink=True),
+    # more than 64 samples: the deal scans the lengths in several 64-lane passes
+    dict(dtype=F16, B=150, N=8, kvN=2, H=64, cap=96, rotary=True, past="shared"),
+    dict(dtype=F32, B=70, N=4, kvN=4, H=64, cap=40, window=7, past="concat"),
 ]
 
 
@@ -176,6 +179,7 @@ QUANT = [
     dict(B=4, S=1, N=16, kvN=4, H=128, cap=2100, past_lens=[2099, 1024, 128, 127], bias="h1",
          smooth_softmax=1, quant=Q8T),
     dict(B=2, S=1, N=2, kvN=1, H=8, cap=8, past_lens=[7, 3], quant=Q8C),
+    dict(B=90, S=1, N=8, kvN=2, H=128, cap=64, rotary=True, quant=Q8T, past="shared"),
 ]
 
 

@@ -97,6 +97,8 @@ SPARSE_GEN = [
     dict(dtype=F32, B=3, S=1, N=4, kvN=1, H=64, bs=16, cap=300, past_lens=[5, 299, 100],
          rotary=True, rot_dim=32, interleaved=1),
     dict(dtype=F16, B=1, S=1, N=16, kvN=4, H=256, bs=32, cap=2000, past_lens=[1234]),
+    dict(dtype=F16, B=80, S=1, N=4, kvN=2, H=64, bs=16, cap=128,
+         past_lens=list(range(3, 128, 2)) + [0] * 17, rotary=True),
 ]
 
 
