@@ -27,6 +27,7 @@
 //            sequence [cum[b], cum[b+1]); work items come from a device work
 //            list (PackedAttention page: Description and Inputs table).
 #include <type_traits>
+#include <utility>
 
 #include "device_common.hpp"
 #include "kvattn_internal.hpp"
@@ -635,7 +636,24 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     // softcap: c * log2(e) * tanh(y) = A - B / (2^u + 1) with u = 2 * log2(e) * y.
     // A plain tile keeps its raw scores: the cap is monotone, so the capped
     // maximum is the cap of the raw one, and the cap is applied in the exponent.
-    if (!plain) {
+    if (!plain && bias == nullptr) {
+      // score (blk, i) of this lane is key kb + c, c = 32 blk + 8 (i / 4) + i % 4
+      // a constant, so the masks reduce to a range [clo, chi] of c per lane
+      const int kb = r.start + 4 * (lane >> 5);
+      int clo = 0, chi = r.lim - 1 - kb;
+      if ((MODE == kDense && p.causal) || MODE == kCsr) chi = min(chi, pos - kb);
+      if (MODE == kDense && p.causal && p.window >= 0) clo = pos - p.window - kb;
+      if (!row_ok) chi = -1;
+#pragma unroll
+      for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 32 * blk + 8 * (i >> 2) + (i & 3);
+          float v = sacc[blk][i];
+          if (use_cap) v = kExactCap ? capA * tanh_from_u(v) : capA - capB * fast_rcp(fast_exp2(v) + 1.f);
+          sacc[blk][i] = (c >= clo && c <= chi) ? v : kNegInf;
+        }
+    } else if (!plain) {
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk)
 #pragma unroll
@@ -852,6 +870,61 @@ template <int HP> struct PipeLayout {
   __device__ static int swv(int r) { return 4 * swv_of_ir(r & 3); }
 };
 
+// Calls f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>).
+template <typename F, int... Is>
+__device__ __forceinline__ void pipe_static_for(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+
+// Transposing LDS read of 4 f16 (ds_read_b64_tr_b16) at byte address
+// addr + OFF, issued as a volatile statement with its wait made explicit
+// (lds_wait_tr): the compiler's own wait counting treats the transposing
+// builtin as an access of unknown memory and makes it wait for every
+// outstanding global-to-LDS copy, which would stall each PV phase behind the
+// copies of the next tiles.  LDS operations complete in issue order, so a wait
+// until at most n LDS operations are outstanding covers every read issued
+// before the last n (a scalar load in between only makes the wait longer).
+// Volatile statements keep their order, and the wait takes the read results as
+// operands, so nothing reads them before it.
+template <int OFF>
+__device__ __forceinline__ uint2v lds_tr16_asm(uint32_t addr) {
+  uint2v r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_tr(uint2v& a, uint2v& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
+// PV of a 64-key tile from V buffer VB of a swizzled V tile pair (vaddr[db]:
+// this lane's byte address of output block db in buffer 0; pb[2 * blk + half]:
+// its probabilities of 16 keys each).  The operand reads run D MFMAs ahead.
+template <int HP, int VB>
+__device__ __forceinline__ void pv_tile64_tr(float16v (&o)[HP / 32], const uint32_t (&vaddr)[HP / 32],
+                                             const half8v (&pb)[4]) {
+  constexpr int ND = HP / 32, NM = 4 * ND, D = 3;
+  constexpr int VOFF = VB * PipeLayout<HP>::VTILE * 2;
+  uint2v lo[NM], hi[NM];
+  auto issue = [&](auto kc) {
+    constexpr int k = decltype(kc)::value, q = k / ND, db = k % ND;
+    lo[k] = lds_tr16_asm<VOFF + 32 * q * HP>(vaddr[db]);
+    hi[k] = lds_tr16_asm<VOFF + 32 * q * HP + 16 * HP>(vaddr[db]);
+  };
+  pipe_static_for(issue, std::make_integer_sequence<int, D>{});
+  pipe_static_for(
+      [&](auto kc) {
+        constexpr int k = decltype(kc)::value, q = k / ND, db = k % ND;
+        // reads of the MFMAs after k that are already issued
+        constexpr int later = (NM - 1 - k) < (D - 1) ? (NM - 1 - k) : (D - 1);
+        lds_wait_tr<2 * later>(lo[k], hi[k]);
+        const uint4v u = {lo[k][0], lo[k][1], hi[k][0], hi[k][1]};
+        o[db] = mfma32x32x16(__builtin_bit_cast(half8v, u), pb[q], o[db]);
+        if constexpr (k + D < NM) issue(std::integral_constant<int, k + D>{});
+      },
+      std::make_integer_sequence<int, NM>{});
+}
+
 // both 32-key blocks of a 64-key tile from a swizzled V tile (pb[2 * blk + half]:
 // this lane's probabilities of 16 keys each); operand reads pinned ahead of the
 // MFMAs, VALU work of the caller may be scheduled between them
@@ -892,6 +965,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
   f16* const K1 = lds + L::KTILE;
   f16* const V0 = lds + 2 * L::KTILE;
   f16* const V1 = V0 + L::VTILE;
+  static_assert(2 * (L::VTILE + 3 * 16 * HP + 8 * HP) < 65536, "V read offsets fit the immediate");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -983,6 +1057,18 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
   };
 
 
+  // byte addresses of this lane's PV operand reads in V0, per output block:
+  // rows 4 (G >> 1) + ir (+ 16 q, + 8), columns 16 (G & 1) + 4 c of block db ^ swv
+  uint32_t vaddr[Mma::ND];
+  {
+    const int G = lane >> 4, t = lane & 15, c = t & 3, ir = t >> 2;
+    const int wsw = L::swv_of_ir(ir);
+    const uint32_t v0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) f16*)V0);
+#pragma unroll
+    for (int db = 0; db < Mma::ND; ++db)
+      vaddr[db] = v0 + 2u * (uint32_t)((4 * (G >> 1) + ir) * HP + 16 * (G & 1) + 4 * c + 32 * (db ^ wsw));
+  }
+
   // ---- queries of this wave ------------------------------------------------
   Mma mma;
   mma.init();
@@ -1016,6 +1102,25 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
   // ---- score helpers -------------------------------------------------------
   // Scores of a tile that is not plain: softcap, bias and masks in the exponent.
   auto mask_scores = [&](const TileRange& r, float16v (&sc)[2]) {
+    if (bias == nullptr) {
+      // Score (blk, i) of this lane is key kb + c, c = 32 blk + 8 (i / 4) + i % 4
+      // a constant, so the masks reduce to a range [clo, chi] of c per lane.
+      const int kb = r.start + 4 * (lane >> 5);
+      int clo = 0, chi = r.lim - 1 - kb;
+      if ((MODE == kDense && p.causal) || MODE == kCsr) chi = min(chi, pos - kb);
+      if (MODE == kDense && p.causal && p.window >= 0) clo = pos - p.window - kb;
+      if (!row_ok) chi = -1;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 32 * blk + 8 * (i >> 2) + (i & 3);
+          float v = sc[blk][i];
+          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
+          sc[blk][i] = (c >= clo && c <= chi) ? v : kNegInf;
+        }
+      return;
+    }
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -1125,11 +1230,11 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
     }
   };
   // PV of a tile with the row sum and the raw maximum of the next tile's scores
-  auto pv_sum_max = [&](const f16* Vt, const half8v (&pb)[4], const float16v (&scn)[2]) -> float {
+  auto pv_sum_max = [&](auto vb, const half8v (&pb)[4], const float16v (&scn)[2]) -> float {
     // the score MFMAs were issued on either side of a branch: their results
     // are read below
     mfma_result_fence();
-    pv_tile64_swz<HP>(mma.o, Vt, pb, lane);
+    pv_tile64_tr<HP, decltype(vb)::value>(mma.o, vaddr, pb);
     const half2v one2 = {(f16)1.f, (f16)1.f};
     float ps[4];
 #pragma unroll
@@ -1140,17 +1245,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
         ps[q] = __builtin_amdgcn_fdot2(half2v{pb[q][2 * j], pb[q][2 * j + 1]}, one2, ps[q], false);
     }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    const float t = raw_max(scn);
-    // six reads ahead, then one MFMA, two reads and two VALU instructions at a time
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 2);
-#pragma unroll
-    for (int i = 0; i < 4 * Mma::ND - 3; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 2);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 2);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 2);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 2);
-    return t;
+    return raw_max(scn);
   };
 
   // ---- prologue: tiles 0 (K, V) and 1 (K); scores and maximum of tile 0 ----
@@ -1173,13 +1268,13 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
   // ---- steady state: step t computes P(t), PV(t), and S(t + 1) ------------
   // sc: scores of tile t (transformed when not plain), scn receives S(t + 1);
   // Kc/Vc: buffers of K(t) / V(t); Kn/Vn: of K(t + 1) / V(t + 1)
-  auto step = [&](int t, float16v (&sc)[2], float16v (&scn)[2], f16* Kc, f16* Kn, f16* Vc, f16* Vn) {
+  auto step = [&](auto vb, int t, float16v (&sc)[2], float16v (&scn)[2], f16* Kc, f16* Kn, f16* Vn) {
     const bool plain_t = plain_n;
     // K(t) and V(t - 1) are no longer read by any wave (barrier of step t - 1)
     if (t + 2 < n_tiles) load_k(t + 2, Kc);
     if (t + 1 < n_tiles) load_v(t + 1, Vn);
     probs_qk(plain_t, sc, pb, Kn, scn);
-    float tmax = pv_sum_max(Vc, pb, scn);
+    float tmax = pv_sum_max(vb, pb, scn);
     const bool more = t + 1 < n_tiles;
     if (more) {
       rn = w.tile(p, t + 1);
@@ -1196,8 +1291,8 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
     if (more) update_max(tmax);
   };
   for (int t = 0; t < n_tiles; t += 2) {
-    step(t, sA, sB, K0, K1, V0, V1);
-    if (t + 1 < n_tiles) step(t + 1, sB, sA, K1, K0, V1, V0);
+    step(std::integral_constant<int, 0>{}, t, sA, sB, K0, K1, V1);
+    if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1, sB, sA, K1, K0, V0);
   }
 
   // ---- normalise and store -------------------------------------------------
