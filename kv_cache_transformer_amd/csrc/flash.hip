@@ -897,6 +897,17 @@ __device__ __forceinline__ void lds_wait_tr(uint2v& a, uint2v& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
 }
 
+// Global-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4) from
+// byte address base + off (base uniform, in SGPRs; off per lane): lane l's
+// bytes land at LDS byte address lds + 16 l.  Issued as a volatile statement:
+// with a copy into LDS outstanding, the compiler's wait counting would wait
+// for all LDS reads at once instead of by count.  The copies are waited for
+// explicitly (vmcnt(0) before the barrier that publishes each tile).
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
 // PV of a 64-key tile from V buffer VB of a swizzled V tile pair (vaddr[db]:
 // this lane's byte address of output block db in buffer 0; pb[2 * blk + half]:
 // its probabilities of 16 keys each).  The operand reads run D MFMAs ahead.
@@ -970,6 +981,9 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H;
+  auto lds_byte = [](const f16* q) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const f16*)q);
+  };
   FlashWork<MODE, BN> w;
   if (!w.init(p, wave)) return;
   const int b = w.b, h = w.h, nrows = w.nrows, past = w.past;
@@ -1029,9 +1043,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
           k_slot(u, rr, col);
           off = min(rr, last) * kj + col;
         }
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(src + off),
-            (__attribute__((address_space(3))) void*)(dst + 512 * (wave + NW * u)), 16, 0, 0);
+        lds_dma16(src, 2u * (uint32_t)off, lds_byte(dst + 512 * (wave + NW * u)));
       }
     }
   };
@@ -1049,9 +1061,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
           v_slot(u, rr, col);
           off = min(rr, last) * kj + col;
         }
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(src + off),
-            (__attribute__((address_space(3))) void*)(dst + 512 * (wave + NW * u)), 16, 0, 0);
+        lds_dma16(src, 2u * (uint32_t)off, lds_byte(dst + 512 * (wave + NW * u)));
       }
     }
   };
@@ -1063,7 +1073,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
   {
     const int G = lane >> 4, t = lane & 15, c = t & 3, ir = t >> 2;
     const int wsw = L::swv_of_ir(ir);
-    const uint32_t v0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) f16*)V0);
+    const uint32_t v0 = lds_byte(V0);
 #pragma unroll
     for (int db = 0; db < Mma::ND; ++db)
       vaddr[db] = v0 + 2u * (uint32_t)((4 * (G >> 1) + ir) * HP + 16 * (G & 1) + 4 * c + 32 * (db ^ wsw));
