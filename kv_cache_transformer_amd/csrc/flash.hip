@@ -936,31 +936,6 @@ __device__ __forceinline__ void pv_tile64_tr(float16v (&o)[HP / 32], const uint3
       std::make_integer_sequence<int, NM>{});
 }
 
-// both 32-key blocks of a 64-key tile from a swizzled V tile (pb[2 * blk + half]:
-// this lane's probabilities of 16 keys each); operand reads pinned ahead of the
-// MFMAs, VALU work of the caller may be scheduled between them
-template <int HP>
-__device__ __forceinline__ void pv_tile64_swz(float16v (&o)[HP / 32], const f16* Vt, const half8v (&pb)[4],
-                                              int lane) {
-  using L = PipeLayout<HP>;
-  constexpr int ND = HP / 32;
-  const int G = lane >> 4, t = lane & 15;
-  const int c = t & 3, ir = t >> 2;
-  const int wsw = L::swv_of_ir(ir);
-  const f16* base = Vt + (4 * (G >> 1) + ir) * HP + 16 * (G & 1) + 4 * c;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const f16* a1 = base + 16 * q * HP + 32 * (db ^ wsw);
-      half4v lo = lds_read_tr16(a1);
-      half4v hi = lds_read_tr16(a1 + 8 * HP);
-      half8v a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[db] = mfma32x32x16(a, pb[q], o[db]);
-    }
-  }
-}
-
 template <int HP, int MODE, int NW, bool SOFTCAP>
 __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
   using T = f16;
