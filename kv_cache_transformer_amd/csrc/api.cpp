@@ -278,10 +278,10 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     return fail(KVATTN_ERR_INVALID_ARG, "present_key and present_value must both share the past buffers or neither");
   if (P.shared && ck.dims[2] != pk.dims[2])
     return fail(KVATTN_ERR_INVALID_ARG, "a shared present buffer must have the past buffer's dims");
-  if (P.bits == 4 && P.has_past)
-    return fail(KVATTN_ERR_UNSUPPORTED, "int4 caches are prompt-only (no past_key)");
-  if (P.bits == 8 && P.has_past && P.S != 1)
-    return fail(KVATTN_ERR_UNSUPPORTED, "int8 caches with a past take one new token (decode)");
+  if (P.bits != 0 && P.has_past && P.S != 1)
+    return fail(KVATTN_ERR_UNSUPPORTED, "int%d caches with a past take one new token (decode)", P.bits);
+  if (P.bits == 4 && P.has_past && P.H % (P.HP / 8) != 0)
+    return fail(KVATTN_ERR_UNSUPPORTED, "int4 decode: head size %d must be a multiple of %d", P.H, P.HP / 8);
   if (P.bits != 0 && P.window_cache)
     return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache with a quantised cache is not implemented");
   if (P.window_cache) {
@@ -358,8 +358,9 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     c.ck = ck.data;
     c.cv = cv.data;
     c.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
-    c.B = P.B; c.kvN = P.kvN; c.H = P.H; c.S = P.S; c.past_seq = P.past_seq; c.cap = P.cap;
-    CHECK(hip_status(launch_copy_past(P.bits == 8 ? DType::Q8 : dt, c, st), "copy_past launch"));
+    // quantised caches copy bytes: H codes (int8) or H / 2 bytes (int4) per row
+    c.B = P.B; c.kvN = P.kvN; c.H = P.bits == 4 ? P.H / 2 : P.H; c.S = P.S; c.past_seq = P.past_seq; c.cap = P.cap;
+    CHECK(hip_status(launch_copy_past(P.bits != 0 ? DType::Q8 : dt, c, st), "copy_past launch"));
   }
 
   if (P.window_cache) {
@@ -410,7 +411,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     d.v_scale = static_cast<const float*>(in[GQA_IN_V_SCALE].data);
     d.k_scale_pc = P.k_pc;
     d.v_scale_pc = P.v_pc;
-    const DType ddt = P.bits == 8 ? DType::Q8 : dt;
+    const DType ddt = P.bits == 8 ? DType::Q8 : (P.bits == 4 ? DType::Q4 : dt);
     CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st, [&] { return launch_decode(ddt, P.HP, d, st); }),
                      "decode launch"));
     CHECK(hip_status(launch_decode_combine(dt, P.HP, d, st), "decode combine launch"));

@@ -77,13 +77,16 @@ constexpr float kDecodeSlack = 3.f;
 // directly (no combine).
 constexpr int kDirectKeys = 64;
 
-// Cache type tag: float32 activations (query, new rows, output) over an int8
-// key/value cache.
+// Cache type tags: float32 activations (query, new rows, output) over an int8
+// key/value cache, or over an int4 one (two codes per byte).
 struct QuantI8 {};
+struct QuantI4 {};
 template <typename T> struct ActOf { using type = T; };
 template <> struct ActOf<QuantI8> { using type = float; };
+template <> struct ActOf<QuantI4> { using type = float; };
 template <typename T> struct CacheOf { using type = T; };
 template <> struct CacheOf<QuantI8> { using type = int8_t; };
+template <> struct CacheOf<QuantI4> { using type = uint8_t; };
 
 // Register ring depth (16-row sub-tiles held per wave): R - 1 are in flight
 // while one is computed, sized to stay within 256 registers without spilling.
@@ -94,6 +97,9 @@ template <> struct Ring<float, 64> { static constexpr int value = 3; };
 template <> struct Ring<QuantI8, 64> { static constexpr int value = 4; };
 template <> struct Ring<QuantI8, 128> { static constexpr int value = 4; };
 template <> struct Ring<QuantI8, 256> { static constexpr int value = 1; };
+template <> struct Ring<QuantI4, 64> { static constexpr int value = 4; };
+template <> struct Ring<QuantI4, 128> { static constexpr int value = 4; };
+template <> struct Ring<QuantI4, 256> { static constexpr int value = 1; };
 
 // Four consecutive elements of a head row ("quad"): the unit of the query
 // set-up, the append and the output stores.
@@ -293,6 +299,35 @@ __device__ __forceinline__ uint32_t quant8(float x, float s) {
   return (uint32_t)(int)c & 0xFFu;
 }
 
+// ------------------------------ int4 ----------------------------------------
+// Eight int4 codes of one 32-bit word (byte i: dim 2i in the low nibble, dim
+// 2i + 1 in the high one, each stored as code + 8) as f16: each nibble
+// becomes the low mantissa bits of 1024.0 (0x6400 | u = 1024 + u, exact) and
+// 1032 is subtracted (exact).
+__device__ __forceinline__ half8v nibbles_to_half8(uint32_t w) {
+  const uint32_t ev = w & 0x0F0F0F0Fu;         // byte k: dim 2k
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // byte k: dim 2k + 1
+  half8v out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // v_perm_b32 (selector bytes 0-3 take bytes of the second operand, 4-7 of
+    // the first, 0x0c gives zero): (ev.bk, 0, od.bk, 0)
+    const uint32_t sel = 0x0C000C00u | (uint32_t)k | ((uint32_t)(4 + k) << 16);
+    const uint32_t u = __builtin_amdgcn_perm(od, ev, sel) | 0x64006400u;
+    const half2v v = __builtin_bit_cast(half2v, u) - half2v{(f16)1032.f, (f16)1032.f};
+    out[2 * k] = v[0];
+    out[2 * k + 1] = v[1];
+  }
+  return out;
+}
+
+// Stored nibble of x for scale s at 4 bits: the float32 quotient rounded half
+// to even, clamped to [-8, 7], plus 8.
+__device__ __forceinline__ uint32_t quant4(float x, float s) {
+  const float c = fminf(fmaxf(rintf(x / s), -8.f), 7.f);
+  return (uint32_t)((int)c + 8);
+}
+
 // Lane layout as the f16 tile (lane l: key row l % 16, quarter g4 = l / 16),
 // the codes packed in the ring and widened when used.  For HP >= 128 a lane
 // loads 16 codes at a time, dims 64 i + 16 g4 .. + 15 (two k-steps: load i
@@ -411,6 +446,109 @@ template <int HP, int R> struct DecTile<QuantI8, HP, R> {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const half8v v = codes_to_half8(step_codes(vr[BUF], s));
+      const float4v tl = mfma16x16x16(half4v{v[0], v[1], v[2], v[3]}, ident, zero);
+      const float4v th = mfma16x16x16(half4v{v[4], v[5], v[6], v[7]}, ident, zero);
+      const half4v al = {(f16)tl[0], (f16)tl[1], (f16)tl[2], (f16)tl[3]};
+      const half4v ah = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
+      o[2 * s] = mfma16x16x16(al, ph, o[2 * s]);
+      o[2 * s] = mfma16x16x16(al, pl, o[2 * s]);
+      o[2 * s + 1] = mfma16x16x16(ah, ph, o[2 * s + 1]);
+      o[2 * s + 1] = mfma16x16x16(ah, pl, o[2 * s + 1]);
+    }
+  }
+};
+
+// int4: the int8 tile's arithmetic on nibble codes.  A lane loads two runs of
+// HP/8 codes per row, dims (HP/2) i + (HP/8) g4 .. + HP/8 - 1 for i = 0, 1
+// (HP/16 bytes each), so that the rotary partners d and d + HP/2 are quads qi
+// and qi + NQ/2 of one lane; 32-bit word w of run i holds the eight codes of
+// k-step i (NS/2) + w.  A run lies inside the head or wholly past it (the head
+// size is a multiple of HP/8); runs past it re-read the row's first bytes
+// (the query is zero there and those outputs are not stored).
+template <int HP, int R> struct DecTile<QuantI4, HP, R> {
+  static constexpr int NS = HP / 32;  // 32-dim k-steps of the score MFMA
+  static constexpr int NQ = HP / 16;  // quads per lane
+  static constexpr int WPR = NS / 2;  // 32-bit words per run
+  using Raw = typename std::conditional<WPR == 1, uint32_t,
+                                        typename std::conditional<WPR == 2, uint2v, uint4v>::type>::type;
+  static constexpr float kPScale = 4096.f;  // probabilities are split at 2^12 scale
+  half8v qh[NS], ql[NS];
+  float4v o[NQ];
+  Raw kr[R][2];
+  Raw vr[R][2];
+
+  __device__ int quad_dim(int qi, int g4) const {
+    const int s = qi >> 1;
+    return (HP / 2) * (s / WPR) + (HP / 8) * g4 + 8 * (s % WPR) + 4 * (qi & 1);
+  }
+  __device__ void set_layout(int, int) {}
+  __device__ void init() {
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) o[e] = float4v{0.f, 0.f, 0.f, 0.f};
+  }
+  // as the int8 tile: hi = f16(x), lo = f16(x - hi)
+  __device__ void set_q(const float (&x)[NQ][4]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = x[2 * s + (i >> 2)][i & 3];
+        const f16 h = (f16)v;
+        qh[s][i] = h;
+        ql[s][i] = (f16)(v - (float)h);
+      }
+  }
+  // Rows j0 + l % 16 (clamped to the last row of the run), H / 2 bytes each.
+  template <int BUF>
+  __device__ void load_kv(const uint8_t* kb, const uint8_t* vb, int j0, int last, int H, int lane) {
+    const int g4 = lane >> 4;
+    const int row = min(j0 + (lane & 15), last);
+    const uint8_t* krow = kb + (int64_t)row * (H / 2);
+    const uint8_t* vrow = vb + (int64_t)row * (H / 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d = (HP / 2) * i + (HP / 8) * g4;
+      const int off = d < H ? d / 2 : 0;
+      kr[BUF][i] = *reinterpret_cast<const Raw*>(krow + off);
+      vr[BUF][i] = *reinterpret_cast<const Raw*>(vrow + off);
+    }
+  }
+  // the 8 codes of k-step s
+  __device__ static uint32_t step_word(const Raw (&r)[2], int s) {
+    if constexpr (WPR == 1) {
+      return r[s];
+    } else {
+      return r[s / WPR][s % WPR];
+    }
+  }
+  template <int BUF>
+  __device__ float4v scores() const {
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const half8v k = nibbles_to_half8(step_word(kr[BUF], s));
+      acc = mfma16x16x32(k, qh[s], acc);
+      acc = mfma16x16x32(k, ql[s], acc);
+    }
+    return acc;
+  }
+  __device__ void scale_o(float a) {
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) o[e] *= a;
+  }
+  template <int BUF>
+  __device__ void pv(const float4v& p, half4v ident) {
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    half4v ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = p[i] * kPScale;
+      ph[i] = (f16)v;
+      pl[i] = (f16)(v - (float)ph[i]);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const half8v v = nibbles_to_half8(step_word(vr[BUF], s));
       const float4v tl = mfma16x16x16(half4v{v[0], v[1], v[2], v[3]}, ident, zero);
       const float4v th = mfma16x16x16(half4v{v[4], v[5], v[6], v[7]}, ident, zero);
       const half4v al = {(f16)tl[0], (f16)tl[1], (f16)tl[2], (f16)tl[3]};
@@ -597,7 +735,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   using Tile = DecTile<T, HP, R>;
   using AT = typename ActOf<T>::type;    // query, new rows, rotary, bias, sink, output
   using CT = typename CacheOf<T>::type;  // cache elements
-  constexpr bool kQuant = std::is_same<T, QuantI8>::value;
+  constexpr bool kQ4 = std::is_same<T, QuantI4>::value;
+  constexpr bool kQuant = std::is_same<T, QuantI8>::value || kQ4;
   using Q4 = Quad<AT>;
   using QT = typename Q4::type;
   constexpr int NQ = HP / 16, NH = NQ / 2;
@@ -695,8 +834,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
   const int kv_div = csr ? max(p.kv_div, 1) : 1;
   const int64_t slab = (int64_t)b * (p.kvN / kv_div) + kvh / kv_div;
-  CT* kb = static_cast<CT*>(p.kc) + slab * p.cap * H;
-  CT* vb = static_cast<CT*>(p.vc) + slab * p.cap * H;
+  const int rowel = kQ4 ? H / 2 : H;  // cache elements per row
+  CT* kb = static_cast<CT*>(p.kc) + slab * p.cap * rowel;
+  CT* vb = static_cast<CT*>(p.vc) + slab * p.cap * rowel;
   // CSR: the cache block of each block of the run (both waves of the pair
   // fill the table; every wave of the group passes the barrier)
   if constexpr (csr) {
@@ -861,7 +1001,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
       }
     }
     if (alane) {
-      if constexpr (kQuant) {
+      if constexpr (kQ4) {
+        // dims 4l .. 4l + 3 are bytes 2l, 2l + 1 (even dim in the low nibble)
+        uint32_t kw = 0, vw = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kw |= quant4(y[e], aks[e]) << (4 * e);
+          vw |= quant4(av[e], avs[e]) << (4 * e);
+        }
+        *reinterpret_cast<uint16_t*>(kb + (int64_t)newrow * rowel + 2 * lane) = (uint16_t)kw;
+        *reinterpret_cast<uint16_t*>(vb + (int64_t)newrow * rowel + 2 * lane) = (uint16_t)vw;
+      } else if constexpr (kQuant) {
         uint32_t kw = 0, vw = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1208,7 +1358,7 @@ hipError_t launch_decode_f(const DecodeParams& p, hipStream_t s) {
 
 template <typename T, int HP>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  if constexpr (!std::is_same<T, QuantI8>::value) {
+  if constexpr (!std::is_same<T, QuantI8>::value && !std::is_same<T, QuantI4>::value) {
     // CSR block keys come without bias, mask, qk or softcap
     if (p.csr_rp != nullptr) return launch_decode_f<T, HP, kCsrKeys>(p, s);
   }
@@ -1244,6 +1394,11 @@ hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s)
     if (hp == 64) return launch_decode_t<QuantI8, 64>(p, s);
     if (hp == 128) return launch_decode_t<QuantI8, 128>(p, s);
     return launch_decode_t<QuantI8, 256>(p, s);
+  }
+  if (dt == DType::Q4) {
+    if (hp == 64) return launch_decode_t<QuantI4, 64>(p, s);
+    if (hp == 128) return launch_decode_t<QuantI4, 128>(p, s);
+    return launch_decode_t<QuantI4, 256>(p, s);
   }
   if (hp == 64) return launch_decode_t<float, 64>(p, s);
   if (hp == 128) return launch_decode_t<float, 128>(p, s);

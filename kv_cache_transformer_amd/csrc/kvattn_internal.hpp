@@ -10,7 +10,7 @@ namespace kvattn {
 
 // Q8: float32 activations over an int8 key/value cache (decode, and the
 // byte copies of such a cache)
-enum class DType : int { F32 = 1, F16 = 2, Q8 = 3 };
+enum class DType : int { F32 = 1, F16 = 2, Q8 = 3, Q4 = 4 };
 
 // ---------------------------------------------------------------------------
 // K1 prep: per new token, optional per-head RMSNorm and rotary on the query

@@ -194,8 +194,13 @@ def test_gqa_quant_validation(lib):
     assert code(lambda i, o, a: o.__setitem__(1, T(F32, 2, 2, 64, 64))) == -1   # float cache
     assert code(lambda i, o, a: o.__setitem__(1, T(U8, 2, 2, 64, 64, ptr=0x40000)), bits=4) == -1  # H/2 bytes
     assert code(lambda i, o, a: o.__setitem__(1, T(I8, 2, 2, 64, 64, ptr=0x40000)), bits=4) == -1  # uint8
-    assert code(lambda i, o, a: None, bits=4, past="shared", S=1) == -2         # int4 is prompt-only
-    assert code(lambda i, o, a: None, past="shared", S=4) == -2                 # int8 past: decode only
+    assert code(lambda i, o, a: None, bits=4, past="shared", S=1) == 0          # int4 decode
+    assert code(lambda i, o, a: None, bits=4, past="separate", S=1) == 0
+    assert code(lambda i, o, a: None, bits=4, past="shared", S=1, H=80) == 0    # 80 = 5 * 128 / 8
+    assert code(lambda i, o, a: None, bits=4, past="shared", S=1, H=72) == -2   # not a multiple of 16
+    assert code(lambda i, o, a: None, bits=4, past="shared", S=1, H=176) == -2  # not a multiple of 32
+    assert code(lambda i, o, a: None, bits=4, past="shared", S=4) == -2         # quantised past: decode only
+    assert code(lambda i, o, a: None, past="shared", S=4) == -2
     assert code(lambda i, o, a: a.update(sliding_window_cache=1, local_window_size=8),
                 past="shared", S=1) == -2
 

@@ -157,9 +157,11 @@ def test_workload_window_decode():
 
 # Quantised caches (GroupQueryAttention page, Attributes table: k_quant_type,
 # v_quant_type, kv_cache_bit_width; Inputs table: k_scale, v_scale): float32
-# activations, int8 for prompts and decode, packed int4 for prompts.
+# activations, int8 and packed int4 caches for prompts and decode.
 Q8T = dict(bits=8, k="tensor", v="tensor")
 Q8C = dict(bits=8, k="channel", v="channel")
+Q4T = dict(bits=4, k="tensor", v="tensor")
+Q4C = dict(bits=4, k="channel", v="channel")
 QUANT = [
     dict(B=2, S=150, N=8, kvN=2, H=64, quant=Q8T),
     dict(B=2, S=130, N=8, kvN=2, H=128, window=37, softcap=30.0, sink=True, bias="full",
@@ -180,6 +182,18 @@ QUANT = [
          smooth_softmax=1, quant=Q8T),
     dict(B=2, S=1, N=2, kvN=1, H=8, cap=8, past_lens=[7, 3], quant=Q8C),
     dict(B=90, S=1, N=8, kvN=2, H=128, cap=64, rotary=True, quant=Q8T, past="shared"),
+    # int4 decode: two codes per byte, runs of Hp / 8 dims per lane
+    dict(B=3, S=1, N=32, kvN=8, H=128, cap=600, past_lens=[1, 300, 599], rotary=True, quant=Q4C),
+    dict(B=2, S=1, N=8, kvN=2, H=64, past="concat", cap=200, past_lens=[0, 150],
+         quant=dict(bits=4, k="tensor", v="channel")),
+    dict(B=2, S=1, N=4, kvN=4, H=256, cap=1100, past_lens=[1099, 513], softcap=20.0, sink=True,
+         window=100, quant=dict(bits=4, k="channel", v="tensor")),
+    dict(B=1, S=1, N=8, kvN=2, H=80, cap=300, past_lens=[299], norm=True, rotary=True, quant=Q4C),
+    dict(B=1, S=1, N=4, kvN=2, H=192, cap=100, past_lens=[99], rotary=True, quant=Q4T),
+    dict(B=4, S=1, N=16, kvN=4, H=128, cap=2100, past_lens=[2099, 1024, 128, 127], bias="h1",
+         smooth_softmax=1, quant=Q4T),
+    dict(B=2, S=1, N=2, kvN=1, H=8, cap=8, past_lens=[7, 3], quant=Q4C),
+    dict(B=70, S=1, N=8, kvN=2, H=128, cap=64, rotary=True, quant=Q4T, past="shared"),
 ]
 
 
