@@ -10,8 +10,9 @@ second (K and V rows 0..past_b of every sample and kv head).  The decode call
 rotates over several independently generated caches so that every call
 streams from HBM rather than from the 256 MB last-level cache.
 
-The other workloads (long prefill, small fp32 prompt, block-sparse prompt,
-packed varlen) are timed in the same run and reported under "workloads",
+The other workloads (long prefill, small fp32 prompt, block-sparse prompt
+and token generation, packed varlen, sliding-window decode, int8 and packed
+int4 cache decode) are timed in the same run and reported under "workloads",
 each with its own roofline object.  Kernel durations come from HIP events
 that the library records around the kernel of interest
 (kvattn_profile_events); call durations from torch events on the same
@@ -159,10 +160,10 @@ def decode_workload(torch, kv, wl, args, timer):
                 kv_bytes=kv_bytes)
 
 
-def decode_int8_workload(torch, kv, wl, args, timer):
-    """The decode over an int8 cache (float32 Q/K/V, per-channel scales):
-    rotations of random int8 caches as for the float16 decode."""
-    case = wl.gqa_decode_int8()
+def decode_quant_workload(torch, kv, wl, args, timer, bits=8):
+    """The decode over an int8 or packed int4 cache (float32 Q/K/V,
+    per-channel scales): rotations of random caches as for the float16 decode."""
+    case = wl.gqa_decode_int8() if bits == 8 else wl.gqa_decode_int4()
     i = case["inputs"]
     dev = "cuda:0"
     t = {k: torch.from_numpy(v).to(dev) for k, v in i.items() if k not in ("present_key", "present_value")}
@@ -170,8 +171,9 @@ def decode_int8_workload(torch, kv, wl, args, timer):
     g = torch.Generator(device=dev)
     g.manual_seed(54321)
     for _ in range(args.rotations - 1):
-        sets.append(tuple(torch.randint(-128, 128, t["past_key"].shape, generator=g, device=dev,
-                                        dtype=torch.int8) for _ in range(2)))
+        lo, hi, cdt = (-128, 128, torch.int8) if bits == 8 else (0, 256, torch.uint8)
+        sets.append(tuple(torch.randint(lo, hi, t["past_key"].shape, generator=g, device=dev,
+                                        dtype=cdt) for _ in range(2)))
     a = case["attrs"]
     out = torch.empty_like(t["query"])
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
@@ -182,13 +184,13 @@ def decode_int8_workload(torch, kv, wl, args, timer):
                          case["total_sequence_length"], t["cos_cache"], t["sin_cache"],
                          k_scale=t["k_scale"], v_scale=t["v_scale"],
                          num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"], do_rotary=1,
-                         k_quant_type=2, v_quant_type=2, kv_cache_bit_width=8,
+                         k_quant_type=2, v_quant_type=2, kv_cache_bit_width=bits,
                          output=out, present_key=pk, present_value=pv, workspace=ws)
 
     call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
     lens = i["seqlens_k"].astype(np.int64) + 1
     kvN, H = 8, 128
-    kv_bytes = int(lens.sum()) * kvN * H * 2     # K and V codes, one byte each
+    kv_bytes = int(lens.sum()) * kvN * H * 2 * bits // 8   # K and V codes
     return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, kv_bytes=kv_bytes)
 
 
@@ -416,6 +418,8 @@ TRAFFIC_KERNELS = [
      "gqa_window_decode"),
     ("decode_gqa_decode_int8", r"decode_kernel(?:INS0_7QuantI8ELi128E|<[^<>]*QuantI8, 128,)",
      "kv_cache_transformer_amd/csrc/decode.hip", "gqa_decode_int8"),
+    ("decode_gqa_decode_int4", r"decode_kernel(?:INS0_7QuantI4ELi128E|<[^<>]*QuantI4, 128,)",
+     "kv_cache_transformer_amd/csrc/decode.hip", "gqa_decode_int4"),
 ]
 
 
@@ -535,9 +539,9 @@ def summarise_counters(d, cmd):
             dm = re.search(r"<float(?:, (\d+), (\d+), (\d+))?", r["Kernel_Name"])
             if not t and dm:  # names of float instances come demangled
                 t, hd, md = "f32", dm.group(1), dm.group(3)
-            qm = re.search(r"QuantI8(?:E|, )(?:Li)?(\d+)", r["Kernel_Name"])
-            if qm:  # int8-cache decode
-                t, hd, md = "q8", qm.group(1), None
+            qm = re.search(r"QuantI([48])(?:E|, )(?:Li)?(\d+)", r["Kernel_Name"])
+            if qm:  # quantised-cache decode
+                t, hd, md = "q" + qm.group(1), qm.group(2), None
             mode = {"0": "dense", "1": "csr", "2": "varlen"}.get(md, "")
             if m.group(1) == "decode_kernel" and m.group(4) is not None and not qm:
                 mode = "feat" + m.group(4)  # decode_kernel<type, head, features>
@@ -643,10 +647,11 @@ def main():
     if want("gqa_window_decode"):
         res["gqa_window_decode"] = window_decode_workload(torch, kv, wl, args, Timer(torch, lib, 5, hip))
         print("# gqa_window_decode done", file=sys.stderr, flush=True)
-    if want("gqa_decode_int8"):
-        res["gqa_decode_int8"] = decode_int8_workload(torch, kv, wl, args, Timer(torch, lib, 1, hip))
-        print(f"# gqa_decode_int8 done: {res['gqa_decode_int8']['call_ms']*1e3:.1f} us/call",
-              file=sys.stderr, flush=True)
+    for bits in (8, 4):
+        name = f"gqa_decode_int{bits}"
+        if want(name):
+            res[name] = decode_quant_workload(torch, kv, wl, args, Timer(torch, lib, 1, hip), bits)
+            print(f"# {name} done: {res[name]['call_ms']*1e3:.1f} us/call", file=sys.stderr, flush=True)
     if want("packed_varlen"):
         res["packed_varlen"] = packed_workload(torch, kv, wl, args, Timer(torch, lib, 4, hip))
         print("# packed_varlen done", file=sys.stderr, flush=True)
@@ -718,18 +723,21 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
                          "kernel_us": round(r["kern_ms"] * 1e3, 3), "algorithmic_bytes": r["kv_bytes"],
                          "traffic": None}}
-    if "gqa_decode_int8" in res:
-        r = res["gqa_decode_int8"]
+    for bits, cname in ((8, "int8"), (4, "packed int4")):
+        name = f"gqa_decode_int{bits}"
+        if name not in res:
+            continue
+        r = res[name]
         gbs_k = r["kv_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
-        workloads["gqa_decode_int8"] = {
-            "config": "B16 N32 kvN8 H128 fp32 Q/K/V, shared int8 cache 4096, per-channel scales, "
+        workloads[name] = {
+            "config": f"B16 N32 kvN8 H128 fp32 Q/K/V, shared {cname} cache 4096, per-channel scales, "
                       "past lengths U[1024,4095], rotary",
             "call_us": round(r["call_ms"] * 1e3, 2),
             "call_GBs": round(r["kv_bytes"] / (r["call_ms"] * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs_k, 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
                          "kernel_us": round(r["kern_ms"] * 1e3, 3), "algorithmic_bytes": r["kv_bytes"],
-                         "traffic": traffic_for("decode_gqa_decode_int8")}}
+                         "traffic": traffic_for(f"decode_{name}")}}
 
     line = {"metric": "GQA prefill TFLOP/s and decode KV GB/s on 1 MI355X, % of roofline",
             "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

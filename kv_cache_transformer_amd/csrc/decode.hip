@@ -301,22 +301,28 @@ __device__ __forceinline__ uint32_t quant8(float x, float s) {
 
 // ------------------------------ int4 ----------------------------------------
 // Eight int4 codes of one 32-bit word (byte i: dim 2i in the low nibble, dim
-// 2i + 1 in the high one, each stored as code + 8) as f16: each nibble
-// becomes the low mantissa bits of 1024.0 (0x6400 | u = 1024 + u, exact) and
-// 1032 is subtracted (exact).
+// 2i + 1 in the high one, each stored as code + 8) as f16: the nibbles are
+// spread to one byte each in dim order, each byte becomes the low mantissa
+// bits of 1024.0 (0x6400 | u = 1024 + u, exact) and 1032 is subtracted
+// (exact).  v_perm_b32: selector bytes 0-3 take bytes of the second operand,
+// 4-7 of the first.
 __device__ __forceinline__ half8v nibbles_to_half8(uint32_t w) {
-  const uint32_t ev = w & 0x0F0F0F0Fu;         // byte k: dim 2k
-  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // byte k: dim 2k + 1
+  const uint32_t ev = w & 0x0F0F0F0Fu;                              // byte k: dim 2k
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;                       // byte k: dim 2k + 1
+  const uint32_t d03 = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // dims 0, 1, 2, 3
+  const uint32_t d47 = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // dims 4, 5, 6, 7
   half8v out;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // v_perm_b32 (selector bytes 0-3 take bytes of the second operand, 4-7 of
-    // the first, 0x0c gives zero): (ev.bk, 0, od.bk, 0)
-    const uint32_t sel = 0x0C000C00u | (uint32_t)k | ((uint32_t)(4 + k) << 16);
-    const uint32_t u = __builtin_amdgcn_perm(od, ev, sel) | 0x64006400u;
-    const half2v v = __builtin_bit_cast(half2v, u) - half2v{(f16)1032.f, (f16)1032.f};
-    out[2 * k] = v[0];
-    out[2 * k + 1] = v[1];
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t a = k ? d47 : d03;
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u);
+    const half2v l2 = __builtin_bit_cast(half2v, lo) - half2v{(f16)1032.f, (f16)1032.f};
+    const half2v h2 = __builtin_bit_cast(half2v, hi) - half2v{(f16)1032.f, (f16)1032.f};
+    out[4 * k] = l2[0];
+    out[4 * k + 1] = l2[1];
+    out[4 * k + 2] = h2[0];
+    out[4 * k + 3] = h2[1];
   }
   return out;
 }

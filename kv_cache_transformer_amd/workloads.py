@@ -17,6 +17,8 @@ Named workloads (sizes and distributions):
 * ``gqa_decode_int8``   the decode above over an int8 cache: float32 Q/K/V,
   uniform random int8 codes, per-channel key and value scales 3/127 times
   uniform [0.5, 1.5).
+* ``gqa_decode_int4``   the same over a packed int4 cache (two codes per byte),
+  uniform random bytes, scales drawn as for int8.
 * ``gqa_long_prefill``  GroupQueryAttention prompt: B=4, S=4096, N=32, kvN=8,
   H=128, fp16, causal, local window 1024, softcap 50, head_sink ~ N(0,1),
   Q/K RMSNorm weights ~ 1+N(0,0.1), rotary theta 10000.
@@ -292,6 +294,16 @@ def gqa_decode_int8(seed=8, batch=16, cap=4096):
                     quant=dict(bits=8, k="channel", v="channel")) | dict(name="gqa_decode_int8")
 
 
+def gqa_decode_int4(seed=9, batch=16, cap=4096):
+    """GroupQueryAttention decode over a packed int4 cache: as gqa_decode_int8
+    with two codes per byte (uniform random bytes)."""
+    rng = np.random.default_rng(seed)
+    past = rng.integers(1024, cap, batch)
+    return gqa_case(rng, B=batch, S=1, N=32, kvN=8, H=128, dtype=F32, past="shared",
+                    past_lens=past, cap=cap, rotary=True,
+                    quant=dict(bits=4, k="channel", v="channel")) | dict(name="gqa_decode_int4")
+
+
 def gqa_long_prefill(seed=3, batch=4, seq=4096):
     """GroupQueryAttention prompt: B=4 S=4096 N=32 kvN=8 H=128 fp16, window 1024,
     softcap 50, head sink, Q/K RMSNorm, rotary."""
@@ -533,6 +545,7 @@ WORKLOADS = {
     "gqa_decode": gqa_decode,
     "gqa_window_decode": gqa_window_decode,
     "gqa_decode_int8": gqa_decode_int8,
+    "gqa_decode_int4": gqa_decode_int4,
     "gqa_long_prefill": gqa_long_prefill,
     "sparse_prompt": sparse_prompt,
     "sparse_generation": sparse_generation,

@@ -218,6 +218,16 @@ def test_workload_gqa_decode_int8():
     print(f"key codes on the other side of a near tie: {n}")
 
 
+def test_workload_gqa_decode_int4():
+    case = wl.gqa_decode_int4()
+    print("gqa_decode_int4", flush=True)
+    got = gqa_gpu(case)
+    info = {}
+    ref = gqa_oracle(case, info=info)
+    n = check_quant_gqa(case, got, ref, info)
+    print(f"key codes on the other side of a near tie: {n}")
+
+
 def _empty_case(B, S, past=None, cap=64, N=8, kvN=2, H=64, dtype=F16):
     """A call over an empty batch (B = 0) or with no new tokens (S = 0)."""
     rng = np.random.default_rng(900 + B + S)

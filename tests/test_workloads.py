@@ -63,6 +63,20 @@ def test_window_decode_workload():
     assert i["cos_cache"].shape[0] >= c["total_sequence_length"]
 
 
+def test_int4_decode_workload():
+    c = wl.WORKLOADS["gqa_decode_int4"]()
+    i, a = c["inputs"], c["attrs"]
+    assert c["name"] == "gqa_decode_int4" and c["shared"]
+    assert i["query"].dtype == np.float32 and i["query"].shape == (16, 1, 32 * 128)
+    assert i["past_key"].dtype == np.uint8 and i["past_key"].shape == (16, 8, 4096, 64)
+    assert i["present_key"] is i["past_key"] and i["present_value"] is i["past_value"]
+    assert i["k_scale"].shape == (8 * 128,) and i["v_scale"].dtype == np.float32
+    assert a["kv_cache_bit_width"] == 4 and a["k_quant_type"] == 2 and a["v_quant_type"] == 2
+    # both nibble values occur in every position of a byte
+    b = i["past_key"][:2, :2, :64]
+    assert len(np.unique(b & 15)) == 16 and len(np.unique(b >> 4)) == 16
+
+
 def test_int8_decode_workload():
     c = wl.WORKLOADS["gqa_decode_int8"]()
     i, a = c["inputs"], c["attrs"]
