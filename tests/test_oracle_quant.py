@@ -127,21 +127,23 @@ def test_prompt_lossless_equals_float_path(bits, per_channel, causal, window):
     assert np.array_equal(quant.load_codes(qv, bits), vc.transpose(0, 2, 1, 3))
 
 
-def test_decode_lossless_past_and_append():
-    """int8 decode onto a shared past: the past codes are read through their
-    scales and the new row is appended as codes (lossless values), so the output
-    equals the float path over the dequantised cache."""
+@pytest.mark.parametrize("bits", [8, 4])
+def test_decode_lossless_past_and_append(bits):
+    """Decode onto a shared past (int8, or packed int4): the past codes are read
+    through their scales and the new row is appended as codes (lossless
+    values), so the output equals the float path over the dequantised cache."""
     rng = np.random.default_rng(11)
     B, N, kvN, H, C = 3, 8, 2, 16, 12
+    lo, hi = -(1 << (bits - 1)), 1 << (bits - 1)
     ks = _pow2_scales(rng, kvN, H, True)
     vs = _pow2_scales(rng, kvN, H, False)
     ksc = quant.channel_scales(ks, 2, kvN, H)
     vsc = quant.channel_scales(vs, 1, kvN, H)
     lens = np.array([4, 11, 0], np.int32)          # seqlens_k: totals 5, 12, 1
-    past_c = rng.integers(-128, 128, (B, kvN, C, H)).astype(np.int8)
-    past_v = rng.integers(-128, 128, (B, kvN, C, H)).astype(np.int8)
-    nk = rng.integers(-128, 128, (B, 1, kvN, H))
-    nv = rng.integers(-128, 128, (B, 1, kvN, H))
+    past_c = rng.integers(lo, hi, (B, kvN, C, H))
+    past_v = rng.integers(lo, hi, (B, kvN, C, H))
+    nk = rng.integers(lo, hi, (B, 1, kvN, H))
+    nv = rng.integers(lo, hi, (B, 1, kvN, H))
     k = (nk * ksc).astype(np.float32).reshape(B, 1, kvN * H)
     v = (nv * vsc).astype(np.float32).reshape(B, 1, kvN * H)
     q = rng.standard_normal((B, 1, N * H)).astype(np.float32)
@@ -150,9 +152,11 @@ def test_decode_lossless_past_and_append():
     fv = (past_v * vsc[None, :, None, :]).astype(np.float32)
     ref, rk, rv = oracle.gqa(q, k, v, past_key=fk, past_value=fv, present_key=fk,
                              present_value=fv, **common)
-    got, gk, gv = oracle.gqa(q, k, v, past_key=past_c, past_value=past_v, present_key=past_c,
-                             present_value=past_v, k_scale=ks, v_scale=vs, k_quant_type=2,
-                             v_quant_type=1, kv_cache_bit_width=8, **common)
+    pk, pv = quant.store_codes(past_c, bits), quant.store_codes(past_v, bits)
+    got, gk, gv = oracle.gqa(q, k, v, past_key=pk, past_value=pv, present_key=pk,
+                             present_value=pv, k_scale=ks, v_scale=vs, k_quant_type=2,
+                             v_quant_type=1, kv_cache_bit_width=bits, **common)
+    gk, gv = quant.load_codes(gk, bits), quant.load_codes(gv, bits)
     assert np.array_equal(got, ref)
     assert np.array_equal(gk * ksc[None, :, None, :], rk)
     assert np.array_equal(gv * vsc[None, :, None, :], rv)
