@@ -367,11 +367,14 @@ template <int MODE, int BN> struct FlashWork {
       // Workgroups are dealt to the eight XCDs round-robin by linear id; the
       // remap gives each XCD a contiguous range of (row block, head group,
       // sample) items, so the workgroups sharing a K/V slab share one L2.
+      // Row blocks go last to first: under a causal bound the late blocks see
+      // the most keys, so the longest items start first and short ones fill
+      // the tail.
       const int gx = gridDim.x, gy = gridDim.y;
       const int n = gx * gy * (int)gridDim.z;
       int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
       if (n % 8 == 0) id = (id % 8) * (n / 8) + id / 8;
-      const int bx = id % gx, by = (id / gx) % gy;
+      const int bx = gx - 1 - id % gx, by = (id / gx) % gy;
       b = id / (gx * gy);
       const int groups = g / HW;
       kvh = by / groups;
