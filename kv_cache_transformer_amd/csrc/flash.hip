@@ -354,11 +354,14 @@ template <int MODE, int BN> struct FlashWork {
     const int HW = p.heads_per_wg;
     row_base = 0;
     if (MODE == kVarlen) {
+      // item-major: all heads of the list's first (longest) item go first
       const int count = p.work[0];
-      if ((int)blockIdx.x >= count) return false;
-      b = p.work[1 + 2 * blockIdx.x];
-      const int tile = p.work[2 + 2 * blockIdx.x];
-      h = blockIdx.y;
+      const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+      const int item = lin / (int)gridDim.y;
+      if (item >= count) return false;
+      b = p.work[1 + 2 * item];
+      const int tile = p.work[2 + 2 * item];
+      h = lin % (int)gridDim.y;
       kvh = h / g;
       r0 = tile * p.rows_per_wg;
       row_base = p.lens[2 * b];
