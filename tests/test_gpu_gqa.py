@@ -38,6 +38,10 @@ PREFILL = [
     dict(dtype=F16, B=1, S=130, N=6, kvN=2, H=64, softcap=5.0),
     dict(dtype=F16, B=1, S=33, N=32, kvN=1, H=64, scale=-0.3),
     dict(dtype=F16, B=1, S=1, N=8, kvN=2, H=128, rotary=True),
+    # windows without softcap or bias: the per-lane key-offset masks of the
+    # pipelined kernel, tiles partly visible to a workgroup's rows
+    dict(dtype=F16, B=2, S=300, N=8, kvN=2, H=128, window=90),
+    dict(dtype=F16, B=1, S=257, N=4, kvN=1, H=64, window=40, rotary=True),
 ]
 
 DECODE = [
