@@ -602,7 +602,7 @@ def main():
                           args.copy_probe_mib or 512, merge=args.traffic_merge)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
               "no multi-GPU path: every workload here is one GPU's share.", file=sys.stderr)
         sys.exit(2)
     import torch
