@@ -143,7 +143,7 @@ def decode_workload(torch, kv, wl, args, timer):
                      torch.randn(t["past_value"].shape, generator=g, device=dev).half()))
     a = case["attrs"]
     out = torch.empty_like(t["query"])
-    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
 
     def step(n):
         pk, pv = sets[n % len(sets)]
@@ -176,7 +176,7 @@ def decode_quant_workload(torch, kv, wl, args, timer, bits=8):
                                         dtype=cdt) for _ in range(2)))
     a = case["attrs"]
     out = torch.empty_like(t["query"])
-    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
 
     def step(n):
         pk, pv = sets[n % len(sets)]
@@ -205,7 +205,7 @@ def window_decode_workload(torch, kv, wl, args, timer):
     dev = "cuda:0"
     t = {k: torch.from_numpy(v).to(dev) for k, v in i.items() if k not in ("present_key", "present_value")}
     out = torch.empty_like(t["query"])
-    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
 
     def step(n):
         kv.gqa_attention(t["query"], t["key"], t["value"], t["past_key"], t["past_value"],
@@ -237,7 +237,7 @@ def prefill_workload(torch, kv, wl, args, timer):
     dev = "cuda:0"
     t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
     out = torch.empty_like(t["query"])
-    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device=dev)
 
     def step(n):
         kv.gqa_attention(t["query"], t["key"], t["value"], None, None, t["seqlens_k"],
@@ -294,7 +294,7 @@ def sparse_workload(torch, kv, wl, args, timer):
     dev = "cuda:0"
     t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
     out = torch.empty_like(t["query"])
-    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device=dev)
 
     def step(n):
         kv.sparse_attention(t["query"], t["key"], t["value"], t["past_key"], t["past_value"],
@@ -318,7 +318,7 @@ def sparse_generation_workload(torch, kv, wl, args, timer):
     dev = "cuda:0"
     t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
     out = torch.empty_like(t["query"])
-    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
     total = case["total_sequence_length"]
 
     def step(n):
@@ -350,7 +350,7 @@ def packed_workload(torch, kv, wl, args, timer):
     t = {k: torch.from_numpy(v).to(dev) for k, v in i.items()}
     T = i["input"].shape[0]
     out = torch.empty((T, 768), dtype=torch.float16, device=dev)
-    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device=dev)
 
     def step(n):
         kv.packed_attention(t["input"], t["weights"], t["bias"], t["token_offset"],

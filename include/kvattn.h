@@ -33,7 +33,17 @@
  * The library never allocates, frees or synchronises; all work is enqueued
  * on `stream` (a hipStream_t; NULL = the default stream).  The workspace size
  * comes from the matching *_workspace_size call made with the same
- * arguments; its contents need no initialisation and are not preserved.
+ * arguments.  Every non-empty workspace begins with KVATTN_COUNTER_BYTES of
+ * arrival counters: single-token decode calls (gqa_attention with a past and
+ * S = 1, decode_mha, sparse_attention generating one token) keep one int32
+ * there per (sample, kv head, query-head group) unit whose keys they split
+ * over several pairs of waves; the pairs count themselves in and the last
+ * one merges the unit (one launch, no merge dispatch).  Those bytes must be
+ * zero when a call starts; every call leaves them zero and no call writes
+ * anything else there.  So: allocate a workspace zero-filled once, then
+ * reuse it for calls of any operator and shape.  The rest of the workspace
+ * needs no initialisation and is not preserved.  Calls that may run at the
+ * same time must not share a workspace.
  *
  * Errors.  Every call returns KVATTN_OK (0) or a negative kvattn_status.
  * All validation happens before the first launch, so a failed call writes
@@ -79,6 +89,9 @@ typedef enum kvattn_dtype {
   KVATTN_DT_U8 = 5     /* uint8: two packed 4-bit cache codes */
 } kvattn_dtype;
 
+/* Bytes of decode arrival counters at the start of every non-empty workspace. */
+#define KVATTN_COUNTER_BYTES 32768
+
 typedef struct kvattn_tensor {
   void* data;        /* device pointer, NULL = absent optional tensor */
   int32_t dtype;     /* kvattn_dtype */
@@ -115,6 +128,21 @@ enum {
   KVATTN_PROFILE_SHIFT = 5
 };
 void kvattn_profile_events(void* start, void* stop, int32_t kind);
+
+/*
+ * Decode split control.  Single-token decode spreads every (sample, kv head,
+ * query-head group) unit's live keys over pairs of waves so that the grid
+ * fills the device; the split (GroupQueryAttention page, Implementation
+ * variants: partitioning cached decode along the key axis and merging the
+ * partial online-softmax results) aims at waves_per_cu waves per compute
+ * unit (default 8).  kvattn_set_decode_split(w) sets that target for later
+ * calls on the calling thread: 1..32, or 0 for the default.  Smaller targets
+ * give fewer pairs per unit (1 gives one pair per unit at the decode
+ * workload's shape); results agree up to float32 rounding order.  Returns the
+ * previous setting (0 = default), or KVATTN_ERR_INVALID_ARG for values
+ * outside 0..32 (the setting is then unchanged).
+ */
+int32_t kvattn_set_decode_split(int32_t waves_per_cu);
 
 /* ------------------------------------------------------------------------ */
 /* GroupQueryAttention                                                      */

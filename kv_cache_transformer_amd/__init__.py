@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     library_path,
     packed_attention,
     packed_schedule,
+    set_decode_split,
     sparse_attention,
 )
 
@@ -34,6 +35,7 @@ __all__ = [
     "sparse_attention",
     "packed_attention",
     "packed_schedule",
+    "set_decode_split",
     "library",
     "library_path",
 ]

@@ -103,6 +103,8 @@ def library():
         lib.kvattn_packed_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         lib.kvattn_profile_events.restype = None
         lib.kvattn_profile_events.argtypes = [vp, vp, i32]
+        lib.kvattn_set_decode_split.restype = i32
+        lib.kvattn_set_decode_split.argtypes = [i32]
         for name in ("gqa_attrs_default", "dmmha_attrs_default", "sparse_attrs_default",
                      "packed_attrs_default"):
             getattr(lib, name).restype = None
@@ -158,6 +160,9 @@ def _stream(stream, device):
 
 
 def _workspace(nbytes, device, workspace):
+    """The caller's workspace, or a new zero-filled one (decode calls need
+    their arrival counters zero when they start and leave them zero, so a
+    caller that reuses a workspace allocates it zero-filled once)."""
     torch = _torch()
     if nbytes == 0:
         return None, 0
@@ -165,7 +170,7 @@ def _workspace(nbytes, device, workspace):
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace of {nbytes} bytes needed")
         return workspace, workspace.numel() * workspace.element_size()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def _ptr(t):
@@ -333,6 +338,16 @@ def packed_attention(input, weights, bias, token_offset, cumulative_sequence_len
     _check(lib.packed_attention(ctypes.byref(a), ins, PACKED_NUM_INPUTS, outs, PACKED_NUM_OUTPUTS,
                                 _ptr(ws), wsb, _stream(stream, input.device)))
     return output
+
+
+def set_decode_split(waves_per_cu):
+    """Decode split target for later calls on this thread (include/kvattn.h,
+    kvattn_set_decode_split): waves per compute unit, 1..32, or 0 for the
+    default.  Returns the previous setting."""
+    prev = library().kvattn_set_decode_split(int(waves_per_cu))
+    if prev < 0:
+        _check(prev)
+    return prev
 
 
 def packed_schedule(cumulative_sequence_length, token_count, padded_sequence_length,

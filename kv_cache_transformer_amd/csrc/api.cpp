@@ -26,10 +26,19 @@ thread_local std::string g_last_error;
 constexpr int64_t kDecodeWavesPerCu = 8;
 // decode: a wave streams at least this many keys when a unit is split
 constexpr int64_t kDecodeMinKeysPerWave = 64;
+// Every non-empty workspace starts with this many bytes of decode arrival
+// counters (one int32 per split unit); no call writes anything else there,
+// so one zero-filled workspace can serve calls of any operator and shape.
+constexpr size_t kCounterBytes = KVATTN_COUNTER_BYTES;
+constexpr int64_t kCounterSlots = kCounterBytes / sizeof(int32_t);
 
 // measurement hook (kvattn_profile_events)
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 thread_local int g_prof_kind = 0;
+
+// decode grid fill target in waves per compute unit (kvattn_set_decode_split;
+// 0 = kDecodeWavesPerCu)
+thread_local int g_decode_waves_per_cu = 0;
 
 // Launch `f` bracketed by the profiling events when `kind` is the one asked for.
 template <typename F>
@@ -137,14 +146,13 @@ int device_cu_count() {
 
 // Waves of the decode grid: enough to fill the device, no more than the
 // units could use (a pair of waves streams >= 128 keys of a split unit), at
-// least one pair per unit, a multiple of eight (workgroups of four pairs).  KVATTN_DECODE_WAVES_PER_CU=<1..32> overrides the fill
-// target (tuning aid).
+// least one pair per unit, a multiple of eight (workgroups of four pairs).
+// kvattn_set_decode_split changes the fill target for the calling thread.
 int64_t decode_waves(int64_t units, int64_t max_keys) {
-  int64_t per_cu = kDecodeWavesPerCu;
-  if (const char* e = std::getenv("KVATTN_DECODE_WAVES_PER_CU")) {
-    const int v = std::atoi(e);
-    if (v >= 1 && v <= 32) per_cu = v;
-  }
+  // more units than counter slots: one pair per unit (the grid is full
+  // anyway; the kernel then splits nothing, see DecodeParams::split)
+  if (units > kCounterSlots) return (2 * units + 7) / 8 * 8;
+  const int64_t per_cu = g_decode_waves_per_cu > 0 ? g_decode_waves_per_cu : kDecodeWavesPerCu;
   const int64_t fill = per_cu * device_cu_count();
   const int64_t pair_keys = 2 * kDecodeMinKeysPerWave;
   const int64_t useful = 2 * (units + (units * std::max<int64_t>(max_keys, 0) + pair_keys - 1) / pair_keys);
@@ -170,7 +178,7 @@ struct GqaPlan {
   // decode
   int head_groups, hpw;
   int64_t waves;
-  size_t ws_q, ws_part, ws_deq, ws_total;
+  size_t ws_cnt, ws_q, ws_part, ws_deq, ws_total;  // workspace: counters first
 };
 
 // Quantised-cache attributes and scales (GroupQueryAttention page,
@@ -325,6 +333,7 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   P.decode = P.has_past && P.S == 1;
   P.q_transform = qn || a->do_rotary;
   size_t esz = elem_size(dt);
+  P.ws_cnt = 0;
   P.ws_q = 0;
   P.ws_part = 0;
   P.ws_deq = 0;
@@ -339,7 +348,9 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   }
   if (P.bits != 0 && !P.decode)  // prompt: the dequantised keys and values, float32 (B, kvN, S, H) each
     P.ws_deq = 2 * align256((size_t)P.B * P.kvN * P.S * P.H * sizeof(float));
-  P.ws_total = P.ws_q + P.ws_part + P.ws_deq;
+  const size_t body = P.ws_q + P.ws_part + P.ws_deq;
+  P.ws_cnt = body ? kCounterBytes : 0;
+  P.ws_total = P.ws_cnt + body;
   return KVATTN_OK;
 }
 
@@ -402,11 +413,13 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     d.window = a->local_window_size;
     d.win_cap = P.window_cache ? P.cap : 0;
     d.out = out[GQA_OUT_OUTPUT].data;
-    d.part = reinterpret_cast<float*>(wsb + P.ws_q);
+    d.counters = reinterpret_cast<int*>(wsb);
+    d.part = reinterpret_cast<float*>(wsb + P.ws_cnt + P.ws_q);
     d.B = P.B; d.N = P.N; d.kvN = P.kvN; d.H = P.H; d.cap = P.cap;
     d.scale = scale;
     d.softcap = a->softcap;
     d.head_groups = P.head_groups; d.hpw = P.hpw; d.waves = (int)P.waves;
+    d.split = (int64_t)d.B * d.kvN * d.head_groups <= kCounterSlots;
     d.k_scale = static_cast<const float*>(in[GQA_IN_K_SCALE].data);
     d.v_scale = static_cast<const float*>(in[GQA_IN_V_SCALE].data);
     d.k_scale_pc = P.k_pc;
@@ -414,7 +427,6 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     const DType ddt = P.bits == 8 ? DType::Q8 : (P.bits == 4 ? DType::Q4 : dt);
     CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st, [&] { return launch_decode(ddt, P.HP, d, st); }),
                      "decode launch"));
-    CHECK(hip_status(launch_decode_combine(dt, P.HP, d, st), "decode combine launch"));
     return ok();
   }
 
@@ -448,8 +460,8 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   float* deq_k = nullptr;
   float* deq_v = nullptr;
   if (P.bits != 0) {
-    deq_k = reinterpret_cast<float*>(wsb + P.ws_q + P.ws_part);
-    deq_v = reinterpret_cast<float*>(wsb + P.ws_q + P.ws_part + P.ws_deq / 2);
+    deq_k = reinterpret_cast<float*>(wsb + P.ws_cnt + P.ws_q + P.ws_part);
+    deq_v = reinterpret_cast<float*>(wsb + P.ws_cnt + P.ws_q + P.ws_part + P.ws_deq / 2);
     pp.bits = P.bits;
     pp.kq = ck.data;
     pp.vq = cv.data;
@@ -524,7 +536,7 @@ struct DmmhaPlan {
   int B, N, H, HP, dt, cap, kv_len;
   bool self;
   int64_t waves;
-  size_t ws_total;
+  size_t ws_cnt, ws_total;  // workspace: arrival counters, then partials
 };
 
 int dmmha_validate(const dmmha_attrs* a, const kvattn_tensor* in, int n_in,
@@ -608,7 +620,8 @@ int dmmha_validate(const dmmha_attrs* a, const kvattn_tensor* in, int n_in,
   const int64_t units = (int64_t)P.B * P.N;
   P.waves = decode_waves(units, P.kv_len);
   if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode_mha: too many (sample, head) units");
-  P.ws_total = align256((size_t)(P.waves / 2) * (P.HP + 4) * sizeof(float));
+  P.ws_cnt = kCounterBytes;
+  P.ws_total = P.ws_cnt + align256((size_t)(P.waves / 2) * (P.HP + 4) * sizeof(float));
   return KVATTN_OK;
 }
 
@@ -645,14 +658,15 @@ int dmmha_run(const dmmha_attrs* a, const kvattn_tensor* in, const kvattn_tensor
   d.mask_filter = a->mask_filter_value;
   d.window = -1;
   d.out = out[DMMHA_OUT_OUTPUT].data;
-  d.part = static_cast<float*>(ws);
+  d.counters = static_cast<int*>(ws);
+  d.part = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_cnt);
   d.B = P.B; d.N = P.N; d.kvN = P.N; d.H = P.H; d.cap = P.cap;
   d.scale = resolve_scale(a->scale, P.H);
   d.head_groups = 1; d.hpw = 1; d.waves = (int)P.waves;
+  d.split = (int64_t)d.B * d.kvN * d.head_groups <= kCounterSlots;
   CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st,
                             [&] { return launch_decode(to_dtype(P.dt), P.HP, d, st); }),
                    "decode launch"));
-  CHECK(hip_status(launch_decode_combine(to_dtype(P.dt), P.HP, d, st), "decode combine launch"));
   return ok();
 }
 
@@ -664,7 +678,7 @@ struct SparsePlan {
   bool packed_qkv, rotary, generation;
   bool decode;      // one new token: split-key decode over the CSR blocks
   int64_t waves;
-  size_t ws_q, ws_part, ws_total;
+  size_t ws_cnt, ws_q, ws_part, ws_total;  // workspace: counters first
 };
 
 // most CSR blocks per row the decode route takes (its block table sits in LDS)
@@ -752,6 +766,7 @@ int sparse_validate(const sparse_attrs* a, const kvattn_tensor* in, int n_in, in
   if ((has(out[SPARSE_OUT_PRESENT_KEY]) && out[SPARSE_OUT_PRESENT_KEY].data != pk.data) ||
       (has(out[SPARSE_OUT_PRESENT_VALUE]) && out[SPARSE_OUT_PRESENT_VALUE].data != pv.data))
     return fail(KVATTN_ERR_INVALID_ARG, "the present caches are the past buffers updated in place");
+  P.ws_cnt = 0;
   P.ws_q = 0;  // the flash kernel rotates the queries as it loads them
   P.ws_part = 0;
   P.waves = 0;
@@ -762,10 +777,11 @@ int sparse_validate(const sparse_attrs* a, const kvattn_tensor* in, int n_in, in
     const int64_t units = (int64_t)P.B * P.N;
     P.waves = decode_waves(units, std::min<int64_t>(total, (int64_t)P.max_nnz * bs));
     if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "sparse decode: too many units");
+    P.ws_cnt = kCounterBytes;
     P.ws_q = align256((size_t)P.B * P.N * P.H * elem_size(dt));
     P.ws_part = align256((size_t)(P.waves / 2) * (P.HP + 4) * sizeof(float));
   }
-  P.ws_total = P.ws_q + P.ws_part;
+  P.ws_total = P.ws_cnt + P.ws_q + P.ws_part;
   return KVATTN_OK;
 }
 
@@ -800,7 +816,8 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
   pp.pos_mode = P.generation ? 2 : 0;  // past_b = key_total[b] - S
   pp.B = P.B; pp.S = P.S; pp.N = P.N; pp.kvN = P.kvN; pp.H = P.H; pp.cap = P.cap;
   pp.write_q = P.decode ? 1 : 0;
-  pp.q_out = P.decode ? ws : nullptr;
+  void* q_ws = P.decode ? static_cast<char*>(ws) + P.ws_cnt : nullptr;  // rotated query
+  pp.q_out = q_ws;
   pp.write_kv = 1;
   pp.win_cap = 0;
   CHECK(hip_status(profiled(KVATTN_PROFILE_PREP, st, [&] { return launch_prep(dt, pp, st); }),
@@ -808,7 +825,7 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
 
   if (P.decode) {
     DecodeParams d{};
-    d.q = ws;
+    d.q = q_ws;
     d.k_new = d.v_new = nullptr;  // prep wrote the new rows
     d.kc = in[SPARSE_IN_PAST_KEY].data;
     d.vc = in[SPARSE_IN_PAST_VALUE].data;
@@ -816,11 +833,13 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
     d.len_mode = 3;
     d.window = -1;
     d.out = out[SPARSE_OUT_OUTPUT].data;
-    d.part = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_q);
+    d.counters = static_cast<int*>(ws);
+    d.part = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_cnt + P.ws_q);
     d.B = P.B; d.N = P.N; d.kvN = P.N; d.H = P.H; d.cap = P.cap;
     d.kv_div = P.N / P.kvN;
     d.scale = resolve_scale(a->scale, P.H);
     d.head_groups = 1; d.hpw = 1; d.waves = (int)P.waves;
+    d.split = (int64_t)d.B * d.kvN * d.head_groups <= kCounterSlots;
     d.csr_rp = static_cast<const int32_t*>(in[SPARSE_IN_BLOCK_ROW_INDICES].data);
     d.csr_cols = static_cast<const int32_t*>(in[SPARSE_IN_BLOCK_COL_INDICES].data);
     d.rp_stride = P.max_blocks + 1;
@@ -830,7 +849,6 @@ int sparse_run(const sparse_attrs* a, const kvattn_tensor* in, const kvattn_tens
     d.max_blocks = P.max_blocks;
     CHECK(hip_status(profiled(KVATTN_PROFILE_DECODE, st, [&] { return launch_decode(dt, P.HP, d, st); }),
                      "decode launch"));
-    CHECK(hip_status(launch_decode_combine(dt, P.HP, d, st), "decode combine launch"));
     return ok();
   }
 
@@ -885,7 +903,7 @@ constexpr int kPackedTile = 128;
 
 struct PackedPlan {
   int T, D, C, B, S, N, H, HP, dt, qh, kh, vh;
-  size_t ws_y, ws_bounds, ws_work, ws_total;
+  size_t ws_y, ws_bounds, ws_work, ws_total;  // after the counter bytes
 };
 
 int packed_validate(const packed_attrs* a, const kvattn_tensor* in, int n_in,
@@ -949,14 +967,14 @@ int packed_validate(const packed_attrs* a, const kvattn_tensor* in, int n_in,
   P.ws_bounds = align256((size_t)2 * P.B * sizeof(int32_t));
   const size_t items = (size_t)P.B * ((P.S + kPackedTile - 1) / kPackedTile);
   P.ws_work = align256((1 + 2 * items) * sizeof(int32_t));
-  P.ws_total = P.ws_y + P.ws_bounds + P.ws_work;
+  P.ws_total = kCounterBytes + P.ws_y + P.ws_bounds + P.ws_work;
   return KVATTN_OK;
 }
 
 int packed_run(const packed_attrs* a, const kvattn_tensor* in, const kvattn_tensor* out,
                const PackedPlan& P, void* ws, hipStream_t st) {
   const DType dt = to_dtype(P.dt);
-  char* wsb = static_cast<char*>(ws);
+  char* wsb = static_cast<char*>(ws) + kCounterBytes;
   void* y = wsb;
   int32_t* bounds = reinterpret_cast<int32_t*>(wsb + P.ws_y);
   int32_t* work = reinterpret_cast<int32_t*>(wsb + P.ws_y + P.ws_bounds);
@@ -1047,12 +1065,21 @@ const char* kvattn_status_string(int32_t s) {
 
 const char* kvattn_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvattn_version(void) { return 100; }
+int32_t kvattn_version(void) { return 200; }
 
 void kvattn_profile_events(void* start, void* stop, int32_t kind) {
   g_prof_start = static_cast<hipEvent_t>(start);
   g_prof_stop = static_cast<hipEvent_t>(stop);
   g_prof_kind = (start && stop) ? kind : 0;
+}
+
+int32_t kvattn_set_decode_split(int32_t waves_per_cu) {
+  const int32_t prev = g_decode_waves_per_cu;
+  if (waves_per_cu < 0 || waves_per_cu > 32)
+    return fail(KVATTN_ERR_INVALID_ARG, "kvattn_set_decode_split: %d waves per compute unit (0..32)", waves_per_cu);
+  g_decode_waves_per_cu = waves_per_cu;
+  ok();
+  return prev;
 }
 
 void gqa_attrs_default(gqa_attrs* a) {

@@ -18,11 +18,14 @@
 // they claim from an LDS counter.  Each chunk's partial (max, sum,
 // unnormalised output per head) goes to its own LDS record and the pair
 // merges them in chunk order, so the result does not depend on which wave
-// took which chunk.  A pair writes one partial per head, or the output when
-// its unit is small enough for one pair; decode_combine_kernel merges the
-// pairs of the other units with a log-sum-exp combine and adds the head-sink
-// term.  A wave reads its rows of the cache once for all query heads of its
-// unit, with up to three 16-row sub-tiles in flight in a register ring.
+// took which chunk.  A unit served by one pair gets its output from that
+// pair.  Otherwise each pair writes one partial per head to the workspace and
+// counts its arrival on the unit's counter; the pair that arrives last merges
+// the unit's partials in pair order with a log-sum-exp combine, adds the
+// head-sink term, writes the output and sets the counter back to zero (the
+// merge dispatch the page describes is folded into this one launch).  A wave
+// reads its rows of the cache once for all query heads of its unit, with up
+// to three 16-row sub-tiles in flight in a register ring.
 //
 // The query (optionally RMS-normed per head, then NeoX-rotated at the new
 // token's position) is built in registers in the MFMA operand layout before
@@ -72,10 +75,6 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // Slack of the running maximum (log2 units): probabilities stay <= 2^3, which
 // the int8 tile's 2^12-scaled f16 split holds (2^15 < 65504).
 constexpr float kDecodeSlack = 3.f;
-
-// A unit with at most this many keys and a single pair writes the output
-// directly (no combine).
-constexpr int kDirectKeys = 64;
 
 // Cache type tags: float32 activations (query, new rows, output) over an int8
 // key/value cache, or over an int4 one (two codes per byte).
@@ -630,7 +629,7 @@ __device__ int64_t deal_quota(const DecodeParams& p, int ups, int lane, int c0) 
   k *= ups;
   const int64_t units = (int64_t)p.B * ups;
   const int64_t spare = (int64_t)(p.waves / 2) - units;
-  if (spare <= 0) return INT64_MAX;
+  if (spare <= 0 || !p.split) return INT64_MAX;
   return max(2 * kMinKeysPerWave, (k + spare - 1) / spare);
 }
 
@@ -680,20 +679,32 @@ __device__ bool find_sample(const DecodeParams& p, int ups, int64_t quota, int p
   return false;
 }
 
-// First pair of sample b (all lanes of a wave call it).
-template <bool CSR>
-__device__ int sample_first_pair(const DecodeParams& p, int ups, int64_t quota, int b, int lane) {
-  int acc = 0;
-  for (int b0 = 0; b0 < b; b0 += 64) {
-    const int s = b0 + lane;
-    acc += (s < b) ? pairs_for(sample_count<CSR>(p, s), quota) * ups : 0;
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m, 64);
-  return acc;
-}
+// Partial records merged per batch by the last pair of a unit.
+constexpr int kMergeBatch = 8;
 
-__device__ __forceinline__ bool unit_direct(int c, int nb) { return nb == 1 && c <= kDirectKeys; }
+// Partial records cross compute units on different XCDs, whose L2 caches are
+// not coherent with each other: they are stored and loaded at device scope
+// (the sc1 cache policy: written through to, and read from, the level all
+// XCDs share), through a buffer resource over the partial records
+// (out-of-range accesses read 0 and drop the store).
+constexpr int kDeviceScope = 16;               // cache-policy bit of sc1
+constexpr int kBufferFormat = 0x00020000;      // raw 32-bit buffer (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const DecodeParams& p, int rs) {
+  const int64_t bytes = (int64_t)(p.waves / 2) * p.hpw * rs * 4;
+  return __builtin_amdgcn_make_buffer_rsrc(p.part, 0, (int)min(bytes, (int64_t)0x7fffffff), kBufferFormat);
+}
+__device__ __forceinline__ void store_partial_ml(__amdgpu_buffer_rsrc_t r, int off, float m, float l) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, float2v{m, l}), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void store_partial_o(__amdgpu_buffer_rsrc_t r, int off, float4v o) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4v, o), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ float2v load_partial_ml(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float2v, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kDeviceScope));
+}
+__device__ __forceinline__ float4v load_partial_o(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+}
 
 template <typename T>
 __device__ __forceinline__ float read_sink(const DecodeParams& p, int h, bool& has) {
@@ -799,7 +810,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   const int local = pr - first;
   const int ui = live ? local / nb : 0;
   const int kp = live ? local % nb : 0;  // pair within the unit
-  const bool direct = unit_direct(c, nb);
+  const bool direct = nb == 1;  // the unit's only pair writes its output
   const int kvh = ui / hg, hgrp = ui % hg;
   const int h0 = kvh * g + hgrp * 16;
   const int nh = min(16, g - hgrp * 16);
@@ -1042,6 +1053,55 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   };
 
+  // ---- streaming: chunks claimed by the two waves of the pair ----------------
+  // Chunk sub-tiles go through a ring of R register buffers; the load of the
+  // sub-tile R - 1 places ahead is issued before a sub-tile is computed, and
+  // the next chunk is claimed when the loads reach the end of the current one.
+  // Loads are issued on every step (past the end they re-read a valid row), so
+  // every path between a load and its use issues the same loads.
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_claim[jp], 1);
+    v = __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
+    return v < claimable ? v : nch;
+  };
+  // next load: chunk lc, its keys [ca, ce), sub-tile ls of ns
+  int lc = nch, ls = 0, ca = 0, ce = 0, ns = 0;
+  auto enter = [&](int ch) {
+    lc = ch;
+    ls = 0;
+    ca = lo + ch * csz;
+    ce = min(ca + csz, lo + len);
+    ns = (ce - ca + 15) / 16;
+  };
+  if (live) enter(appender ? nch - 1 : claim());
+  // b_off: cache row minus key index in the sub-tile (CSR block keys; else 0)
+  int b_j0[R], b_end[R], b_ch[R], b_off[R];
+  bool b_last[R];
+  auto next_load = [&](auto rt) {
+    constexpr int r = decltype(rt)::value;
+    b_off[r] = 0;
+    if (lc < nch) {
+      b_j0[r] = ca + 16 * ls;
+      b_end[r] = ce;
+      b_ch[r] = lc;
+      b_last[r] = ls == ns - 1;
+      if constexpr (csr) {
+        const int e = b_j0[r] / p.block;
+        b_off[r] = __builtin_amdgcn_readfirstlane((tbl[e - blk0] - e) * p.block);
+      }
+      if (++ls == ns) enter(claim());
+    } else {
+      b_j0[r] = kstart;
+      b_end[r] = kstart + 1;
+      b_ch[r] = -1;
+      b_last[r] = false;
+    }
+    // rows of the sub-tile (a 16-key sub-tile lies inside one block)
+    const int pj = min(b_j0[r] + b_off[r], p.cap - 1);
+    const int pl = min(min(b_end[r] - 1, b_j0[r] + 15) + b_off[r], p.cap - 1);
+    tile.template load_kv<r>(kb, vb, pj, pl, H, lane);
+  };
   // ---- finish the query (and the append) before streaming --------------------
   // The query and rotary rows are isolated lines: issued behind the key/value
   // stream of the whole grid they would wait for most of it, so every wave
@@ -1164,55 +1224,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     tile.template pv<BUF>(pr, ident);
   };
 
-  // ---- streaming: chunks claimed by the two waves of the pair ----------------
-  // Chunk sub-tiles go through a ring of R register buffers; the load of the
-  // sub-tile R - 1 places ahead is issued before a sub-tile is computed, and
-  // the next chunk is claimed when the loads reach the end of the current one.
-  // Loads are issued on every step (past the end they re-read a valid row), so
-  // every path between a load and its use issues the same loads.
-  auto claim = [&]() -> int {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&s_claim[jp], 1);
-    v = __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
-    return v < claimable ? v : nch;
-  };
-  // next load: chunk lc, its keys [ca, ce), sub-tile ls of ns
-  int lc = nch, ls = 0, ca = 0, ce = 0, ns = 0;
-  auto enter = [&](int ch) {
-    lc = ch;
-    ls = 0;
-    ca = lo + ch * csz;
-    ce = min(ca + csz, lo + len);
-    ns = (ce - ca + 15) / 16;
-  };
-  if (live) enter(appender ? nch - 1 : claim());
-  // b_off: cache row minus key index in the sub-tile (CSR block keys; else 0)
-  int b_j0[R], b_end[R], b_ch[R], b_off[R];
-  bool b_last[R];
-  auto next_load = [&](auto rt) {
-    constexpr int r = decltype(rt)::value;
-    b_off[r] = 0;
-    if (lc < nch) {
-      b_j0[r] = ca + 16 * ls;
-      b_end[r] = ce;
-      b_ch[r] = lc;
-      b_last[r] = ls == ns - 1;
-      if constexpr (csr) {
-        const int e = b_j0[r] / p.block;
-        b_off[r] = __builtin_amdgcn_readfirstlane((tbl[e - blk0] - e) * p.block);
-      }
-      if (++ls == ns) enter(claim());
-    } else {
-      b_j0[r] = kstart;
-      b_end[r] = kstart + 1;
-      b_ch[r] = -1;
-      b_last[r] = false;
-    }
-    // rows of the sub-tile (a 16-key sub-tile lies inside one block)
-    const int pj = min(b_j0[r] + b_off[r], p.cap - 1);
-    const int pl = min(min(b_end[r] - 1, b_j0[r] + 15) + b_off[r], p.cap - 1);
-    tile.template load_kv<r>(kb, vb, pj, pl, H, lane);
-  };
   // the chunk's (m, l, o) into its LDS record; the state restarts
   auto flush = [&](int ch) {
     mfma_result_fence();
@@ -1252,107 +1263,111 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   __syncthreads();
 
   // ---- merge the pair's chunks in chunk order: output or the pair's partial --
-  if (!live) return;
   const int t = younger * 64 + lane;
   constexpr int NQD = HP / 4;
+  const __amdgpu_buffer_rsrc_t part = partial_rsrc(p, RS);
+  if (live) {
+    for (int e = t; e < nh * NQD; e += 2 * 64) {
+      const int hj = e / NQD, d = 4 * (e % NQD);
+      if (d >= H) continue;
+      const float* base = pair_part + hj * RS;
+      float M = kNegInf;
+      for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, base[ch * nh * RS]);
+      const float Mu = (M == kNegInf) ? 0.f : M;
+      float L = 0.f;
+      float4v O = {0.f, 0.f, 0.f, 0.f};
+      for (int ch = 0; ch < nch; ++ch) {
+        const float* row = base + ch * nh * RS;
+        const float f = fast_exp2(row[0] - Mu);
+        L += row[1] * f;
+        O += *reinterpret_cast<const float4v*>(row + 4 + d) * f;
+      }
+      const int hq = h0 + hj;
+      if constexpr (kQuant) {
+        // value scales, and the 2^12 of the probabilities
+        const float u = 1.f / Tile::kPScale;
+        if (p.v_scale_pc) O *= *reinterpret_cast<const float4v*>(p.v_scale + (int64_t)kvh * H + d) * u;
+        else O *= p.v_scale[0] * u;
+      }
+      if (direct) {
+        bool has;
+        const float sg = read_sink<AT>(p, hq, has);
+        const float inv = final_scale(M, L, has, sg);
+        const float v[4] = {O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
+        Q4::store(static_cast<AT*>(p.out) + ((int64_t)b * p.N + hq) * H + d, v);
+      } else {
+        const int rec = ((pr * p.hpw + hj) * RS) * 4;  // byte offset of the record
+        if (d == 0) store_partial_ml(part, rec, M, L);
+        store_partial_o(part, rec + (4 + d) * 4, O);
+      }
+    }
+  }
+
+  // ---- arrival: the last pair of a split unit merges the unit's partials ------
+  // The partials are written through to the device-coherent level (no L2
+  // write-back of the whole cache is needed); each wave waits for its stores
+  // to complete before the group barrier, then one lane per pair counts the
+  // pair in.  The counter goes back to zero when the unit is merged, so the
+  // next call finds it so.
+  __shared__ int s_last[kPairsPerGroup];
+  const bool split = live && !direct;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's partial stores are done
+  __syncthreads();
+  const int unit = b * ups + ui;
+  if (!younger && lane == 0) {
+    int last = 0;
+    if (split)
+      last = __hip_atomic_fetch_add(p.counters + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nb - 1;
+    s_last[jp] = last;
+  }
+  __syncthreads();
+  if (!s_last[jp]) return;
+  const int pair0 = first + ui * nb;
+  const int rstride = p.hpw * RS * 4;  // bytes between the unit's pair records
   for (int e = t; e < nh * NQD; e += 2 * 64) {
     const int hj = e / NQD, d = 4 * (e % NQD);
     if (d >= H) continue;
-    const float* base = pair_part + hj * RS;
-    float M = kNegInf;
-    for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, base[ch * nh * RS]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    float L = 0.f;
+    const int base = ((pair0 * p.hpw + hj) * RS) * 4;
+    // records in batches of kMergeBatch, all loads of a batch in flight at
+    // once (each is a round trip to the shared level); the running (M, L, O)
+    // is rescaled once per batch
+    float M = kNegInf, L = 0.f;
     float4v O = {0.f, 0.f, 0.f, 0.f};
-    for (int ch = 0; ch < nch; ++ch) {
-      const float* row = base + ch * nh * RS;
-      const float f = fast_exp2(row[0] - Mu);
-      L += row[1] * f;
-      O += *reinterpret_cast<const float4v*>(row + 4 + d) * f;
+    for (int i0 = 0; i0 < nb; i0 += kMergeBatch) {
+      float2v mlb[kMergeBatch];
+      float4v ob[kMergeBatch];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const int rec = base + min(i0 + k, nb - 1) * rstride;
+        mlb[k] = load_partial_ml(part, rec);
+        ob[k] = load_partial_o(part, rec + (4 + d) * 4);
+      }
+      float mn = M;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k)
+        if (i0 + k < nb) mn = fmaxf(mn, mlb[k][0]);
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      const float fo = fast_exp2(M - mu);
+      L *= fo;
+      O *= fo;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k)
+        if (i0 + k < nb) {
+          const float f = fast_exp2(mlb[k][0] - mu);
+          L += mlb[k][1] * f;
+          O += ob[k] * f;
+        }
+      M = mn;
     }
     const int hq = h0 + hj;
-    if constexpr (kQuant) {
-      // value scales, and the 2^12 of the probabilities
-      const float u = 1.f / Tile::kPScale;
-      if (p.v_scale_pc) O *= *reinterpret_cast<const float4v*>(p.v_scale + (int64_t)kvh * H + d) * u;
-      else O *= p.v_scale[0] * u;
-    }
-    if (direct) {
-      bool has;
-      const float sg = read_sink<AT>(p, hq, has);
-      const float inv = final_scale(M, L, has, sg);
-      const float v[4] = {O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
-      Q4::store(static_cast<AT*>(p.out) + ((int64_t)b * p.N + hq) * H + d, v);
-    } else {
-      float* rec = p.part + ((int64_t)pr * p.hpw + hj) * RS;
-      if (d == 0) *reinterpret_cast<float2v*>(rec) = float2v{M, L};
-      *reinterpret_cast<float4v*>(rec + 4 + d) = O;
-    }
-  }
-}
-
-// Merge the partials of one (sample, query head): every thread merges one
-// quad of dims over a stride of the partials in one pass (running maximum),
-// and the strides are merged in LDS.
-template <typename T, int HP, bool CSR>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
-  constexpr int NQD = HP / 4;            // quads of a padded head
-  constexpr int NG = 256 / NQD;          // partial strides
-  __shared__ float4v acc_s[NG][NQD];
-  __shared__ float2v ml_s[NG];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int g = p.N / p.kvN, hg = p.head_groups, ups = p.kvN * hg;
-  const int64_t quota = deal_quota<CSR>(p, ups, lane, lane < p.B ? sample_count<CSR>(p, lane) : 0);
-  const int c = sample_count<CSR>(p, b);
-  const int nb = pairs_for(c, quota);
-  if (unit_direct(c, nb)) return;  // written directly
-  const int first = sample_first_pair<CSR>(p, ups, quota, b, lane);
-  const int kvh = h / g, hgrp = (h % g) / 16, hh = (h % g) % 16;
-  const int pair0 = first + (kvh * hg + hgrp) * nb;
-  const int wb = nb;  // one partial per pair of the unit
-  auto rec = [&](int i) { return p.part + ((int64_t)(pair0 + i) * p.hpw + hh) * (HP + 4); };
-
-  // One pass: thread (dq, gs) merges the partials gs, gs + NG, ... of its quad
-  // of dims online (running max); the NG strides are then merged in LDS.
-  const int dq = tid % NQD, gs = tid / NQD;
-  const bool dq_ok = 4 * dq < p.H;
-  float Ms = kNegInf, Ls = 0.f;
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int i = gs; i < wb; i += NG) {
-    const float* r = rec(i);
-    const float2v ml = *reinterpret_cast<const float2v*>(r);
-    const float4v o4 = dq_ok ? *reinterpret_cast<const float4v*>(r + 4 + 4 * dq) : float4v{0.f, 0.f, 0.f, 0.f};
-    const float mn = fmaxf(Ms, ml[0]);
-    const float mu = (mn == kNegInf) ? 0.f : mn;
-    const float fa = fast_exp2(Ms - mu), fb = fast_exp2(ml[0] - mu);
-    Ls = Ls * fa + ml[1] * fb;
-    acc = acc * fa + o4 * fb;
-    Ms = mn;
-  }
-  acc_s[gs][dq] = acc;
-  if (dq == 0) ml_s[gs] = float2v{Ms, Ls};
-  __syncthreads();
-  if (tid < NQD && dq_ok) {
-    float M = kNegInf;
-#pragma unroll
-    for (int s = 0; s < NG; ++s) M = fmaxf(M, ml_s[s][0]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    float L = 0.f;
-    float4v o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NG; ++s) {
-      const float f = fast_exp2(ml_s[s][0] - Mu);
-      L += ml_s[s][1] * f;
-      o += acc_s[s][tid] * f;
-    }
     bool has;
-    const float sg = read_sink<T>(p, h, has);
+    const float sg = read_sink<AT>(p, hq, has);
     const float inv = final_scale(M, L, has, sg);
-    const float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-    Quad<T>::store(static_cast<T*>(p.out) + ((int64_t)b * p.N + h) * p.H + 4 * tid, v);
+    const float v[4] = {O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
+    Q4::store(static_cast<AT*>(p.out) + ((int64_t)b * p.N + hq) * H + d, v);
   }
+  if (t == 0) __hip_atomic_store(p.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int HP, int FEAT>
@@ -1378,15 +1393,6 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   return launch_decode_f<T, HP, 0>(p, s);
 }
 
-template <typename T, int HP>
-hipError_t launch_combine_t(const DecodeParams& p, hipStream_t s) {
-  if (p.csr_rp != nullptr)
-    hipLaunchKernelGGL((decode_combine_kernel<T, HP, true>), dim3(p.N, p.B), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((decode_combine_kernel<T, HP, false>), dim3(p.N, p.B), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s) {
@@ -1409,20 +1415,6 @@ hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s)
   if (hp == 64) return launch_decode_t<float, 64>(p, s);
   if (hp == 128) return launch_decode_t<float, 128>(p, s);
   return launch_decode_t<float, 256>(p, s);
-}
-
-// Merges the units that more than one wave served (the others return at once).
-// The partials are float32 for every cache type; Q8 merges as F32.
-hipError_t launch_decode_combine(DType dt, int hp, const DecodeParams& p, hipStream_t s) {
-  if (p.B == 0) return hipSuccess;
-  if (dt == DType::F16) {
-    if (hp == 64) return launch_combine_t<f16, 64>(p, s);
-    if (hp == 128) return launch_combine_t<f16, 128>(p, s);
-    return launch_combine_t<f16, 256>(p, s);
-  }
-  if (hp == 64) return launch_combine_t<float, 64>(p, s);
-  if (hp == 128) return launch_combine_t<float, 128>(p, s);
-  return launch_combine_t<float, 256>(p, s);
 }
 
 }  // namespace kvattn

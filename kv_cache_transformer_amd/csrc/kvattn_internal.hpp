@@ -86,7 +86,7 @@ struct CopyPastParams {
 
 // ---------------------------------------------------------------------------
 // K3 decode: one query token per sample against a BNSH cache, split over the
-// key axis with a log-sum-exp combine.
+// key axis with a log-sum-exp combine done by the last pair of each unit.
 // ---------------------------------------------------------------------------
 struct DecodeParams {
   const void* q;            // (B, N*H)
@@ -115,7 +115,9 @@ struct DecodeParams {
   int win_cap;              // > 0: sliding-window cache of this capacity (len_mode 0 only)
   void* out;                // (B, N*H)
   void* qk;                 // (B, N, 1, host_n) scores after mask, or null
-  float* part;              // (waves, hpw, HP + 4) per-wave partials: m, l, -, -, o[HP]
+  float* part;              // (waves / 2, hpw, HP + 4) per-pair partials: m, l, -, -, o[HP]
+  int* counters;            // (B * kvN * head_groups) arrivals per unit: zero on entry, left zero
+  int split;                // 0: every unit gets one pair (no counters are touched)
   int B, N, kvN, H, cap;
   float scale, softcap;
   int head_groups;          // query-head groups of <= 16 per kv head
@@ -216,7 +218,6 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s);
 hipError_t launch_copy_past(DType dt, const CopyPastParams& p, hipStream_t s);
 hipError_t launch_window_shift(DType dt, const WindowShiftParams& p, hipStream_t s);
 hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s);
-hipError_t launch_decode_combine(DType dt, int hp, const DecodeParams& p, hipStream_t s);
 hipError_t launch_flash(DType dt, int hp, const FlashParams& p, int grid_x, int grid_y,
                         int grid_z, hipStream_t s);
 hipError_t launch_packed_sched(const PackedSchedParams& p, hipStream_t s);

@@ -43,6 +43,19 @@ def test_version_and_status_strings(lib):
     assert lib.kvattn_status_string(-2) == b"unsupported"
 
 
+def test_decode_split_setting(lib):
+    assert lib.kvattn_set_decode_split(4) == 0
+    assert lib.kvattn_set_decode_split(33) == kb_ERR_INVALID   # rejected, unchanged
+    assert lib.kvattn_set_decode_split(0) == 4
+    assert lib.kvattn_set_decode_split(-1) == kb_ERR_INVALID
+    assert lib.kvattn_set_decode_split(0) == 0
+
+
+kb_ERR_INVALID = -1
+# every non-empty workspace starts with the decode arrival counters
+COUNTER_BYTES = 32768
+
+
 def test_attribute_defaults(lib):
     a = kb.GqaAttrs()
     a.causal = 7
@@ -107,7 +120,7 @@ def test_gqa_valid_shapes_give_workspace(lib):
     assert rc == 0 and size == 0
     ins, outs = gqa_args(past="shared", S=1, cap=4096)
     rc, size, _ = gqa_call(lib, ins, outs, total=4000)
-    assert rc == 0 and size > 0        # split-key partials
+    assert rc == 0 and size > COUNTER_BYTES        # arrival counters, then split-key partials
     c = T(F16, 64, 32)
     ins, outs = gqa_args(slots={6: c, 7: T(F16, 64, 32)})
     rc, size, _ = gqa_call(lib, ins, outs, do_rotary=1)
@@ -171,7 +184,7 @@ def test_gqa_quant_validation(lib):
         ins, outs, at = quant_args(bits=bits)
         rc, size, msg = gqa_call(lib, ins, outs, **at)
         assert rc == 0, msg
-        assert size == 2 * align(2 * 2 * 16 * 64 * 4)
+        assert size == COUNTER_BYTES + 2 * align(2 * 2 * 16 * 64 * 4)
     ins, outs, at = quant_args(past="shared", S=1, cap=4096, kpc=True)
     rc, size, msg = gqa_call(lib, ins, outs, total=4000, **at)   # int8 decode, shared buffer
     assert rc == 0 and size > 0, msg

@@ -105,6 +105,58 @@ def test_decode_repeat_is_deterministic():
     np.testing.assert_array_equal(o1, o2)
 
 
+# Split-key decode (GroupQueryAttention page, Implementation variants: cached
+# decode partitioned along the key axis, partial online-softmax results
+# merged): one fixed input at several split targets, from one pair of waves
+# per (sample, kv head) unit (no merge) to many pairs per unit, every output
+# against the oracle.
+SPLITS = [1, 2, 8, 32]
+
+
+def test_decode_split_count_sweep():
+    import kv_cache_transformer_amd as kv
+    case = wl.gqa_decode()
+    ref, rpk, rpv = gqa_oracle(case)
+    outs = {}
+    try:
+        for w in SPLITS:
+            kv.set_decode_split(w)
+            print(f"gqa_decode at {w} waves per compute unit", flush=True)
+            out, pk, pv = gqa_gpu(case)
+            check_output(out, ref, np.float16, f"output at split {w}")
+            check_cache(pk, rpk, gqa_transformed_rows(case), "present_key")
+            check_cache(pv, rpv, None, "present_value")
+            outs[w] = out
+    finally:
+        kv.set_decode_split(0)
+    for w in SPLITS[1:]:
+        print(f"split {w} vs 1: {int(np.sum(outs[w] != outs[1]))} elements differ in the last bit(s)")
+
+
+def test_decode_workspace_reuse_leaves_counters_zero():
+    """Decode calls keep per-unit arrival counters in the workspace and leave
+    them zero: one zero-filled workspace serves a sequence of calls of
+    different shapes, each checked against the oracle."""
+    import torch
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda:0")
+    specs = [(DECODE[0], 310), (DECODE[7], 311), (DECODE[8], 312), (DECODE[0], 310)]
+    for spec, seed in specs:
+        case = _case(dict(spec, S=1), seed)
+        out, _, _ = gqa_gpu(case, workspace=ws)
+        ref, _, _ = gqa_oracle(case)
+        check_output(out, ref, case["inputs"]["query"].dtype)
+        # the first 32 KiB hold the counters (one int32 per split unit); the
+        # partials follow them
+        assert int(torch.count_nonzero(ws[:32768])) == 0, f"counters left non-zero after {spec}"
+
+
+def test_decode_split_setting_is_validated():
+    import kv_cache_transformer_amd as kv
+    with pytest.raises(kv.KvattnError):
+        kv.set_decode_split(33)
+    assert kv.set_decode_split(0) == 0
+
+
 def test_workload_gqa_prompt_small():
     case = wl.gqa_prompt_small()
     print("gqa_prompt_small", flush=True)
