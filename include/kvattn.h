@@ -260,6 +260,26 @@ int32_t gqa_attention(const gqa_attrs* attrs,
                       const kvattn_tensor* outputs, int32_t n_outputs,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gqa_attention_noalloc — gqa_attention for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments and results as gqa_attention,
+ * without the workspace: the library keeps KVATTN_NOALLOC_SCRATCH_BYTES of
+ * device memory per GPU (a static array, held until the process ends) and
+ * uses it as the workspace.  The first call on a device looks that array up
+ * and clears its arrival counters on `stream`; no call allocates or frees.
+ * Calls whose workspace would exceed the scratch (gqa_attention_workspace_size
+ * tells) return KVATTN_ERR_WORKSPACE before any launch.  Every call on a GPU
+ * shares that GPU's scratch: calls that may overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ */
+#define KVATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int32_t gqa_attention_noalloc(const gqa_attrs* attrs,
+                              const kvattn_tensor* inputs, int32_t n_inputs,
+                              int32_t total_sequence_length,
+                              const kvattn_tensor* outputs, int32_t n_outputs,
+                              void* stream);
+
 /* Workspace bytes gqa_attention needs for these arguments (validates them). */
 int32_t gqa_attention_workspace_size(const gqa_attrs* attrs,
                                      const kvattn_tensor* inputs, int32_t n_inputs,

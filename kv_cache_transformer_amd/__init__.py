@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     KvattnError,
     decode_mha,
     gqa_attention,
+    gqa_attention_noalloc,
     library,
     library_path,
     packed_attention,
@@ -31,6 +32,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "KvattnError",
     "gqa_attention",
+    "gqa_attention_noalloc",
     "decode_mha",
     "sparse_attention",
     "packed_attention",

@@ -85,6 +85,8 @@ def library():
         lib.kvattn_version.restype = i32
         lib.gqa_attention.restype = i32
         lib.gqa_attention.argtypes = [ctypes.POINTER(GqaAttrs), _PT, i32, i32, _PT, i32, vp, sz, vp]
+        lib.gqa_attention_noalloc.restype = i32
+        lib.gqa_attention_noalloc.argtypes = [ctypes.POINTER(GqaAttrs), _PT, i32, i32, _PT, i32, vp]
         lib.gqa_attention_workspace_size.restype = i32
         lib.gqa_attention_workspace_size.argtypes = [ctypes.POINTER(GqaAttrs), _PT, i32, i32, _PT, i32, _SZ]
         lib.decode_mha.restype = i32
@@ -198,6 +200,54 @@ def gqa_attention(query, key, value, past_key=None, past_value=None, seqlens_k=N
     the caches are int8 / packed uint8 tensors and ``k_scale``/``v_scale``
     float32 tensors.  Returns (output, present_key, present_value).
     """
+    a, ins, outs, output, present_key, present_value = _gqa_args(
+        query, key, value, past_key, past_value, seqlens_k, total_sequence_length, cos_cache,
+        sin_cache, attention_bias, head_sink, q_norm_weight, k_norm_weight, k_scale, v_scale,
+        num_heads, kv_num_heads, causal, do_rotary, local_window_size, qk_norm_epsilon, scale,
+        smooth_softmax, softcap, sliding_window_cache, k_quant_type, v_quant_type,
+        kv_cache_bit_width, output, present_key, present_value)
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.gqa_attention_workspace_size(ctypes.byref(a), ins, GQA_NUM_INPUTS,
+                                            int(total_sequence_length), outs, GQA_NUM_OUTPUTS,
+                                            ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, query.device, workspace)
+    _check(lib.gqa_attention(ctypes.byref(a), ins, GQA_NUM_INPUTS, int(total_sequence_length),
+                             outs, GQA_NUM_OUTPUTS, _ptr(ws), wsb, _stream(stream, query.device)))
+    return output, present_key, present_value
+
+
+def gqa_attention_noalloc(query, key, value, past_key=None, past_value=None, seqlens_k=None,
+                          total_sequence_length=None, cos_cache=None, sin_cache=None,
+                          attention_bias=None, head_sink=None, q_norm_weight=None,
+                          k_norm_weight=None, k_scale=None, v_scale=None,
+                          *, num_heads, kv_num_heads, causal=1, do_rotary=0,
+                          local_window_size=-1, qk_norm_epsilon=1e-6, scale=0.0,
+                          smooth_softmax=-1, softcap=0.0, sliding_window_cache=0,
+                          k_quant_type=0, v_quant_type=0, kv_cache_bit_width=0,
+                          output=None, present_key=None, present_value=None, stream=None):
+    """GroupQueryAttention with the library's own scratch as the workspace
+    (include/kvattn.h, gqa_attention_noalloc): arguments as gqa_attention
+    without ``workspace``.  Returns (output, present_key, present_value)."""
+    a, ins, outs, output, present_key, present_value = _gqa_args(
+        query, key, value, past_key, past_value, seqlens_k, total_sequence_length, cos_cache,
+        sin_cache, attention_bias, head_sink, q_norm_weight, k_norm_weight, k_scale, v_scale,
+        num_heads, kv_num_heads, causal, do_rotary, local_window_size, qk_norm_epsilon, scale,
+        smooth_softmax, softcap, sliding_window_cache, k_quant_type, v_quant_type,
+        kv_cache_bit_width, output, present_key, present_value)
+    _check(library().gqa_attention_noalloc(ctypes.byref(a), ins, GQA_NUM_INPUTS,
+                                           int(total_sequence_length), outs, GQA_NUM_OUTPUTS,
+                                           _stream(stream, query.device)))
+    return output, present_key, present_value
+
+
+def _gqa_args(query, key, value, past_key, past_value, seqlens_k, total_sequence_length,
+              cos_cache, sin_cache, attention_bias, head_sink, q_norm_weight, k_norm_weight,
+              k_scale, v_scale, num_heads, kv_num_heads, causal, do_rotary, local_window_size,
+              qk_norm_epsilon, scale, smooth_softmax, softcap, sliding_window_cache, k_quant_type,
+              v_quant_type, kv_cache_bit_width, output, present_key, present_value):
+    """Attribute struct and descriptor arrays of a gqa_attention call;
+    allocates the output and the presents when they are not given."""
     torch = _torch()
     lib = library()
     B, S, _ = query.shape
@@ -227,14 +277,7 @@ def gqa_attention(query, key, value, past_key=None, past_value=None, seqlens_k=N
                   _desc(head_sink), _desc(k_scale), _desc(v_scale), _desc(q_norm_weight),
                   _desc(k_norm_weight)])
     outs = _array([_desc(output), _desc(present_key), _desc(present_value)])
-    nbytes = ctypes.c_size_t(0)
-    _check(lib.gqa_attention_workspace_size(ctypes.byref(a), ins, GQA_NUM_INPUTS,
-                                            int(total_sequence_length), outs, GQA_NUM_OUTPUTS,
-                                            ctypes.byref(nbytes)))
-    ws, wsb = _workspace(nbytes.value, query.device, workspace)
-    _check(lib.gqa_attention(ctypes.byref(a), ins, GQA_NUM_INPUTS, int(total_sequence_length),
-                             outs, GQA_NUM_OUTPUTS, _ptr(ws), wsb, _stream(stream, query.device)))
-    return output, present_key, present_value
+    return a, ins, outs, output, present_key, present_value
 
 
 def decode_mha(query, key, value, mask_index=None, attention_bias=None, past_key=None,

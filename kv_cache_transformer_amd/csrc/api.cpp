@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kvattn.h"
@@ -1045,6 +1046,49 @@ int check_ws(size_t need, void* ws, size_t bytes) {
   return KVATTN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Library-held scratch for gqa_attention_noalloc: a file-scope device array,
+// one copy per GPU, that serves as the workspace.  Host code never uses the
+// array's name as an address: each device's copy is looked up once, with that
+// device current, and kept in g_scratch_ptr.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)KVATTN_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Zero words [0, n) (the arrival counters); a kernel rather than a memset so
+// that a call captured into a graph records no memset node.
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The current device's scratch.  The first call on a device looks the array
+// up and clears its counter bytes on `st` (they start zero and every call
+// leaves them zero).
+int scratch_for_device(void** out, hipStream_t st) {
+  int dev = -1;
+  CHECK(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KVATTN_ERR_UNSUPPORTED, "gqa_attention_noalloc: device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    CHECK(hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (ptr == nullptr) return fail(KVATTN_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    const int words = (int)(kCounterBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st,
+                       static_cast<uint32_t*>(ptr), words);
+    CHECK(hip_status(hipGetLastError(), "scratch counter clear launch"));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVATTN_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -1126,6 +1170,22 @@ int32_t gqa_attention(const gqa_attrs* a, const kvattn_tensor* in, int32_t n_in,
   // no new token still copies the past rows into a separate present buffer
   if (P.B == 0 || (P.S == 0 && !(P.has_past && !P.shared))) return ok();
   return gqa_run(a, in, out, P, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t gqa_attention_noalloc(const gqa_attrs* a, const kvattn_tensor* in, int32_t n_in,
+                              int32_t total, const kvattn_tensor* out, int32_t n_out,
+                              void* stream) {
+  GqaPlan P{};
+  CHECK(gqa_validate(a, in, n_in, total, out, n_out, P));
+  if (P.ws_total > kScratchBytes)
+    return fail(KVATTN_ERR_WORKSPACE,
+                "gqa_attention_noalloc: this call needs %zu bytes of scratch, the library holds %zu "
+                "(use gqa_attention with a workspace)", P.ws_total, kScratchBytes);
+  if (P.B == 0 || (P.S == 0 && !(P.has_past && !P.shared))) return ok();
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (P.ws_total > 0) CHECK(scratch_for_device(&ws, st));
+  return gqa_run(a, in, out, P, ws, st);
 }
 
 int32_t decode_mha_workspace_size(const dmmha_attrs* a, const kvattn_tensor* in, int32_t n_in,

@@ -56,6 +56,24 @@ kb_ERR_INVALID = -1
 COUNTER_BYTES = 32768
 
 
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    # an int8 prompt whose dequantised rows (2 * B * kvN * S * H * 4 bytes)
+    # exceed the library's scratch: rejected on the host, before any launch
+    ins, outs, at = quant_args(bits=8, B=4, S=1024, kvN=8, N=32, H=128, cap=1024)
+    a = kb.GqaAttrs()
+    lib.gqa_attrs_default(ctypes.byref(a))
+    a.num_heads, a.kv_num_heads = 32, 8
+    for k, v in at.items():
+        setattr(a, k, v)
+    rc = lib.gqa_attention_noalloc(ctypes.byref(a), kb._array(ins), len(ins), 1024,
+                                   kb._array(outs), len(outs), None)
+    assert rc == -3 and b"scratch" in lib.kvattn_last_error()
+    size = ctypes.c_size_t(0)
+    assert lib.gqa_attention_workspace_size(ctypes.byref(a), kb._array(ins), len(ins), 1024,
+                                            kb._array(outs), len(outs), ctypes.byref(size)) == 0
+    assert size.value > 16 << 20
+
+
 def test_attribute_defaults(lib):
     a = kb.GqaAttrs()
     a.causal = 7

@@ -1,0 +1,67 @@
+"""gqa_attention_noalloc (the allocation-free variant of gqa_attention, whose
+workspace is the library's own per-GPU scratch) against gqa_attention on the
+same inputs: two decode calls in a row, the second smaller, and a quantised
+prompt, which also uses the scratch.  The same kernels run with the same
+split, so outputs and caches must agree bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_transformer_amd as kv
+from kv_cache_transformer_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _run(fn, case, **extra):
+    i, a = case["inputs"], case["attrs"]
+    t = {k: _dev(v) for k, v in i.items()}
+    if case.get("shared"):
+        pk, pv = t["past_key"], t["past_value"]
+    else:
+        pk, pv = t["present_key"], t["present_value"]
+    out, pk, pv = fn(t["query"], t["key"], t["value"], t.get("past_key"), t.get("past_value"),
+                     t["seqlens_k"], case["total_sequence_length"], t.get("cos_cache"),
+                     t.get("sin_cache"), t.get("attention_bias"), t.get("head_sink"),
+                     t.get("q_norm_weight"), t.get("k_norm_weight"), t.get("k_scale"),
+                     t.get("v_scale"), num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"],
+                     causal=a["causal"], do_rotary=a["do_rotary"],
+                     local_window_size=a["local_window_size"], qk_norm_epsilon=a["qk_norm_epsilon"],
+                     scale=a["scale"], smooth_softmax=a["smooth_softmax"], softcap=a["softcap"],
+                     k_quant_type=a.get("k_quant_type", 0), v_quant_type=a.get("v_quant_type", 0),
+                     kv_cache_bit_width=a.get("kv_cache_bit_width", 0), present_key=pk,
+                     present_value=pv, **extra)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), pk.cpu().numpy(), pv.cpu().numpy()
+
+
+def _same(case, what):
+    print(what, flush=True)
+    ref = _run(kv.gqa_attention, case)
+    got = _run(kv.gqa_attention_noalloc, case)
+    for g, r, name in zip(got, ref, ("output", "present_key", "present_value")):
+        assert g.shape == r.shape and g.dtype == r.dtype, name
+        assert np.array_equal(g.view(np.uint8), r.view(np.uint8)), (
+            f"{what}: {name} differs in {int(np.sum(g != r))} elements")
+
+
+def test_noalloc_matches_gqa_attention_on_consecutive_calls():
+    # the full decode workload (B16, cache 4096): split units, arrival counters
+    _same(wl.gqa_decode(), "decode B16 N32 kvN8 H128, cache 4096")
+    # then a smaller decode on the same scratch
+    rng = np.random.default_rng(77)
+    small = wl.gqa_case(rng, dtype=np.float16, past="shared", B=3, S=1, N=32, kvN=8, H=128,
+                        cap=600, past_lens=[1, 300, 599], rotary=True)
+    _same(small, "decode B3, cache 600")
+    # a quantised prompt (its dequantised rows live in the scratch)
+    rng = np.random.default_rng(78)
+    q = wl.gqa_case(rng, dtype=np.float32, B=2, S=150, N=8, kvN=2, H=64,
+                    quant=dict(bits=8, k="channel", v="tensor"))
+    _same(q, "int8 prompt B2 S150")
