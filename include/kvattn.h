@@ -442,11 +442,13 @@ typedef struct packed_attrs {
 void packed_attrs_default(packed_attrs* attrs);
 
 /*
- * packed_attention — self-attention with a fused QKV projection over a
- * padding-removed token stream.
+ * packed_attention — self-attention over a batch whose padding has been
+ * removed (tokens of all sequences back to back), with the QKV projection
+ * done in the same call.
  *
- * qkv = input . weights + bias (columns [Q all heads | K all heads | V all
- * heads]); sequence b owns packed tokens [cum[b], cum[b+1]) and each token
+ * qkv = input . weights + bias (the weight columns hold Q for every head,
+ * then K for every head, then V); the tokens cum[b] .. cum[b+1] - 1 belong
+ * to sequence b and each token
  * attends every key of its own sequence (no mask); score = scale*q.k +
  * attention_bias[b|0, h|0, pad(t), pad(t')] with pad(t) = token_offset.flat[t]
  * - b*S; softmax; output (token_count, v_hidden) in packed order.
@@ -467,8 +469,8 @@ int32_t packed_attention_workspace_size(const packed_attrs* attrs,
 
 /*
  * kvattn_packed_schedule — the device schedule packed_attention builds from
- * cumulative_sequence_length (PackedAttention page, Inputs table: sequence i
- * owns packed tokens [cum[i], cum[i+1])), exposed so that it can be checked
+ * cumulative_sequence_length (PackedAttention page, Inputs table: the
+ * tokens cum[i] .. cum[i+1] - 1 belong to sequence i), exposed so that it can be checked
  * on its own.  All pointers are device int32 buffers:
  *   cum             (batch + 1)    input
  *   bounds          (batch, 2)     per sequence [start, end): cum clamped to

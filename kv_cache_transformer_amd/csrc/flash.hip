@@ -427,7 +427,10 @@ template <int MODE, int BN> struct FlashWork {
     tiles_per_block = 1;
     if (MODE == kCsr) {
       layout = h % p.num_layout;
-      const int rb = pmin / p.block;
+      // the row of the block's first query, clamped into the row pointers
+      // (a key total beyond max_blocks * block violates a precondition the
+      // host cannot check; the reads stay in bounds)
+      const int rb = min(max(pmin / p.block, 0), p.max_blocks - 1);
       csr_lo = max(p.rp[layout * p.rp_stride + rb], 0);
       const int csr_hi = min(p.rp[layout * p.rp_stride + rb + 1], (int)p.cols_stride);
       tiles_per_block = p.block > BN ? p.block / BN : 1;

@@ -8,8 +8,8 @@
 //     position) map.  All integer work, on the device, so the call never
 //     waits for the host.
 //   * QKV projection: qkv[T, q+k+v] = input[T, D] . weights[D, q+k+v] + bias
-//     (PackedAttention page, Inputs table: weights columns are [Q all heads |
-//     K all heads | V all heads]) as an MFMA GEMM with 128x128 output tiles,
+//     (PackedAttention page, Inputs table: the weight columns hold Q for
+//     every head, then K, then V) as an MFMA GEMM with 128x128 output tiles,
 //     LDS double buffering fed from register stages a few tiles ahead, and
 //     the bias added in an epilogue that goes through LDS so that the output
 //     is stored in 16-byte chunks.  The weights are row-major [D][cols], so

@@ -30,8 +30,8 @@ def dmmha(query, key, value, *, num_heads,
       attention only), plus ``mask_filter_value`` where ``mask_index[b, j]``
       is zero: the mask is additive and never removes a key.
     * Plain softmax over the attended keys, then the weighted sum of values.
-    * ``qk`` (cross attention with ``output_qk`` = 1) is the score row after
-      the mask and before the softmax, shape (B, N, 1, kv_S).
+    * ``qk`` (cross attention with ``output_qk`` = 1) is the score row once
+      the mask term is added, not yet normalised, shape (B, N, 1, kv_S).
 
     Returns ``(output float64 (B, 1, N*H), present_key, present_value, qk)``;
     the present arrays are None for cross attention, qk is None unless asked.

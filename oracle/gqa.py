@@ -17,7 +17,7 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
         num_heads, kv_num_heads, causal=1, do_rotary=0, local_window_size=-1,
         qk_norm_epsilon=1e-6, scale=0.0, smooth_softmax=-1, softcap_value=0.0,
         sliding_window_cache=0, k_scale=None, v_scale=None, k_quant_type=0, v_quant_type=0,
-        kv_cache_bit_width=0, query_rows=None, info=None):
+        kv_cache_bit_width=0, query_rows=None, info=None, stored_key_codes=None):
     """Grouped-query attention with a BNSH key/value cache.
 
     Follows the GroupQueryAttention page: Description, Inputs, Outputs and
@@ -57,12 +57,13 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
        ``smooth_softmax`` = 1 and no sink is given) adds exp(sink) to the
        denominator only.  Output is the weighted sum of values, BSH layout.
 
-    With ``sliding_window_cache`` = 1 (Attributes table: the caches are
-    fixed-size window buffers that evict old tokens from the front; needs
-    ``local_window_size`` > 0 and enough capacity; Implementation variants: the
-    window-shift pass compacts surviving rows and appends the chunk, and
-    attention keeps both the window floor and the causal bound) steps 2 and 5
-    read, for cache capacity C:
+    With ``sliding_window_cache`` = 1 (Attributes table: the past and present
+    buffers have a fixed capacity and the oldest tokens leave at the front;
+    the attribute requires ``local_window_size`` > 0 and a capacity that is
+    large enough; Implementation variants: a shift step moves the rows that
+    stay to the start of the buffer, the new chunk is written after them, and
+    the attention applies the window's lower bound as well as the causal one)
+    steps 2 and 5 read, for cache capacity C:
 
     2'. The buffer holds the most recent tokens, oldest first: before the call
         rows [0, F_b) with F_b = min(total_b - S, C).  Query s still sits at
@@ -83,6 +84,13 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
     is a dict it receives ``k_quotient`` and ``v_quotient``, the float32
     quotients of the new rows (B, kvN, S, H), from which a caller can tell how
     close each code is to a rounding boundary.
+
+    ``stored_key_codes`` (quantised caches only; optional) is a present_key
+    buffer whose new key rows replace the codes computed here before the
+    attention reads the cache.  A test passes the codes a kernel stored where
+    its float32 norm/rotary arithmetic put a quotient on the other side of a
+    rounding tie, so that the attention definition is evaluated on the cache
+    that kernel actually attended.
 
     ``query_rows`` (optional iterable of s indices) restricts the attention
     output to those query rows (the cache is always updated in full); the
@@ -153,7 +161,9 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
         raise ValueError("seqlens_k inconsistent with sequence length or cache capacity")
 
     sc = default_scale(scale, H)
-    q = q_in.astype(np.float64).reshape(B, S, N, H)
+    # only the query rows asked for are transformed (each row on its own)
+    rows = np.arange(S) if query_rows is None else np.asarray(list(query_rows), dtype=np.int64)
+    q = q_in.astype(np.float64).reshape(B, S, N, H)[:, rows]
     k = k_in.astype(np.float64).reshape(B, S, kvN, H)
     v = v_in.astype(np.float64).reshape(B, S, kvN, H)
 
@@ -173,7 +183,7 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
             raise ValueError("rotary position beyond the cos/sin cache")
         c = cos[pos][:, :, None, :]                          # (B, S, 1, H/2)
         s_ = sin[pos][:, :, None, :]
-        q = rotary(q, c, s_)
+        q = rotary(q, c[:, rows], s_[:, rows])
         k = rotary(k, c, s_)
 
     # present cache (materialised in T)
@@ -197,12 +207,13 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
                 info["k_quotient"][b] = quant.quotient(k[b].transpose(1, 0, 2), ks[:, None, :])
                 info["v_quotient"][b] = quant.quotient(v[b].transpose(1, 0, 2), vs[:, None, :])
             pk_out[b, :, pb:pb + S, :] = quant.store_codes(kc, bits)
+            if stored_key_codes is not None:
+                pk_out[b, :, pb:pb + S, :] = np.asarray(stored_key_codes)[b, :, pb:pb + S, :]
             pv_out[b, :, pb:pb + S, :] = quant.store_codes(vc, bits)
         else:
             pk_out[b, :, pb:pb + S, :] = round_to(k[b].transpose(1, 0, 2), dtype)
             pv_out[b, :, pb:pb + S, :] = round_to(v[b].transpose(1, 0, 2), dtype)
 
-    rows = np.arange(S) if query_rows is None else np.asarray(list(query_rows), dtype=np.int64)
     out = np.zeros((B, len(rows), N, H), dtype=np.float64)
     if head_sink is not None:
         sinks = np.asarray(head_sink, dtype=np.float64).reshape(N)
@@ -234,7 +245,7 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
             else:
                 keys = pk_out[b, kh, :n_keys, :].astype(np.float64)
                 vals = pv_out[b, kh, :n_keys, :].astype(np.float64)
-            x = sc * (q[b, rows, h, :] @ keys.T)
+            x = sc * (q[b, :, h, :] @ keys.T)
             x = softcap(x, softcap_value)
             if bias is not None:
                 bb = bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]

@@ -11,8 +11,8 @@ from .common import attend, default_scale
 def packed_schedule(cumulative_sequence_length, token_count):
     """Per packed token: owning sequence and position inside it.
 
-    PackedAttention page, Inputs table (``cumulative_sequence_length``:
-    sequence i owns packed tokens [cum[i], cum[i + 1])).  seq(t) is the b with
+    PackedAttention page, Inputs table (``cumulative_sequence_length``: the
+    packed tokens cum[i] .. cum[i + 1] - 1 belong to sequence i).  seq(t) is the b with
     cum[b] <= t < cum[b + 1]; pos(t) = t - cum[b].  Written as a plain scan.
     Returns two int32 arrays of length ``token_count``.
     """
@@ -34,11 +34,11 @@ def packed(input, weights, bias, token_offset, cumulative_sequence_length, *,
     Follows the PackedAttention page: Description, Inputs, Outputs and
     Attributes tables.
 
-    1. qkv = input @ weights + bias in float64, no rounding; columns are
-       [Q all heads | K all heads | V all heads].
+    1. qkv = input @ weights + bias in float64, no rounding; the columns
+       hold Q for every head, then K for every head, then V.
     2. Sizes come from ``qkv_hidden_sizes`` or, when omitted, bias length / 3;
        q_hidden must equal k_hidden.  Hq = q_hidden / N, Hv = v_hidden / N.
-    3. Sequence b owns packed tokens [cum[b], cum[b + 1]); a token attends
+    3. The packed tokens cum[b] .. cum[b + 1] - 1 form sequence b; a token attends
        every key of its own sequence and no other (there is no mask input).
     4. score = scale * q . k (+ attention_bias[b|0, h|0, pad(t), pad(t')]);
        the bias is indexed in padded coordinates, pad(t) = token_offset.flat[t]

@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 GroupQueryAttention page: Attributes table (``k_quant_type``,
 ``v_quant_type``: NONE, PER_TENSOR or PER_CHANNEL; ``kv_cache_bit_width``: 8
-or 4) and Inputs table (``k_scale``/``v_scale``: float32, one value for
-PER_TENSOR or ``kv_num_heads * head_size`` values for PER_CHANNEL; int4 cache
+or 4) and Inputs table (``k_scale``/``v_scale``: float32; a single scale
+with PER_TENSOR, ``kv_num_heads * head_size`` scales with PER_CHANNEL; int4 cache
 elements are +8-biased nibbles, two per byte, the even head coordinate in the
 low nibble).  The pages give no quantisation formula; the reading is the
 symmetric one: a cache value is code * scale, and a new value x is stored as

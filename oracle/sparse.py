@@ -71,7 +71,9 @@ def sparse(query, key, value, past_key, past_value, *, block_row_indices,
         v = np.asarray(value, dtype=np.float64)
     g = N // kvN
     bs = int(sparse_block_size)
-    q = q.reshape(B, S, N, H)
+    # only the query rows asked for are rotated (each row on its own)
+    rows = np.arange(S) if query_rows is None else np.asarray(list(query_rows), dtype=np.int64)
+    q = q.reshape(B, S, N, H)[:, rows]
     k = k.reshape(B, S, kvN, H)
     v = v.reshape(B, S, kvN, H)
     rp = np.asarray(block_row_indices)
@@ -90,7 +92,7 @@ def sparse(query, key, value, past_key, past_value, *, block_row_indices,
         sin = np.asarray(sin_cache, dtype=np.float64)
         c = cos[pos][:, :, None, :]
         s_ = sin[pos][:, :, None, :]
-        q = rotary(q, c, s_, interleaved=(rotary_interleaved == 1))
+        q = rotary(q, c[:, rows], s_[:, rows], interleaved=(rotary_interleaved == 1))
         k = rotary(k, c, s_, interleaved=(rotary_interleaved == 1))
     for b in range(B):
         pb = int(past_b[b])
@@ -98,7 +100,6 @@ def sparse(query, key, value, past_key, past_value, *, block_row_indices,
         pv[b, :, pb:pb + S, :] = round_to(v[b].transpose(1, 0, 2), dtype)
 
     sc = default_scale(scale, H)
-    rows = np.arange(S) if query_rows is None else np.asarray(list(query_rows), dtype=np.int64)
     out = np.zeros((B, len(rows), N, H))
     for b in range(B):
         n_keys = int(key_total[b])
@@ -118,7 +119,7 @@ def sparse(query, key, value, past_key, past_value, *, block_row_indices,
                 kh = h // g
                 keys = pk[b, kh, :n_keys].astype(np.float64)
                 vals = pv[b, kh, :n_keys].astype(np.float64)
-                x = sc * (q[b, rows, h, :] @ keys.T)
+                x = sc * (q[b, :, h, :] @ keys.T)
                 o, _ = attend(x, vis, vals)
                 out[b, :, h, :] = o
     return out.reshape(B, len(rows), N * H), pk, pv

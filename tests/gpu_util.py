@@ -9,7 +9,10 @@ Cache rows: copied rows (values, untouched and copied past rows, keys without
 norm/rotary) bit-exact; keys transformed by norm and/or rotary within 1 ulp of
 T (float16) of the float64 result rounded to T, plus 8 float32 ulps of the
 largest element of their row (the float32 arithmetic's error, which matters
-only where a pair cancels to a value far below its operands).
+only where a pair cancels to a value far below its operands).  For float16
+caches at most MAX_OFF_FRACTION of the transformed elements may differ from
+the oracle's rounding at all (a double rounding lands on the other side of a
+float16 tie only when the float32 result sits within its error of the tie).
 """
 
 import numpy as np
@@ -107,19 +110,25 @@ def check_cache(got, ref, transformed_rows=None, what="cache"):
     bad = tr & (err > lim)
     assert not bad.any(), (f"{what}: {int(bad.sum())} transformed elements beyond the bound "
                            f"(worst {float(np.max(np.where(tr, err - lim, -1))):.3g} over)")
-    return int(np.sum(d[tr] > 0))
+    n_off = int(np.sum(d[tr] > 0))
+    if got.dtype == np.float16:
+        n_tr = int(tr.sum())
+        assert n_off <= MAX_OFF_FRACTION * n_tr + 2, (
+            f"{what}: {n_off} of {n_tr} transformed elements differ from the oracle's rounding")
+    return n_off
 
 
 # ---------------------------------------------------------------------------
 # GroupQueryAttention
 # ---------------------------------------------------------------------------
-def gqa_oracle(case, query_rows=None, info=None):
+def gqa_oracle(case, query_rows=None, info=None, stored_key_codes=None):
     i = dict(case["inputs"])
     a = dict(case["attrs"])
     a["softcap_value"] = a.pop("softcap")
     return oracle.gqa(i.pop("query"), i.pop("key"), i.pop("value"),
                       total_sequence_length=case["total_sequence_length"],
-                      query_rows=query_rows, info=info, **i, **a)
+                      query_rows=query_rows, info=info, stored_key_codes=stored_key_codes,
+                      **i, **a)
 
 
 def gqa_gpu(case, workspace=None):
@@ -164,15 +173,23 @@ def gqa_new_rows(case):
 # oracle's quotient lies this close to a rounding boundary.
 QUANT_SLACK = 1e-3
 
+# Largest fraction of norm/rotary-transformed float16 cache elements allowed
+# to differ (by one ulp) from the float64 result rounded once: measured about
+# 2e-4 on the long prefill (normed and rotated keys), 1.5e-5 on the rotated
+# block-sparse keys.
+MAX_OFF_FRACTION = 1e-3
+
 
 def check_quant_gqa(case, got, ref, info, query_rows=None):
     """Compare a quantised-cache call: codes of values and of untransformed
     keys bit-exact; codes of normed/rotated keys bit-exact except within
     QUANT_SLACK of a rounding boundary, where they may differ by one; every
     other cache row untouched or copied exactly; the output within the float32
-    tolerance for every (sample, kv head) whose codes all match the oracle's
-    (the others depend on the tie's side and are only counted).  Returns the
-    number of codes taken on the other side of a near tie."""
+    tolerance everywhere: against the oracle for every (sample, kv head) whose
+    codes all match the oracle's, and for the others against the oracle
+    evaluated on the codes the kernel stored (the tie's side decides what the
+    attention reads).  Returns the number of codes taken on the other side of
+    a near tie."""
     from oracle import quant
     out, pk, pv = got
     rout, rpk, rpv = ref
@@ -211,8 +228,12 @@ def check_quant_gqa(case, got, ref, info, query_rows=None):
     o = o.reshape(o.shape[0], o.shape[1], N, H)
     r = rout.reshape(rout.shape[0], rout.shape[1], N, H)
     keep = np.repeat(~bad_units, N // kvN, axis=1)  # (B, N)
-    assert keep.mean() >= 0.9, "too many units off a near tie"
     check_output(o.transpose(0, 2, 1, 3)[keep], r.transpose(0, 2, 1, 3)[keep], np.float32)
+    if bad_units.any():
+        r2, _, _ = gqa_oracle(case, query_rows=query_rows, stored_key_codes=pk)
+        r2 = r2.reshape(r2.shape[0], r2.shape[1], N, H)
+        check_output(o.transpose(0, 2, 1, 3)[~keep], r2.transpose(0, 2, 1, 3)[~keep], np.float32,
+                     "output of units whose key codes sit across a near tie")
     return n_off
 
 

@@ -1,8 +1,8 @@
 """GPU parity of gqa_attention (prefill and decode paths) against the oracle.
 
 Small cases span several key tiles, ragged tails and every feature; the named
-workloads run at full size (the long prefill on sampled query rows, which the
-oracle computes one by one)."""
+workloads run at full size with every output element compared (the long
+prefill's oracle runs over row chunks in child processes)."""
 
 import numpy as np
 import pytest
@@ -170,14 +170,19 @@ def test_workload_gqa_decode():
     print(f"max |d| {err:.3g}; rotated key elements off by 1 ulp: {n1}")
 
 
-def test_workload_gqa_long_prefill_sampled_rows():
+def test_workload_gqa_long_prefill():
+    """The long prefill at full size (B4 S4096 N32 kvN8 H128, window 1024,
+    softcap, sink, q/k norm, rotary): every output element and every cache
+    row against the oracle, which runs over row chunks in child processes."""
+    import oracle_pool
     case = wl.gqa_long_prefill()
-    rng = np.random.default_rng(7)
-    rows = sorted(set([0, 1, 31, 32, 33, 1023, 1024, 1025, 1056, 2047, 2048, 3000, 4064, 4095]
-                      + rng.integers(0, 4096, 10).tolist()))
-    print("gqa_long_prefill rows", rows, flush=True)
-    err, n1 = _compare(case, rows)
-    print(f"max |d| {err:.3g}; normed+rotated key elements off by 1 ulp: {n1}")
+    print("gqa_long_prefill: GPU call, then the oracle over 16 row chunks", flush=True)
+    out, pk, pv = gqa_gpu(case)
+    ref, rpk, rpv = oracle_pool.gqa_full("gqa_long_prefill", 4096)
+    err = check_output(out, ref, np.float16)
+    n1 = check_cache(pk, rpk, gqa_transformed_rows(case), "present_key")
+    check_cache(pv, rpv, None, "present_value")
+    print(f"max |d| {err:.3g}; normed+rotated key elements off by 1 ulp: {n1} of {pk.size}")
 
 
 # Sliding-window cache (GroupQueryAttention page, Attributes table): shared

@@ -42,7 +42,7 @@ def test_dmmha_self_matches_brute(mask, bias, dtype):
     np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
     np.testing.assert_array_equal(pk, pkb)
     np.testing.assert_array_equal(pv, pvb)
-    # every row other than the appended one keeps its past value
+    # the append writes one row; all the others still hold the past cache
     keep = np.ones(9, bool)
     keep[5] = False
     np.testing.assert_array_equal(pk[:, :, keep], case["inputs"]["past_key"][:, :, keep])

@@ -205,6 +205,48 @@ def test_lossy_append_is_rounded_float_row():
     assert np.any(np.abs(v) / vs[0] > 128)    # the clamp was exercised
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_stored_key_codes_read_as_given(bits):
+    """stored_key_codes: attention over a present cache whose new key codes
+    are given equals attention over the cache those codes come from through
+    the input path (keys that are exact multiples of the scales, with the
+    chosen codes), and passing the oracle's own codes changes nothing."""
+    rng = np.random.default_rng(21 + bits)
+    B, S, N, kvN, H = 2, 5, 4, 2, 8
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    ks = _pow2_scales(rng, kvN, H, True)
+    vs = _pow2_scales(rng, kvN, H, False)
+    ksc = quant.channel_scales(ks, 2, kvN, H)
+    vsc = quant.channel_scales(vs, 1, kvN, H)
+    kc = rng.integers(lo + 1, hi, (B, S, kvN, H))
+    vc = rng.integers(lo, hi + 1, (B, S, kvN, H))
+    q = rng.standard_normal((B, S, N * H)).astype(np.float32)
+    v = (vc * vsc[None, None]).astype(np.float32).reshape(B, S, kvN * H)
+    hb = H if bits == 8 else H // 2
+    cdt = np.int8 if bits == 8 else np.uint8
+    common = dict(seqlens_k=np.full(B, S - 1, np.int32), total_sequence_length=S, num_heads=N,
+                  kv_num_heads=kvN, k_scale=ks, v_scale=vs, k_quant_type=2, v_quant_type=1,
+                  kv_cache_bit_width=bits)
+
+    def run(codes, stored=None):
+        k = (codes * ksc[None, None]).astype(np.float32).reshape(B, S, kvN * H)
+        return oracle.gqa(q, k, v, present_key=np.zeros((B, kvN, S, hb), cdt),
+                          present_value=np.zeros((B, kvN, S, hb), cdt), stored_key_codes=stored,
+                          **common)
+
+    out, pk, _ = run(kc)
+    again, _, _ = run(kc, stored=pk)
+    assert np.array_equal(again, out)
+    moved = kc.copy()
+    moved[1, 3, 0, 5] += 1                          # one code one step up
+    moved[0, 0, 1, 2] -= 1                          # and one down
+    want, wk, _ = run(moved)
+    got, gk, _ = run(kc, stored=wk)
+    assert np.array_equal(gk, wk)
+    assert np.array_equal(got, want)
+    assert not np.array_equal(got, out)
+
+
 def test_quant_argument_errors():
     B, S, N, kvN, H = 1, 2, 2, 1, 8
     q = np.zeros((B, S, N * H), np.float32)
