@@ -13,11 +13,21 @@ streams from HBM rather than from the 256 MB last-level cache.
 The other workloads (long prefill, small fp32 prompt, block-sparse prompt
 and token generation, packed varlen, sliding-window decode, int8 and packed
 int4 cache decode) are timed in the same run and reported under "workloads",
-each with its own roofline object.  Kernel durations come from HIP events
-that the library records around the kernel of interest
-(kvattn_profile_events); call durations from torch events on the same
-stream.  The CPU oracle is timed on a bounded sample of the decode workload
-("cpu_baseline").
+each with its own roofline object.
+
+Timing.  `ms_per_step` / `call_ms` come from a HIP graph of `steps` calls
+replayed between two events (no host launch overhead).  `eager_ms` holds
+p10 / p50 / p90 / mean over `steps` eager calls, each bracketed by torch
+events on the stream, with its dominant kernel bracketed by HIP events the
+library records on the same stream (kvattn_profile_events): kernel and call
+come from the same calls, so kernel <= call.  The roofline's `achieved` uses
+the eager kernel mean, which includes the kernel's dispatch (about 2 us more
+than rocprofv3's kernel duration).
+
+CPU baselines: the float64 oracle on the host, on whole decode passes for
+about 12 s (the headline's `cpu_baseline`), and on the full outputs of the
+long prefill, block-sparse prompt, small prompt and packed batch (their
+`cpu_baseline`); `--no-cpu` skips them.
 """
 
 import argparse
@@ -90,10 +100,15 @@ class HipEvents:
 
 
 class Timer:
-    """Dominant-kernel time from HIP events that the library records around
-    that kernel on eager calls, and step time from a HIP graph holding exactly
-    `steps` calls (replayed once untimed, then once between two events), so
-    that host launch overhead is not part of the step."""
+    """Per-call timing of one workload.
+
+    Eager calls: each call is bracketed by torch events on the current stream
+    and its dominant kernel by HIP events that the library records on the same
+    stream around that kernel's launch (kvattn_profile_events), so for every
+    call the kernel interval lies inside the call interval (kernel <= call).
+    Graph: the same number of calls captured in one HIP graph and replayed
+    between two events, so that host launch overhead is not part of the time
+    (the figure `value` is computed from)."""
 
     def __init__(self, torch, lib, kind, hip):
         self.torch, self.lib, self.kind, self.hip = torch, lib, kind, hip
@@ -105,14 +120,21 @@ class Timer:
         torch.cuda.synchronize()
         ks = [self.hip.create() for _ in range(steps)]
         ke = [self.hip.create() for _ in range(steps)]
+        cs = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         for i in range(steps):
+            cs[i].record()
             self.lib.kvattn_profile_events(ks[i], ke[i], self.kind)
             fn(warmup + i)
+            ce[i].record()
         self.lib.kvattn_profile_events(None, None, 0)
         torch.cuda.synchronize()
-        kern = [self.hip.elapsed_ms(ks[i], ke[i]) for i in range(steps)]
+        kern = np.array([self.hip.elapsed_ms(ks[i], ke[i]) for i in range(steps)])
+        call = np.array([cs[i].elapsed_time(ce[i]) for i in range(steps)])
         for e in ks + ke:
             self.hip.destroy(e)
+        if np.any(kern > call + 1e-3):
+            print("# warning: a kernel interval exceeds its call interval", file=sys.stderr)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(steps):
@@ -125,9 +147,21 @@ class Timer:
         graph.replay()
         c1.record()
         torch.cuda.synchronize()
-        call_ms = c0.elapsed_time(c1) / steps
+        graph_ms = c0.elapsed_time(c1) / steps
         del graph
-        return call_ms, float(np.mean(kern)), float(np.median(kern))
+        return dict(call_ms=graph_ms, kern_ms=float(np.mean(kern)), kern_samples=kern,
+                    call_samples=call)
+
+
+def eager_stats(r, scale=1.0, digits=4):
+    """p10 / p50 / p90 / mean of the eager per-call samples (kernel <= call per call)."""
+    def q(x):
+        x = np.asarray(x) * scale
+        return {"p10": round(float(np.percentile(x, 10)), digits),
+                "p50": round(float(np.median(x)), digits),
+                "p90": round(float(np.percentile(x, 90)), digits),
+                "mean": round(float(np.mean(x)), digits)}
+    return {"kernel": q(r["kern_samples"]), "call": q(r["call_samples"])}
 
 
 def decode_workload(torch, kv, wl, args, timer):
@@ -152,11 +186,11 @@ def decode_workload(torch, kv, wl, args, timer):
                          num_heads=a["num_heads"], kv_num_heads=a["kv_num_heads"],
                          do_rotary=1, output=out, present_key=pk, present_value=pv, workspace=ws)
 
-    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    tm = timer.run(step, args.steps, args.warmup)
     lens = i["seqlens_k"].astype(np.int64) + 1
     kvN, H = 8, 128
     kv_bytes = int(lens.sum()) * kvN * H * 2 * 2
-    return dict(case=case, call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med,
+    return dict(case=case, **tm,
                 kv_bytes=kv_bytes)
 
 
@@ -187,11 +221,11 @@ def decode_quant_workload(torch, kv, wl, args, timer, bits=8):
                          k_quant_type=2, v_quant_type=2, kv_cache_bit_width=bits,
                          output=out, present_key=pk, present_value=pv, workspace=ws)
 
-    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    tm = timer.run(step, args.steps, args.warmup)
     lens = i["seqlens_k"].astype(np.int64) + 1
     kvN, H = 8, 128
     kv_bytes = int(lens.sum()) * kvN * H * 2 * bits // 8   # K and V codes
-    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, kv_bytes=kv_bytes)
+    return dict(**tm, kv_bytes=kv_bytes)
 
 
 def window_decode_workload(torch, kv, wl, args, timer):
@@ -215,13 +249,13 @@ def window_decode_workload(torch, kv, wl, args, timer):
                          sliding_window_cache=1, output=out, present_key=t["past_key"],
                          present_value=t["past_value"], workspace=ws)
 
-    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    tm = timer.run(step, args.steps, args.warmup)
     B, kvN, H = 16, 8, 128
     cap = i["past_key"].shape[2]
     row = H * 2                                      # bytes of one fp16 row
     shift_bytes = B * kvN * 2 * (cap - 1) * row * 2  # K and V: read and written once
     read_bytes = B * kvN * 2 * cap * row             # rows attended (K and V)
-    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, shift_bytes=shift_bytes,
+    return dict(**tm, shift_bytes=shift_bytes,
                 read_bytes=read_bytes)
 
 
@@ -248,10 +282,10 @@ def prefill_workload(torch, kv, wl, args, timer):
                          softcap=a["softcap"], output=out, present_key=t["present_key"],
                          present_value=t["present_value"], workspace=ws)
 
-    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    tm = timer.run(step, args.steps, args.warmup)
     B, S, N, H = 4, 4096, 32, 128
     flops = 4 * H * causal_window_pairs(S, a["local_window_size"]) * B * N
-    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, flops=flops)
+    return dict(**tm, flops=flops)
 
 
 def prompt_small_workload(torch, kv, wl, args, timer):
@@ -267,9 +301,9 @@ def prompt_small_workload(torch, kv, wl, args, timer):
                          num_heads=8, kv_num_heads=2, scale=0.125, output=out,
                          present_key=t["present_key"], present_value=t["present_value"])
 
-    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    tm = timer.run(step, args.steps, args.warmup)
     flops = 4 * 64 * causal_window_pairs(128, -1) * 8
-    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, flops=flops)
+    return dict(**tm, flops=flops)
 
 
 def sparse_pairs(rp, cols, N, B, S, bs):
@@ -303,9 +337,9 @@ def sparse_workload(torch, kv, wl, args, timer):
                             num_heads=32, kv_num_heads=8, sparse_block_size=64, do_rotary=1,
                             output=out, workspace=ws)
 
-    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    tm = timer.run(step, args.steps, args.warmup)
     pairs = sparse_pairs(i["block_row_indices"], i["block_col_indices"], 32, 2, 8192, 64)
-    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, flops=4 * 128 * pairs)
+    return dict(**tm, flops=4 * 128 * pairs)
 
 
 def sparse_generation_workload(torch, kv, wl, args, timer):
@@ -328,7 +362,7 @@ def sparse_generation_workload(torch, kv, wl, args, timer):
                             num_heads=32, kv_num_heads=8, sparse_block_size=64, do_rotary=1,
                             output=out, workspace=ws)
 
-    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    tm = timer.run(step, args.steps, args.warmup)
     rp, cols = i["block_row_indices"], i["block_col_indices"]
     B, N, kvN, H, bs = 2, 32, 8, 128, 64
     row = (total - 1) // bs
@@ -340,7 +374,7 @@ def sparse_generation_workload(torch, kv, wl, args, timer):
             seen |= set(int(c) for c in cols[l, rp[l, row]:rp[l, row + 1]])
         blocks += len(seen)
     kv_bytes = B * blocks * bs * H * 2 * 2
-    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, kv_bytes=kv_bytes)
+    return dict(**tm, kv_bytes=kv_bytes)
 
 
 def packed_workload(torch, kv, wl, args, timer):
@@ -357,12 +391,20 @@ def packed_workload(torch, kv, wl, args, timer):
                             t["cumulative_sequence_length"], num_heads=12, output=out,
                             workspace=ws)
 
-    call_ms, kern_ms, kern_med = timer.run(step, args.steps, args.warmup)
+    tm = timer.run(step, args.steps, args.warmup)
     L = case["lengths"].astype(np.int64)
     gemm = 2 * T * 768 * 2304
     attn = 4 * 64 * 12 * int((L * L).sum())
-    return dict(call_ms=call_ms, kern_ms=kern_ms, kern_med=kern_med, gemm_flops=gemm,
+    return dict(**tm, gemm_flops=gemm,
                 attn_flops=attn, tokens=T)
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
 
 
 def cpu_baseline(case, budget_s=12.0):
@@ -370,11 +412,7 @@ def cpu_baseline(case, budget_s=12.0):
     repeating passes until about budget_s seconds of CPU work; report live KV
     GB/s of the oracle."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     i = case["inputs"]
     lens = i["seqlens_k"].astype(np.int64) + 1
     B = lens.shape[0]
@@ -399,6 +437,47 @@ def cpu_baseline(case, budget_s=12.0):
             "sample": f"float64 numpy oracle over the whole decode workload (16 samples, "
                       f"{per_pass / 1e6:.1f} MB of live K/V per pass), {passes} passes in "
                       f"{elapsed:.1f} s"}
+
+
+def cpu_baseline_workload(name, wl, flops):
+    """The oracle's full outputs of one prompt workload, timed on the host:
+    the long prefill and the block-sparse prompt over row chunks in child
+    processes (one BLAS thread each, one per core up to 16), the small prompt
+    and the packed batch in this process (best of three).  Reported as
+    algorithmic TFLOP/s of the oracle."""
+    import oracle
+    from oracle import pool
+    if name in ("gqa_long_prefill", "sparse_prompt"):
+        S = 4096 if name == "gqa_long_prefill" else 8192
+        t0 = time.perf_counter()
+        if name == "gqa_long_prefill":
+            pool.gqa_full(name, S)
+        else:
+            pool.sparse_full(name, S)
+        best, runs, cores = time.perf_counter() - t0, 1, pool.workers()
+        how = f"{cores} child processes over row chunks, 1 run"
+    else:
+        case = getattr(wl, name)()
+        i = dict(case["inputs"])
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            if name == "packed_varlen":
+                j = dict(i)
+                oracle.packed(j.pop("input"), j.pop("weights"), j.pop("bias"), j.pop("token_offset"),
+                              j.pop("cumulative_sequence_length"), **j, **case["attrs"])
+            else:
+                j = dict(i)
+                a = dict(case["attrs"])
+                a["softcap_value"] = a.pop("softcap")
+                oracle.gqa(j.pop("query"), j.pop("key"), j.pop("value"),
+                           total_sequence_length=case["total_sequence_length"], **j, **a)
+            times.append(time.perf_counter() - t0)
+        best, runs, cores = min(times), 3, _blas_threads()
+        how = f"this process, BLAS on {cores} threads, best of {runs}"
+    return {"value": round(flops / best / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, full outputs of the whole workload in {best:.2f} s ({how})"}
 
 
 # Kernels whose HBM traffic is summarised, keyed as bench lines look them up:
@@ -657,87 +736,78 @@ def main():
         print("# packed_varlen done", file=sys.stderr, flush=True)
 
     workloads = {}
+
+    def timing(r):
+        """Graph call time per call, plus the eager per-call samples (kernel
+        and call from the same calls, kernel <= call), in ms."""
+        return {"call_ms": round(r["call_ms"], 5), "eager_ms": eager_stats(r, digits=5)}
+
+    def mfma_line(name, config, r, flops, peak, kernel, traffic_key, extra=None):
+        tf_k = flops / (r["kern_ms"] * 1e-3) / 1e12
+        d = {"config": config, **timing(r),
+             "call_TFLOPs": round(flops / (r["call_ms"] * 1e-3) / 1e12, 3),
+             "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(tf_k, 3),
+                          "peak": peak, "unit": "TFLOP/s", "frac": round(tf_k / peak, 5),
+                          "kernel_ms": round(r["kern_ms"], 5), "algorithmic_flops": flops,
+                          "traffic": traffic_for(traffic_key) if traffic_key else None}}
+        if extra:
+            d.update(extra)
+        if not args.no_cpu:
+            d["cpu_baseline"] = cpu_baseline_workload(name, wl, r.get("all_flops", flops))
+        workloads[name] = d
+
     if "gqa_long_prefill" in res:
         r = res["gqa_long_prefill"]
-        tf_k = r["flops"] / (r["kern_ms"] * 1e-3) / 1e12
-        workloads["gqa_long_prefill"] = {
-            "config": "B4 S4096 N32 kvN8 H128 fp16 causal window 1024 softcap 50 sink qk-norm rotary",
-            "call_ms": round(r["call_ms"], 4), "call_TFLOPs": round(r["flops"] / (r["call_ms"] * 1e-3) / 1e12, 2),
-            "roofline": {"bound": "mfma", "kernel": "flash", "achieved": round(tf_k, 2),
-                         "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tf_k / MFMA_F16_PEAK_TFS, 4), "kernel_ms": round(r["kern_ms"], 4),
-                         "algorithmic_flops": r["flops"], "traffic": traffic_for("flash_gqa_long_prefill")}}
+        mfma_line("gqa_long_prefill",
+                  "B4 S4096 N32 kvN8 H128 fp16 causal window 1024 softcap 50 sink qk-norm rotary",
+                  r, r["flops"], MFMA_F16_PEAK_TFS, "flash", "flash_gqa_long_prefill")
+        print("# gqa_long_prefill reported", file=sys.stderr, flush=True)
     if "gqa_prompt_small" in res:
         r = res["gqa_prompt_small"]
-        tf_k = r["flops"] / (r["kern_ms"] * 1e-3) / 1e12
-        workloads["gqa_prompt_small"] = {
-            "config": "B1 S128 N8 kvN2 H64 fp32 causal", "call_us": round(r["call_ms"] * 1e3, 2),
-            "roofline": {"bound": "mfma", "kernel": "flash", "achieved": round(tf_k, 4),
-                         "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tf_k / MFMA_F32_PEAK_TFS, 5), "kernel_us": round(r["kern_ms"] * 1e3, 2),
-                         "algorithmic_flops": r["flops"], "traffic": None}}
+        mfma_line("gqa_prompt_small", "B1 S128 N8 kvN2 H64 fp32 causal", r, r["flops"],
+                  MFMA_F32_PEAK_TFS, "flash", None)
     if "sparse_prompt" in res:
         r = res["sparse_prompt"]
-        tf_k = r["flops"] / (r["kern_ms"] * 1e-3) / 1e12
-        workloads["sparse_prompt"] = {
-            "config": "B2 S8192 N32 kvN8 H128 fp16 block 64, 4 CSR layouts, NeoX rotary",
-            "call_ms": round(r["call_ms"], 4), "call_TFLOPs": round(r["flops"] / (r["call_ms"] * 1e-3) / 1e12, 2),
-            "roofline": {"bound": "mfma", "kernel": "flash", "achieved": round(tf_k, 2),
-                         "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tf_k / MFMA_F16_PEAK_TFS, 4), "kernel_ms": round(r["kern_ms"], 4),
-                         "algorithmic_flops": r["flops"], "traffic": traffic_for("flash_sparse_prompt")}}
+        mfma_line("sparse_prompt", "B2 S8192 N32 kvN8 H128 fp16 block 64, 4 CSR layouts, NeoX rotary",
+                  r, r["flops"], MFMA_F16_PEAK_TFS, "flash", "flash_sparse_prompt")
+        print("# sparse_prompt reported", file=sys.stderr, flush=True)
     if "packed_varlen" in res:
         r = res["packed_varlen"]
-        tot = r["gemm_flops"] + r["attn_flops"]
-        tf_g = r["gemm_flops"] / (r["kern_ms"] * 1e-3) / 1e12
-        workloads["packed_varlen"] = {
-            "config": f"64 seqs of 32..512 tokens (T={r['tokens']}), D768, QKV 768x2304, 12x64 fp16",
-            "call_ms": round(r["call_ms"], 4), "call_TFLOPs": round(tot / (r["call_ms"] * 1e-3) / 1e12, 2),
-            "roofline": {"bound": "mfma", "kernel": "qkv_gemm", "achieved": round(tf_g, 2),
-                         "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tf_g / MFMA_F16_PEAK_TFS, 4), "kernel_ms": round(r["kern_ms"], 4),
-                         "algorithmic_flops": r["gemm_flops"], "traffic": traffic_for("qkv_gemm_packed_varlen")}}
+        r["all_flops"] = r["gemm_flops"] + r["attn_flops"]
+        mfma_line("packed_varlen",
+                  f"64 seqs of 32..512 tokens (T={r['tokens']}), D768, QKV 768x2304, 12x64 fp16",
+                  r, r["gemm_flops"], MFMA_F16_PEAK_TFS, "qkv_gemm", "qkv_gemm_packed_varlen",
+                  {"call_TFLOPs": round(r["all_flops"] / (r["call_ms"] * 1e-3) / 1e12, 3),
+                   "algorithmic_flops_call": r["all_flops"]})
+
+    def hbm_line(name, config, r, nbytes, kernel, traffic_key, call_bytes=None):
+        gbs_k = nbytes / (r["kern_ms"] * 1e-3) / 1e9
+        cb = call_bytes if call_bytes is not None else nbytes
+        workloads[name] = {
+            "config": config, **timing(r),
+            "call_GBs": round(cb / (r["call_ms"] * 1e-3) / 1e9, 2), "algorithmic_bytes_call": cb,
+            "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(gbs_k, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
+                         "kernel_ms": round(r["kern_ms"], 5), "algorithmic_bytes": nbytes,
+                         "traffic": traffic_for(traffic_key) if traffic_key else None}}
 
     if "gqa_window_decode" in res:
         r = res["gqa_window_decode"]
-        tot = r["shift_bytes"] + r["read_bytes"]
-        gbs_k = r["shift_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
-        workloads["gqa_window_decode"] = {
-            "config": "B16 N32 kvN8 H128 fp16, sliding-window cache 1024 (window 1023), "
-                      "past tokens U[1024,4095], rotary",
-            "call_ms": round(r["call_ms"], 4),
-            "call_GBs": round(tot / (r["call_ms"] * 1e-3) / 1e9, 2),
-            "algorithmic_bytes": tot,
-            "roofline": {"bound": "hbm", "kernel": "window_shift", "achieved": round(gbs_k, 2),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
-                         "kernel_ms": round(r["kern_ms"], 4), "algorithmic_bytes": r["shift_bytes"],
-                         "traffic": traffic_for("window_shift_gqa_window_decode")}}
-
+        hbm_line("gqa_window_decode",
+                 "B16 N32 kvN8 H128 fp16, sliding-window cache 1024 (window 1023), past tokens U[1024,4095], rotary",
+                 r, r["shift_bytes"], "window_shift", "window_shift_gqa_window_decode",
+                 call_bytes=r["shift_bytes"] + r["read_bytes"])
     if "sparse_generation" in res:
         r = res["sparse_generation"]
-        gbs_k = r["kv_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
-        workloads["sparse_generation"] = {
-            "config": "B2 S1 after 8191 past rows, N32 kvN8 H128 fp16 block 64, 4 CSR layouts, NeoX rotary",
-            "call_us": round(r["call_ms"] * 1e3, 2),
-            "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs_k, 2),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
-                         "kernel_us": round(r["kern_ms"] * 1e3, 3), "algorithmic_bytes": r["kv_bytes"],
-                         "traffic": None}}
+        hbm_line("sparse_generation",
+                 "B2 S1 after 8191 past rows, N32 kvN8 H128 fp16 block 64, 4 CSR layouts, NeoX rotary",
+                 r, r["kv_bytes"], "decode", None)
     for bits, cname in ((8, "int8"), (4, "packed int4")):
         name = f"gqa_decode_int{bits}"
-        if name not in res:
-            continue
-        r = res[name]
-        gbs_k = r["kv_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
-        workloads[name] = {
-            "config": f"B16 N32 kvN8 H128 fp32 Q/K/V, shared {cname} cache 4096, per-channel scales, "
-                      "past lengths U[1024,4095], rotary",
-            "call_us": round(r["call_ms"] * 1e3, 2),
-            "call_GBs": round(r["kv_bytes"] / (r["call_ms"] * 1e-3) / 1e9, 2),
-            "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs_k, 2),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
-                         "kernel_us": round(r["kern_ms"] * 1e3, 3), "algorithmic_bytes": r["kv_bytes"],
-                         "traffic": traffic_for(f"decode_{name}")}}
+        if name in res:
+            hbm_line(name, f"B16 N32 kvN8 H128 fp32 Q/K/V, shared {cname} cache 4096, per-channel scales, "
+                           "past lengths U[1024,4095], rotary", res[name], res[name]["kv_bytes"],
+                     "decode", f"decode_{name}")
 
     line = {"metric": "GQA prefill TFLOP/s and decode KV GB/s on 1 MI355X, % of roofline",
             "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -754,11 +824,12 @@ def main():
         line["ms_per_step"] = round(r["call_ms"], 5)
         line["config"]["live_kv_bytes"] = r["kv_bytes"]
         line["config"]["cache_rotations"] = args.rotations
-        tr = traffic_for("decode")
+        line["timing"] = {"ms_per_step": "graph replay of `steps` calls, per call",
+                          "eager_ms": eager_stats(r, digits=5)}
         line["roofline"] = {"bound": "hbm", "kernel": "decode", "achieved": round(gbs_k, 2),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_k / HBM_PEAK_GBS, 4),
                             "kernel_us": round(r["kern_ms"] * 1e3, 3),
-                            "algorithmic_bytes": r["kv_bytes"], "traffic": tr}
+                            "algorithmic_bytes": r["kv_bytes"], "traffic": traffic_for("decode")}
         if not args.no_cpu:
             line["cpu_baseline"] = cpu_baseline(r["case"])
     line["workloads"] = workloads

@@ -18,6 +18,10 @@ The operators follow four ONNX-Runtime contrib operator pages:
 Each function cites the page and section it follows.  Where a page is silent
 the reading taken is stated in the docstring.
 
+``oracle.pool`` runs the GroupQueryAttention and SparseAttention oracles over
+chunks of query rows of a named full-size workload in child processes (rows
+are independent, so the chunks are the whole computation cut into pieces).
+
 Parity pins (tests/test_oracle_*.py) check this oracle against pure-Python
 brute force (``oracle.brute``), torch's float64 SDPA and rms_norm on the CPU,
 closed forms and invariants.  No function here is "parity unpinned".

@@ -1,8 +1,10 @@
 """The oracle over chunks of a named full-size workload, in child processes.
 
-Test infrastructure: the full-size parity tests compare every output element
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): no arithmetic of the
+method lives here.  The full-size parity tests compare every output element
 of the long prefill (4 x 4096 query rows) and the block-sparse prompt
-(2 x 8192 rows) with the oracle.  The oracle computes a chunk of query rows
+(2 x 8192 rows) with the oracle, and the benchmark's CPU baseline times the
+same full-output runs.  The oracle computes a chunk of query rows
 exactly as it computes the whole (rows are independent), so the chunks run
 in separate Python processes, at most one per core (16 at most).  Each child
 generates the workload itself from its seed, limits its BLAS to one thread,
@@ -11,7 +13,7 @@ the children as plain subprocesses (they inherit no GPU state), waits for
 each with a time limit and fails on any non-zero exit.
 
 Run as a script it is one such child:
-    python oracle_pool.py {gqa|sparse} WORKLOAD ROW0 ROW1 OUT.npy WANT_CACHE
+    python oracle/pool.py {gqa|sparse} WORKLOAD ROW0 ROW1 OUT.npy WANT_CACHE
 """
 
 import os
@@ -24,6 +26,8 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
 
 
 def workers():
@@ -31,16 +35,26 @@ def workers():
     return max(1, min(16, os.cpu_count() or 1))
 
 
+def _workloads():
+    """The seeded input generators (kv_cache_transformer_amd/workloads.py),
+    loaded from their file alone so that nothing of the HIP library's package
+    is imported here."""
+    import importlib.util
+    path = os.path.join(ROOT, "kv_cache_transformer_amd", "workloads.py")
+    spec = importlib.util.spec_from_file_location("_seeded_workloads", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def _child(kind, name, r0, r1, out_path, want_cache):
-    sys.path.insert(0, ROOT)
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(1)
     except Exception:  # pragma: no cover
         pass
     import oracle
-    from kv_cache_transformer_amd import workloads as wl
-    case = getattr(wl, name)()
+    case = getattr(_workloads(), name)()
     i = dict(case["inputs"])
     rows = list(range(r0, r1))
     if kind == "gqa":

@@ -174,7 +174,7 @@ def test_workload_gqa_long_prefill():
     """The long prefill at full size (B4 S4096 N32 kvN8 H128, window 1024,
     softcap, sink, q/k norm, rotary): every output element and every cache
     row against the oracle, which runs over row chunks in child processes."""
-    import oracle_pool
+    from oracle import pool as oracle_pool
     case = wl.gqa_long_prefill()
     print("gqa_long_prefill: GPU call, then the oracle over 16 row chunks", flush=True)
     out, pk, pv = gqa_gpu(case)

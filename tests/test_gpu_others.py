@@ -155,7 +155,7 @@ def test_workload_sparse_prompt():
     """The block-sparse prompt at full size (B2 S8192 N32 kvN8 H128, block
     64, four layouts, rotary): every output element and every cache row
     against the oracle, which runs over row chunks in child processes."""
-    import oracle_pool
+    from oracle import pool as oracle_pool
     case = wl.sparse_prompt()
     print("sparse_prompt: GPU call, then the oracle over 16 row chunks", flush=True)
     out, pk, pv = sparse_gpu(case)
