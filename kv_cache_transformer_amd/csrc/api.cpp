@@ -1091,6 +1091,9 @@ int scratch_for_device(void** out, hipStream_t st) {
 
 }  // namespace
 
+// Compute units of the current device, for the launch code of the kernels.
+int kvattn::cu_count() { return device_cu_count(); }
+
 // ===========================================================================
 // exported symbols
 // ===========================================================================

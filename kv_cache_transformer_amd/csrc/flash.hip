@@ -85,6 +85,21 @@ template <int HP> struct FlashMma<f16, HP> {
       for (int i = 0; i < 8; ++i) x[8 * s + i] = (float)v[i];
     }
   }
+  // a row laid out like the query, unconverted: element e is r[e / 8][e % 8]
+  // (NR = NS: all of it; NR = NS / 2: elements e < NE / 2, the first members
+  // of the NeoX pairs)
+  using Raw = half8v;
+  template <int NR>
+  __device__ static void load_rows(const f16* row, int H, int lane, Raw (&r)[NR]) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const int d = 16 * s + 8 * h;
+      r[s] = (d < H) ? load_half8(row + d) : half8v{};
+    }
+  }
+  __device__ static float raw_at(const Raw* r, int e) { return (float)r[e >> 3][e & 7]; }
+  static constexpr int kRawPer = 8;   // elements per Raw
   __device__ void set_q(const float (&x)[NE]) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -218,6 +233,18 @@ template <int HP> struct FlashMma<float, HP> {
       x[s] = (d < H) ? qrow[d] : 0.f;
     }
   }
+  using Raw = float;
+  template <int NR>
+  __device__ static void load_rows(const float* row, int H, int lane, Raw (&r)[NR]) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int e = 0; e < NR; ++e) {
+      const int d = 2 * e + h;
+      r[e] = (d < H) ? row[d] : 0.f;
+    }
+  }
+  __device__ static float raw_at(const Raw* r, int e) { return r[e]; }
+  static constexpr int kRawPer = 1;
   __device__ void set_q(const float (&x)[NE]) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = x[s];
@@ -261,9 +288,28 @@ __device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& 
                            int lane) {
   constexpr int NE = Mma::NE;
   const int H = p.H, h = lane >> 5;
-  float x[NE];
-  Mma::load_raw(qrow, H, lane, x);
   const T* qn = static_cast<const T*>(p.q_norm);
+  const T* cs = static_cast<const T*>(p.cos);
+  const T* sn = static_cast<const T*>(p.sin);
+  const int rh = p.rot_half;
+  const int prow = min(max(pos, 0), p.rot_rows - 1);
+  const T* cr = cs + (int64_t)prow * rh;
+  const T* sr = sn + (int64_t)prow * rh;
+  // both members of every NeoX pair (d, d + H/2) are elements e, e + NE/2 of this lane
+  const bool neox_lane = cs != nullptr && !p.interleaved && 2 * rh == H && H == Mma::NE * 2;
+  // every load of the row (query, norm weights, cos / sin) goes out before
+  // the first use: one memory latency per row
+  constexpr int NR = NE / Mma::kRawPer;
+  typename Mma::Raw xr[NR], wr[NR], cr2[NR / 2], sr2[NR / 2];
+  Mma::load_rows(qrow, H, lane, xr);
+  if (qn != nullptr) Mma::load_rows(qn, H, lane, wr);
+  if (neox_lane) {
+    Mma::load_rows(cr, H, lane, cr2);
+    Mma::load_rows(sr, H, lane, sr2);
+  }
+  float x[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) x[e] = Mma::raw_at(xr, e);
   float rn = 1.f;
   if (qn != nullptr) {
     float ss = 0.f;
@@ -272,29 +318,18 @@ __device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& 
     ss += shfl_xor(ss, 32);
     rn = rsqrtf(ss / (float)H + p.eps);
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const int d = Mma::edim(e, h);
-      if (d < H) x[e] *= rn * to_f32(qn[d]);
-    }
+    for (int e = 0; e < NE; ++e) x[e] *= rn * Mma::raw_at(wr, e);
   }
-  const T* cs = static_cast<const T*>(p.cos);
-  if (cs != nullptr) {
-    const T* sn = static_cast<const T*>(p.sin);
-    const int rh = p.rot_half;
-    const int prow = min(max(pos, 0), p.rot_rows - 1);
-    const T* cr = cs + (int64_t)prow * rh;
-    const T* sr = sn + (int64_t)prow * rh;
-    if (!p.interleaved && 2 * rh == H && H == Mma::NE * 2) {
-      // both members of every pair (d, d + H/2) are elements e, e + NE/2 of this lane
+  if (neox_lane) {
 #pragma unroll
-      for (int e = 0; e < NE / 2; ++e) {
-        const int i = Mma::edim(e, h);
-        const float c = to_f32(cr[i]), s = to_f32(sr[i]);
-        const float a = x[e], z = x[e + NE / 2];
-        x[e] = a * c - z * s;
-        x[e + NE / 2] = z * c + a * s;
-      }
-    } else if (p.interleaved) {
+    for (int e = 0; e < NE / 2; ++e) {
+      const float c = Mma::raw_at(cr2, e), s = Mma::raw_at(sr2, e);
+      const float a = x[e], z = x[e + NE / 2];
+      x[e] = a * c - z * s;
+      x[e + NE / 2] = z * c + a * s;
+    }
+  } else if (cs != nullptr) {
+    if (p.interleaved) {
       // pairs (2i, 2i + 1): the partner is element e ^ 1 (f16) or lane l ^ 32 (f32)
       float y[NE];
 #pragma unroll
@@ -350,33 +385,44 @@ template <int MODE, int BN> struct FlashWork {
 
   // false when the workgroup has no work item (varlen grids are padded)
   __device__ bool init(const FlashParams& p, int wave) {
+    const int gx = gridDim.x, gy = gridDim.y, gz = gridDim.z;
+    int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    // Workgroups are dealt to the eight XCDs round-robin by linear id; the
+    // remap gives each XCD a contiguous range of (row block, head group,
+    // sample) items, so the workgroups sharing a K/V slab share one L2.
+    if (MODE != kVarlen) id = xcd_grouped(id, gx * gy * gz);
+    return init_item(p, wave, id, gx, gy, gz);
+  }
+
+  // linear id -> id of a contiguous per-XCD range (n ids dealt round-robin
+  // over eight XCDs)
+  __device__ static int xcd_grouped(int id, int n) {
+    return (n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id;
+  }
+
+  // Work item `id` of a (gx, gy, gz) item grid (the layout of the launch grid
+  // of the one-item-per-workgroup kernels).
+  __device__ bool init_item(const FlashParams& p, int wave, int id, int gx, int gy, int gz) {
     const int g = p.N / p.kvN;
     const int HW = p.heads_per_wg;
     row_base = 0;
     if (MODE == kVarlen) {
       // item-major: all heads of the list's first (longest) item go first
       const int count = p.work[0];
-      const int lin = blockIdx.x + gridDim.x * blockIdx.y;
-      const int item = lin / (int)gridDim.y;
+      const int item = id / gy;
       if (item >= count) return false;
       b = p.work[1 + 2 * item];
       const int tile = p.work[2 + 2 * item];
-      h = lin % (int)gridDim.y;
+      h = id % gy;
       kvh = h / g;
       r0 = tile * p.rows_per_wg;
       row_base = p.lens[2 * b];
       nrows = p.lens[2 * b + 1] - p.lens[2 * b];
     } else {
-      // Workgroups are dealt to the eight XCDs round-robin by linear id; the
-      // remap gives each XCD a contiguous range of (row block, head group,
-      // sample) items, so the workgroups sharing a K/V slab share one L2.
       // Row blocks go last to first: under a causal bound the late blocks see
       // the most keys, so the longest items start first and short ones fill
       // the tail.
-      const int gx = gridDim.x, gy = gridDim.y;
-      const int n = gx * gy * (int)gridDim.z;
-      int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
-      if (n % 8 == 0) id = (id % 8) * (n / 8) + id / 8;
+      if (id >= gx * gy * gz) return false;
       const int bx = gx - 1 - id % gx, by = (id / gx) % gy;
       b = id / (gx * gy);
       const int groups = g / HW;
@@ -945,6 +991,94 @@ __device__ __forceinline__ void pv_tile64_tr(float16v (&o)[HP / 32], const uint3
       std::make_integer_sequence<int, NM>{});
 }
 
+// ds_read_b128 at byte address addr + OFF, issued as a volatile statement
+// whose wait is explicit (lds_wait_b128), as for the transposing reads.
+template <int OFF>
+__device__ __forceinline__ uint4v lds_b128_asm(uint32_t addr) {
+  uint4v r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_b128(uint4v& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+}
+
+// The MFMA phase of the ping-pong kernel: the PV MFMAs of one tile
+// (probabilities pb, V buffer VB) and the score MFMAs of the next (K buffer
+// KB), interleaved one to one, with the LDS operand reads of D pairs of MFMAs
+// in flight, and the phase's NDMA global-to-LDS copies (dma(i)) spread over
+// the pairs, so that the copies queue behind MFMAs rather than ahead of them.  Pair j is score MFMA j (k-step j / 2, key block j % 2) and PV
+// MFMA j (16-key group j / ND, output block j % ND).  LDS reads complete in
+// issue order, so the wait before each MFMA counts the reads issued after its
+// own operands.  kaddr: this lane's byte address of its first score operand
+// in K buffer 0; vaddr as for pv_tile64_tr.
+template <int HP, int VB, int KB, bool DO_PV, bool DO_QK, int D, int NDMA, typename DMA>
+__device__ __forceinline__ void mphase(float16v (&o)[HP / 32], float16v (&sc)[2],
+                                       const uint32_t (&vaddr)[HP / 32], uint32_t kaddr,
+                                       const half8v (&pb)[4], const half8v (&qf)[HP / 16], DMA&& dma) {
+  using L = PipeLayout<HP>;
+  constexpr int ND = HP / 32, NS = HP / 16;
+  constexpr int N = 4 * ND;
+  static_assert(N == 2 * NS, "as many score as PV MFMAs per tile");
+  constexpr int VOFF = VB * L::VTILE * 2, KOFF = KB * L::KTILE * 2;
+  constexpr int RQ = DO_QK ? 1 : 0, RP = DO_PV ? 2 : 0, RJ = RQ + RP;  // reads per pair
+  uint4v kr[N];
+  uint2v lo[N], hi[N];
+  if (DO_QK) {
+    sc[0] = float16v{};
+    sc[1] = float16v{};
+  }
+  auto issue = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (DO_QK) kr[j] = lds_b128_asm<KOFF + (j % 2) * 64 * L::KS + 32 * (j / 2)>(kaddr);
+    if constexpr (DO_PV) {
+      constexpr int q = j / ND, db = j % ND;
+      lo[j] = lds_tr16_asm<VOFF + 32 * q * HP>(vaddr[db]);
+      hi[j] = lds_tr16_asm<VOFF + 32 * q * HP + 16 * HP>(vaddr[db]);
+    }
+  };
+  auto issue_q = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    kr[j] = lds_b128_asm<KOFF + (j % 2) * 64 * L::KS + 32 * (j / 2)>(kaddr);
+  };
+  auto issue_p = [&](auto jc) {
+    constexpr int j = decltype(jc)::value, q = j / ND, db = j % ND;
+    lo[j] = lds_tr16_asm<VOFF + 32 * q * HP>(vaddr[db]);
+    hi[j] = lds_tr16_asm<VOFF + 32 * q * HP + 16 * HP>(vaddr[db]);
+  };
+  pipe_static_for(issue, std::make_integer_sequence<int, (D < N ? D : N)>{});
+  pipe_static_for(
+      [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int last = (j + D - 1 < N - 1) ? j + D - 1 : N - 1;  // last pair issued in full
+        constexpr bool more = j + D < N;
+        if constexpr (DO_QK) {
+          lds_wait_b128<RP + RJ * (last - j)>(kr[j]);
+          sc[j % 2] = mfma32x32x16(__builtin_bit_cast(half8v, kr[j]), qf[j / 2], sc[j % 2]);
+          if constexpr (more) issue_q(std::integral_constant<int, j + D>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (DO_PV) {
+          constexpr int q = j / ND, db = j % ND;
+          lds_wait_tr<RJ * (last - j) + ((DO_QK && more) ? 1 : 0)>(lo[j], hi[j]);
+          const uint4v u = {lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
+          o[db] = mfma32x32x16(__builtin_bit_cast(half8v, u), pb[q], o[db]);
+          if constexpr (more) issue_p(std::integral_constant<int, j + D>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // copies i with i * N / NDMA == j go out after pair j
+        pipe_static_for(
+            [&](auto ic) {
+              constexpr int i = decltype(ic)::value;
+              if constexpr (i * N / NDMA == j) dma(ic);
+            },
+            std::make_integer_sequence<int, NDMA>{});
+        __builtin_amdgcn_sched_barrier(0);
+      },
+      std::make_integer_sequence<int, N>{});
+}
+
 template <int HP, int MODE, int NW, bool SOFTCAP>
 __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
   using T = f16;
@@ -1327,6 +1461,478 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong f16 kernel (64-key tiles, heads of 64 or 128): two work items per
+// workgroup of eight waves, one per group of four waves (waves 0-3 and 4-7,
+// so that wave j of one group shares a SIMD with wave j of the other).  Each
+// group streams its own K/V tiles (global-to-LDS copies, two buffers each,
+// the pipelined kernel's LDS layout) and runs its item as that kernel does,
+// but cut into two kinds of phase separated by workgroup barriers:
+//   M(s): the PV MFMAs of tile s - 1 and the score MFMAs of tile s (and the
+//         copies of K(s + 1) and V(s) into LDS);
+//   V(s): the softmax of tile s: masks, softcap, running maximum, exp2, row
+//         sums (vector ALU only).
+// The second group runs one phase behind the first, so on every SIMD one wave
+// issues MFMAs while the other keeps the vector ALU busy.  A group with fewer
+// tiles idles through the remaining phases; every wave passes every barrier.
+template <int HP, int MODE, bool SOFTCAP>
+__global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx, int gy, int gz) {
+  using Mma = FlashMma<f16, HP>;
+  using L = PipeLayout<HP>;
+  constexpr int NW = 4;   // waves per group
+  constexpr int BN = 64;
+  static_assert(L::KS == Mma::KS, "score operand reads use the padded K rows");
+  constexpr int MK = (L::NKI + NW - 1) / NW;   // K copies per wave per tile
+  constexpr int MV = (L::NVI + NW - 1) / NW;   // V copies per wave per tile
+  constexpr int GL = 2 * L::KTILE + 2 * L::VTILE;   // elements of one group's tiles
+  __shared__ __attribute__((aligned(1024))) f16 lds[2 * GL];
+  static_assert(2 * (L::VTILE + 3 * 16 * HP + 8 * HP) < 65536, "V read offsets fit the immediate");
+
+  const int n_items = gx * gy * gz;
+  const int NPH = (gy + 1) / 2;
+  const int npairs = (MODE == kVarlen) ? (n_items + 1) / 2 : gx * NPH * gz;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int wx = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
+  for (int round = 0;; ++round) {
+  // per-lane values are recomputed in every round rather than held across
+  // the loop (register pressure)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv >> 2;   // group
+  const int wave = wv & 3;   // wave within the group
+  const int H = p.H;
+  auto lds_byte = [](const f16* q) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const f16*)q);
+  };
+  f16* const K0 = lds + grp * GL;
+  f16* const K1 = K0 + L::KTILE;
+  f16* const V0 = K0 + 2 * L::KTILE;
+  f16* const V1 = V0 + L::VTILE;
+
+  // ---- the workgroup's pairs of items ------------------------------------------
+  // Varlen: pair blockIdx.x of the list order (items 2 f and 2 f + 1), one per
+  // workgroup.  Dense: at most one workgroup per CU, looping over pairs f =
+  // (row block, sample, pair of adjacent head groups) ordered latest row block
+  // first (the most keys under a causal bound).  Round k gives workgroup w the
+  // pair k G + w', w' the rank of w in an XCD-contiguous order, mirrored on odd
+  // rounds: the long pairs of one round meet the short pairs of the next, and
+  // neighbouring pairs (heads sharing a K/V head) run in one XCD's L2.
+  int f = round * G + ((round & 1) ? G - 1 - wx : wx);
+  if (MODE == kVarlen) f = round == 0 ? wg : npairs;
+  if (f >= npairs) break;
+  int id_own, id_other;
+  if (MODE == kVarlen) {
+    id_own = 2 * f + grp;
+    id_other = 2 * f + (grp ^ 1);
+  } else {
+    const int rbi = f / (NPH * gz), rem = f - rbi * (NPH * gz);
+    const int bb = rem / NPH, jp = rem - bb * NPH;
+    const int base = rbi + gx * gy * bb;
+    id_own = (2 * jp + grp < gy) ? base + gx * (2 * jp + grp) : n_items;
+    id_other = (2 * jp + (grp ^ 1) < gy) ? base + gx * (2 * jp + (grp ^ 1)) : n_items;
+  }
+  FlashWork<MODE, BN> w{}, wo{};
+  const bool live = w.init_item(p, wave, id_own, gx, gy, gz);
+  const bool live_o = wo.init_item(p, wave, id_other, gx, gy, gz);
+  const int n_tiles = live ? w.n_tiles : 0;
+  const int n_steps = max(n_tiles, live_o ? wo.n_tiles : 0);   // the same in every wave
+  const int b = w.b, h = w.h, nrows = w.nrows, past = w.past;
+  const int64_t row_base = w.row_base;
+  const f16* kg = static_cast<const f16*>(p.kc) + (live ? w.kv_base : 0);
+  const f16* vg = static_cast<const f16*>(p.vc) + (live ? w.kv_base : 0);
+  const int kj = (int)p.k_j;
+
+  // ---- per-lane copy slots (as in the pipelined kernel) ----------------------
+  auto k_slot = [&](int u, int& r, int& col) {
+    const int j = 64 * (wave + NW * u) + lane;
+    r = j / (L::CPR + 1);
+    const int pc = j - r * (L::CPR + 1);
+    int cc = pc < L::CPR ? pc : 0;
+    if (8 * cc >= H) cc = 0;
+    col = 8 * cc;
+  };
+  auto v_slot = [&](int u, int& r, int& col) {
+    const int j = 64 * (wave + NW * u) + lane;
+    r = j / L::CPR;
+    int cc = (j % L::CPR) ^ L::swv(r);
+    if (8 * cc >= H) cc = 0;
+    col = 8 * cc;
+  };
+  int koff[MK], voff[MV];
+#pragma unroll
+  for (int u = 0; u < MK; ++u) {
+    int r, col;
+    k_slot(u, r, col);
+    koff[u] = r * kj + col;
+  }
+#pragma unroll
+  for (int u = 0; u < MV; ++u) {
+    int r, col;
+    v_slot(u, r, col);
+    voff[u] = r * kj + col;
+  }
+  // a tile with fewer valid rows repeats its last valid row
+  auto load_k = [&](int t, f16* dst) {
+    const TileRange r = w.tile(p, t);
+    const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
+    const f16* src = kg + (int64_t)r.start * p.k_j;
+    const bool whole = last == BN - 1;
+#pragma unroll
+    for (int u = 0; u < MK; ++u) {
+      if (wave + NW * u < L::NKI) {
+        int off = koff[u];
+        if (!whole) {
+          int rr, col;
+          k_slot(u, rr, col);
+          off = min(rr, last) * kj + col;
+        }
+        lds_dma16(src, 2u * (uint32_t)off, lds_byte(dst + 512 * (wave + NW * u)));
+      }
+    }
+  };
+  auto load_v = [&](int t, f16* dst) {
+    const TileRange r = w.tile(p, t);
+    const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
+    const f16* src = vg + (int64_t)r.start * p.k_j;
+    const bool whole = last == BN - 1;
+#pragma unroll
+    for (int u = 0; u < MV; ++u) {
+      if (wave + NW * u < L::NVI) {
+        int off = voff[u];
+        if (!whole) {
+          int rr, col;
+          v_slot(u, rr, col);
+          off = min(rr, last) * kj + col;
+        }
+        lds_dma16(src, 2u * (uint32_t)off, lds_byte(dst + 512 * (wave + NW * u)));
+      }
+    }
+  };
+  // byte addresses of this lane's PV operand reads in V0, per output block
+  uint32_t vaddr[Mma::ND];
+  {
+    const int G = lane >> 4, t = lane & 15, cc = t & 3, ir = t >> 2;
+    const int wsw = L::swv_of_ir(ir);
+    const uint32_t v0 = lds_byte(V0);
+#pragma unroll
+    for (int db = 0; db < Mma::ND; ++db)
+      vaddr[db] = v0 + 2u * (uint32_t)((4 * (G >> 1) + ir) * HP + 16 * (G & 1) + 4 * cc + 32 * (db ^ wsw));
+  }
+
+  // ---- queries of this wave --------------------------------------------------
+  Mma mma;
+  mma.init();
+  const int qrow = w.wrow0 + (lane & 31);
+  const bool row_ok = live && w.wave_rows && qrow < w.wg_rows_end;
+  const float cap = p.softcap;
+  constexpr bool use_cap = SOFTCAP;  // launched only with a positive cap
+  const float qscale = use_cap ? 2.f * kLog2e * p.scale / cap : kLog2e * p.scale;
+  const float capA = cap * kLog2e, capB = 2.f * cap * kLog2e;
+  if (live) {
+    const int rr = min(qrow, nrows - 1);
+    const f16* qg = static_cast<const f16*>(p.q);
+    const f16* qp = (MODE == kVarlen)
+                        ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
+                        : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
+    prep_query(mma, qp, w.rot_past + rr, p, qscale, lane);
+  }
+  const int pos = past + qrow;
+  const f16* bias = static_cast<const f16*>(p.bias);
+  int64_t bias_row = 0;
+  if (bias != nullptr && live) {
+    if (MODE == kVarlen) {
+      int pad_q = p.token_offset[row_base + min(qrow, nrows - 1)] - b * p.pad_seq;
+      pad_q = min(max(pad_q, 0), p.pad_seq - 1);
+      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)pad_q * p.bias_ss;
+    } else {
+      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)min(qrow, nrows - 1) * p.bias_ss;
+    }
+  }
+
+  // ---- softmax of one tile (vector ALU) -----------------------------------------
+  auto mask_scores = [&](const TileRange& r, float16v (&sc)[2]) {
+    if (bias == nullptr) {
+      // score (blk, i) of this lane is key kb + c, c = 32 blk + 8 (i / 4) + i % 4,
+      // a constant, so the masks reduce to a range [clo, chi] of c per lane
+      const int kb = r.start + 4 * (lane >> 5);
+      int clo = 0, chi = r.lim - 1 - kb;
+      if ((MODE == kDense && p.causal) || MODE == kCsr) chi = min(chi, pos - kb);
+      if (MODE == kDense && p.causal && p.window >= 0) clo = pos - p.window - kb;
+      if (!row_ok) chi = -1;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int cc = 32 * blk + 8 * (i >> 2) + (i & 3);
+          float v = sc[blk][i];
+          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
+          sc[blk][i] = (cc >= clo && cc <= chi) ? v : kNegInf;
+        }
+      return;
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        bool ok = row_ok && key < r.lim;
+        if (MODE == kDense) {
+          if (p.causal) {
+            ok = ok && key <= pos;
+            if (p.window >= 0) ok = ok && key >= pos - p.window;
+          }
+        } else if (MODE == kCsr) {
+          ok = ok && key <= pos;
+        }
+        float v = sc[blk][i];
+        if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
+        if (bias != nullptr && ok) {
+          if (MODE == kVarlen) {
+            int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
+            pad_k = min(max(pad_k, 0), p.pad_seq - 1);
+            v += kLog2e * to_f32(bias[bias_row + pad_k]);
+          } else if (key < p.bias_cols) {
+            v += kLog2e * to_f32(bias[bias_row + key]);
+          }
+        }
+        sc[blk][i] = ok ? v : kNegInf;
+      }
+  };
+  auto raw_max = [&](const float16v (&sc)[2]) -> float {
+    float t = kNegInf;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t = fmaxf(t, sc[blk][i]);
+    return t;
+  };
+  auto raw_min = [&](const float16v (&sc)[2]) -> float {
+    float t = -kNegInf;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t = fminf(t, sc[blk][i]);
+    return t;
+  };
+  // raw scores u = 2 log2(e) x / c with |x / c| <= 1/4 take the series
+  constexpr float kPolyU = 0.25f * 2.f * kLog2e;
+  float m = kNegInf, lsum = 0.f;
+  float16v sc[2];
+  half8v pb[4];
+  auto softmax = [&](int t) {
+    const TileRange r = w.tile(p, t);
+    const bool plain = w.full(p, r) && bias == nullptr;
+    float tmax;
+    bool poly = false;
+    if (plain) {
+      tmax = raw_max(sc);
+      if (use_cap) {
+        // tanh by its odd series through y^5 where every raw score of the
+        // wave's tile is small (|y| = |x / c| <= 1/4): one exp2 per score
+        // instead of three, with a relative error in tanh below 1.3e-5 (under
+        // the f16 rounding of the probabilities)
+        poly = __all(fmaxf(tmax, -raw_min(sc)) <= kPolyU);
+        tmax = capA - capB * fast_rcp(fast_exp2(tmax) + 1.f);
+      }
+    } else {
+      mask_scores(r, sc);
+      tmax = raw_max(sc);
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over lanes l and l ^ 32
+    // the running max moves only when a score exceeds it by more than
+    // kMaxSlack: probabilities stay <= 2^kMaxSlack and O is rescaled rarely
+    const bool grow = tmax > m + kMaxSlack;
+    if (__any(grow)) {
+      asm volatile("" ::: "memory");
+      const float mnew = grow ? tmax : m;
+      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
+    }
+    const float muse = (m == kNegInf) ? 0.f : m;
+    if (use_cap && poly) {
+      // exponent = (c / 2) u (1 - y^2 / 3 + 2 y^4 / 15), y^2 = u^2 / (4 log2(e)^2)
+      constexpr float k2 = 0.12011325347955035f;  // 1 / (4 log2(e)^2)
+      const float a0 = 0.5f * cap, a1 = -a0 * k2 / 3.f, a2 = a0 * 2.f * k2 * k2 / 15.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float u = sc[q >> 1][8 * (q & 1) + i], w2 = u * u;
+          pb[q][i] = (f16)fast_exp2(fmaf(u, fmaf(w2, fmaf(w2, a2, a1), a0), -muse));
+        }
+    } else if (use_cap && plain) {
+      const float c0 = capA - muse;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pb[q][i] = (f16)fast_exp2(c0 - capB * fast_rcp(fast_exp2(sc[q >> 1][8 * (q & 1) + i]) + 1.f));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[q][i] = (f16)fast_exp2(sc[q >> 1][8 * (q & 1) + i] - muse);
+    }
+    const half2v one2 = {(f16)1.f, (f16)1.f};
+    float ps[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ps[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ps[q] = __builtin_amdgcn_fdot2(half2v{pb[q][2 * j], pb[q][2 * j + 1]}, one2, ps[q], false);
+    }
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // ---- phases ------------------------------------------------------------------
+  // M(s): copies of K(s + 1) and V(s) into LDS; PV(s - 1); scores of tile s.
+  // Buffers alternate with the parity of s (compile time here).
+  constexpr int kLook = 4;  // MFMA pairs whose operand reads are in flight
+  const uint32_t kaddr = lds_byte(K0) + 2u * (uint32_t)((lane & 31) * L::KS + 8 * (lane >> 5));
+  // M(s) for s >= 1 (parity O of s): copies of K(s + 1) and V(s), then PV(s - 1)
+  // and the scores of tile s.  At s = n_tiles the scores read a stale K buffer
+  // and are never used (one MFMA mix for every M phase keeps the code, and the
+  // register allocation, to a single variant).
+  // the copies of an M phase: K(tk) into kdst and V(tv) into vdst (each when
+  // its flag is set); copy i < MK is this wave's K slot i, the others its V
+  // slots
+  struct Copies {
+    const f16* ksrc; const f16* vsrc;
+    f16* kdst; f16* vdst;
+    int klast, vlast;
+    bool kon, von, kwhole, vwhole;
+  };
+  auto plan = [&](bool kon, int tk, f16* kdst, bool von, int tv, f16* vdst) {
+    Copies c{};
+    c.kon = kon;
+    c.von = von;
+    c.kdst = kdst;
+    c.vdst = vdst;
+    if (kon) {
+      const TileRange r = w.tile(p, tk);
+      c.klast = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
+      c.ksrc = kg + (int64_t)r.start * p.k_j;
+      c.kwhole = c.klast == BN - 1;
+    }
+    if (von) {
+      const TileRange r = w.tile(p, tv);
+      c.vlast = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
+      c.vsrc = vg + (int64_t)r.start * p.k_j;
+      c.vwhole = c.vlast == BN - 1;
+    }
+    return c;
+  };
+  auto copy = [&](const Copies& c, auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < MK) {
+      constexpr int u = i;
+      if (c.kon && wave + NW * u < L::NKI) {
+        int off = koff[u];
+        if (!c.kwhole) {
+          int rr, col;
+          k_slot(u, rr, col);
+          off = min(rr, c.klast) * kj + col;
+        }
+        lds_dma16(c.ksrc, 2u * (uint32_t)off, lds_byte(c.kdst + 512 * (wave + NW * u)));
+      }
+    } else {
+      constexpr int u = i - MK;
+      if (c.von && wave + NW * u < L::NVI) {
+        int off = voff[u];
+        if (!c.vwhole) {
+          int rr, col;
+          v_slot(u, rr, col);
+          off = min(rr, c.vlast) * kj + col;
+        }
+        lds_dma16(c.vsrc, 2u * (uint32_t)off, lds_byte(c.vdst + 512 * (wave + NW * u)));
+      }
+    }
+  };
+  auto phase_m = [&](auto odd, int s) {
+    constexpr bool O = decltype(odd)::value;
+    const Copies c = plan(s + 1 < n_tiles, s + 1, O ? K0 : K1, s < n_tiles, s, O ? V1 : V0);
+    if (s <= n_tiles)
+      mphase<HP, O ? 0 : 1, O ? 1 : 0, true, true, kLook, MK + MV>(mma.o, sc, vaddr, kaddr, pb, mma.qf,
+                                                                 [&](auto ic) { copy(c, ic); });
+    // the phase's MFMA results are read after the barrier: wait for them here
+    mfma_result_fence();
+  };
+  // end of a phase: the copies a wave issued have landed (except after an M
+  // phase, whose copies stay in flight through the next V phase), then the
+  // workgroup barrier
+  auto end_phase = [&](bool wait_copies) {
+    if (wait_copies) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  };
+  if (n_tiles > 0) load_k(0, K0);
+  end_phase(true);
+  if (grp == 1) end_phase(true);  // the second group runs one phase behind
+  // M(0): copies of K(1) and V(0), scores of tile 0
+  if (n_tiles > 0) {
+    const Copies c = plan(1 < n_tiles, 1, K1, true, 0, V0);
+    mphase<HP, 1, 0, false, true, kLook, MK + MV>(mma.o, sc, vaddr, kaddr, pb, mma.qf,
+                                                 [&](auto ic) { copy(c, ic); });
+  }
+  mfma_result_fence();
+  end_phase(false);
+  for (int s = 0; s < n_steps; s += 2) {
+    if (s < n_tiles) softmax(s);  // V(s)
+    end_phase(true);
+    phase_m(std::true_type{}, s + 1);
+    end_phase(false);
+    if (s + 1 < n_tiles) softmax(s + 1);  // V(s + 1)
+    end_phase(true);
+    phase_m(std::false_type{}, s + 2);
+    end_phase(false);
+  }
+  if (grp == 0) end_phase(true);
+
+  // ---- normalise and store -------------------------------------------------
+  mfma_result_fence();
+  if (!live || !w.wave_rows) continue;
+  lsum += shfl_xor(lsum, 32);
+  bool has_sink = false;
+  float sg = 0.f;
+  if (p.sink != nullptr) {
+    has_sink = true;
+    sg = kLog2e * to_f32(static_cast<const f16*>(p.sink)[h]);
+  } else if (p.smooth == 1) {
+    has_sink = true;
+  }
+  float inv;
+  if (lsum == 0.f) {
+    inv = 0.f;
+  } else if (has_sink) {
+    const float M2 = fmaxf(m, sg);
+    const float den = lsum * fast_exp2(m - M2) + fast_exp2(sg - M2);
+    inv = fast_exp2(m - M2) / den;
+  } else {
+    inv = 1.f / lsum;
+  }
+  if (!row_ok) continue;
+  f16* og = static_cast<f16*>(p.out);
+  f16* orow = (MODE == kVarlen) ? og + (row_base + qrow) * p.o_s + (int64_t)h * p.o_h
+                                : og + (int64_t)b * p.o_b + (int64_t)qrow * p.o_s + (int64_t)h * p.o_h;
+#pragma unroll
+  for (int db = 0; db < Mma::ND; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 32 * db + 8 * gq + 4 * (lane >> 5);
+      if (d < H) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) orow[d + i] = (f16)(mma.o[db][4 * gq + i] * inv);
+      }
+    }
+  }
+}
+
 template <int HP, int MODE, bool SOFTCAP = false>
 hipError_t launch_pipe(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
   if (nw != 4) return hipErrorInvalidValue;
@@ -1342,16 +1948,34 @@ hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Two items of the (gx, gy, gz) item grid per eight-wave workgroup.
+template <int HP, int MODE, bool SOFTCAP = false>
+hipError_t launch_pp(const FlashParams& p, dim3 grid, hipStream_t s) {
+  const int items = (int)(grid.x * grid.y * grid.z);
+  int wgs = (items + 1) / 2;
+  if (MODE == kDense) {
+    // pairs of head groups: one workgroup per CU, each looping over pairs
+    const int pairs = (int)grid.x * (((int)grid.y + 1) / 2) * (int)grid.z;
+    wgs = std::min(pairs, cu_count());
+  }
+  if (wgs <= 0) return hipSuccess;
+  hipLaunchKernelGGL((flash_pp_kernel<HP, MODE, SOFTCAP>), dim3(wgs), dim3(512), 0, s, p,
+                     (int)grid.x, (int)grid.y, (int)grid.z);
+  return hipGetLastError();
+}
+
 template <typename T, int HP, int BN>
 hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
-  // dense f16 prompts with heads up to 128 run on the pipelined kernel
-  constexpr bool kPipeDense = std::is_same<T, f16>::value && BN == 64 && HP <= 128;
+  // dense and varlen f16 prompts with heads up to 128 run on the ping-pong
+  // kernel (four waves of 32 rows per item)
+  constexpr bool kPipe = std::is_same<T, f16>::value && BN == 64 && HP <= 128;
   switch (p.mode) {
     case kDense: {
       const int nw = p.rows_per_wg / 32 * p.heads_per_wg;
-      if constexpr (kPipeDense) {
-        if (p.softcap > 0.f) return launch_pipe<HP, kDense, true>(p, grid, nw, s);
-        return launch_pipe<HP, kDense, false>(p, grid, nw, s);
+      if constexpr (kPipe) {
+        if (nw != 4) return hipErrorInvalidValue;
+        if (p.softcap > 0.f) return launch_pp<HP, kDense, true>(p, grid, s);
+        return launch_pp<HP, kDense, false>(p, grid, s);
       } else {
         if (nw != 4) return hipErrorInvalidValue;
         if (p.softcap > 0.f) hipLaunchKernelGGL((flash_kernel<T, HP, BN, kDense, 4, true>), grid, dim3(256), 0, s, p);
@@ -1364,6 +1988,9 @@ hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
       return launch_mode<T, HP, BN, kCsr>(p, grid, nw >= 4 ? 4 : (nw == 2 ? 2 : 1), s);
     }
     default:
+      if constexpr (kPipe) {
+        if (p.rows_per_wg / 32 * p.heads_per_wg == 4) return launch_pp<HP, kVarlen>(p, grid, s);
+      }
       hipLaunchKernelGGL((flash_kernel<T, HP, BN, kVarlen, 4, false>), grid, dim3(256), 0, s, p);
       return hipGetLastError();
   }

@@ -144,6 +144,9 @@ struct DecodeParams {
 // ---------------------------------------------------------------------------
 enum FlashMode : int { kDense = 0, kCsr = 1, kVarlen = 2 };
 
+// Compute units of the current device (cached per device).
+int cu_count();
+
 struct FlashParams {
   const void* q;            // queries, element (b, s, h, d) at q_b*b + q_s*s + q_h*h + d
   int64_t q_b, q_s, q_h;
