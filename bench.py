@@ -487,7 +487,7 @@ _KERNEL_SOURCES = ["kv_cache_transformer_amd/csrc/device_common.hpp",
                    "kv_cache_transformer_amd/csrc/api.cpp"]
 TRAFFIC_KERNELS = [
     ("decode", r"decode_kernelIDF16_Li128ELi0E", "kv_cache_transformer_amd/csrc/decode.hip", "gqa_decode"),
-    ("flash_gqa_long_prefill", r"flash_pipe_kernel(?:ILi128ELi0E|<128, 0,)", "kv_cache_transformer_amd/csrc/flash.hip",
+    ("flash_gqa_long_prefill", r"flash_pp_kernel(?:ILi128ELi0E|<128, 0,)", "kv_cache_transformer_amd/csrc/flash.hip",
      "gqa_long_prefill"),
     ("flash_sparse_prompt", r"flash_kernelIDF16_Li128ELi\d+ELi1E", "kv_cache_transformer_amd/csrc/flash.hip",
      "sparse_prompt", lambda grid: grid >= 1 << 20),
@@ -602,7 +602,7 @@ def summarise_counters(d, cmd):
     import csv
     import glob
     import re
-    pat = re.compile(r"(flash_pipe_kernel|flash_kernel|decode_kernel|decode_combine_kernel|qkv_gemm_kernel|prep_kv_kernel|"
+    pat = re.compile(r"(flash_pp_kernel|flash_pipe_kernel|flash_kernel|decode_kernel|qkv_gemm_kernel|prep_kv_kernel|"
                      r"window_shift_kernel|prep_kernel|packed_sched_kernel)(?:I(DF16_|f)(?:Li(\d+)ELi(\d+)(?:ELi(\d+))?)?)?")
     agg, dur = {}, {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -612,7 +612,7 @@ def summarise_counters(d, cmd):
                 continue
             t = {"DF16_": "f16", "f": "f32", None: ""}[m.group(2)]
             hd, md = m.group(3), m.group(5)
-            pm = re.search(r"flash_pipe_kernel(?:ILi(\d+)ELi(\d+)E|<(\d+), (\d+),)", r["Kernel_Name"])
+            pm = re.search(r"flash_p(?:ipe|p)_kernel(?:ILi(\d+)ELi(\d+)E|<(\d+), (\d+),)", r["Kernel_Name"])
             if pm:  # f16 only; template arguments (head, mode, ...)
                 t, hd, md = "f16", pm.group(1) or pm.group(3), pm.group(2) or pm.group(4)
             dm = re.search(r"<float(?:, (\d+), (\d+), (\d+))?", r["Kernel_Name"])

@@ -1493,6 +1493,8 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   const int npairs = (MODE == kVarlen) ? (n_items + 1) / 2 : gx * NPH * gz;
   const int G = gridDim.x, wg = blockIdx.x;
   const int wx = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
+  const int S = NPH * gz;  // dense: slab pairs
+  const bool xcd_slabs = S % 8 == 0 && G % 8 == 0;
   for (int round = 0;; ++round) {
   // per-lane values are recomputed in every round rather than held across
   // the loop (register pressure)
@@ -1513,22 +1515,35 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
 
   // ---- the workgroup's pairs of items ------------------------------------------
   // Varlen: pair blockIdx.x of the list order (items 2 f and 2 f + 1), one per
-  // workgroup.  Dense: at most one workgroup per CU, looping over pairs f =
-  // (row block, sample, pair of adjacent head groups) ordered latest row block
-  // first (the most keys under a causal bound).  Round k gives workgroup w the
-  // pair k G + w', w' the rank of w in an XCD-contiguous order, mirrored on odd
-  // rounds: the long pairs of one round meet the short pairs of the next, and
-  // neighbouring pairs (heads sharing a K/V head) run in one XCD's L2.
+  // workgroup.  Dense: at most one workgroup per CU, looping over pairs =
+  // (row block, slab pair), a slab pair being a sample and a pair of adjacent
+  // head groups, row blocks taken latest first (the most keys under a causal
+  // bound), mirrored on odd rounds so that the long pairs of one round meet
+  // the short pairs of the next.  When the slab pairs split evenly over the
+  // eight XCDs, each XCD takes its own slab pairs through all row blocks: the
+  // rows in flight on one XCD then share the K/V windows of a few slabs, which
+  // stay in its L2.  Otherwise round k gives workgroup w the pair k G + w', w'
+  // its rank in an XCD-contiguous order.
   int f = round * G + ((round & 1) ? G - 1 - wx : wx);
   if (MODE == kVarlen) f = round == 0 ? wg : npairs;
-  if (f >= npairs) break;
+  int rbi = 0, sp = 0;
+  if (MODE == kDense && xcd_slabs) {
+    const int NB = S / 8, G8 = G / 8, wl = wg / 8;
+    const int q = round * G8 + ((round & 1) ? G8 - 1 - wl : wl);
+    if (q >= gx * NB) break;
+    rbi = q / NB;
+    sp = (wg % 8) * NB + (q - rbi * NB);
+  } else {
+    if (f >= npairs) break;
+    rbi = f / S;
+    sp = f - rbi * S;
+  }
   int id_own, id_other;
   if (MODE == kVarlen) {
     id_own = 2 * f + grp;
     id_other = 2 * f + (grp ^ 1);
   } else {
-    const int rbi = f / (NPH * gz), rem = f - rbi * (NPH * gz);
-    const int bb = rem / NPH, jp = rem - bb * NPH;
+    const int bb = sp / NPH, jp = sp - bb * NPH;
     const int base = rbi + gx * gy * bb;
     id_own = (2 * jp + grp < gy) ? base + gx * (2 * jp + grp) : n_items;
     id_other = (2 * jp + (grp ^ 1) < gy) ? base + gx * (2 * jp + (grp ^ 1)) : n_items;
