@@ -1,9 +1,13 @@
 // K2: tiled online-softmax attention on MFMA (prefill / prompt paths).
 //
-// One workgroup owns a block of query rows for one or more query heads that
+// A work item is a block of query rows for one or more query heads that
 // share a kv head; every wave owns 32 query rows of one head.  Key/value
-// tiles of BN rows are staged in LDS (double-buffered, filled from registers
-// loaded one tile ahead) and shared by all waves of the workgroup.
+// tiles of BN rows are staged in LDS and shared by the waves of the item:
+// flash_pp_kernel (dense and varlen f16 prompts, heads up to 128) copies them
+// from global memory straight into LDS and runs two items per workgroup in
+// alternating MFMA and softmax phases; flash_kernel (block-sparse, float32,
+// heads of 256) fills double-buffered LDS tiles from registers loaded one
+// tile ahead.
 //
 //   S^T[keys][32 queries] = K_tile . Q^T        (f16: 32x32x16, f32: 32x32x2)
 //   O^T[H][32 queries]   += V_tile^T . P^T
@@ -896,14 +900,10 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined f16 kernel (64-key tiles, heads of 64 or 128).
+// LDS tiles of the ping-pong f16 kernel (64-key tiles, heads of 64 or 128).
 //
 // K and V tiles go straight from global memory into LDS (global_load_lds, 16
-// bytes per lane; no register staging), K one tile ahead of V, each in two
-// buffers.  Per tile t a wave issues the loads of K(t + 2) and V(t + 1), then
-// the score MFMAs of tile t + 1 interleaved with the softmax of tile t, then
-// the PV MFMAs of tile t interleaved with the maximum of tile t + 1, so the
-// matrix pipe and the vector ALU work side by side within the wave.
+// bytes per lane; no register staging), two buffers each.
 //
 // LDS rows: K rows are padded by one 16-byte chunk (the score operand reads
 // of 16 consecutive rows then hit distinct banks); V rows are unpadded with
@@ -963,34 +963,6 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32
                : "memory", "m0");
 }
 
-// PV of a 64-key tile from V buffer VB of a swizzled V tile pair (vaddr[db]:
-// this lane's byte address of output block db in buffer 0; pb[2 * blk + half]:
-// its probabilities of 16 keys each).  The operand reads run D MFMAs ahead.
-template <int HP, int VB>
-__device__ __forceinline__ void pv_tile64_tr(float16v (&o)[HP / 32], const uint32_t (&vaddr)[HP / 32],
-                                             const half8v (&pb)[4]) {
-  constexpr int ND = HP / 32, NM = 4 * ND, D = 3;
-  constexpr int VOFF = VB * PipeLayout<HP>::VTILE * 2;
-  uint2v lo[NM], hi[NM];
-  auto issue = [&](auto kc) {
-    constexpr int k = decltype(kc)::value, q = k / ND, db = k % ND;
-    lo[k] = lds_tr16_asm<VOFF + 32 * q * HP>(vaddr[db]);
-    hi[k] = lds_tr16_asm<VOFF + 32 * q * HP + 16 * HP>(vaddr[db]);
-  };
-  pipe_static_for(issue, std::make_integer_sequence<int, D>{});
-  pipe_static_for(
-      [&](auto kc) {
-        constexpr int k = decltype(kc)::value, q = k / ND, db = k % ND;
-        // reads of the MFMAs after k that are already issued
-        constexpr int later = (NM - 1 - k) < (D - 1) ? (NM - 1 - k) : (D - 1);
-        lds_wait_tr<2 * later>(lo[k], hi[k]);
-        const uint4v u = {lo[k][0], lo[k][1], hi[k][0], hi[k][1]};
-        o[db] = mfma32x32x16(__builtin_bit_cast(half8v, u), pb[q], o[db]);
-        if constexpr (k + D < NM) issue(std::integral_constant<int, k + D>{});
-      },
-      std::make_integer_sequence<int, NM>{});
-}
-
 // ds_read_b128 at byte address addr + OFF, issued as a volatile statement
 // whose wait is explicit (lds_wait_b128), as for the transposing reads.
 template <int OFF>
@@ -1012,7 +984,8 @@ __device__ __forceinline__ void lds_wait_b128(uint4v& a) {
 // MFMA j (16-key group j / ND, output block j % ND).  LDS reads complete in
 // issue order, so the wait before each MFMA counts the reads issued after its
 // own operands.  kaddr: this lane's byte address of its first score operand
-// in K buffer 0; vaddr as for pv_tile64_tr.
+// in K buffer 0; vaddr[db]: its byte address of output block db's PV
+// operand in V buffer 0.
 template <int HP, int VB, int KB, bool DO_PV, bool DO_QK, int D, int NDMA, typename DMA>
 __device__ __forceinline__ void mphase(float16v (&o)[HP / 32], float16v (&sc)[2],
                                        const uint32_t (&vaddr)[HP / 32], uint32_t kaddr,
@@ -1079,395 +1052,13 @@ __device__ __forceinline__ void mphase(float16v (&o)[HP / 32], float16v (&sc)[2]
       std::make_integer_sequence<int, N>{});
 }
 
-template <int HP, int MODE, int NW, bool SOFTCAP>
-__global__ __launch_bounds__(64 * NW, 2) void flash_pipe_kernel(FlashParams p) {
-  using T = f16;
-  using Mma = FlashMma<f16, HP>;
-  using L = PipeLayout<HP>;
-  constexpr int BN = 64;
-  constexpr int KS = L::KS;
-  static_assert(KS == Mma::KS, "score operand reads use the padded K rows");
-  constexpr int MK = (L::NKI + NW - 1) / NW;   // K loads per wave per tile
-  constexpr int MV = (L::NVI + NW - 1) / NW;   // V loads per wave per tile
-  __shared__ __attribute__((aligned(1024))) f16 lds[2 * L::KTILE + 2 * L::VTILE];
-  f16* const K0 = lds;
-  f16* const K1 = lds + L::KTILE;
-  f16* const V0 = lds + 2 * L::KTILE;
-  f16* const V1 = V0 + L::VTILE;
-  static_assert(2 * (L::VTILE + 3 * 16 * HP + 8 * HP) < 65536, "V read offsets fit the immediate");
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = p.H;
-  auto lds_byte = [](const f16* q) {
-    return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const f16*)q);
-  };
-  FlashWork<MODE, BN> w;
-  if (!w.init(p, wave)) return;
-  const int b = w.b, h = w.h, nrows = w.nrows, past = w.past;
-  const int n_tiles = w.n_tiles;
-  const int64_t row_base = w.row_base;
-  const f16* kg = static_cast<const f16*>(p.kc) + w.kv_base;
-  const f16* vg = static_cast<const f16*>(p.vc) + w.kv_base;
-  const int kj = (int)p.k_j;
-
-  // ---- per-lane load slots ---------------------------------------------------
-  // Slot j of a K tile is row j / (CPR + 1), chunk j % (CPR + 1) (the last
-  // chunk of a row is padding and repeats chunk 0); slot j of a V tile is row
-  // j / CPR, stored chunk j % CPR, which holds chunk (j % CPR) ^ swv(row).
-  // Chunks past the head read chunk 0 (any valid data: Q is zero there, and
-  // those output columns are not stored).
-  auto k_slot = [&](int u, int& r, int& col) {
-    const int j = 64 * (wave + NW * u) + lane;
-    r = j / (L::CPR + 1);
-    const int pc = j - r * (L::CPR + 1);
-    int cc = pc < L::CPR ? pc : 0;
-    if (8 * cc >= H) cc = 0;
-    col = 8 * cc;
-  };
-  auto v_slot = [&](int u, int& r, int& col) {
-    const int j = 64 * (wave + NW * u) + lane;
-    r = j / L::CPR;
-    int cc = (j % L::CPR) ^ L::swv(r);
-    if (8 * cc >= H) cc = 0;
-    col = 8 * cc;
-  };
-  // offsets (elements) of this lane's slots in a tile whose rows are all valid
-  int koff[MK], voff[MV];
-#pragma unroll
-  for (int u = 0; u < MK; ++u) {
-    int r, col;
-    k_slot(u, r, col);
-    koff[u] = r * kj + col;
-  }
-#pragma unroll
-  for (int u = 0; u < MV; ++u) {
-    int r, col;
-    v_slot(u, r, col);
-    voff[u] = r * kj + col;
-  }
-  // a tile with fewer valid rows repeats its last valid row
-  auto load_k = [&](int t, f16* dst) {
-    const TileRange r = w.tile(p, t);
-    const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
-    const f16* src = kg + (int64_t)r.start * p.k_j;
-    const bool whole = last == BN - 1;
-#pragma unroll
-    for (int u = 0; u < MK; ++u) {
-      if (wave + NW * u < L::NKI) {
-        int off = koff[u];
-        if (!whole) {
-          int rr, col;
-          k_slot(u, rr, col);
-          off = min(rr, last) * kj + col;
-        }
-        lds_dma16(src, 2u * (uint32_t)off, lds_byte(dst + 512 * (wave + NW * u)));
-      }
-    }
-  };
-  auto load_v = [&](int t, f16* dst) {
-    const TileRange r = w.tile(p, t);
-    const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
-    const f16* src = vg + (int64_t)r.start * p.k_j;
-    const bool whole = last == BN - 1;
-#pragma unroll
-    for (int u = 0; u < MV; ++u) {
-      if (wave + NW * u < L::NVI) {
-        int off = voff[u];
-        if (!whole) {
-          int rr, col;
-          v_slot(u, rr, col);
-          off = min(rr, last) * kj + col;
-        }
-        lds_dma16(src, 2u * (uint32_t)off, lds_byte(dst + 512 * (wave + NW * u)));
-      }
-    }
-  };
-
-
-  // byte addresses of this lane's PV operand reads in V0, per output block:
-  // rows 4 (G >> 1) + ir (+ 16 q, + 8), columns 16 (G & 1) + 4 c of block db ^ swv
-  uint32_t vaddr[Mma::ND];
-  {
-    const int G = lane >> 4, t = lane & 15, c = t & 3, ir = t >> 2;
-    const int wsw = L::swv_of_ir(ir);
-    const uint32_t v0 = lds_byte(V0);
-#pragma unroll
-    for (int db = 0; db < Mma::ND; ++db)
-      vaddr[db] = v0 + 2u * (uint32_t)((4 * (G >> 1) + ir) * HP + 16 * (G & 1) + 4 * c + 32 * (db ^ wsw));
-  }
-
-  // ---- queries of this wave ------------------------------------------------
-  Mma mma;
-  mma.init();
-  const int qrow = w.wrow0 + (lane & 31);
-  const bool row_ok = w.wave_rows && qrow < w.wg_rows_end;
-  const float cap = p.softcap;
-  constexpr bool use_cap = SOFTCAP;  // launched only with a positive cap
-  const float qscale = use_cap ? 2.f * kLog2e * p.scale / cap : kLog2e * p.scale;
-  const float capA = cap * kLog2e, capB = 2.f * cap * kLog2e;
-  {
-    const int rr = min(qrow, nrows - 1);
-    const f16* qg = static_cast<const f16*>(p.q);
-    const f16* qp = (MODE == kVarlen)
-                        ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
-                        : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
-    prep_query(mma, qp, w.rot_past + rr, p, qscale, lane);
-  }
-  const int pos = past + qrow;
-  const f16* bias = static_cast<const f16*>(p.bias);
-  int64_t bias_row = 0;
-  if (bias != nullptr) {
-    if (MODE == kVarlen) {
-      int pad_q = p.token_offset[row_base + min(qrow, nrows - 1)] - b * p.pad_seq;
-      pad_q = min(max(pad_q, 0), p.pad_seq - 1);
-      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)pad_q * p.bias_ss;
-    } else {
-      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)min(qrow, nrows - 1) * p.bias_ss;
-    }
-  }
-
-  // ---- score helpers -------------------------------------------------------
-  // Scores of a tile that is not plain: softcap, bias and masks in the exponent.
-  auto mask_scores = [&](const TileRange& r, float16v (&sc)[2]) {
-    if (bias == nullptr) {
-      // Score (blk, i) of this lane is key kb + c, c = 32 blk + 8 (i / 4) + i % 4
-      // a constant, so the masks reduce to a range [clo, chi] of c per lane.
-      const int kb = r.start + 4 * (lane >> 5);
-      int clo = 0, chi = r.lim - 1 - kb;
-      if ((MODE == kDense && p.causal) || MODE == kCsr) chi = min(chi, pos - kb);
-      if (MODE == kDense && p.causal && p.window >= 0) clo = pos - p.window - kb;
-      if (!row_ok) chi = -1;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = 32 * blk + 8 * (i >> 2) + (i & 3);
-          float v = sc[blk][i];
-          if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
-          sc[blk][i] = (c >= clo && c <= chi) ? v : kNegInf;
-        }
-      return;
-    }
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = r.start + 32 * blk + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        bool ok = row_ok && key < r.lim;
-        if (MODE == kDense) {
-          if (p.causal) {
-            ok = ok && key <= pos;
-            if (p.window >= 0) ok = ok && key >= pos - p.window;
-          }
-        } else if (MODE == kCsr) {
-          ok = ok && key <= pos;
-        }
-        float v = sc[blk][i];
-        if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
-        if (bias != nullptr && ok) {
-          if (MODE == kVarlen) {
-            int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
-            pad_k = min(max(pad_k, 0), p.pad_seq - 1);
-            v += kLog2e * to_f32(bias[bias_row + pad_k]);
-          } else if (key < p.bias_cols) {
-            v += kLog2e * to_f32(bias[bias_row + key]);
-          }
-        }
-        sc[blk][i] = ok ? v : kNegInf;
-      }
-  };
-  auto raw_max = [&](const float16v (&sc)[2]) -> float {
-    float t = kNegInf;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) t = fmaxf(t, sc[blk][i]);
-    return t;
-  };
-  float m = kNegInf, lsum = 0.f;
-  // running-max update from this lane's tile maximum (exponent domain)
-  auto update_max = [&](float tmax) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over lanes l and l ^ 32
-    // The running max moves only when a score exceeds it by more than
-    // kMaxSlack: probabilities stay <= 2^kMaxSlack and O is rescaled rarely.
-    const bool grow = tmax > m + kMaxSlack;
-    if (__any(grow)) {
-      asm volatile("" ::: "memory");
-      mfma_result_fence();  // O may still be accumulating
-      const float mnew = grow ? tmax : m;
-      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
-      m = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < Mma::ND; ++db) mma.o[db] *= alpha;
-    }
-  };
-  // tile maximum in the exponent domain (plain tiles: cap of the raw maximum)
-  auto tile_max = [&](const TileRange& r, bool plain, float16v (&sc)[2]) -> float {
-    float t;
-    if (plain) {
-      t = raw_max(sc);
-      if (use_cap) t = capA - capB * fast_rcp(fast_exp2(t) + 1.f);
-    } else {
-      mask_scores(r, sc);
-      t = raw_max(sc);
-    }
-    return t;
-  };
-  auto plain_of = [&](const TileRange& r) { return w.full(p, r) && bias == nullptr; };
-
-  // probabilities of tile scores sc (f16, PV operand layout) and their sum,
-  // with the score MFMAs of the next tile (Kn -> scn) interleaved
-  auto probs_qk = [&](bool plain, float16v (&sc)[2], half8v (&pb)[4], const f16* Kn, float16v (&scn)[2]) {
-    const float muse = (m == kNegInf) ? 0.f : m;
-    const float c0 = capA - muse;
-    constexpr int NMF = 2 * Mma::NS;  // score MFMAs (and operand reads) of a tile
-    if (use_cap && plain) {
-      mma.template qk_tile64<false>(Kn, lane, scn);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          pb[q][i] = (f16)fast_exp2(c0 - capB * fast_rcp(fast_exp2(sc[q >> 1][8 * (q & 1) + i]) + 1.f));
-      // four operand reads ahead, then one MFMA, one read and a share of the
-      // softmax's VALU work at a time (176 VALU instructions in all)
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
-#pragma unroll
-      for (int i = 0; i < NMF - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 176 / NMF, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
-    } else {
-      mma.template qk_tile64<false>(Kn, lane, scn);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[q][i] = (f16)fast_exp2(sc[q >> 1][8 * (q & 1) + i] - muse);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
-#pragma unroll
-      for (int i = 0; i < NMF - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 80 / NMF, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
-    }
-  };
-  // PV of a tile with the row sum and the raw maximum of the next tile's scores
-  auto pv_sum_max = [&](auto vb, const half8v (&pb)[4], const float16v (&scn)[2]) -> float {
-    // the score MFMAs were issued on either side of a branch: their results
-    // are read below
-    mfma_result_fence();
-    pv_tile64_tr<HP, decltype(vb)::value>(mma.o, vaddr, pb);
-    const half2v one2 = {(f16)1.f, (f16)1.f};
-    float ps[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ps[q] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ps[q] = __builtin_amdgcn_fdot2(half2v{pb[q][2 * j], pb[q][2 * j + 1]}, one2, ps[q], false);
-    }
-    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    return raw_max(scn);
-  };
-
-  // ---- prologue: tiles 0 (K, V) and 1 (K); scores and maximum of tile 0 ----
-  float16v sA[2], sB[2];
-  half8v pb[4];
-  TileRange rn = {0, 0};
-  bool plain_n = true;
-  if (n_tiles > 0) {
-    load_k(0, K0);
-    load_v(0, V0);
-    if (n_tiles > 1) load_k(1, K1);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    mma.qk_tile64(K0, lane, sA);
-    mfma_result_fence();
-    rn = w.tile(p, 0);
-    plain_n = plain_of(rn);
-    update_max(tile_max(rn, plain_n, sA));
-  }
-  // ---- steady state: step t computes P(t), PV(t), and S(t + 1) ------------
-  // sc: scores of tile t (transformed when not plain), scn receives S(t + 1);
-  // Kc/Vc: buffers of K(t) / V(t); Kn/Vn: of K(t + 1) / V(t + 1)
-  auto step = [&](auto vb, int t, float16v (&sc)[2], float16v (&scn)[2], f16* Kc, f16* Kn, f16* Vn) {
-    const bool plain_t = plain_n;
-    // K(t) and V(t - 1) are no longer read by any wave (barrier of step t - 1)
-    if (t + 2 < n_tiles) load_k(t + 2, Kc);
-    if (t + 1 < n_tiles) load_v(t + 1, Vn);
-    probs_qk(plain_t, sc, pb, Kn, scn);
-    float tmax = pv_sum_max(vb, pb, scn);
-    const bool more = t + 1 < n_tiles;
-    if (more) {
-      rn = w.tile(p, t + 1);
-      plain_n = plain_of(rn);
-      if (!plain_n) {
-        mfma_result_fence();
-        tmax = tile_max(rn, false, scn);
-      } else if (use_cap) {
-        tmax = capA - capB * fast_rcp(fast_exp2(tmax) + 1.f);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (more) update_max(tmax);
-  };
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t, sA, sB, K0, K1, V1);
-    if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1, sB, sA, K1, K0, V0);
-  }
-
-  // ---- normalise and store -------------------------------------------------
-  mfma_result_fence();
-  if (!w.wave_rows) return;
-  lsum += shfl_xor(lsum, 32);
-  bool has_sink = false;
-  float sg = 0.f;
-  if (p.sink != nullptr) {
-    has_sink = true;
-    sg = kLog2e * to_f32(static_cast<const f16*>(p.sink)[h]);
-  } else if (p.smooth == 1) {
-    has_sink = true;
-  }
-  float inv;
-  if (lsum == 0.f) {
-    inv = 0.f;
-  } else if (has_sink) {
-    const float M2 = fmaxf(m, sg);
-    const float den = lsum * fast_exp2(m - M2) + fast_exp2(sg - M2);
-    inv = fast_exp2(m - M2) / den;
-  } else {
-    inv = 1.f / lsum;
-  }
-  if (!row_ok) return;
-  f16* og = static_cast<f16*>(p.out);
-  f16* orow = (MODE == kVarlen) ? og + (row_base + qrow) * p.o_s + (int64_t)h * p.o_h
-                                : og + (int64_t)b * p.o_b + (int64_t)qrow * p.o_s + (int64_t)h * p.o_h;
-#pragma unroll
-  for (int db = 0; db < Mma::ND; ++db)
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int d = 32 * db + 8 * gq + 4 * (lane >> 5);
-      if (d < H) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) orow[d + i] = (f16)(mma.o[db][4 * gq + i] * inv);
-      }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Ping-pong f16 kernel (64-key tiles, heads of 64 or 128): two work items per
 // workgroup of eight waves, one per group of four waves (waves 0-3 and 4-7,
 // so that wave j of one group shares a SIMD with wave j of the other).  Each
 // group streams its own K/V tiles (global-to-LDS copies, two buffers each,
-// the pipelined kernel's LDS layout) and runs its item as that kernel does,
-// but cut into two kinds of phase separated by workgroup barriers:
+// the layout above) and runs its item in two kinds of phase separated by
+// workgroup barriers:
 //   M(s): the PV MFMAs of tile s - 1 and the score MFMAs of tile s (and the
 //         copies of K(s + 1) and V(s) into LDS);
 //   V(s): the softmax of tile s: masks, softcap, running maximum, exp2, row
@@ -1559,7 +1150,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   const f16* vg = static_cast<const f16*>(p.vc) + (live ? w.kv_base : 0);
   const int kj = (int)p.k_j;
 
-  // ---- per-lane copy slots (as in the pipelined kernel) ----------------------
+  // ---- per-lane copy slots ---------------------------------------------------
   auto k_slot = [&](int u, int& r, int& col) {
     const int j = 64 * (wave + NW * u) + lane;
     r = j / (L::CPR + 1);
@@ -1946,13 +1537,6 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
       }
     }
   }
-}
-
-template <int HP, int MODE, bool SOFTCAP = false>
-hipError_t launch_pipe(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
-  if (nw != 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((flash_pipe_kernel<HP, MODE, 4, SOFTCAP>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
 }
 
 template <typename T, int HP, int BN, int MODE, bool SOFTCAP = false>
