@@ -287,9 +287,36 @@ struct TileRange {
 // SparseAttention page, Attributes table: rotary_interleaved; the first
 // 2 * rot_half dims rotate), then the factor qscale that turns the scores
 // into the exponent the softmax needs.  Lanes l and l ^ 32 share a row.
+// prep_query_issue sends every load of the row (query, norm weights, cos /
+// sin) before any is used, so a row costs one memory latency;
+// prep_query_finish does the arithmetic.
+template <typename Mma> struct QueryLoads {
+  static constexpr int NR = Mma::NE / Mma::kRawPer;
+  typename Mma::Raw xr[NR], wr[NR], cr[NR / 2], sr[NR / 2];
+};
+
+// both members of every NeoX pair (d, d + H/2) are elements e, e + NE/2 of a lane
+template <typename Mma>
+__device__ __forceinline__ bool neox_in_lane(const FlashParams& p) {
+  return p.cos != nullptr && !p.interleaved && 2 * p.rot_half == p.H && p.H == Mma::NE * 2;
+}
+
 template <typename Mma, typename T>
-__device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& p, float qscale,
-                           int lane) {
+__device__ void prep_query_issue(QueryLoads<Mma>& ql, const T* qrow, int pos, const FlashParams& p, int lane) {
+  const int H = p.H;
+  const T* qn = static_cast<const T*>(p.q_norm);
+  Mma::load_rows(qrow, H, lane, ql.xr);
+  if (qn != nullptr) Mma::load_rows(qn, H, lane, ql.wr);
+  if (neox_in_lane<Mma>(p)) {
+    const int prow = min(max(pos, 0), p.rot_rows - 1);
+    Mma::load_rows(static_cast<const T*>(p.cos) + (int64_t)prow * p.rot_half, H, lane, ql.cr);
+    Mma::load_rows(static_cast<const T*>(p.sin) + (int64_t)prow * p.rot_half, H, lane, ql.sr);
+  }
+}
+
+template <typename Mma, typename T>
+__device__ void prep_query_finish(Mma& mma, const QueryLoads<Mma>& ql, const T* qrow, int pos,
+                                  const FlashParams& p, float qscale, int lane) {
   constexpr int NE = Mma::NE;
   const int H = p.H, h = lane >> 5;
   const T* qn = static_cast<const T*>(p.q_norm);
@@ -299,21 +326,9 @@ __device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& 
   const int prow = min(max(pos, 0), p.rot_rows - 1);
   const T* cr = cs + (int64_t)prow * rh;
   const T* sr = sn + (int64_t)prow * rh;
-  // both members of every NeoX pair (d, d + H/2) are elements e, e + NE/2 of this lane
-  const bool neox_lane = cs != nullptr && !p.interleaved && 2 * rh == H && H == Mma::NE * 2;
-  // every load of the row (query, norm weights, cos / sin) goes out before
-  // the first use: one memory latency per row
-  constexpr int NR = NE / Mma::kRawPer;
-  typename Mma::Raw xr[NR], wr[NR], cr2[NR / 2], sr2[NR / 2];
-  Mma::load_rows(qrow, H, lane, xr);
-  if (qn != nullptr) Mma::load_rows(qn, H, lane, wr);
-  if (neox_lane) {
-    Mma::load_rows(cr, H, lane, cr2);
-    Mma::load_rows(sr, H, lane, sr2);
-  }
   float x[NE];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) x[e] = Mma::raw_at(xr, e);
+  for (int e = 0; e < NE; ++e) x[e] = Mma::raw_at(ql.xr, e);
   float rn = 1.f;
   if (qn != nullptr) {
     float ss = 0.f;
@@ -322,12 +337,12 @@ __device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& 
     ss += shfl_xor(ss, 32);
     rn = rsqrtf(ss / (float)H + p.eps);
 #pragma unroll
-    for (int e = 0; e < NE; ++e) x[e] *= rn * Mma::raw_at(wr, e);
+    for (int e = 0; e < NE; ++e) x[e] *= rn * Mma::raw_at(ql.wr, e);
   }
-  if (neox_lane) {
+  if (neox_in_lane<Mma>(p)) {
 #pragma unroll
     for (int e = 0; e < NE / 2; ++e) {
-      const float c = Mma::raw_at(cr2, e), s = Mma::raw_at(sr2, e);
+      const float c = Mma::raw_at(ql.cr, e), s = Mma::raw_at(ql.sr, e);
       const float a = x[e], z = x[e + NE / 2];
       x[e] = a * c - z * s;
       x[e + NE / 2] = z * c + a * s;
@@ -375,6 +390,14 @@ __device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& 
   mma.set_q(x);
 }
 
+template <typename Mma, typename T>
+__device__ void prep_query(Mma& mma, const T* qrow, int pos, const FlashParams& p, float qscale,
+                           int lane) {
+  QueryLoads<Mma> ql;
+  prep_query_issue<Mma>(ql, qrow, pos, p, lane);
+  prep_query_finish(mma, ql, qrow, pos, p, qscale, lane);
+}
+
 // What one workgroup and wave of a flash launch cover: sample, heads, query
 // rows, the key range and its tile schedule, and the K/V slab base.
 template <int MODE, int BN> struct FlashWork {
@@ -406,7 +429,9 @@ template <int MODE, int BN> struct FlashWork {
 
   // Work item `id` of a (gx, gy, gz) item grid (the layout of the launch grid
   // of the one-item-per-workgroup kernels).
-  __device__ bool init_item(const FlashParams& p, int wave, int id, int gx, int gy, int gz) {
+  // lens: a copy of the first nlens entries of p.lens (dense mode), or null
+  __device__ bool init_item(const FlashParams& p, int wave, int id, int gx, int gy, int gz,
+                            const int* lens = nullptr, int nlens = 0) {
     const int g = p.N / p.kvN;
     const int HW = p.heads_per_wg;
     row_base = 0;
@@ -448,13 +473,15 @@ template <int MODE, int BN> struct FlashWork {
 
     past = 0;
     if (MODE == kDense) {
-      n_keys = p.causal ? p.lens[b] + 1 : p.S;
+      // (the same value in every lane: made scalar, as the tile bounds are)
+      const int len_b = (b < nlens) ? __builtin_amdgcn_readfirstlane(lens[b]) : p.lens[b];
+      n_keys = p.causal ? len_b + 1 : p.S;
       if (p.has_past) past = n_keys - p.S;
       rot_past = past;
       if (p.win_cap > 0) {
         // sliding-window cache: keys are the buffer's rows after the eviction,
         // masks work in row coordinates, rotary in absolute positions
-        n_keys = window_geom(p.lens[b] + 1, p.S, p.win_cap).fill;
+        n_keys = window_geom(len_b + 1, p.S, p.win_cap).fill;
         past = n_keys - p.S;
       }
     } else if (MODE == kCsr) {
@@ -1086,6 +1113,40 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   const int wx = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
   const int S = NPH * gz;  // dense: slab pairs
   const bool xcd_slabs = S % 8 == 0 && G % 8 == 0;
+  // the samples' lengths (dense), read once per workgroup: every round needs
+  // them again, and a global load there would cost a memory latency
+  constexpr int kLensMax = 1024;
+  __shared__ int s_lens[kLensMax];
+  const int nlens = (MODE == kDense) ? min(p.B, kLensMax) : 0;
+  for (int i = threadIdx.x; i < nlens; i += 512) s_lens[i] = p.lens[i];
+  __syncthreads();
+  // The output of a round waits in LDS (each wave's 32 x HP tile, row-major,
+  // 16-byte chunks XOR-swizzled by row, in its quarter of the group's V
+  // buffers) and is stored once the next round's query loads are out, in
+  // whole-row 16-byte chunks: the stores' latency then overlaps theirs.
+  constexpr int OCH = HP / 8, OSW = OCH < 16 ? OCH - 1 : 15;  // chunks per row, swizzle mask
+  static_assert(4 * 32 * HP <= 2 * L::VTILE, "the group's outputs fit its V buffers");
+  // per wave: rows pending (0: none) and the output address of the first
+  // one, kept in LDS rather than in registers through the tile loop
+  __shared__ int s_pend_rows[8];
+  __shared__ f16* s_pend_base[8];
+  if ((threadIdx.x & 63) == 0) s_pend_rows[threadIdx.x >> 6] = 0;  // wave-private
+  auto store_pending = [&](const f16* stage) {
+    const int wv8 = threadIdx.x >> 6;
+    int ln = threadIdx.x & 63;
+    asm volatile("" : "+v"(ln));  // per-lane addresses are made here, not held across rounds
+    const int rows = __builtin_amdgcn_readfirstlane(s_pend_rows[wv8]);
+    if (rows > 0) {
+      f16* base = s_pend_base[wv8];
+#pragma unroll
+      for (int k = 0; k < 32 * OCH / 64; ++k) {
+        const int c = ln + 64 * k, r = c / OCH, cc = c - r * OCH;
+        const half8v v = *reinterpret_cast<const half8v*>(stage + r * HP + 8 * (cc ^ (r & OSW)));
+        if (r < rows && 8 * cc < p.H) *reinterpret_cast<half8v*>(base + r * p.o_s + 8 * cc) = v;
+      }
+      if (ln == 0) s_pend_rows[wv8] = 0;
+    }
+  };
   for (int round = 0;; ++round) {
   // per-lane values are recomputed in every round rather than held across
   // the loop (register pressure)
@@ -1140,8 +1201,8 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
     id_other = (2 * jp + (grp ^ 1) < gy) ? base + gx * (2 * jp + (grp ^ 1)) : n_items;
   }
   FlashWork<MODE, BN> w{}, wo{};
-  const bool live = w.init_item(p, wave, id_own, gx, gy, gz);
-  const bool live_o = wo.init_item(p, wave, id_other, gx, gy, gz);
+  const bool live = w.init_item(p, wave, id_own, gx, gy, gz, s_lens, nlens);
+  const bool live_o = wo.init_item(p, wave, id_other, gx, gy, gz, s_lens, nlens);
   const int n_tiles = live ? w.n_tiles : 0;
   const int n_steps = max(n_tiles, live_o ? wo.n_tiles : 0);   // the same in every wave
   const int b = w.b, h = w.h, nrows = w.nrows, past = w.past;
@@ -1229,21 +1290,24 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
 
   // ---- queries of this wave --------------------------------------------------
   Mma mma;
-  mma.init();
   const int qrow = w.wrow0 + (lane & 31);
   const bool row_ok = live && w.wave_rows && qrow < w.wg_rows_end;
   const float cap = p.softcap;
   constexpr bool use_cap = SOFTCAP;  // launched only with a positive cap
   const float qscale = use_cap ? 2.f * kLog2e * p.scale / cap : kLog2e * p.scale;
   const float capA = cap * kLog2e, capB = 2.f * cap * kLog2e;
-  if (live) {
+  {
     const int rr = min(qrow, nrows - 1);
     const f16* qg = static_cast<const f16*>(p.q);
     const f16* qp = (MODE == kVarlen)
                         ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
                         : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
-    prep_query(mma, qp, w.rot_past + rr, p, qscale, lane);
+    // the previous round's stores and this round's query loads are in flight
+    // together (one wait covers both)
+    store_pending(V0 + wave * 32 * HP);
+    if (live) prep_query(mma, qp, w.rot_past + rr, p, qscale, lane);
   }
+  mma.init();
   const int pos = past + qrow;
   const f16* bias = static_cast<const f16*>(p.bias);
   int64_t bias_row = 0;
@@ -1500,7 +1564,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   }
   if (grp == 0) end_phase(true);
 
-  // ---- normalise and store -------------------------------------------------
+  // ---- normalise into LDS; the stores go out with the next round's loads ----
   mfma_result_fence();
   if (!live || !w.wave_rows) continue;
   lsum += shfl_xor(lsum, 32);
@@ -1522,20 +1586,30 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   } else {
     inv = 1.f / lsum;
   }
-  if (!row_ok) continue;
-  f16* og = static_cast<f16*>(p.out);
-  f16* orow = (MODE == kVarlen) ? og + (row_base + qrow) * p.o_s + (int64_t)h * p.o_h
-                                : og + (int64_t)b * p.o_b + (int64_t)qrow * p.o_s + (int64_t)h * p.o_h;
+  {
+    f16* stage = V0 + wave * 32 * HP;
+    const int r = lane & 31;
 #pragma unroll
-  for (int db = 0; db < Mma::ND; ++db)
+    for (int db = 0; db < Mma::ND; ++db)
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int d = 32 * db + 8 * gq + 4 * (lane >> 5);
-      if (d < H) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) orow[d + i] = (f16)(mma.o[db][4 * gq + i] * inv);
+      for (int gq = 0; gq < 4; ++gq) {
+        const int c = 4 * db + gq;  // 16-byte chunk of dims 32 db + 8 gq ..
+        const half4v v = {(f16)(mma.o[db][4 * gq] * inv), (f16)(mma.o[db][4 * gq + 1] * inv),
+                          (f16)(mma.o[db][4 * gq + 2] * inv), (f16)(mma.o[db][4 * gq + 3] * inv)};
+        *reinterpret_cast<half4v*>(stage + r * HP + 8 * (c ^ (r & OSW)) + 4 * (lane >> 5)) = v;
       }
-    }
+  }
+  if (lane == 0) {
+    f16* og = static_cast<f16*>(p.out);
+    s_pend_rows[wv] = min(32, w.wg_rows_end - w.wrow0);
+    s_pend_base[wv] = (MODE == kVarlen) ? og + (row_base + w.wrow0) * p.o_s + (int64_t)h * p.o_h
+                                        : og + (int64_t)b * p.o_b + (int64_t)w.wrow0 * p.o_s + (int64_t)h * p.o_h;
+  }
+  }
+  {
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) & 3;
+    const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) >> 2;
+    store_pending(lds + grp * GL + 2 * L::KTILE + wave * 32 * HP);
   }
 }
 
