@@ -1108,7 +1108,8 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
 
   const int n_items = gx * gy * gz;
   const int NPH = (gy + 1) / 2;
-  const int npairs = (MODE == kVarlen) ? (n_items + 1) / 2 : gx * NPH * gz;
+  // varlen: the work list holds work[0] items (of at most gx) per head
+  const int npairs = (MODE == kVarlen) ? (min(p.work[0], gx) * gy * gz + 1) / 2 : gx * NPH * gz;
   const int G = gridDim.x, wg = blockIdx.x;
   const int wx = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
   const int S = NPH * gz;  // dense: slab pairs
@@ -1166,18 +1167,17 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   f16* const V1 = V0 + L::VTILE;
 
   // ---- the workgroup's pairs of items ------------------------------------------
-  // Varlen: pair blockIdx.x of the list order (items 2 f and 2 f + 1), one per
-  // workgroup.  Dense: at most one workgroup per CU, looping over pairs =
-  // (row block, slab pair), a slab pair being a sample and a pair of adjacent
-  // head groups, row blocks taken latest first (the most keys under a causal
-  // bound), mirrored on odd rounds so that the long pairs of one round meet
-  // the short pairs of the next.  When the slab pairs split evenly over the
+  // At most one workgroup per CU, looping over pairs of items, mirrored on odd
+  // rounds so that the long pairs of one round meet the short pairs of the
+  // next.  Varlen: pair f is items 2 f and 2 f + 1 of the list order (longest
+  // sequences first).  Dense: pairs = (row block, slab pair), a slab pair
+  // being a sample and a pair of adjacent head groups, row blocks taken latest
+  // first (the most keys under a causal bound).  When the slab pairs split evenly over the
   // eight XCDs, each XCD takes its own slab pairs through all row blocks: the
   // rows in flight on one XCD then share the K/V windows of a few slabs, which
   // stay in its L2.  Otherwise round k gives workgroup w the pair k G + w', w'
   // its rank in an XCD-contiguous order.
   int f = round * G + ((round & 1) ? G - 1 - wx : wx);
-  if (MODE == kVarlen) f = round == 0 ? wg : npairs;
   int rbi = 0, sp = 0;
   if (MODE == kDense && xcd_slabs) {
     const int NB = S / 8, G8 = G / 8, wl = wg / 8;
@@ -1625,12 +1625,10 @@ hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
 template <int HP, int MODE, bool SOFTCAP = false>
 hipError_t launch_pp(const FlashParams& p, dim3 grid, hipStream_t s) {
   const int items = (int)(grid.x * grid.y * grid.z);
-  int wgs = (items + 1) / 2;
-  if (MODE == kDense) {
-    // pairs of head groups: one workgroup per CU, each looping over pairs
-    const int pairs = (int)grid.x * (((int)grid.y + 1) / 2) * (int)grid.z;
-    wgs = std::min(pairs, cu_count());
-  }
+  // one workgroup per CU at most, each looping over pairs of items (varlen:
+  // of the items the work list may hold; dense: pairs of head groups)
+  const int pairs = (MODE == kDense) ? (int)grid.x * (((int)grid.y + 1) / 2) * (int)grid.z : (items + 1) / 2;
+  const int wgs = std::min(pairs, cu_count());
   if (wgs <= 0) return hipSuccess;
   hipLaunchKernelGGL((flash_pp_kernel<HP, MODE, SOFTCAP>), dim3(wgs), dim3(512), 0, s, p,
                      (int)grid.x, (int)grid.y, (int)grid.z);
