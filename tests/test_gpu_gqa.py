@@ -42,6 +42,8 @@ PREFILL = [
     # pipelined kernel, tiles partly visible to a workgroup's rows
     dict(dtype=F16, B=2, S=300, N=8, kvN=2, H=128, window=90),
     dict(dtype=F16, B=1, S=257, N=4, kvN=1, H=64, window=40, rotary=True),
+    # more samples than a persistent prompt workgroup copies lengths of (1024)
+    dict(dtype=F16, B=1100, S=3, N=2, kvN=1, H=64, past="shared", cap=12, rotary=True),
 ]
 
 DECODE = [
@@ -88,6 +90,16 @@ def _compare(case, rows=None):
 def test_prefill_parity(idx):
     print(f"prefill case {idx}: {PREFILL[idx]}", flush=True)
     _compare(_case(PREFILL[idx], 100 + idx))
+
+
+# Dense f16 prompts run one workgroup per CU over pairs of row blocks; with
+# the (sample, head-group pair) slabs a multiple of eight, each XCD takes its
+# own slabs through all row blocks, in several rounds here (38 row blocks x 8
+# slabs over at most 256 workgroups).  Every seventh query row is compared.
+def test_prefill_persistent_rounds():
+    case = _case(dict(dtype=F16, B=8, S=1200, N=4, kvN=1, H=64, window=300, rotary=True, norm=True,
+                      softcap=20.0), 150)
+    _compare(case, rows=np.arange(0, 1200, 7))
 
 
 @pytest.mark.parametrize("idx", range(len(DECODE)))
