@@ -679,8 +679,9 @@ __device__ bool find_sample(const DecodeParams& p, int ups, int64_t quota, int p
   return false;
 }
 
-// Partial records merged per batch by the last pair of a unit.
-constexpr int kMergeBatch = 8;
+// Partial records merged per batch by the last pair of a unit (a unit split
+// over at most this many pairs is merged after one round trip).
+constexpr int kMergeBatch = 16;
 
 // Partial records cross compute units on different XCDs, whose L2 caches are
 // not coherent with each other: they are stored and loaded at device scope
@@ -1329,6 +1330,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     const int hj = e / NQD, d = 4 * (e % NQD);
     if (d >= H) continue;
     const int base = ((pair0 * p.hpw + hj) * RS) * 4;
+    const int hq = h0 + hj;
+    // the sink's load is in flight with the first batch
+    bool has;
+    const float sg = read_sink<AT>(p, hq, has);
     // records in batches of kMergeBatch, all loads of a batch in flight at
     // once (each is a round trip to the shared level); the running (M, L, O)
     // is rescaled once per batch
@@ -1360,9 +1365,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         }
       M = mn;
     }
-    const int hq = h0 + hj;
-    bool has;
-    const float sg = read_sink<AT>(p, hq, has);
     const float inv = final_scale(M, L, has, sg);
     const float v[4] = {O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
     Q4::store(static_cast<AT*>(p.out) + ((int64_t)b * p.N + hq) * H + d, v);
