@@ -455,7 +455,8 @@ void packed_attrs_default(packed_attrs* attrs);
  * cum must start at 0, be non-decreasing with steps <= S and end at
  * token_count.
  *
- * UNSUPPORTED on the GPU: v_hidden != q_hidden.
+ * UNSUPPORTED on the GPU: v_hidden != q_hidden; an input hidden size or a
+ * weight column count that is not a multiple of 8; weights over 2 GiB.
  */
 int32_t packed_attention(const packed_attrs* attrs,
                          const kvattn_tensor* inputs, int32_t n_inputs,

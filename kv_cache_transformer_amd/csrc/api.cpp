@@ -946,6 +946,9 @@ int packed_validate(const packed_attrs* a, const kvattn_tensor* in, int n_in,
   P.HP = padded_head(P.H);
   if (P.D <= 0) return fail(KVATTN_ERR_INVALID_ARG, "input hidden size must be positive");
   if (P.D % 8 || P.C % 8) return fail(KVATTN_ERR_UNSUPPORTED, "input hidden %d and weight columns %d must be multiples of 8", P.D, P.C);
+  // the projection reads the weights through one buffer resource (32-bit offsets)
+  if ((int64_t)P.D * P.C * (dt == KVATTN_DT_F32 ? 4 : 2) > INT32_MAX)
+    return fail(KVATTN_ERR_UNSUPPORTED, "weights of %d x %d elements exceed 2 GiB", P.D, P.C);
   const kvattn_tensor& to = in[PACKED_IN_TOKEN_OFFSET];
   const kvattn_tensor& cum = in[PACKED_IN_CUMULATIVE_SEQUENCE_LENGTH];
   if (!has(to) || !has(cum)) return fail(KVATTN_ERR_INVALID_ARG, "token_offset and cumulative_sequence_length are required");

@@ -89,6 +89,8 @@ __global__ __launch_bounds__(256) void packed_sched_kernel(PackedSchedParams p) 
 constexpr int BNC = 128;
 // register stages of the operand prefetch (tiles in flight while one is used)
 constexpr int kGemmStages = 3;
+// buffer resource word 3 for raw 32-bit buffer accesses (gfx9 family)
+constexpr int kGemmBufferFormat = 0x00020000;
 // 32-row blocks per wave of the f16 GEMM (workgroup tile 256 x 128)
 constexpr int kGemmMbF16 = 4;
 
@@ -222,45 +224,67 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmParams p) {
   // tiles up to kt + NS are still in flight
   constexpr int NS = kGemmStages;
   uint4v stages[NS][CPT];
-  // Every load is issued (addresses clamped into the operands, K >= CH and
-  // Ncol a multiple of CH), so the waits can stay partial; chunks past the
-  // operands' edges are zeroed when they are written to LDS.
+  // Operand chunks are read through buffer resources made per k step (A from
+  // row m0 and column k0 on, over the tile's valid rows; B from row k0 and
+  // column n0 on), at per-lane offsets fixed for the launch, so a load costs
+  // no vector address arithmetic.  The range check covers the per-lane offset
+  // only (not a scalar one), hence the per-step resources.  Out-of-range chunks
+  // read 0: A rows past M, B rows past K.  B chunks past Ncol read the next
+  // row's first columns; they only reach output columns that are never
+  // stored.  A chunks past K (a partial last k step) read the next row and are
+  // zeroed when written to LDS.
   static_assert(A_CH % 256 == 0 && B_CH % 256 == 0, "whole chunk rows per thread");
+  constexpr int NA = A_CH / 256, NB = B_CH / 256;
+  constexpr int ES = sizeof(T);
+  const int rows_a = min(p.M - m0, BM);
+  auto rsrc_a = [&](int k0) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(X) + (int64_t)m0 * p.K + k0, 0,
+                                             (rows_a * p.K - k0) * ES, kGemmBufferFormat);
+  };
+  auto rsrc_b = [&](int k0) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(W) + (int64_t)k0 * p.Ncol + n0, 0,
+                                             ((p.K - k0) * p.Ncol - n0) * ES, kGemmBufferFormat);
+  };
+  int aoff[NA], boff[NB], alds[NA], blds[NB], akc[NA];
+#pragma unroll
+  for (int u = 0; u < NA; ++u) {
+    const int idx = tid + 256 * u;
+    const int r = idx / (BK / CH), kc = (idx % (BK / CH)) * CH;
+    aoff[u] = (r * p.K + kc) * ES;
+    alds[u] = r * AS + kc;
+    akc[u] = kc;
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int bi = tid + 256 * u;
+    const int r = bi / (BNC / CH), nc = (bi % (BNC / CH)) * CH;
+    boff[u] = (r * p.Ncol + nc) * ES;
+    blds[u] = r * BS + nc;
+  }
   auto load = [&](auto st, int k0) {
     uint4v (&stage)[CPT] = stages[decltype(st)::value];
+    const __amdgpu_buffer_rsrc_t ra = rsrc_a(k0), rb = rsrc_b(k0);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int idx = tid + 256 * u;
-      if (u < A_CH / 256) {
-        const int r = idx / (BK / CH), kc = (idx % (BK / CH)) * CH;
-        const int gm = min(m0 + r, p.M - 1), gk = min(k0 + kc, p.K - CH);
-        stage[u] = *reinterpret_cast<const uint4v*>(X + (int64_t)gm * p.K + gk);
-      } else {
-        const int bi = idx - A_CH;
-        const int r = bi / (BNC / CH), nc = (bi % (BNC / CH)) * CH;
-        const int gk = min(k0 + r, p.K - 1), gn = min(n0 + nc, p.Ncol - CH);
-        stage[u] = *reinterpret_cast<const uint4v*>(W + (int64_t)gk * p.Ncol + gn);
-      }
-    }
+    for (int u = 0; u < NA; ++u)
+      stage[u] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[u], 0, 0));
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      stage[NA + u] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(rb, boff[u], 0, 0));
   };
   auto store = [&](auto st, int buf, int k0) {
-    const uint4v (&stage)[CPT] = stages[decltype(st)::value];
+    uint4v (&stage)[CPT] = stages[decltype(st)::value];
     T* As = lds + buf * (A_EL + B_EL);
     T* Bs = As + A_EL;
-    const uint4v zero = {0u, 0u, 0u, 0u};
+    if (k0 + BK > p.K) {
+      const uint4v zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int idx = tid + 256 * u;
-      if (u < A_CH / 256) {
-        const int r = idx / (BK / CH), kc = (idx % (BK / CH)) * CH;
-        *reinterpret_cast<uint4v*>(As + r * AS + kc) = (k0 + kc < p.K) ? stage[u] : zero;
-      } else {
-        const int bi = idx - A_CH;
-        const int r = bi / (BNC / CH), nc = (bi % (BNC / CH)) * CH;
-        *reinterpret_cast<uint4v*>(Bs + r * BS + nc) =
-            (k0 + r < p.K && n0 + nc < p.Ncol) ? stage[u] : zero;
-      }
+      for (int u = 0; u < NA; ++u)
+        if (k0 + akc[u] >= p.K) stage[u] = zero;
     }
+#pragma unroll
+    for (int u = 0; u < NA; ++u) *reinterpret_cast<uint4v*>(As + alds[u]) = stage[u];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) *reinterpret_cast<uint4v*>(Bs + blds[u]) = stage[NA + u];
   };
 
   float16v acc[MB][2];

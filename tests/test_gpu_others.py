@@ -194,6 +194,10 @@ PACKED = [
     dict(dtype=F32, lengths=[33, 70], padded_seq=80, D=48, N=4, H=32, bias_attn="full"),
     dict(dtype=F16, lengths=[200, 0, 17], padded_seq=256, D=128, N=3, H=128, bias_attn="h1"),
     dict(dtype=F16, lengths=[2, 1], padded_seq=4, D=8, N=1, H=8, wstd=0.3),
+    # an input hidden size with a partial last k step of the projection, over
+    # several k steps and two row tiles
+    dict(dtype=F16, lengths=[300, 45, 129], padded_seq=320, D=104, N=2, H=64),
+    dict(dtype=F32, lengths=[70, 3], padded_seq=96, D=72, N=2, H=32),
 ]
 
 
