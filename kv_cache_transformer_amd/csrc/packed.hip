@@ -9,12 +9,13 @@
 //     waits for the host.
 //   * QKV projection: qkv[T, q+k+v] = input[T, D] . weights[D, q+k+v] + bias
 //     (PackedAttention page, Inputs table: the weight columns hold Q for
-//     every head, then K, then V) as an MFMA GEMM with 128x128 output tiles,
-//     LDS double buffering fed from register stages a few tiles ahead, and
-//     the bias added in an epilogue that goes through LDS so that the output
-//     is stored in 16-byte chunks.  The weights are row-major [D][cols], so
-//     the B operand (k-contiguous per lane) is read from the LDS tile with
-//     ds_read_b64_tr_b16.
+//     every head, then K, then V) as an MFMA GEMM with the bias added in an
+//     epilogue that goes through LDS so that the output is stored in 16-byte
+//     chunks.  f16: 256x128 output tiles, both operands copied from memory
+//     straight into three LDS stages; float32: 128x128 tiles, LDS double
+//     buffering fed from register stages a few tiles ahead.  The weights are
+//     row-major [D][cols], so the B operand (k-contiguous per lane) is read
+//     from the LDS tile with a transposing read (f16: ds_read_b64_tr_b16).
 #include <type_traits>
 #include <utility>
 
@@ -103,9 +104,6 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for_int(F&& f) {
   static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
-// k depth of a tile (64 measured slower for f16: three waves per SIMD become two)
-template <typename T> struct GemmBK { static constexpr int value = 32; };
-template <> struct GemmBK<float> { static constexpr int value = 32; };
 
 typedef __fp16 lds_half4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 __device__ __forceinline__ half4v lds_tr16(const f16* ptr) {
@@ -120,53 +118,25 @@ template <> struct Quad4<f16> {
   __device__ static void store(f16* y, const float (&v)[4]) {
     *reinterpret_cast<half4v*>(y) = half4v{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
   }
+  __device__ static void load(const f16* x, float (&v)[4]) {
+    const half4v h = *reinterpret_cast<const half4v*>(x);
+    for (int r = 0; r < 4; ++r) v[r] = (float)h[r];
+  }
 };
 template <> struct Quad4<float> {
   __device__ static void store(float* y, const float (&v)[4]) {
     *reinterpret_cast<float4v*>(y) = float4v{v[0], v[1], v[2], v[3]};
   }
+  __device__ static void load(const float* x, float (&v)[4]) {
+    const float4v f = *reinterpret_cast<const float4v*>(x);
+    for (int r = 0; r < 4; ++r) v[r] = f[r];
+  }
 };
 
 template <typename T> struct GemmTile;
 
-template <> struct GemmTile<f16> {
-  static constexpr int BK = GemmBK<f16>::value;
-  static constexpr int AS = BK + 8;     // A tile row stride (elements), rows = M
-  // B tile row stride (elements), rows = K: 64 modulo 256 bytes, so the four
-  // rows of one transposing read (64 bytes each) tile the banks exactly
-  static constexpr int BS = BNC + 32;
-  static constexpr int CH = 8;
-  // acc[i][j]: 32x32 output block (i: m, j: n) of this wave's (32 MB)x64,
-  // held transposed (B^T A^T): lane l has m = l % 32 and four runs of four
-  // consecutive n, so the epilogue stores 4 elements at a time
-  template <int MB>
-  __device__ static void step(const f16* As, const f16* Bs, int wm, int wn, int lane,
-                              float16v (&acc)[MB][2]) {
-    const int G = lane >> 4, t = lane & 15, c = t & 3, ir = t >> 2;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      half8v a[MB], b[2];
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-        a[i] = *reinterpret_cast<const half8v*>(As + (32 * MB * wm + 32 * i + (lane & 31)) * AS +
-                                                16 * ks + 8 * (lane >> 5));
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const f16* base = Bs + (16 * ks + 8 * (G >> 1) + ir) * BS + 64 * wn + 32 * j + 16 * (G & 1) + 4 * c;
-        half4v lo = lds_tr16(base);
-        half4v hi = lds_tr16(base + 4 * BS);
-        b[j] = half8v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
-    }
-  }
-};
-
 template <> struct GemmTile<float> {
-  static constexpr int BK = GemmBK<float>::value;
+  static constexpr int BK = 32;
   static constexpr int AS = BK + 4;
   static constexpr int BS = BNC + 4;
   static constexpr int CH = 4;
@@ -189,8 +159,64 @@ template <> struct GemmTile<float> {
   }
 };
 
-// MB: 32-row blocks of a wave's tile; the workgroup tile is (64 MB) x 128
-// (four waves, 2 x 2).  Taller wave tiles read less LDS per MFMA.
+// Epilogue through LDS: the transposed blocks (element e of acc[i][j] is
+// m = ... + lane % 32, n = ... + 8 (e / 4) + 4 (lane / 32) + e % 4) go with
+// the bias into a row-major tile, which is then stored in 16-byte chunks
+// (Ncol and the head size are multiples of 8, so a chunk stays in one head).
+// Cs: LDS of at least (64 MB) x (BNC + 8) elements, free on entry.
+template <typename T, int MB>
+__device__ __forceinline__ void gemm_epilogue(const float16v (&acc)[MB][2], T* Cs, const GemmParams& p,
+                                              int m0, int n0, int wm, int wn, int lane, int tid) {
+  constexpr int BM = 64 * MB;
+  constexpr int CS = BNC + 8;  // output tile row stride (elements)
+  constexpr int CH = 16 / sizeof(T);
+  const T* bias = static_cast<const T*>(p.bias);
+  // the bias runs of four columns, all loads issued before any is used (Ncol
+  // is a multiple of 4, so a run is wholly inside or wholly past the columns;
+  // a run past them reads the last one and is dropped)
+  float bias4[2][4][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
+      Quad4<T>::load(bias + min(n, p.Ncol - 4), bias4[j][q]);
+    }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
+      const bool in = n0 + nl < p.Ncol;
+      float bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bv[r] = in ? bias4[j][q][r] : 0.f;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int ml = 32 * MB * wm + 32 * i + (lane & 31);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + bv[r];
+        Quad4<T>::store(Cs + ml * CS + nl, v);
+      }
+    }
+  __syncthreads();
+  T* Y = static_cast<T*>(p.y);
+  constexpr int CPR = BNC / CH;  // chunks per tile row
+  for (int c = tid; c < BM * CPR; c += 256) {
+    const int r = c / CPR, cc = (c % CPR) * CH;
+    const int m = m0 + r, n = n0 + cc;
+    if (m >= p.M || n >= p.Ncol) continue;
+    // row-major Y[m][n], or head-major Y[n / hd][m][n % hd] for head size hd
+    const int64_t at = (p.head_dim > 0)
+                           ? ((int64_t)(n / p.head_dim) * p.M + m) * p.head_dim + n % p.head_dim
+                           : (int64_t)m * p.Ncol + n;
+    *reinterpret_cast<uint4v*>(Y + at) = *reinterpret_cast<const uint4v*>(Cs + r * CS + cc);
+  }
+}
+
+// float32 projection.  MB: 32-row blocks of a wave's tile; the workgroup tile
+// is (64 MB) x 128 (four waves, 2 x 2).
 template <typename T, int MB>
 __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmParams p) {
   using G = GemmTile<T>;
@@ -318,43 +344,162 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmParams p) {
   }
 
   mfma_result_fence();
-  // Epilogue through LDS: the transposed blocks (element e of acc[i][j] is
-  // m = ... + lane % 32, n = ... + 8 (e / 4) + 4 (lane / 32) + e % 4) go with
-  // the bias into a row-major tile, which is then stored in 16-byte chunks
-  // (Ncol and the head size are multiples of 8, so a chunk stays in one head).
   // The last loop iteration ended with a barrier, so the stage buffers are free.
-  T* Cs = lds;
-  const T* bias = static_cast<const T*>(p.bias);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int nl = 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
-      float bv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bv[r] = (n0 + nl + r < p.Ncol) ? to_f32(bias[n0 + nl + r]) : 0.f;
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int ml = 32 * MB * wm + 32 * i + (lane & 31);
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + bv[r];
-        Quad4<T>::store(Cs + ml * CS + nl, v);
-      }
+  gemm_epilogue<T, MB>(acc, lds, p, m0, n0, wm, wn, lane, tid);
+}
+
+
+// ---------------------------------------------------------------------------
+// f16 projection with both operands copied from memory straight into LDS
+// (buffer loads to LDS: no register staging, no LDS store instructions),
+// three LDS stages, the copies of tile kt + 2 issued while tile kt is used.
+// A copy instruction fills 64 consecutive 16-byte LDS slots, so the tiles are
+// unpadded and the bank spread comes from XOR swizzles of the 16-byte chunks
+// within a row, applied by choosing which chunk each lane copies:
+//   A (rows of BK = 32 elements, 4 chunks): chunk c of row r in slot
+//     c ^ swz_a(r mod 16); the 16 rows of one operand read land in 16
+//     distinct slots of a 256-byte bank window (and 8 rows in 8 of a 128-byte
+//     one);
+//   B (rows of BNC = 128 elements, 16 chunks): chunk c of row k in slot
+//     c ^ 4 (k mod 4); the eight 64-byte row pieces of one transposing read
+//     cover every bank twice.
+// ---------------------------------------------------------------------------
+constexpr int kDmaStages = 3;
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
+
+// Copy 16 bytes per lane from buffer r at per-lane byte offset voff into LDS
+// at byte address lds + 16 * lane (lds uniform).  The copy is waited for
+// explicitly (vmcnt), so it is a volatile statement the compiler does not
+// count.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               ::"v"(voff), "s"(r), "s"(lds) : "memory");
+}
+
+template <int MB>
+__global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
+  constexpr int BK = 32, BM = 64 * MB;
+  constexpr int A_EL = BM * BK, B_EL = BK * BNC, ST_EL = A_EL + B_EL;   // one stage
+  constexpr int CS = BNC + 8;
+  constexpr int LDS_EL = (kDmaStages * ST_EL > BM * CS) ? kDmaStages * ST_EL : BM * CS;
+  __shared__ __attribute__((aligned(1024))) f16 lds[LDS_EL];
+  static_assert(sizeof(lds) / (sizeof(int32_t)) >= 3 * kGemmSchedMaxB + 1, "schedule fits the tile LDS");
+  // copy instructions per wave and tile: A fills BM / 16 KB-blocks, B eight
+  constexpr int DA = BM / 64, DB = 2;
+  static_assert(A_EL * 2 == 4 * DA * 1024 && B_EL * 2 == 4 * DB * 1024, "whole copy blocks per wave");
+
+  if (p.with_sched) {
+    if (blockIdx.x == 0) {
+      build_schedule(p.sched, reinterpret_cast<int32_t*>(lds));
+      return;
     }
-  __syncthreads();
-  T* Y = static_cast<T*>(p.y);
-  constexpr int CPR = BNC / CH;  // chunks per tile row
-  for (int c = tid; c < BM * CPR; c += 256) {
-    const int r = c / CPR, cc = (c % CPR) * CH;
-    const int m = m0 + r, n = n0 + cc;
-    if (m >= p.M || n >= p.Ncol) continue;
-    // row-major Y[m][n], or head-major Y[n / hd][m][n % hd] for head size hd
-    const int64_t at = (p.head_dim > 0)
-                           ? ((int64_t)(n / p.head_dim) * p.M + m) * p.head_dim + n % p.head_dim
-                           : (int64_t)m * p.Ncol + n;
-    *reinterpret_cast<uint4v*>(Y + at) = *reinterpret_cast<const uint4v*>(Cs + r * CS + cc);
   }
+  const int tile = blockIdx.x - (p.with_sched ? 1 : 0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = (p.Ncol + BNC - 1) / BNC;
+  const int m0 = (tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BNC;
+  const f16* X = static_cast<const f16*>(p.x);
+  const f16* W = static_cast<const f16*>(p.w);
+  const int rows_a = min(p.M - m0, BM);
+  // Per-k-step resources (the range check covers the per-lane offset only):
+  // A from row m0 and column k0 over the tile's valid rows, B from row k0 and
+  // column n0.  Out-of-range chunks read 0 (A rows past M, B rows past K); B
+  // chunks past Ncol reach only output columns that are never stored; A
+  // chunks past K (a partial last step) read the next row and are zeroed.
+  auto rsrc_a = [&](int k0) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<f16*>(X) + (int64_t)m0 * p.K + k0, 0,
+                                             (rows_a * p.K - k0) * 2, kGemmBufferFormat);
+  };
+  auto rsrc_b = [&](int k0) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<f16*>(W) + (int64_t)k0 * p.Ncol + n0, 0,
+                                             ((p.K - k0) * p.Ncol - n0) * 2, kGemmBufferFormat);
+  };
+  // this lane's copy slots: A block q = wave DA + a holds rows 16 q .. 16 q + 15
+  // (four lanes per row); B block q = wave DB + b holds rows 4 q .. 4 q + 3
+  // (sixteen lanes per row)
+  const int ca = (lane & 3) ^ swz_a(lane >> 2);
+  int aoff[DA], boff[DB];
+#pragma unroll
+  for (int a = 0; a < DA; ++a) {
+    const int r = 16 * (wave * DA + a) + (lane >> 2);
+    aoff[a] = (r * p.K + 8 * ca) * 2;
+  }
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    const int k = 4 * (wave * DB + b) + (lane >> 4);
+    boff[b] = (k * p.Ncol + 8 * ((lane & 15) ^ swz_b(k))) * 2;
+  }
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) f16*)lds);
+  auto issue = [&](int kt, int st) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_a(kt * BK), rb = rsrc_b(kt * BK);
+    const uint32_t base = lds0 + 2u * (uint32_t)(st * ST_EL);
+#pragma unroll
+    for (int a = 0; a < DA; ++a) dma16(ra, aoff[a], base + 1024u * (uint32_t)(wave * DA + a));
+#pragma unroll
+    for (int b = 0; b < DB; ++b) dma16(rb, boff[b], base + 2u * A_EL + 1024u * (uint32_t)(wave * DB + b));
+  };
+
+  float16v acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = float16v{};
+
+  // operand read addresses (elements, relative to a stage): A row
+  // 32 MB wm + 32 i + lane % 32 (row mod 16 = lane mod 16), chunk 2 ks + lane / 32;
+  // B rows 16 ks + 8 (G / 2) + ir (+ 4), G = lane / 16, ir = lane / 4 mod 4
+  const int fa = swz_a(lane & 15);
+  const int G = lane >> 4, cq = lane & 3, ir = (lane >> 2) & 3;
+  const int nk = (p.K + BK - 1) / BK;
+  issue(0, 0);
+  issue(min(1, nk - 1), 1);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % kDmaStages;
+    // this wave's copies of tile kt are done (those of tile kt + 1 may run on)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DA + DB) : "memory");
+    if ((kt + 1) * BK > p.K) {
+      // partial last step: A chunks past K hold the next row's elements
+#pragma unroll
+      for (int a = 0; a < DA; ++a)
+        if (kt * BK + 8 * ca >= p.K)
+          *reinterpret_cast<uint4v*>(lds + st * ST_EL + 512 * (wave * DA + a) + 8 * lane) = uint4v{0u, 0u, 0u, 0u};
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zeros land before the barrier
+    }
+    asm volatile("s_barrier" ::: "memory");
+    // stage (kt + 2) mod 3 was read in step kt - 1, which every wave has finished
+    issue(min(kt + 2, nk - 1), (kt + 2) % kDmaStages);
+    const f16* As = lds + st * ST_EL;
+    const f16* Bs = As + A_EL;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      half8v a[MB], b[2];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        a[i] = *reinterpret_cast<const half8v*>(As + (32 * MB * wm + 32 * i + (lane & 31)) * BK +
+                                                8 * ((2 * ks + (lane >> 5)) ^ fa));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int R = 16 * ks + 8 * (G >> 1) + ir;
+        const int ch = 8 * wn + 4 * j + 2 * (G & 1) + (cq >> 1);
+        const f16* base = Bs + R * BNC + 8 * (ch ^ swz_b(R)) + 4 * (cq & 1);
+        half4v lo = lds_tr16(base);
+        half4v hi = lds_tr16(base + 4 * BNC);
+        b[j] = half8v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
+    }
+  }
+  mfma_result_fence();
+  // every copy has landed and every wave is past its last operand read
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  gemm_epilogue<f16, MB>(acc, lds, p, m0, n0, wm, wn, lane, tid);
 }
 
 }  // namespace
@@ -370,7 +515,7 @@ hipError_t launch_qkv_gemm(DType dt, const GemmParams& p, hipStream_t s) {
   const int bm = dt == DType::F16 ? 64 * kGemmMbF16 : 128;
   const int tiles = ((p.M + bm - 1) / bm) * ((p.Ncol + BNC - 1) / BNC) + (p.with_sched ? 1 : 0);
   if (dt == DType::F16)
-    hipLaunchKernelGGL((qkv_gemm_kernel<f16, kGemmMbF16>), dim3(tiles), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((qkv_gemm_dma_kernel<kGemmMbF16>), dim3(tiles), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((qkv_gemm_kernel<float, 2>), dim3(tiles), dim3(256), 0, s, p);
   return hipGetLastError();
