@@ -352,7 +352,8 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // f16 projection with both operands copied from memory straight into LDS
 // (buffer loads to LDS: no register staging, no LDS store instructions),
-// three LDS stages, the copies of tile kt + 2 issued while tile kt is used.
+// kDmaStages LDS stages, the copies of tile kt + kDmaStages - 1 issued while
+// tile kt is used.
 // A copy instruction fills 64 consecutive 16-byte LDS slots, so the tiles are
 // unpadded and the bank spread comes from XOR swizzles of the 16-byte chunks
 // within a row, applied by choosing which chunk each lane copies:
@@ -389,13 +390,20 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
   constexpr int DA = BM / 64, DB = 2;
   static_assert(A_EL * 2 == 4 * DA * 1024 && B_EL * 2 == 4 * DB * 1024, "whole copy blocks per wave");
 
+  // Workgroups are dealt to the eight XCDs round-robin by id; renumbered so
+  // that each XCD takes a contiguous range of tiles (all column tiles of a
+  // few row blocks at a time), whose input rows then stay in its L2.  Id 0
+  // stays 0: the workgroup that builds the attention schedule when asked.
+  const int nwg = gridDim.x, x = blockIdx.x % 8;
+  int idx = blockIdx.x / 8;
+  for (int y = 0; y < x; ++y) idx += (nwg - y + 7) / 8;
   if (p.with_sched) {
-    if (blockIdx.x == 0) {
+    if (idx == 0) {
       build_schedule(p.sched, reinterpret_cast<int32_t*>(lds));
       return;
     }
   }
-  const int tile = blockIdx.x - (p.with_sched ? 1 : 0);
+  const int tile = idx - (p.with_sched ? 1 : 0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -455,12 +463,15 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
   const int fa = swz_a(lane & 15);
   const int G = lane >> 4, cq = lane & 3, ir = (lane >> 2) & 3;
   const int nk = (p.K + BK - 1) / BK;
-  issue(0, 0);
-  issue(min(1, nk - 1), 1);
+  // prologue: tiles 0 .. kDmaStages - 2 in flight (past the last tile: the
+  // last one again, into a stage nothing reads)
+#pragma unroll
+  for (int t = 0; t < kDmaStages - 1; ++t) issue(min(t, nk - 1), t);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt % kDmaStages;
-    // this wave's copies of tile kt are done (those of tile kt + 1 may run on)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DA + DB) : "memory");
+    // this wave's copies of tile kt are done (those of the later tiles in
+    // flight may run on)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDmaStages - 2) * (DA + DB)) : "memory");
     if ((kt + 1) * BK > p.K) {
       // partial last step: A chunks past K hold the next row's elements
 #pragma unroll
@@ -470,8 +481,9 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zeros land before the barrier
     }
     asm volatile("s_barrier" ::: "memory");
-    // stage (kt + 2) mod 3 was read in step kt - 1, which every wave has finished
-    issue(min(kt + 2, nk - 1), (kt + 2) % kDmaStages);
+    // the stage of tile kt + kDmaStages - 1 was read in step kt - 1, which
+    // every wave has finished
+    issue(min(kt + kDmaStages - 1, nk - 1), (kt + kDmaStages - 1) % kDmaStages);
     const f16* As = lds + st * ST_EL;
     const f16* Bs = As + A_EL;
 #pragma unroll
