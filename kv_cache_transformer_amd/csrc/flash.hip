@@ -1386,8 +1386,12 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
       for (int i = 0; i < 16; ++i) t = fminf(t, sc[blk][i]);
     return t;
   };
-  // raw scores u = 2 log2(e) x / c with |x / c| <= 1/4 take the series
-  constexpr float kPolyU = 0.25f * 2.f * kLog2e;
+  // Softcap tiles whose scores all satisfy |x / c| <= tau take tanh from its
+  // odd series through y^3: the next term, 2 y^5 / 15, then changes the
+  // exponent c tanh(x / c) by at most c 2 tau^5 / 15 <= 5e-5 (a tenth of the
+  // f16 rounding of the probabilities), for tau = min(1/4, (7.5e-4 / c)^(1/5)).
+  // In raw scores u = 2 log2(e) x / c the bound is polyU = 2 log2(e) tau.
+  const float polyU = use_cap ? 2.f * kLog2e * fminf(0.25f, fast_exp2(0.2f * __log2f(7.5e-4f / cap))) : 0.f;
   float m = kNegInf, lsum = 0.f;
   float16v sc[2];
   half8v pb[4];
@@ -1399,11 +1403,9 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
     if (plain) {
       tmax = raw_max(sc);
       if (use_cap) {
-        // tanh by its odd series through y^5 where every raw score of the
-        // wave's tile is small (|y| = |x / c| <= 1/4): one exp2 per score
-        // instead of three, with a relative error in tanh below 1.3e-5 (under
-        // the f16 rounding of the probabilities)
-        poly = __all(fmaxf(tmax, -raw_min(sc)) <= kPolyU);
+        // the series (one exp2 per score instead of three) where every raw
+        // score of the wave's tile is small
+        poly = __all(fmaxf(tmax, -raw_min(sc)) <= polyU);
         tmax = capA - capB * fast_rcp(fast_exp2(tmax) + 1.f);
       }
     } else {
@@ -1426,15 +1428,15 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
     }
     const float muse = (m == kNegInf) ? 0.f : m;
     if (use_cap && poly) {
-      // exponent = (c / 2) u (1 - y^2 / 3 + 2 y^4 / 15), y^2 = u^2 / (4 log2(e)^2)
+      // exponent = (c / 2) u (1 - y^2 / 3), y^2 = u^2 / (4 log2(e)^2)
       constexpr float k2 = 0.12011325347955035f;  // 1 / (4 log2(e)^2)
-      const float a0 = 0.5f * cap, a1 = -a0 * k2 / 3.f, a2 = a0 * 2.f * k2 * k2 / 15.f;
+      const float a0 = 0.5f * cap, a1 = -a0 * k2 / 3.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float u = sc[q >> 1][8 * (q & 1) + i], w2 = u * u;
-          pb[q][i] = (f16)fast_exp2(fmaf(u, fmaf(w2, fmaf(w2, a2, a1), a0), -muse));
+          pb[q][i] = (f16)fast_exp2(fmaf(u, fmaf(w2, a1, a0), -muse));
         }
     } else if (use_cap && plain) {
       const float c0 = capA - muse;
