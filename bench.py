@@ -106,6 +106,8 @@ class Timer:
     and its dominant kernel by HIP events that the library records on the same
     stream around that kernel's launch (kvattn_profile_events), so for every
     call the kernel interval lies inside the call interval (kernel <= call).
+    The calls are enqueued behind a spin kernel, so they run back to back on
+    the GPU and the intervals hold GPU time only.
     Graph: the same number of calls captured in one HIP graph and replayed
     between two events, so that host launch overhead is not part of the time
     (the figure `value` is computed from)."""
@@ -122,6 +124,10 @@ class Timer:
         ke = [self.hip.create() for _ in range(steps)]
         cs = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ce = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        # A spin kernel ahead of the timed calls keeps the GPU busy while the
+        # host enqueues them, so the calls then run back to back and no host
+        # launch latency falls inside an event interval.
+        torch.cuda._sleep(int(2e6 + 4e5 * steps))
         for i in range(steps):
             cs[i].record()
             self.lib.kvattn_profile_events(ks[i], ke[i], self.kind)

@@ -18,6 +18,11 @@
 
 using namespace kvattn;
 
+kvattn::LaunchEvents& kvattn::launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -41,16 +46,15 @@ thread_local int g_prof_kind = 0;
 // 0 = kDecodeWavesPerCu)
 thread_local int g_decode_waves_per_cu = 0;
 
-// Launch `f` bracketed by the profiling events when `kind` is the one asked for.
+// Run the launcher `f`; when `kind` is the one asked for, its first kernel
+// records its own start and stop on the profiling events.
 template <typename F>
 hipError_t profiled(int kind, hipStream_t st, F&& f) {
+  (void)st;
   const bool on = g_prof_kind == kind && g_prof_start != nullptr && g_prof_stop != nullptr;
-  if (on) {
-    hipError_t e = hipEventRecord(g_prof_start, st);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = f();
-  if (on && e == hipSuccess) e = hipEventRecord(g_prof_stop, st);
+  if (on) launch_events() = LaunchEvents{g_prof_start, g_prof_stop};
+  const hipError_t e = f();
+  launch_events() = LaunchEvents{};
   return e;
 }
 

@@ -1374,7 +1374,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
 template <typename T, int HP, int FEAT>
 hipError_t launch_decode_f(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<T, HP, FEAT>), dim3(p.waves / kWavesPerGroup), dim3(kThreads),
+  launch_kernel((decode_kernel<T, HP, FEAT>), dim3(p.waves / kWavesPerGroup), dim3(kThreads),
                      0, s, p);
   return hipGetLastError();
 }

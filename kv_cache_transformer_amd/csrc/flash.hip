@@ -1617,9 +1617,9 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
 
 template <typename T, int HP, int BN, int MODE, bool SOFTCAP = false>
 hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
-  if (nw == 4) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 4, SOFTCAP>), grid, dim3(256), 0, s, p);
-  else if (nw == 2) hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 2, SOFTCAP>), grid, dim3(128), 0, s, p);
-  else hipLaunchKernelGGL((flash_kernel<T, HP, BN, MODE, 1, SOFTCAP>), grid, dim3(64), 0, s, p);
+  if (nw == 4) launch_kernel((flash_kernel<T, HP, BN, MODE, 4, SOFTCAP>), grid, dim3(256), 0, s, p);
+  else if (nw == 2) launch_kernel((flash_kernel<T, HP, BN, MODE, 2, SOFTCAP>), grid, dim3(128), 0, s, p);
+  else launch_kernel((flash_kernel<T, HP, BN, MODE, 1, SOFTCAP>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1632,7 +1632,7 @@ hipError_t launch_pp(const FlashParams& p, dim3 grid, hipStream_t s) {
   const int pairs = (MODE == kDense) ? (int)grid.x * (((int)grid.y + 1) / 2) * (int)grid.z : (items + 1) / 2;
   const int wgs = std::min(pairs, cu_count());
   if (wgs <= 0) return hipSuccess;
-  hipLaunchKernelGGL((flash_pp_kernel<HP, MODE, SOFTCAP>), dim3(wgs), dim3(512), 0, s, p,
+  launch_kernel((flash_pp_kernel<HP, MODE, SOFTCAP>), dim3(wgs), dim3(512), 0, s, p,
                      (int)grid.x, (int)grid.y, (int)grid.z);
   return hipGetLastError();
 }
@@ -1651,8 +1651,8 @@ hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
         return launch_pp<HP, kDense, false>(p, grid, s);
       } else {
         if (nw != 4) return hipErrorInvalidValue;
-        if (p.softcap > 0.f) hipLaunchKernelGGL((flash_kernel<T, HP, BN, kDense, 4, true>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((flash_kernel<T, HP, BN, kDense, 4, false>), grid, dim3(256), 0, s, p);
+        if (p.softcap > 0.f) launch_kernel((flash_kernel<T, HP, BN, kDense, 4, true>), grid, dim3(256), 0, s, p);
+        else launch_kernel((flash_kernel<T, HP, BN, kDense, 4, false>), grid, dim3(256), 0, s, p);
         return hipGetLastError();
       }
     }
@@ -1664,7 +1664,7 @@ hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
       if constexpr (kPipe) {
         if (p.rows_per_wg / 32 * p.heads_per_wg == 4) return launch_pp<HP, kVarlen>(p, grid, s);
       }
-      hipLaunchKernelGGL((flash_kernel<T, HP, BN, kVarlen, 4, false>), grid, dim3(256), 0, s, p);
+      launch_kernel((flash_kernel<T, HP, BN, kVarlen, 4, false>), grid, dim3(256), 0, s, p);
       return hipGetLastError();
   }
 }

@@ -2,11 +2,36 @@
 // Parameter blocks are plain structs passed by value to the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace kvattn {
+
+// Measurement hook: events the next kernel launch takes its start and stop
+// times on (the dispatch's own timestamps), or null.  Thread-local, set by the
+// C ABI around the launch it profiles.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+// Launch a kernel on stream s (errors are left for hipGetLastError).  When
+// launch_events() holds events, this launch records its start and stop on
+// them and clears them.
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                          Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.start != nullptr) {
+    const hipEvent_t start = ev.start, stop = ev.stop;
+    ev = LaunchEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, start, stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  }
+}
 
 // Q8: float32 activations over an int8 key/value cache (decode, and the
 // byte copies of such a cache)

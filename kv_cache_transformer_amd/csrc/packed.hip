@@ -92,8 +92,12 @@ constexpr int BNC = 128;
 constexpr int kGemmStages = 3;
 // buffer resource word 3 for raw 32-bit buffer accesses (gfx9 family)
 constexpr int kGemmBufferFormat = 0x00020000;
-// 32-row blocks per wave of the f16 GEMM (workgroup tile 256 x 128)
+// f16 GEMM: 32-row blocks per wave, waves across the columns (64 columns
+// each), LDS stages and workgroups per CU (workgroup tile 256 x 128)
 constexpr int kGemmMbF16 = 4;
+constexpr int kGemmNwnF16 = 2;
+constexpr int kGemmStagesF16 = 3;
+constexpr int kGemmOccF16 = 2;
 
 // Calls f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>).
 template <int N, typename F, int... Is>
@@ -163,12 +167,12 @@ template <> struct GemmTile<float> {
 // m = ... + lane % 32, n = ... + 8 (e / 4) + 4 (lane / 32) + e % 4) go with
 // the bias into a row-major tile, which is then stored in 16-byte chunks
 // (Ncol and the head size are multiples of 8, so a chunk stays in one head).
-// Cs: LDS of at least (64 MB) x (BNC + 8) elements, free on entry.
-template <typename T, int MB>
+// Cs: LDS of at least (64 MB) x (BN + 8) elements, free on entry; NT threads.
+template <typename T, int MB, int BN = BNC, int NT = 256>
 __device__ __forceinline__ void gemm_epilogue(const float16v (&acc)[MB][2], T* Cs, const GemmParams& p,
                                               int m0, int n0, int wm, int wn, int lane, int tid) {
   constexpr int BM = 64 * MB;
-  constexpr int CS = BNC + 8;  // output tile row stride (elements)
+  constexpr int CS = BN + 8;  // output tile row stride (elements)
   constexpr int CH = 16 / sizeof(T);
   const T* bias = static_cast<const T*>(p.bias);
   // the bias runs of four columns, all loads issued before any is used (Ncol
@@ -202,8 +206,8 @@ __device__ __forceinline__ void gemm_epilogue(const float16v (&acc)[MB][2], T* C
     }
   __syncthreads();
   T* Y = static_cast<T*>(p.y);
-  constexpr int CPR = BNC / CH;  // chunks per tile row
-  for (int c = tid; c < BM * CPR; c += 256) {
+  constexpr int CPR = BN / CH;  // chunks per tile row
+  for (int c = tid; c < BM * CPR; c += NT) {
     const int r = c / CPR, cc = (c % CPR) * CH;
     const int m = m0 + r, n = n0 + cc;
     if (m >= p.M || n >= p.Ncol) continue;
@@ -352,8 +356,8 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // f16 projection with both operands copied from memory straight into LDS
 // (buffer loads to LDS: no register staging, no LDS store instructions),
-// kDmaStages LDS stages, the copies of tile kt + kDmaStages - 1 issued while
-// tile kt is used.
+// a few LDS stages, the copies of tile kt + stages - 1 issued while tile kt
+// is used.
 // A copy instruction fills 64 consecutive 16-byte LDS slots, so the tiles are
 // unpadded and the bank spread comes from XOR swizzles of the 16-byte chunks
 // within a row, applied by choosing which chunk each lane copies:
@@ -361,11 +365,10 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmParams p) {
 //     c ^ swz_a(r mod 16); the 16 rows of one operand read land in 16
 //     distinct slots of a 256-byte bank window (and 8 rows in 8 of a 128-byte
 //     one);
-//   B (rows of BNC = 128 elements, 16 chunks): chunk c of row k in slot
+//   B (rows of the tile's 64 NWN columns): chunk c of row k in slot
 //     c ^ 4 (k mod 4); the eight 64-byte row pieces of one transposing read
 //     cover every bank twice.
 // ---------------------------------------------------------------------------
-constexpr int kDmaStages = 3;
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
 
@@ -378,17 +381,20 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32
                ::"v"(voff), "s"(r), "s"(lds) : "memory");
 }
 
-template <int MB>
-__global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
-  constexpr int BK = 32, BM = 64 * MB;
-  constexpr int A_EL = BM * BK, B_EL = BK * BNC, ST_EL = A_EL + B_EL;   // one stage
-  constexpr int CS = BNC + 8;
-  constexpr int LDS_EL = (kDmaStages * ST_EL > BM * CS) ? kDmaStages * ST_EL : BM * CS;
+// MB: 32-row blocks of a wave's tile (the tile has 64 MB rows); NWN: waves
+// across the tile's columns (64 each; 2 NWN waves in all); STAGES: LDS
+// stages; OCC: workgroups per CU the launch bounds ask for.
+template <int MB, int NWN, int STAGES, int OCC>
+__global__ __launch_bounds__(128 * NWN, OCC) void qkv_gemm_dma_kernel(GemmParams p) {
+  constexpr int BK = 32, BM = 64 * MB, BN = 64 * NWN, NT = 128 * NWN, NWAVE = 2 * NWN;
+  constexpr int A_EL = BM * BK, B_EL = BK * BN, ST_EL = A_EL + B_EL;   // one stage
+  constexpr int CS = BN + 8;
+  constexpr int LDS_EL = (STAGES * ST_EL > BM * CS) ? STAGES * ST_EL : BM * CS;
   __shared__ __attribute__((aligned(1024))) f16 lds[LDS_EL];
   static_assert(sizeof(lds) / (sizeof(int32_t)) >= 3 * kGemmSchedMaxB + 1, "schedule fits the tile LDS");
-  // copy instructions per wave and tile: A fills BM / 16 KB-blocks, B eight
-  constexpr int DA = BM / 64, DB = 2;
-  static_assert(A_EL * 2 == 4 * DA * 1024 && B_EL * 2 == 4 * DB * 1024, "whole copy blocks per wave");
+  // copy instructions (1 KB each) per wave and tile; B rows per instruction
+  constexpr int DA = BM / 16 / NWAVE, DB = BN / 16 / NWAVE, BLR = BN / 8, BRI = 64 / BLR;
+  static_assert(A_EL * 2 == NWAVE * DA * 1024 && B_EL * 2 == NWAVE * DB * 1024, "whole copy blocks per wave");
 
   // Workgroups are dealt to the eight XCDs round-robin by id; renumbered so
   // that each XCD takes a contiguous range of tiles (all column tiles of a
@@ -406,10 +412,10 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
   const int tile = idx - (p.with_sched ? 1 : 0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_n = (p.Ncol + BNC - 1) / BNC;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int tiles_n = (p.Ncol + BN - 1) / BN;
   const int m0 = (tile / tiles_n) * BM;
-  const int n0 = (tile % tiles_n) * BNC;
+  const int n0 = (tile % tiles_n) * BN;
   const f16* X = static_cast<const f16*>(p.x);
   const f16* W = static_cast<const f16*>(p.w);
   const int rows_a = min(p.M - m0, BM);
@@ -427,8 +433,8 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
                                              ((p.K - k0) * p.Ncol - n0) * 2, kGemmBufferFormat);
   };
   // this lane's copy slots: A block q = wave DA + a holds rows 16 q .. 16 q + 15
-  // (four lanes per row); B block q = wave DB + b holds rows 4 q .. 4 q + 3
-  // (sixteen lanes per row)
+  // (four lanes per row); B block q = wave DB + b holds rows BRI q ..
+  // BRI q + BRI - 1 (BLR lanes per row)
   const int ca = (lane & 3) ^ swz_a(lane >> 2);
   int aoff[DA], boff[DB];
 #pragma unroll
@@ -438,8 +444,8 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
   }
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
-    const int k = 4 * (wave * DB + b) + (lane >> 4);
-    boff[b] = (k * p.Ncol + 8 * ((lane & 15) ^ swz_b(k))) * 2;
+    const int k = BRI * (wave * DB + b) + lane / BLR;
+    boff[b] = (k * p.Ncol + 8 * ((lane % BLR) ^ swz_b(k))) * 2;
   }
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) f16*)lds);
   auto issue = [&](int kt, int st) {
@@ -463,15 +469,15 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
   const int fa = swz_a(lane & 15);
   const int G = lane >> 4, cq = lane & 3, ir = (lane >> 2) & 3;
   const int nk = (p.K + BK - 1) / BK;
-  // prologue: tiles 0 .. kDmaStages - 2 in flight (past the last tile: the
+  // prologue: tiles 0 .. STAGES - 2 in flight (past the last tile: the
   // last one again, into a stage nothing reads)
 #pragma unroll
-  for (int t = 0; t < kDmaStages - 1; ++t) issue(min(t, nk - 1), t);
+  for (int t = 0; t < STAGES - 1; ++t) issue(min(t, nk - 1), t);
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt % kDmaStages;
+    const int st = kt % STAGES;
     // this wave's copies of tile kt are done (those of the later tiles in
     // flight may run on)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDmaStages - 2) * (DA + DB)) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * (DA + DB)) : "memory");
     if ((kt + 1) * BK > p.K) {
       // partial last step: A chunks past K hold the next row's elements
 #pragma unroll
@@ -481,9 +487,9 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zeros land before the barrier
     }
     asm volatile("s_barrier" ::: "memory");
-    // the stage of tile kt + kDmaStages - 1 was read in step kt - 1, which
-    // every wave has finished
-    issue(min(kt + kDmaStages - 1, nk - 1), (kt + kDmaStages - 1) % kDmaStages);
+    // the stage of tile kt + STAGES - 1 was read in step kt - 1, which every
+    // wave has finished
+    issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
     const f16* As = lds + st * ST_EL;
     const f16* Bs = As + A_EL;
 #pragma unroll
@@ -497,9 +503,9 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
       for (int j = 0; j < 2; ++j) {
         const int R = 16 * ks + 8 * (G >> 1) + ir;
         const int ch = 8 * wn + 4 * j + 2 * (G & 1) + (cq >> 1);
-        const f16* base = Bs + R * BNC + 8 * (ch ^ swz_b(R)) + 4 * (cq & 1);
+        const f16* base = Bs + R * BN + 8 * (ch ^ swz_b(R)) + 4 * (cq & 1);
         half4v lo = lds_tr16(base);
-        half4v hi = lds_tr16(base + 4 * BNC);
+        half4v hi = lds_tr16(base + 4 * BN);
         b[j] = half8v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
 #pragma unroll
@@ -511,25 +517,27 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_dma_kernel(GemmParams p) {
   mfma_result_fence();
   // every copy has landed and every wave is past its last operand read
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  gemm_epilogue<f16, MB>(acc, lds, p, m0, n0, wm, wn, lane, tid);
+  gemm_epilogue<f16, MB, BN, NT>(acc, lds, p, m0, n0, wm, wn, lane, tid);
 }
 
 }  // namespace
 
 hipError_t launch_packed_sched(const PackedSchedParams& p, hipStream_t s) {
   size_t shmem = sizeof(int32_t) * (3 * (size_t)p.B + 1);
-  hipLaunchKernelGGL(packed_sched_kernel, dim3(1), dim3(256), shmem, s, p);
+  launch_kernel(packed_sched_kernel, dim3(1), dim3(256), shmem, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_gemm(DType dt, const GemmParams& p, hipStream_t s) {
   if (p.M == 0 && !p.with_sched) return hipSuccess;
   const int bm = dt == DType::F16 ? 64 * kGemmMbF16 : 128;
-  const int tiles = ((p.M + bm - 1) / bm) * ((p.Ncol + BNC - 1) / BNC) + (p.with_sched ? 1 : 0);
+  const int bn = dt == DType::F16 ? 64 * kGemmNwnF16 : BNC;
+  const int tiles = ((p.M + bm - 1) / bm) * ((p.Ncol + bn - 1) / bn) + (p.with_sched ? 1 : 0);
   if (dt == DType::F16)
-    hipLaunchKernelGGL((qkv_gemm_dma_kernel<kGemmMbF16>), dim3(tiles), dim3(256), 0, s, p);
+    launch_kernel((qkv_gemm_dma_kernel<kGemmMbF16, kGemmNwnF16, kGemmStagesF16, kGemmOccF16>),
+                       dim3(tiles), dim3(128 * kGemmNwnF16), 0, s, p);
   else
-    hipLaunchKernelGGL((qkv_gemm_kernel<float, 2>), dim3(tiles), dim3(256), 0, s, p);
+    launch_kernel((qkv_gemm_kernel<float, 2>), dim3(tiles), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -373,9 +373,9 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
     const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
     const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 8192);
     if (dt == DType::F16)
-      hipLaunchKernelGGL(prep_kv_kernel<f16>, dim3((int)blocks), dim3(kPrepThreads), 0, s, p);
+      launch_kernel(prep_kv_kernel<f16>, dim3((int)blocks), dim3(kPrepThreads), 0, s, p);
     else
-      hipLaunchKernelGGL(prep_kv_kernel<float>, dim3((int)blocks), dim3(kPrepThreads), 0, s, p);
+      launch_kernel(prep_kv_kernel<float>, dim3((int)blocks), dim3(kPrepThreads), 0, s, p);
     return hipGetLastError();
   }
   // few tokens (decode-sized calls): the heads of a token are spread over
@@ -384,9 +384,9 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
   const int gy = (p.B * p.S < 1024) ? std::min((items + 3) / 4, 16) : 1;
   dim3 grid(p.B * p.S, std::max(gy, 1));
   if (dt == DType::F16)
-    hipLaunchKernelGGL(prep_kernel<f16>, grid, dim3(kPrepThreads), 0, s, p);
+    launch_kernel(prep_kernel<f16>, grid, dim3(kPrepThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(prep_kernel<float>, grid, dim3(kPrepThreads), 0, s, p);
+    launch_kernel(prep_kernel<float>, grid, dim3(kPrepThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -394,9 +394,9 @@ hipError_t launch_window_shift(DType dt, const WindowShiftParams& p, hipStream_t
   const int slabs = p.B * p.kvN;
   if (slabs == 0) return hipSuccess;
   if (dt == DType::F16)
-    hipLaunchKernelGGL(window_shift_kernel<f16>, dim3(slabs), dim3(kShiftThreads), 0, s, p);
+    launch_kernel(window_shift_kernel<f16>, dim3(slabs), dim3(kShiftThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(window_shift_kernel<float>, dim3(slabs), dim3(kShiftThreads), 0, s, p);
+    launch_kernel(window_shift_kernel<float>, dim3(slabs), dim3(kShiftThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -407,11 +407,11 @@ hipError_t launch_copy_past(DType dt, const CopyPastParams& p, hipStream_t s) {
   if (gx < 1) gx = 1;
   dim3 grid(gx, p.kvN, p.B);
   if (dt == DType::F16)
-    hipLaunchKernelGGL(copy_past_kernel<f16>, grid, dim3(256), 0, s, p);
+    launch_kernel(copy_past_kernel<f16>, grid, dim3(256), 0, s, p);
   else if (dt == DType::Q8)
-    hipLaunchKernelGGL(copy_past_kernel<int8_t>, grid, dim3(256), 0, s, p);
+    launch_kernel(copy_past_kernel<int8_t>, grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(copy_past_kernel<float>, grid, dim3(256), 0, s, p);
+    launch_kernel(copy_past_kernel<float>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
