@@ -108,10 +108,11 @@ int32_t kvattn_version(void);
 
 /*
  * Measurement hook.  After kvattn_profile_events(start, stop, kind) on a
- * thread, every later call on that thread records the caller-owned HIP events
- * `start` and `stop` (hipEvent_t, created by the caller) on the call's stream
- * immediately before and after the launch of its kernel of the given kind, so
- * hipEventElapsedTime(start, stop) is that kernel's duration.  kind selects:
+ * thread, in every later call on that thread the first kernel of the given
+ * kind is launched so that it records its own dispatch start and stop times
+ * on the caller-owned HIP events `start` and `stop` (hipEvent_t, created by
+ * the caller), so hipEventElapsedTime(start, stop) is that kernel's duration.
+ * kind selects:
  *   KVATTN_PROFILE_DECODE   split-key decode kernel (gqa_attention decode, decode_mha)
  *   KVATTN_PROFILE_FLASH    tiled attention kernel (prefill, sparse, packed)
  *   KVATTN_PROFILE_PREP     norm/rotary/append kernel
