@@ -127,7 +127,7 @@ class Timer:
         # A spin kernel ahead of the timed calls keeps the GPU busy while the
         # host enqueues them, so the calls then run back to back and no host
         # launch latency falls inside an event interval.
-        torch.cuda._sleep(int(2e6 + 4e5 * steps))
+        torch.cuda._sleep(int(1e6 + 2e5 * steps))
         for i in range(steps):
             cs[i].record()
             self.lib.kvattn_profile_events(ks[i], ke[i], self.kind)
@@ -497,7 +497,7 @@ TRAFFIC_KERNELS = [
      "gqa_long_prefill"),
     ("flash_sparse_prompt", r"flash_kernelIDF16_Li128ELi\d+ELi1E", "kv_cache_transformer_amd/csrc/flash.hip",
      "sparse_prompt", lambda grid: grid >= 1 << 20),
-    ("qkv_gemm_packed_varlen", r"qkv_gemm_kernelIDF16_", "kv_cache_transformer_amd/csrc/packed.hip",
+    ("qkv_gemm_packed_varlen", r"qkv_gemm_dma_kernel", "kv_cache_transformer_amd/csrc/packed.hip",
      "packed_varlen"),
     ("window_shift_gqa_window_decode", r"window_shift_kernelIDF16_", "kv_cache_transformer_amd/csrc/prep.hip",
      "gqa_window_decode"),
@@ -608,7 +608,7 @@ def summarise_counters(d, cmd):
     import csv
     import glob
     import re
-    pat = re.compile(r"(flash_pp_kernel|flash_pipe_kernel|flash_kernel|decode_kernel|qkv_gemm_kernel|prep_kv_kernel|"
+    pat = re.compile(r"(flash_pp_kernel|flash_kernel|decode_kernel|qkv_gemm_dma_kernel|qkv_gemm_kernel|prep_kv_kernel|"
                      r"window_shift_kernel|prep_kernel|packed_sched_kernel)(?:I(DF16_|f)(?:Li(\d+)ELi(\d+)(?:ELi(\d+))?)?)?")
     agg, dur = {}, {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -618,7 +618,7 @@ def summarise_counters(d, cmd):
                 continue
             t = {"DF16_": "f16", "f": "f32", None: ""}[m.group(2)]
             hd, md = m.group(3), m.group(5)
-            pm = re.search(r"flash_p(?:ipe|p)_kernel(?:ILi(\d+)ELi(\d+)E|<(\d+), (\d+),)", r["Kernel_Name"])
+            pm = re.search(r"flash_pp_kernel(?:ILi(\d+)ELi(\d+)E|<(\d+), (\d+),)", r["Kernel_Name"])
             if pm:  # f16 only; template arguments (head, mode, ...)
                 t, hd, md = "f16", pm.group(1) or pm.group(3), pm.group(2) or pm.group(4)
             dm = re.search(r"<float(?:, (\d+), (\d+), (\d+))?", r["Kernel_Name"])
