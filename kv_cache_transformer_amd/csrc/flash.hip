@@ -418,7 +418,31 @@ template <int MODE, int BN> struct FlashWork {
     // remap gives each XCD a contiguous range of (row block, head group,
     // sample) items, so the workgroups sharing a K/V slab share one L2.
     if (MODE != kVarlen) id = xcd_grouped(id, gx * gy * gz);
+    if (MODE == kCsr) id = csr_order(p, id, gx, gy);
     return init_item(p, wave, id, gx, gy, gz);
+  }
+
+  // Block-sparse prompts with one head per workgroup: the heads of one kv
+  // head take the same group of kCsrRowGroup row blocks together (row block
+  // fastest, then head, then row group, then kv head and sample), so the
+  // K/V blocks in flight on an XCD are the local and vertical blocks of a
+  // few dozen row blocks of one slab, which fit its L2.  Maps a position in
+  // that order to the item id init_item expects.
+  static constexpr int kCsrRowGroup = 16;
+  __device__ static int csr_order(const FlashParams& p, int id, int gx, int gy) {
+    const int g = p.N / p.kvN;
+    if (p.heads_per_wg != 1 || gx % kCsrRowGroup != 0 || gy != p.N) return id;
+    int t = id;
+    const int r = t % kCsrRowGroup;
+    t /= kCsrRowGroup;
+    const int hh = t % g;
+    t /= g;
+    const int ng = gx / kCsrRowGroup;
+    const int rg = t % ng;
+    t /= ng;
+    const int kvh = t % p.kvN;
+    const int b = t / p.kvN;
+    return (rg * kCsrRowGroup + r) + gx * ((kvh * g + hh) + gy * b);
   }
 
   // linear id -> id of a contiguous per-XCD range (n ids dealt round-robin
