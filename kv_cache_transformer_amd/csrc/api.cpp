@@ -183,7 +183,7 @@ struct GqaPlan {
   // decode
   int head_groups, hpw;
   int64_t waves;
-  size_t ws_cnt, ws_q, ws_part, ws_deq, ws_total;  // workspace: counters first
+  size_t ws_cnt, ws_q, ws_part, ws_total;  // workspace: counters first
 };
 
 // Quantised-cache attributes and scales (GroupQueryAttention page,
@@ -341,7 +341,6 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   P.ws_cnt = 0;
   P.ws_q = 0;
   P.ws_part = 0;
-  P.ws_deq = 0;
   if (P.decode) {
     const int g = P.N / P.kvN;
     P.head_groups = (g + 15) / 16;
@@ -351,9 +350,7 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode: too many (sample, head) units");
     P.ws_part = align256((size_t)(P.waves / 2) * P.hpw * (P.HP + 4) * sizeof(float));
   }
-  if (P.bits != 0 && !P.decode)  // prompt: the dequantised keys and values, float32 (B, kvN, S, H) each
-    P.ws_deq = 2 * align256((size_t)P.B * P.kvN * P.S * P.H * sizeof(float));
-  const size_t body = P.ws_q + P.ws_part + P.ws_deq;
+  const size_t body = P.ws_q + P.ws_part;
   P.ws_cnt = body ? kCounterBytes : 0;
   P.ws_total = P.ws_cnt + body;
   return KVATTN_OK;
@@ -460,20 +457,15 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   pp.write_q = 0;
   pp.write_kv = 1;
   pp.win_cap = P.window_cache ? P.cap : 0;
-  // quantised prompt: codes into the present caches, dequantised rows into
-  // the workspace, which the attention reads
-  float* deq_k = nullptr;
-  float* deq_v = nullptr;
+  // quantised prompt: codes into the present caches, which the attention
+  // reads and widens itself (no float copy)
   if (P.bits != 0) {
-    deq_k = reinterpret_cast<float*>(wsb + P.ws_cnt + P.ws_q + P.ws_part);
-    deq_v = reinterpret_cast<float*>(wsb + P.ws_cnt + P.ws_q + P.ws_part + P.ws_deq / 2);
     pp.bits = P.bits;
     pp.kq = ck.data;
     pp.vq = cv.data;
     pp.qcap = P.cap;
-    pp.kc = deq_k;
-    pp.vc = deq_v;
-    pp.cap = P.S;
+    pp.kc = nullptr;
+    pp.vc = nullptr;
     pp.k_scale = static_cast<const float*>(in[GQA_IN_K_SCALE].data);
     pp.v_scale = static_cast<const float*>(in[GQA_IN_V_SCALE].data);
     pp.k_scale_pc = P.k_pc;
@@ -494,11 +486,18 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   f.q_s = (int64_t)P.N * P.H;
   f.q_b = f.q_s * P.S;
   f.q_h = P.H;
-  f.kc = P.bits != 0 ? deq_k : ck.data;
-  f.vc = P.bits != 0 ? deq_v : cv.data;
+  f.kc = ck.data;
+  f.vc = cv.data;
   f.k_j = P.H;
-  f.k_h = (int64_t)(P.bits != 0 ? P.S : P.cap) * P.H;
+  f.k_h = (int64_t)P.cap * P.H;
   f.k_b = f.k_h * P.kvN;
+  if (P.bits != 0) {
+    f.qbits = P.bits;
+    f.qk_scale = static_cast<const float*>(in[GQA_IN_K_SCALE].data);
+    f.qv_scale = static_cast<const float*>(in[GQA_IN_V_SCALE].data);
+    f.qk_pc = P.k_pc;
+    f.qv_pc = P.v_pc;
+  }
   f.out = out[GQA_OUT_OUTPUT].data;
   f.o_s = (int64_t)P.N * P.H;
   f.o_b = f.o_s * P.S;
@@ -518,7 +517,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   f.win_cap = P.window_cache ? P.cap : 0;
   f.causal = a->causal;
   f.window = a->local_window_size;
-  f.kv_rows = P.bits != 0 ? P.S : P.cap;
+  f.kv_rows = P.cap;
   f.B = P.B; f.S = P.S; f.N = P.N; f.kvN = P.kvN; f.H = P.H;
   f.scale = scale;
   f.softcap = a->softcap;

@@ -677,10 +677,50 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
   // ahead into a second register stage.
   constexpr int kStages = (kPrefetch && HP <= 64) ? 2 : 1;
   uint4v stage2[kStages == 2 ? CPT : 1];
+  // Quantised caches (float32 dense prompts): the tiles are read as codes (4 bytes
+  // of int8 or 2 bytes of nibbles per 4-element chunk) and widened to
+  // code * scale, the product the prep of a float cache would store, as they
+  // go into LDS.  A thread's columns are fixed, so are its scales.
+  constexpr bool kQ = std::is_same<T, float>::value && MODE == kDense && kPrefetch;
+  const int qb = kQ ? p.qbits : 0;
+  float ksc[4] = {0.f, 0.f, 0.f, 0.f}, vsc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (kQ && qb != 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = min(dload + i, H - 1);
+      ksc[i] = p.qk_pc ? p.qk_scale[(int64_t)w.kvh * H + d] : p.qk_scale[0];
+      vsc[i] = p.qv_pc ? p.qv_scale[(int64_t)w.kvh * H + d] : p.qv_scale[0];
+    }
+  }
+  auto widen = [&](uint32_t word, const float (&sc)[4]) -> uint4v {
+    float f[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = qb == 8 ? (int)(int8_t)(word >> (8 * i)) : (int)((word >> (4 * i)) & 15u) - 8;
+      f[i] = (float)c * sc[i];
+    }
+    return uint4v{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+  };
   auto load_tile_to = [&](int t, uint4v* dst) {
     const TileRange r = tile_range(t);
     // uniform base at the tile's first row; per-thread 32-bit offsets
     const int last = min(max(r.start, r.lim - 1), p.kv_rows - 1) - r.start;
+    if (kQ && qb != 0) {
+      // element e of the code caches sits at byte e (int8) or e / 2 (int4)
+      const int sh = qb == 4 ? 1 : 0;
+      const int64_t e0 = kv_base + (int64_t)r.start * p.k_j;
+      const uint8_t* kt8 = static_cast<const uint8_t*>(p.kc) + (e0 >> sh);
+      const uint8_t* vt8 = static_cast<const uint8_t*>(p.vc) + (e0 >> sh);
+#pragma unroll
+      for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
+        const int off = (min(row0 + RSTEP * (u % KU), last) * kj + dload) >> sh;
+        const uint8_t* src = (u < KU ? kt8 : vt8) + off;
+        const uint32_t word = qb == 8 ? *reinterpret_cast<const uint32_t*>(src)
+                                      : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
+        dst[u] = uint4v{word, 0u, 0u, 0u};
+      }
+      return;
+    }
     const T* kt = kg + kv_base + (int64_t)r.start * p.k_j;
     const T* vt = vg + kv_base + (int64_t)r.start * p.k_j;
 #pragma unroll
@@ -697,7 +737,8 @@ __global__ __launch_bounds__(64 * NW, (FlashOcc<NW, HP>::waves_per_simd)) void f
     for (int u = 0; u < (kPrefetch ? CPT : 1); ++u) {
       const int row = row0 + RSTEP * (u % KU);
       T* dst = u < KU ? base + row * KS + d0 : base + BN * KS + row * VS + d0;
-      if (!(pad_cols && zero_col)) *reinterpret_cast<uint4v*>(dst) = srcs[u];
+      if (!(pad_cols && zero_col))
+        *reinterpret_cast<uint4v*>(dst) = (kQ && qb != 0) ? widen(srcs[u][0], u < KU ? ksc : vsc) : srcs[u];
     }
   };
   auto store_tile = [&](int buf) { store_tile_from(buf, stage); };
@@ -1699,6 +1740,9 @@ hipError_t launch_flash(DType dt, int hp, const FlashParams& p, int gx, int gy, 
                         hipStream_t s) {
   dim3 grid(gx, gy, gz);
   if (gx == 0 || gy == 0 || gz == 0) return hipSuccess;
+  // code caches are read by the float32 dense kernel only
+  if (p.qbits != 0 && (dt != DType::F32 || p.mode != kDense || (p.qbits != 8 && p.qbits != 4)))
+    return hipErrorInvalidValue;
   if (dt == DType::F16) {
     if (hp == 64) return launch_flash_t<f16, 64, 64>(p, grid, s);
     if (hp == 128) return launch_flash_t<f16, 128, 64>(p, grid, s);

@@ -67,7 +67,8 @@ struct PrepParams {
   int win_cap;              // > 0: sliding-window cache of this capacity (rows from window_geom)
   // quantised caches (T = float32, write_kv only): the new keys and values
   // are stored as codes in kq/vq (rows of H int8, or H/2 bytes of two
-  // +8-biased nibbles, capacity qcap) and as code * scale in kc/vc
+  // +8-biased nibbles, capacity qcap) and, unless kc/vc are null, as
+  // code * scale in kc/vc
   int bits;                 // 0: float caches; 8 or 4
   void* kq; void* vq;
   int qcap;
@@ -213,6 +214,13 @@ struct FlashParams {
   const void* cos;
   const void* sin;
   int rot_half, rot_rows, interleaved;
+  // quantised caches (float32 queries, dense mode): kc/vc hold codes, rows of
+  // H int8 (qbits 8) or H/2 bytes of two +8-biased nibbles, even dim low
+  // (qbits 4), at the element strides above; each element is code * scale
+  // (per-tensor scale, or per kv head and dim when *_pc)
+  int qbits;
+  const float* qk_scale; const float* qv_scale;
+  int qk_pc, qv_pc;
 };
 
 // ---------------------------------------------------------------------------

@@ -17,8 +17,8 @@
 // kv_cache_bit_width; Inputs table: k_scale, v_scale and the int4 packing;
 // float32 rows only): the transformed key and the value become codes
 // clamp(rint(x / scale)) (float32 quotient) in the code cache, int8 or two
-// +8-biased nibbles per byte with the even dim low, and code * scale in the
-// float cache that the attention kernel reads.
+// +8-biased nibbles per byte with the even dim low (and, when a float cache
+// is given, code * scale there; the prompt's attention reads the codes).
 //
 // One workgroup (4 waves) per token; each wave transforms one head at a
 // time with its lanes spread over the head's dims.  The transformed head is
@@ -47,15 +47,17 @@ __device__ __forceinline__ void store8_or_4(float* p, const float (&x)[4]) {
 }
 
 // Quantised store of row element d = lane + 64u (u < 4) of head h, value y[u]:
-// the code into the code cache row, code * scale into the float cache row.
-// Called by all 64 lanes of a wave (the int4 pairs meet by a lane shuffle).
+// the code into the code cache row, code * scale into the float cache row
+// when there is one.  Called by all 64 lanes of a wave (the int4 pairs meet
+// by a lane shuffle).
 __device__ void quant_store(const PrepParams& p, bool key, int b, int h, int crow, int lane,
                             const float (&y)[4]) {
   const int H = p.H;
   const float* sc = key ? p.k_scale : p.v_scale;
   const bool pc = (key ? p.k_scale_pc : p.v_scale_pc) != 0;
   const int64_t slab = (int64_t)b * p.kvN + h;
-  float* deq = static_cast<float*>(key ? p.kc : p.vc) + (slab * p.cap + crow) * H;
+  float* const fc = static_cast<float*>(key ? p.kc : p.vc);
+  float* deq = fc != nullptr ? fc + (slab * p.cap + crow) * H : nullptr;
   const float top = p.bits == 8 ? 127.f : 7.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -64,7 +66,7 @@ __device__ void quant_store(const PrepParams& p, bool key, int b, int h, int cro
     if (d < H) {
       const float s = pc ? sc[(int64_t)h * H + d] : sc[0];
       c = (int)fminf(fmaxf(rintf(y[u] / s), -top - 1.f), top);
-      deq[d] = (float)c * s;
+      if (deq != nullptr) deq[d] = (float)c * s;
     }
     if (p.bits == 8) {
       int8_t* codes = static_cast<int8_t*>(key ? p.kq : p.vq) + (slab * p.qcap + crow) * H;

@@ -245,6 +245,13 @@ QUANT = [
          quant=dict(bits=4, k="tensor", v="channel")),
     dict(B=1, S=20, N=4, kvN=1, H=128, rotary=True, quant=Q8C),
     dict(B=2, S=9, N=2, kvN=1, H=8, quant=dict(bits=4, k="tensor", v="tensor")),
+    # prompts whose attention reads the codes of a cache longer than the
+    # prompt: heads narrower than the padded tile, and the widest head
+    dict(B=2, S=70, N=4, kvN=2, H=40, cap=100, quant=Q4C),
+    dict(B=2, S=33, N=4, kvN=2, H=24, cap=48, total_lens=[20, 33], quant=Q8C),
+    dict(B=1, S=40, N=2, kvN=1, H=256, cap=64, softcap=25.0,
+         quant=dict(bits=8, k="channel", v="tensor")),
+    dict(B=1, S=50, N=2, kvN=2, H=256, cap=50, quant=Q4T),
     dict(B=3, S=1, N=32, kvN=8, H=128, cap=600, past_lens=[1, 300, 599], rotary=True, quant=Q8C),
     dict(B=2, S=1, N=8, kvN=2, H=64, past="concat", cap=200, past_lens=[0, 150],
          quant=dict(bits=8, k="tensor", v="channel")),

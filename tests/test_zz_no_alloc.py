@@ -1,8 +1,8 @@
 """gqa_attention_noalloc (the allocation-free variant of gqa_attention, whose
 workspace is the library's own per-GPU scratch) against gqa_attention on the
 same inputs: two decode calls in a row, the second smaller, and a quantised
-prompt, which also uses the scratch.  The same kernels run with the same
-split, so outputs and caches must agree bit for bit."""
+prompt (which needs no scratch).  The same kernels run with the same split,
+so outputs and caches must agree bit for bit."""
 
 import numpy as np
 import pytest
@@ -60,7 +60,7 @@ def test_noalloc_matches_gqa_attention_on_consecutive_calls():
     small = wl.gqa_case(rng, dtype=np.float16, past="shared", B=3, S=1, N=32, kvN=8, H=128,
                         cap=600, past_lens=[1, 300, 599], rotary=True)
     _same(small, "decode B3, cache 600")
-    # a quantised prompt (its dequantised rows live in the scratch)
+    # a quantised prompt (no scratch: the attention reads the codes)
     rng = np.random.default_rng(78)
     q = wl.gqa_case(rng, dtype=np.float32, B=2, S=150, N=8, kvN=2, H=64,
                     quant=dict(bits=8, k="channel", v="tensor"))
