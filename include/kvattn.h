@@ -226,14 +226,17 @@ void gqa_attrs_default(gqa_attrs* attrs);
  * of attention_bias.  rotary needs cos/sin rows for every position used.
  *
  * sliding_window_cache = 1 (GroupQueryAttention page, Attributes table): the
- * shared past/present buffers of capacity C hold a sample's most recent
- * tokens, oldest first.  Before the call they hold F_b = min(total_b - S, C)
- * rows; D_b = max(0, F_b + S - C) rows are evicted from the front (rows
- * [D_b, F_b) move to [0, F_b - D_b)) and the S new rows follow, so row i then
- * holds absolute position total_b - fill_b + i, fill_b = F_b - D_b + S.
- * Rotary and the causal/window bounds use absolute positions.  Needs causal,
- * local_window_size > 0, C >= local_window_size + S and shared buffers; no
- * attention_bias.
+ * buffers of capacity C (the present buffer's sequence axis) hold a sample's
+ * most recent tokens, oldest first.  Before the call the past holds
+ * F_b = min(total_b - S, C) rows; D_b = max(0, F_b + S - C) rows are evicted
+ * from the front (past rows [D_b, F_b) go to present rows [0, F_b - D_b): a
+ * shift when the buffers are shared, a copy when they are separate, in which
+ * case the past's sequence axis must hold min(total_sequence_length - S, C)
+ * rows and the present's rows from fill_b on keep what they held) and the S
+ * new rows follow, so row i then holds absolute position total_b - fill_b + i,
+ * fill_b = F_b - D_b + S.  Rotary and the causal/window bounds use absolute
+ * positions.  Needs causal, local_window_size > 0, a past cache and
+ * C >= local_window_size + S; no attention_bias.
  *
  * Quantised caches (GroupQueryAttention page, Attributes table: k_quant_type,
  * v_quant_type, kv_cache_bit_width; Inputs table: k_scale, v_scale and the
@@ -251,9 +254,9 @@ void gqa_attrs_default(gqa_attrs* attrs);
  * int4 decode needs H to be a multiple of Hp / 8, where Hp is H rounded up to
  * 64, 128 or 256.
  *
- * UNSUPPORTED: kv sequence length != S; sliding_window_cache with separate
- * past/present buffers, with attention_bias or with a quantised cache; a
- * quantised cache with a past and S > 1; int4 decode with other head sizes.
+ * UNSUPPORTED: kv sequence length != S; sliding_window_cache with
+ * attention_bias or with a quantised cache; a quantised cache with a past and
+ * S > 1; int4 decode with other head sizes.
  */
 int32_t gqa_attention(const gqa_attrs* attrs,
                       const kvattn_tensor* inputs, int32_t n_inputs,

@@ -298,8 +298,13 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   if (P.bits != 0 && P.window_cache)
     return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache with a quantised cache is not implemented");
   if (P.window_cache) {
-    if (!P.shared)
-      return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache needs shared past/present buffers");
+    if (!P.has_past)
+      return fail(KVATTN_ERR_INVALID_ARG, "sliding_window_cache needs a past cache");
+    // separate buffers: the past holds the window before the call, at most
+    // min(total - S, capacity) rows
+    if (!P.shared && P.past_seq < std::min<int64_t>(std::max<int64_t>(total - P.S, 0), P.cap))
+      return fail(KVATTN_ERR_INVALID_ARG, "sliding_window_cache: past sequence axis %d cannot hold the window (%lld rows)",
+                  P.past_seq, (long long)std::min<int64_t>(total - P.S, P.cap));
     if (P.cap < a->local_window_size + P.S)
       return fail(KVATTN_ERR_INVALID_ARG, "sliding_window_cache: capacity %d < local_window_size + sequence_length (%d)",
                   P.cap, a->local_window_size + P.S);
@@ -373,10 +378,13 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     c.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
     // quantised caches copy bytes: H codes (int8) or H / 2 bytes (int4) per row
     c.B = P.B; c.kvN = P.kvN; c.H = P.bits == 4 ? P.H / 2 : P.H; c.S = P.S; c.past_seq = P.past_seq; c.cap = P.cap;
+    // sliding-window cache over separate buffers: the copy moves the rows
+    // that survive the eviction to the front (the shift of the shared case)
+    c.win_cap = P.window_cache ? P.cap : 0;
     CHECK(hip_status(launch_copy_past(P.bits != 0 ? DType::Q8 : dt, c, st), "copy_past launch"));
   }
 
-  if (P.window_cache) {
+  if (P.window_cache && P.shared) {
     WindowShiftParams w{};
     w.kc = ck.data;
     w.vc = cv.data;

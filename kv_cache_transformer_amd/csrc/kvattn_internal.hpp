@@ -102,12 +102,16 @@ struct WindowShiftParams {
   int B, kvN, H, S, cap;
 };
 
-// Copy the live past rows [0, past_b) into a separate present buffer.
+// Copy the live past rows [0, past_b) into a separate present buffer, or,
+// for a sliding-window cache (win_cap > 0), the rows that survive the
+// eviction, [drop, held), to [0, held - drop) (window_geom with capacity
+// win_cap; held never beyond past_seq).
 struct CopyPastParams {
   const void* pk; const void* pv;   // (B, kvN, past_seq, H)
   void* ck; void* cv;               // (B, kvN, cap, H)
   const int32_t* lens;              // seqlens_k
   int B, kvN, H, S, past_seq, cap;
+  int win_cap;
 };
 
 // ---------------------------------------------------------------------------

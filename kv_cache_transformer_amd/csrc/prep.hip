@@ -306,12 +306,17 @@ template <typename T>
 __global__ __launch_bounds__(256) void copy_past_kernel(CopyPastParams p) {
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int total = p.lens[b] + 1;
-  int rows = total - p.S;
-  rows = min(rows, min(p.past_seq, p.cap));
+  int rows = total - p.S, first = 0;
+  if (p.win_cap > 0) {
+    const WindowGeom g = window_geom(total, p.S, p.win_cap);
+    first = g.drop;
+    rows = min(g.held, p.past_seq) - g.drop;
+  }
+  rows = min(rows, min(p.past_seq - first, p.cap));
   if (rows <= 0) return;
   const int64_t n = (int64_t)rows * p.H;
-  const T* sk = static_cast<const T*>(p.pk) + ((int64_t)b * p.kvN + kvh) * p.past_seq * p.H;
-  const T* sv = static_cast<const T*>(p.pv) + ((int64_t)b * p.kvN + kvh) * p.past_seq * p.H;
+  const T* sk = static_cast<const T*>(p.pk) + (((int64_t)b * p.kvN + kvh) * p.past_seq + first) * p.H;
+  const T* sv = static_cast<const T*>(p.pv) + (((int64_t)b * p.kvN + kvh) * p.past_seq + first) * p.H;
   T* dk = static_cast<T*>(p.ck) + ((int64_t)b * p.kvN + kvh) * p.cap * p.H;
   T* dv = static_cast<T*>(p.cv) + ((int64_t)b * p.kvN + kvh) * p.cap * p.H;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;

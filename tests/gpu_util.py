@@ -105,7 +105,7 @@ def check_cache(got, ref, transformed_rows=None, what="cache"):
     err = np.abs(g64 - r64)
     lim = 8 * 2.0 ** -24 * scale
     if got.dtype == np.float16:
-        ulp16 = np.spacing(np.abs(ref)).astype(np.float64)
+        ulp16 = np.spacing(np.abs(np.where(np.isnan(ref), 0, ref))).astype(np.float64)
         lim = lim + ulp16
     bad = tr & (err > lim)
     assert not bad.any(), (f"{what}: {int(bad.sum())} transformed elements beyond the bound "

@@ -154,7 +154,7 @@ def test_gqa_valid_shapes_give_workspace(lib):
     (lambda ins, outs, a: ins.__setitem__(12, T(F16, 64)), -1),             # unpaired norm
     (lambda ins, outs, a: a.update(k_quant_type=1), -1),                    # quant type, no bit width
     (lambda ins, outs, a: a.update(sliding_window_cache=1), -1),            # needs a window
-    (lambda ins, outs, a: a.update(sliding_window_cache=1, local_window_size=4), -2),  # no shared past
+    (lambda ins, outs, a: a.update(sliding_window_cache=1, local_window_size=4), -1),  # no past cache
     (lambda ins, outs, a: a.update(causal=0, local_window_size=4), -1),
     (lambda ins, outs, a: a.update(do_rotary=1), -1),                       # no cos/sin
     (lambda ins, outs, a: ins.__setitem__(10, T(F32, 1)), -1),              # k_scale, no bit width
@@ -374,9 +374,17 @@ def test_gqa_window_cache_validation(lib):
     assert rc == 0, msg
     rc, _, msg = gqa_call(lib, ins, outs, total=500, sliding_window_cache=1, local_window_size=49)
     assert rc == -1 and "capacity" in msg          # 64 < 49 + 16
-    ins, outs = gqa_args(past="concat", S=16, cap=64)
-    rc, _, _ = gqa_call(lib, ins, outs, total=60, sliding_window_cache=1, local_window_size=8)
-    assert rc == -2                                 # separate buffers
+    # separate past/present buffers: the past must hold the window before the
+    # call, min(total - S, capacity) rows
+    ins, outs = gqa_args(past="concat", S=16, cap=64)   # past axis 64, present 64
+    rc, _, msg = gqa_call(lib, ins, outs, total=500, sliding_window_cache=1, local_window_size=8)
+    assert rc == 0, msg
+    ins[3] = T(F16, 2, 2, 40, 64, ptr=0x20000)
+    ins[4] = T(F16, 2, 2, 40, 64, ptr=0x30000)
+    rc, _, msg = gqa_call(lib, ins, outs, total=500, sliding_window_cache=1, local_window_size=8)
+    assert rc == -1 and "window" in msg            # 40 rows < min(484, 64)
+    rc, _, msg = gqa_call(lib, ins, outs, total=56, sliding_window_cache=1, local_window_size=8)
+    assert rc == 0, msg                             # 40 rows hold the 40 tokens seen
     ins, outs = gqa_args(past="shared", S=16, cap=64, slots={8: T(F16, 2, 8, 16, 500)})
     rc, _, _ = gqa_call(lib, ins, outs, total=500, sliding_window_cache=1, local_window_size=8)
     assert rc == -2                                 # attention_bias

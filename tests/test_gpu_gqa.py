@@ -221,6 +221,21 @@ def test_window_cache_parity(idx):
     assert err >= 0
 
 
+# The same windows over separate past and present buffers: the rows that
+# survive the eviction are copied to the front of the present buffer, the new
+# rows follow, and its other rows keep what they held (NaN here).
+@pytest.mark.parametrize("idx", range(len(WINDOW)))
+def test_window_cache_separate_buffers(idx):
+    case = _case(WINDOW[idx], 3100 + idx)
+    case["attrs"]["sliding_window_cache"] = 1
+    i = case["inputs"]
+    fill = np.full_like(i["past_key"], np.nan)
+    i["present_key"], i["present_value"] = fill, fill.copy()
+    case["shared"] = False
+    err, _ = _compare(case)
+    assert err >= 0
+
+
 def test_workload_window_decode():
     """The sliding-window decode workload at full size, every output checked."""
     case = wl.gqa_window_decode()
