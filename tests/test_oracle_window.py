@@ -91,6 +91,38 @@ def test_window_cache_without_eviction_is_the_shared_cache():
         np.testing.assert_array_equal(x, y)
 
 
+def test_window_cache_separate_buffers_match_the_shared_ones():
+    # a stream through separate past and present window buffers (each call's
+    # present becomes the next call's past) gives the shared buffer's outputs
+    # and rows; present rows from fill on keep what they held
+    rng = np.random.default_rng(11)
+    B, N, kvN, H, C, W = 2, 4, 2, 16, 9, 5
+    shared_k = rng.standard_normal((B, kvN, C, H))
+    shared_v = rng.standard_normal((B, kvN, C, H))
+    past_k, past_v = shared_k.copy(), shared_v.copy()
+    done = 0
+    for S in [3, 4, 1, 1, 2, 4, 1]:
+        q = rng.standard_normal((B, S, N * H))
+        k = rng.standard_normal((B, S, kvN * H))
+        v = rng.standard_normal((B, S, kvN * H))
+        total = done + S
+        common = dict(seqlens_k=np.full(B, total - 1, np.int32), total_sequence_length=total,
+                      num_heads=N, kv_num_heads=kvN, local_window_size=W, sliding_window_cache=1)
+        ref, shared_k, shared_v = oracle.gqa(q, k, v, past_key=shared_k, past_value=shared_v,
+                                             present_key=shared_k, present_value=shared_v, **common)
+        pres_k = np.full((B, kvN, C, H), np.nan)
+        pres_v = np.full((B, kvN, C, H), np.nan)
+        got, pres_k, pres_v = oracle.gqa(q, k, v, past_key=past_k, past_value=past_v,
+                                         present_key=pres_k, present_value=pres_v, **common)
+        fill = min(total, C)
+        np.testing.assert_array_equal(got, ref)
+        np.testing.assert_array_equal(pres_k[:, :, :fill], shared_k[:, :, :fill])
+        np.testing.assert_array_equal(pres_v[:, :, :fill], shared_v[:, :, :fill])
+        assert np.isnan(pres_k[:, :, fill:]).all() and np.isnan(pres_v[:, :, fill:]).all()
+        past_k, past_v = pres_k, pres_v
+        done = total
+
+
 @pytest.mark.parametrize("bad", [
     dict(local_window_size=-1),
     dict(local_window_size=0),
