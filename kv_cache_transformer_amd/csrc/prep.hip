@@ -327,7 +327,9 @@ __global__ __launch_bounds__(256) void copy_past_kernel(CopyPastParams p) {
 }
 
 // Sliding-window eviction: rows [drop, held) of every (sample, kv head) slab
-// move to [0, held - drop), in steps of kShiftRows rows.  A step loads all its
+// of the keys and of the values (one workgroup each) move to
+// [0, held - drop), in steps of whole rows (kShiftChunks 16-byte chunks per
+// thread).  A step loads all its
 // rows before any is stored (barrier), so a step's stores may overwrite its
 // own sources; the next step's sources lie above the rows stored so far
 // (drop >= 1), so steps need no further ordering.
@@ -335,13 +337,14 @@ constexpr int kShiftThreads = 1024, kShiftChunks = 8;  // 16-byte chunks per thr
 template <typename T>
 __global__ __launch_bounds__(kShiftThreads) void window_shift_kernel(WindowShiftParams p) {
   const int slab = blockIdx.x;           // (b, kvh)
+  const int which = blockIdx.y;          // 0: keys, 1: values
   const int b = slab / p.kvN;
   const WindowGeom g = window_geom(p.lens[b] + 1, p.S, p.cap);
   const int keep = g.held - g.drop;
   if (g.drop <= 0 || keep <= 0) return;  // nothing moves (block-uniform)
   const int cpr = p.H * (int)sizeof(T) / 16;                   // chunks per row
   const int rows_step = kShiftThreads * kShiftChunks / cpr;     // whole rows per step
-  for (int which = 0; which < 2; ++which) {
+  {
     char* base = static_cast<char*>(which == 0 ? p.kc : p.vc) +
                  (int64_t)slab * p.cap * p.H * sizeof(T);
     for (int r0 = 0; r0 < keep; r0 += rows_step) {
@@ -400,10 +403,11 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
 hipError_t launch_window_shift(DType dt, const WindowShiftParams& p, hipStream_t s) {
   const int slabs = p.B * p.kvN;
   if (slabs == 0) return hipSuccess;
+  // one workgroup per (slab, keys or values)
   if (dt == DType::F16)
-    launch_kernel(window_shift_kernel<f16>, dim3(slabs), dim3(kShiftThreads), 0, s, p);
+    launch_kernel(window_shift_kernel<f16>, dim3(slabs, 2), dim3(kShiftThreads), 0, s, p);
   else
-    launch_kernel(window_shift_kernel<float>, dim3(slabs), dim3(kShiftThreads), 0, s, p);
+    launch_kernel(window_shift_kernel<float>, dim3(slabs, 2), dim3(kShiftThreads), 0, s, p);
   return hipGetLastError();
 }
 
