@@ -4,7 +4,11 @@ tolerances of the attention outputs and the exactness rules of the caches.
 
 Output tolerance (per element, against the float64 oracle):
   float16 storage: |gpu - ref| <= 2e-3 + 2e-3 * |ref|
-  float32 storage: |gpu - ref| <= 1e-4 * |ref| + 1e-6
+  float32 storage: |gpu - ref| <= 1e-4 * |ref| + 1e-6 * max(1, V)
+where V is the largest magnitude among the values the outputs average (an
+output is a weighted average of value rows, so the float32 error of the sum
+scales with them, not with the output, which may cancel far below them); V
+is taken for quantised caches, whose values code * scale reach about 5.
 Cache rows: copied rows (values, untouched and copied past rows, keys without
 norm/rotary) bit-exact; keys transformed by norm and/or rotary within 1 ulp of
 T (float16) of the float64 result rounded to T, plus 8 float32 ulps of the
@@ -33,20 +37,20 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-def tolerance(ref, dtype):
+def tolerance(ref, dtype, value_max=1.0):
     ref = np.abs(np.asarray(ref, np.float64))
     if np.dtype(dtype) == np.float16:
         return 2e-3 + 2e-3 * ref
-    return 1e-4 * ref + 1e-6
+    return 1e-4 * ref + 1e-6 * max(1.0, float(value_max))
 
 
-def check_output(got, ref, dtype, what="output"):
+def check_output(got, ref, dtype, what="output", value_max=1.0):
     got = np.asarray(got).astype(np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     err = np.abs(got - ref)
-    tol = tolerance(ref, dtype)
+    tol = tolerance(ref, dtype, value_max)
     bad = err > tol
     if bad.any():
         i = np.unravel_index(np.argmax(err - tol), err.shape)
@@ -163,6 +167,10 @@ def gqa_new_rows(case):
     B, S = i["query"].shape[:2]
     total = i["seqlens_k"].astype(np.int64) + 1
     past = total - S if i.get("past_key") is not None else np.zeros(B, np.int64)
+    if case["attrs"].get("sliding_window_cache"):
+        cap = i["present_key"].shape[2]
+        held = np.minimum(past, cap)
+        past = held - np.maximum(0, held + S - cap)      # rows kept before the new ones
     return past[:, None] + np.arange(S)[None, :]
 
 
@@ -228,12 +236,15 @@ def check_quant_gqa(case, got, ref, info, query_rows=None):
     o = o.reshape(o.shape[0], o.shape[1], N, H)
     r = rout.reshape(rout.shape[0], rout.shape[1], N, H)
     keep = np.repeat(~bad_units, N // kvN, axis=1)  # (B, N)
-    check_output(o.transpose(0, 2, 1, 3)[keep], r.transpose(0, 2, 1, 3)[keep], np.float32)
+    vs = quant.channel_scales(case["inputs"]["v_scale"], a["v_quant_type"], kvN, H)
+    vmax = float(np.max(np.abs(quant.load_codes(rpv, bits)) * vs[None, :, None, :]))
+    check_output(o.transpose(0, 2, 1, 3)[keep], r.transpose(0, 2, 1, 3)[keep], np.float32,
+                 value_max=vmax)
     if bad_units.any():
         r2, _, _ = gqa_oracle(case, query_rows=query_rows, stored_key_codes=pk)
         r2 = r2.reshape(r2.shape[0], r2.shape[1], N, H)
         check_output(o.transpose(0, 2, 1, 3)[~keep], r2.transpose(0, 2, 1, 3)[~keep], np.float32,
-                     "output of units whose key codes sit across a near tie")
+                     "output of units whose key codes sit across a near tie", value_max=vmax)
     return n_off
 
 
