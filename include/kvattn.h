@@ -249,14 +249,15 @@ void gqa_attrs_default(gqa_attrs* attrs);
  * its kv head and dim); a new key (after norm and rotary) or value x is
  * stored as code = clamp(rint(x / scale), -2^(b-1), 2^(b-1) - 1), the
  * quotient in float32 and rounded half to even.  Scales must be positive and
- * finite (other values give unspecified codes).  Both widths serve the
- * prompt (no past) and decode (a past, S = 1, shared or separate buffers);
- * int4 decode needs H to be a multiple of Hp / 8, where Hp is H rounded up to
- * 64, 128 or 256.
+ * finite (other values give unspecified codes).  Both widths serve prompts
+ * (with or without a past: the new rows' codes are written, then the
+ * attention reads every row's codes), decode (a past, S = 1) and the
+ * sliding-window cache (the eviction moves code rows), over shared or
+ * separate buffers; int4 decode (S = 1 with a past) needs H to be a multiple
+ * of Hp / 8, where Hp is H rounded up to 64, 128 or 256.
  *
  * UNSUPPORTED: kv sequence length != S; sliding_window_cache with
- * attention_bias or with a quantised cache; a quantised cache with a past and
- * S > 1; int4 decode with other head sizes.
+ * attention_bias; int4 decode with other head sizes.
  */
 int32_t gqa_attention(const gqa_attrs* attrs,
                       const kvattn_tensor* inputs, int32_t n_inputs,

@@ -291,12 +291,8 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     return fail(KVATTN_ERR_INVALID_ARG, "present_key and present_value must both share the past buffers or neither");
   if (P.shared && ck.dims[2] != pk.dims[2])
     return fail(KVATTN_ERR_INVALID_ARG, "a shared present buffer must have the past buffer's dims");
-  if (P.bits != 0 && P.has_past && P.S != 1)
-    return fail(KVATTN_ERR_UNSUPPORTED, "int%d caches with a past take one new token (decode)", P.bits);
-  if (P.bits == 4 && P.has_past && P.H % (P.HP / 8) != 0)
+  if (P.bits == 4 && P.has_past && P.S == 1 && P.H % (P.HP / 8) != 0)
     return fail(KVATTN_ERR_UNSUPPORTED, "int4 decode: head size %d must be a multiple of %d", P.H, P.HP / 8);
-  if (P.bits != 0 && P.window_cache)
-    return fail(KVATTN_ERR_UNSUPPORTED, "sliding_window_cache with a quantised cache is not implemented");
   if (P.window_cache) {
     if (!P.has_past)
       return fail(KVATTN_ERR_INVALID_ARG, "sliding_window_cache needs a past cache");
@@ -389,8 +385,10 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
     w.kc = ck.data;
     w.vc = cv.data;
     w.lens = static_cast<const int32_t*>(in[GQA_IN_SEQLENS_K].data);
-    w.B = P.B; w.kvN = P.kvN; w.H = P.H; w.S = P.S; w.cap = P.cap;
-    CHECK(hip_status(profiled(KVATTN_PROFILE_SHIFT, st, [&] { return launch_window_shift(dt, w, st); }),
+    w.B = P.B; w.kvN = P.kvN; w.S = P.S; w.cap = P.cap;
+    // quantised caches move code rows: H bytes (int8) or H / 2 (int4)
+    w.row_bytes = P.bits == 8 ? P.H : (P.bits == 4 ? P.H / 2 : P.H * (int)elem_size(P.dt));
+    CHECK(hip_status(profiled(KVATTN_PROFILE_SHIFT, st, [&] { return launch_window_shift(w, st); }),
                      "window shift launch"));
   }
 

@@ -97,9 +97,10 @@ __host__ __device__ inline WindowGeom window_geom(int total, int S, int cap) {
 // Move the rows of each (sample, kv head) slab that survive the eviction to
 // the front of the buffer (rows [drop, held) to [0, held - drop)).
 struct WindowShiftParams {
-  void* kc; void* vc;               // (B, kvN, cap, H), shifted in place
+  void* kc; void* vc;               // (B, kvN, cap, row_bytes), shifted in place
   const int32_t* lens;              // seqlens_k (total = lens[b] + 1)
-  int B, kvN, H, S, cap;
+  int B, kvN, S, cap;
+  int row_bytes;                    // bytes per cache row: a multiple of 4, at most 1024
 };
 
 // Copy the live past rows [0, past_b) into a separate present buffer, or,
@@ -256,7 +257,7 @@ constexpr int kGemmSchedMaxB = 3000;
 // launch error.
 hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s);
 hipError_t launch_copy_past(DType dt, const CopyPastParams& p, hipStream_t s);
-hipError_t launch_window_shift(DType dt, const WindowShiftParams& p, hipStream_t s);
+hipError_t launch_window_shift(const WindowShiftParams& p, hipStream_t s);
 hipError_t launch_decode(DType dt, int hp, const DecodeParams& p, hipStream_t s);
 hipError_t launch_flash(DType dt, int hp, const FlashParams& p, int grid_x, int grid_y,
                         int grid_z, hipStream_t s);

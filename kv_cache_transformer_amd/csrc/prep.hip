@@ -328,13 +328,14 @@ __global__ __launch_bounds__(256) void copy_past_kernel(CopyPastParams p) {
 
 // Sliding-window eviction: rows [drop, held) of every (sample, kv head) slab
 // of the keys and of the values (one workgroup each) move to
-// [0, held - drop), in steps of whole rows (kShiftChunks 16-byte chunks per
-// thread).  A step loads all its
-// rows before any is stored (barrier), so a step's stores may overwrite its
-// own sources; the next step's sources lie above the rows stored so far
-// (drop >= 1), so steps need no further ordering.
-constexpr int kShiftThreads = 1024, kShiftChunks = 8;  // 16-byte chunks per thread per step
-template <typename T>
+// [0, held - drop), as raw bytes in chunks of C (16, 8 or 4 bytes, the widest
+// that divides a row: float rows, int8 code rows of H bytes, int4 rows of
+// H / 2), in steps of whole rows (kShiftChunks chunks per thread).  A step
+// loads all its rows before any is stored (barrier), so a step's stores may
+// overwrite its own sources; the next step's sources lie above the rows
+// stored so far (drop >= 1), so steps need no further ordering.
+constexpr int kShiftThreads = 1024, kShiftChunks = 8;  // chunks per thread per step
+template <typename C>
 __global__ __launch_bounds__(kShiftThreads) void window_shift_kernel(WindowShiftParams p) {
   const int slab = blockIdx.x;           // (b, kvh)
   const int which = blockIdx.y;          // 0: keys, 1: values
@@ -342,19 +343,18 @@ __global__ __launch_bounds__(kShiftThreads) void window_shift_kernel(WindowShift
   const WindowGeom g = window_geom(p.lens[b] + 1, p.S, p.cap);
   const int keep = g.held - g.drop;
   if (g.drop <= 0 || keep <= 0) return;  // nothing moves (block-uniform)
-  const int cpr = p.H * (int)sizeof(T) / 16;                   // chunks per row
+  const int cpr = p.row_bytes / (int)sizeof(C);                 // chunks per row
   const int rows_step = kShiftThreads * kShiftChunks / cpr;     // whole rows per step
   {
-    char* base = static_cast<char*>(which == 0 ? p.kc : p.vc) +
-                 (int64_t)slab * p.cap * p.H * sizeof(T);
+    char* base = static_cast<char*>(which == 0 ? p.kc : p.vc) + (int64_t)slab * p.cap * p.row_bytes;
     for (int r0 = 0; r0 < keep; r0 += rows_step) {
-      uint4v v[kShiftChunks];
+      C v[kShiftChunks];
 #pragma unroll
       for (int u = 0; u < kShiftChunks; ++u) {
         const int idx = threadIdx.x + kShiftThreads * u;
         const int r = r0 + idx / cpr, c = idx % cpr;
         if (r < keep && r < r0 + rows_step)
-          v[u] = *reinterpret_cast<const uint4v*>(base + ((int64_t)(r + g.drop) * cpr + c) * 16);
+          v[u] = *reinterpret_cast<const C*>(base + ((int64_t)(r + g.drop) * cpr + c) * sizeof(C));
       }
       __syncthreads();
 #pragma unroll
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kShiftThreads) void window_shift_kernel(WindowShift
         const int idx = threadIdx.x + kShiftThreads * u;
         const int r = r0 + idx / cpr, c = idx % cpr;
         if (r < keep && r < r0 + rows_step)
-          *reinterpret_cast<uint4v*>(base + ((int64_t)r * cpr + c) * 16) = v[u];
+          *reinterpret_cast<C*>(base + ((int64_t)r * cpr + c) * sizeof(C)) = v[u];
       }
       __syncthreads();
     }
@@ -400,14 +400,18 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_window_shift(DType dt, const WindowShiftParams& p, hipStream_t s) {
+hipError_t launch_window_shift(const WindowShiftParams& p, hipStream_t s) {
   const int slabs = p.B * p.kvN;
   if (slabs == 0) return hipSuccess;
+  if (p.row_bytes <= 0 || p.row_bytes % 4 != 0 || p.row_bytes > 1024) return hipErrorInvalidValue;
   // one workgroup per (slab, keys or values)
-  if (dt == DType::F16)
-    launch_kernel(window_shift_kernel<f16>, dim3(slabs, 2), dim3(kShiftThreads), 0, s, p);
+  const dim3 grid(slabs, 2);
+  if (p.row_bytes % 16 == 0)
+    launch_kernel(window_shift_kernel<uint4v>, grid, dim3(kShiftThreads), 0, s, p);
+  else if (p.row_bytes % 8 == 0)
+    launch_kernel(window_shift_kernel<uint2v>, grid, dim3(kShiftThreads), 0, s, p);
   else
-    launch_kernel(window_shift_kernel<float>, dim3(slabs, 2), dim3(kShiftThreads), 0, s, p);
+    launch_kernel(window_shift_kernel<uint32_t>, grid, dim3(kShiftThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -229,10 +229,16 @@ def test_gqa_quant_validation(lib):
     assert code(lambda i, o, a: None, bits=4, past="shared", S=1, H=80) == 0    # 80 = 5 * 128 / 8
     assert code(lambda i, o, a: None, bits=4, past="shared", S=1, H=72) == -2   # not a multiple of 16
     assert code(lambda i, o, a: None, bits=4, past="shared", S=1, H=176) == -2  # not a multiple of 32
-    assert code(lambda i, o, a: None, bits=4, past="shared", S=4) == -2         # quantised past: decode only
-    assert code(lambda i, o, a: None, past="shared", S=4) == -2
+    # a prompt continuing a quantised past (no head-size rule: the prompt path)
+    assert code(lambda i, o, a: None, bits=4, past="shared", S=4) == 0
+    assert code(lambda i, o, a: None, bits=4, past="separate", S=4, H=72) == 0
+    assert code(lambda i, o, a: None, past="shared", S=4) == 0
+    # sliding-window caches of codes (int8 rows of 40 bytes, int4 rows of 20)
+    for bits, S in ((8, 1), (8, 16), (4, 1), (4, 16)):
+        assert code(lambda i, o, a: a.update(sliding_window_cache=1, local_window_size=8),
+                    bits=bits, past="shared", S=S, H=40) == 0
     assert code(lambda i, o, a: a.update(sliding_window_cache=1, local_window_size=8),
-                past="shared", S=1) == -2
+                bits=4, past="separate", S=1) == 0
 
 
 def test_gqa_head_size_and_sharing_rules(lib):

@@ -267,6 +267,16 @@ QUANT = [
     dict(B=1, S=40, N=2, kvN=1, H=256, cap=64, softcap=25.0,
          quant=dict(bits=8, k="channel", v="tensor")),
     dict(B=1, S=50, N=2, kvN=2, H=256, cap=50, quant=Q4T),
+    # prompts continuing a quantised past (chunked prefill): codes of the
+    # past read together with the new rows' codes, in place or copied
+    dict(B=2, S=40, N=8, kvN=2, H=128, past="shared", cap=300, past_lens=[0, 200],
+         rotary=True, window=64, quant=Q8C),
+    dict(B=2, S=17, N=4, kvN=2, H=64, past="concat", cap=60, past_lens=[5, 30], bias="full",
+         quant=Q4T),
+    dict(B=1, S=33, N=4, kvN=1, H=72, past="shared", cap=100, past_lens=[50], rotary=True,
+         norm=True, quant=Q4C),
+    dict(B=2, S=64, N=8, kvN=2, H=40, past="concat", cap=200, past_lens=[100, 136], softcap=20.0,
+         sink=True, quant=dict(bits=8, k="tensor", v="channel")),
     dict(B=3, S=1, N=32, kvN=8, H=128, cap=600, past_lens=[1, 300, 599], rotary=True, quant=Q8C),
     dict(B=2, S=1, N=8, kvN=2, H=64, past="concat", cap=200, past_lens=[0, 150],
          quant=dict(bits=8, k="tensor", v="channel")),
@@ -296,6 +306,38 @@ QUANT = [
 def test_quant_cache_parity(idx):
     print(f"quant case {idx}: {QUANT[idx]}", flush=True)
     case = _case(dict(QUANT[idx], dtype=F32), 400 + idx)
+    got = gqa_gpu(case)
+    info = {}
+    ref = gqa_oracle(case, info=info)
+    n = check_quant_gqa(case, got, ref, info)
+    print(f"key codes on the other side of a near tie: {n}")
+
+
+# Sliding-window caches of codes: the eviction moves code rows (H bytes for
+# int8, H / 2 for int4: 40-wide heads give 40- and 20-byte rows), in place or
+# by the copy into a separate present buffer.
+QWINDOW = [
+    dict(B=3, S=1, N=8, kvN=2, H=128, cap=300, window=200, past_lens=[150, 299, 700],
+         rotary=True, norm=True, quant=Q8C),
+    dict(B=2, S=1, N=4, kvN=2, H=40, cap=64, window=32, past_lens=[10, 100], quant=Q4C),
+    dict(B=2, S=40, N=8, kvN=2, H=40, cap=120, window=64, past_lens=[30, 500], softcap=10.0,
+         sink=True, quant=Q8T),
+    dict(B=1, S=17, N=4, kvN=1, H=128, cap=50, window=33, past_lens=[90], rotary=True,
+         quant=Q4T),
+]
+
+
+@pytest.mark.parametrize("separate", [False, True])
+@pytest.mark.parametrize("idx", range(len(QWINDOW)))
+def test_quant_window_cache_parity(idx, separate):
+    print(f"quant window case {idx} separate={separate}: {QWINDOW[idx]}", flush=True)
+    case = _case(dict(QWINDOW[idx], dtype=F32, past="shared"), 4200 + idx + 10 * separate)
+    case["attrs"]["sliding_window_cache"] = 1
+    if separate:
+        i = case["inputs"]
+        fill = np.full(i["past_key"].shape, 0x5A, np.uint8).view(i["past_key"].dtype)
+        i["present_key"], i["present_value"] = fill, fill.copy()
+        case["shared"] = False
     got = gqa_gpu(case)
     info = {}
     ref = gqa_oracle(case, info=info)
