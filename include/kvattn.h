@@ -314,7 +314,7 @@ typedef enum dmmha_output {
   DMMHA_OUT_OUTPUT = 0,        /* T (B, 1, N*H)                                  required */
   DMMHA_OUT_PRESENT_KEY,       /* T, the past_key buffer itself (in place) or absent */
   DMMHA_OUT_PRESENT_VALUE,     /* T, the past_value buffer itself or absent          */
-  DMMHA_OUT_QK,                /* T (B, N, 1, kv_S), cross attention with output_qk = 1 */
+  DMMHA_OUT_QK,                /* QK (B, N, 1, kv_S): float32 or float16, either with any T; cross attention with output_qk = 1 */
   DMMHA_NUM_OUTPUTS
 } dmmha_output;
 

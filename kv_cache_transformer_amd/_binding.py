@@ -283,11 +283,12 @@ def _gqa_args(query, key, value, past_key, past_value, seqlens_k, total_sequence
 def decode_mha(query, key, value, mask_index=None, attention_bias=None, past_key=None,
                past_value=None, past_sequence_length=None, *, num_heads,
                mask_filter_value=-10000.0, output_qk=0, past_present_share_buffer=None,
-               scale=0.0, output=None, qk=None, workspace=None, stream=None):
+               scale=0.0, output=None, qk=None, qk_dtype=None, workspace=None, stream=None):
     """DecoderMaskedMultiHeadAttention (include/kvattn.h, decode_mha).
 
     Self attention (past_key given) appends in place to past_key/past_value.
-    Returns (output, qk) where qk is None unless output_qk = 1.
+    Returns (output, qk) where qk is None unless output_qk = 1; qk is
+    allocated as qk_dtype (float32 or float16; default the query's dtype).
     """
     torch = _torch()
     lib = library()
@@ -297,7 +298,8 @@ def decode_mha(query, key, value, mask_index=None, attention_bias=None, past_key
     if output is None:
         output = torch.empty_like(query)
     if output_qk and qk is None:
-        qk = torch.empty((B, num_heads, 1, key.shape[2]), dtype=query.dtype, device=query.device)
+        qk = torch.empty((B, num_heads, 1, key.shape[2]), dtype=qk_dtype or query.dtype,
+                         device=query.device)
     a = DmmhaAttrs()
     lib.dmmha_attrs_default(ctypes.byref(a))
     a.num_heads = num_heads

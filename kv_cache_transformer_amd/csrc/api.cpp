@@ -614,7 +614,9 @@ int dmmha_validate(const dmmha_attrs* a, const kvattn_tensor* in, int n_in,
       return fail(KVATTN_ERR_INVALID_ARG, "cross attention has no present cache");
     if ((a->output_qk != 0) != has(qk))
       return fail(KVATTN_ERR_INVALID_ARG, "output_qk must agree with the presence of the qk output");
-    if (has(qk)) CHECK(check(qk, "qk", dt, 4, {P.B, P.N, 1, P.kv_len}));
+    // qk has its own type, float32 or float16, whatever T is
+    if (has(qk)) CHECK(check(qk, "qk", qk.dtype == KVATTN_DT_F32 ? KVATTN_DT_F32 : KVATTN_DT_F16, 4,
+                             {P.B, P.N, 1, P.kv_len}));
   }
   const kvattn_tensor& m = in[DMMHA_IN_MASK_INDEX];
   if (has(m)) {
@@ -652,6 +654,7 @@ int dmmha_run(const dmmha_attrs* a, const kvattn_tensor* in, const kvattn_tensor
     d.len_mode = 2;
     d.host_n = P.kv_len;
     d.qk = out[DMMHA_OUT_QK].data;
+    d.qk_f32 = out[DMMHA_OUT_QK].dtype == KVATTN_DT_F32;
   }
   const kvattn_tensor& bias = in[DMMHA_IN_ATTENTION_BIAS];
   if (has(bias)) {

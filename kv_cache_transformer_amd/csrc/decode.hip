@@ -1162,7 +1162,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   const int h = h0 + hh;
   const float cap = p.softcap, inv_cap = p.softcap > 0.f ? 1.f / p.softcap : 0.f;
   const AT* bias = static_cast<const AT*>(p.bias);
-  AT* qk = static_cast<AT*>(p.qk);
+  void* const qk = p.qk;
 
   float m = kNegInf, l = 0.f;
   // plain scores go to the log2 domain in the same multiply
@@ -1194,7 +1194,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
           v += to_f32(bias[b * p.bias_sb + h * p.bias_sh + key]);
         if (ok && p.mask != nullptr && key < p.mask_cols)
           v += (p.mask[(int64_t)b * p.mask_cols + key] == 0) ? p.mask_filter : 0.f;
-        if (ok && qk != nullptr) qk[((int64_t)b * p.N + h) * p.host_n + key] = from_f32<AT>(v);
+        if (ok && qk != nullptr) {
+          const int64_t at = ((int64_t)b * p.N + h) * p.host_n + key;
+          if (p.qk_f32) static_cast<float*>(qk)[at] = v;
+          else static_cast<f16*>(qk)[at] = from_f32<f16>(v);
+        }
       }
       v = ok ? v * kLog2e : kNegInf;
       x[i] = v;

@@ -146,6 +146,7 @@ struct DecodeParams {
   int win_cap;              // > 0: sliding-window cache of this capacity (len_mode 0 only)
   void* out;                // (B, N*H)
   void* qk;                 // (B, N, 1, host_n) scores after mask, or null
+  int qk_f32;               // qk element type: 1 float32, 0 float16 (either, whatever T is)
   float* part;              // (waves / 2, hpw, HP + 4) per-pair partials: m, l, -, -, o[HP]
   int* counters;            // (B * kvN * head_groups) arrivals per unit: zero on entry, left zero
   int split;                // 0: every unit gets one pair (no counters are touched)

@@ -288,7 +288,7 @@ def dmmha_gpu(case):
                             t.get("past_sequence_length"), num_heads=a["num_heads"],
                             mask_filter_value=a["mask_filter_value"], output_qk=a["output_qk"],
                             past_present_share_buffer=a["past_present_share_buffer"],
-                            scale=a["scale"])
+                            scale=a["scale"], qk_dtype=case.get("qk_dtype"))
     torch.cuda.synchronize()
     pk = host(t["past_key"]) if "past_key" in t else None
     pv = host(t["past_value"]) if "past_value" in t else None

@@ -305,6 +305,10 @@ def test_dmmha_rules(lib):
     o4 = list(outs)
     o4[3] = T(F16, B, N, 1, 10)
     assert dmmha_call(lib, cross, o4, output_qk=1) == 0
+    o4[3] = T(F32, B, N, 1, 10)                       # qk in float32 with float16 T
+    assert dmmha_call(lib, cross, o4, output_qk=1) == 0
+    o4[3] = T(I32, B, N, 1, 10)                       # qk is float32 or float16
+    assert dmmha_call(lib, cross, o4, output_qk=1) == -1
     c2 = list(cross)
     c2[4] = T(F16, 1, 1, 1, 10)                       # bias with cross attention
     assert dmmha_call(lib, c2, outs) == -1

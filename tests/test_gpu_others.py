@@ -30,6 +30,9 @@ DMMHA_CROSS = [
     dict(dtype=F16, B=2, N=2, H=16, kv_len=1, output_qk=1),
     dict(dtype=F32, B=2, N=4, H=64, kv_len=77, mask=True, output_qk=1, mask_filter_value=-5.0),
     dict(dtype=F16, B=1, N=8, H=128, kv_len=1500, mask=True, output_qk=0),
+    # qk in the other type (the page's QK type is float32 or float16, apart from T)
+    dict(dtype=F16, B=2, N=4, H=64, kv_len=300, mask=True, output_qk=1, qk_dtype=F32),
+    dict(dtype=F32, B=1, N=2, H=128, kv_len=50, output_qk=1, qk_dtype=F16),
 ]
 
 
@@ -51,12 +54,15 @@ def test_dmmha_cross_parity(idx):
     spec = dict(DMMHA_CROSS[idx])
     print(f"dmmha cross {idx}: {spec}", flush=True)
     dtype = spec.pop("dtype")
+    qk_dtype = spec.pop("qk_dtype", dtype)
     case = wl.dmmha_cross_case(np.random.default_rng(500 + idx), dtype=dtype, **spec)
+    case["qk_dtype"] = {F16: torch.float16, F32: torch.float32}[qk_dtype]
     out, _, _, qk = dmmha_gpu(case)
     ref, _, _, rqk = dmmha_oracle(case)
     check_output(out, ref, dtype)
     if spec.get("output_qk"):
-        check_output(qk, rqk, dtype, "qk")
+        assert qk.dtype == qk_dtype
+        check_output(qk, rqk, qk_dtype, "qk")
 
 
 def test_dmmha_all_zero_mask_matches_unmasked():
