@@ -66,13 +66,14 @@ def rope_cache(max_seq, rot_dim, dtype, theta=10000.0):
 def gqa_case(rng, *, B, S, N, kvN, H, dtype=F16, past=None, past_lens=None,
              cap=None, rotary=False, rope_rows=None, norm=False, bias=None,
              sink=False, smooth_softmax=-1, softcap=0.0, window=-1, causal=1,
-             scale=0.0, total_lens=None, quant=None):
+             scale=0.0, total_lens=None, quant=None, cache_dtype=None):
     """A GroupQueryAttention call with random data.
 
     past: None (prompt), "shared" (present buffer is the past buffer, capacity
     ``cap``) or "concat" (separate present buffer of seq past_seq + S).
     past_lens: per-batch past length (int array); drawn when None.
     total_lens: prompt only: per-batch total length (<= S); default S.
+    cache_dtype: prompt only: the present buffers' float type (default dtype).
     bias: None or one of "full", "b1" (batch dim 1), "h1" (head dim 1), "11".
     quant: None or dict(bits=8|4, k="tensor"|"channel", v=...): quantised
     caches (float32 dtype) holding uniform random codes, with scales drawn by
@@ -94,8 +95,10 @@ def gqa_case(rng, *, B, S, N, kvN, H, dtype=F16, past=None, past_lens=None,
         tl = np.full(B, S, dtype=np.int64) if total_lens is None else np.asarray(total_lens)
         seqlens_k = (tl - 1).astype(np.int32)
         present_seq = S if cap is None else cap
-        pk = np.zeros((B, kvN, present_seq, H), dtype)
-        pv = np.zeros((B, kvN, present_seq, H), dtype)
+        # a prompt's present cache may have its own float type
+        cdt = dtype if cache_dtype is None else cache_dtype
+        pk = np.zeros((B, kvN, present_seq, H), cdt)
+        pv = np.zeros((B, kvN, present_seq, H), cdt)
         inputs.update(present_key=pk, present_value=pv)
         max_pos = S
     else:

@@ -46,7 +46,13 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
        [past_b, past_b + S) are the new (normed, rotated) keys and the values,
        rounded to T; other rows keep the buffer's prior contents (Outputs
        table; Implementation variants on retaining unchanged cache rows).
-    6. Attention reads keys/values from the T-rounded present cache.  With
+       Without a past the float present cache may have its own type,
+       float16 or float32 (Description: the cache a call over direct Q/K/V
+       generates may be stored as either, whatever T is; a past cache has
+       T's type).  Its new rows are then the same keys and values rounded
+       to that type instead.
+    6. Attention reads keys/values rounded to T: the present cache's rows
+       (when the cache has T's type), else the new rows rounded to T.  With
        ``causal`` key j is visible iff j < total_b and j <= p, and, when
        ``local_window_size`` W >= 0, j >= p - W (W keys to the left of the
        query plus the query's own position).  With ``causal`` = 0 (allowed
@@ -96,7 +102,8 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
     output to those query rows (the cache is always updated in full); the
     output then has shape (B, len(query_rows), num_heads * H).
 
-    Returns ``(output float64, present_key T, present_value T)``.
+    Returns ``(output float64, present_key, present_value)`` (the present
+    buffers in their own types).
     """
     q_in = np.asarray(query)
     k_in = np.asarray(key)
@@ -138,6 +145,15 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
             info["v_quotient"] = np.zeros((B, kvN, S, H))
     elif int(k_quant_type) or int(v_quant_type):
         raise ValueError("quantisation types need kv_cache_bit_width 8 or 4")
+    cache_dt = pk_out.dtype if not bits else None
+    # float64 caches are the oracle's exact mode for its own pins (any T, with
+    # or without a past; the attention reads the unrounded cache rows)
+    own_cache_type = not bits and cache_dt not in (dtype, np.float64)
+    if not bits:
+        if cache_dt not in (np.float16, np.float32, np.float64) or pv_out.dtype != cache_dt:
+            raise ValueError("float caches are float16 or float32, keys and values alike")
+        if own_cache_type and past_key is not None:
+            raise ValueError("a past cache has the type of query, key and value")
     total_b = np.asarray(seqlens_k, dtype=np.int64) + 1
     win = bool(sliding_window_cache)
     if past_key is not None:
@@ -211,8 +227,14 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
                 pk_out[b, :, pb:pb + S, :] = np.asarray(stored_key_codes)[b, :, pb:pb + S, :]
             pv_out[b, :, pb:pb + S, :] = quant.store_codes(vc, bits)
         else:
-            pk_out[b, :, pb:pb + S, :] = round_to(k[b].transpose(1, 0, 2), dtype)
-            pv_out[b, :, pb:pb + S, :] = round_to(v[b].transpose(1, 0, 2), dtype)
+            pk_out[b, :, pb:pb + S, :] = round_to(k[b].transpose(1, 0, 2), cache_dt)
+            pv_out[b, :, pb:pb + S, :] = round_to(v[b].transpose(1, 0, 2), cache_dt)
+    if own_cache_type:
+        # no past: the attention's keys and values are the new rows in T
+        att_k = round_to(k.transpose(0, 2, 1, 3), dtype)
+        att_v = round_to(v.transpose(0, 2, 1, 3), dtype)
+    else:
+        att_k, att_v = pk_out, pv_out
 
     out = np.zeros((B, len(rows), N, H), dtype=np.float64)
     if head_sink is not None:
@@ -243,8 +265,8 @@ def gqa(query, key, value, *, seqlens_k, total_sequence_length,
                 keys = quant.dequantize(quant.load_codes(pk_out[b, kh, :n_keys, :], bits), ks[kh])
                 vals = quant.dequantize(quant.load_codes(pv_out[b, kh, :n_keys, :], bits), vs[kh])
             else:
-                keys = pk_out[b, kh, :n_keys, :].astype(np.float64)
-                vals = pv_out[b, kh, :n_keys, :].astype(np.float64)
+                keys = att_k[b, kh, :n_keys, :].astype(np.float64)
+                vals = att_v[b, kh, :n_keys, :].astype(np.float64)
             x = sc * (q[b, :, h, :] @ keys.T)
             x = softcap(x, softcap_value)
             if bias is not None:

@@ -335,6 +335,59 @@ def test_transformed_cache_rows_are_rounded_float64():
     np.testing.assert_array_equal(pk[0, 0, :3], k.astype(np.float16))
 
 
+# A prompt's present cache in its own float type (GroupQueryAttention page,
+# Description: the cache generated from direct Q/K/V may be float16 or float32
+# whatever T is).  The attention does not depend on that type; the cache
+# holds the same rows stored in it.
+@pytest.mark.parametrize("T,C", [(np.float16, np.float32), (np.float32, np.float16)])
+def test_prompt_cache_in_its_own_type(T, C):
+    spec = dict(B=2, S=7, N=4, kvN=2, H=8, dtype=T, window=3, sink=True, total_lens=[5, 7])
+    same = wl.gqa_case(np.random.default_rng(23), **spec)
+    own = wl.gqa_case(np.random.default_rng(23), cache_dtype=C, **spec)
+    out, pk, pv = _run(own)
+    assert pk.dtype == C and pv.dtype == C
+    # the attention: brute force of the call whose cache has T's type
+    np.testing.assert_allclose(out, _brute(same)[0], rtol=1e-12, atol=1e-12)
+    for x, c in ((own["inputs"]["key"], pk), (own["inputs"]["value"], pv)):
+        x = x.astype(np.float64).reshape(2, 7, 2, 8).transpose(0, 2, 1, 3)
+        c = c.astype(np.float64)
+        if C == np.float32:
+            np.testing.assert_array_equal(c, x)            # float16 widens exactly
+        else:
+            # the nearest float16: no neighbour of the stored value is closer
+            c16 = c.astype(np.float16)
+            up = np.nextafter(c16, np.float16(np.inf)).astype(np.float64)
+            dn = np.nextafter(c16, np.float16(-np.inf)).astype(np.float64)
+            d = np.abs(x - c)
+            assert np.all(d <= np.abs(x - up)) and np.all(d <= np.abs(x - dn))
+            assert np.any(d > 0)
+
+
+def test_prompt_cache_in_its_own_type_transformed_keys():
+    # normed and rotated keys are stored in the cache's type, rounded once
+    # from the exact result; the attention still reads them in T
+    spec = dict(B=1, S=5, N=2, kvN=1, H=8, dtype=np.float16, rotary=True, norm=True)
+    same = wl.gqa_case(np.random.default_rng(24), **spec)
+    own = wl.gqa_case(np.random.default_rng(24), cache_dtype=np.float32, **spec)
+    out, pk, _ = _run(own)
+    np.testing.assert_allclose(out, _brute(same)[0], rtol=1e-12, atol=1e-12)
+    i = own["inputs"]
+    k = oracle.rms_norm(i["key"].astype(np.float64).reshape(5, 8), i["k_norm_weight"], 1e-6)
+    k = oracle.rotary(k, i["cos_cache"][:5], i["sin_cache"][:5])
+    np.testing.assert_array_equal(pk[0, 0], k.astype(np.float32))
+    assert not np.array_equal(pk[0, 0], k.astype(np.float16).astype(np.float32))
+
+
+def test_past_cache_has_the_inputs_type():
+    case = wl.gqa_case(np.random.default_rng(25), B=1, S=2, N=2, kvN=1, H=8, dtype=np.float16,
+                       past="concat", cap=6, past_lens=[3])
+    i = case["inputs"]
+    i["present_key"] = i["present_key"].astype(np.float32)
+    i["present_value"] = i["present_value"].astype(np.float32)
+    with pytest.raises(ValueError):
+        _run(case)
+
+
 def test_query_rows_subset_matches_full():
     rng = np.random.default_rng(21)
     case = wl.gqa_case(rng, B=2, S=9, N=4, kvN=2, H=8, dtype=np.float16, window=3, sink=True,
