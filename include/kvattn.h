@@ -221,7 +221,12 @@ void gqa_attrs_default(gqa_attrs* attrs);
  * Shared buffer: present_key.data == past_key.data (and likewise for values)
  * appends in place; the present must then have the past's dims.  Otherwise the
  * present's seq axis must hold past_b + S rows and rows [0, past_b) are copied.
- * Without a past cache the present's seq axis must be >= S.
+ * Without a past cache the present's seq axis must be >= S, and a float
+ * present cache may be float16 or float32 whatever T is (GroupQueryAttention
+ * page, Description): the attention then reads the new keys and values in T
+ * from the workspace (2 * B * kvN * S * H elements of T), and the present
+ * holds the same rows rounded once to its own type.  A past cache (and a
+ * present with a past) has T's type.
  * total_sequence_length (host) must be >= every total_b and is the last dim
  * of attention_bias.  rotary needs cos/sin rows for every position used.
  *

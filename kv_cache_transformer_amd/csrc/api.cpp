@@ -184,6 +184,11 @@ struct GqaPlan {
   int head_groups, hpw;
   int64_t waves;
   size_t ws_cnt, ws_q, ws_part, ws_total;  // workspace: counters first
+  // a prompt's present cache in its own float type: the new rows in T for
+  // the attention (keys, then values, each (B, kvN, S, H)) after the rest
+  int cache_dt;
+  bool own_cache_type;
+  size_t ws_kv;
 };
 
 // Quantised-cache attributes and scales (GroupQueryAttention page,
@@ -283,8 +288,14 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
   const kvattn_tensor& cv = out[GQA_OUT_PRESENT_VALUE];
   if (!has(o) || !has(ck) || !has(cv)) return fail(KVATTN_ERR_INVALID_ARG, "output, present_key and present_value are required");
   CHECK(check(o, "output", dt, 3, {P.B, P.S, (int64_t)P.N * P.H}));
-  CHECK(check(ck, "present_key", cdt, 4, {P.B, P.kvN, -1, Hc}));
-  CHECK(check(cv, "present_value", cdt, 4, {P.B, P.kvN, ck.dims[2], Hc}));
+  // without a past the float cache may be float16 or float32 whatever T is
+  // (GroupQueryAttention page, Description); a past fixes it to T
+  P.cache_dt = cdt;
+  if (P.bits == 0 && !P.has_past && (ck.dtype == KVATTN_DT_F16 || ck.dtype == KVATTN_DT_F32))
+    P.cache_dt = ck.dtype;
+  P.own_cache_type = P.cache_dt != cdt;
+  CHECK(check(ck, "present_key", P.cache_dt, 4, {P.B, P.kvN, -1, Hc}));
+  CHECK(check(cv, "present_value", P.cache_dt, 4, {P.B, P.kvN, ck.dims[2], Hc}));
   P.cap = (int)ck.dims[2];
   P.shared = P.has_past && ck.data == pk.data;
   if (P.has_past && ((cv.data == pv.data) != P.shared))
@@ -351,9 +362,10 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     if (P.waves > (int64_t)1 << 30) return fail(KVATTN_ERR_INVALID_ARG, "decode: too many (sample, head) units");
     P.ws_part = align256((size_t)(P.waves / 2) * P.hpw * (P.HP + 4) * sizeof(float));
   }
+  P.ws_kv = P.own_cache_type ? align256(2 * (size_t)P.B * P.kvN * P.S * P.H * esz) : 0;
   const size_t body = P.ws_q + P.ws_part;
   P.ws_cnt = body ? kCounterBytes : 0;
-  P.ws_total = P.ws_cnt + body;
+  P.ws_total = P.ws_cnt + body + P.ws_kv;
   return KVATTN_OK;
 }
 
@@ -465,6 +477,24 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   pp.win_cap = P.window_cache ? P.cap : 0;
   // quantised prompt: codes into the present caches, which the attention
   // reads and widens itself (no float copy)
+  // a present cache of another float type: the rows in T go to the
+  // workspace, which the attention reads, and to the cache in its type
+  void* att_k = ck.data;
+  void* att_v = cv.data;
+  int att_rows = P.cap;
+  if (P.own_cache_type) {
+    const size_t half = (size_t)P.B * P.kvN * P.S * P.H * elem_size(P.dt);
+    att_k = wsb + P.ws_cnt + P.ws_q + P.ws_part;
+    att_v = static_cast<char*>(att_k) + half;
+    att_rows = P.S;
+    pp.kc = att_k;
+    pp.vc = att_v;
+    pp.cap = P.S;
+    pp.kx = ck.data;
+    pp.vx = cv.data;
+    pp.xcap = P.cap;
+    pp.x_f32 = P.cache_dt == KVATTN_DT_F32;
+  }
   if (P.bits != 0) {
     pp.bits = P.bits;
     pp.kq = ck.data;
@@ -492,10 +522,10 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   f.q_s = (int64_t)P.N * P.H;
   f.q_b = f.q_s * P.S;
   f.q_h = P.H;
-  f.kc = ck.data;
-  f.vc = cv.data;
+  f.kc = att_k;
+  f.vc = att_v;
   f.k_j = P.H;
-  f.k_h = (int64_t)P.cap * P.H;
+  f.k_h = (int64_t)att_rows * P.H;
   f.k_b = f.k_h * P.kvN;
   if (P.bits != 0) {
     f.qbits = P.bits;
@@ -523,7 +553,7 @@ int gqa_run(const gqa_attrs* a, const kvattn_tensor* in, const kvattn_tensor* ou
   f.win_cap = P.window_cache ? P.cap : 0;
   f.causal = a->causal;
   f.window = a->local_window_size;
-  f.kv_rows = P.cap;
+  f.kv_rows = att_rows;
   f.B = P.B; f.S = P.S; f.N = P.N; f.kvN = P.kvN; f.H = P.H;
   f.scale = scale;
   f.softcap = a->softcap;

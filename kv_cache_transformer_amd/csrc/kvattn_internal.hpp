@@ -74,6 +74,11 @@ struct PrepParams {
   int qcap;
   const float* k_scale; const float* v_scale;
   int k_scale_pc, v_scale_pc;  // 1: kvN*H per-channel scales; 0: one scale
+  // a prompt's present cache in its own float type (write_kv only): the new
+  // rows also go to kx/vx (B, kvN, xcap, H), float32 when x_f32 else
+  // float16, each rounded once from the float32 result; null = none
+  void* kx; void* vx;
+  int xcap, x_f32;
 };
 
 // Sliding-window cache of capacity cap (GroupQueryAttention page, Attributes

@@ -79,6 +79,13 @@ __device__ void quant_store(const PrepParams& p, bool key, int b, int h, int cro
   }
 }
 
+// Element d of a row of the cache in its own float type (kx / vx).
+__device__ __forceinline__ void store_x(const PrepParams& p, void* x, int64_t row, int d, float y) {
+  const int64_t at = row * p.H + d;
+  if (p.x_f32) static_cast<float*>(x)[at] = y;
+  else static_cast<f16*>(x)[at] = from_f32<f16>(y);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
   __shared__ float row[4][256];
@@ -129,6 +136,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
           if (!done) {
             T* dst = static_cast<T*>(p.vc) + (((int64_t)b * p.kvN + h) * p.cap + crow) * H;
             for (int d = lane; d < H; d += 64) dst[d] = src[d];
+            if (p.vx != nullptr && crow < p.xcap)
+              for (int d = lane; d < H; d += 64)
+                store_x(p, p.vx, ((int64_t)b * p.kvN + h) * p.xcap + crow, d, to_f32(src[d]));
           }
         }
       } else {
@@ -201,6 +211,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepParams p) {
             for (int u = 0; u < 4; ++u) {
               int d = lane + 64 * u;
               if (d < H) dst[d] = from_f32<T>(y[u]);
+            }
+            if (p.kx != nullptr && crow < p.xcap) {
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                int d = lane + 64 * u;
+                if (d < H) store_x(p, p.kx, ((int64_t)b * p.kvN + h) * p.xcap + crow, d, y[u]);
+              }
             }
           }
         }
@@ -375,7 +392,7 @@ hipError_t launch_prep(DType dt, const PrepParams& p, hipStream_t s) {
   if (p.B * p.S == 0) return hipSuccess;
   const int ch = dt == DType::F16 ? 8 : 4;
   const int lpr = p.H / ch;  // lanes per row: a power of two (the norm sums by xor)
-  const bool vec_ok = p.bits == 0 && !p.write_q && p.write_kv && p.H % ch == 0 && lpr <= 64 && (lpr & (lpr - 1)) == 0 &&
+  const bool vec_ok = p.bits == 0 && p.kx == nullptr && !p.write_q && p.write_kv && p.H % ch == 0 && lpr <= 64 && (lpr & (lpr - 1)) == 0 &&
                       (p.cos == nullptr || p.interleaved || p.rot_half % ch == 0);
   if (vec_ok) {
     const int64_t rows = (int64_t)p.B * p.S * p.kvN;

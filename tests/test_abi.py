@@ -241,6 +241,27 @@ def test_gqa_quant_validation(lib):
                 bits=4, past="separate", S=1) == 0
 
 
+def test_gqa_prompt_cache_type(lib):
+    # without a past the float cache may be float16 or float32 whatever T is;
+    # the attention then reads the new rows in T from the workspace
+    for dt, ct in ((F16, F32), (F32, F16)):
+        ins, outs = gqa_args(dt=dt)
+        outs[1] = T(ct, 2, 2, 64, 64, ptr=0x40000)
+        outs[2] = T(ct, 2, 2, 64, 64, ptr=0x50000)
+        rc, size, msg = gqa_call(lib, ins, outs)
+        assert rc == 0 and size >= 2 * 2 * 2 * 16 * 64 * (2 if dt == F16 else 4), msg
+    ins, outs = gqa_args()
+    outs[1] = T(F32, 2, 2, 64, 64, ptr=0x40000)        # keys and values alike
+    assert gqa_call(lib, ins, outs)[0] == -1
+    outs[1] = T(I8, 2, 2, 64, 64, ptr=0x40000)
+    outs[2] = T(I8, 2, 2, 64, 64, ptr=0x50000)         # int8 without a bit width
+    assert gqa_call(lib, ins, outs)[0] == -1
+    ins, outs = gqa_args(past="concat", S=4, cap=64)   # a past fixes the type to T
+    outs[1] = T(F32, 2, 2, 64, 64, ptr=0x40000)
+    outs[2] = T(F32, 2, 2, 64, 64, ptr=0x50000)
+    assert gqa_call(lib, ins, outs, total=40)[0] == -1
+
+
 def test_gqa_head_size_and_sharing_rules(lib):
     ins, outs = gqa_args(H=12)
     assert gqa_call(lib, ins, outs)[0] == -2           # head size not a multiple of 8

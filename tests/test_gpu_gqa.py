@@ -96,6 +96,29 @@ def test_prefill_parity(idx):
 # the (sample, head-group pair) slabs a multiple of eight, each XCD takes its
 # own slabs through all row blocks, in several rounds here (38 row blocks x 8
 # slabs over at most 256 workgroups).  Every seventh query row is compared.
+# A prompt's present cache in its own float type (GroupQueryAttention page,
+# Description): the attention reads the new rows in T, the cache holds them
+# in its own type.
+CACHE_TYPE = [
+    dict(dtype=F16, cache_dtype=F32, B=2, S=150, N=8, kvN=2, H=64),
+    dict(dtype=F16, cache_dtype=F32, B=2, S=200, N=8, kvN=2, H=128, cap=230, window=37,
+         softcap=30.0, sink=True, norm=True, rotary=True),
+    dict(dtype=F32, cache_dtype=F16, B=1, S=90, N=4, kvN=1, H=128, rotary=True, norm=True,
+         window=20, bias="full"),
+    dict(dtype=F32, cache_dtype=F16, B=2, S=64, N=8, kvN=2, H=72, causal=0, total_lens=[40, 64]),
+    dict(dtype=F16, cache_dtype=F32, B=1, S=33, N=32, kvN=1, H=256),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(CACHE_TYPE)))
+def test_prompt_cache_in_its_own_type(idx):
+    print(f"cache type case {idx}: {CACHE_TYPE[idx]}", flush=True)
+    case = _case(CACHE_TYPE[idx], 5000 + idx)
+    assert case["inputs"]["present_key"].dtype == CACHE_TYPE[idx]["cache_dtype"]
+    err, n1 = _compare(case)
+    print(f"max |d| {err:.3g}; transformed key elements off: {n1}")
+
+
 def test_prefill_persistent_rounds():
     case = _case(dict(dtype=F16, B=8, S=1200, N=4, kvN=1, H=64, window=300, rotary=True, norm=True,
                       softcap=20.0), 150)
