@@ -815,7 +815,10 @@ int sparse_validate(const sparse_attrs* a, const kvattn_tensor* in, int n_in, in
   P.waves = 0;
   // one generated token: the decode kernel, one unit per query head, over the
   // blocks of its CSR row; prep writes the rotated query to the workspace
-  P.decode = P.generation && P.S == 1 && P.max_blocks <= kSparseDecodeMaxBlocks;
+  // (a row lists at most max_nnz entries, whatever its pointers say: both
+  // bound the table)
+  P.decode = P.generation && P.S == 1 && P.max_blocks <= kSparseDecodeMaxBlocks &&
+             P.max_nnz <= kSparseDecodeMaxBlocks;
   if (P.decode) {
     const int64_t units = (int64_t)P.B * P.N;
     P.waves = decode_waves(units, std::min<int64_t>(total, (int64_t)P.max_nnz * bs));

@@ -369,6 +369,30 @@ def test_sparse_rules(lib):
     assert sparse_call(lib, packed, outs, 64) == 0
 
 
+def test_sparse_generation_route_bounds_the_block_table(lib):
+    # one generated token takes the split-key decode (a workspace of counters
+    # and partials) while its per-pair block table fits LDS: a column list
+    # wider than 4096 entries sends it to the block-sparse flash route instead
+    # (no workspace), however few blocks the layout has
+    B, H = 1, 16
+    def size(width):
+        ins = [T(F16, B, 1, 4 * H), T(F16, B, 1, 2 * H), T(F16, B, 1, 2 * H),
+               T(F16, B, 2, 64, H, ptr=0x20000), T(F16, B, 2, 64, H, ptr=0x30000),
+               T(I32, 2, 5), T(I32, 2, width), T(I32, B), kb.Tensor(), kb.Tensor()]
+        a = kb.SparseAttrs()
+        lib.sparse_attrs_default(ctypes.byref(a))
+        a.num_heads, a.kv_num_heads, a.sparse_block_size = 4, 2, 16
+        n = ctypes.c_size_t(0)
+        rc = lib.sparse_attention_workspace_size(ctypes.byref(a), kb._array(ins), len(ins), 48,
+                                                 kb._array([T(F16, B, 1, 4 * H), kb.Tensor(), kb.Tensor()]),
+                                                 3, ctypes.byref(n))
+        assert rc == 0
+        return n.value
+    assert size(10) > COUNTER_BYTES
+    assert size(4096) > COUNTER_BYTES
+    assert size(4097) == 0
+
+
 def packed_call(lib, ins, outs, N=2, sizes=(0, 0, 0)):
     a = kb.PackedAttrs()
     lib.packed_attrs_default(ctypes.byref(a))

@@ -126,6 +126,23 @@ def test_sparse_generation_parity(idx):
     check_cache(pv, rpv, None, "value cache")
 
 
+def test_sparse_generation_wide_column_list():
+    # one generated token whose column list is padded past 4096 entries:
+    # the block-sparse flash route serves it (the decode route's block table
+    # would not fit LDS); the padding is never read
+    spec = dict(SPARSE_GEN[0])
+    dtype = spec.pop("dtype")
+    case = wl.sparse_case(np.random.default_rng(650), dtype=dtype, **spec)
+    i = case["inputs"]
+    cols = i["block_col_indices"]
+    i["block_col_indices"] = np.concatenate(
+        [cols, np.full((cols.shape[0], 4100 - cols.shape[1]), 7, np.int32)], axis=1)
+    out, pk, pv = sparse_gpu(case)
+    ref, rpk, rpv = sparse_oracle(case)
+    check_output(out, ref, dtype)
+    check_cache(pv, rpv, None, "value cache")
+
+
 @pytest.mark.parametrize("idx", range(len(SPARSE)))
 def test_sparse_parity(idx):
     spec = dict(SPARSE[idx])
