@@ -224,7 +224,8 @@ void gqa_attrs_default(gqa_attrs* attrs);
  * Without a past cache the present's seq axis must be >= S, and a float
  * present cache may be float16 or float32 whatever T is (GroupQueryAttention
  * page, Description): the attention then reads the new keys and values in T
- * from the workspace (2 * B * kvN * S * H elements of T), and the present
+ * from the workspace (2 * B * kvN * S * H elements of T after the counter
+ * bytes, which such a prompt leaves untouched), and the present
  * holds the same rows rounded once to its own type.  A past cache (and a
  * present with a past) has T's type.
  * total_sequence_length (host) must be >= every total_b and is the last dim

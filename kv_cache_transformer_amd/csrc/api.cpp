@@ -363,9 +363,11 @@ int gqa_validate(const gqa_attrs* a, const kvattn_tensor* in, int n_in, int tota
     P.ws_part = align256((size_t)(P.waves / 2) * P.hpw * (P.HP + 4) * sizeof(float));
   }
   P.ws_kv = P.own_cache_type ? align256(2 * (size_t)P.B * P.kvN * P.S * P.H * esz) : 0;
-  const size_t body = P.ws_q + P.ws_part;
+  // every non-empty workspace starts with the arrival counters, which no
+  // other use may touch
+  const size_t body = P.ws_q + P.ws_part + P.ws_kv;
   P.ws_cnt = body ? kCounterBytes : 0;
-  P.ws_total = P.ws_cnt + body + P.ws_kv;
+  P.ws_total = P.ws_cnt + body;
   return KVATTN_OK;
 }
 

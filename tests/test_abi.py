@@ -249,7 +249,8 @@ def test_gqa_prompt_cache_type(lib):
         outs[1] = T(ct, 2, 2, 64, 64, ptr=0x40000)
         outs[2] = T(ct, 2, 2, 64, 64, ptr=0x50000)
         rc, size, msg = gqa_call(lib, ins, outs)
-        assert rc == 0 and size >= 2 * 2 * 2 * 16 * 64 * (2 if dt == F16 else 4), msg
+        # the counters first (untouched by a prompt), then its rows in T
+        assert rc == 0 and size >= COUNTER_BYTES + 2 * 2 * 2 * 16 * 64 * (2 if dt == F16 else 4), msg
     ins, outs = gqa_args()
     outs[1] = T(F32, 2, 2, 64, 64, ptr=0x40000)        # keys and values alike
     assert gqa_call(lib, ins, outs)[0] == -1

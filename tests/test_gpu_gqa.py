@@ -174,9 +174,12 @@ def test_decode_workspace_reuse_leaves_counters_zero():
     different shapes, each checked against the oracle."""
     import torch
     ws = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda:0")
-    specs = [(DECODE[0], 310), (DECODE[7], 311), (DECODE[8], 312), (DECODE[0], 310)]
+    # a prompt whose cache has its own type puts its T rows in the workspace,
+    # after the counters: the decode after it still finds them zero
+    specs = [(DECODE[0], 310), (DECODE[7], 311), (CACHE_TYPE[0], 313), (DECODE[8], 312),
+             (DECODE[0], 310)]
     for spec, seed in specs:
-        case = _case(dict(spec, S=1), seed)
+        case = _case(spec if "cache_dtype" in spec else dict(spec, S=1), seed)
         out, _, _ = gqa_gpu(case, workspace=ws)
         ref, _, _ = gqa_oracle(case)
         check_output(out, ref, case["inputs"]["query"].dtype)

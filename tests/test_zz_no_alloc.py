@@ -1,7 +1,8 @@
 """gqa_attention_noalloc (the allocation-free variant of gqa_attention, whose
 workspace is the library's own per-GPU scratch) against gqa_attention on the
-same inputs: two decode calls in a row, the second smaller, and a quantised
-prompt (which needs no scratch).  The same kernels run with the same split,
+same inputs: two decode calls in a row, the second smaller, a quantised
+prompt (which needs no scratch), a prompt into a cache of another float type
+(whose rows in T use the scratch after its counters) and a decode after it.  The same kernels run with the same split,
 so outputs and caches must agree bit for bit."""
 
 import numpy as np
@@ -65,3 +66,10 @@ def test_noalloc_matches_gqa_attention_on_consecutive_calls():
     q = wl.gqa_case(rng, dtype=np.float32, B=2, S=150, N=8, kvN=2, H=64,
                     quant=dict(bits=8, k="channel", v="tensor"))
     _same(q, "int8 prompt B2 S150")
+    # a prompt whose float16 activations fill a float32 cache (its rows in T
+    # sit in the scratch, after the counters), then a decode again
+    rng = np.random.default_rng(79)
+    c = wl.gqa_case(rng, dtype=np.float16, B=2, S=150, N=8, kvN=2, H=64, rotary=True,
+                    cache_dtype=np.float32)
+    _same(c, "float16 prompt into a float32 cache, B2 S150")
+    _same(small, "decode B3, cache 600, after the prompt")
