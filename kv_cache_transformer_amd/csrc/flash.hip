@@ -3,11 +3,11 @@
 // A work item is a block of query rows for one or more query heads that
 // share a kv head; every wave owns 32 query rows of one head.  Key/value
 // tiles of BN rows are staged in LDS and shared by the waves of the item:
-// flash_pp_kernel (dense and varlen f16 prompts, heads up to 128) copies them
+// flash_pp_kernel (dense f16 prompts, heads up to 128) copies them
 // from global memory straight into LDS and runs two items per workgroup in
-// alternating MFMA and softmax phases; flash_kernel (block-sparse, float32,
-// heads of 256) fills double-buffered LDS tiles from registers loaded one
-// tile ahead.
+// alternating MFMA and softmax phases; flash_kernel (block-sparse, varlen,
+// float32, heads of 256) fills double-buffered LDS tiles from registers
+// loaded one tile ahead.
 //
 //   S^T[keys][32 queries] = K_tile . Q^T        (f16: 32x32x16, f32: 32x32x2)
 //   O^T[H][32 queries]   += V_tile^T . P^T
@@ -1173,8 +1173,8 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
 
   const int n_items = gx * gy * gz;
   const int NPH = (gy + 1) / 2;
-  // varlen: the work list holds work[0] items (of at most gx) per head
-  const int npairs = (MODE == kVarlen) ? (min(p.work[0], gx) * gy * gz + 1) / 2 : gx * NPH * gz;
+  static_assert(MODE == kDense, "the ping-pong kernel serves dense prompts");
+  const int npairs = gx * NPH * gz;
   const int G = gridDim.x, wg = blockIdx.x;
   const int wx = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
   const int S = NPH * gz;  // dense: slab pairs
@@ -1183,7 +1183,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   // them again, and a global load there would cost a memory latency
   constexpr int kLensMax = 1024;
   __shared__ int s_lens[kLensMax];
-  const int nlens = (MODE == kDense) ? min(p.B, kLensMax) : 0;
+  const int nlens = min(p.B, kLensMax);
   for (int i = threadIdx.x; i < nlens; i += 512) s_lens[i] = p.lens[i];
   __syncthreads();
   // The output of a round waits in LDS (each wave's 32 x HP tile, row-major,
@@ -1234,9 +1234,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   // ---- the workgroup's pairs of items ------------------------------------------
   // At most one workgroup per CU, looping over pairs of items, mirrored on odd
   // rounds so that the long pairs of one round meet the short pairs of the
-  // next.  Varlen: pair f is items 2 f and 2 f + 1 of the list order (longest
-  // sequences first).  Dense: pairs = (row block, slab pair), a slab pair
-  // being a sample and a pair of adjacent head groups, row blocks taken latest
+  // next.  Pairs = (row block, slab pair), a slab pair being a sample and a pair of adjacent head groups, row blocks taken latest
   // first (the most keys under a causal bound).  When the slab pairs split evenly over the
   // eight XCDs, each XCD takes its own slab pairs through all row blocks: the
   // rows in flight on one XCD then share the K/V windows of a few slabs, which
@@ -1244,7 +1242,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   // its rank in an XCD-contiguous order.
   int f = round * G + ((round & 1) ? G - 1 - wx : wx);
   int rbi = 0, sp = 0;
-  if (MODE == kDense && xcd_slabs) {
+  if (xcd_slabs) {
     const int NB = S / 8, G8 = G / 8, wl = wg / 8;
     const int q = round * G8 + ((round & 1) ? G8 - 1 - wl : wl);
     if (q >= gx * NB) break;
@@ -1256,10 +1254,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
     sp = f - rbi * S;
   }
   int id_own, id_other;
-  if (MODE == kVarlen) {
-    id_own = 2 * f + grp;
-    id_other = 2 * f + (grp ^ 1);
-  } else {
+  {
     const int bb = sp / NPH, jp = sp - bb * NPH;
     const int base = rbi + gx * gy * bb;
     id_own = (2 * jp + grp < gy) ? base + gx * (2 * jp + grp) : n_items;
@@ -1271,7 +1266,6 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   const int n_tiles = live ? w.n_tiles : 0;
   const int n_steps = max(n_tiles, live_o ? wo.n_tiles : 0);   // the same in every wave
   const int b = w.b, h = w.h, nrows = w.nrows, past = w.past;
-  const int64_t row_base = w.row_base;
   const f16* kg = static_cast<const f16*>(p.kc) + (live ? w.kv_base : 0);
   const f16* vg = static_cast<const f16*>(p.vc) + (live ? w.kv_base : 0);
   const int kj = (int)p.k_j;
@@ -1364,9 +1358,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   {
     const int rr = min(qrow, nrows - 1);
     const f16* qg = static_cast<const f16*>(p.q);
-    const f16* qp = (MODE == kVarlen)
-                        ? qg + (row_base + rr) * p.q_s + (int64_t)h * p.q_h
-                        : qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
+    const f16* qp = qg + (int64_t)b * p.q_b + (int64_t)rr * p.q_s + (int64_t)h * p.q_h;
     // the previous round's stores and this round's query loads are in flight
     // together (one wait covers both)
     store_pending(V0 + wave * 32 * HP);
@@ -1376,15 +1368,8 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   const int pos = past + qrow;
   const f16* bias = static_cast<const f16*>(p.bias);
   int64_t bias_row = 0;
-  if (bias != nullptr && live) {
-    if (MODE == kVarlen) {
-      int pad_q = p.token_offset[row_base + min(qrow, nrows - 1)] - b * p.pad_seq;
-      pad_q = min(max(pad_q, 0), p.pad_seq - 1);
-      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)pad_q * p.bias_ss;
-    } else {
-      bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)min(qrow, nrows - 1) * p.bias_ss;
-    }
-  }
+  if (bias != nullptr && live)
+    bias_row = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)min(qrow, nrows - 1) * p.bias_ss;
 
   // ---- softmax of one tile (vector ALU) -----------------------------------------
   auto mask_scores = [&](const TileRange& r, float16v (&sc)[2]) {
@@ -1423,15 +1408,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
         }
         float v = sc[blk][i];
         if (use_cap) v = capA - capB * fast_rcp(fast_exp2(v) + 1.f);
-        if (bias != nullptr && ok) {
-          if (MODE == kVarlen) {
-            int pad_k = p.token_offset[row_base + key] - b * p.pad_seq;
-            pad_k = min(max(pad_k, 0), p.pad_seq - 1);
-            v += kLog2e * to_f32(bias[bias_row + pad_k]);
-          } else if (key < p.bias_cols) {
-            v += kLog2e * to_f32(bias[bias_row + key]);
-          }
-        }
+        if (bias != nullptr && ok && key < p.bias_cols) v += kLog2e * to_f32(bias[bias_row + key]);
         sc[blk][i] = ok ? v : kNegInf;
       }
   };
@@ -1669,8 +1646,7 @@ __global__ __launch_bounds__(512, 1) void flash_pp_kernel(FlashParams p, int gx,
   if (lane == 0) {
     f16* og = static_cast<f16*>(p.out);
     s_pend_rows[wv] = min(32, w.wg_rows_end - w.wrow0);
-    s_pend_base[wv] = (MODE == kVarlen) ? og + (row_base + w.wrow0) * p.o_s + (int64_t)h * p.o_h
-                                        : og + (int64_t)b * p.o_b + (int64_t)w.wrow0 * p.o_s + (int64_t)h * p.o_h;
+    s_pend_base[wv] = og + (int64_t)b * p.o_b + (int64_t)w.wrow0 * p.o_s + (int64_t)h * p.o_h;
   }
   }
   {
@@ -1704,8 +1680,11 @@ hipError_t launch_pp(const FlashParams& p, dim3 grid, hipStream_t s) {
 
 template <typename T, int HP, int BN>
 hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
-  // dense and varlen f16 prompts with heads up to 128 run on the ping-pong
-  // kernel (four waves of 32 rows per item)
+  // dense f16 prompts with heads up to 128 run on the ping-pong kernel (four
+  // waves of 32 rows per item).  Varlen items (a packed sequence's row block,
+  // 32 to 512 keys) are too short for its per-round start: the four-wave
+  // flash kernel, many workgroups per CU, runs them faster (54-58 us against
+  // 64-65 us on the 64-sequence packed batch, the same device)
   constexpr bool kPipe = std::is_same<T, f16>::value && BN == 64 && HP <= 128;
   switch (p.mode) {
     case kDense: {
@@ -1726,9 +1705,6 @@ hipError_t launch_flash_t(const FlashParams& p, dim3 grid, hipStream_t s) {
       return launch_mode<T, HP, BN, kCsr>(p, grid, nw >= 4 ? 4 : (nw == 2 ? 2 : 1), s);
     }
     default:
-      if constexpr (kPipe) {
-        if (p.rows_per_wg / 32 * p.heads_per_wg == 4) return launch_pp<HP, kVarlen>(p, grid, s);
-      }
       launch_kernel((flash_kernel<T, HP, BN, kVarlen, 4, false>), grid, dim3(256), 0, s, p);
       return hipGetLastError();
   }
