@@ -1667,10 +1667,10 @@ hipError_t launch_mode(const FlashParams& p, dim3 grid, int nw, hipStream_t s) {
 // Two items of the (gx, gy, gz) item grid per eight-wave workgroup.
 template <int HP, int MODE, bool SOFTCAP = false>
 hipError_t launch_pp(const FlashParams& p, dim3 grid, hipStream_t s) {
-  const int items = (int)(grid.x * grid.y * grid.z);
-  // one workgroup per CU at most, each looping over pairs of items (varlen:
-  // of the items the work list may hold; dense: pairs of head groups)
-  const int pairs = (MODE == kDense) ? (int)grid.x * (((int)grid.y + 1) / 2) * (int)grid.z : (items + 1) / 2;
+  static_assert(MODE == kDense, "the ping-pong kernel serves dense prompts");
+  // one workgroup per CU at most, each looping over pairs of items (pairs of
+  // head groups)
+  const int pairs = (int)grid.x * (((int)grid.y + 1) / 2) * (int)grid.z;
   const int wgs = std::min(pairs, cu_count());
   if (wgs <= 0) return hipSuccess;
   launch_kernel((flash_pp_kernel<HP, MODE, SOFTCAP>), dim3(wgs), dim3(512), 0, s, p,
